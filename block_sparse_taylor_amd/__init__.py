@@ -1,0 +1,195 @@
+"""PISA piecewise sparse attention forward for MI355X (gfx950).
+
+Thin Python binding over libpisa's C ABI (include/pisa.h). Tensors are torch
+tensors on a ROCm device; torch provides device memory and the current HIP
+stream, the library does every step of the computation. There is no CPU or
+eager fallback: if libpisa.so is missing, the calls raise.
+
+The three calls follow the PISA paper's Algorithm 1 (prepare phase steps 1-2,
+fused kernel Phases 1-3):
+
+    stats     = pisa_block_stats(k, v, second_order=...)
+    idx, wg   = pisa_route_topk(q, stats, topk=..., band=1, second_order=...)
+    o         = pisa_attn_fwd(q, k, v, stats, idx, wg, ...)
+
+``piecewise_sparse_attention`` chains them with topk = floor(density * N).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib
+from ._lib import PISA_BF16, PISA_F32, PisaError
+
+__all__ = ["PisaStats", "pisa_block_stats", "pisa_route_topk", "pisa_attn_fwd",
+           "pisa_attn_fwd_valu", "piecewise_sparse_attention", "num_blocks", "topk_for_density",
+           "PisaError", "library"]
+
+BLOCK = 64
+
+
+def library():
+    return _lib.load()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return PISA_BF16
+    if t.dtype == torch.float32:
+        return PISA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _shape(q: torch.Tensor, scale) -> _lib.Shape:
+    if q.dim() != 4:
+        raise ValueError("expected [batch, heads, seq_len, head_dim]")
+    B, H, T, D = q.shape
+    return _lib.Shape(B, H, T, D, BLOCK, _dtype_code(q), float(scale) if scale else 0.0)
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def num_blocks(seq_len: int) -> int:
+    return -(-seq_len // BLOCK)
+
+
+def topk_for_density(density: float, n_blocks: int) -> int:
+    """k = floor(density * N) routed blocks per query block (band excluded)."""
+    return max(0, min(n_blocks, int(math.floor(density * n_blocks + 1e-9))))
+
+
+@dataclass
+class PisaStats:
+    kbar: torch.Tensor      # fp64 [B,H,N,D]
+    vsum: torch.Tensor      # fp32 [B,H,N,D]
+    ksig2: torch.Tensor | None
+    hsum: torch.Tensor      # fp32 [B,H,D,D]
+    kbar_c: torch.Tensor    # input dtype [B,H,N,D]
+    vbar_c: torch.Tensor
+
+    def as_c(self) -> _lib.Stats:
+        return _lib.Stats(_ptr(self.kbar), _ptr(self.vsum), _ptr(self.ksig2), _ptr(self.hsum),
+                          _ptr(self.kbar_c), _ptr(self.vbar_c))
+
+
+def _contig(*ts):
+    for t in ts:
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def alloc_stats(k: torch.Tensor, second_order: bool) -> PisaStats:
+    B, H, T, D = k.shape
+    N = num_blocks(T)
+    dev = k.device
+    return PisaStats(
+        kbar=torch.empty(B, H, N, D, dtype=torch.float64, device=dev),
+        vsum=torch.empty(B, H, N, D, dtype=torch.float32, device=dev),
+        ksig2=torch.empty(B, H, N, D, dtype=torch.float64, device=dev) if second_order else None,
+        hsum=torch.empty(B, H, D, D, dtype=torch.float32, device=dev),
+        kbar_c=torch.empty(B, H, N, D, dtype=k.dtype, device=dev),
+        vbar_c=torch.empty(B, H, N, D, dtype=k.dtype, device=dev),
+    )
+
+
+def stats_workspace(k: torch.Tensor, scale=None) -> torch.Tensor:
+    lib = library()
+    sh = _shape(k, scale)
+    n = lib.pisa_stats_workspace_bytes(ctypes.byref(sh))
+    return torch.empty(max(16, n), dtype=torch.uint8, device=k.device)
+
+
+def pisa_block_stats(k, v, second_order=False, scale=None, out: PisaStats | None = None,
+                     workspace: torch.Tensor | None = None) -> PisaStats:
+    lib = library()
+    _contig(k, v)
+    sh = _shape(k, scale)
+    out = out or alloc_stats(k, second_order)
+    ws = workspace if workspace is not None else stats_workspace(k, scale)
+    prm = _lib.Params(0, 0, int(second_order), 1, 0)
+    cs = out.as_c()
+    _lib.check("pisa_block_stats", lib.pisa_block_stats(
+        ctypes.byref(sh), ctypes.byref(prm), _ptr(k), _ptr(v), ctypes.byref(cs), _ptr(ws),
+        ws.numel(), _stream(k.device)))
+    return out
+
+
+def pisa_route_topk(q, stats: PisaStats, topk: int, band: int = 1, second_order=False, scale=None,
+                    idx: torch.Tensor | None = None, wgate: torch.Tensor | None = None):
+    lib = library()
+    _contig(q)
+    sh = _shape(q, scale)
+    B, H, T, D = q.shape
+    N = num_blocks(T)
+    if idx is None:
+        idx = torch.empty(B, H, N, max(topk, 1), dtype=torch.int32, device=q.device)[..., :topk]
+        idx = idx.contiguous() if topk else idx
+    if second_order and wgate is None:
+        wgate = torch.empty(B, H, N, N, dtype=torch.float32, device=q.device)
+    prm = _lib.Params(int(topk), int(band), int(second_order), 1, 0)
+    cs = stats.as_c()
+    _lib.check("pisa_route_topk", lib.pisa_route_topk(
+        ctypes.byref(sh), ctypes.byref(prm), _ptr(q), ctypes.byref(cs),
+        _ptr(idx) if topk else None, _ptr(wgate) if second_order else None, _stream(q.device)))
+    return idx, (wgate if second_order else None)
+
+
+def _attn(fn_name, q, k, v, stats, idx, wgate, topk, band, second_order, first_order,
+          phase_mask, scale, out):
+    lib = library()
+    _contig(q, k, v, idx, wgate)
+    sh = _shape(q, scale)
+    o = out if out is not None else torch.empty_like(q)
+    prm = _lib.Params(int(topk), int(band), int(second_order), int(first_order), int(phase_mask))
+    cs = stats.as_c()
+    fn = getattr(lib, fn_name)
+    _lib.check(fn_name, fn(ctypes.byref(sh), ctypes.byref(prm), _ptr(q), _ptr(k), _ptr(v),
+                           ctypes.byref(cs), _ptr(idx) if topk else None,
+                           _ptr(wgate) if second_order else None, _ptr(o), _stream(q.device)))
+    return o
+
+
+def pisa_attn_fwd(q, k, v, stats, idx, wgate=None, band=1, second_order=False, first_order=True,
+                  phase_mask=0, scale=None, out=None):
+    topk = 0 if idx is None else idx.shape[-1]
+    return _attn("pisa_attn_fwd", q, k, v, stats, idx, wgate, topk, band, second_order,
+                 first_order, phase_mask, scale, out)
+
+
+def pisa_attn_fwd_valu(q, k, v, stats, idx, wgate=None, band=1, second_order=False,
+                       first_order=True, phase_mask=0, scale=None, out=None):
+    topk = 0 if idx is None else idx.shape[-1]
+    return _attn("pisa_attn_fwd_valu", q, k, v, stats, idx, wgate, topk, band, second_order,
+                 first_order, phase_mask, scale, out)
+
+
+def piecewise_sparse_attention(q, k, v, density=0.125, variant="pisa", band=1, scale=None,
+                               n_sink_blocks=0, cov_bias=False, reorder="none"):
+    """PISA (variant="pisa") or PISA with the gated second-order term ("pwt").
+
+    q, k, v: [B, H, T, D] bf16 or fp32 on the GPU. topk = floor(density * N)
+    routed blocks per query block, plus the +-band, are computed exactly.
+    """
+    if n_sink_blocks or cov_bias or reorder != "none":
+        raise NotImplementedError("sink blocks, covariance bias and token reordering are not built")
+    if variant not in ("pisa", "pwt"):
+        raise ValueError(variant)
+    so = variant == "pwt"
+    N = num_blocks(q.shape[2])
+    topk = topk_for_density(density, N)
+    topk = min(topk, N)
+    st = pisa_block_stats(k, v, second_order=so, scale=scale)
+    idx, wg = pisa_route_topk(q, st, topk, band=band, second_order=so, scale=scale)
+    return pisa_attn_fwd(q, k, v, st, idx if topk else None, wg, band=band, second_order=so,
+                         scale=scale)

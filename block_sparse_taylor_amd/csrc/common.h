@@ -1,0 +1,64 @@
+// Internal declarations shared by the libpisa translation units (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pisa.h"
+
+namespace pisa {
+
+constexpr int kBlock = 64;        // rows per query / KV block (the paper's 64x64 kernel block)
+constexpr int kThreads = 256;     // workgroup size of every kernel (4 wave64)
+
+typedef unsigned short bf16_t;    // bf16 storage (bit pattern)
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t x) {
+    return __uint_as_float(static_cast<uint32_t>(x) << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 (inputs here are finite).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return static_cast<bf16_t>(u >> 16);
+}
+
+template <typename T> __device__ __forceinline__ float load_f32(const T* p);
+template <> __device__ __forceinline__ float load_f32<float>(const float* p) { return *p; }
+template <> __device__ __forceinline__ float load_f32<bf16_t>(const bf16_t* p) { return bf16_to_f32(*p); }
+
+template <typename T> __device__ __forceinline__ T store_cast(float x);
+template <> __device__ __forceinline__ float store_cast<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16_t store_cast<bf16_t>(float x) { return f32_to_bf16(x); }
+
+// Problem geometry resolved once on the host.
+struct Geom {
+    int64_t BH;       // batch * heads
+    int T;            // tokens
+    int D;            // head dim
+    int N;            // blocks
+    float scale;      // softmax scale
+};
+
+// Kernel launchers (return hipSuccess or the launch error).
+hipError_t launch_block_stats(const Geom& g, int dtype, int second_order, const void* k, const void* v,
+                              const pisa_stats_t* out, void* workspace, hipStream_t stream);
+size_t stats_workspace_bytes(const Geom& g);
+
+hipError_t launch_route_topk(const Geom& g, int dtype, const pisa_params_t* p, const void* q,
+                             const pisa_stats_t* st, int32_t* idx, float* wgate, hipStream_t stream);
+
+hipError_t launch_attn_fwd_valu(const Geom& g, int dtype, const pisa_params_t* p, const void* q,
+                                const void* k, const void* v, const pisa_stats_t* st,
+                                const int32_t* idx, const float* wgate, void* o, hipStream_t stream);
+
+hipError_t launch_attn_fwd_mfma(const Geom& g, const pisa_params_t* p, const void* q, const void* k,
+                                const void* v, const pisa_stats_t* st, const int32_t* idx,
+                                const float* wgate, void* o, hipStream_t stream);
+
+}  // namespace pisa

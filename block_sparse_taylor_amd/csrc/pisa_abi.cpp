@@ -1,0 +1,175 @@
+// C ABI of libpisa: host-side argument validation and kernel dispatch.
+// Every check runs before the first HIP call, so invalid requests return a
+// status without touching the device (and can be tested on a GPU-less host).
+#include <math.h>
+#include <stdint.h>
+
+#include "common.h"
+
+using namespace pisa;
+
+namespace {
+
+constexpr int64_t kMaxSeq = 524288;   // N <= 8192 keeps a routing row in LDS
+constexpr int64_t kMaxBH = 65535;     // grid y dimension
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+pisa_status_t check_shape(const pisa_shape_t* s, Geom* g) {
+    if (!s) return PISA_ERR_NULL;
+    if (s->dtype != PISA_F32 && s->dtype != PISA_BF16) return PISA_ERR_DTYPE;
+    if (s->batch < 1 || s->heads < 1 || s->seq_len < 1 || s->seq_len > kMaxSeq) return PISA_ERR_SHAPE;
+    if (s->batch > kMaxBH || s->heads > kMaxBH || s->batch * s->heads > kMaxBH) return PISA_ERR_SHAPE;
+    if (s->head_dim != 64 && s->head_dim != 128) return PISA_ERR_SHAPE;
+    if (s->block_size != kBlock) return PISA_ERR_PARAM;
+    if (!isfinite(s->scale)) return PISA_ERR_PARAM;
+    if (g) {
+        g->BH = s->batch * s->heads;
+        g->T = (int)s->seq_len;
+        g->D = (int)s->head_dim;
+        g->N = (int)((s->seq_len + kBlock - 1) / kBlock);
+        g->scale = s->scale > 0.f ? s->scale : 1.0f / sqrtf((float)s->head_dim);
+    }
+    return PISA_OK;
+}
+
+pisa_status_t check_params(const pisa_params_t* p, const Geom& g) {
+    if (!p) return PISA_ERR_NULL;
+    if (p->topk < 0 || p->topk > g.N) return PISA_ERR_PARAM;
+    if (p->band < 0) return PISA_ERR_PARAM;
+    if (p->second_order != 0 && p->second_order != 1) return PISA_ERR_PARAM;
+    if (p->first_order != 0 && p->first_order != 1) return PISA_ERR_PARAM;
+    if (p->phase_mask < 0 || p->phase_mask > 7) return PISA_ERR_PARAM;
+    return PISA_OK;
+}
+
+pisa_status_t check_ptr(const void* p) {
+    if (!p) return PISA_ERR_NULL;
+    return aligned16(p) ? PISA_OK : PISA_ERR_ALIGN;
+}
+
+#define PISA_TRY(expr)                        \
+    do {                                      \
+        pisa_status_t st_ = (expr);           \
+        if (st_ != PISA_OK) return st_;       \
+    } while (0)
+
+pisa_status_t check_stats(const pisa_stats_t* st, int second_order, bool need_c) {
+    if (!st) return PISA_ERR_NULL;
+    PISA_TRY(check_ptr(st->kbar));
+    PISA_TRY(check_ptr(st->vsum));
+    PISA_TRY(check_ptr(st->hsum));
+    if (need_c) {
+        PISA_TRY(check_ptr(st->kbar_c));
+        PISA_TRY(check_ptr(st->vbar_c));
+    }
+    if (second_order) PISA_TRY(check_ptr(st->ksig2));
+    else if (st->ksig2 && !aligned16(st->ksig2)) return PISA_ERR_ALIGN;
+    return PISA_OK;
+}
+
+pisa_status_t from_hip(hipError_t e) { return e == hipSuccess ? PISA_OK : PISA_ERR_HIP; }
+
+pisa_status_t attn_common(const pisa_shape_t* shape, const pisa_params_t* params, const void* q,
+                          const void* k, const void* v, const pisa_stats_t* stats,
+                          const int32_t* idx, const float* wgate, void* o, Geom* g) {
+    PISA_TRY(check_shape(shape, g));
+    PISA_TRY(check_params(params, *g));
+    PISA_TRY(check_ptr(q));
+    PISA_TRY(check_ptr(k));
+    PISA_TRY(check_ptr(v));
+    PISA_TRY(check_ptr(o));
+    PISA_TRY(check_stats(stats, 0, shape->dtype == PISA_BF16));
+    if (params->topk > 0) PISA_TRY(check_ptr(idx));
+    if (params->second_order) PISA_TRY(check_ptr(wgate));
+    if (o == q || o == k || o == v) return PISA_ERR_PARAM;
+    return PISA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pisa_abi_version(void) { return PISA_ABI_VERSION; }
+
+const char* pisa_status_str(pisa_status_t s) {
+    switch (s) {
+        case PISA_OK: return "ok";
+        case PISA_ERR_NULL: return "null pointer";
+        case PISA_ERR_SHAPE: return "shape out of range";
+        case PISA_ERR_DTYPE: return "unknown dtype";
+        case PISA_ERR_PARAM: return "parameter out of range";
+        case PISA_ERR_ALIGN: return "pointer not 16-byte aligned";
+        case PISA_ERR_UNSUPPORTED: return "unsupported";
+        case PISA_ERR_HIP: return "HIP launch/runtime error";
+        case PISA_ERR_WORKSPACE: return "workspace too small";
+    }
+    return "unknown status";
+}
+
+int64_t pisa_num_blocks(const pisa_shape_t* shape) {
+    Geom g;
+    if (check_shape(shape, &g) != PISA_OK) return -1;
+    return g.N;
+}
+
+size_t pisa_stats_workspace_bytes(const pisa_shape_t* shape) {
+    Geom g;
+    if (check_shape(shape, &g) != PISA_OK) return 0;
+    return stats_workspace_bytes(g);
+}
+
+pisa_status_t pisa_block_stats(const pisa_shape_t* shape, const pisa_params_t* params, const void* k,
+                               const void* v, const pisa_stats_t* out, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+    Geom g;
+    PISA_TRY(check_shape(shape, &g));
+    PISA_TRY(check_params(params, g));
+    PISA_TRY(check_ptr(k));
+    PISA_TRY(check_ptr(v));
+    PISA_TRY(check_stats(out, params->second_order, true));
+    PISA_TRY(check_ptr(workspace));
+    if (workspace_bytes < stats_workspace_bytes(g)) return PISA_ERR_WORKSPACE;
+    return from_hip(launch_block_stats(g, shape->dtype, params->second_order, k, v, out, workspace,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+pisa_status_t pisa_route_topk(const pisa_shape_t* shape, const pisa_params_t* params, const void* q,
+                              const pisa_stats_t* stats, int32_t* idx, float* wgate, void* stream) {
+    Geom g;
+    PISA_TRY(check_shape(shape, &g));
+    PISA_TRY(check_params(params, g));
+    PISA_TRY(check_ptr(q));
+    if (!stats) return PISA_ERR_NULL;
+    PISA_TRY(check_ptr(stats->kbar));
+    if (params->second_order) {
+        PISA_TRY(check_ptr(stats->ksig2));
+        PISA_TRY(check_ptr(wgate));
+    }
+    if (params->topk > 0) PISA_TRY(check_ptr(idx));
+    return from_hip(launch_route_topk(g, shape->dtype, params, q, stats, idx, wgate,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+pisa_status_t pisa_attn_fwd(const pisa_shape_t* shape, const pisa_params_t* params, const void* q,
+                            const void* k, const void* v, const pisa_stats_t* stats,
+                            const int32_t* idx, const float* wgate, void* o, void* stream) {
+    Geom g;
+    PISA_TRY(attn_common(shape, params, q, k, v, stats, idx, wgate, o, &g));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (shape->dtype == PISA_BF16)
+        return from_hip(launch_attn_fwd_mfma(g, params, q, k, v, stats, idx, wgate, o, s));
+    return from_hip(launch_attn_fwd_valu(g, shape->dtype, params, q, k, v, stats, idx, wgate, o, s));
+}
+
+pisa_status_t pisa_attn_fwd_valu(const pisa_shape_t* shape, const pisa_params_t* params,
+                                 const void* q, const void* k, const void* v,
+                                 const pisa_stats_t* stats, const int32_t* idx, const float* wgate,
+                                 void* o, void* stream) {
+    Geom g;
+    PISA_TRY(attn_common(shape, params, q, k, v, stats, idx, wgate, o, &g));
+    return from_hip(launch_attn_fwd_valu(g, shape->dtype, params, q, k, v, stats, idx, wgate, o,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

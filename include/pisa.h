@@ -1,0 +1,184 @@
+/*
+ * pisa.h - C ABI of libpisa, the gfx950 (MI355X) forward path of PISA
+ * piecewise sparse attention.
+ *
+ * Method: "PISA: Piecewise Sparse Attention Is Wiser for Efficient Diffusion
+ * Transformers" (arXiv 2602.01077), §3.2 Eqs. 3-6, §3.3 Eqs. 9-10, §3.4
+ * Algorithm 1; the optional second-order mass term and its gate follow the
+ * "Piecewise-Taylor-Attention" README ("Blog post" section and changelog).
+ *
+ * The operator is split along the paper's own phases (Algorithm 1, "Prepare
+ * Phase" steps 1-2, then the fused kernel's Phases 1-3):
+ *
+ *   pisa_block_stats  - per-KV-block statistics and the global H   (step 1)
+ *   pisa_route_topk   - pooled-score routing, top-k per query block (step 2)
+ *   pisa_attn_fwd     - exact + virtual-token + global first order (Phases 1-3)
+ *
+ * Conventions shared by all entry points
+ * --------------------------------------
+ * - Tensors q, k, v, o are [batch, heads, seq_len, head_dim] row-major and
+ *   contiguous, in the dtype named by pisa_shape_t.dtype (PISA_BF16: bf16
+ *   storage; PISA_F32: fp32). N = ceil(seq_len / block_size) blocks; block j
+ *   holds rows [64 j, min(64 j + 64, seq_len)); the last block may be partial.
+ * - Every pointer argument is a DEVICE pointer (HBM), except the shape and
+ *   parameter structs, which are host pointers read during the call.
+ * - All work is enqueued asynchronously on `stream` (a hipStream_t; NULL is
+ *   the null stream). No call synchronises, allocates or frees memory; the
+ *   caller owns every buffer, sized with the helpers below.
+ * - Every argument is validated on the host before any HIP call; a failing
+ *   check returns a status and enqueues nothing. A launch failure returns
+ *   PISA_ERR_HIP. Faults inside kernels surface at the caller's next
+ *   synchronisation. Device data (e.g. routing table contents) are not
+ *   validated: out-of-range block ids are undefined behaviour.
+ * - Results are deterministic: no floating-point atomics, fixed reduction
+ *   orders, identical bits for identical inputs and launch shapes.
+ * - Softmax scale s = shape.scale, or 1/sqrt(head_dim) when scale <= 0; it
+ *   multiplies every logit (exact, virtual and routing), and the Taylor
+ *   terms use q' = s q (Appendix C of the paper puts 1/sqrt(d) in alpha).
+ */
+#ifndef PISA_H_
+#define PISA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PISA_ABI_VERSION 1
+
+typedef enum {
+    PISA_OK = 0,
+    PISA_ERR_NULL = 1,        /* a required pointer is NULL                         */
+    PISA_ERR_SHAPE = 2,       /* batch/heads/seq_len/head_dim out of range           */
+    PISA_ERR_DTYPE = 3,       /* unknown dtype                                      */
+    PISA_ERR_PARAM = 4,       /* topk, band, flags or scale out of range            */
+    PISA_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned                   */
+    PISA_ERR_UNSUPPORTED = 6, /* valid request this build does not implement        */
+    PISA_ERR_HIP = 7,         /* a HIP launch or runtime call failed                */
+    PISA_ERR_WORKSPACE = 8    /* workspace smaller than pisa_stats_workspace_bytes   */
+} pisa_status_t;
+
+typedef enum { PISA_F32 = 0, PISA_BF16 = 1 } pisa_dtype_t;
+
+typedef struct {
+    int64_t batch;      /* >= 1                                            */
+    int64_t heads;      /* >= 1                                            */
+    int64_t seq_len;    /* T >= 1, at most 524288 (N <= 8192 blocks)         */
+    int64_t head_dim;   /* D, 64 or 128                                     */
+    int32_t block_size; /* B; must be 64 (the paper's kernel block, §4.1)   */
+    int32_t dtype;      /* pisa_dtype_t of q, k, v, o                       */
+    float scale;        /* softmax scale; <= 0 selects 1/sqrt(head_dim)     */
+} pisa_shape_t;
+
+typedef struct {
+    int32_t topk;         /* routed KV blocks per query block, band excluded, 0..N */
+    int32_t band;         /* |i - j| <= band is always exact (>= 0)               */
+    int32_t second_order; /* 1: add the gated second-order term w (README)        */
+    int32_t first_order;  /* 1: global first order (Eq. 10, Phase 3); 0: off     */
+    int32_t phase_mask;   /* 0 = all phases; bit0 exact, bit1 virtual, bit2 first
+                             order (measurement only)                            */
+} pisa_params_t;
+
+/*
+ * Block statistics (Algorithm 1 step 1; §3.2 Formulation; Appendix C):
+ *   kbar[j]   = (1/n_j) sum_n k_{j,n}                  fp64 [B,H,N,D]
+ *   vsum[j]   = sum_n v_{j,n}               (V-hat)    fp32 [B,H,N,D]
+ *   ksig2[j]  = (1/n_j) sum_n (k_{j,n} - kbar_j)^2     fp64 [B,H,N,D]
+ *               (per-dim population variance; README "Blog post")
+ *   hsum      = sum_j sum_n (k_{j,n} - kbar_j)^T v_{j,n}
+ *                                            (D x D)   fp32 [B,H,D,D]
+ *               (row index: key dim, column index: value dim)
+ *   kbar_c[j] = kbar[j] rounded to the input dtype      [B,H,N,D]
+ *   vbar_c[j] = vsum[j] / n_j rounded to the input dtype [B,H,N,D]
+ * kbar and ksig2 are fp64 so that routing decisions (a top-k, a gate) match
+ * a float64 evaluation; kbar_c / vbar_c feed the virtual-token phase.
+ */
+typedef struct {
+    double *kbar;
+    float *vsum;
+    double *ksig2; /* may be NULL unless params.second_order */
+    float *hsum;
+    void *kbar_c;
+    void *vbar_c;
+} pisa_stats_t;
+
+/* ABI version of the library (PISA_ABI_VERSION). */
+int pisa_abi_version(void);
+
+/* Human-readable name of a status code (static storage). */
+const char *pisa_status_str(pisa_status_t s);
+
+/* N = ceil(seq_len / block_size), or -1 if the shape is invalid. */
+int64_t pisa_num_blocks(const pisa_shape_t *shape);
+
+/* Bytes of device workspace pisa_block_stats needs (partial H sums), or 0 if
+ * the shape is invalid. */
+size_t pisa_stats_workspace_bytes(const pisa_shape_t *shape);
+
+/*
+ * pisa_block_stats: reads k, v; writes every field of `out` (ksig2 only if
+ * params->second_order). `workspace` is caller-owned device memory of at
+ * least pisa_stats_workspace_bytes(shape) bytes; its contents on entry are
+ * ignored and on return are unspecified. Outputs must not alias inputs.
+ */
+pisa_status_t pisa_block_stats(const pisa_shape_t *shape, const pisa_params_t *params,
+                               const void *k, const void *v, const pisa_stats_t *out,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * pisa_route_topk (Algorithm 1 step 2 with the pooled score of Eq. 11 minus
+ * its covariance term; README router): for each query block i,
+ *   qbar_i  = mean of its query rows, q2bar_i = mean of (s q)^2,
+ *   r_ij    = s qbar_i . kbar_j + [second_order] min(w_ij, ln B),
+ *   w_ij    = 1/2 q2bar_i . ksig2_j,
+ * over the candidates j with |i - j| > band. idx[b,h,i,:] receives the
+ * min(topk, #candidates) best j (ties: lower j wins), ascending, then -1.
+ * Scores, pooled means and w are evaluated in fp64.
+ * idx: int32 [B,H,N,topk] (may be NULL iff topk == 0).
+ * wgate: fp32 [B,H,N,N], required iff second_order: the gated term used by
+ *   the virtual-token logits: w_ij where w_ij <= ln B, and 0 where w_ij is
+ *   larger (the README's gate, not a clamp).
+ * Reads stats->kbar (and ksig2 if second_order).
+ */
+pisa_status_t pisa_route_topk(const pisa_shape_t *shape, const pisa_params_t *params,
+                              const void *q, const pisa_stats_t *stats, int32_t *idx,
+                              float *wgate, void *stream);
+
+/*
+ * pisa_attn_fwd (Algorithm 1 Phases 1-3, Eqs. 3-5 and 9-10): for each query
+ * row t of block i, with S_i = {|i-j| <= band} U idx[i] and U_i its
+ * complement,
+ *   o_t = (sum_{j in S_i} sum_n e^{s q.k} v  +  sum_{j in U_i} e^{lam} V-hat_j
+ *          + F_t) / (sum_{j in S_i} sum_n e^{s q.k}  +  l_tail_t),
+ *   lam_tj = s q_t.kbar_j + [second_order] wgate_ij,
+ *   l_tail_t = sum_{j in U_i} n_j e^{lam_tj},
+ *   F_t = first_order ? (l_tail_t / T) (s q_t) H : 0.
+ * idx entries must be -1 or distinct block ids outside the band (as
+ * pisa_route_topk writes them). o: [B,H,T,D] in the input dtype; must not
+ * alias q, k, v. bf16 runs compute QK^T and PV with bf16 MFMA (fp32
+ * accumulation, P rounded to bf16); fp32 runs compute in fp32.
+ * Reads stats->kbar_c, vbar_c, vsum (fp32 path), kbar (fp32 path), hsum.
+ */
+pisa_status_t pisa_attn_fwd(const pisa_shape_t *shape, const pisa_params_t *params,
+                            const void *q, const void *k, const void *v,
+                            const pisa_stats_t *stats, const int32_t *idx,
+                            const float *wgate, void *o, void *stream);
+
+/*
+ * pisa_attn_fwd_valu: the same contract as pisa_attn_fwd, computed by a plain
+ * fp32 VALU kernel for either dtype (bf16 inputs are widened exactly; P is
+ * not rounded). It is the fp32 path of pisa_attn_fwd and a GPU reference for
+ * the bf16 MFMA kernel.
+ */
+pisa_status_t pisa_attn_fwd_valu(const pisa_shape_t *shape, const pisa_params_t *params,
+                                 const void *q, const void *k, const void *v,
+                                 const pisa_stats_t *stats, const int32_t *idx,
+                                 const float *wgate, void *o, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PISA_H_ */

@@ -1,0 +1,149 @@
+"""CPU checks of the C ABI: the library loads, exports every function that
+include/pisa.h declares, and rejects invalid arguments before any HIP call
+(so these run on a host without a GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_sparse_taylor_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "pisa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pisa_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_exports_every_declared_function(lib):
+    declared = header_functions()
+    assert set(declared) == set(_lib.EXPORTED), declared
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.pisa_abi_version() == 1
+    for code in range(9):
+        assert lib.pisa_status_str(code)
+    assert lib.pisa_status_str(99) == b"unknown status"
+
+
+def shape(T=1024, D=64, dtype=_lib.PISA_BF16, B=1, H=2, block=64, scale=0.0):
+    return _lib.Shape(B, H, T, D, block, dtype, scale)
+
+
+@pytest.mark.parametrize("T,N", [(1, 1), (64, 1), (65, 2), (32760, 512), (118800, 1857), (524288, 8192)])
+def test_num_blocks(lib, T, N):
+    assert lib.pisa_num_blocks(ctypes.byref(shape(T=T))) == N
+
+
+@pytest.mark.parametrize("bad", [
+    dict(T=0), dict(T=524289), dict(D=96), dict(D=256), dict(block=32), dict(dtype=7),
+    dict(B=0), dict(H=0), dict(B=300, H=300), dict(scale=float("nan")),
+])
+def test_invalid_shapes(lib, bad):
+    s = shape(**bad)
+    assert lib.pisa_num_blocks(ctypes.byref(s)) == -1
+    assert lib.pisa_stats_workspace_bytes(ctypes.byref(s)) == 0
+
+
+def test_workspace_bytes(lib):
+    # one D x D fp32 partial per group of 32 blocks per head
+    s = shape(T=32760, D=128, H=40)
+    assert lib.pisa_stats_workspace_bytes(ctypes.byref(s)) == 40 * 16 * 128 * 128 * 4
+
+
+FAKE = 1 << 20          # 16-byte aligned fake device address: only used where validation fails first
+MIS = FAKE + 4
+
+
+def stats(**kw):
+    d = dict(kbar=FAKE, vsum=FAKE, ksig2=None, hsum=FAKE, kbar_c=FAKE, vbar_c=FAKE)
+    d.update(kw)
+    return _lib.Stats(**d)
+
+
+def call_stats(lib, s=None, p=None, k=FAKE, v=FAKE, st=None, ws=FAKE, wsb=1 << 30):
+    s = s or shape()
+    p = p or _lib.Params(4, 1, 0, 1, 0)
+    st = st or stats()
+    return lib.pisa_block_stats(ctypes.byref(s), ctypes.byref(p), k, v, ctypes.byref(st), ws, wsb, None)
+
+
+def call_route(lib, s=None, p=None, q=FAKE, st=None, idx=FAKE, wg=None):
+    s = s or shape()
+    p = p or _lib.Params(4, 1, 0, 1, 0)
+    st = st or stats()
+    return lib.pisa_route_topk(ctypes.byref(s), ctypes.byref(p), q, ctypes.byref(st), idx, wg, None)
+
+
+def call_attn(lib, name="pisa_attn_fwd", s=None, p=None, q=FAKE, k=FAKE + 64, v=FAKE + 128,
+              st=None, idx=FAKE, wg=None, o=FAKE + 256):
+    s = s or shape()
+    p = p or _lib.Params(4, 1, 0, 1, 0)
+    st = st or stats()
+    fn = getattr(lib, name)
+    return fn(ctypes.byref(s), ctypes.byref(p), q, k, v, ctypes.byref(st), idx, wg, o, None)
+
+
+E = {n: c for c, n in _lib.STATUS_NAMES.items()}
+
+
+def test_stats_validation(lib):
+    assert call_stats(lib, k=None) == E["PISA_ERR_NULL"]
+    assert call_stats(lib, v=MIS) == E["PISA_ERR_ALIGN"]
+    assert call_stats(lib, s=shape(D=32)) == E["PISA_ERR_SHAPE"]
+    assert call_stats(lib, st=stats(hsum=None)) == E["PISA_ERR_NULL"]
+    assert call_stats(lib, st=stats(kbar_c=MIS)) == E["PISA_ERR_ALIGN"]
+    # second order needs ksig2
+    assert call_stats(lib, p=_lib.Params(4, 1, 1, 1, 0)) == E["PISA_ERR_NULL"]
+    assert call_stats(lib, ws=None) == E["PISA_ERR_NULL"]
+    assert call_stats(lib, wsb=16) == E["PISA_ERR_WORKSPACE"]
+    assert call_stats(lib, p=_lib.Params(4, 1, 2, 1, 0)) == E["PISA_ERR_PARAM"]
+
+
+def test_route_validation(lib):
+    N = 16
+    assert call_route(lib, p=_lib.Params(N + 1, 1, 0, 1, 0)) == E["PISA_ERR_PARAM"]
+    assert call_route(lib, p=_lib.Params(-1, 1, 0, 1, 0)) == E["PISA_ERR_PARAM"]
+    assert call_route(lib, p=_lib.Params(4, -1, 0, 1, 0)) == E["PISA_ERR_PARAM"]
+    assert call_route(lib, q=None) == E["PISA_ERR_NULL"]
+    assert call_route(lib, idx=None) == E["PISA_ERR_NULL"]
+    assert call_route(lib, st=stats(kbar=None)) == E["PISA_ERR_NULL"]
+    # second order: ksig2 and wgate required
+    assert call_route(lib, p=_lib.Params(4, 1, 1, 1, 0)) == E["PISA_ERR_NULL"]
+    assert call_route(lib, p=_lib.Params(4, 1, 1, 1, 0), st=stats(ksig2=FAKE)) == E["PISA_ERR_NULL"]
+    assert call_route(lib, s=shape(block=128)) == E["PISA_ERR_PARAM"]
+
+
+@pytest.mark.parametrize("name", ["pisa_attn_fwd", "pisa_attn_fwd_valu"])
+def test_attn_validation(lib, name):
+    assert call_attn(lib, name, o=None) == E["PISA_ERR_NULL"]
+    assert call_attn(lib, name, o=FAKE) == E["PISA_ERR_PARAM"]          # o aliases q
+    assert call_attn(lib, name, k=MIS) == E["PISA_ERR_ALIGN"]
+    assert call_attn(lib, name, idx=None) == E["PISA_ERR_NULL"]
+    assert call_attn(lib, name, p=_lib.Params(4, 1, 1, 1, 0)) == E["PISA_ERR_NULL"]   # wgate
+    assert call_attn(lib, name, p=_lib.Params(4, 1, 0, 1, 8)) == E["PISA_ERR_PARAM"]  # phase mask
+    assert call_attn(lib, name, p=_lib.Params(4, 1, 0, 3, 0)) == E["PISA_ERR_PARAM"]
+    assert call_attn(lib, name, st=stats(vbar_c=None)) == E["PISA_ERR_NULL"]
+    assert call_attn(lib, name, s=shape(dtype=2)) == E["PISA_ERR_DTYPE"]
+    assert call_attn(lib, name, s=shape(T=10 ** 7)) == E["PISA_ERR_SHAPE"]
+
+
+def test_null_structs(lib):
+    st = stats()
+    p = _lib.Params(4, 1, 0, 1, 0)
+    s = shape()
+    assert lib.pisa_block_stats(None, ctypes.byref(p), FAKE, FAKE, ctypes.byref(st), FAKE, 1 << 30, None) == E["PISA_ERR_NULL"]
+    assert lib.pisa_route_topk(ctypes.byref(s), None, FAKE, ctypes.byref(st), FAKE, None, None) == E["PISA_ERR_NULL"]
+    assert lib.pisa_attn_fwd(ctypes.byref(s), ctypes.byref(p), FAKE, FAKE + 64, FAKE + 128, None, FAKE, None, FAKE + 256, None) == E["PISA_ERR_NULL"]

@@ -1,0 +1,155 @@
+"""GPU edge cases and properties of the HIP path (through the C ABI):
+ragged and tiny sequences, both dtypes and head dims, density 1.0 equals
+dense attention, the second-order gate, invariances and determinism."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_taylor_amd as P
+from oracle import pisa_oracle as O
+
+from gpu_common import say
+
+pytestmark = pytest.mark.gpu
+
+
+def make(T, D, dtype, seed, H=2, kscale=1.0):
+    r = np.random.default_rng(seed)
+    x = [r.standard_normal((1, H, T, D)) for _ in range(3)]
+    x[1] *= kscale
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    dev = [torch.from_numpy(a).to(tdt).cuda().contiguous() for a in x]
+    host = [t.double().cpu().numpy() for t in dev]   # exact values the GPU sees
+    return dev, host
+
+
+def run_all(q, k, v, topk, band, second_order=False, first_order=True, fn=P.pisa_attn_fwd):
+    st = P.pisa_block_stats(k, v, second_order=second_order)
+    idx, wg = P.pisa_route_topk(q, st, topk, band=band, second_order=second_order)
+    o = fn(q, k, v, st, idx if topk else None, wg, band=band, second_order=second_order,
+           first_order=first_order)
+    torch.cuda.synchronize()
+    return st, idx, wg, o
+
+
+def tol_check(o, ref, dtype):
+    o = o.double().cpu().numpy()
+    err = np.abs(o - ref).max()
+    if dtype == "f32":
+        assert err / np.abs(ref).max() <= 1e-5, err
+    else:
+        assert err <= 2e-2, err
+    return err
+
+
+CASES = [
+    (1, 64, "f32", 0, 0), (37, 128, "bf16", 0, 1), (64, 64, "bf16", 0, 1), (65, 128, "f32", 0, 0),
+    (200, 128, "bf16", 1, 1), (333, 64, "f32", 2, 1), (700, 128, "bf16", 3, 2), (1000, 64, "bf16", 4, 0),
+]
+
+
+@pytest.mark.parametrize("T,D,dtype,topk,band", CASES)
+@pytest.mark.parametrize("second_order", [False, True])
+def test_small_shapes_match_oracle(T, D, dtype, topk, band, second_order):
+    say(f"[gpu] small T={T} D={D} {dtype} topk={topk} band={band} so={second_order}")
+    (q, k, v), (qh, kh, vh) = make(T, D, dtype, T + D)
+    st, idx, wg, o = run_all(q, k, v, topk, band, second_order)
+    N = -(-T // 64)
+    idx_h = idx.cpu().numpy() if topk else np.zeros((1, 2, N, 0), np.int32)
+    for h in range(2):
+        ref = O.pisa_forward_head(qh[0, h], kh[0, h], vh[0, h], topk=topk, band=band,
+                                  second_order=second_order, routing=idx_h[0, h])
+        tol_check(o[0, h], ref, dtype)
+        # routing equals the oracle's own (random inputs: no near ties expected)
+        ref_idx = O.pisa_forward_head(qh[0, h], kh[0, h], vh[0, h], topk=topk, band=band,
+                                      second_order=second_order, return_parts=True)[1]["idx"]
+        if topk:
+            assert np.array_equal(idx_h[0, h], ref_idx)
+
+
+@pytest.mark.parametrize("dtype,D", [("f32", 64), ("bf16", 128), ("bf16", 64)])
+@pytest.mark.parametrize("second_order", [False, True])
+def test_density_one_is_dense(dtype, D, second_order):
+    T = 640
+    N = 10
+    say(f"[gpu] density 1 {dtype} D={D} so={second_order}")
+    (q, k, v), (qh, kh, vh) = make(T, D, dtype, 5)
+    _, _, _, o = run_all(q, k, v, N, 1, second_order)
+    for h in range(2):
+        ref = O.dense_attention(qh[0, h], kh[0, h], vh[0, h], 1 / math.sqrt(D))
+        tol_check(o[0, h], ref, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_first_order_off_and_phases(dtype):
+    T, D = 512, 128
+    (q, k, v), (qh, kh, vh) = make(T, D, dtype, 9)
+    st, idx, wg, o = run_all(q, k, v, 2, 1, first_order=False)
+    ref = O.pisa_forward_head(qh[0, 0], kh[0, 0], vh[0, 0], topk=2, band=1, first_order="none",
+                              routing=idx.cpu().numpy()[0, 0])
+    tol_check(o[0, 0], ref, dtype)
+    # exact phase only == keep-or-drop block sparse attention
+    o1 = P.pisa_attn_fwd(q, k, v, st, idx, None, band=1, phase_mask=1)
+    ref1 = O.pisa_forward_head(qh[0, 0], kh[0, 0], vh[0, 0], topk=2, band=1, sparse_only=True,
+                               routing=idx.cpu().numpy()[0, 0])
+    tol_check(o1[0, 0], ref1, dtype)
+
+
+def test_second_order_gate_on_gpu():
+    """Keys +-a on one dim, identical query rows in a block: w = 1/2 (s q_d a)^2.
+    With x = s q_d a = 4 every block's w exceeds ln 64 and is gated off, so the
+    output equals the first-order-only PISA result."""
+    B, D, T = 64, 64, 512
+    N = T // B
+    s = 1 / math.sqrt(D)
+    r = np.random.default_rng(3)
+    kb = r.standard_normal((N, D)) * 0.5
+    sign = np.where(np.arange(B) % 2 == 0, 1.0, -1.0)
+    a_dev = 4.0 / (s * 2.0)
+    k = np.concatenate([np.tile(kb[j], (B, 1)) + np.outer(sign, np.eye(D)[1]) * a_dev for j in range(N)])
+    v = r.standard_normal((T, D))
+    qrow = r.standard_normal((N, D))
+    qrow[:, 1] = 2.0
+    q = np.repeat(qrow, B, axis=0)
+    dev = [torch.from_numpy(x[None, None]).float().cuda().contiguous() for x in (q, k, v)]
+    st, idx, wg, o2 = run_all(*dev, 0, 0, second_order=True)
+    assert (wg.cpu().numpy() == 0).all()
+    _, _, _, o1 = run_all(*dev, 0, 0, second_order=False)
+    assert torch.equal(o1, o2)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_invariances(dtype):
+    """o(v + c) = o(v) + c; k -> k + c leaves o unchanged (up to rounding)."""
+    T, D = 640, 128
+    (q, k, v), _ = make(T, D, dtype, 17)
+    _, _, _, o = run_all(q, k, v, 2, 1)
+    c = torch.linspace(-1, 1, D, device="cuda").to(v.dtype)
+    _, _, _, ov = run_all(q, k, (v + c).contiguous(), 2, 1)
+    tol = 1e-5 if dtype == "f32" else 2e-2
+    assert (ov.double() - o.double() - c.double()).abs().max() <= tol
+    _, _, _, ok = run_all(q, (k + 0.5).contiguous(), v, 2, 1)
+    assert (ok.double() - o.double()).abs().max() <= tol
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_deterministic(dtype):
+    (q, k, v), _ = make(1000, 128, dtype, 23)
+    a = run_all(q, k, v, 3, 1, second_order=True)
+    b = run_all(q, k, v, 3, 1, second_order=True)
+    for x, y in zip(a[0].__dict__.values(), b[0].__dict__.values()):
+        if x is not None:
+            assert torch.equal(x, y)
+    assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2]) and torch.equal(a[3], b[3])
+
+
+def test_mfma_matches_valu_reference():
+    """The bf16 MFMA kernel and the fp32 VALU kernel agree on the same routing."""
+    (q, k, v), _ = make(2048, 128, "bf16", 31, H=3)
+    st, idx, wg, o = run_all(q, k, v, 4, 1, second_order=True)
+    o_ref = P.pisa_attn_fwd_valu(q, k, v, st, idx, wg, band=1, second_order=True)
+    torch.cuda.synchronize()
+    assert (o.double() - o_ref.double()).abs().max() <= 2e-2

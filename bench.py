@@ -1,0 +1,210 @@
+"""Benchmark of the PISA forward hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload wan14]
+
+A step is one pass of the whole path over one batch of synthetic input that
+is already resident in HBM: pisa_block_stats -> pisa_route_topk ->
+pisa_attn_fwd. Prints ONE JSON line. ``value`` is the dense-equivalent
+throughput of the whole step, 4 B H T^2 D / t_step (the convention that
+credits a sparse method with the full attention's work); the fused kernel's
+own milliseconds and dense-equivalent TFLOP/s are reported beside it.
+
+``roofline`` refers to the dominant kernel (pisa_attn_fwd, bf16 MFMA): its
+algorithmic flops per launch (4 D per (query row, exact key) and per
+(query row, virtual token) pair, plus 2 D^2 per query row for the global
+first order) over its mean launch time measured with HIP events on the
+stream it is launched on. ``cpu_baseline`` times the fp64 oracle (as it
+stands) on a bounded sample of the same workload on the host cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, datasheet
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, datasheet
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="wan14")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-blocks", type=int, default=256,
+                    help="query blocks of head 0 the oracle evaluates for the CPU baseline")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the operator shards by (batch, head) with no exchange, see the design notes",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import block_sparse_taylor_amd as P
+    from block_sparse_taylor_amd import inputs as I
+
+    w = I.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.time()
+    qa, ka, va = I.make_inputs(w)
+    gen_s = time.time() - t0
+
+    def to_dev(x):
+        if w.dtype == "bf16":
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(x).to(dev)
+
+    q, k, v = to_dev(qa), to_dev(ka), to_dev(va)
+    B, H, T, D = q.shape
+    N = P.num_blocks(T)
+    topk = P.topk_for_density(w.density, N)
+    so = w.second_order
+    st = P.alloc_stats(k, so)
+    ws = P.stats_workspace(k)
+    idx = torch.empty(B, H, N, max(topk, 1), dtype=torch.int32, device=dev)[..., :topk].contiguous()
+    wg = torch.empty(B, H, N, N, dtype=torch.float32, device=dev) if so else None
+    o = torch.empty_like(q)
+    stream = torch.cuda.current_stream(dev)
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def step(record=None):
+        if record:
+            record[0].record(stream)
+        P.pisa_block_stats(k, v, second_order=so, out=st, workspace=ws)
+        if record:
+            record[1].record(stream)
+        P.pisa_route_topk(q, st, topk, band=w.band, second_order=so, idx=idx, wgate=wg)
+        if record:
+            record[2].record(stream)
+        P.pisa_attn_fwd(q, k, v, st, idx if topk else None, wg, band=w.band, second_order=so, out=o)
+        if record:
+            record[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    recs = [[ev() for _ in range(4)] for _ in range(args.steps)]
+    start, end = ev(), ev()
+    torch.cuda.synchronize()
+    start.record(stream)
+    for r in recs:
+        step(r)
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_step = total_ms / args.steps
+    stats_ms = float(np.mean([r[0].elapsed_time(r[1]) for r in recs]))
+    route_ms = float(np.mean([r[1].elapsed_time(r[2]) for r in recs]))
+    attn_ms = float(np.mean([r[2].elapsed_time(r[3]) for r in recs]))
+
+    # ---- algorithmic work of the fused kernel (from the routing table actually used)
+    idx_h = idx.cpu().numpy().reshape(B * H, N, topk)
+    nrow = np.array([min(64, T - 64 * j) for j in range(N)], dtype=np.int64)
+    exact_pairs = 0
+    virt_pairs = 0
+    for bh in range(B * H):
+        for i in range(N):
+            sel = set(range(max(0, i - w.band), min(N, i + w.band + 1)))
+            sel.update(int(j) for j in idx_h[bh, i] if j >= 0)
+            keys = int(nrow[list(sel)].sum())
+            exact_pairs += int(nrow[i]) * keys
+            virt_pairs += int(nrow[i]) * (N - len(sel))
+    attn_flops = 4 * D * (exact_pairs + virt_pairs) + 2 * D * D * B * H * T
+    dense_flops = 4.0 * B * H * T * T * D
+    attn_tflops = attn_flops / (attn_ms * 1e-3) / 1e12
+
+    e = 2 if w.dtype == "bf16" else 4
+    G = -(-N // 32)
+    stats_bytes = (2 * B * H * T * D * e                     # read K, V
+                   + B * H * N * D * (8 + 4 + 2 * e + (8 if so else 0))   # kbar, vsum, kbar_c, vbar_c, ksig2
+                   + B * H * D * D * 4                       # hsum
+                   + 2 * B * H * G * D * D * 4)              # partial H write + read
+    route_bytes = (B * H * T * D * e + B * H * N * D * 8 * (2 if so else 1)
+                   + B * H * N * topk * 4 + (B * H * N * N * 4 if so else 0))
+
+    out = {
+        "metric": "pisa_attn_fwd ms & dense-equiv TFLOP/s, Wan2.1-14B shape, density 0.125",
+        "value": round(dense_flops / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s dense-equivalent (4 B H T^2 D per full step: stats + route + fused forward)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded spatially correlated q/k in 3D Morton order, v ~ N(0,1))",
+        "config": {"workload": f"{w.name}: batch {B}, heads {H}, T {T}, head_dim {D}, {w.dtype}, "
+                               f"block 64, density {w.density} (topk {topk}) + band {w.band}"
+                               + (", second order" if so else ""),
+                   "topk": topk, "band": w.band, "second_order": so},
+        "pisa_attn_fwd": {"ms": round(attn_ms, 4),
+                          "dense_equiv_tflops": round(dense_flops / (attn_ms * 1e-3) / 1e12, 2),
+                          "algorithmic_tflop": round(attn_flops / 1e12, 4)},
+        "pisa_block_stats": {"ms": round(stats_ms, 4), "algorithmic_bytes": stats_bytes,
+                             "gbs": round(stats_bytes / (stats_ms * 1e-3) / 1e9, 1),
+                             "frac_hbm": round(stats_bytes / (stats_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+        "pisa_route_topk": {"ms": round(route_ms, 4), "algorithmic_bytes": route_bytes,
+                            "gbs": round(route_bytes / (route_ms * 1e-3) / 1e9, 1),
+                            "frac_hbm": round(route_bytes / (route_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "kernel": "attn_mfma_kernel (pisa_attn_fwd)"},
+        "input_generation_s": round(gen_s, 1),
+    }
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, qa, ka, va, args.cpu_sample_blocks, topk)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(w, qa, ka, va, nblocks, topk):
+    """The fp64 oracle, timed on head 0: its block statistics, routing and the
+    forward of the first `nblocks` query blocks; scaled to dense-equivalent
+    TFLOP/s of the rows it produced."""
+    from block_sparse_taylor_amd import inputs as I
+    from oracle import pisa_oracle as O
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    q, k, v = (I.as_f64(x[0, 0], w.dtype) for x in (qa, ka, va))
+    T, D = q.shape
+    N = -(-T // 64)
+    nblocks = min(nblocks, N)
+    t0 = time.time()
+    o = O.pisa_forward_head(q, k, v, topk=topk, band=w.band, second_order=w.second_order,
+                            query_blocks=range(nblocks))
+    dt = time.time() - t0
+    rows = min(T, nblocks * 64)
+    assert np.isfinite(o[:rows]).all()
+    dense_flops = 4.0 * rows * T * D
+    return {"value": round(dense_flops / dt / 1e12, 5), "unit": "TFLOP/s dense-equivalent",
+            "cores": threads, "kind": "oracle",
+            "sample": f"head 0 of {w.name}: block statistics + routing of the head, forward of "
+                      f"query blocks 0..{nblocks - 1} ({rows} of {T} rows); {dt:.1f} s",
+            "seconds": round(dt, 2)}
+
+
+if __name__ == "__main__":
+    main()

@@ -155,8 +155,8 @@ pisa_status_t pisa_route_topk(const pisa_shape_t *shape, const pisa_params_t *pa
  *   lam_tj = s q_t.kbar_j + [second_order] wgate_ij,
  *   l_tail_t = sum_{j in U_i} n_j e^{lam_tj},
  *   F_t = first_order ? (l_tail_t / T) (s q_t) H : 0.
- * idx entries must be -1 or distinct block ids outside the band (as
- * pisa_route_topk writes them). o: [B,H,T,D] in the input dtype; must not
+ * idx rows hold distinct block ids outside the band, then -1 padding (as
+ * pisa_route_topk writes them: valid ids first, -1 only after them). o: [B,H,T,D] in the input dtype; must not
  * alias q, k, v. bf16 runs compute QK^T and PV with bf16 MFMA (fp32
  * accumulation, P rounded to bf16); fp32 runs compute in fp32.
  * Reads stats->kbar_c, vbar_c, vsum (fp32 path), kbar (fp32 path), hsum.

@@ -39,8 +39,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="wan14")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-blocks", type=int, default=256,
-                    help="query blocks of head 0 the oracle evaluates for the CPU baseline")
+    ap.add_argument("--cpu-heads", type=int, default=8,
+                    help="heads the oracle evaluates for the CPU baseline")
     return ap.parse_args()
 
 
@@ -86,7 +86,7 @@ def main():
     def step(record=None):
         if record:
             record[0].record(stream)
-        P.pisa_block_stats(k, v, second_order=so, out=st, workspace=ws)
+        P.pisa_block_stats(q, k, v, second_order=so, out=st, workspace=ws)
         if record:
             record[1].record(stream)
         P.pisa_route_topk(q, st, topk, band=w.band, second_order=so, idx=idx, wgate=wg)
@@ -132,12 +132,15 @@ def main():
 
     e = 2 if w.dtype == "bf16" else 4
     G = -(-N // 32)
-    stats_bytes = (2 * B * H * T * D * e                     # read K, V
-                   + B * H * N * D * (8 + 4 + 2 * e + (8 if so else 0))   # kbar, vsum, kbar_c, vbar_c, ksig2
+    BHND = B * H * N * D
+    stats_bytes = (3 * B * H * T * D * e                     # read Q, K, V
+                   + BHND * (8 + 8 + 4 + 2 * e)              # qbar, kbar, vsum, kbar_c, vbar_c
+                   + (BHND * 16 if so else 0)                # q2bar, ksig2
                    + B * H * D * D * 4                       # hsum
                    + 2 * B * H * G * D * D * 4)              # partial H write + read
-    route_bytes = (B * H * T * D * e + B * H * N * D * 8 * (2 if so else 1)
-                   + B * H * N * topk * 4 + (B * H * N * N * 4 if so else 0))
+    route_bytes = (BHND * 16 * (2 if so else 1)              # qbar, kbar (+ q2bar, ksig2)
+                   + B * H * N * topk * 4                    # idx
+                   + (B * H * N * N * 4 if so else 0))       # gated w table
 
     out = {
         "metric": "pisa_attn_fwd ms & dense-equiv TFLOP/s, Wan2.1-14B shape, density 0.125",
@@ -172,14 +175,14 @@ def main():
     }
 
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, qa, ka, va, args.cpu_sample_blocks, topk)
+        out["cpu_baseline"] = cpu_baseline(w, qa, ka, va, args.cpu_heads, topk)
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(w, qa, ka, va, nblocks, topk):
-    """The fp64 oracle, timed on head 0: its block statistics, routing and the
-    forward of the first `nblocks` query blocks; scaled to dense-equivalent
-    TFLOP/s of the rows it produced."""
+def cpu_baseline(w, qa, ka, va, nheads, topk):
+    """The fp64 oracle (as it stands), timed on the first `nheads` heads of the
+    same inputs: block statistics, routing and the forward of every query
+    block; reported as dense-equivalent TFLOP/s of the rows it produced."""
     from block_sparse_taylor_amd import inputs as I
     from oracle import pisa_oracle as O
 
@@ -188,21 +191,20 @@ def cpu_baseline(w, qa, ka, va, nblocks, topk):
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
         threads = len(os.sched_getaffinity(0))
-    q, k, v = (I.as_f64(x[0, 0], w.dtype) for x in (qa, ka, va))
-    T, D = q.shape
-    N = -(-T // 64)
-    nblocks = min(nblocks, N)
-    t0 = time.time()
-    o = O.pisa_forward_head(q, k, v, topk=topk, band=w.band, second_order=w.second_order,
-                            query_blocks=range(nblocks))
-    dt = time.time() - t0
-    rows = min(T, nblocks * 64)
-    assert np.isfinite(o[:rows]).all()
-    dense_flops = 4.0 * rows * T * D
+    nheads = min(nheads, qa.shape[1])
+    T, D = qa.shape[2], qa.shape[3]
+    dt = 0.0
+    for h in range(nheads):
+        q, k, v = (I.as_f64(x[0, h], w.dtype) for x in (qa, ka, va))
+        t0 = time.time()
+        o = O.pisa_forward_head(q, k, v, topk=topk, band=w.band, second_order=w.second_order)
+        dt += time.time() - t0
+        assert np.isfinite(o).all()
+    dense_flops = 4.0 * nheads * T * T * D
     return {"value": round(dense_flops / dt / 1e12, 5), "unit": "TFLOP/s dense-equivalent",
             "cores": threads, "kind": "oracle",
-            "sample": f"head 0 of {w.name}: block statistics + routing of the head, forward of "
-                      f"query blocks 0..{nblocks - 1} ({rows} of {T} rows); {dt:.1f} s",
+            "sample": f"heads 0..{nheads - 1} of {w.name} (of {qa.shape[1]}), every query block: "
+                      f"statistics, routing and forward in float64 numpy; {dt:.1f} s",
             "seconds": round(dt, 2)}
 
 

@@ -8,7 +8,7 @@ eager fallback: if libpisa.so is missing, the calls raise.
 The three calls follow the PISA paper's Algorithm 1 (prepare phase steps 1-2,
 fused kernel Phases 1-3):
 
-    stats     = pisa_block_stats(k, v, second_order=...)
+    stats     = pisa_block_stats(q, k, v, second_order=...)
     idx, wg   = pisa_route_topk(q, stats, topk=..., band=1, second_order=...)
     o         = pisa_attn_fwd(q, k, v, stats, idx, wg, ...)
 
@@ -71,6 +71,8 @@ def topk_for_density(density: float, n_blocks: int) -> int:
 
 @dataclass
 class PisaStats:
+    qbar: torch.Tensor      # fp64 [B,H,N,D]
+    q2bar: torch.Tensor | None
     kbar: torch.Tensor      # fp64 [B,H,N,D]
     vsum: torch.Tensor      # fp32 [B,H,N,D]
     ksig2: torch.Tensor | None
@@ -79,8 +81,8 @@ class PisaStats:
     vbar_c: torch.Tensor
 
     def as_c(self) -> _lib.Stats:
-        return _lib.Stats(_ptr(self.kbar), _ptr(self.vsum), _ptr(self.ksig2), _ptr(self.hsum),
-                          _ptr(self.kbar_c), _ptr(self.vbar_c))
+        return _lib.Stats(_ptr(self.qbar), _ptr(self.q2bar), _ptr(self.kbar), _ptr(self.vsum),
+                          _ptr(self.ksig2), _ptr(self.hsum), _ptr(self.kbar_c), _ptr(self.vbar_c))
 
 
 def _contig(*ts):
@@ -94,6 +96,8 @@ def alloc_stats(k: torch.Tensor, second_order: bool) -> PisaStats:
     N = num_blocks(T)
     dev = k.device
     return PisaStats(
+        qbar=torch.empty(B, H, N, D, dtype=torch.float64, device=dev),
+        q2bar=torch.empty(B, H, N, D, dtype=torch.float64, device=dev) if second_order else None,
         kbar=torch.empty(B, H, N, D, dtype=torch.float64, device=dev),
         vsum=torch.empty(B, H, N, D, dtype=torch.float32, device=dev),
         ksig2=torch.empty(B, H, N, D, dtype=torch.float64, device=dev) if second_order else None,
@@ -110,37 +114,36 @@ def stats_workspace(k: torch.Tensor, scale=None) -> torch.Tensor:
     return torch.empty(max(16, n), dtype=torch.uint8, device=k.device)
 
 
-def pisa_block_stats(k, v, second_order=False, scale=None, out: PisaStats | None = None,
+def pisa_block_stats(q, k, v, second_order=False, scale=None, out: PisaStats | None = None,
                      workspace: torch.Tensor | None = None) -> PisaStats:
     lib = library()
-    _contig(k, v)
+    _contig(q, k, v)
     sh = _shape(k, scale)
     out = out or alloc_stats(k, second_order)
     ws = workspace if workspace is not None else stats_workspace(k, scale)
     prm = _lib.Params(0, 0, int(second_order), 1, 0)
     cs = out.as_c()
     _lib.check("pisa_block_stats", lib.pisa_block_stats(
-        ctypes.byref(sh), ctypes.byref(prm), _ptr(k), _ptr(v), ctypes.byref(cs), _ptr(ws),
+        ctypes.byref(sh), ctypes.byref(prm), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(cs), _ptr(ws),
         ws.numel(), _stream(k.device)))
     return out
 
 
 def pisa_route_topk(q, stats: PisaStats, topk: int, band: int = 1, second_order=False, scale=None,
                     idx: torch.Tensor | None = None, wgate: torch.Tensor | None = None):
+    """q is used for its shape and device only; routing reads the pooled statistics."""
     lib = library()
-    _contig(q)
     sh = _shape(q, scale)
     B, H, T, D = q.shape
     N = num_blocks(T)
     if idx is None:
-        idx = torch.empty(B, H, N, max(topk, 1), dtype=torch.int32, device=q.device)[..., :topk]
-        idx = idx.contiguous() if topk else idx
+        idx = torch.empty(B, H, N, topk, dtype=torch.int32, device=q.device)
     if second_order and wgate is None:
         wgate = torch.empty(B, H, N, N, dtype=torch.float32, device=q.device)
     prm = _lib.Params(int(topk), int(band), int(second_order), 1, 0)
     cs = stats.as_c()
     _lib.check("pisa_route_topk", lib.pisa_route_topk(
-        ctypes.byref(sh), ctypes.byref(prm), _ptr(q), ctypes.byref(cs),
+        ctypes.byref(sh), ctypes.byref(prm), ctypes.byref(cs),
         _ptr(idx) if topk else None, _ptr(wgate) if second_order else None, _stream(q.device)))
     return idx, (wgate if second_order else None)
 
@@ -189,7 +192,7 @@ def piecewise_sparse_attention(q, k, v, density=0.125, variant="pisa", band=1, s
     N = num_blocks(q.shape[2])
     topk = topk_for_density(density, N)
     topk = min(topk, N)
-    st = pisa_block_stats(k, v, second_order=so, scale=scale)
+    st = pisa_block_stats(q, k, v, second_order=so, scale=scale)
     idx, wg = pisa_route_topk(q, st, topk, band=band, second_order=so, scale=scale)
     return pisa_attn_fwd(q, k, v, st, idx if topk else None, wg, band=band, second_order=so,
                          scale=scale)

@@ -34,8 +34,9 @@ class Params(ctypes.Structure):
 
 
 class Stats(ctypes.Structure):
-    _fields_ = [("kbar", ctypes.c_void_p), ("vsum", ctypes.c_void_p), ("ksig2", ctypes.c_void_p),
-                ("hsum", ctypes.c_void_p), ("kbar_c", ctypes.c_void_p), ("vbar_c", ctypes.c_void_p)]
+    _fields_ = [("qbar", ctypes.c_void_p), ("q2bar", ctypes.c_void_p), ("kbar", ctypes.c_void_p),
+                ("vsum", ctypes.c_void_p), ("ksig2", ctypes.c_void_p), ("hsum", ctypes.c_void_p),
+                ("kbar_c", ctypes.c_void_p), ("vbar_c", ctypes.c_void_p)]
 
 
 class PisaError(RuntimeError):
@@ -66,9 +67,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pisa_stats_workspace_bytes.restype = ctypes.c_size_t
     lib.pisa_stats_workspace_bytes.argtypes = [P(Shape)]
     lib.pisa_block_stats.restype = ctypes.c_int
-    lib.pisa_block_stats.argtypes = [P(Shape), P(Params), vp, vp, P(Stats), vp, ctypes.c_size_t, vp]
+    lib.pisa_block_stats.argtypes = [P(Shape), P(Params), vp, vp, vp, P(Stats), vp, ctypes.c_size_t, vp]
     lib.pisa_route_topk.restype = ctypes.c_int
-    lib.pisa_route_topk.argtypes = [P(Shape), P(Params), vp, P(Stats), vp, vp, vp]
+    lib.pisa_route_topk.argtypes = [P(Shape), P(Params), P(Stats), vp, vp, vp]
     for name in ("pisa_attn_fwd", "pisa_attn_fwd_valu"):
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int

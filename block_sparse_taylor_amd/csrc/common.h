@@ -42,16 +42,18 @@ struct Geom {
     int T;            // tokens
     int D;            // head dim
     int N;            // blocks
-    float scale;      // softmax scale
+    float scale;      // softmax scale (fp32)
+    double scale64;   // the same scale in fp64 (routing decisions)
 };
 
 // Kernel launchers (return hipSuccess or the launch error).
-hipError_t launch_block_stats(const Geom& g, int dtype, int second_order, const void* k, const void* v,
-                              const pisa_stats_t* out, void* workspace, hipStream_t stream);
+hipError_t launch_block_stats(const Geom& g, int dtype, int second_order, const void* q, const void* k,
+                              const void* v, const pisa_stats_t* out, void* workspace,
+                              hipStream_t stream);
 size_t stats_workspace_bytes(const Geom& g);
 
-hipError_t launch_route_topk(const Geom& g, int dtype, const pisa_params_t* p, const void* q,
-                             const pisa_stats_t* st, int32_t* idx, float* wgate, hipStream_t stream);
+hipError_t launch_route_topk(const Geom& g, const pisa_params_t* p, const pisa_stats_t* st,
+                             int32_t* idx, float* wgate, hipStream_t stream);
 
 hipError_t launch_attn_fwd_valu(const Geom& g, int dtype, const pisa_params_t* p, const void* q,
                                 const void* k, const void* v, const pisa_stats_t* st,

@@ -10,7 +10,7 @@ using namespace pisa;
 
 namespace {
 
-constexpr int64_t kMaxSeq = 524288;   // N <= 8192 keeps a routing row in LDS
+constexpr int64_t kMaxSeq = 524288;   // N <= 8192 blocks
 constexpr int64_t kMaxBH = 65535;     // grid y dimension
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -28,7 +28,8 @@ pisa_status_t check_shape(const pisa_shape_t* s, Geom* g) {
         g->T = (int)s->seq_len;
         g->D = (int)s->head_dim;
         g->N = (int)((s->seq_len + kBlock - 1) / kBlock);
-        g->scale = s->scale > 0.f ? s->scale : 1.0f / sqrtf((float)s->head_dim);
+        g->scale64 = s->scale > 0.f ? (double)s->scale : 1.0 / sqrt((double)s->head_dim);
+        g->scale = (float)g->scale64;
     }
     return PISA_OK;
 }
@@ -119,36 +120,39 @@ size_t pisa_stats_workspace_bytes(const pisa_shape_t* shape) {
     return stats_workspace_bytes(g);
 }
 
-pisa_status_t pisa_block_stats(const pisa_shape_t* shape, const pisa_params_t* params, const void* k,
-                               const void* v, const pisa_stats_t* out, void* workspace,
+pisa_status_t pisa_block_stats(const pisa_shape_t* shape, const pisa_params_t* params, const void* q,
+                               const void* k, const void* v, const pisa_stats_t* out, void* workspace,
                                size_t workspace_bytes, void* stream) {
     Geom g;
     PISA_TRY(check_shape(shape, &g));
     PISA_TRY(check_params(params, g));
+    PISA_TRY(check_ptr(q));
     PISA_TRY(check_ptr(k));
     PISA_TRY(check_ptr(v));
     PISA_TRY(check_stats(out, params->second_order, true));
+    PISA_TRY(check_ptr(out->qbar));
+    if (params->second_order) PISA_TRY(check_ptr(out->q2bar));
     PISA_TRY(check_ptr(workspace));
     if (workspace_bytes < stats_workspace_bytes(g)) return PISA_ERR_WORKSPACE;
-    return from_hip(launch_block_stats(g, shape->dtype, params->second_order, k, v, out, workspace,
-                                       static_cast<hipStream_t>(stream)));
+    return from_hip(launch_block_stats(g, shape->dtype, params->second_order, q, k, v, out,
+                                       workspace, static_cast<hipStream_t>(stream)));
 }
 
-pisa_status_t pisa_route_topk(const pisa_shape_t* shape, const pisa_params_t* params, const void* q,
+pisa_status_t pisa_route_topk(const pisa_shape_t* shape, const pisa_params_t* params,
                               const pisa_stats_t* stats, int32_t* idx, float* wgate, void* stream) {
     Geom g;
     PISA_TRY(check_shape(shape, &g));
     PISA_TRY(check_params(params, g));
-    PISA_TRY(check_ptr(q));
     if (!stats) return PISA_ERR_NULL;
+    PISA_TRY(check_ptr(stats->qbar));
     PISA_TRY(check_ptr(stats->kbar));
     if (params->second_order) {
+        PISA_TRY(check_ptr(stats->q2bar));
         PISA_TRY(check_ptr(stats->ksig2));
         PISA_TRY(check_ptr(wgate));
     }
     if (params->topk > 0) PISA_TRY(check_ptr(idx));
-    return from_hip(launch_route_topk(g, shape->dtype, params, q, stats, idx, wgate,
-                                      static_cast<hipStream_t>(stream)));
+    return from_hip(launch_route_topk(g, params, stats, idx, wgate, static_cast<hipStream_t>(stream)));
 }
 
 pisa_status_t pisa_attn_fwd(const pisa_shape_t* shape, const pisa_params_t* params, const void* q,

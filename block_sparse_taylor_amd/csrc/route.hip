@@ -1,17 +1,26 @@
-// Pooled-score routing (PISA, Algorithm 1 step 2 with the pooled block score
-// of Eq. 11 minus its covariance term; Piecewise-Taylor-Attention README:
-// +-band forced exact, clamped ranking spread min(w, ln B), set-identical
-// top-k).
+// Routing: top-k KV blocks per query block from pooled block scores (PISA,
+// Algorithm 1 step 2, the block score of Eq. 11 without its covariance term;
+// Piecewise-Taylor-Attention README: +-band forced exact, clamped ranking
+// spread min(w, ln B), set-identical top-k).
 //
-// One workgroup per (batch*head, tile of query blocks). For each query block:
-//   1. pool its rows: qbar = mean(q), q2bar = mean((s q)^2)        (fp64, exact sums)
-//   2. score every KV block j: r_j = s qbar.kbar_j [+ min(w_j, ln B)], with
-//      w_j = 1/2 q2bar.ksig2_j; the band |i-j| <= band is excluded   (fp64)
-//   3. radix-select the topk-th largest 64-bit order-preserving key, then
-//      keep every key above it plus the lowest-index keys equal to it
-//   4. write the chosen ids ascending (block prefix sum), then -1 padding.
-// The score row lives only in LDS; nothing N x N is written except the
-// gated second-order table the fused kernel consumes.
+//   r_ij = s qbar_i . kbar_j  [+ min(w_ij, ln B)],   w_ij = 1/2 q2bar_i . ksig2_j
+//   Top_i = the topk largest r_ij over |i - j| > band, ties to the lower j.
+//
+// The decision must equal a float64 evaluation, so the kernel scores in fp32
+// and settles every close call in fp64:
+//   1. One workgroup per (batch*head, 16 query blocks). fp32 MFMA
+//      (16x16x4) computes the 16 x N score rows into LDS; the inputs are the
+//      fp64 pooled statistics rounded to fp32. |r~ - r| <= eps_i with a
+//      rigorous bound eps_i = c (D + 4) u (s ||qbar_i|| max_j ||kbar_j|| [+ ln B]).
+//   2. Per row (one wave), a radix select over order-preserving 32-bit keys
+//      finds tau~, the topk-th largest r~. Blocks with r~ > tau~ + 2 eps are
+//      in Top_i; blocks with r~ < tau~ - 2 eps are out; the few in between
+//      are ranked exactly: their r_ij is recomputed in fp64 and a second radix
+//      select on 64-bit keys (ties: lower j) picks the remaining members.
+//   3. Ids are written ascending, -1 padded.
+// The gate of the second-order term is decided the same way (fp32, with an
+// fp64 recomputation within the error bound of ln B) and the gated w table is
+// written for the fused kernel. No N x N score matrix leaves the chip.
 #include <math.h>
 
 #include "common.h"
@@ -19,15 +28,283 @@
 namespace pisa {
 namespace {
 
-constexpr int kMaxN = 8192;   // LDS-resident key row (64 KiB)
+constexpr int kQB = 16;               // query blocks per workgroup
+constexpr int kFastMaxN = 1920;       // 16 score rows of N fp32 fit in LDS
+constexpr double kU = 5.9604644775390625e-08;   // 2^-24
 
-__device__ __forceinline__ uint64_t order_key(double r) {
-    r = r + 0.0;  // -0 -> +0
-    uint64_t u = __double_as_longlong(r);
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f4_t;
+
+__device__ __forceinline__ uint32_t key32(float f) {
+    f = f + 0.0f;
+    const uint32_t u = __float_as_uint(f);
+    return (u >> 31) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float unkey32(uint32_t k) {
+    return __uint_as_float((k >> 31) ? (k & 0x7FFFFFFFu) : ~k);
+}
+__device__ __forceinline__ uint64_t key64(double r) {
+    r = r + 0.0;
+    const uint64_t u = __double_as_longlong(r);
     return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
 }
 
-// Block-wide exclusive prefix sum over kThreads ints; returns the total.
+// Wave-wide inclusive prefix sum (lanes ascending).
+__device__ __forceinline__ int wave_scan(int x) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+    }
+    return x;
+}
+__device__ __forceinline__ int wave_sum(int x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+    return x;
+}
+
+// Radix select over one wave: the need-th largest key among those for which
+// `take(j)` holds, j in [0, n); keys from key(j). Returns the key and, through
+// need_eq, how many keys equal to it belong to the selection. hist: 256
+// unsigned per wave in LDS.
+template <typename Key, int BITS, typename KeyFn, typename TakeFn>
+__device__ __forceinline__ Key wave_radix_select(int n, int need, KeyFn key, TakeFn take,
+                                                 unsigned* hist, int* need_eq) {
+    const int lane = threadIdx.x & 63;
+    Key prefix = 0;
+    for (int pass = 0; pass < BITS / 8; ++pass) {
+        const int shift = BITS - 8 - 8 * pass;
+        const Key hmask = pass == 0 ? (Key)0 : (Key)(~(Key)0 << (shift + 8));
+#pragma unroll
+        for (int b = 0; b < 4; ++b) hist[lane * 4 + b] = 0u;
+        __builtin_amdgcn_wave_barrier();
+        for (int j = lane; j < n; j += 64) {
+            if (!take(j)) continue;
+            const Key kk = key(j);
+            if ((kk & hmask) == prefix) atomicAdd(&hist[(unsigned)((kk >> shift) & 255)], 1u);
+        }
+        __builtin_amdgcn_wave_barrier();
+        // lane L owns bins 255-4L .. 252-4L (top bins first)
+        int c[4], s = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            c[b] = (int)hist[255 - 4 * lane - b];
+            s += c[b];
+        }
+        const int incl = wave_scan(s);
+        const int excl = incl - s;
+        const unsigned long long hit = __ballot(incl >= need);
+        const int L = __ffsll((long long)hit) - 1;       // first lane reaching need
+        int digit = 0, rest = need;
+        if (lane == L) {
+            rest = need - excl;
+            int b = 0;
+            for (; b < 3; ++b) {
+                if (c[b] >= rest) break;
+                rest -= c[b];
+            }
+            digit = 255 - 4 * lane - b;
+        }
+        digit = __shfl(digit, L);
+        need = __shfl(rest, L);
+        prefix |= (Key)digit << shift;
+        __builtin_amdgcn_wave_barrier();
+    }
+    *need_eq = need;
+    return prefix;
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void route_fast_kernel(
+    const double* __restrict__ qbar, const double* __restrict__ q2bar, const double* __restrict__ kbar,
+    const double* __restrict__ ksig2, int N, double s64, int topk, int band, int second_order,
+    int32_t* __restrict__ idx, float* __restrict__ wgate) {
+    constexpr int KS = D / 4;       // 16x16x4 k-steps; MFMA k-slot (ks, l/16) <-> dim (D/4)(l/16) + ks
+    __shared__ double qb_s[kQB * D];
+    __shared__ double q2_s[kQB * D];
+    __shared__ float score_s[kQB * kFastMaxN];
+    __shared__ unsigned hist_s[4 * 256];
+    __shared__ float kmax_s[4];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t bh = blockIdx.y;
+    const int i0 = blockIdx.x * kQB;
+    const int nq = min(kQB, N - i0);
+    const double lnB = log((double)kBlock);
+    const float lnBf = (float)lnB;
+
+    // pooled statistics of the tile's query blocks (zeros past N)
+    for (int e = tid; e < kQB * D; e += kThreads) {
+        const int r = e / D;
+        const int64_t o = (bh * N + i0 + r) * (int64_t)D + e % D;
+        qb_s[e] = r < nq ? qbar[o] : 0.0;
+        q2_s[e] = (second_order && r < nq) ? q2bar[o] : 0.0;
+    }
+    __syncthreads();
+
+    // ---- scores: S[r][j] = s qbar_r . kbar_j (+ min(w, ln B)) via fp32 MFMA
+    const int m16 = lane & 15, g4 = lane >> 4;
+    float a[KS], a2[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        a[ks] = (float)qb_s[m16 * D + (D / 4) * g4 + ks];
+        a2[ks] = second_order ? (float)q2_s[m16 * D + (D / 4) * g4 + ks] : 0.f;
+    }
+    const double* kb = kbar + bh * (int64_t)N * D;
+    const double* sg = second_order ? ksig2 + bh * (int64_t)N * D : nullptr;
+    float kmax2 = 0.f;
+    const int NC = (N + 15) / 16;
+    for (int c = wave; c < NC; c += 4) {
+        const int col = c * 16 + m16;
+        const bool ok = col < N;
+        const double* kr = kb + (int64_t)(ok ? col : N - 1) * D + (D / 4) * g4;
+        f4_t acc = {0.f, 0.f, 0.f, 0.f}, accw = {0.f, 0.f, 0.f, 0.f};
+        float n2 = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const float b = ok ? (float)kr[ks] : 0.f;
+            n2 = fmaf(b, b, n2);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[ks], b, acc, 0, 0, 0);
+        }
+        if (second_order) {
+            const double* sr = sg + (int64_t)(ok ? col : N - 1) * D + (D / 4) * g4;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const float b = ok ? (float)sr[ks] : 0.f;
+                accw = __builtin_amdgcn_mfma_f32_16x16x4f32(a2[ks], b, accw, 0, 0, 0);
+            }
+        }
+        n2 += __shfl_xor(n2, 16);
+        n2 += __shfl_xor(n2, 32);
+        kmax2 = fmaxf(kmax2, n2);
+        // C layout: lane holds column m16, rows 4 g4 + e
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g4 + e;
+            float sc = (float)s64 * acc[e];
+            if (second_order && ok && r < nq) {
+                const float w = 0.5f * accw[e];
+                const float ew = 2.0f * (float)((D + 4) * kU) * w + 1e-30f;
+                float wg;
+                if (fabsf(w - lnBf) > ew) {
+                    wg = w > lnBf ? 0.f : w;
+                } else {   // too close to call in fp32: decide in fp64
+                    double w64 = 0.0;
+                    for (int d = 0; d < D; ++d) w64 = fma(q2_s[r * D + d], sg[(int64_t)col * D + d], w64);
+                    w64 *= 0.5;
+                    wg = w64 > lnB ? 0.f : (float)w64;
+                }
+                wgate[(bh * N + i0 + r) * (int64_t)N + col] = wg;
+                sc += fminf(w, lnBf);
+            }
+            if (ok) score_s[r * kFastMaxN + col] = sc;
+        }
+    }
+    kmax2 = fmaxf(kmax2, __shfl_xor(kmax2, 1));
+    kmax2 = fmaxf(kmax2, __shfl_xor(kmax2, 2));
+    kmax2 = fmaxf(kmax2, __shfl_xor(kmax2, 4));
+    kmax2 = fmaxf(kmax2, __shfl_xor(kmax2, 8));
+    if (lane == 0) kmax_s[wave] = kmax2;
+    __syncthreads();
+    const double kmax = sqrt((double)fmaxf(fmaxf(kmax_s[0], kmax_s[1]), fmaxf(kmax_s[2], kmax_s[3]))) *
+                        (1.0 + 1e-6);
+
+    // ---- selection: wave w handles rows w, w+4, w+8, w+12
+    unsigned* hist = hist_s + wave * 256;
+    for (int r = wave; r < nq; r += 4) {
+        const int i = i0 + r;
+        int32_t* out = idx + (bh * N + i) * (int64_t)topk;
+        const int blo = max(0, i - band), bhi = min(N - 1, i + band);
+        const int ncand = N - (bhi - blo + 1);
+        const int k = min(topk, ncand);
+        const float* sr = score_s + r * kFastMaxN;
+        auto is_cand = [&](int j) { return j < blo || j > bhi; };
+        int written = 0;
+        if (k > 0) {
+            double qn = 0.0;
+            for (int d = lane; d < D; d += 64) qn += qb_s[r * D + d] * qb_s[r * D + d];
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) qn += __shfl_xor(qn, off);
+            const double bound = s64 * sqrt(qn) * kmax + (second_order ? lnB : 0.0);
+            const float eps = (float)(4.0 * (D + 8) * kU * bound) + 1e-30f;
+            int need_eq;
+            const uint32_t tk = wave_radix_select<uint32_t, 32>(
+                N, k, [&](int j) { return key32(sr[j]); }, is_cand, hist, &need_eq);
+            const float tau = unkey32(tk);
+            const float hi_thr = tau + 2.f * eps, lo_thr = tau - 2.f * eps;
+            int cg = 0, ca = 0;
+            for (int j = lane; j < N; j += 64) {
+                if (!is_cand(j)) continue;
+                const float x = sr[j];
+                cg += x > hi_thr;
+                ca += (x >= lo_thr && x <= hi_thr);
+            }
+            cg = wave_sum(cg);
+            ca = wave_sum(ca);
+            const int need = k - cg;      // members still to choose among the ambiguous ones
+            auto exact = [&](int j) {     // fp64 score of block j
+                const double* kr = kb + (int64_t)j * D;
+                double dot = 0.0;
+                for (int d = 0; d < D; ++d) dot = fma(qb_s[r * D + d], kr[d], dot);
+                double rr = s64 * dot;
+                if (second_order) {
+                    const double* sq = sg + (int64_t)j * D;
+                    double w = 0.0;
+                    for (int d = 0; d < D; ++d) w = fma(q2_s[r * D + d], sq[d], w);
+                    rr += fmin(0.5 * w, lnB);
+                }
+                return rr;
+            };
+            auto ambiguous = [&](int j) {
+                const float x = sr[j];
+                return is_cand(j) && x >= lo_thr && x <= hi_thr;
+            };
+            uint64_t t64 = 0;
+            int eq_need = 0;
+            const bool all_amb = need >= ca;   // every ambiguous block is in
+            if (need > 0 && !all_amb)
+                t64 = wave_radix_select<uint64_t, 64>(
+                    N, need, [&](int j) { return key64(exact(j)); }, ambiguous, hist, &eq_need);
+            // write ascending
+            int eq_seen = 0;
+            for (int base = 0; base < N; base += 64) {
+                const int j = base + lane;
+                bool take = false;
+                bool eq = false;
+                if (j < N && is_cand(j)) {
+                    const float x = sr[j];
+                    if (x > hi_thr) {
+                        take = true;
+                    } else if (x >= lo_thr && need > 0) {
+                        if (all_amb) {
+                            take = true;
+                        } else {
+                            const uint64_t kk = key64(exact(j));
+                            take = kk > t64;
+                            eq = kk == t64;
+                        }
+                    }
+                }
+                const unsigned long long eqm = __ballot(eq);
+                const int eq_before = __popcll(eqm & ((1ull << lane) - 1ull));
+                if (eq && eq_seen + eq_before < eq_need) take = true;
+                eq_seen += __popcll(eqm);
+                const unsigned long long tm = __ballot(take);
+                const int pos = __popcll(tm & ((1ull << lane) - 1ull));
+                if (take && written + pos < topk) out[written + pos] = j;
+                written += __popcll(tm);
+            }
+        }
+        for (int c = written + lane; c < topk; c += 64) out[c] = -1;
+    }
+}
+
+// General fallback for long sequences (N > kFastMaxN): one workgroup per
+// query block, fp64 scores of every candidate, radix select on 64-bit keys.
+constexpr int kMaxN = 8192;
+
 __device__ __forceinline__ int block_scan(int x, int* scratch, int* excl) {
     const int tid = threadIdx.x;
     scratch[tid] = x;
@@ -45,11 +322,11 @@ __device__ __forceinline__ int block_scan(int x, int* scratch, int* excl) {
     return total;
 }
 
-template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void route_kernel(
-    const T* __restrict__ q, const double* __restrict__ kbar, const double* __restrict__ ksig2,
-    int Tn, int N, float scale, int topk, int band, int second_order, int32_t* __restrict__ idx,
-    float* __restrict__ wgate) {
+template <int D>
+__global__ __launch_bounds__(kThreads) void route_slow_kernel(
+    const double* __restrict__ qbar, const double* __restrict__ q2bar, const double* __restrict__ kbar,
+    const double* __restrict__ ksig2, int N, double s64, int topk, int band, int second_order,
+    int32_t* __restrict__ idx, float* __restrict__ wgate) {
     __shared__ double qbar_s[D];
     __shared__ double q2_s[D];
     __shared__ uint64_t key_s[kMaxN];
@@ -61,27 +338,12 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
     const int tid = threadIdx.x;
     const int64_t bh = blockIdx.y;
     const int i = blockIdx.x;
-    const T* qh = q + bh * (int64_t)Tn * D;
-    const int r0 = i * kBlock;
-    const int rows = min(kBlock, Tn - r0);
-    const double s = (double)scale;
     const double lnB = log((double)kBlock);
-
-    // 1. pooling
     if (tid < D) {
-        double a = 0.0, b = 0.0;
-        for (int n = 0; n < rows; ++n) {
-            const double x = (double)load_f32(qh + (int64_t)(r0 + n) * D + tid);
-            a += x;
-            const double y = s * x;
-            b += y * y;
-        }
-        qbar_s[tid] = a / rows;
-        q2_s[tid] = b / rows;
+        qbar_s[tid] = qbar[(bh * N + i) * (int64_t)D + tid];
+        q2_s[tid] = second_order ? q2bar[(bh * N + i) * (int64_t)D + tid] : 0.0;
     }
     __syncthreads();
-
-    // 2. scores (candidates only; band entries get key 0, below every real key)
     const double* kb = kbar + bh * (int64_t)N * D;
     const double* sg = second_order ? ksig2 + bh * (int64_t)N * D : nullptr;
     float* wrow = second_order ? wgate + (bh * (int64_t)N + i) * N : nullptr;
@@ -90,7 +352,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
         double dot = 0.0;
         const double* kr = kb + (int64_t)j * D;
         for (int d = 0; d < D; ++d) dot = fma(qbar_s[d], kr[d], dot);
-        double r = s * dot;
+        double r = s64 * dot;
         if (second_order) {
             const double* sr = sg + (int64_t)j * D;
             double w = 0.0;
@@ -100,10 +362,9 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
             wrow[j] = (float)(w > lnB ? 0.0 : w);
         }
         const bool cand = abs(i - j) > band;
-        key_s[j] = cand ? order_key(r) : 0ull;
+        key_s[j] = cand ? key64(r) : 0ull;
         ncand += cand;
     }
-    // count candidates
     int dummy;
     ncand = block_scan(ncand, scan_s, &dummy);
     const int k = min(topk, ncand);
@@ -112,8 +373,6 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
         for (int c = tid; c < topk; c += kThreads) out[c] = -1;
         return;
     }
-
-    // 3. radix select of the k-th largest key (8 passes of 8 bits, MSB first)
     if (tid == 0) { prefix_s = 0ull; need_s = k; }
     __syncthreads();
     for (int pass = 0; pass < 8; ++pass) {
@@ -140,11 +399,8 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
         }
         __syncthreads();
     }
-    const uint64_t thr = prefix_s;   // the k-th largest key
-    const int need_eq = need_s;       // how many keys equal to thr are taken (lowest index first)
-
-    // 4. chosen = key > thr, or key == thr among the first need_eq such keys in j order.
-    // Pass A: rank the equal keys in j order; pass B: write ids ascending.
+    const uint64_t thr = prefix_s;
+    const int need_eq = need_s;
     int written = 0, eq_seen = 0;
     for (int base = 0; base < N; base += kThreads) {
         const int j = base + tid;
@@ -164,29 +420,27 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
 
 }  // namespace
 
-hipError_t launch_route_topk(const Geom& g, int dtype, const pisa_params_t* p, const void* q,
-                             const pisa_stats_t* st, int32_t* idx, float* wgate, hipStream_t stream) {
-    dim3 grid(g.N, (unsigned)g.BH), block(kThreads);
+hipError_t launch_route_topk(const Geom& g, const pisa_params_t* p, const pisa_stats_t* st,
+                             int32_t* idx, float* wgate, hipStream_t stream) {
     const int so = p->second_order;
     if (p->topk == 0 && !so) return hipSuccess;
-    int32_t* out = idx;
-    // topk == 0 with the second-order table requested: still run for wgate.
-    if (dtype == PISA_BF16) {
-        auto qq = static_cast<const bf16_t*>(q);
-        if (g.D == 128)
-            hipLaunchKernelGGL((route_kernel<bf16_t, 128>), grid, block, 0, stream, qq, st->kbar,
-                               st->ksig2, g.T, g.N, g.scale, p->topk, p->band, so, out, wgate);
-        else
-            hipLaunchKernelGGL((route_kernel<bf16_t, 64>), grid, block, 0, stream, qq, st->kbar,
-                               st->ksig2, g.T, g.N, g.scale, p->topk, p->band, so, out, wgate);
+    dim3 block(kThreads);
+    if (g.N <= kFastMaxN) {
+        dim3 grid((g.N + kQB - 1) / kQB, (unsigned)g.BH);
+#define PISA_ROUTE_LAUNCH(DD)                                                                      \
+    hipLaunchKernelGGL(route_fast_kernel<DD>, grid, block, 0, stream, st->qbar, st->q2bar,         \
+                       st->kbar, st->ksig2, g.N, g.scale64, p->topk, p->band, so, idx, wgate)
+        if (g.D == 128) PISA_ROUTE_LAUNCH(128);
+        else PISA_ROUTE_LAUNCH(64);
+#undef PISA_ROUTE_LAUNCH
     } else {
-        auto qq = static_cast<const float*>(q);
-        if (g.D == 128)
-            hipLaunchKernelGGL((route_kernel<float, 128>), grid, block, 0, stream, qq, st->kbar,
-                               st->ksig2, g.T, g.N, g.scale, p->topk, p->band, so, out, wgate);
-        else
-            hipLaunchKernelGGL((route_kernel<float, 64>), grid, block, 0, stream, qq, st->kbar,
-                               st->ksig2, g.T, g.N, g.scale, p->topk, p->band, so, out, wgate);
+        dim3 grid(g.N, (unsigned)g.BH);
+#define PISA_ROUTE_LAUNCH(DD)                                                                      \
+    hipLaunchKernelGGL(route_slow_kernel<DD>, grid, block, 0, stream, st->qbar, st->q2bar,         \
+                       st->kbar, st->ksig2, g.N, g.scale64, p->topk, p->band, so, idx, wgate)
+        if (g.D == 128) PISA_ROUTE_LAUNCH(128);
+        else PISA_ROUTE_LAUNCH(64);
+#undef PISA_ROUTE_LAUNCH
     }
     return hipGetLastError();
 }

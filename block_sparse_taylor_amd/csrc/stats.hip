@@ -1,56 +1,97 @@
-// Block statistics of K and V (PISA, Algorithm 1 step 1 / Fig. 4 "Prepare
-// Phase"; Appendix C notation; Piecewise-Taylor-Attention README, "Blog
-// post" for the per-dimension key variance and the changelog's "hc-free"
-// identity sum_j (K_j - kbar_j)^T V_j = K^T V - sum_j kbar_j (x) V-hat_j).
+// Prepare phase: block statistics of Q, K and V (PISA, Algorithm 1 step 1
+// and Fig. 4 "Prepare Phase": block means Q-bar, K-bar, block value sums
+// V-hat and the global first-order matrix H; Appendix C notation;
+// Piecewise-Taylor-Attention README, "Blog post" for the per-dimension key
+// variance and the pooled q^2, changelog "hc-free" statistics for
+// sum_j (K_j - kbar_j)^T V_j = K^T V - sum_j kbar_j (x) V-hat_j).
 //
-// One workgroup streams BPW consecutive 64-row blocks of one (batch, head):
-//   * column statistics per block (kbar, V-hat, sigma^2) in fp64 from the
-//     exact input values, written once per block;
-//   * the partial first-order matrix sum_j (K_j^T V_j - kbar_j (x) V-hat_j)
-//     accumulated on chip: bf16 inputs use bf16 MFMA (exact products, fp32
-//     accumulation), fp32 inputs an fp64 VALU loop;
-//   * the partial is written to the workspace, and a second kernel adds the
-//     partials of a head in a fixed order (no atomics, deterministic).
-// HBM traffic: K and V are read once (2 B T D bytes per head in bf16).
+// One workgroup streams BPW consecutive 64-row blocks of one (batch, head);
+// the Q, K, V tiles of the next block are fetched while the current one is
+// reduced, so Q, K and V are each read from HBM exactly once.
+//   * Column statistics in fp64 (all 256 threads; each column's rows split
+//     over the threads of that column, partials combined in LDS). Sums of
+//     bf16 or fp32 inputs are exact in fp64, so the means equal a float64
+//     evaluation bit for bit; the key variance uses sums shifted by the
+//     block's first row (no cancellation against the mean).
+//   * The partial first-order matrix sum_j (K_j^T V_j - kbar_j (x) V-hat_j):
+//     bf16 inputs use bf16 MFMA (exact products, fp32 accumulation), fp32
+//     inputs an fp64 VALU loop. Partials go to the workspace and a second
+//     kernel adds those of a head in a fixed order (deterministic).
 #include "common.h"
 
 namespace pisa {
 namespace {
 
-constexpr int kPad = 4;  // LDS row padding (elements): rows 8 apart fall on disjoint bank halves
+constexpr int kPad = 4;   // LDS row padding (elements): rows 8 apart fall on disjoint bank halves
+constexpr int kBPW = 32;  // blocks per workgroup
 
-template <int D> constexpr int bpw() { return 32; }
+struct StatsOut {
+    double* qbar;
+    double* q2bar;
+    double* kbar;
+    float* vsum;
+    double* ksig2;
+    void* kbar_c;
+    void* vbar_c;
+};
 
-// ---------------------------------------------------------------- column statistics
+// Column statistics of one block from its LDS tiles (row pitch ld).
 template <typename T, int D>
-__device__ __forceinline__ void column_stats(const T* tile_k, const T* tile_v, int ld, int rows,
-                                             int64_t out_off, int second_order, double* kbar,
-                                             float* vsum, double* ksig2, T* kbar_c, T* vbar_c,
-                                             float* kb_s, float* vs_s) {
+__device__ __forceinline__ void column_stats(const T* tq, const T* tk, const T* tv, int ld, int rows,
+                                             int64_t off, int second_order, double s64,
+                                             const StatsOut& out, double* red, float* kb_s,
+                                             float* vs_s) {
+    constexpr int H = kThreads / D;           // threads per column
+    constexpr int RH = kBlock / H;            // rows per thread
     const int tid = threadIdx.x;
+    const int c = tid % D, h = tid / D;
+    const double shift = (double)load_f32(tk + c);   // block row 0 of this key column
+    double sq = 0.0, sq2 = 0.0, sk = 0.0, skx = 0.0, skx2 = 0.0, sv = 0.0;
+    const int n0 = h * RH, n1 = min(rows, n0 + RH);
+    for (int n = n0; n < n1; ++n) {
+        const double xq = (double)load_f32(tq + n * ld + c);
+        const double xk = (double)load_f32(tk + n * ld + c);
+        const double xv = (double)load_f32(tv + n * ld + c);
+        sq += xq;
+        const double yq = s64 * xq;
+        sq2 += yq * yq;
+        sk += xk;
+        const double dk = xk - shift;
+        skx += dk;
+        skx2 += dk * dk;
+        sv += xv;
+    }
+    double* r = red + tid;
+    r[0 * kThreads] = sq;
+    r[1 * kThreads] = sq2;
+    r[2 * kThreads] = sk;
+    r[3 * kThreads] = skx;
+    r[4 * kThreads] = skx2;
+    r[5 * kThreads] = sv;
+    __syncthreads();
     if (tid < D) {
-        const int d = tid;
-        double s = 0.0;
-        for (int n = 0; n < rows; ++n) s += (double)load_f32(tile_k + n * ld + d);
-        const double mean = s / (double)rows;
-        kbar[out_off + d] = mean;
-        kbar_c[out_off + d] = store_cast<T>((float)mean);
-        kb_s[d] = (float)mean;
-        if (second_order) {
-            double q = 0.0;
-            for (int n = 0; n < rows; ++n) {
-                const double x = (double)load_f32(tile_k + n * ld + d) - mean;
-                q += x * x;
-            }
-            ksig2[out_off + d] = q / (double)rows;
+        double a[6];
+#pragma unroll
+        for (int s = 0; s < 6; ++s) {
+            double x = 0.0;
+#pragma unroll
+            for (int hh = 0; hh < H; ++hh) x += red[s * kThreads + hh * D + tid];
+            a[s] = x;
         }
-    } else if (tid < 2 * D) {
-        const int d = tid - D;
-        double s = 0.0;
-        for (int n = 0; n < rows; ++n) s += (double)load_f32(tile_v + n * ld + d);
-        vsum[out_off + d] = (float)s;
-        vbar_c[out_off + d] = store_cast<T>((float)(s / (double)rows));
-        vs_s[d] = (float)s;
+        const double n = (double)rows;
+        const double mean = a[2] / n;
+        out.qbar[off + c] = a[0] / n;
+        out.kbar[off + c] = mean;
+        static_cast<T*>(out.kbar_c)[off + c] = store_cast<T>((float)mean);
+        out.vsum[off + c] = (float)a[5];
+        static_cast<T*>(out.vbar_c)[off + c] = store_cast<T>((float)(a[5] / n));
+        kb_s[c] = (float)mean;
+        vs_s[c] = (float)a[5];
+        if (second_order) {
+            out.q2bar[off + c] = a[1] / n;
+            const double mx = a[3] / n;
+            out.ksig2[off + c] = fmax(a[4] / n - mx * mx, 0.0);
+        }
     }
 }
 
@@ -58,31 +99,30 @@ __device__ __forceinline__ void column_stats(const T* tile_k, const T* tile_v, i
 // 32x32x16 bf16 MFMA operand layout (lane l, element e in 0..7):
 //   A[m = l%32][k = 8(l/32) + e],  B[k = 8(l/32) + e][n = l%32]
 //   C[m = 8(i/4) + 4(l/32) + i%4][n = l%32] for accumulator register i.
-// H^T-free form: C[a][b] += sum_t K[t][a] V[t][b], so A = K^T and B = V, both
-// gathered column-wise from the row-major LDS tiles.
+// C[a][b] += sum_t K[t][a] V[t][b]: A = K^T and B = V, both gathered
+// column-wise from the row-major LDS tiles.
 template <int D>
 __global__ __launch_bounds__(kThreads) void stats_bf16_kernel(
-    const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, int T, int N, int second_order,
-    double* __restrict__ kbar, float* __restrict__ vsum, double* __restrict__ ksig2,
-    bf16_t* __restrict__ kbar_c, bf16_t* __restrict__ vbar_c, float* __restrict__ hpart) {
-    constexpr int BPW = bpw<D>();
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, int T,
+    int N, int second_order, double s64, StatsOut out, float* __restrict__ hpart) {
     constexpr int LD = D + kPad;
     constexpr int CH = D / 8;                       // 16-byte chunks per row
     constexpr int LOADS = kBlock * CH / kThreads;   // uint4 loads per thread per tensor
     constexpr int NT = D / 32;                      // 32-wide tiles per dim
     constexpr int TPW = NT * NT / 4;                // output tiles per wave
+    __shared__ __attribute__((aligned(16))) bf16_t sq[kBlock * LD];
     __shared__ __attribute__((aligned(16))) bf16_t sk[kBlock * LD];
     __shared__ __attribute__((aligned(16))) bf16_t sv[kBlock * LD];
+    __shared__ double red[6 * kThreads];
     __shared__ float kb_s[D];
     __shared__ float vs_s[D];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t bh = blockIdx.y;
     const int g = blockIdx.x;
-    const int j0 = g * BPW;
-    const int j1 = min(N, j0 + BPW);
-    const bf16_t* kh = k + bh * (int64_t)T * D;
-    const bf16_t* vh = v + bh * (int64_t)T * D;
+    const int j0 = g * kBPW;
+    const int j1 = min(N, j0 + kBPW);
+    const int64_t base = bh * (int64_t)T * D;
 
     f32x16_t acc[TPW];
 #pragma unroll
@@ -90,18 +130,20 @@ __global__ __launch_bounds__(kThreads) void stats_bf16_kernel(
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[t][i] = 0.f;
 
-    uint4 pk[LOADS], pv[LOADS];
+    uint4 pq[LOADS], pk[LOADS], pv[LOADS];
     auto fetch = [&](int j) {
-        const int r0 = j * kBlock;
 #pragma unroll
         for (int L = 0; L < LOADS; ++L) {
             const int c = L * kThreads + tid;
             const int row = c / CH, ch = c % CH;
-            const int t = r0 + row;
+            const int t = j * kBlock + row;
             if (t < T) {
-                pk[L] = *reinterpret_cast<const uint4*>(kh + (int64_t)t * D + ch * 8);
-                pv[L] = *reinterpret_cast<const uint4*>(vh + (int64_t)t * D + ch * 8);
+                const int64_t o = base + (int64_t)t * D + ch * 8;
+                pq[L] = *reinterpret_cast<const uint4*>(q + o);
+                pk[L] = *reinterpret_cast<const uint4*>(k + o);
+                pv[L] = *reinterpret_cast<const uint4*>(v + o);
             } else {
+                pq[L] = make_uint4(0, 0, 0, 0);
                 pk[L] = make_uint4(0, 0, 0, 0);
                 pv[L] = make_uint4(0, 0, 0, 0);
             }
@@ -116,8 +158,12 @@ __global__ __launch_bounds__(kThreads) void stats_bf16_kernel(
         for (int L = 0; L < LOADS; ++L) {
             const int c = L * kThreads + tid;
             const int row = c / CH, ch = c % CH;
-            uint2* dk = reinterpret_cast<uint2*>(sk + row * LD + ch * 8);
-            uint2* dv = reinterpret_cast<uint2*>(sv + row * LD + ch * 8);
+            const int o = row * LD + ch * 8;
+            uint2* dq = reinterpret_cast<uint2*>(sq + o);
+            uint2* dk = reinterpret_cast<uint2*>(sk + o);
+            uint2* dv = reinterpret_cast<uint2*>(sv + o);
+            dq[0] = make_uint2(pq[L].x, pq[L].y);
+            dq[1] = make_uint2(pq[L].z, pq[L].w);
             dk[0] = make_uint2(pk[L].x, pk[L].y);
             dk[1] = make_uint2(pk[L].z, pk[L].w);
             dv[0] = make_uint2(pv[L].x, pv[L].y);
@@ -125,10 +171,6 @@ __global__ __launch_bounds__(kThreads) void stats_bf16_kernel(
         }
         __syncthreads();
         if (j + 1 < j1) fetch(j + 1);
-
-        const int64_t off = (bh * N + j) * D;
-        column_stats<bf16_t, D>(sk, sv, LD, rows, off, second_order, kbar, vsum, ksig2, kbar_c,
-                                vbar_c, kb_s, vs_s);
 
         // acc += K_j^T V_j  (rows >= `rows` are zero in LDS)
         const int m = lane & 31, hi = lane >> 5;
@@ -148,6 +190,9 @@ __global__ __launch_bounds__(kThreads) void stats_bf16_kernel(
                 acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[t], 0, 0, 0);
             }
         }
+
+        const int64_t off = (bh * N + j) * D;
+        column_stats<bf16_t, D>(sq, sk, sv, LD, rows, off, second_order, s64, out, red, kb_s, vs_s);
         __syncthreads();  // kb_s / vs_s visible
         // acc -= kbar_j (x) V-hat_j
 #pragma unroll
@@ -180,22 +225,21 @@ __global__ __launch_bounds__(kThreads) void stats_bf16_kernel(
 // ---------------------------------------------------------------- fp32 path (VALU, fp64 accumulate)
 template <int D>
 __global__ __launch_bounds__(kThreads) void stats_f32_kernel(
-    const float* __restrict__ k, const float* __restrict__ v, int T, int N, int second_order,
-    double* __restrict__ kbar, float* __restrict__ vsum, double* __restrict__ ksig2,
-    float* __restrict__ kbar_c, float* __restrict__ vbar_c, float* __restrict__ hpart) {
-    constexpr int BPW = bpw<D>();
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v, int T,
+    int N, int second_order, double s64, StatsOut out, float* __restrict__ hpart) {
     constexpr int LD = D + 1;
     constexpr int PER = D * D / kThreads;
+    __shared__ float sq[kBlock * LD];
     __shared__ float sk[kBlock * LD];
     __shared__ float sv[kBlock * LD];
+    __shared__ double red[6 * kThreads];
     __shared__ float kb_s[D];
     __shared__ float vs_s[D];
     const int tid = threadIdx.x;
     const int64_t bh = blockIdx.y;
     const int g = blockIdx.x;
-    const int j0 = g * BPW, j1 = min(N, j0 + BPW);
-    const float* kh = k + bh * (int64_t)T * D;
-    const float* vh = v + bh * (int64_t)T * D;
+    const int j0 = g * kBPW, j1 = min(N, j0 + kBPW);
+    const int64_t base = bh * (int64_t)T * D;
     double acc[PER];
 #pragma unroll
     for (int r = 0; r < PER; ++r) acc[r] = 0.0;
@@ -204,26 +248,26 @@ __global__ __launch_bounds__(kThreads) void stats_f32_kernel(
         __syncthreads();
         for (int c = tid; c < kBlock * D; c += kThreads) {
             const int row = c / D, col = c % D;
-            const int t = j * kBlock + row;
-            sk[row * LD + col] = t < T ? kh[(int64_t)t * D + col] : 0.f;
-            sv[row * LD + col] = t < T ? vh[(int64_t)t * D + col] : 0.f;
+            const bool ok = row < rows;
+            const int64_t o = base + ((int64_t)j * kBlock + row) * D + col;
+            sq[row * LD + col] = ok ? q[o] : 0.f;
+            sk[row * LD + col] = ok ? k[o] : 0.f;
+            sv[row * LD + col] = ok ? v[o] : 0.f;
         }
         __syncthreads();
-        const int64_t off = (bh * N + j) * D;
-        column_stats<float, D>(sk, sv, LD, rows, off, second_order, kbar, vsum, ksig2, kbar_c,
-                               vbar_c, kb_s, vs_s);
-        __syncthreads();
+        column_stats<float, D>(sq, sk, sv, LD, rows, (bh * N + j) * D, second_order, s64, out, red,
+                               kb_s, vs_s);
+        // partial H in fp64 from the exact products and exact column sums
 #pragma unroll
         for (int r = 0; r < PER; ++r) {
             const int e = tid + r * kThreads;
             const int a = e / D, b = e % D;
-            double s = 0.0;
-            for (int n = 0; n < rows; ++n) s += (double)sk[n * LD + a] * (double)sv[n * LD + b];
-            // kbar (x) V-hat in fp64 from the exact column sums
-            double ka = 0.0, vb = 0.0;
+            double s = 0.0, ka = 0.0, vb = 0.0;
             for (int n = 0; n < rows; ++n) {
-                ka += (double)sk[n * LD + a];
-                vb += (double)sv[n * LD + b];
+                const double x = (double)sk[n * LD + a], y = (double)sv[n * LD + b];
+                s += x * y;
+                ka += x;
+                vb += y;
             }
             acc[r] += s - ka * vb / (double)rows;
         }
@@ -245,7 +289,7 @@ __global__ __launch_bounds__(kThreads) void hsum_reduce_kernel(const float* __re
     hsum[bh * DD + e] = (float)s;
 }
 
-int stats_groups(const Geom& g) { return (g.N + 31) / 32; }
+int stats_groups(const Geom& g) { return (g.N + kBPW - 1) / kBPW; }
 
 }  // namespace
 
@@ -253,39 +297,30 @@ size_t stats_workspace_bytes(const Geom& g) {
     return (size_t)g.BH * stats_groups(g) * g.D * g.D * sizeof(float);
 }
 
-hipError_t launch_block_stats(const Geom& g, int dtype, int second_order, const void* k, const void* v,
-                              const pisa_stats_t* out, void* workspace, hipStream_t stream) {
+hipError_t launch_block_stats(const Geom& g, int dtype, int second_order, const void* q, const void* k,
+                              const void* v, const pisa_stats_t* st, void* workspace,
+                              hipStream_t stream) {
     const int G = stats_groups(g);
     dim3 grid(G, (unsigned)g.BH), block(kThreads);
     float* hpart = static_cast<float*>(workspace);
+    StatsOut out{st->qbar, st->q2bar, st->kbar, st->vsum, st->ksig2, st->kbar_c, st->vbar_c};
+#define PISA_STATS_LAUNCH(KERN, TT, DD)                                                            \
+    hipLaunchKernelGGL(KERN<DD>, grid, block, 0, stream, static_cast<const TT*>(q),               \
+                       static_cast<const TT*>(k), static_cast<const TT*>(v), g.T, g.N,            \
+                       second_order, g.scale64, out, hpart)
     if (dtype == PISA_BF16) {
-        auto kc = static_cast<bf16_t*>(out->kbar_c);
-        auto vc = static_cast<bf16_t*>(out->vbar_c);
-        auto kk = static_cast<const bf16_t*>(k);
-        auto vv = static_cast<const bf16_t*>(v);
-        if (g.D == 128)
-            hipLaunchKernelGGL(stats_bf16_kernel<128>, grid, block, 0, stream, kk, vv, g.T, g.N,
-                               second_order, out->kbar, out->vsum, out->ksig2, kc, vc, hpart);
-        else
-            hipLaunchKernelGGL(stats_bf16_kernel<64>, grid, block, 0, stream, kk, vv, g.T, g.N,
-                               second_order, out->kbar, out->vsum, out->ksig2, kc, vc, hpart);
+        if (g.D == 128) PISA_STATS_LAUNCH(stats_bf16_kernel, bf16_t, 128);
+        else PISA_STATS_LAUNCH(stats_bf16_kernel, bf16_t, 64);
     } else {
-        auto kc = static_cast<float*>(out->kbar_c);
-        auto vc = static_cast<float*>(out->vbar_c);
-        auto kk = static_cast<const float*>(k);
-        auto vv = static_cast<const float*>(v);
-        if (g.D == 128)
-            hipLaunchKernelGGL(stats_f32_kernel<128>, grid, block, 0, stream, kk, vv, g.T, g.N,
-                               second_order, out->kbar, out->vsum, out->ksig2, kc, vc, hpart);
-        else
-            hipLaunchKernelGGL(stats_f32_kernel<64>, grid, block, 0, stream, kk, vv, g.T, g.N,
-                               second_order, out->kbar, out->vsum, out->ksig2, kc, vc, hpart);
+        if (g.D == 128) PISA_STATS_LAUNCH(stats_f32_kernel, float, 128);
+        else PISA_STATS_LAUNCH(stats_f32_kernel, float, 64);
     }
+#undef PISA_STATS_LAUNCH
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int DD = g.D * g.D;
     dim3 rgrid((DD + kThreads - 1) / kThreads, (unsigned)g.BH);
-    hipLaunchKernelGGL(hsum_reduce_kernel, rgrid, block, 0, stream, hpart, G, DD, out->hsum);
+    hipLaunchKernelGGL(hsum_reduce_kernel, rgrid, block, 0, stream, hpart, G, DD, st->hsum);
     return hipGetLastError();
 }
 

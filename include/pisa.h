@@ -82,23 +82,30 @@ typedef struct {
 } pisa_params_t;
 
 /*
- * Block statistics (Algorithm 1 step 1; §3.2 Formulation; Appendix C):
+ * Block statistics (Algorithm 1 step 1 and Fig. 4: block means of Q and K,
+ * block value sums, the global first-order matrix; §3.2 Formulation;
+ * Appendix C; README "Blog post" for the variance and the pooled q^2):
+ *   qbar[i]   = (1/n_i) sum_t q_t                      fp64 [B,H,N,D]
+ *   q2bar[i]  = (1/n_i) sum_t (s q_t)^2  (elementwise)  fp64 [B,H,N,D]
  *   kbar[j]   = (1/n_j) sum_n k_{j,n}                  fp64 [B,H,N,D]
  *   vsum[j]   = sum_n v_{j,n}               (V-hat)    fp32 [B,H,N,D]
  *   ksig2[j]  = (1/n_j) sum_n (k_{j,n} - kbar_j)^2     fp64 [B,H,N,D]
- *               (per-dim population variance; README "Blog post")
  *   hsum      = sum_j sum_n (k_{j,n} - kbar_j)^T v_{j,n}
  *                                            (D x D)   fp32 [B,H,D,D]
  *               (row index: key dim, column index: value dim)
  *   kbar_c[j] = kbar[j] rounded to the input dtype      [B,H,N,D]
  *   vbar_c[j] = vsum[j] / n_j rounded to the input dtype [B,H,N,D]
- * kbar and ksig2 are fp64 so that routing decisions (a top-k, a gate) match
- * a float64 evaluation; kbar_c / vbar_c feed the virtual-token phase.
+ * n_i, n_j are the rows present in the block (the last one may be partial).
+ * qbar, kbar, q2bar and ksig2 are fp64 so that routing decisions (a top-k, a
+ * gate) match a float64 evaluation; kbar_c / vbar_c feed the virtual tokens.
+ * q2bar and ksig2 may be NULL unless params.second_order.
  */
 typedef struct {
+    double *qbar;
+    double *q2bar;
     double *kbar;
     float *vsum;
-    double *ksig2; /* may be NULL unless params.second_order */
+    double *ksig2;
     float *hsum;
     void *kbar_c;
     void *vbar_c;
@@ -118,33 +125,36 @@ int64_t pisa_num_blocks(const pisa_shape_t *shape);
 size_t pisa_stats_workspace_bytes(const pisa_shape_t *shape);
 
 /*
- * pisa_block_stats: reads k, v; writes every field of `out` (ksig2 only if
- * params->second_order). `workspace` is caller-owned device memory of at
- * least pisa_stats_workspace_bytes(shape) bytes; its contents on entry are
- * ignored and on return are unspecified. Outputs must not alias inputs.
+ * pisa_block_stats: reads q, k, v once; writes every field of `out` (q2bar
+ * and ksig2 only if params->second_order). `workspace` is caller-owned
+ * device memory of at least pisa_stats_workspace_bytes(shape) bytes; its
+ * contents on entry are ignored and on return are unspecified. Outputs must
+ * not alias inputs.
  */
 pisa_status_t pisa_block_stats(const pisa_shape_t *shape, const pisa_params_t *params,
-                               const void *k, const void *v, const pisa_stats_t *out,
-                               void *workspace, size_t workspace_bytes, void *stream);
+                               const void *q, const void *k, const void *v,
+                               const pisa_stats_t *out, void *workspace,
+                               size_t workspace_bytes, void *stream);
 
 /*
  * pisa_route_topk (Algorithm 1 step 2 with the pooled score of Eq. 11 minus
  * its covariance term; README router): for each query block i,
- *   qbar_i  = mean of its query rows, q2bar_i = mean of (s q)^2,
- *   r_ij    = s qbar_i . kbar_j + [second_order] min(w_ij, ln B),
- *   w_ij    = 1/2 q2bar_i . ksig2_j,
+ *   r_ij = s qbar_i . kbar_j + [second_order] min(w_ij, ln B),
+ *   w_ij = 1/2 q2bar_i . ksig2_j,
  * over the candidates j with |i - j| > band. idx[b,h,i,:] receives the
  * min(topk, #candidates) best j (ties: lower j wins), ascending, then -1.
- * Scores, pooled means and w are evaluated in fp64.
+ * Every decision equals a float64 evaluation of r (scores are computed in
+ * fp32 and every block within the fp32 error bound of the cut is re-ranked
+ * in fp64).
  * idx: int32 [B,H,N,topk] (may be NULL iff topk == 0).
  * wgate: fp32 [B,H,N,N], required iff second_order: the gated term used by
  *   the virtual-token logits: w_ij where w_ij <= ln B, and 0 where w_ij is
- *   larger (the README's gate, not a clamp).
- * Reads stats->kbar (and ksig2 if second_order).
+ *   larger (the README's gate, not a clamp), decided as in float64.
+ * Reads stats->qbar, kbar (and q2bar, ksig2 if second_order).
  */
 pisa_status_t pisa_route_topk(const pisa_shape_t *shape, const pisa_params_t *params,
-                              const void *q, const pisa_stats_t *stats, int32_t *idx,
-                              float *wgate, void *stream);
+                              const pisa_stats_t *stats, int32_t *idx, float *wgate,
+                              void *stream);
 
 /*
  * pisa_attn_fwd (Algorithm 1 Phases 1-3, Eqs. 3-5 and 9-10): for each query

@@ -68,23 +68,23 @@ MIS = FAKE + 4
 
 
 def stats(**kw):
-    d = dict(kbar=FAKE, vsum=FAKE, ksig2=None, hsum=FAKE, kbar_c=FAKE, vbar_c=FAKE)
+    d = dict(qbar=FAKE, q2bar=None, kbar=FAKE, vsum=FAKE, ksig2=None, hsum=FAKE, kbar_c=FAKE, vbar_c=FAKE)
     d.update(kw)
     return _lib.Stats(**d)
 
 
-def call_stats(lib, s=None, p=None, k=FAKE, v=FAKE, st=None, ws=FAKE, wsb=1 << 30):
+def call_stats(lib, s=None, p=None, q=FAKE, k=FAKE, v=FAKE, st=None, ws=FAKE, wsb=1 << 30):
     s = s or shape()
     p = p or _lib.Params(4, 1, 0, 1, 0)
     st = st or stats()
-    return lib.pisa_block_stats(ctypes.byref(s), ctypes.byref(p), k, v, ctypes.byref(st), ws, wsb, None)
+    return lib.pisa_block_stats(ctypes.byref(s), ctypes.byref(p), q, k, v, ctypes.byref(st), ws, wsb, None)
 
 
-def call_route(lib, s=None, p=None, q=FAKE, st=None, idx=FAKE, wg=None):
+def call_route(lib, s=None, p=None, st=None, idx=FAKE, wg=None):
     s = s or shape()
     p = p or _lib.Params(4, 1, 0, 1, 0)
     st = st or stats()
-    return lib.pisa_route_topk(ctypes.byref(s), ctypes.byref(p), q, ctypes.byref(st), idx, wg, None)
+    return lib.pisa_route_topk(ctypes.byref(s), ctypes.byref(p), ctypes.byref(st), idx, wg, None)
 
 
 def call_attn(lib, name="pisa_attn_fwd", s=None, p=None, q=FAKE, k=FAKE + 64, v=FAKE + 128,
@@ -101,12 +101,15 @@ E = {n: c for c, n in _lib.STATUS_NAMES.items()}
 
 def test_stats_validation(lib):
     assert call_stats(lib, k=None) == E["PISA_ERR_NULL"]
+    assert call_stats(lib, q=MIS) == E["PISA_ERR_ALIGN"]
+    assert call_stats(lib, st=stats(qbar=None)) == E["PISA_ERR_NULL"]
     assert call_stats(lib, v=MIS) == E["PISA_ERR_ALIGN"]
     assert call_stats(lib, s=shape(D=32)) == E["PISA_ERR_SHAPE"]
     assert call_stats(lib, st=stats(hsum=None)) == E["PISA_ERR_NULL"]
     assert call_stats(lib, st=stats(kbar_c=MIS)) == E["PISA_ERR_ALIGN"]
-    # second order needs ksig2
+    # second order needs ksig2 and q2bar
     assert call_stats(lib, p=_lib.Params(4, 1, 1, 1, 0)) == E["PISA_ERR_NULL"]
+    assert call_stats(lib, p=_lib.Params(4, 1, 1, 1, 0), st=stats(ksig2=FAKE)) == E["PISA_ERR_NULL"]
     assert call_stats(lib, ws=None) == E["PISA_ERR_NULL"]
     assert call_stats(lib, wsb=16) == E["PISA_ERR_WORKSPACE"]
     assert call_stats(lib, p=_lib.Params(4, 1, 2, 1, 0)) == E["PISA_ERR_PARAM"]
@@ -117,12 +120,13 @@ def test_route_validation(lib):
     assert call_route(lib, p=_lib.Params(N + 1, 1, 0, 1, 0)) == E["PISA_ERR_PARAM"]
     assert call_route(lib, p=_lib.Params(-1, 1, 0, 1, 0)) == E["PISA_ERR_PARAM"]
     assert call_route(lib, p=_lib.Params(4, -1, 0, 1, 0)) == E["PISA_ERR_PARAM"]
-    assert call_route(lib, q=None) == E["PISA_ERR_NULL"]
+    assert call_route(lib, st=stats(qbar=None)) == E["PISA_ERR_NULL"]
     assert call_route(lib, idx=None) == E["PISA_ERR_NULL"]
     assert call_route(lib, st=stats(kbar=None)) == E["PISA_ERR_NULL"]
-    # second order: ksig2 and wgate required
+    # second order: q2bar, ksig2 and wgate required
     assert call_route(lib, p=_lib.Params(4, 1, 1, 1, 0)) == E["PISA_ERR_NULL"]
     assert call_route(lib, p=_lib.Params(4, 1, 1, 1, 0), st=stats(ksig2=FAKE)) == E["PISA_ERR_NULL"]
+    assert call_route(lib, p=_lib.Params(4, 1, 1, 1, 0), st=stats(ksig2=FAKE, q2bar=FAKE)) == E["PISA_ERR_NULL"]
     assert call_route(lib, s=shape(block=128)) == E["PISA_ERR_PARAM"]
 
 
@@ -144,6 +148,7 @@ def test_null_structs(lib):
     st = stats()
     p = _lib.Params(4, 1, 0, 1, 0)
     s = shape()
-    assert lib.pisa_block_stats(None, ctypes.byref(p), FAKE, FAKE, ctypes.byref(st), FAKE, 1 << 30, None) == E["PISA_ERR_NULL"]
-    assert lib.pisa_route_topk(ctypes.byref(s), None, FAKE, ctypes.byref(st), FAKE, None, None) == E["PISA_ERR_NULL"]
+    assert lib.pisa_block_stats(None, ctypes.byref(p), FAKE, FAKE, FAKE, ctypes.byref(st), FAKE, 1 << 30, None) == E["PISA_ERR_NULL"]
+    assert lib.pisa_route_topk(ctypes.byref(s), None, ctypes.byref(st), FAKE, None, None) == E["PISA_ERR_NULL"]
+    assert lib.pisa_route_topk(ctypes.byref(s), ctypes.byref(p), None, FAKE, None, None) == E["PISA_ERR_NULL"]
     assert lib.pisa_attn_fwd(ctypes.byref(s), ctypes.byref(p), FAKE, FAKE + 64, FAKE + 128, None, FAKE, None, FAKE + 256, None) == E["PISA_ERR_NULL"]

@@ -27,7 +27,7 @@ def make(T, D, dtype, seed, H=2, kscale=1.0):
 
 
 def run_all(q, k, v, topk, band, second_order=False, first_order=True, fn=P.pisa_attn_fwd):
-    st = P.pisa_block_stats(k, v, second_order=second_order)
+    st = P.pisa_block_stats(q, k, v, second_order=second_order)
     idx, wg = P.pisa_route_topk(q, st, topk, band=band, second_order=second_order)
     o = fn(q, k, v, st, idx if topk else None, wg, band=band, second_order=second_order,
            first_order=first_order)
@@ -153,3 +153,23 @@ def test_mfma_matches_valu_reference():
     o_ref = P.pisa_attn_fwd_valu(q, k, v, st, idx, wg, band=1, second_order=True)
     torch.cuda.synchronize()
     assert (o.double() - o_ref.double()).abs().max() <= 2e-2
+
+
+@pytest.mark.parametrize("second_order", [False, True])
+def test_long_sequence_routing(second_order):
+    """N above the LDS-resident score-row limit (1920 blocks) takes the
+    per-query-block routing path; its table must equal the oracle's."""
+    T, D = 124000, 64
+    N = -(-T // 64)
+    topk = 24
+    say(f"[gpu] long routing T={T} N={N} so={second_order}")
+    (q, k, v), (qh, kh, vh) = make(T, D, "bf16", 77, H=1)
+    st = P.pisa_block_stats(q, k, v, second_order=second_order)
+    idx, wg = P.pisa_route_topk(q, st, topk, band=1, second_order=second_order)
+    torch.cuda.synchronize()
+    s = 1 / math.sqrt(D)
+    ks = O.kv_block_stats(kh[0, 0], vh[0, 0], 64)
+    qbar, q2bar = O.pool_queries(qh[0, 0], 64, s)
+    wr = O.second_order_w(q2bar, ks.sig2, 64)[2] if second_order else None
+    ref, _ = O.route_topk(qbar, ks.kbar, s, topk, 1, wr)
+    assert np.array_equal(idx.cpu().numpy()[0, 0], ref)

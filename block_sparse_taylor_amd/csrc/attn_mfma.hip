@@ -8,28 +8,32 @@
 //   ids) followed by its virtual-token groups (64 consecutive KV blocks'
 //   (kbar_j, V-hat_j / n_j) rows each). Items are dealt round-robin to the 4
 //   waves; each wave keeps its own online-softmax state for all 64 query rows
-//   (split-KV inside the workgroup) and the states are merged at the end, so
-//   no K/V tile is shared through LDS and LDS bandwidth is spent only on V.
+//   (split-KV inside the workgroup) and the states are merged at the end.
 //
 // Per item and wave (32x32x16 bf16 MFMA, fp32 accumulation):
-//   S^T = K Q^T        A = K rows straight from global memory, B = Q^T from
-//                      registers (loaded once); lane l holds query l%32 of
-//                      query tile qt and 16 keys per key tile.
-//   P   = exp2(S^T s log2e + bias - m)   bias: 0 / -inf for exact keys past
-//                      T; log2 n_j + log2e w_ij, or -inf for selected blocks,
-//                      for virtual tokens (a virtual token is a key with
-//                      logit lam + ln n_j and value V-hat_j / n_j: mass
-//                      n_j e^lam, numerator e^lam V-hat_j).
-//   O^T += V^T P       A = V^T read from a per-wave LDS buffer (written
-//                      transposed from registers), B = P straight from the
-//                      S^T accumulator (no lane movement). O^T keeps query =
-//                      lane, so the softmax rescale is a per-lane multiply.
-//   The PV product of item n-1 is issued before the softmax of item n, so
-//   the MFMA pipe has independent work while the VALU evaluates exponentials.
-// Epilogue: every wave writes (m, l, l_tail, O^T) to LDS; wave w then merges
-//   the 4 states for output dims [32w, 32w+32), adds the global first order
-//   F = (l_tail / T) s (Q H) computed with bf16 MFMA on H split into
-//   hi + lo bf16 parts, divides by l and stores bf16.
+//   S^T = K Q^T     A = K rows by buffer loads straight into registers (the
+//                   buffer descriptor's record count zero-fills rows past the
+//                   item's end); B = Q^T from an LDS copy shared by the waves.
+//                   Lane l then holds query l%32 of query tile qt, 16 keys
+//                   per key tile.
+//   P = exp2(S^T s log2e + bias - m)   bias: -inf for keys past T; for
+//                   virtual tokens log2 n_j + log2e w_ij, or -inf for
+//                   selected blocks (a virtual token is a key with logit
+//                   lam + ln n_j and value V-hat_j / n_j).
+//   O^T += V^T P    B = P straight from the S^T accumulator (no lane
+//                   movement); A = V^T read with the gfx950 LDS transpose
+//                   read from a row-major V tile (rows XOR-swizzled by
+//                   row % 4 in 8-byte units, so 16-byte row writes and the
+//                   transposed reads are both bank-conflict free). O^T keeps
+//                   query = lane, so any rescale is a per-lane multiply.
+//   The reference max only moves when a tile exceeds it by more than kTau
+//   (log2 units); otherwise P <= 2^kTau is taken against the stale max and
+//   the accumulator is left alone. The PV product of item n-1 is issued
+//   before the softmax of item n.
+// Epilogue: every wave writes (m, l, l_tail, O^T) to LDS; wave w merges the
+//   4 states for output dims [32w, 32w+32), adds the global first order
+//   F = (l_tail / T) s (Q H) (bf16 MFMA on H split into hi + lo parts),
+//   divides by l and stores bf16.
 #include <math.h>
 
 #include "common.h"
@@ -38,28 +42,29 @@ namespace pisa {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kPitch = 68;              // V^T row pitch in bf16 (64 keys + 4)
 constexpr int kMaxWords = 8192 / 32;    // selection bitmask words (N <= 8192)
-constexpr float kTau = 8.0f;            // stale-max tolerance of the softmax (log2 units)
+constexpr float kTau = 64.0f;           // headroom of the fixed softmax reference (log2 units)
+constexpr uint32_t kRsrcWord3 = 0x00020000u;   // gfx9 raw buffer descriptor, dword 3
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 template <int D>
 struct Cfg {
     static constexpr int KS = D / 16;          // QK k-steps
     static constexpr int DT = D / 32;          // 32-wide output-dim tiles
     static constexpr int CH = D / 8;           // 16-byte chunks per row
-    static constexpr int KGP = 64 / CH;        // 4-key groups per V load pass
-    static constexpr int VIT = 16 / KGP;       // V load passes
-    static constexpr int VT = D * kPitch;      // bf16 elements per V^T buffer
-    static constexpr int VT_BYTES = 8 * VT * 2;
+    static constexpr int VL = CH;              // V loads per lane per item (64 rows * CH / 64)
+    static constexpr int RB = 2 * D;           // row bytes
+    static constexpr int VBUF = 64 * RB;       // bytes of one V tile
+    static constexpr int V_BYTES = 8 * VBUF;   // 4 waves x 2 buffers
     static constexpr int MERGE_BYTES = 4 * DT * 2 * 16 * 64 * 4 + 3 * 4 * 64 * 4;
-    static constexpr int REGION = VT_BYTES > MERGE_BYTES ? VT_BYTES : MERGE_BYTES;
+    static constexpr int REGION = V_BYTES > MERGE_BYTES ? V_BYTES : MERGE_BYTES;
     static constexpr int QP = D + 8;           // Q row pitch in LDS (bf16)
     static constexpr int QBYTES = 64 * QP * 2;
 };
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // Two fp32 -> bf16 (round to nearest even) packed in one dword.
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
@@ -68,6 +73,39 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Buffer descriptor of a wave-uniform range. The fields are passed through
+// readfirstlane so the descriptor stays in SGPRs even where the compiler
+// cannot prove uniformity (a VGPR descriptor becomes a per-lane loop).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    void* p = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes),
+                                             (int)kRsrcWord3);
+}
+
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
+}
+
+// 16 bytes per lane from a buffer straight into LDS: lane l writes M0 base +
+// 16 l (the LDS address is wave-uniform). The host pass of this compiler
+// drops any kernel whose body names this builtin, so only the device pass
+// sees it.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, unsigned char* lds, uint32_t voff,
+                                      uint32_t soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
+                                             (int)voff, (int)soff, 0, 0);
+#endif
+}
+
+__device__ __forceinline__ uint2 lds_tr16(const unsigned char* p) {
+    typedef __attribute__((address_space(3))) v4i16_t lds_v4i16;
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p));
+}
 
 template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -120,11 +158,6 @@ void attn_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
         }
     }
     if (myvalid) atomicAdd(&nvalid_s, myvalid);
-    __syncthreads();
-    const int nvalid = nvalid_s;
-    const int E = do_exact ? nb + nvalid : 0;
-    const int GV = do_virtual ? (N + 63) / 64 : 0;
-    const int items = E + GV;
 
     // ---- Q rows of the block staged once in LDS (shared by the 4 waves); the
     // Q^T operand of S^T = K Q^T is read from there: dim d = (D/2) g + 8 ks + e
@@ -140,6 +173,10 @@ void attn_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
         }
     }
     __syncthreads();
+    const int nvalid = __builtin_amdgcn_readfirstlane(nvalid_s);   // LDS value, uniform: keep item data in SGPRs
+    const int E = do_exact ? nb + nvalid : 0;
+    const int GV = do_virtual ? (N + 63) / 64 : 0;
+    const int items = E + GV;
     auto qop = [&](int qt, int ks) {
         return as_bf16x8(*reinterpret_cast<const uint4*>(qs + (qt * 32 + r32) * C::QP + (D / 2) * g + 8 * ks));
     };
@@ -157,19 +194,21 @@ void attn_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[dt][qt][e] = 0.f;
 
-    bf16_t* vt_base = reinterpret_cast<bf16_t*>(smem) + wave * 2 * C::VT;
+    unsigned char* vbuf0 = smem + wave * 2 * C::VBUF;
 
-    // ---- item description
+    // ---- item description (wave-uniform: lives in SGPRs)
     struct Item {
         const bf16_t* ks;
         const bf16_t* vs;
         int nval;       // valid rows
         int vgroup;     // virtual group index, or -1 for an exact block
     };
+    typedef __attribute__((address_space(4))) const int32_t cint32_t;
+    cint32_t* crow = (cint32_t*)(uintptr_t)row;   // uniform index: scalar loads
     auto item_of = [&](int t) {
         Item it;
         if (t < E) {
-            const int j = t < nb ? lo + t : row[t - nb];
+            const int j = t < nb ? lo + t : crow[t - nb];
             const int64_t off = (bh * T + (int64_t)j * 64) * D;
             it.ks = k + off;
             it.vs = v + off;
@@ -186,69 +225,55 @@ void attn_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
         return it;
     };
 
+    // Per-lane byte offsets (constant over items)
+    const uint32_t koff = (uint32_t)(r32 * C::RB + D * g);              // K operand: row r32, dims (D/2) g..
+    // V tile: buffer -> LDS DMA, 1 KB per instruction: lane l fills LDS slot l,
+    // i.e. row RPI n + l / CH, 16-byte position l % CH. That position holds
+    // the row's chunk (l % CH) ^ 2 (row % 4) (the swizzle the transposed
+    // reads expect), so the lane loads that chunk. RPI = 64 / CH rows per
+    // instruction is a multiple of 4, so row % 4 = (l / CH) % 4 for every n.
+    constexpr int RPI = 64 / C::CH;
+    const int vrow0 = lane / C::CH;
+    const uint32_t voff = (uint32_t)(vrow0 * C::RB + 16 * ((lane % C::CH) ^ (2 * (vrow0 & 3))));
+
     uint4 kreg[2][C::KS];
-    uint4 vreg[C::VIT][4];
-    // Rows past the item's valid count are read from its last valid row and
-    // zeroed, so every load is unconditional (no divergent branches).
     auto load_k = [&](const Item& it) {
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(it.ks, (uint32_t)(it.nval * C::RB));
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-            const int rr = kt * 32 + r32;
-            const bool ok = rr < it.nval;
-            const bf16_t* src = it.ks + (ok ? rr : it.nval - 1) * D + (D / 2) * g;
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-            for (int ks = 0; ks < C::KS; ++ks) {
-                uint4 u = *reinterpret_cast<const uint4*>(src + 8 * ks);
-                if (!ok) u = make_uint4(0, 0, 0, 0);
-                kreg[kt][ks] = u;
-            }
-        }
+            for (int ks = 0; ks < C::KS; ++ks) kreg[kt][ks] = bload16(r, koff + kt * 32 * C::RB + 16 * ks);
     };
-    const int vc = lane % C::CH, vkg0 = lane / C::CH;
-    auto load_v = [&](const Item& it) {
+    // Rows past the item's end are zero-filled by the descriptor's range check.
+    auto dma_v = [&](const Item& it, unsigned char* buf) {
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(it.vs, (uint32_t)(it.nval * C::RB));
 #pragma unroll
-        for (int p = 0; p < C::VIT; ++p)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int key = 4 * (vkg0 + C::KGP * p) + r;
-                const bool ok = key < it.nval;
-                uint4 u = *reinterpret_cast<const uint4*>(it.vs + (ok ? key : it.nval - 1) * D + 8 * vc);
-                if (!ok) u = make_uint4(0, 0, 0, 0);
-                vreg[p][r] = u;
-            }
+        for (int n = 0; n < C::VL; ++n)
+            dma16(r, buf + n * RPI * C::RB, voff, n * RPI * C::RB);
     };
-    // V rows (registers) -> V^T buffer: 4 keys x 8 dims per (pass), 4x4 bf16 transposes
-    auto store_vt = [&](bf16_t* buf) {
-#pragma unroll
-        for (int p = 0; p < C::VIT; ++p) {
-            const int kg = vkg0 + C::KGP * p;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const uint32_t a0 = (&vreg[p][0].x)[w], a1 = (&vreg[p][1].x)[w];
-                const uint32_t a2 = (&vreg[p][2].x)[w], a3 = (&vreg[p][3].x)[w];
-                const uint2 lo2 = make_uint2(__builtin_amdgcn_perm(a1, a0, 0x05040100u),
-                                             __builtin_amdgcn_perm(a3, a2, 0x05040100u));
-                const uint2 hi2 = make_uint2(__builtin_amdgcn_perm(a1, a0, 0x07060302u),
-                                             __builtin_amdgcn_perm(a3, a2, 0x07060302u));
-                const int d = 8 * vc + 2 * w;
-                *reinterpret_cast<uint2*>(buf + d * kPitch + 4 * kg) = lo2;
-                *reinterpret_cast<uint2*>(buf + (d + 1) * kPitch + 4 * kg) = hi2;
-            }
-        }
+
+    // Transposed-read addresses (lane-constant part): in each 16-lane group,
+    // lane a + 4e fetches row base + 4g + e, dims C0 + 4a (8 bytes); the read
+    // hands lane 4a + b element b of the fetches of lanes a, a+4, a+8, a+12.
+    const int trG = lane >> 4, tri = lane & 15, tra = tri & 3, tre = tri >> 2;
+    const uint32_t trow = (uint32_t)((4 * g + tre) * C::RB);
+    auto tr_off = [&](int dt) {   // byte offset within a row of this lane's 8-byte chunk
+        const int c8 = (dt * 32 + 16 * (trG & 1) + 4 * tra) >> 2;
+        return (uint32_t)(8 * (c8 ^ (4 * tre)));
     };
 
     bf16x8_t pp[2][2][2];   // [kt][half][qt] P operands of the previous item
-    auto pv = [&](const bf16_t* buf) {
+    auto pv = [&](const unsigned char* buf) {
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) {
-            const bf16_t* vrow = buf + (dt * 32 + r32) * kPitch + 4 * g;
+            const unsigned char* base = buf + trow + tr_off(dt);
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
                 for (int half = 0; half < 2; ++half) {
-                    const int base = kt * 32 + half * 16;
-                    const uint2 a = *reinterpret_cast<const uint2*>(vrow + base);
-                    const uint2 b = *reinterpret_cast<const uint2*>(vrow + base + 8);
+                    const int r0 = kt * 32 + half * 16;
+                    const uint2 a = lds_tr16(base + r0 * C::RB);
+                    const uint2 b = lds_tr16(base + (r0 + 8) * C::RB);
                     const bf16x8_t av = as_bf16x8(make_uint4(a.x, a.y, b.x, b.y));
 #pragma unroll
                     for (int qt = 0; qt < 2; ++qt)
@@ -257,17 +282,42 @@ void attn_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
         }
     };
 
-    int t = wave;
-    bool has_prev = false;
-    int parity = 0;
+    // Pipeline per wave: item n's K sits in registers (loaded during item n-1)
+    // and its V tile in LDS buffer n % 2 (DMA issued during item n-1, right
+    // after PV of item n-2 released that buffer).
+    //
+    // Softmax reference: the accumulator is never rescaled. A query's
+    // reference m2 is the first finite tile max it sees (its accumulator is
+    // still zero then); later tiles are taken against it, P = 2^(z - m2) <=
+    // 2^kTau. If a tile ever exceeds its reference by more than kTau, the wave
+    // raises the reference and restarts its items from zero (each restart
+    // raises some reference by more than kTau, so restarts are finite).
+    int t;
+    bool has_prev;
+    int parity;
     Item cur;
+    for (;;) {
+    t = wave;
+    has_prev = false;
+    parity = 0;
+    bool restart = false;
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[dt][qt][e] = 0.f;
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+        lsum[qt] = 0.f;
+        ltail[qt] = 0.f;
+    }
     if (t < items) {
         cur = item_of(t);
         load_k(cur);
+        dma_v(cur, vbuf0);
     }
     for (; t < items; t += 4) {
-        // this item's V^T into its buffer (the buffer PV read two items ago)
-        load_v(cur);
         // S^T = K Q^T
         f32x16_t s[2][2];
 #pragma unroll
@@ -280,31 +330,42 @@ void attn_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
                 for (int ks = 0; ks < C::KS; ++ks)
                     s[kt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kreg[kt][ks]), qop(qt, ks), s[kt][qt], 0, 0, 0);
             }
-        // this item's V^T into its buffer (the one PV read two items ago)
-        store_vt(vt_base + parity * C::VT);
         const bool has_next = t + 4 < items;
         Item nxt = cur;
-        // O^T += V^T P of the previous item (independent of this item's softmax)
-        if (has_prev) pv(vt_base + (parity ^ 1) * C::VT);
         if (has_next) {
             nxt = item_of(t + 4);
             load_k(nxt);
         }
+        // O^T += V^T P of the previous item (independent of this item's softmax)
+        if (has_prev) pv(vbuf0 + (parity ^ 1) * C::VBUF);
+        if (has_next) {
+            // the previous item's buffer is free once its reads have returned
+            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+            dma_v(nxt, vbuf0 + (parity ^ 1) * C::VBUF);
+        }
 
-        // softmax of this item. The reference max m2 only moves when a tile
-        // exceeds it by more than kTau (log2 units); otherwise P <= 2^kTau is
-        // taken against the stale max and the accumulator is not rescaled.
+        // ---- softmax of this item
         const bool virt = cur.vgroup >= 0;
-        const bool full = !virt && cur.nval == 64;
+        const bool plain = !virt && cur.nval == 64;   // no masking, no bias
         float mx[2] = {-INFINITY, -INFINITY};
+        if (plain) {
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+            for (int qt = 0; qt < 2; ++qt) {
+                float a = s[0][qt][0];
 #pragma unroll
-            for (int run = 0; run < 4; ++run) {
-                // keys kt*32 + 8 run + 4 g + (0..3) of this lane
-                const int key0 = kt * 32 + 8 * run + 4 * g;
-                float b[4] = {0.f, 0.f, 0.f, 0.f};
-                if (!full) {
+                for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) a = fmaxf(a, s[kt][qt][e]);
+                mx[qt] = a * c2;
+            }
+        } else {
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int run = 0; run < 4; ++run) {
+                    // keys kt*32 + 8 run + 4 g + (0..3) of this lane
+                    const int key0 = kt * 32 + 8 * run + 4 * g;
+                    float b[4];
                     if (!virt) {
 #pragma unroll
                         for (int e = 0; e < 4; ++e) b[e] = key0 + e < cur.nval ? 0.f : -INFINITY;
@@ -319,48 +380,52 @@ void attn_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
                             b[e] = (j >= N || ((bits >> e) & 1u)) ? -INFINITY : bb;
                         }
                     }
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+#pragma unroll
+                        for (int qt = 0; qt < 2; ++qt) {
+                            const float z = fmaf(s[kt][qt][4 * run + e], c2, b[e]);
+                            s[kt][qt][4 * run + e] = z;
+                            mx[qt] = fmaxf(mx[qt], z);
+                        }
                 }
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-#pragma unroll
-                    for (int qt = 0; qt < 2; ++qt) {
-                        const float z = fmaf(s[kt][qt][4 * run + e], c2, b[e]);
-                        s[kt][qt][4 * run + e] = z;
-                        mx[qt] = fmaxf(mx[qt], z);
-                    }
-            }
+        }
         bool need = false;
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt) {
             mx[qt] = fmaxf(mx[qt], __shfl_xor(mx[qt], 32));
+            if (m2[qt] == -INFINITY) m2[qt] = mx[qt];   // first finite max: accumulator still zero
             need |= mx[qt] > m2[qt] + kTau;
         }
-        if (__any(need)) {
+        if (__builtin_amdgcn_ballot_w64(need) != 0) {   // ballot is wave-uniform
 #pragma unroll
-            for (int qt = 0; qt < 2; ++qt) {
-                const float mnew = fmaxf(m2[qt], mx[qt]);
-                const float alpha = fast_exp2(m2[qt] - (mnew == -INFINITY ? 0.f : mnew));
-                m2[qt] = mnew;
-                lsum[qt] *= alpha;
-                ltail[qt] *= alpha;
-#pragma unroll
-                for (int dt = 0; dt < C::DT; ++dt)
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) acc[dt][qt][e] *= alpha;
-            }
+            for (int qt = 0; qt < 2; ++qt) m2[qt] = fmaxf(m2[qt], mx[qt]);
+            restart = true;
+            break;
         }
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt) {
             const float muse = m2[qt] == -INFINITY ? 0.f : m2[qt];
             float rs = 0.f;
+            if (plain) {
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
+                for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const float pe = fast_exp2(s[kt][qt][e] - muse);
-                    s[kt][qt][e] = pe;
-                    rs += pe;
-                }
+                    for (int e = 0; e < 16; ++e) {
+                        const float pe = fast_exp2(fmaf(s[kt][qt][e], c2, -muse));
+                        s[kt][qt][e] = pe;
+                        rs += pe;
+                    }
+            } else {
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const float pe = fast_exp2(s[kt][qt][e] - muse);
+                        s[kt][qt][e] = pe;
+                        rs += pe;
+                    }
+            }
             lsum[qt] += rs;
             if (virt) ltail[qt] += rs;
         }
@@ -377,12 +442,14 @@ void attn_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
                     u.w = pack_bf16x2(s[kt][qt][8 * half + 6], s[kt][qt][8 * half + 7]);
                     pp[kt][half][qt] = as_bf16x8(u);
                 }
-
         cur = nxt;
         has_prev = true;
         parity ^= 1;
     }
-    if (has_prev) pv(vt_base + (parity ^ 1) * C::VT);
+    if (!restart) break;
+    __builtin_amdgcn_s_waitcnt(0);   // drain the abandoned prefetches before reusing the buffers
+    }
+    if (has_prev) pv(vbuf0 + (parity ^ 1) * C::VBUF);
 
     // ---- merge the four wave states and finish (Phase 3)
 #pragma unroll
@@ -390,7 +457,7 @@ void attn_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
         lsum[qt] += __shfl_xor(lsum[qt], 32);
         ltail[qt] += __shfl_xor(ltail[qt], 32);
     }
-    __syncthreads();   // every wave is done with its V^T buffers
+    __syncthreads();   // every wave is done with its V buffers
     float* mo = reinterpret_cast<float*>(smem);
     float* ms = mo + 4 * C::DT * 2 * 16 * 64;
     float* ls = ms + 4 * 64;
@@ -465,15 +532,15 @@ void attn_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
             for (int w = 0; w < 4; ++w) a = fmaf(f[w], mo[(((w * C::DT + dt) * 2 + qt) * 16 + e) * 64 + lane], a);
             out[e] = (a + cF * gacc[qt][e]) * inv;
         }
-        const int trow = i * 64 + qi;
-        if (trow < T) {
+        const int trow_o = i * 64 + qi;
+        if (trow_o < T) {
 #pragma unroll
             for (int a4 = 0; a4 < 4; ++a4) {
                 const int d0 = dt * 32 + 8 * a4 + 4 * g;
                 uint2 u;
                 u.x = pack_bf16x2(out[4 * a4 + 0], out[4 * a4 + 1]);
                 u.y = pack_bf16x2(out[4 * a4 + 2], out[4 * a4 + 3]);
-                *reinterpret_cast<uint2*>(oh + (int64_t)trow * D + d0) = u;
+                *reinterpret_cast<uint2*>(oh + (int64_t)trow_o * D + d0) = u;
             }
         }
     }

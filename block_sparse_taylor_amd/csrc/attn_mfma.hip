@@ -36,6 +36,8 @@
 //   divides by l and stores bf16.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace pisa {
@@ -54,14 +56,12 @@ struct Cfg {
     static constexpr int KS = D / 16;          // QK k-steps
     static constexpr int DT = D / 32;          // 32-wide output-dim tiles
     static constexpr int CH = D / 8;           // 16-byte chunks per row
-    static constexpr int VL = CH;              // V loads per lane per item (64 rows * CH / 64)
+    static constexpr int VL = CH;              // V DMA instructions per item (64 rows * CH / 64)
     static constexpr int RB = 2 * D;           // row bytes
     static constexpr int VBUF = 64 * RB;       // bytes of one V tile
-    static constexpr int V_BYTES = 8 * VBUF;   // 4 waves x 2 buffers
-    static constexpr int MERGE_BYTES = 4 * DT * 2 * 16 * 64 * 4 + 3 * 4 * 64 * 4;
-    static constexpr int REGION = V_BYTES > MERGE_BYTES ? V_BYTES : MERGE_BYTES;
     static constexpr int QP = D + 8;           // Q row pitch in LDS (bf16)
-    static constexpr int QBYTES = 64 * QP * 2;
+    // the merge of the wave states reuses the V tiles: two waves' O^T per parity array
+    static_assert(2 * DT * 2 * 16 * 64 * 4 == 4 * VBUF, "merge layout");
 };
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
@@ -116,7 +116,13 @@ void attn_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
                       bf16_t* __restrict__ o, int T, int N, int total, float scale, int topk,
                       int band, int second_order, int first_order, int phase_mask) {
     using C = Cfg<D>;
-    __shared__ __attribute__((aligned(16))) unsigned char smem[C::REGION + C::QBYTES];
+    // V tiles of the two pipeline parities live in separate arrays, so that the
+    // compiler can tell the asynchronous buffer->LDS writes into one parity from
+    // reads of the other (and of the Q tile) and waits only where data is needed.
+    __shared__ __attribute__((aligned(16))) unsigned char vb0[4 * C::VBUF];
+    __shared__ __attribute__((aligned(16))) unsigned char vb1[4 * C::VBUF];
+    __shared__ __attribute__((aligned(16))) bf16_t qs[64 * C::QP];
+    __shared__ float mstat[3 * 4 * 64];
     __shared__ uint32_t selbits[kMaxWords];
     __shared__ int nvalid_s;
 
@@ -161,7 +167,6 @@ void attn_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
 
     // ---- Q rows of the block staged once in LDS (shared by the 4 waves); the
     // Q^T operand of S^T = K Q^T is read from there: dim d = (D/2) g + 8 ks + e
-    bf16_t* qs = reinterpret_cast<bf16_t*>(smem + C::REGION);
     {
         const bf16_t* qh = q + bh * (int64_t)T * D;
         for (int c = tid; c < 64 * C::CH; c += kThreads) {
@@ -177,9 +182,14 @@ void attn_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
     const int E = do_exact ? nb + nvalid : 0;
     const int GV = do_virtual ? (N + 63) / 64 : 0;
     const int items = E + GV;
-    auto qop = [&](int qt, int ks) {
-        return as_bf16x8(*reinterpret_cast<const uint4*>(qs + (qt * 32 + r32) * C::QP + (D / 2) * g + 8 * ks));
+    // per-lane element offset of the Q^T operand; each step launders it so the
+    // compiler re-reads Q from LDS per item instead of pinning its 16 operands
+    // (64 VGPRs) in registers for the whole loop
+    const int qlane = r32 * C::QP + (D / 2) * g;
+    auto qop_at = [&](int qb, int qt, int ks) {
+        return as_bf16x8(*reinterpret_cast<const uint4*>(qs + qb + qt * 32 * C::QP + 8 * ks));
     };
+    auto qop = [&](int qt, int ks) { return qop_at(qlane, qt, ks); };
 
     const float c2 = scale * kLog2e;
     const float lnlast2 = log2f((float)(T - (N - 1) * 64));   // log2 n of the last block
@@ -194,7 +204,6 @@ void attn_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[dt][qt][e] = 0.f;
 
-    unsigned char* vbuf0 = smem + wave * 2 * C::VBUF;
 
     // ---- item description (wave-uniform: lives in SGPRs)
     struct Item {
@@ -292,33 +301,22 @@ void attn_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
     // 2^kTau. If a tile ever exceeds its reference by more than kTau, the wave
     // raises the reference and restarts its items from zero (each restart
     // raises some reference by more than kTau, so restarts are finite).
-    int t;
-    bool has_prev;
-    int parity;
+    // One pipeline step for the wave's current item `cur` (its K already in
+    // registers), with the V tiles of parity PAR: DMA cur's V into this
+    // parity's tile (its last reader, the PV of the item before the previous
+    // one, has finished), S^T = K Q^T, K loads of the next item, PV of the
+    // previous item (its V arrived during the previous step), softmax of cur.
+    int t = 0;
+    bool has_prev = false;
     Item cur;
-    for (;;) {
-    t = wave;
-    has_prev = false;
-    parity = 0;
-    bool restart = false;
-#pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt)
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[dt][qt][e] = 0.f;
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-        lsum[qt] = 0.f;
-        ltail[qt] = 0.f;
-    }
-    if (t < items) {
-        cur = item_of(t);
-        load_k(cur);
-        dma_v(cur, vbuf0);
-    }
-    for (; t < items; t += 4) {
+    auto step = [&](auto par) -> bool {
+        constexpr int PAR = decltype(par)::value;
+        unsigned char* vcur = (PAR == 0 ? vb0 : vb1) + wave * C::VBUF;
+        const unsigned char* vprev = (PAR == 0 ? vb1 : vb0) + wave * C::VBUF;
+        dma_v(cur, vcur);
         // S^T = K Q^T
+        int qb = qlane;
+        asm volatile("" : "+v"(qb));
         f32x16_t s[2][2];
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
@@ -328,7 +326,7 @@ void attn_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
                 for (int e = 0; e < 16; ++e) s[kt][qt][e] = 0.f;
 #pragma unroll
                 for (int ks = 0; ks < C::KS; ++ks)
-                    s[kt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kreg[kt][ks]), qop(qt, ks), s[kt][qt], 0, 0, 0);
+                    s[kt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kreg[kt][ks]), qop_at(qb, qt, ks), s[kt][qt], 0, 0, 0);
             }
         const bool has_next = t + 4 < items;
         Item nxt = cur;
@@ -337,12 +335,7 @@ void attn_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
             load_k(nxt);
         }
         // O^T += V^T P of the previous item (independent of this item's softmax)
-        if (has_prev) pv(vbuf0 + (parity ^ 1) * C::VBUF);
-        if (has_next) {
-            // the previous item's buffer is free once its reads have returned
-            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-            dma_v(nxt, vbuf0 + (parity ^ 1) * C::VBUF);
-        }
+        if (has_prev) pv(vprev);
 
         // ---- softmax of this item
         const bool virt = cur.vgroup >= 0;
@@ -393,63 +386,90 @@ void attn_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
         bool need = false;
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt) {
-            mx[qt] = fmaxf(mx[qt], __shfl_xor(mx[qt], 32));
+            {   // lanes l and l ^ 32 hold the same query: swap halves and combine
+                const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, mx[qt]),
+                                                                 __builtin_bit_cast(uint32_t, mx[qt]), false, false);
+                mx[qt] = fmaxf(__builtin_bit_cast(float, (uint32_t)sw[0]), __builtin_bit_cast(float, (uint32_t)sw[1]));
+            }
             if (m2[qt] == -INFINITY) m2[qt] = mx[qt];   // first finite max: accumulator still zero
             need |= mx[qt] > m2[qt] + kTau;
         }
         if (__builtin_amdgcn_ballot_w64(need) != 0) {   // ballot is wave-uniform
 #pragma unroll
             for (int qt = 0; qt < 2; ++qt) m2[qt] = fmaxf(m2[qt], mx[qt]);
-            restart = true;
-            break;
+            return true;
         }
+        typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+        const bf16x2v_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+        const float cm = plain ? c2 : 1.0f;
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt) {
             const float muse = m2[qt] == -INFINITY ? 0.f : m2[qt];
             float rs = 0.f;
-            if (plain) {
 #pragma unroll
-                for (int kt = 0; kt < 2; ++kt)
+            for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        const float pe = fast_exp2(fmaf(s[kt][qt][e], c2, -muse));
-                        s[kt][qt][e] = pe;
-                        rs += pe;
+                for (int half = 0; half < 2; ++half) {
+                    uint32_t w[4];
+#pragma unroll
+                    for (int h2 = 0; h2 < 4; ++h2) {
+                        const float p0 = fast_exp2(fmaf(s[kt][qt][8 * half + 2 * h2], cm, -muse));
+                        const float p1 = fast_exp2(fmaf(s[kt][qt][8 * half + 2 * h2 + 1], cm, -muse));
+                        w[h2] = pack_bf16x2(p0, p1);
+                        // row sum of the rounded weights (the ones PV uses)
+                        rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, w[h2]), ones, rs, false);
                     }
-            } else {
-#pragma unroll
-                for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        const float pe = fast_exp2(s[kt][qt][e] - muse);
-                        s[kt][qt][e] = pe;
-                        rs += pe;
-                    }
-            }
+                    pp[kt][half][qt] = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
+                }
             lsum[qt] += rs;
             if (virt) ltail[qt] += rs;
         }
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int half = 0; half < 2; ++half)
-#pragma unroll
-                for (int qt = 0; qt < 2; ++qt) {
-                    uint4 u;
-                    u.x = pack_bf16x2(s[kt][qt][8 * half + 0], s[kt][qt][8 * half + 1]);
-                    u.y = pack_bf16x2(s[kt][qt][8 * half + 2], s[kt][qt][8 * half + 3]);
-                    u.z = pack_bf16x2(s[kt][qt][8 * half + 4], s[kt][qt][8 * half + 5]);
-                    u.w = pack_bf16x2(s[kt][qt][8 * half + 6], s[kt][qt][8 * half + 7]);
-                    pp[kt][half][qt] = as_bf16x8(u);
-                }
         cur = nxt;
         has_prev = true;
-        parity ^= 1;
+        return false;
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    int last_par = 0;
+    for (;;) {
+        t = wave;
+        has_prev = false;
+        last_par = 0;
+        bool restart = false;
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+            for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[dt][qt][e] = 0.f;
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+            lsum[qt] = 0.f;
+            ltail[qt] = 0.f;
+        }
+        if (t < items) {
+            cur = item_of(t);
+            load_k(cur);
+        }
+        while (t < items) {
+            if (step(I0{})) {
+                restart = true;
+                break;
+            }
+            last_par = 0;
+            t += 4;
+            if (t >= items) break;
+            if (step(I1{})) {
+                restart = true;
+                break;
+            }
+            last_par = 1;
+            t += 4;
+        }
+        if (!restart) break;
+        __builtin_amdgcn_s_waitcnt(0);   // drain the abandoned prefetches before reusing the tiles
     }
-    if (!restart) break;
-    __builtin_amdgcn_s_waitcnt(0);   // drain the abandoned prefetches before reusing the buffers
-    }
-    if (has_prev) pv(vbuf0 + (parity ^ 1) * C::VBUF);
+    if (has_prev) pv((last_par == 0 ? vb0 : vb1) + wave * C::VBUF);
 
     // ---- merge the four wave states and finish (Phase 3)
 #pragma unroll
@@ -457,17 +477,23 @@ void attn_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
         lsum[qt] += __shfl_xor(lsum[qt], 32);
         ltail[qt] += __shfl_xor(ltail[qt], 32);
     }
-    __syncthreads();   // every wave is done with its V buffers
-    float* mo = reinterpret_cast<float*>(smem);
-    float* ms = mo + 4 * C::DT * 2 * 16 * 64;
-    float* ls = ms + 4 * 64;
-    float* lts = ls + 4 * 64;
+    __syncthreads();   // every wave is done with its V tiles
+    // wave w's O^T goes to the tile array of parity w / 2 (two waves per array)
+    auto mo_of = [&](int w) {
+        return reinterpret_cast<float*>(w < 2 ? vb0 : vb1) + (w & 1) * (C::DT * 2 * 16 * 64);
+    };
+    float* ms = mstat;
+    float* ls = mstat + 4 * 64;
+    float* lts = mstat + 8 * 64;
+    {
+        float* mo = mo_of(wave);
 #pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt)
+        for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt)
+            for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) mo[(((wave * C::DT + dt) * 2 + qt) * 16 + e) * 64 + lane] = acc[dt][qt][e];
+                for (int e = 0; e < 16; ++e) mo[((dt * 2 + qt) * 16 + e) * 64 + lane] = acc[dt][qt][e];
+    }
     if (g == 0) {
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt) {
@@ -529,7 +555,7 @@ void attn_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
         for (int e = 0; e < 16; ++e) {
             float a = 0.f;
 #pragma unroll
-            for (int w = 0; w < 4; ++w) a = fmaf(f[w], mo[(((w * C::DT + dt) * 2 + qt) * 16 + e) * 64 + lane], a);
+            for (int w = 0; w < 4; ++w) a = fmaf(f[w], mo_of(w)[((dt * 2 + qt) * 16 + e) * 64 + lane], a);
             out[e] = (a + cF * gacc[qt][e]) * inv;
         }
         const int trow_o = i * 64 + qi;

@@ -15,8 +15,10 @@
 //   2. Per row (one wave), a radix select over order-preserving 32-bit keys
 //      finds tau~, the topk-th largest r~. Blocks with r~ > tau~ + 2 eps are
 //      in Top_i; blocks with r~ < tau~ - 2 eps are out; the few in between
-//      are ranked exactly: their r_ij is recomputed in fp64 and a second radix
-//      select on 64-bit keys (ties: lower j) picks the remaining members.
+//      (close calls) are ranked exactly: each one's r_ij is recomputed once in
+//      fp64 and the remaining members are those of smallest rank (ties: lower
+//      j). Rows with more than kAmbCap close calls use a 64-bit radix select
+//      over the fp64 scores instead.
 //   3. Ids are written ascending, -1 padded.
 // The gate of the second-order term is decided the same way (fp32, with an
 // fp64 recomputation within the error bound of ln B) and the gated w table is
@@ -29,7 +31,8 @@ namespace pisa {
 namespace {
 
 constexpr int kQB = 16;               // query blocks per workgroup
-constexpr int kFastMaxN = 1920;       // 16 score rows of N fp32 fit in LDS
+constexpr int kAmbCap = 64;           // close calls ranked pairwise per row (more: radix select)
+constexpr int kLdsMax = 160 * 1024;   // LDS of a gfx950 workgroup
 constexpr double kU = 5.9604644775390625e-08;   // 2^-24
 
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f4_t;
@@ -115,16 +118,30 @@ __device__ __forceinline__ Key wave_radix_select(int n, int need, KeyFn key, Tak
     return prefix;
 }
 
+// LDS of the fast kernel: fp64 pooled query statistics, fp32 score rows of
+// pitch NP, per-wave radix histograms, close-call lists and taken-bit masks.
+__host__ __device__ inline int fast_np(int N) { return (N + 3) & ~3; }
+__host__ __device__ inline size_t fast_lds_bytes(int D, int N, int second_order) {
+    const int NP = fast_np(N);
+    return (size_t)8 * kQB * D * (second_order ? 2 : 1) + (size_t)4 * kQB * NP + 4 * 4 * 256 +
+           (size_t)4 * kAmbCap * (4 + 8) + (size_t)4 * 4 * ((NP + 31) / 32);
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void route_fast_kernel(
     const double* __restrict__ qbar, const double* __restrict__ q2bar, const double* __restrict__ kbar,
     const double* __restrict__ ksig2, int N, double s64, int topk, int band, int second_order,
     int32_t* __restrict__ idx, float* __restrict__ wgate) {
     constexpr int KS = D / 4;       // 16x16x4 k-steps; MFMA k-slot (ks, l/16) <-> dim (D/4)(l/16) + ks
-    __shared__ double qb_s[kQB * D];
-    __shared__ double q2_s[kQB * D];
-    __shared__ float score_s[kQB * kFastMaxN];
-    __shared__ unsigned hist_s[4 * 256];
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+    const int NP = fast_np(N), NW = (NP + 31) / 32;
+    double* qb_s = reinterpret_cast<double*>(lds);
+    double* q2_s = qb_s + kQB * D;                                   // second order only
+    float* score_s = reinterpret_cast<float*>(q2_s + (second_order ? kQB * D : 0));
+    unsigned* hist_s = reinterpret_cast<unsigned*>(score_s + kQB * NP);
+    int* amb_j_s = reinterpret_cast<int*>(hist_s + 4 * 256);
+    double* amb_r_s = reinterpret_cast<double*>(amb_j_s + 4 * kAmbCap);
+    uint32_t* take_s = reinterpret_cast<uint32_t*>(amb_r_s + 4 * kAmbCap);
     __shared__ float kmax_s[4];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -140,7 +157,7 @@ __global__ __launch_bounds__(kThreads) void route_fast_kernel(
         const int r = e / D;
         const int64_t o = (bh * N + i0 + r) * (int64_t)D + e % D;
         qb_s[e] = r < nq ? qbar[o] : 0.0;
-        q2_s[e] = (second_order && r < nq) ? q2bar[o] : 0.0;
+        if (second_order) q2_s[e] = r < nq ? q2bar[o] : 0.0;
     }
     __syncthreads();
 
@@ -199,7 +216,7 @@ __global__ __launch_bounds__(kThreads) void route_fast_kernel(
                 wgate[(bh * N + i0 + r) * (int64_t)N + col] = wg;
                 sc += fminf(w, lnBf);
             }
-            if (ok) score_s[r * kFastMaxN + col] = sc;
+            if (ok) score_s[r * NP + col] = sc;
         }
     }
     kmax2 = fmaxf(kmax2, __shfl_xor(kmax2, 1));
@@ -213,13 +230,17 @@ __global__ __launch_bounds__(kThreads) void route_fast_kernel(
 
     // ---- selection: wave w handles rows w, w+4, w+8, w+12
     unsigned* hist = hist_s + wave * 256;
+    int* amb_j = amb_j_s + wave * kAmbCap;
+    double* amb_r = amb_r_s + wave * kAmbCap;
+    uint32_t* tbits = take_s + wave * NW;
+    const unsigned long long lt_mask = (1ull << lane) - 1ull;
     for (int r = wave; r < nq; r += 4) {
         const int i = i0 + r;
         int32_t* out = idx + (bh * N + i) * (int64_t)topk;
         const int blo = max(0, i - band), bhi = min(N - 1, i + band);
         const int ncand = N - (bhi - blo + 1);
         const int k = min(topk, ncand);
-        const float* sr = score_s + r * kFastMaxN;
+        const float* sr = score_s + r * NP;
         auto is_cand = [&](int j) { return j < blo || j > bhi; };
         int written = 0;
         if (k > 0) {
@@ -234,16 +255,22 @@ __global__ __launch_bounds__(kThreads) void route_fast_kernel(
                 N, k, [&](int j) { return key32(sr[j]); }, is_cand, hist, &need_eq);
             const float tau = unkey32(tk);
             const float hi_thr = tau + 2.f * eps, lo_thr = tau - 2.f * eps;
+            // certain members (above the band around tau) and the close calls
+            // inside it, the latter listed in ascending j
             int cg = 0, ca = 0;
-            for (int j = lane; j < N; j += 64) {
-                if (!is_cand(j)) continue;
-                const float x = sr[j];
-                cg += x > hi_thr;
-                ca += (x >= lo_thr && x <= hi_thr);
+            for (int base = 0; base < N; base += 64) {
+                const int j = base + lane;
+                const bool cand = j < N && is_cand(j);
+                const float x = cand ? sr[j] : 0.f;
+                const bool in = cand && x > hi_thr;
+                const bool amb = cand && !in && x >= lo_thr;
+                cg += __popcll(__ballot(in));
+                const unsigned long long am = __ballot(amb);
+                const int pos = ca + __popcll(am & lt_mask);
+                if (amb && pos < kAmbCap) amb_j[pos] = j;
+                ca += __popcll(am);
             }
-            cg = wave_sum(cg);
-            ca = wave_sum(ca);
-            const int need = k - cg;      // members still to choose among the ambiguous ones
+            const int need = k - cg;      // members still to choose among the close calls
             auto exact = [&](int j) {     // fp64 score of block j
                 const double* kr = kb + (int64_t)j * D;
                 double dot = 0.0;
@@ -261,12 +288,39 @@ __global__ __launch_bounds__(kThreads) void route_fast_kernel(
                 const float x = sr[j];
                 return is_cand(j) && x >= lo_thr && x <= hi_thr;
             };
+            // mode 0: every close call is in; 1: taken-bit mask; 2: 64-bit radix threshold
+            const int mode = need >= ca ? 0 : (ca <= kAmbCap ? 1 : 2);
             uint64_t t64 = 0;
             int eq_need = 0;
-            const bool all_amb = need >= ca;   // every ambiguous block is in
-            if (need > 0 && !all_amb)
+            if (need > 0 && mode == 1) {
+                // score each close call once in fp64, then rank them (ties: lower j)
+                for (int w = lane; w < NW; w += 64) tbits[w] = 0u;
+                double rmine = 0.0;
+                int jmine = -1;
+                if (lane < ca) {
+                    jmine = amb_j[lane];
+                    rmine = exact(jmine);
+                    amb_r[lane] = rmine;
+                }
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                if (lane < ca) {
+                    int rank = 0;
+                    for (int b = 0; b < ca; ++b) {
+                        const double rb = amb_r[b];
+                        const int jb = amb_j[b];
+                        rank += (rb > rmine) || (rb == rmine && jb < jmine);
+                    }
+                    if (rank < need) atomicOr(&tbits[jmine >> 5], 1u << (jmine & 31));
+                }
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            } else if (need > 0 && mode == 2) {
                 t64 = wave_radix_select<uint64_t, 64>(
                     N, need, [&](int j) { return key64(exact(j)); }, ambiguous, hist, &eq_need);
+            }
             // write ascending
             int eq_seen = 0;
             for (int base = 0; base < N; base += 64) {
@@ -278,8 +332,10 @@ __global__ __launch_bounds__(kThreads) void route_fast_kernel(
                     if (x > hi_thr) {
                         take = true;
                     } else if (x >= lo_thr && need > 0) {
-                        if (all_amb) {
+                        if (mode == 0) {
                             take = true;
+                        } else if (mode == 1) {
+                            take = (tbits[j >> 5] >> (j & 31)) & 1u;
                         } else {
                             const uint64_t kk = key64(exact(j));
                             take = kk > t64;
@@ -288,11 +344,11 @@ __global__ __launch_bounds__(kThreads) void route_fast_kernel(
                     }
                 }
                 const unsigned long long eqm = __ballot(eq);
-                const int eq_before = __popcll(eqm & ((1ull << lane) - 1ull));
+                const int eq_before = __popcll(eqm & lt_mask);
                 if (eq && eq_seen + eq_before < eq_need) take = true;
                 eq_seen += __popcll(eqm);
                 const unsigned long long tm = __ballot(take);
-                const int pos = __popcll(tm & ((1ull << lane) - 1ull));
+                const int pos = __popcll(tm & lt_mask);
                 if (take && written + pos < topk) out[written + pos] = j;
                 written += __popcll(tm);
             }
@@ -301,7 +357,7 @@ __global__ __launch_bounds__(kThreads) void route_fast_kernel(
     }
 }
 
-// General fallback for long sequences (N > kFastMaxN): one workgroup per
+// General fallback for long sequences (score rows beyond the LDS): one workgroup per
 // query block, fp64 scores of every candidate, radix select on 64-bit keys.
 constexpr int kMaxN = 8192;
 
@@ -425,10 +481,22 @@ hipError_t launch_route_topk(const Geom& g, const pisa_params_t* p, const pisa_s
     const int so = p->second_order;
     if (p->topk == 0 && !so) return hipSuccess;
     dim3 block(kThreads);
-    if (g.N <= kFastMaxN) {
+    const size_t lds = fast_lds_bytes(g.D, g.N, so);
+    if (lds + 64 <= (size_t)kLdsMax) {
+        static bool attr_set[2] = {false, false};   // opt in to more than 64 KB of dynamic LDS
+        bool& set = attr_set[g.D == 128];
+        if (!set) {
+            const hipError_t e = g.D == 128
+                ? hipFuncSetAttribute(reinterpret_cast<const void*>(&route_fast_kernel<128>),
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax - 64)
+                : hipFuncSetAttribute(reinterpret_cast<const void*>(&route_fast_kernel<64>),
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax - 64);
+            if (e != hipSuccess) return e;
+            set = true;
+        }
         dim3 grid((g.N + kQB - 1) / kQB, (unsigned)g.BH);
 #define PISA_ROUTE_LAUNCH(DD)                                                                      \
-    hipLaunchKernelGGL(route_fast_kernel<DD>, grid, block, 0, stream, st->qbar, st->q2bar,         \
+    hipLaunchKernelGGL(route_fast_kernel<DD>, grid, block, lds, stream, st->qbar, st->q2bar,       \
                        st->kbar, st->ksig2, g.N, g.scale64, p->topk, p->band, so, idx, wgate)
         if (g.D == 128) PISA_ROUTE_LAUNCH(128);
         else PISA_ROUTE_LAUNCH(64);

@@ -127,12 +127,13 @@ __host__ __device__ inline size_t fast_lds_bytes(int D, int N, int second_order)
            (size_t)4 * kAmbCap * (4 + 8) + (size_t)4 * 4 * ((NP + 31) / 32);
 }
 
-template <int D>
+template <int D, bool SO>
 __global__ __launch_bounds__(kThreads) void route_fast_kernel(
     const double* __restrict__ qbar, const double* __restrict__ q2bar, const double* __restrict__ kbar,
-    const double* __restrict__ ksig2, int N, double s64, int topk, int band, int second_order,
+    const double* __restrict__ ksig2, int N, double s64, int topk, int band,
     int32_t* __restrict__ idx, float* __restrict__ wgate) {
     constexpr int KS = D / 4;       // 16x16x4 k-steps; MFMA k-slot (ks, l/16) <-> dim (D/4)(l/16) + ks
+    constexpr bool second_order = SO;
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     const int NP = fast_np(N), NW = (NP + 31) / 32;
     double* qb_s = reinterpret_cast<double*>(lds);
@@ -161,36 +162,60 @@ __global__ __launch_bounds__(kThreads) void route_fast_kernel(
     }
     __syncthreads();
 
-    // ---- scores: S[r][j] = s qbar_r . kbar_j (+ min(w, ln B)) via fp32 MFMA
+    // ---- scores: S[r][j] = s qbar_r . kbar_j (+ min(w, ln B)) via fp32 MFMA.
+    // Wave w takes the 16-column chunks c = w, w+4, ...; lane (m16, g4) needs
+    // kbar[16 c + m16][(D/4) g4 + ks] for ks < KS: KS/2 contiguous 16-byte
+    // loads, issued one chunk ahead of the MFMAs that use them.
+    typedef double d2_t __attribute__((ext_vector_type(2)));
     const int m16 = lane & 15, g4 = lane >> 4;
     float a[KS], a2[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
         a[ks] = (float)qb_s[m16 * D + (D / 4) * g4 + ks];
-        a2[ks] = second_order ? (float)q2_s[m16 * D + (D / 4) * g4 + ks] : 0.f;
+        a2[ks] = SO ? (float)q2_s[m16 * D + (D / 4) * g4 + ks] : 0.f;
     }
     const double* kb = kbar + bh * (int64_t)N * D;
-    const double* sg = second_order ? ksig2 + bh * (int64_t)N * D : nullptr;
+    const double* sg = SO ? ksig2 + bh * (int64_t)N * D : nullptr;
     float kmax2 = 0.f;
     const int NC = (N + 15) / 16;
+    auto kptr = [&](const double* base, int c) {   // this lane's 16-byte-aligned run of chunk c
+        const int col = min(c * 16 + m16, N - 1);
+        return reinterpret_cast<const d2_t*>(base + (int64_t)col * D + (D / 4) * g4);
+    };
+    d2_t kv[KS / 2];
+    if (wave < NC) {
+        const d2_t* src = kptr(kb, wave);
+#pragma unroll
+        for (int h = 0; h < KS / 2; ++h) kv[h] = src[h];
+    }
     for (int c = wave; c < NC; c += 4) {
         const int col = c * 16 + m16;
         const bool ok = col < N;
-        const double* kr = kb + (int64_t)(ok ? col : N - 1) * D + (D / 4) * g4;
+        float b[KS];
+#pragma unroll
+        for (int h = 0; h < KS / 2; ++h) {
+            b[2 * h] = ok ? (float)kv[h].x : 0.f;
+            b[2 * h + 1] = ok ? (float)kv[h].y : 0.f;
+        }
+        if (c + 4 < NC) {   // prefetch the next chunk
+            const d2_t* src = kptr(kb, c + 4);
+#pragma unroll
+            for (int h = 0; h < KS / 2; ++h) kv[h] = src[h];
+        }
         f4_t acc = {0.f, 0.f, 0.f, 0.f}, accw = {0.f, 0.f, 0.f, 0.f};
         float n2 = 0.f;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const float b = ok ? (float)kr[ks] : 0.f;
-            n2 = fmaf(b, b, n2);
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[ks], b, acc, 0, 0, 0);
+            n2 = fmaf(b[ks], b[ks], n2);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[ks], b[ks], acc, 0, 0, 0);
         }
-        if (second_order) {
-            const double* sr = sg + (int64_t)(ok ? col : N - 1) * D + (D / 4) * g4;
+        if (SO) {
+            const d2_t* src = kptr(sg, c);
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const float b = ok ? (float)sr[ks] : 0.f;
-                accw = __builtin_amdgcn_mfma_f32_16x16x4f32(a2[ks], b, accw, 0, 0, 0);
+            for (int h = 0; h < KS / 2; ++h) {
+                const d2_t x = src[h];
+                accw = __builtin_amdgcn_mfma_f32_16x16x4f32(a2[2 * h], ok ? (float)x.x : 0.f, accw, 0, 0, 0);
+                accw = __builtin_amdgcn_mfma_f32_16x16x4f32(a2[2 * h + 1], ok ? (float)x.y : 0.f, accw, 0, 0, 0);
             }
         }
         n2 += __shfl_xor(n2, 16);
@@ -201,7 +226,7 @@ __global__ __launch_bounds__(kThreads) void route_fast_kernel(
         for (int e = 0; e < 4; ++e) {
             const int r = 4 * g4 + e;
             float sc = (float)s64 * acc[e];
-            if (second_order && ok && r < nq) {
+            if (SO && ok && r < nq) {
                 const float w = 0.5f * accw[e];
                 const float ew = 2.0f * (float)((D + 4) * kU) * w + 1e-30f;
                 float wg;
@@ -483,24 +508,19 @@ hipError_t launch_route_topk(const Geom& g, const pisa_params_t* p, const pisa_s
     dim3 block(kThreads);
     const size_t lds = fast_lds_bytes(g.D, g.N, so);
     if (lds + 64 <= (size_t)kLdsMax) {
-        static bool attr_set[2] = {false, false};   // opt in to more than 64 KB of dynamic LDS
-        bool& set = attr_set[g.D == 128];
-        if (!set) {
-            const hipError_t e = g.D == 128
-                ? hipFuncSetAttribute(reinterpret_cast<const void*>(&route_fast_kernel<128>),
-                                      hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax - 64)
-                : hipFuncSetAttribute(reinterpret_cast<const void*>(&route_fast_kernel<64>),
-                                      hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax - 64);
+        static bool attr_set[2][2] = {{false, false}, {false, false}};
+        bool& set = attr_set[g.D == 128][so ? 1 : 0];
+        auto fn = g.D == 128 ? (so ? &route_fast_kernel<128, true> : &route_fast_kernel<128, false>)
+                             : (so ? &route_fast_kernel<64, true> : &route_fast_kernel<64, false>);
+        if (!set) {   // opt in to more than 64 KB of dynamic LDS
+            const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax - 64);
             if (e != hipSuccess) return e;
             set = true;
         }
         dim3 grid((g.N + kQB - 1) / kQB, (unsigned)g.BH);
-#define PISA_ROUTE_LAUNCH(DD)                                                                      \
-    hipLaunchKernelGGL(route_fast_kernel<DD>, grid, block, lds, stream, st->qbar, st->q2bar,       \
-                       st->kbar, st->ksig2, g.N, g.scale64, p->topk, p->band, so, idx, wgate)
-        if (g.D == 128) PISA_ROUTE_LAUNCH(128);
-        else PISA_ROUTE_LAUNCH(64);
-#undef PISA_ROUTE_LAUNCH
+        hipLaunchKernelGGL(fn, grid, block, lds, stream, st->qbar, st->q2bar, st->kbar, st->ksig2, g.N,
+                           g.scale64, p->topk, p->band, idx, wgate);
     } else {
         dim3 grid(g.N, (unsigned)g.BH);
 #define PISA_ROUTE_LAUNCH(DD)                                                                      \

@@ -31,6 +31,77 @@ import numpy as np
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, datasheet
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, datasheet
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
+ATTN_SRC = os.path.join(ROOT, "block_sparse_taylor_amd", "csrc", "attn_mfma.hip")
+ATTN_KERNEL = "attn_mfma_kernel"
+COPY_KERNEL = "elementwise"            # torch's elementwise kernel used as the calibration copy
+COPY_BYTES = 1 << 30                   # bytes read (and written) per calibration copy
+
+
+def traffic_file(workload):
+    return os.path.join(ROOT, "profiles", f"attn_mfma_{workload}_traffic.json")
+
+
+def source_digest():
+    import hashlib
+    with open(ATTN_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def load_traffic(workload):
+    """HBM bytes per launch of the fused kernel recorded from counters, if they
+    were taken on the current kernel source (else None)."""
+    try:
+        with open(traffic_file(workload)) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != source_digest():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def _pmc_means(path, counter):
+    """Mean counter value per dispatch for the fused kernel and the calibration copy."""
+    import csv
+    vals = {"attn": [], "copy": []}
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            if row.get("Counter_Name") != counter:
+                continue
+            name = row.get("Kernel_Name", "")
+            key = "attn" if ATTN_KERNEL in name else ("copy" if COPY_KERNEL in name else None)
+            if key:
+                vals[key].append(float(row["Counter_Value"]))
+    if not vals["attn"] or not vals["copy"]:
+        raise SystemExit(f"{path}: no {counter} rows for {ATTN_KERNEL} and the calibration copy")
+    return float(np.mean(vals["attn"])), float(np.mean(vals["copy"])), len(vals["attn"])
+
+
+def record_traffic(fetch_csv, write_csv, workload):
+    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch)
+    into HBM bytes per launch of the fused kernel, each counter scaled by what it
+    reads for a plain copy of COPY_BYTES."""
+    fa, fc, nf = _pmc_means(fetch_csv, "FETCH_SIZE")
+    wa, wc, nw = _pmc_means(write_csv, "WRITE_SIZE")
+    kf = fc * 1024.0 / COPY_BYTES      # counter bytes per true byte read
+    kw = wc * 1024.0 / COPY_BYTES
+    rec = {
+        "workload": workload,
+        "kernel": ATTN_KERNEL,
+        "source_sha256": source_digest(),
+        "fetch_kib_per_launch": fa, "write_kib_per_launch": wa, "dispatches": [nf, nw],
+        "copy_fetch_kib": fc, "copy_write_kib": wc, "copy_bytes": COPY_BYTES,
+        "fetch_scale": kf, "write_scale": kw,
+        "hbm_read_bytes_per_launch": fa * 1024.0 / kf,
+        "hbm_write_bytes_per_launch": wa * 1024.0 / kw,
+        "hbm_bytes_per_launch": fa * 1024.0 / kf + wa * 1024.0 / kw,
+    }
+    with open(traffic_file(workload), "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec))
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -41,11 +112,20 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=8,
                     help="heads the oracle evaluates for the CPU baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed steps, run a plain copy of COPY_BYTES three times "
+                         "(the reference kernel for the HBM byte counters)")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU run: derive the fused kernel's HBM bytes per launch from two "
+                         "rocprofv3 --pmc counter_collection.csv files and record them")
     return ap.parse_args()
 
 
 def main():
     args = parse()
+    if args.record_traffic:
+        record_traffic(args.record_traffic[0], args.record_traffic[1], args.workload)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
               "the operator shards by (batch, head) with no exchange, see the design notes",
@@ -170,9 +250,17 @@ def main():
                             "frac_hbm": round(route_bytes / (route_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "kernel": "attn_mfma_kernel (pisa_attn_fwd)"},
+                     "traffic": load_traffic(w.name), "kernel": "attn_mfma_kernel (pisa_attn_fwd)"},
         "input_generation_s": round(gen_s, 1),
     }
+
+    if args.copy_calibration:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, qa, ka, va, args.cpu_heads, topk)

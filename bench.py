@@ -32,8 +32,9 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, datasheet
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, datasheet
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-ATTN_SRC = os.path.join(ROOT, "block_sparse_taylor_amd", "csrc", "attn_mfma.hip")
-ATTN_KERNEL = "attn_mfma_kernel"
+ATTN_SRCS = [os.path.join(ROOT, "block_sparse_taylor_amd", "csrc", f)
+             for f in ("attn_mfma.hip", "attn_loop_d128.inc")]
+ATTN_KERNEL = "attn_asm_kernel"        # the fused forward's kernel at head_dim 128
 COPY_KERNEL = "elementwise"            # torch's elementwise kernel used as the calibration copy
 COPY_BYTES = 1 << 30                   # bytes read (and written) per calibration copy
 
@@ -44,8 +45,11 @@ def traffic_file(workload):
 
 def source_digest():
     import hashlib
-    with open(ATTN_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for path in ATTN_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def load_traffic(workload):
@@ -250,7 +254,7 @@ def main():
                             "frac_hbm": round(route_bytes / (route_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": load_traffic(w.name), "kernel": "attn_mfma_kernel (pisa_attn_fwd)"},
+                     "traffic": load_traffic(w.name), "kernel": ATTN_KERNEL + " (pisa_attn_fwd)"},
         "input_generation_s": round(gen_s, 1),
     }
 

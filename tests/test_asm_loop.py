@@ -1,0 +1,51 @@
+"""The inline-assembly item loop of the fused forward is generated: the
+committed include must be exactly what the generator produces."""
+
+import os
+import subprocess
+import sys
+import tempfile
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "block_sparse_taylor_amd", "csrc")
+
+
+def test_generated_loop_is_current():
+    with tempfile.TemporaryDirectory() as d:
+        out = os.path.join(d, "loop.inc")
+        subprocess.run([sys.executable, os.path.join(CSRC, "gen_attn_loop.py"), out], check=True,
+                       capture_output=True)
+        with open(out) as f:
+            fresh = f.read()
+    with open(os.path.join(CSRC, "attn_loop_d128.inc")) as f:
+        committed = f.read()
+    assert fresh == committed, "attn_loop_d128.inc is stale: rerun gen_attn_loop.py"
+
+
+def test_loop_register_plan():
+    with open(os.path.join(CSRC, "attn_loop_d128.inc")) as f:
+        text = f.read()
+    # every explicitly named VGPR lies in the clobbered range v56..v255
+    import re
+    body = text.split("#define PISA_ATTN_LOOP_D128_CLOBBERS")[0]
+    regs = [int(x) for x in re.findall(r"\bv(\d+)\b", body)]
+    regs += [int(a) for a, b in re.findall(r"\bv\[(\d+):(\d+)\]", body)]
+    regs += [int(b) for a, b in re.findall(r"\bv\[(\d+):(\d+)\]", body)]
+    assert min(regs) >= 56 and max(regs) <= 255
+    sregs = [int(x) for x in re.findall(r"\bs(\d+)\b", body)]
+    sregs += [int(x) for pair in re.findall(r"\bs\[(\d+):(\d+)\]", body) for x in pair]
+    assert min(sregs) >= 70 and max(sregs) <= 89
+    # the loop's instruction set: memory is read with vector buffer loads and
+    # LDS reads only; scalar instructions are ALU and control flow
+    ops = set(re.findall(r'^\s*"\s*([a-z_0-9]+)', body, re.M))
+    allowed = {
+        "buffer_load_dwordx4", "ds_read_b128", "ds_read_b64", "ds_read_b64_tr_b16",
+        "s_add_u32", "s_addc_u32", "s_branch", "s_cbranch_scc0", "s_cbranch_scc1",
+        "s_cmp_eq_u32", "s_cmp_ge_u32", "s_cmp_lt_u32", "s_lshl_b32", "s_min_u32",
+        "s_mov_b32", "s_movk_i32", "s_nop", "s_sub_u32", "s_waitcnt",
+        "v_add_f32", "v_add_u32", "v_cmp_eq_f32", "v_cmp_gt_f32", "v_cmp_gt_u32",
+        "v_cndmask_b32", "v_cndmask_b32_e64", "v_cvt_pk_bf16_f32", "v_dot2c_f32_bf16",
+        "v_exp_f32", "v_fma_f32", "v_max3_f32", "v_max_f32", "v_mfma_f32_32x32x16_bf16",
+        "v_mov_b32", "v_mul_f32", "v_permlane32_swap_b32", "v_readfirstlane_b32", "v_xor_b32",
+    }
+    assert ops and ops <= allowed, sorted(ops - allowed)

@@ -220,6 +220,7 @@ def main():
     stats_bytes = (3 * B * H * T * D * e                     # read Q, K, V
                    + BHND * (8 + 8 + 4 + 2 * e)              # qbar, kbar, vsum, kbar_c, vbar_c
                    + (BHND * 16 if so else 0)                # q2bar, ksig2
+                   + (B * H * N * 64 * D * 2 if w.dtype == "bf16" else 0)   # packed K copy
                    + B * H * D * D * 4                       # hsum
                    + 2 * B * H * G * D * D * 4)              # partial H write + read
     route_bytes = (BHND * 16 * (2 if so else 1)              # qbar, kbar (+ q2bar, ksig2)

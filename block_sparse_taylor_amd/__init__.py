@@ -79,10 +79,12 @@ class PisaStats:
     hsum: torch.Tensor      # fp32 [B,H,D,D]
     kbar_c: torch.Tensor    # input dtype [B,H,N,D]
     vbar_c: torch.Tensor
+    kpack: torch.Tensor | None   # bf16 [B,H,N,64*D]: K in the fused kernel's operand order
 
     def as_c(self) -> _lib.Stats:
         return _lib.Stats(_ptr(self.qbar), _ptr(self.q2bar), _ptr(self.kbar), _ptr(self.vsum),
-                          _ptr(self.ksig2), _ptr(self.hsum), _ptr(self.kbar_c), _ptr(self.vbar_c))
+                          _ptr(self.ksig2), _ptr(self.hsum), _ptr(self.kbar_c), _ptr(self.vbar_c),
+                          _ptr(self.kpack))
 
 
 def _contig(*ts):
@@ -104,6 +106,7 @@ def alloc_stats(k: torch.Tensor, second_order: bool) -> PisaStats:
         hsum=torch.empty(B, H, D, D, dtype=torch.float32, device=dev),
         kbar_c=torch.empty(B, H, N, D, dtype=k.dtype, device=dev),
         vbar_c=torch.empty(B, H, N, D, dtype=k.dtype, device=dev),
+        kpack=torch.empty(B, H, N, BLOCK * D, dtype=k.dtype, device=dev) if k.dtype == torch.bfloat16 else None,
     )
 
 

@@ -5,7 +5,8 @@
 
 Register plan inside the block (all explicitly named and declared clobbered,
 so they live across the whole loop): v56-v119 K operands of the current item
-(kreg[kt][ks], loaded one item ahead), v120-v183 the S^T accumulators
+(kreg[kt][ks], loaded one item ahead from the packed copy of K, one
+contiguous 1 KB run per load), v120-v183 the S^T accumulators
 (s[kt][qt]), v184-v215 the bf16 P operands, v216-v231 Q^T operand buffers,
 v232-v243 transposed-V operand buffers, v244-v255 scratch; s70-s89 loop
 state and buffer descriptors. The PV accumulators, the softmax state and the
@@ -66,10 +67,14 @@ def label(name):
 
 
 def rsrc(base, lo, hi, off, nv):
-    # {address = (hi:lo) + off, stride 0, num_records = nv * RB, word 3}
+    # {address = (hi:lo) + off, stride 0, num_records = nv * RB (nv = None:
+    # the whole 64-row block), word 3}
     emit(f"s_add_u32 s{base}, {lo}, s{off}")
     emit(f"s_addc_u32 s{base+1}, {hi}, 0")
-    emit(f"s_lshl_b32 s{base+2}, s{nv}, 8")
+    if nv is None:
+        emit(f"s_movk_i32 s{base+2}, {64 * RB}")
+    else:
+        emit(f"s_lshl_b32 s{base+2}, s{nv}, 8")
     emit(f"s_mov_b32 s{base+3}, 0x00020000")
 
 
@@ -81,9 +86,18 @@ def dma(i, vl):
     emit(f"buffer_load_dwordx4 %[voff], {SR(S_VRS)}, s{S_SOFF} offen lds")
 
 
+def kload_lines(kt, ks):
+    # packed K: k-step ks of key tile kt (chunks 2 ks, 2 ks + 1 of its 32 rows)
+    # is the contiguous 1 KB run at 8192 kt + 1024 ks; lane l reads its 16
+    # bytes at 16 l (%[koff])
+    off = 1024 * (KS * kt + ks)
+    return [f"s_movk_i32 s{S_Y}, {off & ~4095}",
+            f"buffer_load_dwordx4 {kreg(kt, ks)}, %[koff], {SR(S_KRS)}, s{S_Y} offen offset:{off & 4095}"]
+
+
 def kload(kt, ks):
-    emit(f"s_movk_i32 s{S_Y}, {kt * 32 * RB}")
-    emit(f"buffer_load_dwordx4 {kreg(kt, ks)}, %[koff], {SR(S_KRS)}, s{S_Y} offen offset:{32 * ks}")
+    for ln in kload_lines(kt, ks):
+        emit(ln)
 
 
 def qread(qt, ks, buf):
@@ -181,9 +195,7 @@ def phase_a_ops(vl):
     for ks in range(KS):
         for kt in range(2):
             last_reader = max(idx[(kt, qt, ks)] for qt in range(2))
-            kls.append(Op("vmem", [f"s_movk_i32 s{S_Y}, {kt * 32 * RB}",
-                                   f"buffer_load_dwordx4 {kreg(kt, ks)}, %[koff], {SR(S_KRS)}, s{S_Y} offen offset:{32 * ks}"],
-                          after=last_reader + 1))
+            kls.append(Op("vmem", kload_lines(kt, ks), after=last_reader + 1))
     # DMA first (no constraint), the K loads as their registers free up
     oth = dmas + kls
     return mf, lds, oth
@@ -289,7 +301,7 @@ def step(par, first):
     emit(f"v_readfirstlane_b32 s{S_NNV}, {t(1)}")
     emit("s_nop 1")
     rsrc(S_VRS, "%[vb_lo]", "%[vb_hi]", S_OFF, S_NV)
-    rsrc(S_KRS, "%[kb_lo]", "%[kb_hi]", S_NOFF, S_NNV)
+    rsrc(S_KRS, "%[kb_lo]", "%[kb_hi]", S_NOFF, None)
     emit(f"s_mov_b32 s{S_NVC}, s{S_NV}")
     # prefetch the list entry after next (used by the next step)
     emit(f"s_add_u32 s{S_X}, s{S_N}, 2")
@@ -336,7 +348,7 @@ def program():
     emit(f"v_readfirstlane_b32 s{S_OFF}, {t(0)}")
     emit(f"v_readfirstlane_b32 s{S_NV}, {t(1)}")
     emit("s_nop 1")
-    rsrc(S_KRS, "%[kb_lo]", "%[kb_hi]", S_OFF, S_NV)
+    rsrc(S_KRS, "%[kb_lo]", "%[kb_hi]", S_OFF, None)
     for kt in range(2):
         for ks in range(KS):
             kload(kt, ks)

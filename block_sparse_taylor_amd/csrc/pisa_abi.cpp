@@ -55,7 +55,7 @@ pisa_status_t check_ptr(const void* p) {
         if (st_ != PISA_OK) return st_;       \
     } while (0)
 
-pisa_status_t check_stats(const pisa_stats_t* st, int second_order, bool need_c) {
+pisa_status_t check_stats(const pisa_stats_t* st, int second_order, bool need_c, bool need_kpack) {
     if (!st) return PISA_ERR_NULL;
     PISA_TRY(check_ptr(st->kbar));
     PISA_TRY(check_ptr(st->vsum));
@@ -64,6 +64,7 @@ pisa_status_t check_stats(const pisa_stats_t* st, int second_order, bool need_c)
         PISA_TRY(check_ptr(st->kbar_c));
         PISA_TRY(check_ptr(st->vbar_c));
     }
+    if (need_kpack) PISA_TRY(check_ptr(st->kpack));
     if (second_order) PISA_TRY(check_ptr(st->ksig2));
     else if (st->ksig2 && !aligned16(st->ksig2)) return PISA_ERR_ALIGN;
     return PISA_OK;
@@ -80,7 +81,7 @@ pisa_status_t attn_common(const pisa_shape_t* shape, const pisa_params_t* params
     PISA_TRY(check_ptr(k));
     PISA_TRY(check_ptr(v));
     PISA_TRY(check_ptr(o));
-    PISA_TRY(check_stats(stats, 0, shape->dtype == PISA_BF16));
+    PISA_TRY(check_stats(stats, 0, shape->dtype == PISA_BF16, shape->dtype == PISA_BF16));
     if (params->topk > 0) PISA_TRY(check_ptr(idx));
     if (params->second_order) PISA_TRY(check_ptr(wgate));
     if (o == q || o == k || o == v) return PISA_ERR_PARAM;
@@ -129,7 +130,7 @@ pisa_status_t pisa_block_stats(const pisa_shape_t* shape, const pisa_params_t* p
     PISA_TRY(check_ptr(q));
     PISA_TRY(check_ptr(k));
     PISA_TRY(check_ptr(v));
-    PISA_TRY(check_stats(out, params->second_order, true));
+    PISA_TRY(check_stats(out, params->second_order, true, shape->dtype == PISA_BF16));
     PISA_TRY(check_ptr(out->qbar));
     if (params->second_order) PISA_TRY(check_ptr(out->q2bar));
     PISA_TRY(check_ptr(workspace));

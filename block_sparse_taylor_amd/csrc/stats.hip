@@ -33,6 +33,7 @@ struct StatsOut {
     double* ksig2;
     void* kbar_c;
     void* vbar_c;
+    void* kpack;      // bf16 only: K in the fused kernel's operand order
 };
 
 // Column statistics of one block from its LDS tiles (row pitch ld).
@@ -172,6 +173,21 @@ __global__ __launch_bounds__(kThreads) void stats_bf16_kernel(
         __syncthreads();
         if (j + 1 < j1) fetch(j + 1);
 
+        // K of this block in the fused kernel's operand order: for each 32-row
+        // half, the 16-byte chunks (8 dims) chunk-major, then row, so that one
+        // 1 KB run holds a chunk pair of all 32 rows (rows past T are zero).
+        {
+            uint4* kp = reinterpret_cast<uint4*>(out.kpack) + (bh * N + j) * (int64_t)(kBlock * CH);
+#pragma unroll
+            for (int L = 0; L < LOADS; ++L) {
+                const int c = L * kThreads + tid;
+                const int half = c / (32 * CH), ch = (c / 32) % CH, r = c % 32;
+                const uint2* src = reinterpret_cast<const uint2*>(sk + (32 * half + r) * LD + ch * 8);
+                const uint2 lo = src[0], hi = src[1];
+                kp[c] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+            }
+        }
+
         // acc += K_j^T V_j  (rows >= `rows` are zero in LDS)
         const int m = lane & 31, hi = lane >> 5;
 #pragma unroll
@@ -303,7 +319,7 @@ hipError_t launch_block_stats(const Geom& g, int dtype, int second_order, const 
     const int G = stats_groups(g);
     dim3 grid(G, (unsigned)g.BH), block(kThreads);
     float* hpart = static_cast<float*>(workspace);
-    StatsOut out{st->qbar, st->q2bar, st->kbar, st->vsum, st->ksig2, st->kbar_c, st->vbar_c};
+    StatsOut out{st->qbar, st->q2bar, st->kbar, st->vsum, st->ksig2, st->kbar_c, st->vbar_c, st->kpack};
 #define PISA_STATS_LAUNCH(KERN, TT, DD)                                                            \
     hipLaunchKernelGGL(KERN<DD>, grid, block, 0, stream, static_cast<const TT*>(q),               \
                        static_cast<const TT*>(k), static_cast<const TT*>(v), g.T, g.N,            \

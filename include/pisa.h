@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define PISA_ABI_VERSION 1
+#define PISA_ABI_VERSION 2
 
 typedef enum {
     PISA_OK = 0,
@@ -99,6 +99,12 @@ typedef struct {
  * qbar, kbar, q2bar and ksig2 are fp64 so that routing decisions (a top-k, a
  * gate) match a float64 evaluation; kbar_c / vbar_c feed the virtual tokens.
  * q2bar and ksig2 may be NULL unless params.second_order.
+ * kpack (bf16 inputs; ignored for fp32) is K re-ordered for the fused
+ * kernel's matrix-core operands, bf16 [B,H,N,64*D]: within block j, for each
+ * 32-row half h, chunk c (dims 8c..8c+7) and row r,
+ *   kpack[b,h,j][((h * D/8 + c) * 32 + r) * 8 + e] = k[b,h,64 j + 32 h + r][8 c + e],
+ * and 0 for rows past seq_len. It is not one of the paper's statistics: it
+ * lets every 64-lane load of the fused kernel read one contiguous 1 KB run.
  */
 typedef struct {
     double *qbar;
@@ -109,6 +115,7 @@ typedef struct {
     float *hsum;
     void *kbar_c;
     void *vbar_c;
+    void *kpack;
 } pisa_stats_t;
 
 /* ABI version of the library (PISA_ABI_VERSION). */
@@ -169,7 +176,8 @@ pisa_status_t pisa_route_topk(const pisa_shape_t *shape, const pisa_params_t *pa
  * pisa_route_topk writes them: valid ids first, -1 only after them). o: [B,H,T,D] in the input dtype; must not
  * alias q, k, v. bf16 runs compute QK^T and PV with bf16 MFMA (fp32
  * accumulation, P rounded to bf16); fp32 runs compute in fp32.
- * Reads stats->kbar_c, vbar_c, vsum (fp32 path), kbar (fp32 path), hsum.
+ * Reads stats->kbar_c, vbar_c, kpack (bf16), vsum (fp32 path), kbar (fp32
+ * path), hsum.
  */
 pisa_status_t pisa_attn_fwd(const pisa_shape_t *shape, const pisa_params_t *params,
                             const void *q, const void *k, const void *v,

@@ -32,7 +32,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pisa_abi_version() == 1
+    assert lib.pisa_abi_version() == 2
     for code in range(9):
         assert lib.pisa_status_str(code)
     assert lib.pisa_status_str(99) == b"unknown status"
@@ -68,7 +68,8 @@ MIS = FAKE + 4
 
 
 def stats(**kw):
-    d = dict(qbar=FAKE, q2bar=None, kbar=FAKE, vsum=FAKE, ksig2=None, hsum=FAKE, kbar_c=FAKE, vbar_c=FAKE)
+    d = dict(qbar=FAKE, q2bar=None, kbar=FAKE, vsum=FAKE, ksig2=None, hsum=FAKE, kbar_c=FAKE, vbar_c=FAKE,
+             kpack=FAKE)
     d.update(kw)
     return _lib.Stats(**d)
 
@@ -107,6 +108,9 @@ def test_stats_validation(lib):
     assert call_stats(lib, s=shape(D=32)) == E["PISA_ERR_SHAPE"]
     assert call_stats(lib, st=stats(hsum=None)) == E["PISA_ERR_NULL"]
     assert call_stats(lib, st=stats(kbar_c=MIS)) == E["PISA_ERR_ALIGN"]
+    # kpack: required for bf16 inputs, ignored for fp32
+    assert call_stats(lib, st=stats(kpack=None)) == E["PISA_ERR_NULL"]
+    assert call_stats(lib, st=stats(kpack=MIS)) == E["PISA_ERR_ALIGN"]
     # second order needs ksig2 and q2bar
     assert call_stats(lib, p=_lib.Params(4, 1, 1, 1, 0)) == E["PISA_ERR_NULL"]
     assert call_stats(lib, p=_lib.Params(4, 1, 1, 1, 0), st=stats(ksig2=FAKE)) == E["PISA_ERR_NULL"]
@@ -138,6 +142,7 @@ def test_attn_validation(lib, name):
     assert call_attn(lib, name, idx=None) == E["PISA_ERR_NULL"]
     assert call_attn(lib, name, p=_lib.Params(4, 1, 1, 1, 0)) == E["PISA_ERR_NULL"]   # wgate
     assert call_attn(lib, name, p=_lib.Params(4, 1, 0, 1, 8)) == E["PISA_ERR_PARAM"]  # phase mask
+    assert call_attn(lib, name, st=stats(kpack=None)) == E["PISA_ERR_NULL"]           # bf16 needs kpack
     assert call_attn(lib, name, p=_lib.Params(4, 1, 0, 3, 0)) == E["PISA_ERR_PARAM"]
     assert call_attn(lib, name, st=stats(vbar_c=None)) == E["PISA_ERR_NULL"]
     assert call_attn(lib, name, s=shape(dtype=2)) == E["PISA_ERR_DTYPE"]

@@ -7,7 +7,8 @@ Tolerances (from the operator's specification and the arithmetic):
 * bf16 inputs: max|o - o_ref| <= 2e-2, the oracle fed the GPU's routing.
 * gated second-order table: the gate decision equals float64's; kept values
   within the fp32 dot-product bound 2 (D + 4) u w.
-* statistics: qbar/kbar bit-exact (exact fp64 sums), ksig2 to 1e-12; V-hat is the fp64 sum
+* statistics: qbar/kbar bit-exact (exact fp64 sums), ksig2 to 1e-12; the
+  packed copy of K bit-exact (a re-ordering); V-hat is the fp64 sum
   rounded once to fp32; the bf16 copies are bit-exact roundings; H within
   64 u sum_t |k_ta||v_tb| elementwise (u = 2^-24; fp32 accumulation of
   bf16 products over 2048-row partials, sqrt(n) u growth with a 1.4x margin).
@@ -97,7 +98,15 @@ def test_block_stats(name):
     kbc = run.host(run.st.kbar_c)
     vbc = run.host(run.st.vbar_c)
     ks2 = run.st.ksig2.cpu().numpy() if w.second_order else None
+    kp = run.st.kpack.view(torch.int16).cpu().numpy().view(np.uint16) if w.dtype == "bf16" else None
     for h in heads:
+        if kp is not None:
+            # packed K is a pure re-ordering of k's bits: per block and 32-row
+            # half, 16-byte chunks chunk-major, then row; zero rows past T
+            kb = np.zeros((run.N * 64, w.head_dim), np.uint16)
+            kb[:w.seq_len] = run.arrs[1][0, h]
+            want = kb.reshape(run.N, 2, 32, w.head_dim // 8, 8).transpose(0, 1, 3, 2, 4).reshape(run.N, -1)
+            assert np.array_equal(kp[0, h], want), h
         q, k, v = head_f64(run.arrs, w.dtype, 0, h)
         ref = O.kv_block_stats(k, v, 64)
         rq, rq2 = O.pool_queries(q, 64, 1 / math.sqrt(w.head_dim))

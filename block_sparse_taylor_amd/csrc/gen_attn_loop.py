@@ -1,61 +1,75 @@
 """Generates attn_loop_d128.inc: the exact-item loop of the fused PISA forward
-(D = 128, gfx950) as one inline-assembly block.
+(D = 128, gfx950) as one inline-assembly block, software-pipelined by one item.
 
     python gen_attn_loop.py attn_loop_d128.inc
 
-Register plan inside the block (all explicitly named and declared clobbered,
-so they live across the whole loop): v56-v119 K operands of the current item
-(kreg[kt][ks], loaded one item ahead from the packed copy of K, one
-contiguous 1 KB run per load), v120-v183 the S^T accumulators
-(s[kt][qt]), v184-v215 the bf16 P operands, v216-v231 Q^T operand buffers,
-v232-v243 transposed-V operand buffers, v244-v255 scratch; s70-s89 loop
-state and buffer descriptors. The PV accumulators, the softmax state and the
-per-lane addresses are operands. Every wait (vmcnt, lgkmcnt) and every
-hazard pad (s_nop) is explicit: the compiler's hazard recognizer does not see
-inside inline assembly. The pads follow the ones the compiler itself emits for
-the same dependences on gfx950: 12 wait states from an MFMA result to a VALU
-read, 1 from a transcendental result to a VALU read, 2 from a VALU write to a
-permlane read and 3 from the permlane result, 1 from an M0 write to an LDS DMA.
+With one wave per SIMD the loop is bound by the wave's own instruction issue
+(about one instruction per four cycles besides the MFMA pipe), so the
+generator keeps the instruction count per item low: exact vmcnt/lgkmcnt waits
+only where a value is consumed, one M0 write per four LDS DMAs (the
+instruction's immediate offset moves the global and the LDS address alike),
+buffer offsets held in SGPRs, and the softmax ordered so that no pad is needed
+between an exp2 and its consumer.
 
-Per item (step), with the V tiles of parity p = item % 2:
-  phase A: S^T = K Q^T (32 MFMAs, k-step-major) interleaved with the Q^T
-           reads, the 16 V DMA instructions of this item (into parity p) and
-           the 16 K loads of the next item (each after the MFMAs that read the
-           registers it overwrites);
-  phase B: O^T += V^T P of the previous item (32 MFMAs, transposed reads of
-           parity 1 - p) interleaved with the softmax of this item (row max,
-           reference update, exp2, bf16 pack into P once that group of P is no
-           longer read, bf16 dot2 row sums).
-The softmax keeps a fixed reference (first finite tile max of a row), tracks
-the running tile maximum and flags a tile that exceeds the reference by more
-than 64 (log2 units); the caller reruns with the exact maxima in that case.
+Per step n (n = 0 .. ni - 2), one stream of 64 MFMAs:
+  QK(n+1): S^T(n+1) = K(n+1) Q^T      32 MFMAs, K from AGPRs, Q^T from LDS
+  PV(n):   O^T     += V(n)^T P(n)     32 MFMAs, V^T by transposed LDS reads
+and between them: the softmax of item n (exp2 against the row reference, bf16
+pack into P, bf16 dot2 row sums; the writes of P group g precede the PV MFMAs
+that read it), the K loads of item n+2 (each after the last QK MFMA that reads
+the AGPRs it overwrites), the V DMA of item n+1 into the other LDS tile, and
+after the last QK MFMA the tail mask, row max and reference update of
+S^T(n+1). The last item runs its softmax and PV alone. The softmax keeps a
+fixed reference (a row's first finite tile max), tracks the running maximum
+and flags a tile more than 64 (log2 units) above the reference; the caller
+reruns with the exact maxima in that case.
+
+Register plan (explicitly named, declared clobbered): a128-a191 K of the
+next item (kreg[kt][ks]); v56-v119 / v120-v183 the S^T buffers of two
+consecutive items; v184-v215 P; v216-v231 Q^T operand buffers; v232-v243
+transposed-V operand buffers; v244-v255 scratch (v244:v245 the pending
+item-list entry); s70-s90 loop state, buffer descriptors, offsets and the
+bf16 pair (1, 1) for the row sums. The PV
+accumulators (AGPRs), the softmax state and the per-lane addresses are
+operands. VALU work is written in 4-byte encodings where one exists (an
+8-byte instruction costs about a cycle more to issue). Hazard pads follow the
+ones the compiler itself emits on gfx950:
+12 wait states from an MFMA result to a VALU read, 2 from a VALU write to an
+MFMA operand read, 1 from a transcendental result to a VALU read, 2 from a
+VALU write to a permlane read and 3 from the permlane result, 1 from an M0
+write to an LDS DMA.
 """
 import os
 import sys
 
-D, KS, DT, CH, RPI, VL, RB, QP = 128, 8, 4, 16, 4, 16, 256, 136
-KREG, SREG, PREG, QB, VB, T = 56, 120, 184, 216, 232, 244
+D, KS, DT, CH, VL, RB, QP = 128, 8, 4, 16, 16, 256, 136
+KA, SREG, PREG, QB, VB, T = 128, 56, 184, 216, 232, 244
 
 
-def kreg(kt, ks): b = KREG + 4 * (kt * KS + ks); return f"v[{b}:{b+3}]"
-def sreg(kt, qt): b = SREG + 16 * (kt * 2 + qt); return f"v[{b}:{b+15}]"
-def se(kt, qt, e): return f"v{SREG + 16 * (kt * 2 + qt) + e}"
-def preg(kt, h, qt): b = PREG + 4 * ((kt * 2 + h) * 2 + qt); return f"v[{b}:{b+3}]"
+def kreg(kt, ks): x = KA + 4 * (kt * KS + ks); return f"a[{x}:{x+3}]"
+def sreg(b, kt, qt): x = SREG + 64 * b + 16 * (kt * 2 + qt); return f"v[{x}:{x+15}]"
+def se(b, kt, qt, e): return f"v{SREG + 64 * b + 16 * (kt * 2 + qt) + e}"
+def preg(kt, h, qt): x = PREG + 4 * ((kt * 2 + h) * 2 + qt); return f"v[{x}:{x+3}]"
 def pw(kt, h, qt, w): return f"v{PREG + 4 * ((kt * 2 + h) * 2 + qt) + w}"
-def qbuf(i): b = QB + 4 * i; return f"v[{b}:{b+3}]"
-def vbuf(i): b = VB + 4 * i; return f"v[{b}:{b+3}]"
-def vlo(i): b = VB + 4 * i; return f"v[{b}:{b+1}]"
-def vhi(i): b = VB + 4 * i; return f"v[{b+2}:{b+3}]"
+def qbuf(i): x = QB + 4 * i; return f"v[{x}:{x+3}]"
+def vbuf(i): x = VB + 4 * i; return f"v[{x}:{x+3}]"
+def vlo(i): x = VB + 4 * i; return f"v[{x}:{x+1}]"
+def vhi(i): x = VB + 4 * i; return f"v[{x+2}:{x+3}]"
 def t(i): return f"v{T + i}"
 
 
-S_N, S_NI, S_OFF, S_NV, S_NVC, S_X = 70, 71, 72, 73, 74, 75
-S_KRS, S_VRS = 76, 80          # 4-SGPR buffer descriptors
-S_M0, S_SOFF, S_NOFF, S_NNV, S_Y = 84, 85, 86, 87, 89
-SGPRS = list(range(70, 90))
+S_N, S_NI, S_OFFA, S_NVA, S_OFFB, S_NVB = 70, 71, 72, 73, 74, 75
+S_KRS, S_VRS = 76, 80                     # 4-SGPR buffer descriptors
+S_M0, S_C1, S_X, S_Y, S_C2, S_C3, S_ONES = 84, 85, 86, 87, 88, 89, 90
+SGPRS = list(range(70, 91))
+SOFF = {0: "0", 4096: f"s{S_C1}", 8192: f"s{S_C2}", 12288: f"s{S_C3}"}
 def SR(a, n=4): return f"s[{a}:{a+n-1}]"
-ACC = [f"%[a{i}]" for i in range(8)]   # acc[dt][qt] -> a{2 dt + qt}
+ACC = [f"%[a{i}]" for i in range(8)]      # acc[dt][qt] -> a{2 dt + qt}
 MINF = "0xff800000"
+GROUPS = [(kt, h) for kt in range(2) for h in range(2)]
+TR = {0: ["%[tr0_0]", "%[tr0_1]", "%[tr0_2]", "%[tr0_3]"],
+      1: ["%[tr1_0]", "%[tr1_1]", "%[tr1_2]", "%[tr1_3]"]}
+VLDS = {0: "%[vl0]", 1: "%[vl1]"}
 
 L = []
 def emit(s): L.append(s)
@@ -66,9 +80,109 @@ def label(name):
     return f"PISA_{name}_{LBL[0]}_%="
 
 
+class Op:
+    """A scheduled unit: its lines; for an LDS read its id; for an MFMA the LDS
+    reads and the previous step's VMEM ops it needs; the MFMA it must follow
+    (after) and the MFMA it must precede (before); for a VMEM op its id."""
+    def __init__(self, kind, lines, lds_id=None, needs=(), vneeds=(), after=-1, before=None, vm_id=None):
+        self.kind, self.lines, self.lds_id, self.needs, self.vneeds = kind, lines, lds_id, tuple(needs), tuple(vneeds)
+        self.after, self.before, self.vm_id = after, before, vm_id
+
+    def cost(self):
+        c = 0
+        for ln in self.lines:
+            if ln.startswith("v_exp_f32"):
+                c += 4
+            elif ln.startswith("s_nop"):
+                c += int(ln.split()[1]) + 1
+            else:
+                c += 1
+        return c
+
+
+class Sched:
+    """Merges an MFMA stream with LDS reads (issued a few MFMAs ahead), VMEM
+    ops (in order, at most one per MFMA) and VALU ops (in order, about
+    `budget` issue units per MFMA), with lgkmcnt/vmcnt waits only where an
+    MFMA consumes data that may still be in flight. `prev_after[id]` is the
+    number of VMEM ops issued after op `id` in the previous step."""
+    def __init__(self, prev_after=None, n_lds=0):
+        self.lds_seq, self.n_lds, self.lgkm_ok = {}, n_lds, n_lds - 1
+        self.prev_after, self.vm_issued, self.prev_ok = prev_after or {}, 0, None
+
+    def issue(self, op):
+        for ln in op.lines:
+            emit(ln)
+        if op.lds_id is not None:
+            self.lds_seq[op.lds_id] = self.n_lds
+            self.n_lds += 1
+        if op.kind == "vmem":
+            self.vm_issued += 1
+
+    def wait_lds(self, needs):
+        if not needs:
+            return
+        last = max(self.lds_seq[n] for n in needs)
+        if last <= self.lgkm_ok:
+            return
+        after = min(self.n_lds - 1 - last, 15)
+        emit(f"s_waitcnt lgkmcnt({after})")
+        self.lgkm_ok = self.n_lds - 1 - after
+
+    def wait_vm(self, vneeds):
+        if not vneeds:
+            return
+        need = min(self.prev_after[v] for v in vneeds)     # ops issued after the youngest needed one
+        if self.prev_ok is not None and need >= self.prev_ok:
+            return
+        n = min(need + self.vm_issued, 63)
+        emit(f"s_waitcnt vmcnt({n})")
+        self.prev_ok = n - self.vm_issued
+
+    def run(self, mfmas, lds, vmem, valu, lds_ahead=8, budget=8):
+        li = mi = vi = 0
+        for i, m in enumerate(mfmas):
+            req = max((j for j in range(vi, len(valu)) if valu[j].before is not None and valu[j].before <= i), default=-1)
+            forced = req >= vi
+            while vi <= req:
+                assert valu[vi].after < i, "dependence cycle in the schedule"
+                self.issue(valu[vi])
+                vi += 1
+            horizon = set()
+            for mm in mfmas[i:i + lds_ahead]:
+                horizon.update(mm.needs)
+            while li < len(lds) and lds[li].after < i and (lds[li].lds_id in horizon or lds[li].lds_id in m.needs):
+                self.issue(lds[li])
+                li += 1
+            if forced:
+                emit("s_nop 1")                    # VALU result -> MFMA operand read
+            assert all(nd in self.lds_seq for nd in m.needs), "LDS read not issued before its MFMA"
+            self.wait_lds(m.needs)
+            self.wait_vm(m.vneeds)
+            self.issue(m)
+            # one VMEM op (an M0 write goes with the DMA after it)
+            while mi < len(vmem) and vmem[mi].after <= i:
+                op = vmem[mi]
+                self.issue(op)
+                mi += 1
+                if op.kind == "vmem":
+                    break
+            spent = 0
+            near = False
+            while vi < len(valu) and valu[vi].after <= i and spent < budget:
+                spent += valu[vi].cost()
+                near |= valu[vi].before is not None and valu[vi].before <= i + 1
+                self.issue(valu[vi])
+                vi += 1
+            if near:
+                emit("s_nop 1")                    # VALU result -> the next MFMA's operand read
+        for lst, k in ((lds, li), (vmem, mi), (valu, vi)):
+            for op in lst[k:]:
+                self.issue(op)
+
+
 def rsrc(base, lo, hi, off, nv):
-    # {address = (hi:lo) + off, stride 0, num_records = nv * RB (nv = None:
-    # the whole 64-row block), word 3}
+    # {address = (hi:lo) + off, stride 0, num_records = nv * RB (None: the whole 16 KB block), word 3}
     emit(f"s_add_u32 s{base}, {lo}, s{off}")
     emit(f"s_addc_u32 s{base+1}, {hi}, 0")
     if nv is None:
@@ -78,299 +192,264 @@ def rsrc(base, lo, hi, off, nv):
     emit(f"s_mov_b32 s{base+3}, 0x00020000")
 
 
-def dma(i, vl):
-    # V rows 4 i .. 4 i + 3 of the current item -> LDS tile vl + 1024 i (lane l: +16 l)
-    emit(f"s_add_u32 m0, {vl}, {1024 * i}")
-    emit(f"s_movk_i32 s{S_SOFF}, {1024 * i}")
-    emit("s_nop 0")
-    emit(f"buffer_load_dwordx4 %[voff], {SR(S_VRS)}, s{S_SOFF} offen lds")
-
-
-def kload_lines(kt, ks):
-    # packed K: k-step ks of key tile kt (chunks 2 ks, 2 ks + 1 of its 32 rows)
-    # is the contiguous 1 KB run at 8192 kt + 1024 ks; lane l reads its 16
-    # bytes at 16 l (%[koff])
+def kload_op(kt, ks, after):
+    # packed K: k-step ks of key tile kt is the contiguous 1 KB run at 8192 kt + 1024 ks
     off = 1024 * (KS * kt + ks)
-    return [f"s_movk_i32 s{S_Y}, {off & ~4095}",
-            f"buffer_load_dwordx4 {kreg(kt, ks)}, %[koff], {SR(S_KRS)}, s{S_Y} offen offset:{off & 4095}"]
+    return Op("vmem", [f"buffer_load_dwordx4 {kreg(kt, ks)}, %[koff], {SR(S_KRS)}, {SOFF[off & ~4095]} offen offset:{off & 4095}"],
+              after=after, vm_id=("k", kt, ks))
 
 
-def kload(kt, ks):
-    for ln in kload_lines(kt, ks):
-        emit(ln)
-
-
-def qread(qt, ks, buf):
-    emit(f"ds_read_b128 {qbuf(buf)}, %[qa] offset:{(qt * 32 * QP) * 2 + 16 * ks}")
-
-
-GROUPS = [(kt, h) for kt in range(2) for h in range(2)]
-
-
-class Op:
-    """One scheduled unit: its lines, its kind, the LDS reads it needs, and the
-    MFMA (index in the phase) it must follow."""
-    def __init__(self, kind, lines, lds_id=None, needs=(), after=-1):
-        self.kind, self.lines, self.lds_id, self.needs, self.after = kind, lines, lds_id, tuple(needs), after
-
-
-class Sched:
-    """Merges an MFMA stream with LDS reads (issued a few MFMAs ahead, waits
-    computed from the issue order) and other ops (spread evenly, each after the
-    MFMA it depends on)."""
-    def __init__(self):
-        self.lds_seq = {}      # lds id -> issue number
-        self.n_lds = 0
-
-    def issue(self, op):
-        for ln in op.lines:
-            emit(ln)
-        if op.lds_id is not None:
-            self.lds_seq[op.lds_id] = self.n_lds
-            self.n_lds += 1
-
-    def wait_for(self, needs):
-        if not needs:
-            return
-        last = max(self.lds_seq[n] for n in needs)
-        after = self.n_lds - 1 - last
-        emit(f"s_waitcnt lgkmcnt({min(after, 15)})")
-
-    def run(self, mfmas, lds, others, lds_ahead=8):
-        """mfmas: list of Op (needs = LDS ids); lds: Op list in the order their
-        consumers appear, each with .after = the MFMA index it must follow
-        (register reuse); others: Op list in program order."""
-        li = 0
-        oi = 0
-        n = len(mfmas)
-        quota = (len(others) + n - 1) // n if n else 0
-        for i, m in enumerate(mfmas):
-            # LDS reads needed by the next lds_ahead MFMAs (and allowed now)
-            horizon = set()
-            for mm in mfmas[i:i + lds_ahead]:
-                horizon.update(mm.needs)
-            while li < len(lds) and lds[li].after < i and (lds[li].lds_id in horizon or lds[li].lds_id in m.needs):
-                self.issue(lds[li])
-                li += 1
-            assert all(nd in self.lds_seq for nd in m.needs), "LDS read not issued before its MFMA"
-            self.wait_for(m.needs)
-            self.issue(m)
-            k = 0
-            while oi < len(others) and k < quota and others[oi].after <= i:
-                self.issue(others[oi])
-                oi += 1
-                k += 1
-        while li < len(lds):
-            self.issue(lds[li])
-            li += 1
-        while oi < len(others):
-            self.issue(others[oi])
-            oi += 1
-
-
-def phase_a_ops(vl):
-    """S^T = K Q^T MFMAs (ks-major), their Q reads, the V DMA of the current item and
-    the K loads of the next."""
-    mf, lds, oth = [], [], []
-    idx = {}
-    for ks in range(KS):
-        for kt in range(2):
-            for qt in range(2):
-                src_c = "0" if ks == 0 else sreg(kt, qt)
-                b = (ks % 2) * 2 + qt
-                idx[(kt, qt, ks)] = len(mf)
-                mf.append(Op("mfma", [f"v_mfma_f32_32x32x16_bf16 {sreg(kt, qt)}, {kreg(kt, ks)}, {qbuf(b)}, {src_c}"],
-                             needs=[("q", qt, ks)]))
-    for ks in range(KS):
-        for qt in range(2):
-            # buffer (ks % 2) * 2 + qt last read by the MFMAs of k-step ks - 2
-            after = max(idx[(kt, qt, ks - 2)] for kt in range(2)) if ks >= 2 else -1
-            lds.append(Op("lds", [f"ds_read_b128 {qbuf((ks % 2) * 2 + qt)}, %[qa] offset:{(qt * 32 * QP) * 2 + 32 * ks}"],
-                          lds_id=("q", qt, ks), after=after))
+def vm_list(vl, qk_last_reader):
+    """the step's VMEM ops in issue order: K loads (ks-major, each after the
+    last QK MFMA reading its registers, + 1) and the V DMA of the next item
+    (rows 4 i .. 4 i + 3 -> LDS tile + 1024 i; M0 set once per four)."""
+    ops = []
     dmas = []
-    for i in range(VL):
-        dmas.append(Op("vmem", [f"s_add_u32 m0, {vl}, {1024 * i}", f"s_movk_i32 s{S_SOFF}, {1024 * i}", "s_nop 0",
-                                f"buffer_load_dwordx4 %[voff], {SR(S_VRS)}, s{S_SOFF} offen lds"]))
-    kls = []
+    for a in range(4):
+        dmas.append(Op("m0", [f"s_add_u32 m0, {vl}, {4096 * a}" if a else f"s_mov_b32 m0, {vl}", "s_nop 0"]))
+        for b in range(4):
+            i = 4 * a + b
+            dmas.append(Op("vmem", [f"buffer_load_dwordx4 %[voff], {SR(S_VRS)}, {SOFF[4096 * a]} offen offset:{1024 * b} lds"],
+                           vm_id=("d", i)))
+    di = 0
     for ks in range(KS):
         for kt in range(2):
-            last_reader = max(idx[(kt, qt, ks)] for qt in range(2))
-            kls.append(Op("vmem", kload_lines(kt, ks), after=last_reader + 1))
-    # DMA first (no constraint), the K loads as their registers free up
-    oth = dmas + kls
-    return mf, lds, oth
-
-
-def softmax_max_lines(qt):
-    out = []
-    a = t(2 + qt)
-    v = [se(kt, qt, e) for kt in range(2) for e in range(16)]
-    out.append(f"v_max3_f32 {a}, {v[0]}, {v[1]}, {v[2]}")
-    for i in range(3, 31, 2):
-        out.append(f"v_max3_f32 {a}, {a}, {v[i]}, {v[i+1]}")
-    out.append(f"v_max_f32 {a}, {a}, {v[31]}")
-    out.append(f"v_mov_b32 {t(6 + qt)}, {a}")
-    out.append("s_nop 1")
-    out.append(f"v_permlane32_swap_b32 {a}, {t(6 + qt)}")
-    out.append("s_nop 2")
-    out.append(f"v_max_f32 {a}, {a}, {t(6 + qt)}")
-    out.append(f"v_mul_f32 {a}, {a}, %[c2]")
-    m2 = f"%[m2{qt}]"
-    out.append(f"v_max_f32 %[mx{qt}], %[mx{qt}], {a}")
-    out.append(f"v_cmp_eq_f32 vcc, {MINF}, {m2}")
-    out.append(f"v_cndmask_b32 {m2}, {m2}, {a}, vcc")
-    out.append(f"v_add_f32 {t(6 + qt)}, 0x42800000, {m2}")
-    out.append(f"v_cmp_gt_f32 vcc, {a}, {t(6 + qt)}")
-    out.append(f"v_cndmask_b32_e64 %[need], %[need], 1, vcc")
-    out.append(f"v_cmp_eq_f32 vcc, {MINF}, {m2}")
-    out.append(f"v_cndmask_b32_e64 {t(4 + qt)}, {m2}, 0, vcc")
-    out.append(f"v_xor_b32 {t(4 + qt)}, 0x80000000, {t(4 + qt)}")
-    return out
-
-
-def softmax_ops():
-    """the softmax of the current item as VALU ops; ops writing P of PV group g
-    carry after = the index of that group's last MFMA (set by the caller)."""
-    ops = [Op("valu", ["s_nop 7", "s_nop 4"])]          # S^T MFMA results -> VALU
-    for qt in range(2):
-        for ln in softmax_max_lines(qt):
-            ops.append(Op("valu", [ln]))
-    for gi, (kt, h) in enumerate(GROUPS):
-        for qt in range(2):
-            nm = t(4 + qt)
-            for w in range(4):
-                e = 8 * h + 2 * w
-                x0, x1 = t(8 + 2 * (w % 2)), t(9 + 2 * (w % 2))
-                ops.append(Op("valu", [f"v_fma_f32 {x0}, {se(kt, qt, e)}, %[c2], {nm}"]))
-                ops.append(Op("valu", [f"v_fma_f32 {x1}, {se(kt, qt, e + 1)}, %[c2], {nm}"]))
-                ops.append(Op("valu", [f"v_exp_f32 {x0}, {x0}"]))
-                ops.append(Op("valu", [f"v_exp_f32 {x1}, {x1}", "s_nop 0"]))
-                ops.append(Op("valu", [f"v_cvt_pk_bf16_f32 {pw(kt, h, qt, w)}, {x0}, {x1}"], after=("group", gi)))
-                ops.append(Op("valu", [f"v_dot2c_f32_bf16 %[l{qt}], 0x3f803f80, {pw(kt, h, qt, w)}"], after=("group", gi)))
+            ops.append(kload_op(kt, ks, qk_last_reader[(kt, ks)] + 1))
+        # two DMAs (with their M0 write) per k-step
+        n = 0
+        while di < len(dmas) and n < 2:
+            ops.append(dmas[di])
+            n += dmas[di].kind == "vmem"
+            di += 1
+    ops.extend(dmas[di:])
     return ops
 
 
-def pv_ops(trs):
-    """PV MFMAs of the previous item (group-major) and their transposed V reads."""
+def prev_after_of(vm):
+    ids = [o.vm_id for o in vm if o.kind == "vmem"]
+    return {v: len(ids) - 1 - k for k, v in enumerate(ids)}
+
+
+def qk_ops(sb, vneed):
+    """S^T(sb) = K Q^T: 32 MFMAs (k-step-major), their 16 Q^T reads, and the
+    index of the last MFMA reading each K operand."""
+    mf, lds, idx = [], [], {}
+    for ks in range(KS):
+        for kt in range(2):
+            for qt in range(2):
+                src_c = "0" if ks == 0 else sreg(sb, kt, qt)
+                idx[(kt, qt, ks)] = len(mf)
+                mf.append(Op("mfma", [f"v_mfma_f32_32x32x16_bf16 {sreg(sb, kt, qt)}, {kreg(kt, ks)}, {qbuf((ks % 2) * 2 + qt)}, {src_c}"],
+                             needs=[("q", qt, ks)], vneeds=[("k", kt, ks)] if vneed else []))
+    for ks in range(KS):
+        for qt in range(2):
+            after = max(idx[(kt, qt, ks - 2)] for kt in range(2)) if ks >= 2 else -1
+            lds.append(Op("lds", [f"ds_read_b128 {qbuf((ks % 2) * 2 + qt)}, %[qa] offset:{(qt * 32 * QP) * 2 + 32 * ks}"],
+                          lds_id=("q", qt, ks), after=after))
+    last = {(kt, ks): max(idx[(kt, qt, ks)] for qt in range(2)) for kt in range(2) for ks in range(KS)}
+    return mf, lds, last
+
+
+def pv_ops(par, base, vneed):
+    """O^T += V^T P: 32 MFMAs (group-major) and their 32 transposed V reads from tile par."""
     mf, lds = [], []
     pairs = [(kt, h, dt) for (kt, h) in GROUPS for dt in range(DT)]
     for r, (kt, h, dt) in enumerate(pairs):
         for qt in range(2):
             mf.append(Op("mfma", [f"v_mfma_f32_32x32x16_bf16 {ACC[dt * 2 + qt]}, {vbuf(r % 3)}, {preg(kt, h, qt)}, {ACC[dt * 2 + qt]}"],
-                         needs=[("v", r, 0), ("v", r, 1)]))
+                         needs=[("v", r, 0), ("v", r, 1)], vneeds=[("d", i) for i in range(VL)] if vneed else []))
     for r, (kt, h, dt) in enumerate(pairs):
         r0 = 32 * kt + 16 * h
-        after = 2 * (r - 3) + 1 if r >= 3 else -1       # buffer r % 3 last read by pair r - 3
-        lds.append(Op("lds", [f"ds_read_b64_tr_b16 {vlo(r % 3)}, {trs[dt]} offset:{r0 * RB}"], lds_id=("v", r, 0), after=after))
-        lds.append(Op("lds", [f"ds_read_b64_tr_b16 {vhi(r % 3)}, {trs[dt]} offset:{(r0 + 8) * RB}"], lds_id=("v", r, 1), after=after))
+        after = base + 2 * (r - 3) + 1 if r >= 3 else -1       # buffer r % 3 last read by pair r - 3
+        lds.append(Op("lds", [f"ds_read_b64_tr_b16 {vlo(r % 3)}, {TR[par][dt]} offset:{r0 * RB}"], lds_id=("v", r, 0), after=after))
+        lds.append(Op("lds", [f"ds_read_b64_tr_b16 {vhi(r % 3)}, {TR[par][dt]} offset:{(r0 + 8) * RB}"], lds_id=("v", r, 1), after=after))
     return mf, lds
 
 
-def resolve_after(ops, mfma_count_per_group=8):
-    for o in ops:
-        if isinstance(o.after, tuple):
-            o.after = mfma_count_per_group * (o.after[1] + 1) - 1
-
-
-TR = {0: ["%[tr0_0]", "%[tr0_1]", "%[tr0_2]", "%[tr0_3]"],
-      1: ["%[tr1_0]", "%[tr1_1]", "%[tr1_2]", "%[tr1_3]"]}
-
-
-def mask_block():
+def mask_lines(sb, nv):
+    """keys >= nv of S^T(sb) -> -inf (only the ragged last block of a sequence)."""
     skip = label("nomask")
-    emit(f"s_cmp_lt_u32 s{S_NVC}, 64")
-    emit(f"s_cbranch_scc0 {skip}")
-    emit("s_nop 7")
-    emit("s_nop 4")
-    emit(f"v_mov_b32 {t(7)}, {MINF}")
+    out = [f"s_cmp_lt_u32 s{nv}, 64", f"s_cbranch_scc0 {skip}", "s_nop 7", "s_nop 4", f"v_mov_b32 {t(7)}, {MINF}"]
     for kt in range(2):
         for e in range(16):
             key = 32 * kt + 8 * (e // 4) + (e % 4)
-            emit(f"v_add_u32 {t(6)}, {key}, %[kb4]")
-            emit(f"v_cmp_gt_u32 vcc, s{S_NVC}, {t(6)}")
+            out.append(f"v_add_u32 {t(6)}, {key}, %[kb4]")
+            out.append(f"v_cmp_gt_u32 vcc, s{nv}, {t(6)}")
             for qt in range(2):
-                emit(f"v_cndmask_b32 {se(kt, qt, e)}, {t(7)}, {se(kt, qt, e)}, vcc")
-    emit(f"{skip}:")
+                out.append(f"v_cndmask_b32 {se(sb, kt, qt, e)}, {t(7)}, {se(sb, kt, qt, e)}, vcc")
+    out.append(f"{skip}:")
+    return out
 
 
-def step(par, first):
-    vl = "%[vl0]" if par == 0 else "%[vl1]"
-    emit(f"; ---- item step, V tile parity {par}{' (first item)' if first else ''}")
-    emit("s_waitcnt vmcnt(0) lgkmcnt(0)")      # this item's K, the previous item's V, the next entry
-    emit(f"v_readfirstlane_b32 s{S_NOFF}, {t(0)}")
-    emit(f"v_readfirstlane_b32 s{S_NNV}, {t(1)}")
+def max_lines(sb):
+    """row max of S^T(sb) (scaled by c2) for both query tiles, reference
+    update, running maximum, restart flag, and -reference in t4 / t5."""
+    a = [t(2), t(3)]
+    v = [[se(sb, kt, qt, e) for kt in range(2) for e in range(16)] for qt in range(2)]
+    out = ["s_nop 7", "s_nop 4"]                  # MFMA results -> VALU
+    for qt in range(2):
+        out.append(f"v_max3_f32 {a[qt]}, {v[qt][0]}, {v[qt][1]}, {v[qt][2]}")
+    for i in range(3, 31, 2):
+        for qt in range(2):
+            out.append(f"v_max3_f32 {a[qt]}, {a[qt]}, {v[qt][i]}, {v[qt][i+1]}")
+    for qt in range(2):
+        out.append(f"v_max_f32 {a[qt]}, {a[qt]}, {v[qt][31]}")
+    out += [f"v_mov_b32 {t(6)}, {a[0]}", f"v_mov_b32 {t(7)}, {a[1]}", "s_nop 1",
+            f"v_permlane32_swap_b32 {a[0]}, {t(6)}", f"v_permlane32_swap_b32 {a[1]}, {t(7)}", "s_nop 2"]
+    for qt in range(2):
+        out.append(f"v_max_f32 {a[qt]}, {a[qt]}, {t(6 + qt)}")
+    for qt in range(2):
+        out.append(f"v_mul_f32 {a[qt]}, {a[qt]}, %[c2]")
+    for qt in range(2):
+        m2 = f"%[m2{qt}]"
+        out += [f"v_max_f32 %[mx{qt}], %[mx{qt}], {a[qt]}",
+                f"v_cmp_eq_f32 vcc, {MINF}, {m2}",
+                f"v_cndmask_b32 {m2}, {m2}, {a[qt]}, vcc",
+                f"v_add_f32 {t(6 + qt)}, 0x42800000, {m2}",
+                f"v_cmp_gt_f32 vcc, {a[qt]}, {t(6 + qt)}",
+                f"v_cndmask_b32_e64 %[need], %[need], 1, vcc",
+                f"v_cmp_eq_f32 vcc, {MINF}, {m2}",
+                f"v_cndmask_b32_e64 {t(4 + qt)}, {m2}, 0, vcc",
+                f"v_xor_b32 {t(4 + qt)}, 0x80000000, {t(4 + qt)}"]
+    return out
+
+
+def softmax_ops(sb, pv_base):
+    """exp2(S^T c2 - m) of S^T(sb) packed into P in pairs; the exp2 of pair p
+    is separated from its consumers by the FMAs of pair p + 1. The writes of P
+    group g precede the first PV MFMA of that group (pv_base + 8 g)."""
+    pairs = []
+    for gi, (kt, h) in enumerate(GROUPS):
+        for qt in range(2):
+            for w in range(4):
+                pairs.append((gi, kt, h, qt, w))
+
+    def tmp(p): return t(8 + 2 * (p % 2)), t(9 + 2 * (p % 2))
+
+    def F(p):
+        gi, kt, h, qt, w = pairs[p]
+        x0, x1 = tmp(p)
+        e = 8 * h + 2 * w
+        return [Op("valu", [f"v_fma_f32 {x0}, {se(sb, kt, qt, e)}, %[c2], {t(4 + qt)}"]),
+                Op("valu", [f"v_fma_f32 {x1}, {se(sb, kt, qt, e + 1)}, %[c2], {t(4 + qt)}"])]
+
+    def E(p):
+        x0, x1 = tmp(p)
+        return [Op("valu", [f"v_exp_f32 {x0}, {x0}"]), Op("valu", [f"v_exp_f32 {x1}, {x1}"])]
+
+    def C(p, pad=False):
+        gi, kt, h, qt, w = pairs[p]
+        x0, x1 = tmp(p)
+        return [Op("valu", (["s_nop 0"] if pad else []) + [f"v_cvt_pk_bf16_f32 {pw(kt, h, qt, w)}, {x0}, {x1}"],
+                   before=pv_base + 8 * gi),
+                Op("valu", [f"v_dot2c_f32_bf16 %[l{qt}], s{S_ONES}, {pw(kt, h, qt, w)}"])]
+
+    ops = F(0) + E(0)
+    for p in range(1, len(pairs)):
+        ops += F(p) + C(p - 1) + E(p)
+    ops += C(len(pairs) - 1, pad=True)
+    return ops
+
+
+def read_entry(dst_off, dst_nv):
+    emit(f"v_readfirstlane_b32 s{dst_off}, {t(0)}")
+    emit(f"v_readfirstlane_b32 s{dst_nv}, {t(1)}")
     emit("s_nop 1")
-    rsrc(S_VRS, "%[vb_lo]", "%[vb_hi]", S_OFF, S_NV)
-    rsrc(S_KRS, "%[kb_lo]", "%[kb_hi]", S_NOFF, None)
-    emit(f"s_mov_b32 s{S_NVC}, s{S_NV}")
-    # prefetch the list entry after next (used by the next step)
-    emit(f"s_add_u32 s{S_X}, s{S_N}, 2")
-    emit(f"s_sub_u32 s{S_Y}, s{S_NI}, 1")
-    emit(f"s_min_u32 s{S_X}, s{S_X}, s{S_Y}")
+
+
+def read_list(index_lines):
+    # list entry s{S_X} (computed by index_lines) -> v244:v245
+    for ln in index_lines:
+        emit(ln)
     emit(f"s_lshl_b32 s{S_X}, s{S_X}, 3")
     emit(f"v_add_u32 {t(0)}, s{S_X}, %[il]")
-    sa = Sched()
-    sa.issue(Op("lds", [f"ds_read_b64 v[{T}:{T+1}], {t(0)}"], lds_id=("list",)))
-    mf, lds, oth = phase_a_ops(vl)
-    sa.run(mf, lds, oth)
-    mask_block()
-    sm = softmax_ops()
-    if first:
-        for o in sm:
-            for ln in o.lines:
-                emit(ln)
-    else:
-        mfb, ldsb = pv_ops(TR[1 - par])
-        resolve_after(sm)
-        sb = Sched()
-        sb.run(mfb, ldsb, sm)
-    emit(f"s_mov_b32 s{S_OFF}, s{S_NOFF}")
-    emit(f"s_mov_b32 s{S_NV}, s{S_NNV}")
+    emit(f"ds_read_b64 v[{T}:{T+1}], {t(0)}")
+
+
+def full_step(par, vm_order):
+    """item n = S_N: S^T(n) in buffer par (masked, reference updated), K(n+1)
+    loading into the AGPRs, V(n) in tile par; offA/nvA = item n+1; the
+    pending list read holds entry n+2."""
+    emit(f"; ---- pipelined step, parity {par}")
+    emit("s_waitcnt lgkmcnt(0)")
+    read_entry(S_OFFB, S_NVB)
+    rsrc(S_VRS, "%[vb_lo]", "%[vb_hi]", S_OFFA, S_NVA)   # V of item n+1
+    rsrc(S_KRS, "%[kb_lo]", "%[kb_hi]", S_OFFB, None)    # K of item n+2
+    read_list([f"s_add_u32 s{S_X}, s{S_N}, 3", f"s_sub_u32 s{S_Y}, s{S_NI}, 1", f"s_min_u32 s{S_X}, s{S_X}, s{S_Y}"])
+    s = Sched(prev_after=prev_after_of(vm_order), n_lds=1)
+    mq, lq, last = qk_ops(1 - par, vneed=True)
+    mp, lp = pv_ops(par, len(mq), vneed=True)
+    vm = vm_list(VLDS[1 - par], last)
+    assert [o.vm_id for o in vm] == [o.vm_id for o in vm_order]
+    valu = softmax_ops(par, len(mq))
+    valu.append(Op("valu", mask_lines(1 - par, S_NVA), after=len(mq) - 1))
+    valu += [Op("valu", [ln], after=len(mq) - 1) for ln in max_lines(1 - par)]
+    s.run(mq + mp, lq + lp, vm, valu)
+    emit(f"s_mov_b32 s{S_OFFA}, s{S_OFFB}")
+    emit(f"s_mov_b32 s{S_NVA}, s{S_NVB}")
     emit(f"s_add_u32 s{S_N}, s{S_N}, 1")
 
 
-def final_pv(par):
-    mfb, ldsb = pv_ops(TR[par])
-    sb = Sched()
-    sb.run(mfb, ldsb, [])
+def tail(par):
+    """the last item: softmax of S^T(par), PV from tile par."""
+    emit(f"; ---- last item, parity {par}")
+    emit("s_waitcnt vmcnt(0) lgkmcnt(0)")
+    for o in softmax_ops(par, 0):
+        for ln in o.lines:
+            emit(ln)
+    emit("s_nop 1")
+    mp, lp = pv_ops(par, 0, vneed=False)
+    Sched().run(mp, lp, [], [])
 
 
 def program():
-    done, end0, end1, loop = label("done"), label("end0"), label("end1"), label("loop")
+    done, tail0, tail1, loop = label("done"), label("tail0"), label("tail1"), label("loop")
     emit(f"s_mov_b32 s{S_M0}, m0")
     emit("s_nop 4")                                # the accumulator was just written by VALU
     emit(f"s_mov_b32 s{S_NI}, %[ni]")
     emit(f"s_mov_b32 s{S_N}, 0")
     emit(f"s_cmp_eq_u32 s{S_NI}, 0")
     emit(f"s_cbranch_scc1 {done}")
-    emit(f"ds_read_b64 v[{T}:{T+1}], %[il]")     # item 0: list entry, K loads
+    emit(f"s_movk_i32 s{S_C1}, 4096")
+    emit(f"s_movk_i32 s{S_C2}, 8192")
+    emit(f"s_movk_i32 s{S_C3}, 12288")
+    emit(f"s_mov_b32 s{S_ONES}, 0x3f803f80")       # bf16 (1, 1)
+    # item 0: its K, then (pipelined with QK(0)) K of item 1 and V of item 0
+    emit(f"ds_read_b64 v[{T}:{T+1}], %[il]")
     emit("s_waitcnt lgkmcnt(0)")
-    emit(f"v_readfirstlane_b32 s{S_OFF}, {t(0)}")
-    emit(f"v_readfirstlane_b32 s{S_NV}, {t(1)}")
-    emit("s_nop 1")
-    rsrc(S_KRS, "%[kb_lo]", "%[kb_hi]", S_OFF, None)
-    for kt in range(2):
-        for ks in range(KS):
-            kload(kt, ks)
-    # item 1's entry (clamped) for the first step
-    emit(f"s_sub_u32 s{S_Y}, s{S_NI}, 1")
-    emit(f"s_min_u32 s{S_X}, s{S_Y}, 1")
-    emit(f"s_lshl_b32 s{S_X}, s{S_X}, 3")
-    emit(f"v_add_u32 {t(0)}, s{S_X}, %[il]")
-    emit(f"ds_read_b64 v[{T}:{T+1}], {t(0)}")
-    step(0, True)
+    read_entry(S_OFFB, S_NVB)
+    rsrc(S_KRS, "%[kb_lo]", "%[kb_hi]", S_OFFB, None)
+    rsrc(S_VRS, "%[vb_lo]", "%[vb_hi]", S_OFFB, S_NVB)
+    for ks in range(KS):
+        for kt in range(2):
+            for ln in kload_op(kt, ks, -1).lines:
+                emit(ln)
+    read_list([f"s_sub_u32 s{S_Y}, s{S_NI}, 1", f"s_min_u32 s{S_X}, s{S_Y}, 1"])   # entry 1 (clamped)
+    emit("s_waitcnt lgkmcnt(0)")
+    read_entry(S_OFFA, S_NVA)
+    rsrc(S_KRS, "%[kb_lo]", "%[kb_hi]", S_OFFA, None)
+    read_list([f"s_sub_u32 s{S_Y}, s{S_NI}, 1", f"s_min_u32 s{S_X}, s{S_Y}, 2"])   # entry 2 (clamped), pending
+    emit("s_waitcnt vmcnt(0)")                     # K(0)
+    mq, lq, last = qk_ops(0, vneed=False)
+    vm0 = vm_list(VLDS[0], last)
+    Sched(n_lds=1).run(mq, lq, vm0, [])
+    for ln in mask_lines(0, S_NVB):
+        emit(ln)
+    for ln in max_lines(0):
+        emit(ln)
     emit(f"{loop}:")
-    emit(f"s_cmp_ge_u32 s{S_N}, s{S_NI}")
-    emit(f"s_cbranch_scc1 {end1}")                 # the last item's V is in parity 0
-    step(1, False)
-    emit(f"s_cmp_ge_u32 s{S_N}, s{S_NI}")
-    emit(f"s_cbranch_scc1 {end0}")                 # the last item's V is in parity 1
-    step(0, False)
+    emit(f"s_add_u32 s{S_Y}, s{S_N}, 1")
+    emit(f"s_cmp_ge_u32 s{S_Y}, s{S_NI}")
+    emit(f"s_cbranch_scc1 {tail0}")
+    full_step(0, vm0)
+    emit(f"s_add_u32 s{S_Y}, s{S_N}, 1")
+    emit(f"s_cmp_ge_u32 s{S_Y}, s{S_NI}")
+    emit(f"s_cbranch_scc1 {tail1}")
+    full_step(1, vm0)
     emit(f"s_branch {loop}")
-    for lab, par in ((end1, 0), (end0, 1)):
+    for lab, par in ((tail0, 0), (tail1, 1)):
         emit(f"{lab}:")
-        emit("s_waitcnt vmcnt(0) lgkmcnt(0)")
-        final_pv(par)
+        tail(par)
         emit(f"s_branch {done}")
     emit(f"{done}:")
     emit("s_waitcnt vmcnt(0) lgkmcnt(0)")
@@ -380,7 +459,8 @@ def program():
 
 
 program()
-clob = [f'"v{i}"' for i in range(KREG, 256)] + [f'"s{i}"' for i in SGPRS]
+clob = ([f'"v{i}"' for i in range(SREG, 256)] + [f'"a{i}"' for i in range(KA, KA + 64)] +
+        [f'"s{i}"' for i in SGPRS])
 out = ["// Generated by gen_attn_loop.py (do not edit): the D = 128 exact-item loop of the fused PISA forward for gfx950.",
        "#define PISA_ATTN_LOOP_D128_ASM \\"]
 out.append(" \\\n".join('    "' + l + '\\n"' for l in L))

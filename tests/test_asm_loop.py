@@ -2,6 +2,7 @@
 committed include must be exactly what the generator produces."""
 
 import os
+import re
 import subprocess
 import sys
 import tempfile
@@ -22,19 +23,25 @@ def test_generated_loop_is_current():
     assert fresh == committed, "attn_loop_d128.inc is stale: rerun gen_attn_loop.py"
 
 
+def _expand(kind, text):
+    regs = {int(x) for x in re.findall(rf"\b{kind}(\d+)\b", text)}
+    for lo, hi in re.findall(rf"\b{kind}\[(\d+):(\d+)\]", text):
+        regs.update(range(int(lo), int(hi) + 1))
+    return regs
+
+
 def test_loop_register_plan():
     with open(os.path.join(CSRC, "attn_loop_d128.inc")) as f:
         text = f.read()
-    # every explicitly named VGPR lies in the clobbered range v56..v255
-    import re
-    body = text.split("#define PISA_ATTN_LOOP_D128_CLOBBERS")[0]
-    regs = [int(x) for x in re.findall(r"\bv(\d+)\b", body)]
-    regs += [int(a) for a, b in re.findall(r"\bv\[(\d+):(\d+)\]", body)]
-    regs += [int(b) for a, b in re.findall(r"\bv\[(\d+):(\d+)\]", body)]
-    assert min(regs) >= 56 and max(regs) <= 255
-    sregs = [int(x) for x in re.findall(r"\bs(\d+)\b", body)]
-    sregs += [int(x) for pair in re.findall(r"\bs\[(\d+):(\d+)\]", body) for x in pair]
-    assert min(sregs) >= 70 and max(sregs) <= 89
+    body, clob = text.split("#define PISA_ATTN_LOOP_D128_CLOBBERS")
+    body = re.sub(r"%\[\w+\]", "", body)       # operands the compiler allocates
+    declared = {k: {int(x) for x in re.findall(rf'"{k}(\d+)"', clob)} for k in "vas"}
+    # every register the loop names explicitly is declared clobbered
+    for k in "vas":
+        named = _expand(k, body)
+        assert named <= declared[k], (k, sorted(named - declared[k]))
+    # the compiler keeps v0-v55 and a0-a127 (the PV accumulators) for itself
+    assert min(declared["v"]) >= 56 and min(declared["a"]) >= 128
     # the loop's instruction set: memory is read with vector buffer loads and
     # LDS reads only; scalar instructions are ALU and control flow
     ops = set(re.findall(r'^\s*"\s*([a-z_0-9]+)', body, re.M))

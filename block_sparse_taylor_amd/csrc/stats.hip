@@ -294,15 +294,30 @@ __global__ __launch_bounds__(kThreads) void stats_f32_kernel(
 }
 
 // Fixed-order sum of the per-workgroup partials of each head.
+// Sums the partial H of a head in fixed order. For bf16 inputs it also writes
+// H split into bf16 hi + lo in the fused kernel's MFMA A-operand order for
+// G = Q H: element (dt, ks, part, lane, e) is the part of
+// H[16 ks + 8 (lane / 32) + e][32 dt + lane % 32].
 __global__ __launch_bounds__(kThreads) void hsum_reduce_kernel(const float* __restrict__ hpart,
-                                                               int G, int DD, float* __restrict__ hsum) {
+                                                               int G, int D, float* __restrict__ hsum,
+                                                               bf16_t* __restrict__ hpack) {
     const int64_t bh = blockIdx.y;
+    const int DD = D * D;
     const int e = blockIdx.x * kThreads + threadIdx.x;
     if (e >= DD) return;
     const float* p = hpart + bh * (int64_t)G * DD + e;
     double s = 0.0;
     for (int g = 0; g < G; ++g) s += (double)p[(int64_t)g * DD];
-    hsum[bh * DD + e] = (float)s;
+    const float h = (float)s;
+    hsum[bh * DD + e] = h;
+    if (hpack) {
+        const int a = e / D, b = e % D;            // key dim, value dim
+        const int dt = b / 32, lane = 32 * ((a % 16) / 8) + b % 32, ks = a / 16, el = a % 8;
+        const int64_t o = bh * (int64_t)(2 * DD) + ((int64_t)((dt * (D / 16) + ks) * 2) * 64 + lane) * 8 + el;
+        const bf16_t hi = f32_to_bf16(h);
+        hpack[o] = hi;
+        hpack[o + 64 * 8] = f32_to_bf16(h - bf16_to_f32(hi));
+    }
 }
 
 int stats_groups(const Geom& g) { return (g.N + kBPW - 1) / kBPW; }
@@ -336,7 +351,8 @@ hipError_t launch_block_stats(const Geom& g, int dtype, int second_order, const 
     if (e != hipSuccess) return e;
     const int DD = g.D * g.D;
     dim3 rgrid((DD + kThreads - 1) / kThreads, (unsigned)g.BH);
-    hipLaunchKernelGGL(hsum_reduce_kernel, rgrid, block, 0, stream, hpart, G, DD, st->hsum);
+    hipLaunchKernelGGL(hsum_reduce_kernel, rgrid, block, 0, stream, hpart, G, g.D, st->hsum,
+                       dtype == PISA_BF16 ? static_cast<bf16_t*>(st->hpack) : nullptr);
     return hipGetLastError();
 }
 

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define PISA_ABI_VERSION 2
+#define PISA_ABI_VERSION 3
 
 typedef enum {
     PISA_OK = 0,
@@ -105,6 +105,12 @@ typedef struct {
  *   kpack[b,h,j][((h * D/8 + c) * 32 + r) * 8 + e] = k[b,h,64 j + 32 h + r][8 c + e],
  * and 0 for rows past seq_len. It is not one of the paper's statistics: it
  * lets every 64-lane load of the fused kernel read one contiguous 1 KB run.
+ * hpack (bf16 inputs; ignored for fp32) is hsum split into bf16 hi + lo
+ * (hi = hsum rounded to bf16, lo = the remainder rounded to bf16), in the
+ * fused kernel's operand order, bf16 [B,H,2*D*D]: for dt < D/32, ks < D/16,
+ * part p (0 hi, 1 lo), lane l < 64 and e < 8,
+ *   hpack[b,h][(((dt * D/16 + ks) * 2 + p) * 64 + l) * 8 + e]
+ *     = part p of hsum[b,h][16 ks + 8 (l / 32) + e][32 dt + l % 32].
  */
 typedef struct {
     double *qbar;
@@ -116,6 +122,7 @@ typedef struct {
     void *kbar_c;
     void *vbar_c;
     void *kpack;
+    void *hpack;
 } pisa_stats_t;
 
 /* ABI version of the library (PISA_ABI_VERSION). */
@@ -176,8 +183,8 @@ pisa_status_t pisa_route_topk(const pisa_shape_t *shape, const pisa_params_t *pa
  * pisa_route_topk writes them: valid ids first, -1 only after them). o: [B,H,T,D] in the input dtype; must not
  * alias q, k, v. bf16 runs compute QK^T and PV with bf16 MFMA (fp32
  * accumulation, P rounded to bf16); fp32 runs compute in fp32.
- * Reads stats->kbar_c, vbar_c, kpack (bf16), vsum (fp32 path), kbar (fp32
- * path), hsum.
+ * Reads stats->kbar_c, vbar_c, kpack and hpack (bf16), vsum, kbar and hsum
+ * (fp32 path).
  */
 pisa_status_t pisa_attn_fwd(const pisa_shape_t *shape, const pisa_params_t *params,
                             const void *q, const void *k, const void *v,

@@ -8,7 +8,8 @@ Tolerances (from the operator's specification and the arithmetic):
 * gated second-order table: the gate decision equals float64's; kept values
   within the fp32 dot-product bound 2 (D + 4) u w.
 * statistics: qbar/kbar bit-exact (exact fp64 sums), ksig2 to 1e-12; the
-  packed copy of K bit-exact (a re-ordering); V-hat is the fp64 sum
+  packed copy of K bit-exact (a re-ordering); packed H the exact bf16 hi/lo
+  split of the returned hsum; V-hat is the fp64 sum
   rounded once to fp32; the bf16 copies are bit-exact roundings; H within
   64 u sum_t |k_ta||v_tb| elementwise (u = 2^-24; fp32 accumulation of
   bf16 products over 2048-row partials, sqrt(n) u growth with a 1.4x margin).
@@ -99,6 +100,7 @@ def test_block_stats(name):
     vbc = run.host(run.st.vbar_c)
     ks2 = run.st.ksig2.cpu().numpy() if w.second_order else None
     kp = run.st.kpack.view(torch.int16).cpu().numpy().view(np.uint16) if w.dtype == "bf16" else None
+    hp = run.host(run.st.hpack) if w.dtype == "bf16" else None
     for h in heads:
         if kp is not None:
             # packed K is a pure re-ordering of k's bits: per block and 32-row
@@ -107,6 +109,19 @@ def test_block_stats(name):
             kb[:w.seq_len] = run.arrs[1][0, h]
             want = kb.reshape(run.N, 2, 32, w.head_dim // 8, 8).transpose(0, 1, 3, 2, 4).reshape(run.N, -1)
             assert np.array_equal(kp[0, h], want), h
+            # packed H: hsum split into bf16 hi + lo (exact roundings), operand order
+            D = w.head_dim
+            hf = hsum[0, h].astype(np.float32)
+            hi = bf16_round_f32(hf)
+            lo = bf16_round_f32(hf - hi)
+            parts = np.stack([hi, lo])                                  # [p, a, b]
+            a = 16 * np.arange(D // 16)[:, None, None] + 8 * (np.arange(64) // 32)[None, :, None] + np.arange(8)[None, None, :]
+            want_h = np.empty((D // 32, D // 16, 2, 64, 8), np.float32)
+            for dt in range(D // 32):
+                bcol = 32 * dt + np.arange(64) % 32
+                for p in range(2):
+                    want_h[dt, :, p] = parts[p][a, bcol[None, :, None]]
+            assert np.array_equal(hp[0, h].reshape(want_h.shape), want_h), h
         q, k, v = head_f64(run.arrs, w.dtype, 0, h)
         ref = O.kv_block_stats(k, v, 64)
         rq, rq2 = O.pool_queries(q, 64, 1 / math.sqrt(w.head_dim))

@@ -60,8 +60,9 @@ def t(i): return f"v{T + i}"
 
 S_N, S_NI, S_OFFA, S_NVA, S_OFFB, S_NVB = 70, 71, 72, 73, 74, 75
 S_KRS, S_VRS = 76, 80                     # 4-SGPR buffer descriptors
-S_M0, S_C1, S_X, S_Y, S_C2, S_C3, S_ONES = 84, 85, 86, 87, 88, 89, 90
-SGPRS = list(range(70, 91))
+S_M0, S_C1, S_X, S_Y, S_C2, S_C3, S_ONES, S_NVC = 84, 85, 86, 87, 88, 89, 90, 91
+SGPRS = list(range(70, 92))
+KBA, QBA = 192, 200                       # AGPRs: bias operands of the virtual-token step
 SOFF = {0: "0", 4096: f"s{S_C1}", 8192: f"s{S_C2}", 12288: f"s{S_C3}"}
 def SR(a, n=4): return f"s[{a}:{a+n-1}]"
 ACC = [f"%[a{i}]" for i in range(8)]      # acc[dt][qt] -> a{2 dt + qt}
@@ -181,15 +182,92 @@ class Sched:
                 self.issue(op)
 
 
-def rsrc(base, lo, hi, off, nv):
-    # {address = (hi:lo) + off, stride 0, num_records = nv * RB (None: the whole 16 KB block), word 3}
-    emit(f"s_add_u32 s{base}, {lo}, s{off}")
-    emit(f"s_addc_u32 s{base+1}, {hi}, 0")
-    if nv is None:
+def rsrc_item(base, kind, off, nv):
+    # descriptor of an item's K (kind "k") or V ("v") rows: the exact-block
+    # base, or the virtual-token base when bit 16 of the item word is set;
+    # num_records = the item's rows * RB for V, the whole 16 KB block for K
+    lo_e, hi_e, lo_v, hi_v = {"k": ("%[kb_lo]", "%[kb_hi]", "%[kv_lo]", "%[kv_hi]"),
+                              "v": ("%[vb_lo]", "%[vb_hi]", "%[vv_lo]", "%[vv_hi]")}[kind]
+    emit(f"s_bitcmp1_b32 s{nv}, 16")
+    emit(f"s_cselect_b32 s{S_X}, {lo_v}, {lo_e}")
+    emit(f"s_cselect_b32 s{S_Y}, {hi_v}, {hi_e}")
+    emit(f"s_add_u32 s{base}, s{S_X}, s{off}")
+    emit(f"s_addc_u32 s{base+1}, s{S_Y}, 0")
+    if kind == "k":
         emit(f"s_movk_i32 s{base+2}, {64 * RB}")
     else:
-        emit(f"s_lshl_b32 s{base+2}, s{nv}, 8")
+        emit(f"s_and_b32 s{S_X}, s{nv}, 0xffff")
+        emit(f"s_lshl_b32 s{base+2}, s{S_X}, 8")
     emit(f"s_mov_b32 s{base+3}, 0x00020000")
+
+
+def kbias_lines(off, nv):
+    """for a virtual-token item: the A operand of the bias k-step. Key j = 64 g
+    + 32 kt + lane % 32 of group g = off >> 14 gets b_j = log2(n_j) / c2
+    (+ w_ij / scale with the second-order term), or -inf if block j is
+    selected (exact) or past N, split into bf16 hi + lo in
+    k-slots 0 and 1 of the lower lane half (zero elsewhere); with the constant
+    B operand (1, 1 in slots 0, 1) one MFMA k-step adds b_j to S^T."""
+    skip = label("nokb")
+    out = [f"s_bitcmp1_b32 s{nv}, 16", f"s_cbranch_scc0 {skip}",
+           f"s_lshr_b32 s{S_X}, s{off}, 11",                  # 8 g: byte offset of its two selection words
+           f"s_add_u32 s{S_X}, s{S_X}, %[sbase]",
+           f"v_mov_b32 {t(6)}, s{S_X}",
+           f"ds_read_b64 v[{T+6}:{T+7}], {t(6)}",
+           "s_waitcnt lgkmcnt(0)",
+           f"v_readfirstlane_b32 s{S_X}, {t(6)}",
+           f"v_readfirstlane_b32 s{S_Y}, {t(7)}",
+           "s_nop 1"]
+    j, tmp, sel, pk = t(2), t(3), t(6), t(7)
+    skipw = [label("now"), label("now")]
+    for kt in range(2):
+        word = f"s{S_X}" if kt == 0 else f"s{S_Y}"
+        out += [f"v_bfe_u32 {j}, %[koff], 4, 5",                 # lane % 32 (koff = 16 lane)
+                f"v_lshrrev_b32_e64 {tmp}, 8, s{off}",           # 64 g
+                f"v_add_u32 {j}, {j}, {tmp}"]
+        if kt:
+            out.append(f"v_add_u32 {j}, 32, {j}")
+        out += [f"v_bfe_u32 {sel}, {word}, {j}, 1",              # block j selected
+                f"v_cmp_le_u32 vcc, %[nblk], {j}",
+                f"v_cndmask_b32_e64 {sel}, {sel}, 1, vcc",       # or j >= N
+                f"v_cmp_eq_u32 vcc, %[nm1], {j}",
+                f"v_cndmask_b32 {tmp}, %[bfull], %[blast], vcc", # b_j
+                # second-order term: + w_ij / scale (the gated table row of this
+                # query block; j clamped into the row, keys past N are -inf anyway)
+                "s_cmp_eq_u32 %[so], 0",
+                f"s_cbranch_scc1 {skipw[kt]}",
+                f"v_min_u32 {j}, %[nm1], {j}",
+                f"v_lshlrev_b32 {j}, 2, {j}",
+                f"global_load_dword {j}, {j}, %[wrow]",
+                "s_waitcnt vmcnt(0)",
+                f"v_fma_f32 {tmp}, {j}, %[winv], {tmp}",
+                f"{skipw[kt]}:",
+                f"v_mov_b32 {j}, {tmp}",
+                f"v_cvt_pk_bf16_f32 {pk}, {j}, {j}",
+                f"v_and_b32 {pk}, 0xffff0000, {pk}",             # hi as fp32
+                f"v_sub_f32 {j}, {j}, {pk}",                      # lo = b - hi (exact)
+                f"v_cvt_pk_bf16_f32 {pk}, {pk}, {j}",            # (hi, lo)
+                f"v_mov_b32 {tmp}, 0xff80",
+                f"v_cmp_eq_u32 vcc, 0, {sel}",
+                f"v_cndmask_b32 {pk}, {tmp}, {pk}, vcc",         # selected: (-inf, 0)
+                f"v_bfe_u32 {tmp}, %[koff], 9, 1",               # lane half
+                f"v_subrev_u32 {tmp}, 1, {tmp}",                 # lower half: all ones
+                f"v_and_b32 {pk}, {pk}, {tmp}",
+                f"v_accvgpr_write_b32 a{KBA + 4 * kt}, {pk}"]
+    out.append(f"{skip}:")
+    return out
+
+
+def bias_mfma_op(sb, nv):
+    """the bias k-step of a virtual-token item (skipped for exact blocks)."""
+    skip = label("nobias")
+    lines = [f"s_bitcmp1_b32 s{nv}, 16", f"s_cbranch_scc0 {skip}"]
+    for kt in range(2):
+        for qt in range(2):
+            lines.append(f"v_mfma_f32_32x32x16_bf16 {sreg(sb, kt, qt)}, a[{KBA + 4 * kt}:{KBA + 4 * kt + 3}], "
+                         f"a[{QBA}:{QBA + 3}], {sreg(sb, kt, qt)}")
+    lines.append(f"{skip}:")
+    return Op("mfma", lines)
 
 
 def kload_op(kt, ks, after):
@@ -373,21 +451,36 @@ def full_step(par, vm_order):
     emit(f"; ---- pipelined step, parity {par}")
     emit("s_waitcnt lgkmcnt(0)")
     read_entry(S_OFFB, S_NVB)
-    rsrc(S_VRS, "%[vb_lo]", "%[vb_hi]", S_OFFA, S_NVA)   # V of item n+1
-    rsrc(S_KRS, "%[kb_lo]", "%[kb_hi]", S_OFFB, None)    # K of item n+2
+    rsrc_item(S_VRS, "v", S_OFFA, S_NVA)                  # V of item n+1
+    rsrc_item(S_KRS, "k", S_OFFB, S_NVB)                  # K of item n+2
     read_list([f"s_add_u32 s{S_X}, s{S_N}, 3", f"s_sub_u32 s{S_Y}, s{S_NI}, 1", f"s_min_u32 s{S_X}, s{S_X}, s{S_Y}"])
     s = Sched(prev_after=prev_after_of(vm_order), n_lds=1)
     mq, lq, last = qk_ops(1 - par, vneed=True)
+    mq.append(bias_mfma_op(1 - par, S_NVA))
     mp, lp = pv_ops(par, len(mq), vneed=True)
     vm = vm_list(VLDS[1 - par], last)
     assert [o.vm_id for o in vm] == [o.vm_id for o in vm_order]
-    valu = softmax_ops(par, len(mq))
+    valu = [Op("valu", kbias_lines(S_OFFA, S_NVA), before=len(mq) - 1)]
+    valu += softmax_ops(par, len(mq))
     valu.append(Op("valu", mask_lines(1 - par, S_NVA), after=len(mq) - 1))
     valu += [Op("valu", [ln], after=len(mq) - 1) for ln in max_lines(1 - par)]
     s.run(mq + mp, lq + lp, vm, valu)
+    snapshot()
     emit(f"s_mov_b32 s{S_OFFA}, s{S_OFFB}")
+    emit(f"s_mov_b32 s{S_NVC}, s{S_NVA}")
     emit(f"s_mov_b32 s{S_NVA}, s{S_NVB}")
     emit(f"s_add_u32 s{S_N}, s{S_N}, 1")
+
+
+def snapshot():
+    # after the softmax of an exact item: the row sums so far (the virtual
+    # tokens, which come last, add l_tail = l - ls)
+    skip = label("virt")
+    emit(f"s_bitcmp1_b32 s{S_NVC}, 16")
+    emit(f"s_cbranch_scc1 {skip}")
+    emit("v_mov_b32 %[ls0], %[l0]")
+    emit("v_mov_b32 %[ls1], %[l1]")
+    emit(f"{skip}:")
 
 
 def tail(par):
@@ -397,6 +490,7 @@ def tail(par):
     for o in softmax_ops(par, 0):
         for ln in o.lines:
             emit(ln)
+    snapshot()
     emit("s_nop 1")
     mp, lp = pv_ops(par, 0, vneed=False)
     Sched().run(mp, lp, [], [])
@@ -414,12 +508,20 @@ def program():
     emit(f"s_movk_i32 s{S_C2}, 8192")
     emit(f"s_movk_i32 s{S_C3}, 12288")
     emit(f"s_mov_b32 s{S_ONES}, 0x3f803f80")       # bf16 (1, 1)
+    # constant parts of the bias operands: B = (1, 1, 0, ...) in the lower lane half
+    emit(f"v_bfe_u32 {t(6)}, %[koff], 9, 1")        # lane half
+    emit(f"v_subrev_u32 {t(6)}, 1, {t(6)}")
+    emit(f"v_and_b32 {t(6)}, s{S_ONES}, {t(6)}")
+    emit(f"v_accvgpr_write_b32 a{QBA}, {t(6)}")
+    for r in list(range(QBA + 1, QBA + 4)) + [KBA + 1, KBA + 2, KBA + 3, KBA + 5, KBA + 6, KBA + 7]:
+        emit(f"v_accvgpr_write_b32 a{r}, 0")
     # item 0: its K, then (pipelined with QK(0)) K of item 1 and V of item 0
     emit(f"ds_read_b64 v[{T}:{T+1}], %[il]")
     emit("s_waitcnt lgkmcnt(0)")
     read_entry(S_OFFB, S_NVB)
-    rsrc(S_KRS, "%[kb_lo]", "%[kb_hi]", S_OFFB, None)
-    rsrc(S_VRS, "%[vb_lo]", "%[vb_hi]", S_OFFB, S_NVB)
+    emit(f"s_mov_b32 s{S_NVC}, s{S_NVB}")
+    rsrc_item(S_KRS, "k", S_OFFB, S_NVB)
+    rsrc_item(S_VRS, "v", S_OFFB, S_NVB)
     for ks in range(KS):
         for kt in range(2):
             for ln in kload_op(kt, ks, -1).lines:
@@ -427,12 +529,12 @@ def program():
     read_list([f"s_sub_u32 s{S_Y}, s{S_NI}, 1", f"s_min_u32 s{S_X}, s{S_Y}, 1"])   # entry 1 (clamped)
     emit("s_waitcnt lgkmcnt(0)")
     read_entry(S_OFFA, S_NVA)
-    rsrc(S_KRS, "%[kb_lo]", "%[kb_hi]", S_OFFA, None)
+    rsrc_item(S_KRS, "k", S_OFFA, S_NVA)
     read_list([f"s_sub_u32 s{S_Y}, s{S_NI}, 1", f"s_min_u32 s{S_X}, s{S_Y}, 2"])   # entry 2 (clamped), pending
     emit("s_waitcnt vmcnt(0)")                     # K(0)
     mq, lq, last = qk_ops(0, vneed=False)
     vm0 = vm_list(VLDS[0], last)
-    Sched(n_lds=1).run(mq, lq, vm0, [])
+    Sched(n_lds=1).run(mq + [bias_mfma_op(0, S_NVB)], lq, vm0, [Op("valu", kbias_lines(S_OFFB, S_NVB), before=len(mq))])
     for ln in mask_lines(0, S_NVB):
         emit(ln)
     for ln in max_lines(0):
@@ -459,7 +561,7 @@ def program():
 
 
 program()
-clob = ([f'"v{i}"' for i in range(SREG, 256)] + [f'"a{i}"' for i in range(KA, KA + 64)] +
+clob = ([f'"v{i}"' for i in range(SREG, 256)] + [f'"a{i}"' for i in range(KA, QBA + 4)] +
         [f'"s{i}"' for i in SGPRS])
 out = ["// Generated by gen_attn_loop.py (do not edit): the D = 128 exact-item loop of the fused PISA forward for gfx950.",
        "#define PISA_ATTN_LOOP_D128_ASM \\"]

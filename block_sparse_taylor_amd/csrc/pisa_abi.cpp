@@ -67,6 +67,7 @@ pisa_status_t check_stats(const pisa_stats_t* st, int second_order, bool need_c,
     if (need_kpack) {
         PISA_TRY(check_ptr(st->kpack));
         PISA_TRY(check_ptr(st->hpack));
+        PISA_TRY(check_ptr(st->kbpack));
     }
     if (second_order) PISA_TRY(check_ptr(st->ksig2));
     else if (st->ksig2 && !aligned16(st->ksig2)) return PISA_ERR_ALIGN;

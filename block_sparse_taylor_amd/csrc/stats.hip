@@ -34,12 +34,13 @@ struct StatsOut {
     void* kbar_c;
     void* vbar_c;
     void* kpack;      // bf16 only: K in the fused kernel's operand order
+    void* kbpack;     // bf16 only: kbar_c in the same order, per group of 64 blocks
 };
 
 // Column statistics of one block from its LDS tiles (row pitch ld).
 template <typename T, int D>
 __device__ __forceinline__ void column_stats(const T* tq, const T* tk, const T* tv, int ld, int rows,
-                                             int64_t off, int second_order, double s64,
+                                             int64_t off, int n_blocks, int second_order, double s64,
                                              const StatsOut& out, double* red, float* kb_s,
                                              float* vs_s) {
     constexpr int H = kThreads / D;           // threads per column
@@ -84,6 +85,14 @@ __device__ __forceinline__ void column_stats(const T* tq, const T* tk, const T* 
         out.qbar[off + c] = a[0] / n;
         out.kbar[off + c] = mean;
         static_cast<T*>(out.kbar_c)[off + c] = store_cast<T>((float)mean);
+        if (out.kbpack) {
+            // block j = row j % 64 of virtual group j / 64, laid out like kpack
+            const int64_t bhj = off / D, bh = bhj / n_blocks, j = bhj % n_blocks;
+            const int r = (int)(j % 64);
+            const int64_t gbase = (bh * ((n_blocks + 63) / 64) + j / 64) * (int64_t)(64 * D);
+            static_cast<bf16_t*>(out.kbpack)[gbase + (((r / 32) * (D / 8) + c / 8) * 32 + r % 32) * 8 + c % 8] =
+                f32_to_bf16((float)mean);
+        }
         out.vsum[off + c] = (float)a[5];
         static_cast<T*>(out.vbar_c)[off + c] = store_cast<T>((float)(a[5] / n));
         kb_s[c] = (float)mean;
@@ -208,7 +217,7 @@ __global__ __launch_bounds__(kThreads) void stats_bf16_kernel(
         }
 
         const int64_t off = (bh * N + j) * D;
-        column_stats<bf16_t, D>(sq, sk, sv, LD, rows, off, second_order, s64, out, red, kb_s, vs_s);
+        column_stats<bf16_t, D>(sq, sk, sv, LD, rows, off, N, second_order, s64, out, red, kb_s, vs_s);
         __syncthreads();  // kb_s / vs_s visible
         // acc -= kbar_j (x) V-hat_j
 #pragma unroll
@@ -221,6 +230,16 @@ __global__ __launch_bounds__(kThreads) void stats_bf16_kernel(
                 const int a = mt * 32 + 8 * (i / 4) + 4 * hi + (i % 4);
                 acc[t][i] -= kb_s[a] * vb;
             }
+        }
+    }
+
+    // rows past the last block in the last virtual-key group are zero
+    if (out.kbpack && j1 == N && N % 64 != 0) {
+        const int GV = (N + 63) / 64;
+        bf16_t* gp = static_cast<bf16_t*>(out.kbpack) + (bh * GV + GV - 1) * (int64_t)(64 * D);
+        for (int e = tid; e < 64 * D; e += kThreads) {
+            const int r = (e / (32 * D)) * 32 + (e / 8) % 32;   // row of packed element e
+            if (r >= N % 64) gp[e] = 0;
         }
     }
 
@@ -271,7 +290,7 @@ __global__ __launch_bounds__(kThreads) void stats_f32_kernel(
             sv[row * LD + col] = ok ? v[o] : 0.f;
         }
         __syncthreads();
-        column_stats<float, D>(sq, sk, sv, LD, rows, (bh * N + j) * D, second_order, s64, out, red,
+        column_stats<float, D>(sq, sk, sv, LD, rows, (bh * N + j) * D, N, second_order, s64, out, red,
                                kb_s, vs_s);
         // partial H in fp64 from the exact products and exact column sums
 #pragma unroll
@@ -334,7 +353,8 @@ hipError_t launch_block_stats(const Geom& g, int dtype, int second_order, const 
     const int G = stats_groups(g);
     dim3 grid(G, (unsigned)g.BH), block(kThreads);
     float* hpart = static_cast<float*>(workspace);
-    StatsOut out{st->qbar, st->q2bar, st->kbar, st->vsum, st->ksig2, st->kbar_c, st->vbar_c, st->kpack};
+    StatsOut out{st->qbar, st->q2bar, st->kbar, st->vsum, st->ksig2, st->kbar_c, st->vbar_c, st->kpack,
+                 dtype == PISA_BF16 ? st->kbpack : nullptr};
 #define PISA_STATS_LAUNCH(KERN, TT, DD)                                                            \
     hipLaunchKernelGGL(KERN<DD>, grid, block, 0, stream, static_cast<const TT*>(q),               \
                        static_cast<const TT*>(k), static_cast<const TT*>(v), g.T, g.N,            \

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define PISA_ABI_VERSION 3
+#define PISA_ABI_VERSION 4
 
 typedef enum {
     PISA_OK = 0,
@@ -111,6 +111,10 @@ typedef struct {
  * part p (0 hi, 1 lo), lane l < 64 and e < 8,
  *   hpack[b,h][(((dt * D/16 + ks) * 2 + p) * 64 + l) * 8 + e]
  *     = part p of hsum[b,h][16 ks + 8 (l / 32) + e][32 dt + l % 32].
+ * kbpack (bf16 inputs; ignored for fp32) is kbar_c in kpack's order per group
+ * of 64 consecutive blocks (the keys of the virtual tokens), bf16
+ * [B,H,ceil(N/64),64*D]: kbpack[b,h,g] holds rows kbar_c[b,h,64 g + r] as kpack
+ * holds rows of k, and 0 for 64 g + r >= N.
  */
 typedef struct {
     double *qbar;
@@ -123,6 +127,7 @@ typedef struct {
     void *vbar_c;
     void *kpack;
     void *hpack;
+    void *kbpack;
 } pisa_stats_t;
 
 /* ABI version of the library (PISA_ABI_VERSION). */
@@ -183,8 +188,8 @@ pisa_status_t pisa_route_topk(const pisa_shape_t *shape, const pisa_params_t *pa
  * pisa_route_topk writes them: valid ids first, -1 only after them). o: [B,H,T,D] in the input dtype; must not
  * alias q, k, v. bf16 runs compute QK^T and PV with bf16 MFMA (fp32
  * accumulation, P rounded to bf16); fp32 runs compute in fp32.
- * Reads stats->kbar_c, vbar_c, kpack and hpack (bf16), vsum, kbar and hsum
- * (fp32 path).
+ * Reads stats->kbar_c, vbar_c, kpack, hpack and kbpack (bf16), vsum, kbar and
+ * hsum (fp32 path).
  */
 pisa_status_t pisa_attn_fwd(const pisa_shape_t *shape, const pisa_params_t *params,
                             const void *q, const void *k, const void *v,

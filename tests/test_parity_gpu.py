@@ -101,6 +101,8 @@ def test_block_stats(name):
     ks2 = run.st.ksig2.cpu().numpy() if w.second_order else None
     kp = run.st.kpack.view(torch.int16).cpu().numpy().view(np.uint16) if w.dtype == "bf16" else None
     hp = run.host(run.st.hpack) if w.dtype == "bf16" else None
+    kbp = run.st.kbpack.view(torch.int16).cpu().numpy().view(np.uint16) if w.dtype == "bf16" else None
+    kbb = run.st.kbar_c.view(torch.int16).cpu().numpy().view(np.uint16) if w.dtype == "bf16" else None
     for h in heads:
         if kp is not None:
             # packed K is a pure re-ordering of k's bits: per block and 32-row
@@ -122,6 +124,12 @@ def test_block_stats(name):
                 for p in range(2):
                     want_h[dt, :, p] = parts[p][a, bcol[None, :, None]]
             assert np.array_equal(hp[0, h].reshape(want_h.shape), want_h), h
+            # packed virtual keys: kbar_c rows per group of 64 blocks, kpack's order, zero past N
+            GV = -(-run.N // 64)
+            kc = np.zeros((GV * 64, D), np.uint16)
+            kc[:run.N] = kbb[0, h]
+            want_kb = kc.reshape(GV, 2, 32, D // 8, 8).transpose(0, 1, 3, 2, 4).reshape(GV, -1)
+            assert np.array_equal(kbp[0, h], want_kb), h
         q, k, v = head_f64(run.arrs, w.dtype, 0, h)
         ref = O.kv_block_stats(k, v, 64)
         rq, rq2 = O.pool_queries(q, 64, 1 / math.sqrt(w.head_dim))

@@ -463,7 +463,8 @@ def full_step(par, vm_order):
     valu = [Op("valu", kbias_lines(S_OFFA, S_NVA), before=len(mq) - 1)]
     valu += softmax_ops(par, len(mq))
     valu.append(Op("valu", mask_lines(1 - par, S_NVA), after=len(mq) - 1))
-    valu += [Op("valu", [ln], after=len(mq) - 1) for ln in max_lines(1 - par)]
+    if TRACK_MAX[0]:
+        valu += [Op("valu", [ln], after=len(mq) - 1) for ln in max_lines(1 - par)]
     s.run(mq + mp, lq + lp, vm, valu)
     snapshot()
     emit(f"s_mov_b32 s{S_OFFA}, s{S_OFFB}")
@@ -560,14 +561,23 @@ def program():
     emit(f"s_mov_b32 m0, s{S_M0}")
 
 
-program()
+TRACK_MAX = [True]
+bodies = {}
+for name, track in (("PISA_ATTN_LOOP_D128_ASM", False), ("PISA_ATTN_LOOP_D128_SAFE_ASM", True)):
+    L.clear()
+    TRACK_MAX[0] = track
+    program()
+    bodies[name] = list(L)
 clob = ([f'"v{i}"' for i in range(SREG, 256)] + [f'"a{i}"' for i in range(KA, QBA + 4)] +
         [f'"s{i}"' for i in SGPRS])
-out = ["// Generated by gen_attn_loop.py (do not edit): the D = 128 exact-item loop of the fused PISA forward for gfx950.",
-       "#define PISA_ATTN_LOOP_D128_ASM \\"]
-out.append(" \\\n".join('    "' + l + '\\n"' for l in L))
-out.append("")
+out = ["// Generated by gen_attn_loop.py (do not edit): the D = 128 item loop of the fused PISA forward for gfx950.",
+       "// PISA_ATTN_LOOP_D128_ASM: the row maximum of the first item only (sets the reference);",
+       "// PISA_ATTN_LOOP_D128_SAFE_ASM: the row maximum of every item, the restart flag and the running maximum."]
+for name, body in bodies.items():
+    out.append(f"#define {name} \\")
+    out.append(" \\\n".join('    "' + l + '\\n"' for l in body))
+    out.append("")
 out.append("#define PISA_ATTN_LOOP_D128_CLOBBERS " + ", ".join(clob) + ', "vcc", "scc", "memory"')
 dst = sys.argv[1] if len(sys.argv) > 1 else os.path.join(os.path.dirname(os.path.abspath(__file__)), "attn_loop_d128.inc")
 open(dst, "w").write("\n".join(out) + "\n")
-print(len(L), "instructions/labels ->", dst)
+print(sum(len(b) for b in bodies.values()), "instructions/labels ->", dst)

@@ -173,3 +173,26 @@ def test_long_sequence_routing(second_order):
     wr = O.second_order_w(q2bar, ks.sig2, 64)[2] if second_order else None
     ref, _ = O.route_topk(qbar, ks.kbar, s, topk, 1, wr)
     assert np.array_equal(idx.cpu().numpy()[0, 0], ref)
+
+
+@pytest.mark.parametrize("D", [128, 64])
+@pytest.mark.parametrize("second_order", [False, True])
+def test_wide_logit_range_restarts(D, second_order):
+    """Keys of a few blocks scaled by 40: their logits exceed those of the
+    blocks the waves start with by far more than the fixed reference's
+    headroom, so the waves take the restart passes; the result still matches
+    the oracle."""
+    say(f"[gpu] wide logit range D={D} so={second_order}")
+    T, H, topk, band = 1500, 2, 4, 1
+    r = np.random.default_rng(7 + D)
+    x = [r.standard_normal((1, H, T, D)) for _ in range(3)]
+    for blk in (5, 6, 13, 21):
+        x[1][:, :, 64 * blk:64 * blk + 64] *= 40.0
+    dev = [torch.from_numpy(a).to(torch.bfloat16).cuda().contiguous() for a in x]
+    qh, kh, vh = (t.double().cpu().numpy() for t in dev)
+    st, idx, wg, o = run_all(*dev, topk, band, second_order)
+    idx_h = idx.cpu().numpy()
+    for h in range(H):
+        ref = O.pisa_forward_head(qh[0, h], kh[0, h], vh[0, h], topk=topk, band=band,
+                                  second_order=second_order, routing=idx_h[0, h])
+        tol_check(o[0, h], ref, "bf16")

@@ -17,13 +17,19 @@
 //     bf16 inputs use bf16 MFMA (exact products, fp32 accumulation), fp32
 //     inputs an fp64 VALU loop. Partials go to the workspace and a second
 //     kernel adds those of a head in a fixed order (deterministic).
+#include <algorithm>
+
 #include "common.h"
 
 namespace pisa {
 namespace {
 
 constexpr int kPad = 4;   // LDS row padding (elements): rows 8 apart fall on disjoint bank halves
-constexpr int kBPW = 32;  // blocks per workgroup
+// Blocks per workgroup: the (head, block range) workgroups of one call should
+// all be resident at once. Two of these workgroups fit on a CU and MI355X has
+// 256 CUs, so a head gets max(1, 512 / heads) ranges of at least 16 blocks.
+constexpr int kResidentWGs = 512;
+constexpr int kMinBPW = 16;
 
 struct StatsOut {
     double* qbar;
@@ -114,7 +120,7 @@ __device__ __forceinline__ void column_stats(const T* tq, const T* tk, const T* 
 template <int D>
 __global__ __launch_bounds__(kThreads) void stats_bf16_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, int T,
-    int N, int second_order, double s64, StatsOut out, float* __restrict__ hpart) {
+    int N, int bpw, int second_order, double s64, StatsOut out, float* __restrict__ hpart) {
     constexpr int LD = D + kPad;
     constexpr int CH = D / 8;                       // 16-byte chunks per row
     constexpr int LOADS = kBlock * CH / kThreads;   // uint4 loads per thread per tensor
@@ -130,8 +136,8 @@ __global__ __launch_bounds__(kThreads) void stats_bf16_kernel(
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t bh = blockIdx.y;
     const int g = blockIdx.x;
-    const int j0 = g * kBPW;
-    const int j1 = min(N, j0 + kBPW);
+    const int j0 = g * bpw;
+    const int j1 = min(N, j0 + bpw);
     const int64_t base = bh * (int64_t)T * D;
 
     f32x16_t acc[TPW];
@@ -261,7 +267,7 @@ __global__ __launch_bounds__(kThreads) void stats_bf16_kernel(
 template <int D>
 __global__ __launch_bounds__(kThreads) void stats_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v, int T,
-    int N, int second_order, double s64, StatsOut out, float* __restrict__ hpart) {
+    int N, int bpw, int second_order, double s64, StatsOut out, float* __restrict__ hpart) {
     constexpr int LD = D + 1;
     constexpr int PER = D * D / kThreads;
     __shared__ float sq[kBlock * LD];
@@ -273,7 +279,7 @@ __global__ __launch_bounds__(kThreads) void stats_f32_kernel(
     const int tid = threadIdx.x;
     const int64_t bh = blockIdx.y;
     const int g = blockIdx.x;
-    const int j0 = g * kBPW, j1 = min(N, j0 + kBPW);
+    const int j0 = g * bpw, j1 = min(N, j0 + bpw);
     const int64_t base = bh * (int64_t)T * D;
     double acc[PER];
 #pragma unroll
@@ -339,7 +345,16 @@ __global__ __launch_bounds__(kThreads) void hsum_reduce_kernel(const float* __re
     }
 }
 
-int stats_groups(const Geom& g) { return (g.N + kBPW - 1) / kBPW; }
+int stats_bpw(const Geom& g) {
+    int64_t groups = std::max<int64_t>(1, kResidentWGs / g.BH);
+    groups = std::min<int64_t>(groups, (g.N + kMinBPW - 1) / kMinBPW);
+    return (int)((g.N + groups - 1) / groups);
+}
+
+int stats_groups(const Geom& g) {
+    const int bpw = stats_bpw(g);
+    return (g.N + bpw - 1) / bpw;
+}
 
 }  // namespace
 
@@ -350,14 +365,14 @@ size_t stats_workspace_bytes(const Geom& g) {
 hipError_t launch_block_stats(const Geom& g, int dtype, int second_order, const void* q, const void* k,
                               const void* v, const pisa_stats_t* st, void* workspace,
                               hipStream_t stream) {
-    const int G = stats_groups(g);
+    const int G = stats_groups(g), bpw = stats_bpw(g);
     dim3 grid(G, (unsigned)g.BH), block(kThreads);
     float* hpart = static_cast<float*>(workspace);
     StatsOut out{st->qbar, st->q2bar, st->kbar, st->vsum, st->ksig2, st->kbar_c, st->vbar_c, st->kpack,
                  dtype == PISA_BF16 ? st->kbpack : nullptr};
 #define PISA_STATS_LAUNCH(KERN, TT, DD)                                                            \
     hipLaunchKernelGGL(KERN<DD>, grid, block, 0, stream, static_cast<const TT*>(q),               \
-                       static_cast<const TT*>(k), static_cast<const TT*>(v), g.T, g.N,            \
+                       static_cast<const TT*>(k), static_cast<const TT*>(v), g.T, g.N, bpw,       \
                        second_order, g.scale64, out, hpart)
     if (dtype == PISA_BF16) {
         if (g.D == 128) PISA_STATS_LAUNCH(stats_bf16_kernel, bf16_t, 128);

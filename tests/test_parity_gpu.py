@@ -12,7 +12,9 @@ Tolerances (from the operator's specification and the arithmetic):
   split of the returned hsum; V-hat is the fp64 sum
   rounded once to fp32; the bf16 copies are bit-exact roundings; H within
   64 u sum_t |k_ta||v_tb| elementwise (u = 2^-24; fp32 accumulation of
-  bf16 products over 2048-row partials, sqrt(n) u growth with a 1.4x margin).
+  bf16 products over block-range partials of at most 5.7K rows, 16 products
+  per MFMA step, so about 360 rounded additions per partial: a sqrt(n) u
+  growth of ~19 u, and the partials are summed in fp64).
 """
 
 import math

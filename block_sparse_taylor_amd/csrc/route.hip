@@ -118,6 +118,35 @@ __device__ __forceinline__ Key wave_radix_select(int n, int need, KeyFn key, Tak
     return prefix;
 }
 
+// The need-th largest of the wave's 32-bit keys (KPL per lane, in registers;
+// 0 marks an excluded slot, below every real key): a bitwise search from the
+// top bit down, counting keys >= the candidate with ballots (no atomics).
+// need_eq: how many keys equal to the result belong to the selection.
+constexpr int kKeysPerLane = 36;       // the fast kernel's rows: N <= 64 * 36
+template <int KPL, typename KeyFn>
+__device__ __forceinline__ uint32_t wave_select32(int n, int need, KeyFn key, int* need_eq) {
+    const int lane = threadIdx.x & 63;
+    uint32_t kv[KPL];
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) {
+        const int j = 64 * i + lane;
+        kv[i] = j < n ? key(j) : 0u;
+    }
+    uint32_t t = 0;
+    for (int b = 31; b >= 0; --b) {
+        const uint32_t cand = t | (1u << b);
+        int cnt = 0;
+#pragma unroll
+        for (int i = 0; i < KPL; ++i) cnt += __popcll(__ballot(kv[i] >= cand));
+        if (cnt >= need) t = cand;
+    }
+    int gt = 0;
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) gt += __popcll(__ballot(kv[i] > t));
+    *need_eq = need - gt;
+    return t;
+}
+
 // LDS of the fast kernel: fp64 pooled query statistics, fp32 score rows of
 // pitch NP, per-wave radix histograms, close-call lists and taken-bit masks.
 __host__ __device__ inline int fast_np(int N) { return (N + 3) & ~3; }
@@ -276,8 +305,11 @@ __global__ __launch_bounds__(kThreads) void route_fast_kernel(
             const double bound = s64 * sqrt(qn) * kmax + (second_order ? lnB : 0.0);
             const float eps = (float)(4.0 * (D + 8) * kU * bound) + 1e-30f;
             int need_eq;
-            const uint32_t tk = wave_radix_select<uint32_t, 32>(
-                N, k, [&](int j) { return key32(sr[j]); }, is_cand, hist, &need_eq);
+            auto ckey = [&](int j) { return is_cand(j) ? key32(sr[j]) : 0u; };
+            const int nk = (N + 63) / 64;
+            const uint32_t tk = nk <= 8    ? wave_select32<8>(N, k, ckey, &need_eq)
+                                : nk <= 16 ? wave_select32<16>(N, k, ckey, &need_eq)
+                                           : wave_select32<kKeysPerLane>(N, k, ckey, &need_eq);
             const float tau = unkey32(tk);
             const float hi_thr = tau + 2.f * eps, lo_thr = tau - 2.f * eps;
             // certain members (above the band around tau) and the close calls
@@ -309,6 +341,29 @@ __global__ __launch_bounds__(kThreads) void route_fast_kernel(
                 }
                 return rr;
             };
+            // the same score with the whole wave on one block: each lane takes
+            // two dims (one 16-byte load, contiguous across lanes), then a
+            // wave reduction (the fp64 sum in another order; decisions stay
+            // those of float64 up to near-exact ties)
+            auto exact_wave = [&](int j) {
+                double dot = 0.0, w = 0.0;
+                if (2 * lane < D) {
+                    const d2_t x = *reinterpret_cast<const d2_t*>(kb + (int64_t)j * D + 2 * lane);
+                    dot = fma(qb_s[r * D + 2 * lane], x.x, qb_s[r * D + 2 * lane + 1] * x.y);
+                    if (second_order) {
+                        const d2_t y = *reinterpret_cast<const d2_t*>(sg + (int64_t)j * D + 2 * lane);
+                        w = fma(q2_s[r * D + 2 * lane], y.x, q2_s[r * D + 2 * lane + 1] * y.y);
+                    }
+                }
+#pragma unroll
+                for (int off = 32; off > 0; off >>= 1) {
+                    dot += __shfl_xor(dot, off);
+                    if (second_order) w += __shfl_xor(w, off);
+                }
+                double rr = s64 * dot;
+                if (second_order) rr += fmin(0.5 * w, lnB);
+                return rr;
+            };
             auto ambiguous = [&](int j) {
                 const float x = sr[j];
                 return is_cand(j) && x >= lo_thr && x <= hi_thr;
@@ -322,10 +377,14 @@ __global__ __launch_bounds__(kThreads) void route_fast_kernel(
                 for (int w = lane; w < NW; w += 64) tbits[w] = 0u;
                 double rmine = 0.0;
                 int jmine = -1;
-                if (lane < ca) {
-                    jmine = amb_j[lane];
-                    rmine = exact(jmine);
-                    amb_r[lane] = rmine;
+                for (int c = 0; c < ca; ++c) {     // ca <= kAmbCap here; uniform
+                    const int jc = amb_j[c];
+                    const double rc = exact_wave(jc);
+                    if (lane == c) {
+                        jmine = jc;
+                        rmine = rc;
+                        amb_r[c] = rc;
+                    }
                 }
                 __builtin_amdgcn_wave_barrier();
                 __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -507,7 +566,7 @@ hipError_t launch_route_topk(const Geom& g, const pisa_params_t* p, const pisa_s
     if (p->topk == 0 && !so) return hipSuccess;
     dim3 block(kThreads);
     const size_t lds = fast_lds_bytes(g.D, g.N, so);
-    if (lds + 64 <= (size_t)kLdsMax) {
+    if (lds + 64 <= (size_t)kLdsMax && g.N <= 64 * kKeysPerLane) {
         static bool attr_set[2][2] = {{false, false}, {false, false}};
         bool& set = attr_set[g.D == 128][so ? 1 : 0];
         auto fn = g.D == 128 ? (so ? &route_fast_kernel<128, true> : &route_fast_kernel<128, false>)

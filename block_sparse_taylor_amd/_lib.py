@@ -37,7 +37,8 @@ class Stats(ctypes.Structure):
     _fields_ = [("qbar", ctypes.c_void_p), ("q2bar", ctypes.c_void_p), ("kbar", ctypes.c_void_p),
                 ("vsum", ctypes.c_void_p), ("ksig2", ctypes.c_void_p), ("hsum", ctypes.c_void_p),
                 ("kbar_c", ctypes.c_void_p), ("vbar_c", ctypes.c_void_p), ("kpack", ctypes.c_void_p),
-                ("hpack", ctypes.c_void_p), ("kbpack", ctypes.c_void_p)]
+                ("hpack", ctypes.c_void_p), ("kbpack", ctypes.c_void_p),
+                ("kbar_r", ctypes.c_void_p)]
 
 
 class PisaError(RuntimeError):

@@ -159,7 +159,7 @@ __host__ __device__ inline size_t fast_lds_bytes(int D, int N, int second_order)
 template <int D, bool SO>
 __global__ __launch_bounds__(kThreads) void route_fast_kernel(
     const double* __restrict__ qbar, const double* __restrict__ q2bar, const double* __restrict__ kbar,
-    const double* __restrict__ ksig2, int N, double s64, int topk, int band,
+    const float* __restrict__ kbar_r, const double* __restrict__ ksig2, int N, double s64, int topk, int band,
     int32_t* __restrict__ idx, float* __restrict__ wgate) {
     constexpr int KS = D / 4;       // 16x16x4 k-steps; MFMA k-slot (ks, l/16) <-> dim (D/4)(l/16) + ks
     constexpr bool second_order = SO;
@@ -193,8 +193,8 @@ __global__ __launch_bounds__(kThreads) void route_fast_kernel(
 
     // ---- scores: S[r][j] = s qbar_r . kbar_j (+ min(w, ln B)) via fp32 MFMA.
     // Wave w takes the 16-column chunks c = w, w+4, ...; lane (m16, g4) needs
-    // kbar[16 c + m16][(D/4) g4 + ks] for ks < KS: KS/2 contiguous 16-byte
-    // loads, issued one chunk ahead of the MFMAs that use them.
+    // kbar[16 c + m16][(D/4) g4 + ks] for ks < KS, which kbar_r holds as D/16
+    // 1 KB runs per chunk (16 bytes per lane), loaded one chunk ahead.
     typedef double d2_t __attribute__((ext_vector_type(2)));
     const int m16 = lane & 15, g4 = lane >> 4;
     float a[KS], a2[KS];
@@ -207,30 +207,29 @@ __global__ __launch_bounds__(kThreads) void route_fast_kernel(
     const double* sg = SO ? ksig2 + bh * (int64_t)N * D : nullptr;
     float kmax2 = 0.f;
     const int NC = (N + 15) / 16;
-    auto kptr = [&](const double* base, int c) {   // this lane's 16-byte-aligned run of chunk c
+    auto kptr = [&](const double* base, int c) {   // this lane's 16-byte-aligned run of chunk c (fp64)
         const int col = min(c * 16 + m16, N - 1);
         return reinterpret_cast<const d2_t*>(base + (int64_t)col * D + (D / 4) * g4);
     };
-    d2_t kv[KS / 2];
-    if (wave < NC) {
-        const d2_t* src = kptr(kb, wave);
+    const float4* kr4 = reinterpret_cast<const float4*>(kbar_r + bh * (int64_t)NC * 16 * D);
+    float4 kv[KS / 4];
+    auto kload = [&](int c) {
 #pragma unroll
-        for (int h = 0; h < KS / 2; ++h) kv[h] = src[h];
-    }
+        for (int qq = 0; qq < KS / 4; ++qq) kv[qq] = kr4[((int64_t)c * (KS / 4) + qq) * 64 + lane];
+    };
+    if (wave < NC) kload(wave);
     for (int c = wave; c < NC; c += 4) {
         const int col = c * 16 + m16;
         const bool ok = col < N;
         float b[KS];
 #pragma unroll
-        for (int h = 0; h < KS / 2; ++h) {
-            b[2 * h] = ok ? (float)kv[h].x : 0.f;
-            b[2 * h + 1] = ok ? (float)kv[h].y : 0.f;
+        for (int qq = 0; qq < KS / 4; ++qq) {
+            b[4 * qq + 0] = ok ? kv[qq].x : 0.f;
+            b[4 * qq + 1] = ok ? kv[qq].y : 0.f;
+            b[4 * qq + 2] = ok ? kv[qq].z : 0.f;
+            b[4 * qq + 3] = ok ? kv[qq].w : 0.f;
         }
-        if (c + 4 < NC) {   // prefetch the next chunk
-            const d2_t* src = kptr(kb, c + 4);
-#pragma unroll
-            for (int h = 0; h < KS / 2; ++h) kv[h] = src[h];
-        }
+        if (c + 4 < NC) kload(c + 4);   // the next chunk
         f4_t acc = {0.f, 0.f, 0.f, 0.f}, accw = {0.f, 0.f, 0.f, 0.f};
         float n2 = 0.f;
 #pragma unroll
@@ -578,7 +577,7 @@ hipError_t launch_route_topk(const Geom& g, const pisa_params_t* p, const pisa_s
             set = true;
         }
         dim3 grid((g.N + kQB - 1) / kQB, (unsigned)g.BH);
-        hipLaunchKernelGGL(fn, grid, block, lds, stream, st->qbar, st->q2bar, st->kbar, st->ksig2, g.N,
+        hipLaunchKernelGGL(fn, grid, block, lds, stream, st->qbar, st->q2bar, st->kbar, st->kbar_r, st->ksig2, g.N,
                            g.scale64, p->topk, p->band, idx, wgate);
     } else {
         dim3 grid(g.N, (unsigned)g.BH);

@@ -41,12 +41,13 @@ struct StatsOut {
     void* vbar_c;
     void* kpack;      // bf16 only: K in the fused kernel's operand order
     void* kbpack;     // bf16 only: kbar_c in the same order, per group of 64 blocks
+    float* kbar_r;    // kbar in fp32, in the router's MFMA operand order
 };
 
 // Column statistics of one block from its LDS tiles (row pitch ld).
 template <typename T, int D>
 __device__ __forceinline__ void column_stats(const T* tq, const T* tk, const T* tv, int ld, int rows,
-                                             int64_t off, int n_blocks, int second_order, double s64,
+                                             int64_t bh, int j, int n_blocks, int second_order, double s64,
                                              const StatsOut& out, double* red, float* kb_s,
                                              float* vs_s) {
     constexpr int H = kThreads / D;           // threads per column
@@ -88,13 +89,19 @@ __device__ __forceinline__ void column_stats(const T* tq, const T* tk, const T* 
         }
         const double n = (double)rows;
         const double mean = a[2] / n;
+        const int64_t off = (bh * n_blocks + j) * D;
         out.qbar[off + c] = a[0] / n;
         out.kbar[off + c] = mean;
+        {
+            // router operand order: key j = 16 cc + n, dim c = (D/4) g + 4 q + e
+            const int cc = j / 16, n = j % 16, g = c / (D / 4), q = (c % (D / 4)) / 4, e = c % 4;
+            out.kbar_r[bh * (int64_t)((n_blocks + 15) / 16) * 16 * D +
+                       (((int64_t)cc * (D / 16) + q) * 64 + 16 * g + n) * 4 + e] = (float)mean;
+        }
         static_cast<T*>(out.kbar_c)[off + c] = store_cast<T>((float)mean);
         if (out.kbpack) {
             // block j = row j % 64 of virtual group j / 64, laid out like kpack
-            const int64_t bhj = off / D, bh = bhj / n_blocks, j = bhj % n_blocks;
-            const int r = (int)(j % 64);
+            const int r = j % 64;
             const int64_t gbase = (bh * ((n_blocks + 63) / 64) + j / 64) * (int64_t)(64 * D);
             static_cast<bf16_t*>(out.kbpack)[gbase + (((r / 32) * (D / 8) + c / 8) * 32 + r % 32) * 8 + c % 8] =
                 f32_to_bf16((float)mean);
@@ -118,7 +125,7 @@ __device__ __forceinline__ void column_stats(const T* tq, const T* tk, const T* 
 // C[a][b] += sum_t K[t][a] V[t][b]: A = K^T and B = V, both gathered
 // column-wise from the row-major LDS tiles.
 template <int D>
-__global__ __launch_bounds__(kThreads) void stats_bf16_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void stats_bf16_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, int T,
     int N, int bpw, int second_order, double s64, StatsOut out, float* __restrict__ hpart) {
     constexpr int LD = D + kPad;
@@ -222,8 +229,7 @@ __global__ __launch_bounds__(kThreads) void stats_bf16_kernel(
             }
         }
 
-        const int64_t off = (bh * N + j) * D;
-        column_stats<bf16_t, D>(sq, sk, sv, LD, rows, off, N, second_order, s64, out, red, kb_s, vs_s);
+        column_stats<bf16_t, D>(sq, sk, sv, LD, rows, bh, j, N, second_order, s64, out, red, kb_s, vs_s);
         __syncthreads();  // kb_s / vs_s visible
         // acc -= kbar_j (x) V-hat_j
 #pragma unroll
@@ -296,7 +302,7 @@ __global__ __launch_bounds__(kThreads) void stats_f32_kernel(
             sv[row * LD + col] = ok ? v[o] : 0.f;
         }
         __syncthreads();
-        column_stats<float, D>(sq, sk, sv, LD, rows, (bh * N + j) * D, N, second_order, s64, out, red,
+        column_stats<float, D>(sq, sk, sv, LD, rows, bh, j, N, second_order, s64, out, red,
                                kb_s, vs_s);
         // partial H in fp64 from the exact products and exact column sums
 #pragma unroll
@@ -369,7 +375,7 @@ hipError_t launch_block_stats(const Geom& g, int dtype, int second_order, const 
     dim3 grid(G, (unsigned)g.BH), block(kThreads);
     float* hpart = static_cast<float*>(workspace);
     StatsOut out{st->qbar, st->q2bar, st->kbar, st->vsum, st->ksig2, st->kbar_c, st->vbar_c, st->kpack,
-                 dtype == PISA_BF16 ? st->kbpack : nullptr};
+                 dtype == PISA_BF16 ? st->kbpack : nullptr, st->kbar_r};
 #define PISA_STATS_LAUNCH(KERN, TT, DD)                                                            \
     hipLaunchKernelGGL(KERN<DD>, grid, block, 0, stream, static_cast<const TT*>(q),               \
                        static_cast<const TT*>(k), static_cast<const TT*>(v), g.T, g.N, bpw,       \

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define PISA_ABI_VERSION 4
+#define PISA_ABI_VERSION 5
 
 typedef enum {
     PISA_OK = 0,
@@ -115,6 +115,10 @@ typedef struct {
  * of 64 consecutive blocks (the keys of the virtual tokens), bf16
  * [B,H,ceil(N/64),64*D]: kbpack[b,h,g] holds rows kbar_c[b,h,64 g + r] as kpack
  * holds rows of k, and 0 for 64 g + r >= N.
+ * kbar_r is kbar rounded to fp32 in the router's MFMA operand order, fp32
+ * [B,H,ceil(N/16)*16*D]: key j = 16 c + n, dim d = (D/4) g + 4 q + e (g < 4,
+ * q < D/16, e < 4) sits at ((c * D/16 + q) * 64 + 16 g + n) * 4 + e; slots of
+ * keys past N are unspecified (the router masks them).
  */
 typedef struct {
     double *qbar;
@@ -128,6 +132,7 @@ typedef struct {
     void *kpack;
     void *hpack;
     void *kbpack;
+    float *kbar_r;
 } pisa_stats_t;
 
 /* ABI version of the library (PISA_ABI_VERSION). */
@@ -169,7 +174,7 @@ pisa_status_t pisa_block_stats(const pisa_shape_t *shape, const pisa_params_t *p
  * wgate: fp32 [B,H,N,N], required iff second_order: the gated term used by
  *   the virtual-token logits: w_ij where w_ij <= ln B, and 0 where w_ij is
  *   larger (the README's gate, not a clamp), decided as in float64.
- * Reads stats->qbar, kbar (and q2bar, ksig2 if second_order).
+ * Reads stats->qbar, kbar, kbar_r (and q2bar, ksig2 if second_order).
  */
 pisa_status_t pisa_route_topk(const pisa_shape_t *shape, const pisa_params_t *params,
                               const pisa_stats_t *stats, int32_t *idx, float *wgate,

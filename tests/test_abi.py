@@ -32,7 +32,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pisa_abi_version() == 4
+    assert lib.pisa_abi_version() == 5
     for code in range(9):
         assert lib.pisa_status_str(code)
     assert lib.pisa_status_str(99) == b"unknown status"
@@ -72,7 +72,7 @@ MIS = FAKE + 4
 
 def stats(**kw):
     d = dict(qbar=FAKE, q2bar=None, kbar=FAKE, vsum=FAKE, ksig2=None, hsum=FAKE, kbar_c=FAKE, vbar_c=FAKE,
-             kpack=FAKE, hpack=FAKE, kbpack=FAKE)
+             kpack=FAKE, hpack=FAKE, kbpack=FAKE, kbar_r=FAKE)
     d.update(kw)
     return _lib.Stats(**d)
 
@@ -116,6 +116,8 @@ def test_stats_validation(lib):
     assert call_stats(lib, st=stats(kpack=MIS)) == E["PISA_ERR_ALIGN"]
     assert call_stats(lib, st=stats(hpack=None)) == E["PISA_ERR_NULL"]
     assert call_stats(lib, st=stats(kbpack=None)) == E["PISA_ERR_NULL"]
+    assert call_stats(lib, st=stats(kbar_r=None)) == E["PISA_ERR_NULL"]
+    assert call_stats(lib, st=stats(kbar_r=MIS)) == E["PISA_ERR_ALIGN"]
     # second order needs ksig2 and q2bar
     assert call_stats(lib, p=_lib.Params(4, 1, 1, 1, 0)) == E["PISA_ERR_NULL"]
     assert call_stats(lib, p=_lib.Params(4, 1, 1, 1, 0), st=stats(ksig2=FAKE)) == E["PISA_ERR_NULL"]
@@ -132,6 +134,7 @@ def test_route_validation(lib):
     assert call_route(lib, st=stats(qbar=None)) == E["PISA_ERR_NULL"]
     assert call_route(lib, idx=None) == E["PISA_ERR_NULL"]
     assert call_route(lib, st=stats(kbar=None)) == E["PISA_ERR_NULL"]
+    assert call_route(lib, st=stats(kbar_r=None)) == E["PISA_ERR_NULL"]
     # second order: q2bar, ksig2 and wgate required
     assert call_route(lib, p=_lib.Params(4, 1, 1, 1, 0)) == E["PISA_ERR_NULL"]
     assert call_route(lib, p=_lib.Params(4, 1, 1, 1, 0), st=stats(ksig2=FAKE)) == E["PISA_ERR_NULL"]

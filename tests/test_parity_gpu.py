@@ -105,7 +105,18 @@ def test_block_stats(name):
     hp = run.host(run.st.hpack) if w.dtype == "bf16" else None
     kbp = run.st.kbpack.view(torch.int16).cpu().numpy().view(np.uint16) if w.dtype == "bf16" else None
     kbb = run.st.kbar_c.view(torch.int16).cpu().numpy().view(np.uint16) if w.dtype == "bf16" else None
+    kbr = run.host(run.st.kbar_r)
     for h in heads:
+        # kbar in fp32, router operand order: per 16-column chunk and 16-dim
+        # step q, 64 lanes (g = dim quarter, n = column) of 4 dims each
+        D = w.head_dim
+        NC = -(-run.N // 16)
+        kpad = np.zeros((NC * 16, D), np.float32)
+        kpad[:run.N] = kbar[0, h].astype(np.float32)
+        want_r = kpad.reshape(NC, 16, 4, D // 16, 4).transpose(0, 3, 2, 1, 4)
+        valid = (np.arange(NC * 16) < run.N).reshape(NC, 16)[:, None, None, :, None]
+        got_r = kbr[0, h].reshape(want_r.shape)
+        assert np.array_equal(np.where(valid, got_r, 0), want_r), h
         if kp is not None:
             # packed K is a pure re-ordering of k's bits: per block and 32-row
             # half, 16-byte chunks chunk-major, then row; zero rows past T

@@ -116,6 +116,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=8,
                     help="heads the oracle evaluates for the CPU baseline")
+    ap.add_argument("--no-phase1", action="store_true",
+                    help="skip the extra Phase 1 (exact tiles only) launches, so that a kernel "
+                         "trace or counter run sees only the full fused launches")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run a plain copy of COPY_BYTES three times "
                          "(the reference kernel for the HBM byte counters)")
@@ -198,6 +201,25 @@ def main():
     route_ms = float(np.mean([r[1].elapsed_time(r[2]) for r in recs]))
     attn_ms = float(np.mean([r[2].elapsed_time(r[3]) for r in recs]))
 
+    # Phase 1 alone (exact tiles only, phase_mask bit 0), after the timed steps
+    # and outside them, on the same inputs and routing table
+    phase1_ms = None
+    if not args.no_phase1:
+        o1 = torch.empty_like(q)
+        p1 = [ev() for _ in range(args.steps + 1)]
+        for _ in range(2):
+            P.pisa_attn_fwd(q, k, v, st, idx if topk else None, wg, band=w.band, second_order=so,
+                            phase_mask=1, out=o1)
+        torch.cuda.synchronize()
+        p1[0].record(stream)
+        for e_ in p1[1:]:
+            P.pisa_attn_fwd(q, k, v, st, idx if topk else None, wg, band=w.band, second_order=so,
+                            phase_mask=1, out=o1)
+            e_.record(stream)
+        torch.cuda.synchronize()
+        phase1_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(p1[:-1], p1[1:])]))
+        del o1
+
     # ---- algorithmic work of the fused kernel (from the routing table actually used)
     idx_h = idx.cpu().numpy().reshape(B * H, N, topk)
     nrow = np.array([min(64, T - 64 * j) for j in range(N)], dtype=np.int64)
@@ -211,6 +233,7 @@ def main():
             exact_pairs += int(nrow[i]) * keys
             virt_pairs += int(nrow[i]) * (N - len(sel))
     attn_flops = 4 * D * (exact_pairs + virt_pairs) + 2 * D * D * B * H * T
+    phase1_tflops = 4 * D * exact_pairs / (phase1_ms * 1e-3) / 1e12 if phase1_ms else None
     dense_flops = 4.0 * B * H * T * T * D
     attn_tflops = attn_flops / (attn_ms * 1e-3) / 1e12
 
@@ -219,12 +242,13 @@ def main():
     G = -(-N // -(-N // groups))
     BHND = B * H * N * D
     stats_bytes = (3 * B * H * T * D * e                     # read Q, K, V
-                   + BHND * (8 + 8 + 4 + 2 * e)              # qbar, kbar, vsum, kbar_c, vbar_c
+                   + BHND * (8 + 8 + 4 + 4 + 2 * e)          # qbar, kbar, kbar_r, vsum, kbar_c, vbar_c
                    + (BHND * 16 if so else 0)                # q2bar, ksig2
                    + (B * H * N * 64 * D * 2 if w.dtype == "bf16" else 0)   # packed K copy
                    + B * H * D * D * 4                       # hsum
                    + 2 * B * H * G * D * D * 4)              # partial H write + read
-    route_bytes = (BHND * 16 * (2 if so else 1)              # qbar, kbar (+ q2bar, ksig2)
+    route_bytes = (BHND * 12                                 # qbar (fp64), kbar_r (fp32)
+                   + (BHND * 16 if so else 0)                # q2bar, ksig2
                    + B * H * N * topk * 4                    # idx
                    + (B * H * N * N * 4 if so else 0))       # gated w table
 
@@ -248,6 +272,9 @@ def main():
         "pisa_attn_fwd": {"ms": round(attn_ms, 4),
                           "dense_equiv_tflops": round(dense_flops / (attn_ms * 1e-3) / 1e12, 2),
                           "algorithmic_tflop": round(attn_flops / 1e12, 4)},
+        "phase1_exact": None if phase1_ms is None else {
+            "ms": round(phase1_ms, 4), "algorithmic_tflop": round(4 * D * exact_pairs / 1e12, 4),
+            "tflops": round(phase1_tflops, 2), "frac_mfma": round(phase1_tflops / PEAK_BF16_TFLOPS, 4)},
         "pisa_block_stats": {"ms": round(stats_ms, 4), "algorithmic_bytes": stats_bytes,
                              "gbs": round(stats_bytes / (stats_ms * 1e-3) / 1e9, 1),
                              "frac_hbm": round(stats_bytes / (stats_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},

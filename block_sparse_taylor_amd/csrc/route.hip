@@ -123,15 +123,8 @@ __device__ __forceinline__ Key wave_radix_select(int n, int need, KeyFn key, Tak
 // top bit down, counting keys >= the candidate with ballots (no atomics).
 // need_eq: how many keys equal to the result belong to the selection.
 constexpr int kKeysPerLane = 36;       // the fast kernel's rows: N <= 64 * 36
-template <int KPL, typename KeyFn>
-__device__ __forceinline__ uint32_t wave_select32(int n, int need, KeyFn key, int* need_eq) {
-    const int lane = threadIdx.x & 63;
-    uint32_t kv[KPL];
-#pragma unroll
-    for (int i = 0; i < KPL; ++i) {
-        const int j = 64 * i + lane;
-        kv[i] = j < n ? key(j) : 0u;
-    }
+template <int KPL>
+__device__ __forceinline__ uint32_t wave_select32(const uint32_t (&kv)[KPL], int need, int* need_eq) {
     uint32_t t = 0;
     for (int b = 31; b >= 0; --b) {
         const uint32_t cand = t | (1u << b);
@@ -147,17 +140,21 @@ __device__ __forceinline__ uint32_t wave_select32(int n, int need, KeyFn key, in
     return t;
 }
 
-// LDS of the fast kernel: fp64 pooled query statistics, fp32 score rows of
-// pitch NP, per-wave radix histograms, close-call lists and taken-bit masks.
+// LDS of the fast kernel: the fp64 pooled q'^2 rows (second order only), fp32
+// score rows of pitch NP, per-wave radix histograms, close-call lists and
+// taken-bit masks. At N = 512 without the second order it is 39.3 KB, so four
+// workgroups share a CU.
 __host__ __device__ inline int fast_np(int N) { return (N + 3) & ~3; }
 __host__ __device__ inline size_t fast_lds_bytes(int D, int N, int second_order) {
     const int NP = fast_np(N);
-    return (size_t)8 * kQB * D * (second_order ? 2 : 1) + (size_t)4 * kQB * NP + 4 * 4 * 256 +
+    return (size_t)8 * kQB * D * (second_order ? 1 : 0) + (size_t)4 * kQB * NP + 4 * 4 * 256 +
            (size_t)4 * kAmbCap * (4 + 8) + (size_t)4 * 4 * ((NP + 31) / 32);
 }
 
-template <int D, bool SO>
-__global__ __launch_bounds__(kThreads) void route_fast_kernel(
+// KPL: keys per lane of a score row (N <= 64 KPL); rows of up to 1024 blocks
+// without the second order fit four waves per SIMD.
+template <int D, bool SO, int KPL>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(SO || KPL > 16 ? 2 : 4))) void route_fast_kernel(
     const double* __restrict__ qbar, const double* __restrict__ q2bar, const double* __restrict__ kbar,
     const float* __restrict__ kbar_r, const double* __restrict__ ksig2, int N, double s64, int topk, int band,
     int32_t* __restrict__ idx, float* __restrict__ wgate) {
@@ -165,8 +162,7 @@ __global__ __launch_bounds__(kThreads) void route_fast_kernel(
     constexpr bool second_order = SO;
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     const int NP = fast_np(N), NW = (NP + 31) / 32;
-    double* qb_s = reinterpret_cast<double*>(lds);
-    double* q2_s = qb_s + kQB * D;                                   // second order only
+    double* q2_s = reinterpret_cast<double*>(lds);                   // second order only
     float* score_s = reinterpret_cast<float*>(q2_s + (second_order ? kQB * D : 0));
     unsigned* hist_s = reinterpret_cast<unsigned*>(score_s + kQB * NP);
     int* amb_j_s = reinterpret_cast<int*>(hist_s + 4 * 256);
@@ -182,14 +178,15 @@ __global__ __launch_bounds__(kThreads) void route_fast_kernel(
     const double lnB = log((double)kBlock);
     const float lnBf = (float)lnB;
 
-    // pooled statistics of the tile's query blocks (zeros past N)
-    for (int e = tid; e < kQB * D; e += kThreads) {
-        const int r = e / D;
-        const int64_t o = (bh * N + i0 + r) * (int64_t)D + e % D;
-        qb_s[e] = r < nq ? qbar[o] : 0.0;
-        if (second_order) q2_s[e] = r < nq ? q2bar[o] : 0.0;
+    // pooled q'^2 of the tile's query blocks (zeros past N), second order only
+    if (second_order) {
+        for (int e = tid; e < kQB * D; e += kThreads) {
+            const int r = e / D;
+            q2_s[e] = r < nq ? q2bar[(bh * N + i0 + r) * (int64_t)D + e % D] : 0.0;
+        }
+        __syncthreads();
     }
-    __syncthreads();
+    const double* qrows = qbar + (bh * N + i0) * (int64_t)D;   // fp64 pooled queries of the tile
 
     // ---- scores: S[r][j] = s qbar_r . kbar_j (+ min(w, ln B)) via fp32 MFMA.
     // Wave w takes the 16-column chunks c = w, w+4, ...; lane (m16, g4) needs
@@ -198,11 +195,17 @@ __global__ __launch_bounds__(kThreads) void route_fast_kernel(
     typedef double d2_t __attribute__((ext_vector_type(2)));
     const int m16 = lane & 15, g4 = lane >> 4;
     float a[KS], a2[KS];
+    {
+        const d2_t* qa = reinterpret_cast<const d2_t*>(qrows + min(m16, nq - 1) * D + (D / 4) * g4);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        a[ks] = (float)qb_s[m16 * D + (D / 4) * g4 + ks];
-        a2[ks] = SO ? (float)q2_s[m16 * D + (D / 4) * g4 + ks] : 0.f;
+        for (int h = 0; h < KS / 2; ++h) {
+            const d2_t x = qa[h];
+            a[2 * h] = m16 < nq ? (float)x.x : 0.f;
+            a[2 * h + 1] = m16 < nq ? (float)x.y : 0.f;
+        }
     }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) a2[ks] = SO ? (float)q2_s[m16 * D + (D / 4) * g4 + ks] : 0.f;
     const double* kb = kbar + bh * (int64_t)N * D;
     const double* sg = SO ? ksig2 + bh * (int64_t)N * D : nullptr;
     float kmax2 = 0.f;
@@ -281,56 +284,61 @@ __global__ __launch_bounds__(kThreads) void route_fast_kernel(
     const double kmax = sqrt((double)fmaxf(fmaxf(kmax_s[0], kmax_s[1]), fmaxf(kmax_s[2], kmax_s[3]))) *
                         (1.0 + 1e-6);
 
-    // ---- selection: wave w handles rows w, w+4, w+8, w+12
+    // ---- selection: wave w handles rows w, w+4, w+8, w+12. A row's candidate
+    // keys stay in registers (lane l holds columns 64 i + l, i < KPL) from the
+    // threshold search through the classification and the ascending write.
     unsigned* hist = hist_s + wave * 256;
     int* amb_j = amb_j_s + wave * kAmbCap;
     double* amb_r = amb_r_s + wave * kAmbCap;
     uint32_t* tbits = take_s + wave * NW;
     const unsigned long long lt_mask = (1ull << lane) - 1ull;
-    for (int r = wave; r < nq; r += 4) {
+    auto row_pass = [&](int r) {
         const int i = i0 + r;
         int32_t* out = idx + (bh * N + i) * (int64_t)topk;
         const int blo = max(0, i - band), bhi = min(N - 1, i + band);
         const int ncand = N - (bhi - blo + 1);
         const int k = min(topk, ncand);
         const float* sr = score_s + r * NP;
+        const double* qg = qrows + (int64_t)r * D;   // fp64 pooled query of row i
         auto is_cand = [&](int j) { return j < blo || j > bhi; };
         int written = 0;
         if (k > 0) {
+            uint32_t kv[KPL];
+#pragma unroll
+            for (int t = 0; t < KPL; ++t) {
+                const int j = 64 * t + lane;
+                const float x = sr[min(j, N - 1)];
+                kv[t] = j < N && is_cand(j) ? key32(x) : 0u;
+            }
             double qn = 0.0;
-            for (int d = lane; d < D; d += 64) qn += qb_s[r * D + d] * qb_s[r * D + d];
+            for (int d = lane; d < D; d += 64) qn += qg[d] * qg[d];
 #pragma unroll
             for (int off = 32; off > 0; off >>= 1) qn += __shfl_xor(qn, off);
             const double bound = s64 * sqrt(qn) * kmax + (second_order ? lnB : 0.0);
             const float eps = (float)(4.0 * (D + 8) * kU * bound) + 1e-30f;
             int need_eq;
-            auto ckey = [&](int j) { return is_cand(j) ? key32(sr[j]) : 0u; };
-            const int nk = (N + 63) / 64;
-            const uint32_t tk = nk <= 8    ? wave_select32<8>(N, k, ckey, &need_eq)
-                                : nk <= 16 ? wave_select32<16>(N, k, ckey, &need_eq)
-                                           : wave_select32<kKeysPerLane>(N, k, ckey, &need_eq);
+            const uint32_t tk = wave_select32<KPL>(kv, k, &need_eq);
             const float tau = unkey32(tk);
-            const float hi_thr = tau + 2.f * eps, lo_thr = tau - 2.f * eps;
-            // certain members (above the band around tau) and the close calls
-            // inside it, the latter listed in ascending j
+            // the band around tau in key space: x > hi <=> key > khi, x >= lo <=> key >= klo
+            const uint32_t khi = key32(tau + 2.f * eps), klo = key32(tau - 2.f * eps);
+            // certain members (above the band) and the close calls inside it,
+            // the latter listed in ascending j
             int cg = 0, ca = 0;
-            for (int base = 0; base < N; base += 64) {
-                const int j = base + lane;
-                const bool cand = j < N && is_cand(j);
-                const float x = cand ? sr[j] : 0.f;
-                const bool in = cand && x > hi_thr;
-                const bool amb = cand && !in && x >= lo_thr;
+#pragma unroll
+            for (int t = 0; t < KPL; ++t) {
+                const bool in = kv[t] > khi;
+                const bool amb = !in && kv[t] >= klo && kv[t] != 0u;
                 cg += __popcll(__ballot(in));
                 const unsigned long long am = __ballot(amb);
                 const int pos = ca + __popcll(am & lt_mask);
-                if (amb && pos < kAmbCap) amb_j[pos] = j;
+                if (amb && pos < kAmbCap) amb_j[pos] = 64 * t + lane;
                 ca += __popcll(am);
             }
             const int need = k - cg;      // members still to choose among the close calls
             auto exact = [&](int j) {     // fp64 score of block j
                 const double* kr = kb + (int64_t)j * D;
                 double dot = 0.0;
-                for (int d = 0; d < D; ++d) dot = fma(qb_s[r * D + d], kr[d], dot);
+                for (int d = 0; d < D; ++d) dot = fma(qg[d], kr[d], dot);
                 double rr = s64 * dot;
                 if (second_order) {
                     const double* sq = sg + (int64_t)j * D;
@@ -344,11 +352,13 @@ __global__ __launch_bounds__(kThreads) void route_fast_kernel(
             // two dims (one 16-byte load, contiguous across lanes), then a
             // wave reduction (the fp64 sum in another order; decisions stay
             // those of float64 up to near-exact ties)
+            d2_t qpair = {0.0, 0.0};
+            if (2 * lane < D) qpair = *reinterpret_cast<const d2_t*>(qg + 2 * lane);
             auto exact_wave = [&](int j) {
                 double dot = 0.0, w = 0.0;
                 if (2 * lane < D) {
                     const d2_t x = *reinterpret_cast<const d2_t*>(kb + (int64_t)j * D + 2 * lane);
-                    dot = fma(qb_s[r * D + 2 * lane], x.x, qb_s[r * D + 2 * lane + 1] * x.y);
+                    dot = fma(qpair.x, x.x, qpair.y * x.y);
                     if (second_order) {
                         const d2_t y = *reinterpret_cast<const d2_t*>(sg + (int64_t)j * D + 2 * lane);
                         w = fma(q2_s[r * D + 2 * lane], y.x, q2_s[r * D + 2 * lane + 1] * y.y);
@@ -364,8 +374,8 @@ __global__ __launch_bounds__(kThreads) void route_fast_kernel(
                 return rr;
             };
             auto ambiguous = [&](int j) {
-                const float x = sr[j];
-                return is_cand(j) && x >= lo_thr && x <= hi_thr;
+                const uint32_t x = key32(sr[j]);
+                return is_cand(j) && x >= klo && x <= khi;
             };
             // mode 0: every close call is in; 1: taken-bit mask; 2: 64-bit radix threshold
             const int mode = need >= ca ? 0 : (ca <= kAmbCap ? 1 : 2);
@@ -406,24 +416,20 @@ __global__ __launch_bounds__(kThreads) void route_fast_kernel(
             }
             // write ascending
             int eq_seen = 0;
-            for (int base = 0; base < N; base += 64) {
-                const int j = base + lane;
-                bool take = false;
+#pragma unroll
+            for (int t = 0; t < KPL; ++t) {
+                const int j = 64 * t + lane;
+                bool take = kv[t] > khi;
                 bool eq = false;
-                if (j < N && is_cand(j)) {
-                    const float x = sr[j];
-                    if (x > hi_thr) {
+                if (!take && kv[t] >= klo && kv[t] != 0u && need > 0) {
+                    if (mode == 0) {
                         take = true;
-                    } else if (x >= lo_thr && need > 0) {
-                        if (mode == 0) {
-                            take = true;
-                        } else if (mode == 1) {
-                            take = (tbits[j >> 5] >> (j & 31)) & 1u;
-                        } else {
-                            const uint64_t kk = key64(exact(j));
-                            take = kk > t64;
-                            eq = kk == t64;
-                        }
+                    } else if (mode == 1) {
+                        take = (tbits[j >> 5] >> (j & 31)) & 1u;
+                    } else {
+                        const uint64_t kk = key64(exact(j));
+                        take = kk > t64;
+                        eq = kk == t64;
                     }
                 }
                 const unsigned long long eqm = __ballot(eq);
@@ -437,7 +443,8 @@ __global__ __launch_bounds__(kThreads) void route_fast_kernel(
             }
         }
         for (int c = written + lane; c < topk; c += 64) out[c] = -1;
-    }
+    };
+    for (int r = wave; r < nq; r += 4) row_pass(r);
 }
 
 // General fallback for long sequences (score rows beyond the LDS): one workgroup per
@@ -566,10 +573,21 @@ hipError_t launch_route_topk(const Geom& g, const pisa_params_t* p, const pisa_s
     dim3 block(kThreads);
     const size_t lds = fast_lds_bytes(g.D, g.N, so);
     if (lds + 64 <= (size_t)kLdsMax && g.N <= 64 * kKeysPerLane) {
-        static bool attr_set[2][2] = {{false, false}, {false, false}};
-        bool& set = attr_set[g.D == 128][so ? 1 : 0];
-        auto fn = g.D == 128 ? (so ? &route_fast_kernel<128, true> : &route_fast_kernel<128, false>)
-                             : (so ? &route_fast_kernel<64, true> : &route_fast_kernel<64, false>);
+        using Fn = void (*)(const double*, const double*, const double*, const float*, const double*, int, double,
+                            int, int, int32_t*, float*);
+        static bool attr_set[2][2][3] = {};
+        const int kc = g.N <= 64 * 8 ? 0 : (g.N <= 64 * 16 ? 1 : 2);
+        static const Fn table[2][2][3] = {
+            {{&route_fast_kernel<64, false, 8>, &route_fast_kernel<64, false, 16>,
+              &route_fast_kernel<64, false, kKeysPerLane>},
+             {&route_fast_kernel<64, true, 8>, &route_fast_kernel<64, true, 16>,
+              &route_fast_kernel<64, true, kKeysPerLane>}},
+            {{&route_fast_kernel<128, false, 8>, &route_fast_kernel<128, false, 16>,
+              &route_fast_kernel<128, false, kKeysPerLane>},
+             {&route_fast_kernel<128, true, 8>, &route_fast_kernel<128, true, 16>,
+              &route_fast_kernel<128, true, kKeysPerLane>}}};
+        bool& set = attr_set[g.D == 128][so ? 1 : 0][kc];
+        const Fn fn = table[g.D == 128][so ? 1 : 0][kc];
         if (!set) {   // opt in to more than 64 KB of dynamic LDS
             const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax - 64);

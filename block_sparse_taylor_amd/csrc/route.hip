@@ -120,8 +120,10 @@ __device__ __forceinline__ Key wave_radix_select(int n, int need, KeyFn key, Tak
 
 // The need-th largest of the wave's 32-bit keys (KPL per lane, in registers;
 // 0 marks an excluded slot, below every real key): a bitwise search from the
-// top bit down, counting keys >= the candidate with ballots (no atomics).
-// need_eq: how many keys equal to the result belong to the selection.
+// top bit down, counting keys >= the candidate with ballots (no atomics). It
+// stops as soon as exactly `need` keys reach the candidate: the answer is then
+// the smallest of those keys (a wave minimum). need_eq: how many keys equal to
+// the result belong to the selection.
 constexpr int kKeysPerLane = 36;       // the fast kernel's rows: N <= 64 * 36
 template <int KPL>
 __device__ __forceinline__ uint32_t wave_select32(const uint32_t (&kv)[KPL], int need, int* need_eq) {
@@ -131,8 +133,18 @@ __device__ __forceinline__ uint32_t wave_select32(const uint32_t (&kv)[KPL], int
         int cnt = 0;
 #pragma unroll
         for (int i = 0; i < KPL; ++i) cnt += __popcll(__ballot(kv[i] >= cand));
-        if (cnt >= need) t = cand;
+        if (cnt >= need) {
+            t = cand;
+            if (cnt == need) break;
+        }
     }
+    // the smallest key >= t (t itself when the search ran to the last bit)
+    uint32_t mn = 0xFFFFFFFFu;
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) mn = kv[i] >= t ? min(mn, kv[i]) : mn;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) mn = min(mn, (uint32_t)__shfl_xor((int)mn, off));
+    t = mn;
     int gt = 0;
 #pragma unroll
     for (int i = 0; i < KPL; ++i) gt += __popcll(__ballot(kv[i] > t));

@@ -28,7 +28,7 @@ from ._lib import PISA_BF16, PISA_F32, PisaError
 
 __all__ = ["PisaStats", "pisa_block_stats", "pisa_route_topk", "pisa_attn_fwd",
            "pisa_attn_fwd_valu", "piecewise_sparse_attention", "num_blocks", "topk_for_density",
-           "PisaError", "library"]
+           "z_order", "reorder_gather", "reorder_scatter", "PisaError", "library"]
 
 BLOCK = 64
 
@@ -188,22 +188,76 @@ def pisa_attn_fwd_valu(q, k, v, stats, idx, wgate=None, band=1, second_order=Fal
                  first_order, phase_mask, scale, out)
 
 
+def z_order(grid, prefix: int = 0) -> torch.Tensor:
+    """Z-order (Morton) visiting order of ``prefix`` fixed tokens then a grid
+    (slowest axis first), as an int32 CPU tensor: perm[i] is the raster token
+    index placed at position i (pisa_z_order; host work, no GPU)."""
+    grid = [int(g) for g in grid]
+    n = int(prefix) + math.prod(grid)
+    perm = torch.empty(n, dtype=torch.int32)
+    g = (ctypes.c_int64 * len(grid))(*grid)
+    _lib.check("pisa_z_order", _lib.load().pisa_z_order(
+        g, len(grid), int(prefix), ctypes.cast(perm.data_ptr(), ctypes.POINTER(ctypes.c_int32)), n))
+    return perm
+
+
+def _reorder(fn_name, src, perm, bhtd, out_shape, out):
+    if perm.dtype != torch.int32 or perm.dim() != 1 or perm.device != src.device:
+        raise ValueError("perm must be an int32 vector on the tensor's device")
+    if perm.numel() != bhtd[2]:
+        raise ValueError("perm must have one entry per token")
+    out = torch.empty(out_shape, dtype=src.dtype, device=src.device) if out is None else out
+    _contig(src, perm, out)
+    sh = _lib.Shape(*bhtd, BLOCK, _dtype_code(src), 0.0)
+    _lib.check(fn_name, getattr(_lib.load(), fn_name)(
+        ctypes.byref(sh), perm.data_ptr(), src.data_ptr(), out.data_ptr(), _stream(src.device)))
+    return out
+
+
+def reorder_gather(x: torch.Tensor, perm: torch.Tensor, out=None) -> torch.Tensor:
+    """[B,T,H,D] -> [B,H,T,D] with out[b,h,i] = x[b, perm[i], h] (pisa_reorder_gather)."""
+    B, T, H, D = x.shape
+    return _reorder("pisa_reorder_gather", x, perm, (B, H, T, D), (B, H, T, D), out)
+
+
+def reorder_scatter(o: torch.Tensor, perm: torch.Tensor, out=None) -> torch.Tensor:
+    """[B,H,T,D] -> [B,T,H,D] with y[b, perm[i], h] = o[b,h,i] (pisa_reorder_scatter)."""
+    B, H, T, D = o.shape
+    return _reorder("pisa_reorder_scatter", o, perm, (B, H, T, D), (B, T, H, D), out)
+
+
 def piecewise_sparse_attention(q, k, v, density=0.125, variant="pisa", band=1, scale=None,
-                               n_sink_blocks=0, cov_bias=False, reorder="none"):
+                               n_sink_blocks=0, cov_bias=False, reorder="none", grid=None,
+                               prefix=0):
     """PISA (variant="pisa") or PISA with the gated second-order term ("pwt").
 
     q, k, v: [B, H, T, D] bf16 or fp32 on the GPU. topk = floor(density * N)
     routed blocks per query block, plus the +-band, are computed exactly.
+    With reorder="morton", q, k, v are token-major [B, T, H, D] in raster
+    order over ``prefix`` fixed tokens then ``grid`` (slowest axis first); the
+    tokens are gathered into Z-order (and [B, H, T, D]) before the operator and
+    the output is scattered back to [B, T, H, D].
     """
-    if n_sink_blocks or cov_bias or reorder != "none":
-        raise NotImplementedError("sink blocks, covariance bias and token reordering are not built")
+    if n_sink_blocks or cov_bias:
+        raise NotImplementedError("sink blocks and the covariance bias are not built")
+    if reorder not in ("none", "morton"):
+        raise ValueError(reorder)
     if variant not in ("pisa", "pwt"):
         raise ValueError(variant)
+    perm = None
+    if reorder == "morton":
+        if grid is None:
+            raise ValueError('reorder="morton" needs the token grid')
+        perm = z_order(grid, prefix).to(q.device)
+        if perm.numel() != q.shape[1]:
+            raise ValueError("prefix + prod(grid) must equal the token count")
+        q, k, v = (reorder_gather(t, perm) for t in (q, k, v))
     so = variant == "pwt"
     N = num_blocks(q.shape[2])
     topk = topk_for_density(density, N)
     topk = min(topk, N)
     st = pisa_block_stats(q, k, v, second_order=so, scale=scale)
     idx, wg = pisa_route_topk(q, st, topk, band=band, second_order=so, scale=scale)
-    return pisa_attn_fwd(q, k, v, st, idx if topk else None, wg, band=band, second_order=so,
-                         scale=scale)
+    o = pisa_attn_fwd(q, k, v, st, idx if topk else None, wg, band=band, second_order=so,
+                      scale=scale)
+    return o if perm is None else reorder_scatter(o, perm)

@@ -19,6 +19,7 @@ PISA_F32, PISA_BF16 = 0, 1
 EXPORTED = (
     "pisa_abi_version", "pisa_status_str", "pisa_num_blocks", "pisa_stats_workspace_bytes",
     "pisa_block_stats", "pisa_route_topk", "pisa_attn_fwd", "pisa_attn_fwd_valu",
+    "pisa_z_order", "pisa_reorder_gather", "pisa_reorder_scatter",
 )
 
 
@@ -76,6 +77,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [P(Shape), P(Params), vp, vp, vp, P(Stats), vp, vp, vp, vp]
+    lib.pisa_z_order.restype = ctypes.c_int
+    lib.pisa_z_order.argtypes = [P(ctypes.c_int64), ctypes.c_int32, ctypes.c_int64, P(ctypes.c_int32),
+                                 ctypes.c_int64]
+    for name in ("pisa_reorder_gather", "pisa_reorder_scatter"):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = [P(Shape), vp, vp, vp, vp]
     _lib = lib
     return lib
 

@@ -59,6 +59,10 @@ hipError_t launch_attn_fwd_valu(const Geom& g, int dtype, const pisa_params_t* p
                                 const void* k, const void* v, const pisa_stats_t* st,
                                 const int32_t* idx, const float* wgate, void* o, hipStream_t stream);
 
+hipError_t launch_reorder(const Geom& g, int64_t batch, int64_t heads, int elem_bytes, bool gather,
+                          const int32_t* perm, const void* src, void* dst, hipStream_t stream);
+void z_order_host(const int64_t* grid, int ndim, int64_t prefix, int32_t* perm);
+
 hipError_t launch_attn_fwd_mfma(const Geom& g, const pisa_params_t* p, const void* q, const void* k,
                                 const void* v, const pisa_stats_t* st, const int32_t* idx,
                                 const float* wgate, void* o, hipStream_t stream);

@@ -183,4 +183,45 @@ pisa_status_t pisa_attn_fwd_valu(const pisa_shape_t* shape, const pisa_params_t*
                                          static_cast<hipStream_t>(stream)));
 }
 
+pisa_status_t pisa_z_order(const int64_t* grid, int32_t ndim, int64_t prefix, int32_t* perm, int64_t n) {
+    if (!grid || !perm) return PISA_ERR_NULL;
+    if (ndim < 1 || ndim > 4 || prefix < 0) return PISA_ERR_SHAPE;
+    int64_t cells = 1;
+    int nb = 1;
+    for (int a = 0; a < ndim; ++a) {
+        if (grid[a] < 1 || grid[a] > 0x7fffffff) return PISA_ERR_SHAPE;
+        cells *= grid[a];
+        if (cells > 0x7fffffff) return PISA_ERR_SHAPE;
+        while ((int64_t{1} << nb) < grid[a]) ++nb;
+    }
+    if (ndim * nb > 63 || prefix > 0x7fffffff - cells || n != prefix + cells) return PISA_ERR_SHAPE;
+    z_order_host(grid, ndim, prefix, perm);
+    return PISA_OK;
+}
+
+static pisa_status_t reorder_common(const pisa_shape_t* shape, const int32_t* perm, const void* src,
+                                    void* dst, bool gather, void* stream) {
+    Geom g;
+    PISA_TRY(check_shape(shape, &g));
+    PISA_TRY(check_ptr(perm));
+    PISA_TRY(check_ptr(src));
+    PISA_TRY(check_ptr(dst));
+    const int e = shape->dtype == PISA_BF16 ? 2 : 4;
+    const uint64_t bytes = (uint64_t)shape->batch * shape->heads * shape->seq_len * shape->head_dim * e;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
+    if (a < b + bytes && b < a + bytes) return PISA_ERR_PARAM;   // overlapping buffers
+    return from_hip(launch_reorder(g, shape->batch, shape->heads, e, gather, perm, src, dst,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+pisa_status_t pisa_reorder_gather(const pisa_shape_t* shape, const int32_t* perm, const void* x, void* out,
+                                  void* stream) {
+    return reorder_common(shape, perm, x, out, true, stream);
+}
+
+pisa_status_t pisa_reorder_scatter(const pisa_shape_t* shape, const int32_t* perm, const void* o, void* y,
+                                   void* stream) {
+    return reorder_common(shape, perm, o, y, false, stream);
+}
+
 }  // extern "C"

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define PISA_ABI_VERSION 5
+#define PISA_ABI_VERSION 6
 
 typedef enum {
     PISA_OK = 0,
@@ -211,6 +211,48 @@ pisa_status_t pisa_attn_fwd_valu(const pisa_shape_t *shape, const pisa_params_t 
                                  const void *q, const void *k, const void *v,
                                  const pisa_stats_t *stats, const int32_t *idx,
                                  const float *wgate, void *o, void *stream);
+
+/*
+ * Morton token reorder ("Piecewise-Taylor-Attention" README: the Wan2.1
+ * results paragraph, where the 64-token blocks are taken over a Morton
+ * (Z-order) tile reordering of the latent grid so that each block is a
+ * compact 3D neighbourhood, and the changelog item on the Morton tile reorder
+ * with its fused gather kernel). Not part of the operator itself: callers
+ * holding token-major activations [B,T,H,D] in raster order use it before and
+ * after the three calls above.
+ *
+ * pisa_z_order (HOST pointers; no GPU work): fills perm[0 .. n) with the
+ * visiting order of `prefix` fixed tokens followed by the cells of a grid
+ * (grid[0 .. ndim), slowest axis first, raster-numbered after the prefix).
+ * A cell's code interleaves the bits of its coordinates: bit b of the axis
+ * in slot a (slot 0 = the fastest axis) is code bit ndim*b + a; cells are
+ * visited in ascending code (a grid that is not a power of two per axis is
+ * walked in its enclosing cube's order, missing cells skipped). perm[i] is
+ * the raster token index placed at position i. Requires 1 <= ndim <= 4,
+ * every grid[a] >= 1, prefix >= 0, n = prefix + prod(grid) <= 2^31 - 1 and
+ * ndim * bits(max grid) <= 63; else PISA_ERR_SHAPE (PISA_ERR_NULL for a NULL
+ * pointer). The caller owns perm.
+ */
+pisa_status_t pisa_z_order(const int64_t *grid, int32_t ndim, int64_t prefix, int32_t *perm,
+                           int64_t n);
+
+/*
+ * pisa_reorder_gather: out[b,h,i,:] = x[b, perm[i], h, :]: tokens gathered
+ * into the order perm while [B,T,H,D] becomes [B,H,T,D] (shape.seq_len = T,
+ * shape.heads = H, shape.head_dim = D, shape.dtype the element type; the
+ * other fields are checked as for the operator). perm: int32 [T] (device),
+ * normally a permutation of [0, T); a position whose perm entry is outside
+ * [0, T) receives zeros. x and out are device buffers that must not overlap.
+ *
+ * pisa_reorder_scatter: the inverse, y[b, perm[i], h, :] = o[b,h,i,:]
+ * ([B,H,T,D] back to raster-order [B,T,H,D]); positions whose perm entry is
+ * outside [0, T) are not written. With a permutation, scatter(gather(x)) = x
+ * bit for bit.
+ */
+pisa_status_t pisa_reorder_gather(const pisa_shape_t *shape, const int32_t *perm, const void *x,
+                                  void *out, void *stream);
+pisa_status_t pisa_reorder_scatter(const pisa_shape_t *shape, const int32_t *perm, const void *o,
+                                   void *y, void *stream);
 
 #ifdef __cplusplus
 }

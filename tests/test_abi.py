@@ -32,7 +32,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pisa_abi_version() == 5
+    assert lib.pisa_abi_version() == 6
     for code in range(9):
         assert lib.pisa_status_str(code)
     assert lib.pisa_status_str(99) == b"unknown status"
@@ -166,3 +166,56 @@ def test_null_structs(lib):
     assert lib.pisa_route_topk(ctypes.byref(s), None, ctypes.byref(st), FAKE, None, None) == E["PISA_ERR_NULL"]
     assert lib.pisa_route_topk(ctypes.byref(s), ctypes.byref(p), None, FAKE, None, None) == E["PISA_ERR_NULL"]
     assert lib.pisa_attn_fwd(ctypes.byref(s), ctypes.byref(p), FAKE, FAKE + 64, FAKE + 128, None, FAKE, None, FAKE + 256, None) == E["PISA_ERR_NULL"]
+
+
+# ---------------------------------------------------------------- Morton reorder
+
+def z_order_call(lib, grid, prefix=0, n=None):
+    g = (ctypes.c_int64 * len(grid))(*grid)
+    cells = 1
+    for x in grid:
+        cells *= x
+    n = prefix + cells if n is None else n
+    perm = (ctypes.c_int32 * max(n, 1))()
+    return lib.pisa_z_order(g, len(grid), prefix, perm, n), list(perm)[:n]
+
+
+@pytest.mark.parametrize("grid,prefix", [((21, 30, 52), 0), ((64, 64), 512), ((3, 5, 7), 2), ((1,), 0),
+                                         ((2, 3, 5, 7), 1), ((33, 45, 80), 0)])
+def test_z_order_host_helper_matches_oracle(lib, grid, prefix):
+    """The library's host-side Z-order (C++) against the oracle's (numpy), bit for bit."""
+    from oracle import reorder_oracle as R
+    code, perm = z_order_call(lib, grid, prefix)
+    assert code == 0
+    assert perm == R.z_order(grid, prefix).tolist()
+
+
+def test_z_order_validation(lib):
+    g = (ctypes.c_int64 * 3)(4, 4, 4)
+    perm = (ctypes.c_int32 * 64)()
+    assert lib.pisa_z_order(None, 3, 0, perm, 64) == E["PISA_ERR_NULL"]
+    assert lib.pisa_z_order(g, 3, 0, None, 64) == E["PISA_ERR_NULL"]
+    assert lib.pisa_z_order(g, 0, 0, perm, 64) == E["PISA_ERR_SHAPE"]
+    assert lib.pisa_z_order(g, 5, 0, perm, 64) == E["PISA_ERR_SHAPE"]
+    assert lib.pisa_z_order(g, 3, -1, perm, 64) == E["PISA_ERR_SHAPE"]
+    assert lib.pisa_z_order(g, 3, 0, perm, 63) == E["PISA_ERR_SHAPE"]        # n != prefix + cells
+    assert z_order_call(lib, (0, 4))[0] == E["PISA_ERR_SHAPE"]
+    assert z_order_call(lib, (1 << 16, 1 << 16), n=1)[0] == E["PISA_ERR_SHAPE"]   # > 2^31 - 1 tokens
+    assert z_order_call(lib, (1 << 30,) * 3, n=1)[0] == E["PISA_ERR_SHAPE"]
+
+
+@pytest.mark.parametrize("name", ["pisa_reorder_gather", "pisa_reorder_scatter"])
+def test_reorder_validation(lib, name):
+    fn = getattr(lib, name)
+    s = shape(T=1000, D=64, H=2)
+    nbytes = 2 * 1000 * 64 * 2
+    ok_dst = FAKE + nbytes + 256
+    assert fn(None, FAKE, FAKE, ok_dst, None) == E["PISA_ERR_NULL"]
+    assert fn(ctypes.byref(s), None, FAKE, ok_dst, None) == E["PISA_ERR_NULL"]
+    assert fn(ctypes.byref(s), FAKE, None, ok_dst, None) == E["PISA_ERR_NULL"]
+    assert fn(ctypes.byref(s), FAKE, FAKE, None, None) == E["PISA_ERR_NULL"]
+    assert fn(ctypes.byref(s), MIS, FAKE, ok_dst, None) == E["PISA_ERR_ALIGN"]
+    assert fn(ctypes.byref(s), FAKE, MIS, ok_dst, None) == E["PISA_ERR_ALIGN"]
+    assert fn(ctypes.byref(s), FAKE, FAKE, FAKE + 1024, None) == E["PISA_ERR_PARAM"]   # overlap
+    assert fn(ctypes.byref(shape(D=96)), FAKE, FAKE, ok_dst, None) == E["PISA_ERR_SHAPE"]
+    assert fn(ctypes.byref(shape(dtype=3)), FAKE, FAKE, ok_dst, None) == E["PISA_ERR_DTYPE"]

@@ -56,7 +56,7 @@ __global__ __launch_bounds__(kRows) void attn_valu_kernel(
         for (int j = max(0, i - band); j <= min(N - 1, i + band); ++j) sel[j] = 1;
         const int32_t* row = idx ? idx + (bh * (int64_t)N + i) * topk : nullptr;
         for (int c = 0; c < topk; ++c)
-            if (row[c] >= 0) sel[row[c]] = 1;
+            if (row[c] >= 0 && row[c] < N) sel[row[c]] = 1;   // anything else counts as padding
     }
     __syncthreads();
 

@@ -24,6 +24,19 @@
 namespace pisa {
 namespace {
 
+// Q, K, V are read once and the packed K copy is not read again by this
+// kernel: both go through non-temporal loads / stores (measured: 322 -> 297 us
+// at the Wan2.1-14B shape; either one alone gains little).
+typedef unsigned int nt_u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 nt_load(const void* p) {
+    const nt_u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x4*>(p));
+    return make_uint4(x.x, x.y, x.z, x.w);
+}
+__device__ __forceinline__ void nt_store(void* p, uint4 v) {
+    __builtin_nontemporal_store((nt_u32x4){v.x, v.y, v.z, v.w}, reinterpret_cast<nt_u32x4*>(p));
+}
+
+
 constexpr int kPad = 4;   // LDS row padding (elements): rows 8 apart fall on disjoint bank halves
 // Blocks per workgroup: the (head, block range) workgroups of one call should
 // all be resident at once. Two of these workgroups fit on a CU and MI355X has
@@ -162,9 +175,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             const int t = j * kBlock + row;
             if (t < T) {
                 const int64_t o = base + (int64_t)t * D + ch * 8;
-                pq[L] = *reinterpret_cast<const uint4*>(q + o);
-                pk[L] = *reinterpret_cast<const uint4*>(k + o);
-                pv[L] = *reinterpret_cast<const uint4*>(v + o);
+                pq[L] = nt_load(q + o);
+                pk[L] = nt_load(k + o);
+                pv[L] = nt_load(v + o);
             } else {
                 pq[L] = make_uint4(0, 0, 0, 0);
                 pk[L] = make_uint4(0, 0, 0, 0);
@@ -206,7 +219,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                 const int half = c / (32 * CH), ch = (c / 32) % CH, r = c % 32;
                 const uint2* src = reinterpret_cast<const uint2*>(sk + (32 * half + r) * LD + ch * 8);
                 const uint2 lo = src[0], hi = src[1];
-                kp[c] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+                nt_store(kp + c, make_uint4(lo.x, lo.y, hi.x, hi.y));
             }
         }
 

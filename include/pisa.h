@@ -28,8 +28,9 @@
  * - Every argument is validated on the host before any HIP call; a failing
  *   check returns a status and enqueues nothing. A launch failure returns
  *   PISA_ERR_HIP. Faults inside kernels surface at the caller's next
- *   synchronisation. Device data (e.g. routing table contents) are not
- *   validated: out-of-range block ids are undefined behaviour.
+ *   synchronisation. Device data are not validated on the host; routing
+ *   table entries outside [0, N) are ignored by the kernels (see
+ *   pisa_attn_fwd).
  * - Results are deterministic: no floating-point atomics, fixed reduction
  *   orders, identical bits for identical inputs and launch shapes.
  * - Softmax scale s = shape.scale, or 1/sqrt(head_dim) when scale <= 0; it
@@ -190,8 +191,10 @@ pisa_status_t pisa_route_topk(const pisa_shape_t *shape, const pisa_params_t *pa
  *   l_tail_t = sum_{j in U_i} n_j e^{lam_tj},
  *   F_t = first_order ? (l_tail_t / T) (s q_t) H : 0.
  * idx rows hold distinct block ids outside the band, then -1 padding (as
- * pisa_route_topk writes them: valid ids first, -1 only after them). o: [B,H,T,D] in the input dtype; must not
- * alias q, k, v. bf16 runs compute QK^T and PV with bf16 MFMA (fp32
+ * pisa_route_topk writes them). An entry outside [0, N), at any position, is
+ * ignored like -1 (the kernels address no memory from it); a repeated id or
+ * one inside the band makes the result unspecified. o: [B,H,T,D] in the input
+ * dtype; must not alias q, k, v. bf16 runs compute QK^T and PV with bf16 MFMA (fp32
  * accumulation, P rounded to bf16); fp32 runs compute in fp32.
  * Reads stats->kbar_c, vbar_c, kpack, hpack and kbpack (bf16), vsum, kbar and
  * hsum (fp32 path).

@@ -196,3 +196,40 @@ def test_wide_logit_range_restarts(D, second_order):
         ref = O.pisa_forward_head(qh[0, h], kh[0, h], vh[0, h], topk=topk, band=band,
                                   second_order=second_order, routing=idx_h[0, h])
         tol_check(o[0, h], ref, "bf16")
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("f32", 64)])
+def test_out_of_range_ids_count_as_padding(dtype, D):
+    """Routing-table entries outside [0, N), anywhere in a row, are ignored like
+    -1 padding: the output equals the one for the table with them removed
+    (the kernels never address memory from such an entry)."""
+    T, H, topk = 64 * 40, 2, 8
+    say(f"[gpu] out-of-range ids {dtype} D={D}")
+    (q, k, v), _ = make(T, D, dtype, 77, H=H)
+    N = T // 64
+    st = P.pisa_block_stats(q, k, v)
+    idx, _ = P.pisa_route_topk(q, st, topk, band=1)
+    good = idx.cpu().numpy()
+    bad_vals = [N, N + 3, -5, 1 << 30, -(1 << 31)]
+    clean = np.full(good.shape[:-1] + (topk + 3,), -1, np.int32)
+    dirty = np.full_like(clean, -1)
+    r = np.random.default_rng(1)
+    for b in range(good.shape[0]):
+        for h in range(H):
+            for i in range(N):
+                row = [int(x) for x in good[b, h, i] if x >= 0]
+                clean[b, h, i, :len(row)] = row
+                ins = sorted(r.choice(len(row) + 1, size=3, replace=True))
+                out = list(row)
+                for n, pos in enumerate(reversed(ins)):
+                    out.insert(pos, bad_vals[(i + n) % len(bad_vals)])
+                dirty[b, h, i] = out
+    oc = P.pisa_attn_fwd(q, k, v, st, torch.from_numpy(clean).cuda(), band=1)
+    od = P.pisa_attn_fwd(q, k, v, st, torch.from_numpy(dirty).cuda(), band=1)
+    torch.cuda.synchronize()
+    oc, od = oc.double().cpu().numpy(), od.double().cpu().numpy()
+    err = np.abs(oc - od).max()
+    if dtype == "f32":
+        assert err / np.abs(oc).max() <= 1e-5, err
+    else:
+        assert err <= 2e-2, err

@@ -41,6 +41,9 @@ R11 q2bar = mean over the query block of (s*q)^2 (elementwise); sigma^2 is
     the population variance (1/n_j).
 R12 gate: w > ln B  ->  0 (strict), w = ln B kept.
 R13 the gated w enters the virtual logit, hence numerator, mass and l_tail.
+R14 sink blocks ([PWT] knobs: n_sink_blocks=n forces the first n KV blocks,
+    e.g. an MMDiT text prefix, into the exact branch): like the band they are
+    forced for every query block and top-k is taken over the other blocks.
 """
 
 from __future__ import annotations
@@ -147,13 +150,14 @@ def second_order_w(q2bar: np.ndarray, sig2: np.ndarray, B: int):
     return w, w_gated, w_rank
 
 
-def route_topk(qbar, kbar, scale, topk, band, w_rank=None, band_mode="additive"):
+def route_topk(qbar, kbar, scale, topk, band, w_rank=None, band_mode="additive", n_sink=0):
     """Per query block, the top-k KV blocks by pooled score.
 
     r_ij = s qbar_i . kbar_j (+ w_rank_ij)   ([PISA] Algorithm 1 step 2 with
     Eq. 11 minus its covariance term, R7; [PWT] router with min(w, ln B)).
     Band_i = {j : |i-j| <= band} is forced exact ([PWT] knobs: band=b).
-    additive (R9): Top_i = the min(topk, |Cand_i|) best of Cand_i = all \\ Band_i.
+    additive (R9): Top_i = the min(topk, |Cand_i|) best of Cand_i = all \\ Band_i
+    \\ Sinks, Sinks = {j < n_sink} (R14).
     union: Top_i = the topk best of all blocks (the band is added afterwards).
     Ranking key (-r_ij, j): ties go to the lower index (R10).
     Returns (idx [Nq, topk] int32 ascending, -1 padded; scores r [Nq, Nk]).
@@ -165,7 +169,7 @@ def route_topk(qbar, kbar, scale, topk, band, w_rank=None, band_mode="additive")
     idx = np.full((Nq, topk), -1, dtype=np.int32)
     for i in range(Nq):
         if band_mode == "additive":
-            cand = np.array([j for j in range(Nk) if abs(i - j) > band], dtype=np.int64)
+            cand = np.array([j for j in range(Nk) if abs(i - j) > band and j >= n_sink], dtype=np.int64)
         elif band_mode == "union":
             cand = np.arange(Nk, dtype=np.int64)
         else:
@@ -177,10 +181,12 @@ def route_topk(qbar, kbar, scale, topk, band, w_rank=None, band_mode="additive")
     return idx, r
 
 
-def selected_sets(idx_row: np.ndarray, i: int, N: int, band: int):
-    """S_i = Band_i union Top_i, U_i = complement  ([PISA] §3.2 Formulation)."""
-    S = set(int(j) for j in idx_row if j >= 0)
+def selected_sets(idx_row: np.ndarray, i: int, N: int, band: int, n_sink: int = 0):
+    """S_i = Band_i union Sinks union Top_i, U_i = complement  ([PISA] §3.2
+    Formulation; sinks R14)."""
+    S = set(int(j) for j in idx_row if 0 <= j < N)
     S.update(j for j in range(max(0, i - band), min(N, i + band + 1)))
+    S.update(range(min(n_sink, N)))
     Ssorted = np.array(sorted(S), dtype=np.int64)
     U = np.array([j for j in range(N) if j not in S], dtype=np.int64)
     return Ssorted, U
@@ -196,7 +202,7 @@ def dense_attention(q, k, v, scale):
 
 def pisa_forward_head(q, k, v, *, B=64, scale=None, topk, band=1, second_order=False,
                       first_order="global", sparse_only=False, routing=None,
-                      query_blocks=None, band_mode="additive", return_parts=False):
+                      query_blocks=None, band_mode="additive", return_parts=False, n_sink=0):
     """PISA forward for one (batch, head); q, k, v are [T, D] float64.
 
     Per query block i and query row t (q' = s q_t):
@@ -218,6 +224,7 @@ def pisa_forward_head(q, k, v, *, B=64, scale=None, topk, band=1, second_order=F
 
     routing: None (computed here) or an [N, topk] table (-1 padded) that is
     used as Top_i verbatim ("fed the GPU's routing").
+    n_sink: the first n_sink KV blocks are exact for every query block (R14).
     query_blocks: iterable of block indices to evaluate (others stay NaN).
     Returns o [T, D] (and a dict of intermediate quantities if return_parts).
     """
@@ -233,7 +240,7 @@ def pisa_forward_head(q, k, v, *, B=64, scale=None, topk, band=1, second_order=F
     else:
         w = w_gated = w_rank = None
     if routing is None:
-        idx, _ = route_topk(qbar, st.kbar, scale, topk, band, w_rank, band_mode)
+        idx, _ = route_topk(qbar, st.kbar, scale, topk, band, w_rank, band_mode, n_sink)
     else:
         idx = np.asarray(routing)
     lnn = np.log(st.n)
@@ -243,7 +250,7 @@ def pisa_forward_head(q, k, v, *, B=64, scale=None, topk, band=1, second_order=F
     blocks = range(N) if query_blocks is None else query_blocks
     for i in blocks:
         a0, a1 = sl[i]
-        S, U = selected_sets(idx[i], i, N, band)
+        S, U = selected_sets(idx[i], i, N, band, n_sink)
         qp = scale * q[a0:a1]                                   # [R, D]
         keys = np.concatenate([np.arange(*sl[j]) for j in S]) if len(S) else np.zeros(0, np.int64)
         logit_ex = qp @ k[keys].T                               # [R, |keys|]

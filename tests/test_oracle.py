@@ -308,6 +308,62 @@ def test_routing_known_ranking_band_ties_padding():
     assert idxu[0].tolist() == [2, 3, 7]
 
 
+def test_routing_with_sink_blocks_known_ranking():
+    """Sinks (R14) are forced like the band: never routed, top-k over the rest."""
+    N = 10
+    qbar = np.ones((N, 1))
+    c = np.array([5.0, 1.0, 9.0, 9.0, 0.0, 7.0, 3.0, 9.0, 2.0, 8.0])
+    idx, _ = O.route_topk(qbar, c[:, None], 1.0, 3, band=1, n_sink=3)
+    # row 0: band {0,1}, sinks {0,1,2}; best of 3..9: 3, 7 (9), 9 (8)
+    assert idx[0].tolist() == [3, 7, 9]
+    # row 8: band {7,8,9}, sinks {0,1,2}; best of 3..6: 3 (9), 5 (7), 6 (3)
+    assert idx[8].tolist() == [3, 5, 6]
+    # everything forced: no candidates, all padding
+    idx2, _ = O.route_topk(qbar, c[:, None], 1.0, 3, band=1, n_sink=N)
+    assert (idx2 == -1).all()
+    S, U = O.selected_sets(idx[8], 8, N, 1, n_sink=3)
+    assert S.tolist() == [0, 1, 2, 3, 5, 6, 7, 8, 9] and U.tolist() == [4]
+
+
+@pytest.mark.parametrize("T,B", [(300, 64), (256, 32)])
+def test_all_blocks_sinks_equals_dense(T, B):
+    """n_sink >= N forces every block exact: o = softmax attention for any topk."""
+    q, k, v = rand_qkv(T, 16, 3 * T)
+    N = O.num_blocks(T, B)
+    s = 0.25
+    for topk in (0, 1):
+        o = O.pisa_forward_head(q, k, v, B=B, scale=s, topk=topk, band=0, n_sink=N)
+        np.testing.assert_allclose(o, sdpa(q, k, v, s), rtol=0, atol=1e-12)
+
+
+def test_sinks_equal_the_same_blocks_routed():
+    """Forcing the sinks equals routing them by hand: the table with the sinks
+    listed as routed ids gives the same output as n_sink with the rest."""
+    T, B = 640, 64
+    q, k, v = rand_qkv(T, 8, 77)
+    N = T // B
+    kw = dict(B=B, scale=0.3, band=1)
+    o_s, parts = O.pisa_forward_head(q, k, v, topk=2, n_sink=2, return_parts=True, **kw)
+    table = np.full((N, 4), -1, np.int32)
+    for i in range(N):
+        ids = sorted(set(int(j) for j in parts["idx"][i] if j >= 0) | {0, 1})
+        table[i, :len(ids)] = ids
+    o_r = O.pisa_forward_head(q, k, v, topk=4, routing=table, **kw)
+    np.testing.assert_allclose(o_s, o_r, rtol=0, atol=1e-13)
+
+
+def test_out_of_range_routing_entries_are_padding():
+    """Table entries outside [0, N) are ignored like -1 (the ABI's reading)."""
+    T, B = 640, 64
+    q, k, v = rand_qkv(T, 8, 78)
+    N = T // B
+    kw = dict(B=B, scale=0.3, band=1, topk=3)
+    o, parts = O.pisa_forward_head(q, k, v, return_parts=True, **kw)
+    bad = np.concatenate([parts["idx"], np.full((N, 2), N + 4, np.int32)], axis=1)
+    bad[:, [0, -1]] = bad[:, [-1, 0]]
+    np.testing.assert_array_equal(O.pisa_forward_head(q, k, v, routing=bad, **kw), o)
+
+
 def test_routing_invariant_to_key_translation():
     q, k, v = rand_qkv(640, 8, 31)
     qbar, _ = O.pool_queries(q, 64, 0.3)

@@ -141,7 +141,7 @@ def pisa_block_stats(q, k, v, second_order=False, scale=None, out: PisaStats | N
 
 
 def pisa_route_topk(q, stats: PisaStats, topk: int, band: int = 1, second_order=False, scale=None,
-                    idx: torch.Tensor | None = None, wgate: torch.Tensor | None = None):
+                    idx: torch.Tensor | None = None, wgate: torch.Tensor | None = None, n_sink: int = 0):
     """q is used for its shape and device only; routing reads the pooled statistics."""
     lib = library()
     sh = _shape(q, scale)
@@ -151,7 +151,7 @@ def pisa_route_topk(q, stats: PisaStats, topk: int, band: int = 1, second_order=
         idx = torch.empty(B, H, N, topk, dtype=torch.int32, device=q.device)
     if second_order and wgate is None:
         wgate = torch.empty(B, H, N, N, dtype=torch.float32, device=q.device)
-    prm = _lib.Params(int(topk), int(band), int(second_order), 1, 0)
+    prm = _lib.Params(int(topk), int(band), int(second_order), 1, 0, int(n_sink))
     cs = stats.as_c()
     _lib.check("pisa_route_topk", lib.pisa_route_topk(
         ctypes.byref(sh), ctypes.byref(prm), ctypes.byref(cs),
@@ -160,12 +160,13 @@ def pisa_route_topk(q, stats: PisaStats, topk: int, band: int = 1, second_order=
 
 
 def _attn(fn_name, q, k, v, stats, idx, wgate, topk, band, second_order, first_order,
-          phase_mask, scale, out):
+          phase_mask, scale, out, n_sink=0):
     lib = library()
     _contig(q, k, v, idx, wgate)
     sh = _shape(q, scale)
     o = out if out is not None else torch.empty_like(q)
-    prm = _lib.Params(int(topk), int(band), int(second_order), int(first_order), int(phase_mask))
+    prm = _lib.Params(int(topk), int(band), int(second_order), int(first_order), int(phase_mask),
+                      int(n_sink))
     cs = stats.as_c()
     fn = getattr(lib, fn_name)
     _lib.check(fn_name, fn(ctypes.byref(sh), ctypes.byref(prm), _ptr(q), _ptr(k), _ptr(v),
@@ -175,17 +176,17 @@ def _attn(fn_name, q, k, v, stats, idx, wgate, topk, band, second_order, first_o
 
 
 def pisa_attn_fwd(q, k, v, stats, idx, wgate=None, band=1, second_order=False, first_order=True,
-                  phase_mask=0, scale=None, out=None):
+                  phase_mask=0, scale=None, out=None, n_sink=0):
     topk = 0 if idx is None else idx.shape[-1]
     return _attn("pisa_attn_fwd", q, k, v, stats, idx, wgate, topk, band, second_order,
-                 first_order, phase_mask, scale, out)
+                 first_order, phase_mask, scale, out, n_sink)
 
 
 def pisa_attn_fwd_valu(q, k, v, stats, idx, wgate=None, band=1, second_order=False,
-                       first_order=True, phase_mask=0, scale=None, out=None):
+                       first_order=True, phase_mask=0, scale=None, out=None, n_sink=0):
     topk = 0 if idx is None else idx.shape[-1]
     return _attn("pisa_attn_fwd_valu", q, k, v, stats, idx, wgate, topk, band, second_order,
-                 first_order, phase_mask, scale, out)
+                 first_order, phase_mask, scale, out, n_sink)
 
 
 def z_order(grid, prefix: int = 0) -> torch.Tensor:
@@ -232,14 +233,16 @@ def piecewise_sparse_attention(q, k, v, density=0.125, variant="pisa", band=1, s
     """PISA (variant="pisa") or PISA with the gated second-order term ("pwt").
 
     q, k, v: [B, H, T, D] bf16 or fp32 on the GPU. topk = floor(density * N)
-    routed blocks per query block, plus the +-band, are computed exactly.
+    routed blocks per query block, plus the +-band and the first
+    ``n_sink_blocks`` KV blocks (e.g. an MMDiT text prefix), are computed
+    exactly.
     With reorder="morton", q, k, v are token-major [B, T, H, D] in raster
     order over ``prefix`` fixed tokens then ``grid`` (slowest axis first); the
     tokens are gathered into Z-order (and [B, H, T, D]) before the operator and
     the output is scattered back to [B, T, H, D].
     """
-    if n_sink_blocks or cov_bias:
-        raise NotImplementedError("sink blocks and the covariance bias are not built")
+    if cov_bias:
+        raise NotImplementedError("the covariance-aware routing bias is not built")
     if reorder not in ("none", "morton"):
         raise ValueError(reorder)
     if variant not in ("pisa", "pwt"):
@@ -256,8 +259,10 @@ def piecewise_sparse_attention(q, k, v, density=0.125, variant="pisa", band=1, s
     N = num_blocks(q.shape[2])
     topk = topk_for_density(density, N)
     topk = min(topk, N)
+    n_sink_blocks = min(int(n_sink_blocks), N)
     st = pisa_block_stats(q, k, v, second_order=so, scale=scale)
-    idx, wg = pisa_route_topk(q, st, topk, band=band, second_order=so, scale=scale)
+    idx, wg = pisa_route_topk(q, st, topk, band=band, second_order=so, scale=scale,
+                              n_sink=n_sink_blocks)
     o = pisa_attn_fwd(q, k, v, st, idx if topk else None, wg, band=band, second_order=so,
-                      scale=scale)
+                      scale=scale, n_sink=n_sink_blocks)
     return o if perm is None else reorder_scatter(o, perm)

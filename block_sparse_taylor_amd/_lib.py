@@ -31,7 +31,8 @@ class Shape(ctypes.Structure):
 
 class Params(ctypes.Structure):
     _fields_ = [("topk", ctypes.c_int32), ("band", ctypes.c_int32), ("second_order", ctypes.c_int32),
-                ("first_order", ctypes.c_int32), ("phase_mask", ctypes.c_int32)]
+                ("first_order", ctypes.c_int32), ("phase_mask", ctypes.c_int32),
+                ("n_sink", ctypes.c_int32)]
 
 
 class Stats(ctypes.Structure):

@@ -24,7 +24,7 @@ __global__ __launch_bounds__(kRows) void attn_valu_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const double* __restrict__ kbar, const float* __restrict__ vsum, const float* __restrict__ hsum,
     const int32_t* __restrict__ idx, const float* __restrict__ wgate, T* __restrict__ o, int Tn,
-    int N, float scale, int topk, int band, int second_order, int first_order, int phase_mask) {
+    int N, float scale, int topk, int band, int n_sink, int second_order, int first_order, int phase_mask) {
     constexpr int kSub = 32;                 // K/V rows staged per step
     __shared__ float sk[kSub * D];
     __shared__ float sv[kSub * D];
@@ -54,6 +54,7 @@ __global__ __launch_bounds__(kRows) void attn_valu_kernel(
     __syncthreads();
     if (tid == 0) {
         for (int j = max(0, i - band); j <= min(N - 1, i + band); ++j) sel[j] = 1;
+        for (int j = 0; j < min(n_sink, N); ++j) sel[j] = 1;   // sink blocks
         const int32_t* row = idx ? idx + (bh * (int64_t)N + i) * topk : nullptr;
         for (int c = 0; c < topk; ++c)
             if (row[c] >= 0 && row[c] < N) sel[row[c]] = 1;   // anything else counts as padding
@@ -154,7 +155,7 @@ hipError_t launch_attn_fwd_valu(const Geom& g, int dtype, const pisa_params_t* p
     hipLaunchKernelGGL((attn_valu_kernel<TT, DD>), grid, block, shm, stream,                       \
                        static_cast<const TT*>(q), static_cast<const TT*>(k),                       \
                        static_cast<const TT*>(v), st->kbar, st->vsum, st->hsum, idx, wgate,        \
-                       static_cast<TT*>(o), g.T, g.N, g.scale, p->topk, p->band, p->second_order,  \
+                       static_cast<TT*>(o), g.T, g.N, g.scale, p->topk, p->band, p->n_sink, p->second_order,  \
                        p->first_order, p->phase_mask)
     if (dtype == PISA_BF16) {
         if (g.D == 128) PISA_VALU_LAUNCH(bf16_t, 128);

@@ -36,6 +36,27 @@ template <typename T> __device__ __forceinline__ T store_cast(float x);
 template <> __device__ __forceinline__ float store_cast<float>(float x) { return x; }
 template <> __device__ __forceinline__ bf16_t store_cast<bf16_t>(float x) { return f32_to_bf16(x); }
 
+// The forced exact set of query block i: the band [lo, hi] = [i - band,
+// i + band] clipped to [0, N), then the sink blocks [0, ns) outside it.
+// forced_count gives its size, forced_block(c) its c-th member (band blocks
+// ascending, then the sinks below lo, then those above hi).
+struct Forced {
+    int lo, hi, ns;
+    __host__ __device__ Forced(int i, int band, int n_sink, int N)
+        : lo(i - band > 0 ? i - band : 0), hi(i + band < N - 1 ? i + band : N - 1),
+          ns(n_sink < N ? n_sink : N) {}
+    __host__ __device__ int below() const { return ns < lo ? ns : lo; }
+    __host__ __device__ int above() const { return ns - hi - 1 > 0 ? ns - hi - 1 : 0; }
+    __host__ __device__ int count() const { return hi - lo + 1 + below() + above(); }
+    __host__ __device__ int block(int c) const {
+        const int nb = hi - lo + 1;
+        if (c < nb) return lo + c;
+        c -= nb;
+        return c < below() ? c : hi + 1 + (c - below());
+    }
+    __host__ __device__ bool forced(int j) const { return (j >= lo && j <= hi) || j < ns; }
+};
+
 // Problem geometry resolved once on the host.
 struct Geom {
     int64_t BH;       // batch * heads

@@ -41,6 +41,7 @@ pisa_status_t check_params(const pisa_params_t* p, const Geom& g) {
     if (p->second_order != 0 && p->second_order != 1) return PISA_ERR_PARAM;
     if (p->first_order != 0 && p->first_order != 1) return PISA_ERR_PARAM;
     if (p->phase_mask < 0 || p->phase_mask > 7) return PISA_ERR_PARAM;
+    if (p->n_sink < 0 || p->n_sink > g.N) return PISA_ERR_PARAM;
     return PISA_OK;
 }
 

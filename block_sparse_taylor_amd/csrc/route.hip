@@ -4,7 +4,8 @@
 // spread min(w, ln B), set-identical top-k).
 //
 //   r_ij = s qbar_i . kbar_j  [+ min(w_ij, ln B)],   w_ij = 1/2 q2bar_i . ksig2_j
-//   Top_i = the topk largest r_ij over |i - j| > band, ties to the lower j.
+//   Top_i = the topk largest r_ij over |i - j| > band and j >= n_sink (the
+//   band and the README's sink blocks are forced exact), ties to the lower j.
 //
 // The decision must equal a float64 evaluation, so the kernel scores in fp32
 // and settles every close call in fp64:
@@ -169,6 +170,7 @@ template <int D, bool SO, int KPL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(SO || KPL > 16 ? 2 : 4))) void route_fast_kernel(
     const double* __restrict__ qbar, const double* __restrict__ q2bar, const double* __restrict__ kbar,
     const float* __restrict__ kbar_r, const double* __restrict__ ksig2, int N, double s64, int topk, int band,
+    int n_sink,
     int32_t* __restrict__ idx, float* __restrict__ wgate) {
     constexpr int KS = D / 4;       // 16x16x4 k-steps; MFMA k-slot (ks, l/16) <-> dim (D/4)(l/16) + ks
     constexpr bool second_order = SO;
@@ -307,12 +309,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(SO || 
     auto row_pass = [&](int r) {
         const int i = i0 + r;
         int32_t* out = idx + (bh * N + i) * (int64_t)topk;
-        const int blo = max(0, i - band), bhi = min(N - 1, i + band);
-        const int ncand = N - (bhi - blo + 1);
+        const Forced fs(i, band, n_sink, N);
+        const int ncand = N - fs.count();
         const int k = min(topk, ncand);
         const float* sr = score_s + r * NP;
         const double* qg = qrows + (int64_t)r * D;   // fp64 pooled query of row i
-        auto is_cand = [&](int j) { return j < blo || j > bhi; };
+        auto is_cand = [&](int j) { return !fs.forced(j); };
         int written = 0;
         if (k > 0) {
             uint32_t kv[KPL];
@@ -483,7 +485,7 @@ __device__ __forceinline__ int block_scan(int x, int* scratch, int* excl) {
 template <int D>
 __global__ __launch_bounds__(kThreads) void route_slow_kernel(
     const double* __restrict__ qbar, const double* __restrict__ q2bar, const double* __restrict__ kbar,
-    const double* __restrict__ ksig2, int N, double s64, int topk, int band, int second_order,
+    const double* __restrict__ ksig2, int N, double s64, int topk, int band, int n_sink, int second_order,
     int32_t* __restrict__ idx, float* __restrict__ wgate) {
     __shared__ double qbar_s[D];
     __shared__ double q2_s[D];
@@ -519,7 +521,7 @@ __global__ __launch_bounds__(kThreads) void route_slow_kernel(
             r += fmin(w, lnB);
             wrow[j] = (float)(w > lnB ? 0.0 : w);
         }
-        const bool cand = abs(i - j) > band;
+        const bool cand = abs(i - j) > band && j >= n_sink;
         key_s[j] = cand ? key64(r) : 0ull;
         ncand += cand;
     }
@@ -586,7 +588,7 @@ hipError_t launch_route_topk(const Geom& g, const pisa_params_t* p, const pisa_s
     const size_t lds = fast_lds_bytes(g.D, g.N, so);
     if (lds + 64 <= (size_t)kLdsMax && g.N <= 64 * kKeysPerLane) {
         using Fn = void (*)(const double*, const double*, const double*, const float*, const double*, int, double,
-                            int, int, int32_t*, float*);
+                            int, int, int, int32_t*, float*);
         static bool attr_set[2][2][3] = {};
         const int kc = g.N <= 64 * 8 ? 0 : (g.N <= 64 * 16 ? 1 : 2);
         static const Fn table[2][2][3] = {
@@ -608,12 +610,12 @@ hipError_t launch_route_topk(const Geom& g, const pisa_params_t* p, const pisa_s
         }
         dim3 grid((g.N + kQB - 1) / kQB, (unsigned)g.BH);
         hipLaunchKernelGGL(fn, grid, block, lds, stream, st->qbar, st->q2bar, st->kbar, st->kbar_r, st->ksig2, g.N,
-                           g.scale64, p->topk, p->band, idx, wgate);
+                           g.scale64, p->topk, p->band, p->n_sink, idx, wgate);
     } else {
         dim3 grid(g.N, (unsigned)g.BH);
 #define PISA_ROUTE_LAUNCH(DD)                                                                      \
     hipLaunchKernelGGL(route_slow_kernel<DD>, grid, block, 0, stream, st->qbar, st->q2bar,         \
-                       st->kbar, st->ksig2, g.N, g.scale64, p->topk, p->band, so, idx, wgate)
+                       st->kbar, st->ksig2, g.N, g.scale64, p->topk, p->band, p->n_sink, so, idx, wgate)
         if (g.D == 128) PISA_ROUTE_LAUNCH(128);
         else PISA_ROUTE_LAUNCH(64);
 #undef PISA_ROUTE_LAUNCH

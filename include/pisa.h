@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define PISA_ABI_VERSION 6
+#define PISA_ABI_VERSION 7
 
 typedef enum {
     PISA_OK = 0,
@@ -80,6 +80,9 @@ typedef struct {
     int32_t first_order;  /* 1: global first order (Eq. 10, Phase 3); 0: off     */
     int32_t phase_mask;   /* 0 = all phases; bit0 exact, bit1 virtual, bit2 first
                              order (measurement only)                            */
+    int32_t n_sink;       /* the first n_sink KV blocks are exact for every query
+                             block, like the band (README knobs: n_sink_blocks,
+                             e.g. an MMDiT text prefix); 0..N                    */
 } pisa_params_t;
 
 /*

@@ -32,7 +32,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pisa_abi_version() == 6
+    assert lib.pisa_abi_version() == 7
     for code in range(9):
         assert lib.pisa_status_str(code)
     assert lib.pisa_status_str(99) == b"unknown status"
@@ -140,6 +140,9 @@ def test_route_validation(lib):
     assert call_route(lib, p=_lib.Params(4, 1, 1, 1, 0), st=stats(ksig2=FAKE)) == E["PISA_ERR_NULL"]
     assert call_route(lib, p=_lib.Params(4, 1, 1, 1, 0), st=stats(ksig2=FAKE, q2bar=FAKE)) == E["PISA_ERR_NULL"]
     assert call_route(lib, s=shape(block=128)) == E["PISA_ERR_PARAM"]
+    # sink blocks: 0..N
+    assert call_route(lib, p=_lib.Params(4, 1, 0, 1, 0, -1)) == E["PISA_ERR_PARAM"]
+    assert call_route(lib, p=_lib.Params(4, 1, 0, 1, 0, 17)) == E["PISA_ERR_PARAM"]
 
 
 @pytest.mark.parametrize("name", ["pisa_attn_fwd", "pisa_attn_fwd_valu"])

@@ -233,3 +233,33 @@ def test_out_of_range_ids_count_as_padding(dtype, D):
         assert err / np.abs(oc).max() <= 1e-5, err
     else:
         assert err <= 2e-2, err
+
+
+SINK_CASES = [  # T, D, dtype, topk, band, n_sink
+    (1000, 128, "bf16", 3, 1, 3), (1000, 64, "bf16", 3, 1, 3), (1000, 64, "f32", 3, 1, 3),
+    (700, 128, "bf16", 2, 0, 11), (333, 64, "f32", 1, 1, 6), (2048, 128, "bf16", 4, 1, 32),
+]
+
+
+@pytest.mark.parametrize("T,D,dtype,topk,band,n_sink", SINK_CASES)
+@pytest.mark.parametrize("second_order", [False, True])
+def test_sink_blocks_match_oracle(T, D, dtype, topk, band, n_sink, second_order):
+    """The first n_sink KV blocks are forced exact (README knobs: n_sink_blocks):
+    routing equals the oracle's (top-k over the non-forced blocks) and the
+    output the oracle's with the same routing and sinks."""
+    say(f"[gpu] sinks T={T} D={D} {dtype} topk={topk} band={band} n_sink={n_sink} so={second_order}")
+    (q, k, v), (qh, kh, vh) = make(T, D, dtype, T + D + n_sink)
+    N = -(-T // 64)
+    st = P.pisa_block_stats(q, k, v, second_order=second_order)
+    idx, wg = P.pisa_route_topk(q, st, topk, band=band, second_order=second_order, n_sink=n_sink)
+    o = P.pisa_attn_fwd(q, k, v, st, idx if topk else None, wg, band=band,
+                        second_order=second_order, n_sink=n_sink)
+    torch.cuda.synchronize()
+    idx_h = idx.cpu().numpy() if topk else np.zeros((1, 2, N, 0), np.int32)
+    for h in range(2):
+        ref, parts = O.pisa_forward_head(qh[0, h], kh[0, h], vh[0, h], topk=topk, band=band,
+                                         second_order=second_order, n_sink=n_sink,
+                                         return_parts=True)
+        if topk:
+            assert np.array_equal(idx_h[0, h], parts["idx"])
+        tol_check(o[0, h], ref, dtype)

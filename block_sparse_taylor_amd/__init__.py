@@ -83,12 +83,13 @@ class PisaStats:
     hpack: torch.Tensor | None   # bf16 [B,H,2*D*D]: hsum split hi + lo in the fused kernel's operand order
     kbpack: torch.Tensor | None  # bf16 [B,H,ceil(N/64),64*D]: kbar_c per group of 64 blocks, in kpack's order
     kbar_r: torch.Tensor         # fp32 [B,H,ceil(N/16)*16*D]: kbar in the router's operand order
+    ksig2_r: torch.Tensor | None  # second order: ksig2 in fp32, the same order
 
     def as_c(self) -> _lib.Stats:
         return _lib.Stats(_ptr(self.qbar), _ptr(self.q2bar), _ptr(self.kbar), _ptr(self.vsum),
                           _ptr(self.ksig2), _ptr(self.hsum), _ptr(self.kbar_c), _ptr(self.vbar_c),
                           _ptr(self.kpack), _ptr(self.hpack), _ptr(self.kbpack),
-                          _ptr(self.kbar_r))
+                          _ptr(self.kbar_r), _ptr(self.ksig2_r))
 
 
 def _contig(*ts):
@@ -115,6 +116,8 @@ def alloc_stats(k: torch.Tensor, second_order: bool) -> PisaStats:
         kbpack=(torch.empty(B, H, -(-N // BLOCK), BLOCK * D, dtype=k.dtype, device=dev)
                 if k.dtype == torch.bfloat16 else None),
         kbar_r=torch.empty(B, H, -(-N // 16) * 16 * D, dtype=torch.float32, device=dev),
+        ksig2_r=(torch.empty(B, H, -(-N // 16) * 16 * D, dtype=torch.float32, device=dev)
+                 if second_order else None),
     )
 
 

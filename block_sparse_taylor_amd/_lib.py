@@ -40,7 +40,7 @@ class Stats(ctypes.Structure):
                 ("vsum", ctypes.c_void_p), ("ksig2", ctypes.c_void_p), ("hsum", ctypes.c_void_p),
                 ("kbar_c", ctypes.c_void_p), ("vbar_c", ctypes.c_void_p), ("kpack", ctypes.c_void_p),
                 ("hpack", ctypes.c_void_p), ("kbpack", ctypes.c_void_p),
-                ("kbar_r", ctypes.c_void_p)]
+                ("kbar_r", ctypes.c_void_p), ("ksig2_r", ctypes.c_void_p)]
 
 
 class PisaError(RuntimeError):

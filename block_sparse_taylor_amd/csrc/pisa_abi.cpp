@@ -138,6 +138,7 @@ pisa_status_t pisa_block_stats(const pisa_shape_t* shape, const pisa_params_t* p
     PISA_TRY(check_stats(out, params->second_order, true, shape->dtype == PISA_BF16));
     PISA_TRY(check_ptr(out->qbar));
     PISA_TRY(check_ptr(out->kbar_r));
+    if (params->second_order) PISA_TRY(check_ptr(out->ksig2_r));
     if (params->second_order) PISA_TRY(check_ptr(out->q2bar));
     PISA_TRY(check_ptr(workspace));
     if (workspace_bytes < stats_workspace_bytes(g)) return PISA_ERR_WORKSPACE;
@@ -154,6 +155,7 @@ pisa_status_t pisa_route_topk(const pisa_shape_t* shape, const pisa_params_t* pa
     PISA_TRY(check_ptr(stats->qbar));
     PISA_TRY(check_ptr(stats->kbar));
     PISA_TRY(check_ptr(stats->kbar_r));
+    if (params->second_order) PISA_TRY(check_ptr(stats->ksig2_r));
     if (params->second_order) {
         PISA_TRY(check_ptr(stats->q2bar));
         PISA_TRY(check_ptr(stats->ksig2));

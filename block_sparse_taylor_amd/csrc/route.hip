@@ -169,8 +169,8 @@ __host__ __device__ inline size_t fast_lds_bytes(int D, int N, int second_order)
 template <int D, bool SO, int KPL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(SO || KPL > 16 ? 2 : 4))) void route_fast_kernel(
     const double* __restrict__ qbar, const double* __restrict__ q2bar, const double* __restrict__ kbar,
-    const float* __restrict__ kbar_r, const double* __restrict__ ksig2, int N, double s64, int topk, int band,
-    int n_sink,
+    const float* __restrict__ kbar_r, const double* __restrict__ ksig2, const float* __restrict__ ksig2_r,
+    int N, double s64, int topk, int band, int n_sink,
     int32_t* __restrict__ idx, float* __restrict__ wgate) {
     constexpr int KS = D / 4;       // 16x16x4 k-steps; MFMA k-slot (ks, l/16) <-> dim (D/4)(l/16) + ks
     constexpr bool second_order = SO;
@@ -224,11 +224,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(SO || 
     const double* sg = SO ? ksig2 + bh * (int64_t)N * D : nullptr;
     float kmax2 = 0.f;
     const int NC = (N + 15) / 16;
-    auto kptr = [&](const double* base, int c) {   // this lane's 16-byte-aligned run of chunk c (fp64)
-        const int col = min(c * 16 + m16, N - 1);
-        return reinterpret_cast<const d2_t*>(base + (int64_t)col * D + (D / 4) * g4);
-    };
     const float4* kr4 = reinterpret_cast<const float4*>(kbar_r + bh * (int64_t)NC * 16 * D);
+    const float4* sr4 = SO ? reinterpret_cast<const float4*>(ksig2_r + bh * (int64_t)NC * 16 * D) : nullptr;
     float4 kv[KS / 4];
     auto kload = [&](int c) {
 #pragma unroll
@@ -247,6 +244,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(SO || 
             b[4 * qq + 3] = ok ? kv[qq].w : 0.f;
         }
         if (c + 4 < NC) kload(c + 4);   // the next chunk
+        float4 sv[SO ? KS / 4 : 1];       // ksig2 of this chunk (second order), same order as kbar_r
+        if (SO) {
+#pragma unroll
+            for (int qq = 0; qq < KS / 4; ++qq) sv[qq] = sr4[((int64_t)c * (KS / 4) + qq) * 64 + lane];
+        }
         f4_t acc = {0.f, 0.f, 0.f, 0.f}, accw = {0.f, 0.f, 0.f, 0.f};
         float n2 = 0.f;
 #pragma unroll
@@ -255,12 +257,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(SO || 
             acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[ks], b[ks], acc, 0, 0, 0);
         }
         if (SO) {
-            const d2_t* src = kptr(sg, c);
 #pragma unroll
-            for (int h = 0; h < KS / 2; ++h) {
-                const d2_t x = src[h];
-                accw = __builtin_amdgcn_mfma_f32_16x16x4f32(a2[2 * h], ok ? (float)x.x : 0.f, accw, 0, 0, 0);
-                accw = __builtin_amdgcn_mfma_f32_16x16x4f32(a2[2 * h + 1], ok ? (float)x.y : 0.f, accw, 0, 0, 0);
+            for (int qq = 0; qq < KS / 4; ++qq) {
+                accw = __builtin_amdgcn_mfma_f32_16x16x4f32(a2[4 * qq + 0], ok ? sv[qq].x : 0.f, accw, 0, 0, 0);
+                accw = __builtin_amdgcn_mfma_f32_16x16x4f32(a2[4 * qq + 1], ok ? sv[qq].y : 0.f, accw, 0, 0, 0);
+                accw = __builtin_amdgcn_mfma_f32_16x16x4f32(a2[4 * qq + 2], ok ? sv[qq].z : 0.f, accw, 0, 0, 0);
+                accw = __builtin_amdgcn_mfma_f32_16x16x4f32(a2[4 * qq + 3], ok ? sv[qq].w : 0.f, accw, 0, 0, 0);
             }
         }
         n2 += __shfl_xor(n2, 16);
@@ -587,8 +589,8 @@ hipError_t launch_route_topk(const Geom& g, const pisa_params_t* p, const pisa_s
     dim3 block(kThreads);
     const size_t lds = fast_lds_bytes(g.D, g.N, so);
     if (lds + 64 <= (size_t)kLdsMax && g.N <= 64 * kKeysPerLane) {
-        using Fn = void (*)(const double*, const double*, const double*, const float*, const double*, int, double,
-                            int, int, int, int32_t*, float*);
+        using Fn = void (*)(const double*, const double*, const double*, const float*, const double*, const float*,
+                            int, double, int, int, int, int32_t*, float*);
         static bool attr_set[2][2][3] = {};
         const int kc = g.N <= 64 * 8 ? 0 : (g.N <= 64 * 16 ? 1 : 2);
         static const Fn table[2][2][3] = {
@@ -609,7 +611,7 @@ hipError_t launch_route_topk(const Geom& g, const pisa_params_t* p, const pisa_s
             set = true;
         }
         dim3 grid((g.N + kQB - 1) / kQB, (unsigned)g.BH);
-        hipLaunchKernelGGL(fn, grid, block, lds, stream, st->qbar, st->q2bar, st->kbar, st->kbar_r, st->ksig2, g.N,
+        hipLaunchKernelGGL(fn, grid, block, lds, stream, st->qbar, st->q2bar, st->kbar, st->kbar_r, st->ksig2, st->ksig2_r, g.N,
                            g.scale64, p->topk, p->band, p->n_sink, idx, wgate);
     } else {
         dim3 grid(g.N, (unsigned)g.BH);

@@ -55,6 +55,7 @@ struct StatsOut {
     void* kpack;      // bf16 only: K in the fused kernel's operand order
     void* kbpack;     // bf16 only: kbar_c in the same order, per group of 64 blocks
     float* kbar_r;    // kbar in fp32, in the router's MFMA operand order
+    float* ksig2_r;   // second order: ksig2 in fp32, the same order
 };
 
 // Column statistics of one block from its LDS tiles (row pitch ld).
@@ -105,12 +106,11 @@ __device__ __forceinline__ void column_stats(const T* tq, const T* tk, const T* 
         const int64_t off = (bh * n_blocks + j) * D;
         out.qbar[off + c] = a[0] / n;
         out.kbar[off + c] = mean;
-        {
-            // router operand order: key j = 16 cc + n, dim c = (D/4) g + 4 q + e
-            const int cc = j / 16, n = j % 16, g = c / (D / 4), q = (c % (D / 4)) / 4, e = c % 4;
-            out.kbar_r[bh * (int64_t)((n_blocks + 15) / 16) * 16 * D +
-                       (((int64_t)cc * (D / 16) + q) * 64 + 16 * g + n) * 4 + e] = (float)mean;
-        }
+        // router operand order: key j = 16 cc + n, dim c = (D/4) g + 4 q + e
+        const int64_t roff = bh * (int64_t)((n_blocks + 15) / 16) * 16 * D +
+                             ((((int64_t)(j / 16)) * (D / 16) + (c % (D / 4)) / 4) * 64 + 16 * (c / (D / 4)) +
+                              j % 16) * 4 + c % 4;
+        out.kbar_r[roff] = (float)mean;
         static_cast<T*>(out.kbar_c)[off + c] = store_cast<T>((float)mean);
         if (out.kbpack) {
             // block j = row j % 64 of virtual group j / 64, laid out like kpack
@@ -126,7 +126,9 @@ __device__ __forceinline__ void column_stats(const T* tq, const T* tk, const T* 
         if (second_order) {
             out.q2bar[off + c] = a[1] / n;
             const double mx = a[3] / n;
-            out.ksig2[off + c] = fmax(a[4] / n - mx * mx, 0.0);
+            const double s2 = fmax(a[4] / n - mx * mx, 0.0);
+            out.ksig2[off + c] = s2;
+            out.ksig2_r[roff] = (float)s2;
         }
     }
 }
@@ -388,7 +390,8 @@ hipError_t launch_block_stats(const Geom& g, int dtype, int second_order, const 
     dim3 grid(G, (unsigned)g.BH), block(kThreads);
     float* hpart = static_cast<float*>(workspace);
     StatsOut out{st->qbar, st->q2bar, st->kbar, st->vsum, st->ksig2, st->kbar_c, st->vbar_c, st->kpack,
-                 dtype == PISA_BF16 ? st->kbpack : nullptr, st->kbar_r};
+                 dtype == PISA_BF16 ? st->kbpack : nullptr, st->kbar_r,
+                 second_order ? st->ksig2_r : nullptr};
 #define PISA_STATS_LAUNCH(KERN, TT, DD)                                                            \
     hipLaunchKernelGGL(KERN<DD>, grid, block, 0, stream, static_cast<const TT*>(q),               \
                        static_cast<const TT*>(k), static_cast<const TT*>(v), g.T, g.N, bpw,       \

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define PISA_ABI_VERSION 7
+#define PISA_ABI_VERSION 8
 
 typedef enum {
     PISA_OK = 0,
@@ -123,6 +123,8 @@ typedef struct {
  * [B,H,ceil(N/16)*16*D]: key j = 16 c + n, dim d = (D/4) g + 4 q + e (g < 4,
  * q < D/16, e < 4) sits at ((c * D/16 + q) * 64 + 16 g + n) * 4 + e; slots of
  * keys past N are unspecified (the router masks them).
+ * ksig2_r (second order only; may be NULL otherwise) is ksig2 rounded to fp32
+ * in the same order and size as kbar_r.
  */
 typedef struct {
     double *qbar;
@@ -137,6 +139,7 @@ typedef struct {
     void *hpack;
     void *kbpack;
     float *kbar_r;
+    float *ksig2_r;
 } pisa_stats_t;
 
 /* ABI version of the library (PISA_ABI_VERSION). */
@@ -178,7 +181,8 @@ pisa_status_t pisa_block_stats(const pisa_shape_t *shape, const pisa_params_t *p
  * wgate: fp32 [B,H,N,N], required iff second_order: the gated term used by
  *   the virtual-token logits: w_ij where w_ij <= ln B, and 0 where w_ij is
  *   larger (the README's gate, not a clamp), decided as in float64.
- * Reads stats->qbar, kbar, kbar_r (and q2bar, ksig2 if second_order).
+ * Reads stats->qbar, kbar, kbar_r (and q2bar, ksig2, ksig2_r if
+ * second_order).
  */
 pisa_status_t pisa_route_topk(const pisa_shape_t *shape, const pisa_params_t *params,
                               const pisa_stats_t *stats, int32_t *idx, float *wgate,

@@ -32,7 +32,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pisa_abi_version() == 7
+    assert lib.pisa_abi_version() == 8
     for code in range(9):
         assert lib.pisa_status_str(code)
     assert lib.pisa_status_str(99) == b"unknown status"
@@ -72,7 +72,7 @@ MIS = FAKE + 4
 
 def stats(**kw):
     d = dict(qbar=FAKE, q2bar=None, kbar=FAKE, vsum=FAKE, ksig2=None, hsum=FAKE, kbar_c=FAKE, vbar_c=FAKE,
-             kpack=FAKE, hpack=FAKE, kbpack=FAKE, kbar_r=FAKE)
+             kpack=FAKE, hpack=FAKE, kbpack=FAKE, kbar_r=FAKE, ksig2_r=None)
     d.update(kw)
     return _lib.Stats(**d)
 
@@ -139,6 +139,10 @@ def test_route_validation(lib):
     assert call_route(lib, p=_lib.Params(4, 1, 1, 1, 0)) == E["PISA_ERR_NULL"]
     assert call_route(lib, p=_lib.Params(4, 1, 1, 1, 0), st=stats(ksig2=FAKE)) == E["PISA_ERR_NULL"]
     assert call_route(lib, p=_lib.Params(4, 1, 1, 1, 0), st=stats(ksig2=FAKE, q2bar=FAKE)) == E["PISA_ERR_NULL"]
+    # ... and ksig2_r
+    assert call_route(lib, p=_lib.Params(4, 1, 1, 1, 0), st=stats(ksig2=FAKE, q2bar=FAKE), wg=FAKE) == E["PISA_ERR_NULL"]
+    assert call_route(lib, p=_lib.Params(4, 1, 1, 1, 0), st=stats(ksig2=FAKE, q2bar=FAKE, ksig2_r=MIS),
+                      wg=FAKE) == E["PISA_ERR_ALIGN"]
     assert call_route(lib, s=shape(block=128)) == E["PISA_ERR_PARAM"]
     # sink blocks: 0..N
     assert call_route(lib, p=_lib.Params(4, 1, 0, 1, 0, -1)) == E["PISA_ERR_PARAM"]

@@ -106,6 +106,7 @@ def test_block_stats(name):
     kbp = run.st.kbpack.view(torch.int16).cpu().numpy().view(np.uint16) if w.dtype == "bf16" else None
     kbb = run.st.kbar_c.view(torch.int16).cpu().numpy().view(np.uint16) if w.dtype == "bf16" else None
     kbr = run.host(run.st.kbar_r)
+    ksr = run.host(run.st.ksig2_r) if w.second_order else None
     for h in heads:
         # kbar in fp32, router operand order: per 16-column chunk and 16-dim
         # step q, 64 lanes (g = dim quarter, n = column) of 4 dims each
@@ -117,6 +118,11 @@ def test_block_stats(name):
         valid = (np.arange(NC * 16) < run.N).reshape(NC, 16)[:, None, None, :, None]
         got_r = kbr[0, h].reshape(want_r.shape)
         assert np.array_equal(np.where(valid, got_r, 0), want_r), h
+        if ksr is not None:   # ksig2 in fp32, the same order
+            spad = np.zeros((NC * 16, D), np.float32)
+            spad[:run.N] = ks2[0, h].astype(np.float32)
+            want_s = spad.reshape(NC, 16, 4, D // 16, 4).transpose(0, 3, 2, 1, 4)
+            assert np.array_equal(np.where(valid, ksr[0, h].reshape(want_s.shape), 0), want_s), h
         if kp is not None:
             # packed K is a pure re-ordering of k's bits: per block and 32-row
             # half, 16-byte chunks chunk-major, then row; zero rows past T

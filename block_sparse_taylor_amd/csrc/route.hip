@@ -158,31 +158,35 @@ __device__ __forceinline__ uint32_t wave_select32(const uint32_t (&kv)[KPL], int
 // taken-bit masks. At N = 512 without the second order it is 39.3 KB, so four
 // workgroups share a CU.
 __host__ __device__ inline int fast_np(int N) { return (N + 3) & ~3; }
-__host__ __device__ inline size_t fast_lds_bytes(int D, int N, int second_order) {
+__host__ __device__ inline size_t fast_lds_bytes(int D, int N, int second_order, int nwv) {
     const int NP = fast_np(N);
-    return (size_t)8 * kQB * D * (second_order ? 1 : 0) + (size_t)4 * kQB * NP + 4 * 4 * 256 +
-           (size_t)4 * kAmbCap * (4 + 8) + (size_t)4 * 4 * ((NP + 31) / 32);
+    return (size_t)8 * kQB * D * (second_order ? 1 : 0) + (size_t)4 * kQB * NP + (size_t)nwv * 4 * 256 +
+           (size_t)nwv * kAmbCap * (4 + 8) + (size_t)4 * nwv * ((NP + 31) / 32);
 }
+// Waves per workgroup: rows of more than 1024 blocks fill most of the LDS
+// (one workgroup per CU), so those take eight waves (two per SIMD).
+__host__ __device__ constexpr int route_waves(int kpl) { return kpl > 16 ? 8 : 4; }
 
 // KPL: keys per lane of a score row (N <= 64 KPL); rows of up to 1024 blocks
 // without the second order fit four waves per SIMD.
 template <int D, bool SO, int KPL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(SO || KPL > 16 ? 2 : 4))) void route_fast_kernel(
+__global__ __launch_bounds__(64 * route_waves(KPL)) __attribute__((amdgpu_waves_per_eu(SO || KPL > 16 ? 2 : 4))) void route_fast_kernel(
     const double* __restrict__ qbar, const double* __restrict__ q2bar, const double* __restrict__ kbar,
     const float* __restrict__ kbar_r, const double* __restrict__ ksig2, const float* __restrict__ ksig2_r,
     int N, double s64, int topk, int band, int n_sink,
     int32_t* __restrict__ idx, float* __restrict__ wgate) {
     constexpr int KS = D / 4;       // 16x16x4 k-steps; MFMA k-slot (ks, l/16) <-> dim (D/4)(l/16) + ks
     constexpr bool second_order = SO;
+    constexpr int NWV = route_waves(KPL), NT = 64 * NWV;
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     const int NP = fast_np(N), NW = (NP + 31) / 32;
     double* q2_s = reinterpret_cast<double*>(lds);                   // second order only
     float* score_s = reinterpret_cast<float*>(q2_s + (second_order ? kQB * D : 0));
     unsigned* hist_s = reinterpret_cast<unsigned*>(score_s + kQB * NP);
-    int* amb_j_s = reinterpret_cast<int*>(hist_s + 4 * 256);
-    double* amb_r_s = reinterpret_cast<double*>(amb_j_s + 4 * kAmbCap);
-    uint32_t* take_s = reinterpret_cast<uint32_t*>(amb_r_s + 4 * kAmbCap);
-    __shared__ float kmax_s[4];
+    int* amb_j_s = reinterpret_cast<int*>(hist_s + NWV * 256);
+    double* amb_r_s = reinterpret_cast<double*>(amb_j_s + NWV * kAmbCap);
+    uint32_t* take_s = reinterpret_cast<uint32_t*>(amb_r_s + NWV * kAmbCap);
+    __shared__ float kmax_s[NWV];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -194,7 +198,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(SO || 
 
     // pooled q'^2 of the tile's query blocks (zeros past N), second order only
     if (second_order) {
-        for (int e = tid; e < kQB * D; e += kThreads) {
+        for (int e = tid; e < kQB * D; e += NT) {
             const int r = e / D;
             q2_s[e] = r < nq ? q2bar[(bh * N + i0 + r) * (int64_t)D + e % D] : 0.0;
         }
@@ -203,7 +207,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(SO || 
     const double* qrows = qbar + (bh * N + i0) * (int64_t)D;   // fp64 pooled queries of the tile
 
     // ---- scores: S[r][j] = s qbar_r . kbar_j (+ min(w, ln B)) via fp32 MFMA.
-    // Wave w takes the 16-column chunks c = w, w+4, ...; lane (m16, g4) needs
+    // Wave w takes the 16-column chunks c = w, w+NWV, ...; lane (m16, g4) needs
     // kbar[16 c + m16][(D/4) g4 + ks] for ks < KS, which kbar_r holds as D/16
     // 1 KB runs per chunk (16 bytes per lane), loaded one chunk ahead.
     typedef double d2_t __attribute__((ext_vector_type(2)));
@@ -232,7 +236,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(SO || 
         for (int qq = 0; qq < KS / 4; ++qq) kv[qq] = kr4[((int64_t)c * (KS / 4) + qq) * 64 + lane];
     };
     if (wave < NC) kload(wave);
-    for (int c = wave; c < NC; c += 4) {
+    for (int c = wave; c < NC; c += NWV) {
         const int col = c * 16 + m16;
         const bool ok = col < N;
         float b[KS];
@@ -243,7 +247,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(SO || 
             b[4 * qq + 2] = ok ? kv[qq].z : 0.f;
             b[4 * qq + 3] = ok ? kv[qq].w : 0.f;
         }
-        if (c + 4 < NC) kload(c + 4);   // the next chunk
+        if (c + NWV < NC) kload(c + NWV);   // the next chunk
         float4 sv[SO ? KS / 4 : 1];       // ksig2 of this chunk (second order), same order as kbar_r
         if (SO) {
 #pragma unroll
@@ -297,10 +301,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(SO || 
     kmax2 = fmaxf(kmax2, __shfl_xor(kmax2, 8));
     if (lane == 0) kmax_s[wave] = kmax2;
     __syncthreads();
-    const double kmax = sqrt((double)fmaxf(fmaxf(kmax_s[0], kmax_s[1]), fmaxf(kmax_s[2], kmax_s[3]))) *
+    float kmx = kmax_s[0];
+#pragma unroll
+    for (int w = 1; w < NWV; ++w) kmx = fmaxf(kmx, kmax_s[w]);
+    const double kmax = sqrt((double)kmx) *
                         (1.0 + 1e-6);
 
-    // ---- selection: wave w handles rows w, w+4, w+8, w+12. A row's candidate
+    // ---- selection: wave w handles rows w, w+NWV, ... A row's candidate
     // keys stay in registers (lane l holds columns 64 i + l, i < KPL) from the
     // threshold search through the classification and the ascending write.
     unsigned* hist = hist_s + wave * 256;
@@ -460,7 +467,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(SO || 
         }
         for (int c = written + lane; c < topk; c += 64) out[c] = -1;
     };
-    for (int r = wave; r < nq; r += 4) row_pass(r);
+    for (int r = wave; r < nq; r += NWV) row_pass(r);
 }
 
 // General fallback for long sequences (score rows beyond the LDS): one workgroup per
@@ -586,13 +593,14 @@ hipError_t launch_route_topk(const Geom& g, const pisa_params_t* p, const pisa_s
                              int32_t* idx, float* wgate, hipStream_t stream) {
     const int so = p->second_order;
     if (p->topk == 0 && !so) return hipSuccess;
-    dim3 block(kThreads);
-    const size_t lds = fast_lds_bytes(g.D, g.N, so);
+    const int kc = g.N <= 64 * 8 ? 0 : (g.N <= 64 * 16 ? 1 : 2);
+    const int nwv = route_waves(kc == 0 ? 8 : (kc == 1 ? 16 : kKeysPerLane));
+    const size_t lds = fast_lds_bytes(g.D, g.N, so, nwv);
     if (lds + 64 <= (size_t)kLdsMax && g.N <= 64 * kKeysPerLane) {
+        const dim3 block(64 * nwv);
         using Fn = void (*)(const double*, const double*, const double*, const float*, const double*, const float*,
                             int, double, int, int, int, int32_t*, float*);
         static bool attr_set[2][2][3] = {};
-        const int kc = g.N <= 64 * 8 ? 0 : (g.N <= 64 * 16 ? 1 : 2);
         static const Fn table[2][2][3] = {
             {{&route_fast_kernel<64, false, 8>, &route_fast_kernel<64, false, 16>,
               &route_fast_kernel<64, false, kKeysPerLane>},
@@ -614,7 +622,7 @@ hipError_t launch_route_topk(const Geom& g, const pisa_params_t* p, const pisa_s
         hipLaunchKernelGGL(fn, grid, block, lds, stream, st->qbar, st->q2bar, st->kbar, st->kbar_r, st->ksig2, st->ksig2_r, g.N,
                            g.scale64, p->topk, p->band, p->n_sink, idx, wgate);
     } else {
-        dim3 grid(g.N, (unsigned)g.BH);
+        const dim3 grid(g.N, (unsigned)g.BH), block(kThreads);
 #define PISA_ROUTE_LAUNCH(DD)                                                                      \
     hipLaunchKernelGGL(route_slow_kernel<DD>, grid, block, 0, stream, st->qbar, st->q2bar,         \
                        st->kbar, st->ksig2, g.N, g.scale64, p->topk, p->band, p->n_sink, so, idx, wgate)

@@ -270,7 +270,7 @@ def main():
     attn_tflops = attn_flops / (attn_ms * 1e-3) / 1e12
 
     e = 2 if w.dtype == "bf16" else 4
-    groups = min(max(1, 512 // (B * H)), -(-N // 16))     # the statistics pass's block ranges per head
+    groups = min(max(1, 512 // (B * H)), -(-N // 4))      # the statistics pass's block ranges per head
     G = -(-N // -(-N // groups))
     BHND = B * H * N * D
     stats_bytes = (3 * B * H * T * D * e                     # read Q, K, V

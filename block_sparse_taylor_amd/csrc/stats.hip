@@ -40,9 +40,11 @@ __device__ __forceinline__ void nt_store(void* p, uint4 v) {
 constexpr int kPad = 4;   // LDS row padding (elements): rows 8 apart fall on disjoint bank halves
 // Blocks per workgroup: the (head, block range) workgroups of one call should
 // all be resident at once. Two of these workgroups fit on a CU and MI355X has
-// 256 CUs, so a head gets max(1, 512 / heads) ranges of at least 16 blocks.
+// 256 CUs, so a head gets max(1, 512 / heads) ranges of at least 4 blocks
+// (small problems still spread over the CUs; each range adds a D x D partial
+// to write and reduce).
 constexpr int kResidentWGs = 512;
-constexpr int kMinBPW = 16;
+constexpr int kMinBPW = 4;
 
 struct StatsOut {
     double* qbar;

@@ -59,11 +59,13 @@ def test_invalid_shapes(lib, bad):
 
 def test_workspace_bytes(lib):
     # one D x D fp32 partial per block range; a head gets max(1, 512 / heads)
-    # ranges of at least 16 blocks: 12 ranges of 43 blocks for 40 heads of 512
+    # ranges of at least 4 blocks: 12 ranges of 43 blocks for 40 heads of 512
     s = shape(T=32760, D=128, H=40)
     assert lib.pisa_stats_workspace_bytes(ctypes.byref(s)) == 40 * 12 * 128 * 128 * 4
-    s = shape(T=1000, D=64, H=2)       # 16 blocks: one range
-    assert lib.pisa_stats_workspace_bytes(ctypes.byref(s)) == 2 * 1 * 64 * 64 * 4
+    s = shape(T=1000, D=64, H=2)       # 16 blocks: four ranges of 4
+    assert lib.pisa_stats_workspace_bytes(ctypes.byref(s)) == 2 * 4 * 64 * 64 * 4
+    s = shape(T=4608, D=128, H=24)     # FLUX: 72 blocks, 18 ranges of 4
+    assert lib.pisa_stats_workspace_bytes(ctypes.byref(s)) == 24 * 18 * 128 * 128 * 4
 
 
 FAKE = 1 << 20          # 16-byte aligned fake device address: only used where validation fails first

@@ -96,45 +96,64 @@ __global__ __launch_bounds__(kRows) void attn_valu_kernel(
         }
     }
 
-    // Phase 2: virtual tokens of the unselected blocks.
+    // Phase 2: virtual tokens of the unselected blocks, kbar (as fp32) and
+    // V-hat of kSub consecutive blocks staged in LDS at a time.
     if (do_virtual) {
         const double* kb = kbar + bh * (int64_t)N * D;
         const float* vs = vsum + bh * (int64_t)N * D;
         const float* wr = second_order ? wgate + (bh * (int64_t)N + i) * N : nullptr;
-        for (int j = 0; j < N; ++j) {
-            if (sel[j]) continue;
-            const int nj = min(kBlock, Tn - j * kBlock);
-            float z = 0.f;
-#pragma unroll
-            for (int d = 0; d < D; ++d) z = fmaf(qv[d], (float)kb[(int64_t)j * D + d], z);
-            if (second_order) z += wr[j];
-            const float lnn = logf((float)nj);
-            const float zm = z + lnn;
-            if (zm > m) {
-                const float c = expf(m - zm);
-                l *= c;
-                ltail *= c;
-#pragma unroll
-                for (int d = 0; d < D; ++d) acc[d] *= c;
-                m = zm;
+        for (int j0 = 0; j0 < N; j0 += kSub) {
+            const int nh = min(kSub, N - j0);
+            __syncthreads();
+            for (int c = tid; c < nh * D; c += kRows) {
+                sk[c] = (float)kb[(int64_t)j0 * D + c];
+                sv[c] = vs[(int64_t)j0 * D + c];
             }
-            const float a = expf(z - m);     // e^{lam - m}
-            const float mass = a * (float)nj;
-            l += mass;
-            ltail += mass;
+            __syncthreads();
+            for (int n = 0; n < nh; ++n) {
+                const int j = j0 + n;
+                if (sel[j]) continue;
+                const int nj = min(kBlock, Tn - j * kBlock);
+                float z = 0.f;
 #pragma unroll
-            for (int d = 0; d < D; ++d) acc[d] = fmaf(a, vs[(int64_t)j * D + d], acc[d]);
+                for (int d = 0; d < D; ++d) z = fmaf(qv[d], sk[n * D + d], z);
+                if (second_order) z += wr[j];
+                const float lnn = logf((float)nj);
+                const float zm = z + lnn;
+                if (zm > m) {
+                    const float c = expf(m - zm);
+                    l *= c;
+                    ltail *= c;
+#pragma unroll
+                    for (int d = 0; d < D; ++d) acc[d] *= c;
+                    m = zm;
+                }
+                const float a = expf(z - m);     // e^{lam - m}
+                const float mass = a * (float)nj;
+                l += mass;
+                ltail += mass;
+#pragma unroll
+                for (int d = 0; d < D; ++d) acc[d] = fmaf(a, sv[n * D + d], acc[d]);
+            }
         }
     }
 
-    // Phase 3: global first order and normalisation.
-    if (do_first && ltail > 0.f) {
+    // Phase 3: global first order, acc += (l_tail / T) (s q) H, with H staged
+    // in LDS kSub rows at a time (every thread takes part in the staging).
+    if (do_first) {
         const float* H = hsum + bh * (int64_t)D * D;
-        const float c = ltail / (float)Tn;
-        for (int e = 0; e < D; ++e) {
-            float gsum = 0.f;
-            for (int d = 0; d < D; ++d) gsum = fmaf(qv[d], H[d * D + e], gsum);
-            acc[e] = fmaf(c, gsum, acc[e]);
+        const float cf = ltail > 0.f ? ltail / (float)Tn : 0.f;
+#pragma unroll
+        for (int d0 = 0; d0 < D; d0 += kSub) {
+            __syncthreads();
+            for (int c = tid; c < kSub * D; c += kRows) sk[c] = H[(int64_t)d0 * D + c];
+            __syncthreads();
+#pragma unroll
+            for (int d = 0; d < kSub; ++d) {
+                const float w = cf * qv[d0 + d];
+#pragma unroll
+                for (int e = 0; e < D; ++e) acc[e] = fmaf(w, sk[d * D + e], acc[e]);
+            }
         }
     }
     if (active) {

@@ -285,7 +285,9 @@ def main():
                    + (B * H * N * N * 4 if so else 0))       # gated w table
 
     out = {
-        "metric": "pisa_attn_fwd ms & dense-equiv TFLOP/s, Wan2.1-14B shape, density 0.125",
+        "metric": ("pisa_attn_fwd ms & dense-equiv TFLOP/s, Wan2.1-14B shape, density 0.125"
+                   if w.name == "wan14" else
+                   f"pisa_attn_fwd ms & dense-equiv TFLOP/s, {w.name} shape, density {w.density}"),
         "value": round(dense_flops / (ms_step * 1e-3) / 1e12, 2),
         "unit": "TFLOP/s dense-equivalent (4 B H T^2 D per full step: stats + route + fused forward)",
         "n_gpus": 1,

@@ -41,7 +41,7 @@ R11 q2bar = mean over the query block of (s*q)^2 (elementwise); sigma^2 is
     the population variance (1/n_j).
 R12 gate: w > ln B  ->  0 (strict), w = ln B kept.
 R13 the gated w enters the virtual logit, hence numerator, mass and l_tail.
-R14 sink blocks ([PWT] knobs: n_sink_blocks=n forces the first n KV blocks,
+R16 sink blocks ([PWT] knobs: n_sink_blocks=n forces the first n KV blocks,
     e.g. an MMDiT text prefix, into the exact branch): like the band they are
     forced for every query block and top-k is taken over the other blocks.
 """
@@ -157,7 +157,7 @@ def route_topk(qbar, kbar, scale, topk, band, w_rank=None, band_mode="additive",
     Eq. 11 minus its covariance term, R7; [PWT] router with min(w, ln B)).
     Band_i = {j : |i-j| <= band} is forced exact ([PWT] knobs: band=b).
     additive (R9): Top_i = the min(topk, |Cand_i|) best of Cand_i = all \\ Band_i
-    \\ Sinks, Sinks = {j < n_sink} (R14).
+    \\ Sinks, Sinks = {j < n_sink} (R16).
     union: Top_i = the topk best of all blocks (the band is added afterwards).
     Ranking key (-r_ij, j): ties go to the lower index (R10).
     Returns (idx [Nq, topk] int32 ascending, -1 padded; scores r [Nq, Nk]).
@@ -183,7 +183,7 @@ def route_topk(qbar, kbar, scale, topk, band, w_rank=None, band_mode="additive",
 
 def selected_sets(idx_row: np.ndarray, i: int, N: int, band: int, n_sink: int = 0):
     """S_i = Band_i union Sinks union Top_i, U_i = complement  ([PISA] §3.2
-    Formulation; sinks R14)."""
+    Formulation; sinks R16)."""
     S = set(int(j) for j in idx_row if 0 <= j < N)
     S.update(j for j in range(max(0, i - band), min(N, i + band + 1)))
     S.update(range(min(n_sink, N)))
@@ -224,7 +224,7 @@ def pisa_forward_head(q, k, v, *, B=64, scale=None, topk, band=1, second_order=F
 
     routing: None (computed here) or an [N, topk] table (-1 padded) that is
     used as Top_i verbatim ("fed the GPU's routing").
-    n_sink: the first n_sink KV blocks are exact for every query block (R14).
+    n_sink: the first n_sink KV blocks are exact for every query block (R16).
     query_blocks: iterable of block indices to evaluate (others stay NaN).
     Returns o [T, D] (and a dict of intermediate quantities if return_parts).
     """

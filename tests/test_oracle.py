@@ -309,7 +309,7 @@ def test_routing_known_ranking_band_ties_padding():
 
 
 def test_routing_with_sink_blocks_known_ranking():
-    """Sinks (R14) are forced like the band: never routed, top-k over the rest."""
+    """Sinks (R16) are forced like the band: never routed, top-k over the rest."""
     N = 10
     qbar = np.ones((N, 1))
     c = np.array([5.0, 1.0, 9.0, 9.0, 0.0, 7.0, 3.0, 9.0, 2.0, 8.0])

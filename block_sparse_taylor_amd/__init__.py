@@ -27,7 +27,7 @@ from . import _lib
 from ._lib import PISA_BF16, PISA_F32, PisaError
 
 __all__ = ["PisaStats", "pisa_block_stats", "pisa_route_topk", "pisa_attn_fwd",
-           "pisa_attn_fwd_valu", "piecewise_sparse_attention", "num_blocks", "topk_for_density",
+           "pisa_attn_fwd_valu", "pisa_attn_bwd", "piecewise_sparse_attention", "num_blocks", "topk_for_density",
            "z_order", "reorder_gather", "reorder_scatter", "PisaError", "library"]
 
 BLOCK = 64
@@ -190,6 +190,31 @@ def pisa_attn_fwd_valu(q, k, v, stats, idx, wgate=None, band=1, second_order=Fal
     topk = 0 if idx is None else idx.shape[-1]
     return _attn("pisa_attn_fwd_valu", q, k, v, stats, idx, wgate, topk, band, second_order,
                  first_order, phase_mask, scale, out, n_sink)
+
+
+def pisa_attn_bwd(q, k, v, o, dout, stats, idx, wgate=None, band=1, second_order=False,
+                  first_order=True, scale=None, n_sink=0, workspace=None, out=None):
+    """(dq, dk, dv) of sum(dout * o) for o = pisa_attn_fwd(q, k, v, stats, idx,
+    wgate, ...) with the same arguments; the routing and the gate are held
+    constant (pisa_attn_bwd). ``out`` may pass three preallocated tensors."""
+    lib = library()
+    _contig(q, k, v, o, dout, idx, wgate)
+    for t in (k, v, o, dout):
+        if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("q, k, v, o, dout must share shape, dtype and device")
+    sh = _shape(q, scale)
+    topk = 0 if idx is None else idx.shape[-1]
+    need = lib.pisa_attn_bwd_workspace_bytes(ctypes.byref(sh))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    dq, dk, dv = out if out is not None else (torch.empty_like(q), torch.empty_like(q), torch.empty_like(q))
+    prm = _lib.Params(int(topk), int(band), int(second_order), int(first_order), 0, int(n_sink))
+    cs = stats.as_c()
+    _lib.check("pisa_attn_bwd", lib.pisa_attn_bwd(
+        ctypes.byref(sh), ctypes.byref(prm), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout),
+        ctypes.byref(cs), _ptr(idx) if topk else None, _ptr(wgate) if second_order else None,
+        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), _stream(q.device)))
+    return dq, dk, dv
 
 
 def z_order(grid, prefix: int = 0) -> torch.Tensor:

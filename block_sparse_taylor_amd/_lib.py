@@ -19,7 +19,8 @@ PISA_F32, PISA_BF16 = 0, 1
 EXPORTED = (
     "pisa_abi_version", "pisa_status_str", "pisa_num_blocks", "pisa_stats_workspace_bytes",
     "pisa_block_stats", "pisa_route_topk", "pisa_attn_fwd", "pisa_attn_fwd_valu",
-    "pisa_z_order", "pisa_reorder_gather", "pisa_reorder_scatter",
+    "pisa_z_order", "pisa_reorder_gather", "pisa_reorder_scatter", "pisa_attn_bwd_workspace_bytes",
+    "pisa_attn_bwd",
 )
 
 
@@ -78,6 +79,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [P(Shape), P(Params), vp, vp, vp, P(Stats), vp, vp, vp, vp]
+    lib.pisa_attn_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.pisa_attn_bwd_workspace_bytes.argtypes = [P(Shape)]
+    lib.pisa_attn_bwd.restype = ctypes.c_int
+    lib.pisa_attn_bwd.argtypes = [P(Shape), P(Params), vp, vp, vp, vp, vp, P(Stats), vp, vp, vp, vp, vp, vp,
+                                  ctypes.c_size_t, vp]
     lib.pisa_z_order.restype = ctypes.c_int
     lib.pisa_z_order.argtypes = [P(ctypes.c_int64), ctypes.c_int32, ctypes.c_int64, P(ctypes.c_int32),
                                  ctypes.c_int64]

@@ -84,6 +84,12 @@ hipError_t launch_reorder(const Geom& g, int64_t batch, int64_t heads, int elem_
                           const int32_t* perm, const void* src, void* dst, hipStream_t stream);
 void z_order_host(const int64_t* grid, int ndim, int64_t prefix, int32_t* perm);
 
+size_t attn_bwd_workspace_bytes(const Geom& g);
+hipError_t launch_attn_bwd(const Geom& g, int dtype, const pisa_params_t* p, const void* q, const void* k,
+                           const void* v, const void* o, const void* dout, const pisa_stats_t* st,
+                           const int32_t* idx, const float* wgate, void* dq, void* dk, void* dv, void* ws,
+                           hipStream_t stream);
+
 hipError_t launch_attn_fwd_mfma(const Geom& g, const pisa_params_t* p, const void* q, const void* k,
                                 const void* v, const pisa_stats_t* st, const int32_t* idx,
                                 const float* wgate, void* o, hipStream_t stream);

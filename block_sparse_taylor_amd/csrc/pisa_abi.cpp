@@ -186,6 +186,39 @@ pisa_status_t pisa_attn_fwd_valu(const pisa_shape_t* shape, const pisa_params_t*
                                          static_cast<hipStream_t>(stream)));
 }
 
+size_t pisa_attn_bwd_workspace_bytes(const pisa_shape_t* shape) {
+    Geom g;
+    if (check_shape(shape, &g) != PISA_OK) return 0;
+    return attn_bwd_workspace_bytes(g);
+}
+
+pisa_status_t pisa_attn_bwd(const pisa_shape_t* shape, const pisa_params_t* params, const void* q,
+                            const void* k, const void* v, const void* o, const void* dout,
+                            const pisa_stats_t* stats, const int32_t* idx, const float* wgate, void* dq,
+                            void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream) {
+    Geom g;
+    PISA_TRY(check_shape(shape, &g));
+    PISA_TRY(check_params(params, g));
+    const void* ptrs[9] = {q, k, v, o, dout, dq, dk, dv, workspace};
+    for (const void* ptr : ptrs) PISA_TRY(check_ptr(ptr));
+    PISA_TRY(check_stats(stats, params->second_order, false, false));
+    if (params->second_order) PISA_TRY(check_ptr(stats->q2bar));
+    if (params->topk > 0) PISA_TRY(check_ptr(idx));
+    if (params->second_order) PISA_TRY(check_ptr(wgate));
+    if (params->phase_mask != 0) return PISA_ERR_UNSUPPORTED;
+    if (workspace_bytes < attn_bwd_workspace_bytes(g)) return PISA_ERR_WORKSPACE;
+    const void* outs[3] = {dq, dk, dv};
+    const void* ins[6] = {q, k, v, o, dout, workspace};
+    for (int a = 0; a < 3; ++a) {
+        for (int b = a + 1; b < 3; ++b)
+            if (outs[a] == outs[b]) return PISA_ERR_PARAM;
+        for (const void* in : ins)
+            if (outs[a] == in) return PISA_ERR_PARAM;
+    }
+    return from_hip(launch_attn_bwd(g, shape->dtype, params, q, k, v, o, dout, stats, idx, wgate, dq, dk,
+                                    dv, workspace, static_cast<hipStream_t>(stream)));
+}
+
 pisa_status_t pisa_z_order(const int64_t* grid, int32_t ndim, int64_t prefix, int32_t* perm, int64_t n) {
     if (!grid || !perm) return PISA_ERR_NULL;
     if (ndim < 1 || ndim > 4 || prefix < 0) return PISA_ERR_SHAPE;

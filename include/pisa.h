@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define PISA_ABI_VERSION 8
+#define PISA_ABI_VERSION 9
 
 typedef enum {
     PISA_OK = 0,
@@ -263,6 +263,42 @@ pisa_status_t pisa_reorder_gather(const pisa_shape_t *shape, const int32_t *perm
                                   void *out, void *stream);
 pisa_status_t pisa_reorder_scatter(const pisa_shape_t *shape, const int32_t *perm, const void *o,
                                    void *y, void *stream);
+
+/*
+ * Backward of pisa_attn_fwd ("Piecewise-Taylor-Attention" README: the
+ * trainable regime, gradients through both the exact and the approximate
+ * branch with the block selection detached; PISA §3.2 Eqs. 3-5 and §3.3
+ * Eqs. 9-10 for the function being differentiated).
+ *
+ * pisa_attn_bwd writes dq, dk, dv = the gradients of L = sum dout . o with
+ * respect to q, k and v, where o is pisa_attn_fwd's output for the same
+ * shape, params, q, k, v, stats, idx and wgate. idx and the gate (which pairs
+ * of wgate hold 0) are constants of the differentiation; every statistic the
+ * forward derives from q, k, v (block means, V-hat, H, and for second order
+ * the pooled q^2 and the key variance inside w_ij) is differentiated through.
+ * Arguments:
+ *   q, k, v, o, dout  [B,H,T,D] in the shape's dtype (o as the forward wrote
+ *                     it: it enters only through delta_t = dout_t . o_t);
+ *   stats             as pisa_block_stats wrote them for q, k, v; reads kbar,
+ *                     vsum, hsum (and q2bar, ksig2 if second_order);
+ *   idx, wgate        as passed to pisa_attn_fwd;
+ *   dq, dk, dv        [B,H,T,D] outputs in the shape's dtype; they must not
+ *                     alias each other, the inputs, or the workspace;
+ *   workspace         caller-owned device memory of at least
+ *                     pisa_attn_bwd_workspace_bytes(shape) bytes (per-row
+ *                     statistics, the selection bitmask, per-block partial
+ *                     gradients, dH); contents on entry are ignored and on
+ *                     return unspecified.
+ * params->phase_mask must be 0 (PISA_ERR_UNSUPPORTED otherwise). All
+ * arithmetic is fp32 (bf16 inputs widened exactly); each gradient is rounded
+ * once to the output dtype. Deterministic: no floating-point atomics.
+ */
+size_t pisa_attn_bwd_workspace_bytes(const pisa_shape_t *shape);
+pisa_status_t pisa_attn_bwd(const pisa_shape_t *shape, const pisa_params_t *params,
+                            const void *q, const void *k, const void *v, const void *o,
+                            const void *dout, const pisa_stats_t *stats, const int32_t *idx,
+                            const float *wgate, void *dq, void *dk, void *dv, void *workspace,
+                            size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -32,7 +32,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pisa_abi_version() == 8
+    assert lib.pisa_abi_version() == 9
     for code in range(9):
         assert lib.pisa_status_str(code)
     assert lib.pisa_status_str(99) == b"unknown status"
@@ -165,6 +165,45 @@ def test_attn_validation(lib, name):
     assert call_attn(lib, name, st=stats(vbar_c=None)) == E["PISA_ERR_NULL"]
     assert call_attn(lib, name, s=shape(dtype=2)) == E["PISA_ERR_DTYPE"]
     assert call_attn(lib, name, s=shape(T=10 ** 7)) == E["PISA_ERR_SHAPE"]
+
+
+def call_bwd(lib, s=None, p=None, q=FAKE, k=FAKE + 64, v=FAKE + 128, o=FAKE + 192, do=FAKE + 256,
+             st=None, idx=FAKE, wg=None, dq=FAKE + 320, dk=FAKE + 384, dv=FAKE + 448, ws=FAKE + 512,
+             wsb=1 << 40):
+    s = s or shape()
+    p = p or _lib.Params(4, 1, 0, 1, 0)
+    st = st or stats()
+    return lib.pisa_attn_bwd(ctypes.byref(s), ctypes.byref(p), q, k, v, o, do, ctypes.byref(st), idx, wg,
+                             dq, dk, dv, ws, wsb, None)
+
+
+def test_bwd_workspace_bytes(lib):
+    s = shape(T=1000, D=128, H=3)
+    n = lib.pisa_attn_bwd_workspace_bytes(ctypes.byref(s))
+    N = 16
+    # per-row statistics, bitmask rows, three per-block gradients, dH and its partial sums
+    assert n >= 3 * 1000 * 16 + 3 * N * 4 + 3 * 3 * N * 128 * 4 + 3 * 2 * 128 * 128 * 4
+    assert lib.pisa_attn_bwd_workspace_bytes(ctypes.byref(shape(T=0))) == 0
+
+
+def test_bwd_validation(lib):
+    for name in ("q", "k", "v", "o", "do", "dq", "dk", "dv", "ws"):
+        assert call_bwd(lib, **{name: None}) == E["PISA_ERR_NULL"], name
+        assert call_bwd(lib, **{name: MIS}) == E["PISA_ERR_ALIGN"], name
+    assert call_bwd(lib, idx=None) == E["PISA_ERR_NULL"]
+    assert call_bwd(lib, st=stats(hsum=None)) == E["PISA_ERR_NULL"]
+    assert call_bwd(lib, st=stats(kpack=None, hpack=None, kbpack=None, kbar_c=None, vbar_c=None),
+                    wsb=0) == E["PISA_ERR_WORKSPACE"]                                  # packs not needed
+    so = _lib.Params(4, 1, 1, 1, 0)
+    assert call_bwd(lib, p=so, wg=FAKE) == E["PISA_ERR_NULL"]                          # ksig2
+    assert call_bwd(lib, p=so, wg=FAKE, st=stats(ksig2=FAKE)) == E["PISA_ERR_NULL"]    # q2bar
+    assert call_bwd(lib, p=so, st=stats(ksig2=FAKE, q2bar=FAKE)) == E["PISA_ERR_NULL"]  # wgate
+    assert call_bwd(lib, p=_lib.Params(4, 1, 0, 1, 1)) == E["PISA_ERR_UNSUPPORTED"]   # phase mask
+    assert call_bwd(lib, wsb=100) == E["PISA_ERR_WORKSPACE"]
+    assert call_bwd(lib, dk=FAKE + 320) == E["PISA_ERR_PARAM"]                          # dq == dk
+    assert call_bwd(lib, dv=FAKE) == E["PISA_ERR_PARAM"]                                # dv == q
+    assert call_bwd(lib, dq=FAKE + 512) == E["PISA_ERR_PARAM"]                          # dq == workspace
+    assert call_bwd(lib, p=_lib.Params(4, 1, 0, 1, 0, 99)) == E["PISA_ERR_PARAM"]      # sinks > N
 
 
 def test_null_structs(lib):

@@ -20,6 +20,7 @@ stands) on a bounded sample of the same workload on the host cores.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import math
 import os
@@ -29,6 +30,7 @@ import time
 import numpy as np
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, datasheet
+PEAK_FP32_TFLOPS = 157.3   # MI355X fp32 vector (packed) peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, datasheet
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -119,6 +121,9 @@ def parse():
     ap.add_argument("--no-phase1", action="store_true",
                     help="skip the extra launches after the timed steps (Phase 1 alone, the Morton "
                          "reorder), so that a kernel trace or counter run sees only the steps")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the pisa_attn_bwd leg (timed after the forward steps)")
+    ap.add_argument("--bwd-steps", type=int, default=3)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run a plain copy of COPY_BYTES three times "
                          "(the reference kernel for the HBM byte counters)")
@@ -269,6 +274,28 @@ def main():
                        "frac_hbm": round(rbytes / (rms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
             del xt, ht, ot
 
+    # Backward (pisa_attn_bwd) of the last step's forward, on seeded dout,
+    # timed on its own after the steps: one call runs all its kernels
+    bwd_ms = None
+    if not args.no_backward:
+        gen = torch.Generator(device=dev).manual_seed(1234)
+        dout = torch.randn(q.shape, generator=gen, device=dev, dtype=torch.float32).to(q.dtype)
+        grads = tuple(torch.empty_like(q) for _ in range(3))
+        bws = torch.empty(P.library().pisa_attn_bwd_workspace_bytes(ctypes.byref(P._shape(q, None))),
+                          dtype=torch.uint8, device=dev)
+        bwd = lambda: P.pisa_attn_bwd(q, k, v, o, dout, st, idx if topk else None, wg, band=w.band,
+                                      second_order=so, workspace=bws, out=grads)
+        bwd()
+        torch.cuda.synchronize()
+        b0, b1 = ev(), ev()
+        b0.record(stream)
+        for _ in range(args.bwd_steps):
+            bwd()
+        b1.record(stream)
+        torch.cuda.synchronize()
+        bwd_ms = b0.elapsed_time(b1) / args.bwd_steps
+        del grads, bws, dout
+
     # ---- algorithmic work of the fused kernel (from the routing table actually used)
     idx_h = idx.cpu().numpy().reshape(B * H, N, topk)
     nrow = np.array([min(64, T - 64 * j) for j in range(N)], dtype=np.int64)
@@ -339,6 +366,16 @@ def main():
                      "traffic": load_traffic(w.name), "kernel": ATTN_KERNEL + " (pisa_attn_fwd)"},
         "input_generation_s": round(gen_s, 1),
     }
+    if bwd_ms is not None:
+        # five products per attended pair (recomputed logits, dP, dV, dK, dQ; the
+        # virtual tokens likewise with kbar and V-hat), plus H g and dH per row
+        bwd_flops = 10 * D * (exact_pairs + virt_pairs) + 4 * D * D * B * H * T
+        bwd_tflops = bwd_flops / (bwd_ms * 1e-3) / 1e12
+        out["pisa_attn_bwd"] = {
+            "ms": round(bwd_ms, 3), "steps": args.bwd_steps, "algorithmic_tflop": round(bwd_flops / 1e12, 4),
+            "roofline": {"bound": "alu", "achieved": round(bwd_tflops, 2), "peak": PEAK_FP32_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(bwd_tflops / PEAK_FP32_TFLOPS, 4), "traffic": None,
+                         "kernel": "pisa_attn_bwd (all its kernels, fp32 VALU)"}}
 
     if args.copy_calibration:
         src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)

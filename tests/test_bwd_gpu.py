@@ -1,16 +1,27 @@
 """GPU parity of pisa_attn_bwd (through the C ABI) against the float64
 gradient oracle (oracle/backward_oracle.py), fed the GPU's routing.
 
+Two kinds of case. End to end: the backward gets the GPU forward's o, and the
+oracle returns the exact gradient. Contract: the backward gets the oracle's
+own forward output rounded to the input dtype (o'), and the oracle returns
+the gradient a backward computes when delta = dout . o' (grads(o_used=o')),
+so only the backward's own arithmetic is measured.
+
 Tolerances, per head and per gradient, on e = max|g - g_ref| / max|g_ref|:
-* fp32 inputs: e <= 2e-5. Every gradient element is an fp32 sum of at most
-  a few thousand products whose terms are bounded by max|g_ref| times the
-  attention weight of their pair; the weights of a row sum to 1, so a sum's
-  rounding stays within about sqrt(n) u ~ 4e-6 of max|g_ref| (u = 2^-24,
-  n <= T), and the forward's o (itself within 1e-5 relative) enters only
-  through delta = dout . o.
-* bf16 inputs: e <= 2e-2. The gradients are rounded once to bf16 (relative
-  2^-9), and delta uses the bf16 output of the MFMA forward, whose P is
-  rounded to bf16 (the forward's own bar is 2e-2 absolute on o).
+* fp32 inputs: e <= 5e-5. Every gradient element is an fp32 sum of at most
+  a few thousand products; the rounding of such a sum stays within about
+  sqrt(n) u (u = 2^-24, n <= T: ~4e-6) of the sum of its terms' magnitudes.
+  Those terms can exceed the result itself: dq_t = sum P (dP - delta) k is a
+  covariance under P, while each term carries the full key, so |terms| /
+  |dq| grows with |mean attended key| / |dq|. On the video-like inputs (keys
+  sharing a smooth field, two key dims scaled by 8) that ratio reaches ~10,
+  hence the bound; the i.i.d. cases stay near 1e-6.
+* bf16, contract: e <= 4e-3: each gradient is rounded once to bf16 (at most
+  2^-9 of its magnitude), on top of the fp32 arithmetic above.
+* bf16, end to end: e <= 2e-2. delta = dout . o uses o stored in bf16, and a
+  delta error c_t moves dq_t by -c_t s E_P[k] (dk likewise; dv not at all),
+  which the mean key of an attended set can make larger than dq_t itself
+  (the oracle module's pins give this closed form).
 """
 
 import dataclasses
@@ -23,12 +34,13 @@ import torch
 import block_sparse_taylor_amd as P
 from block_sparse_taylor_amd import inputs as I
 from oracle import backward_oracle as BO
+from oracle import pisa_oracle as O
 
 from gpu_common import say, to_device
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"f32": 2e-5, "bf16": 2e-2}
+TOL = {("f32", False): 5e-5, ("bf16", False): 2e-2, ("f32", True): 5e-5, ("bf16", True): 4e-3}
 
 
 def device_case(w, seed):
@@ -41,22 +53,44 @@ def device_case(w, seed):
     return [to_device(a, w.dtype) for a in (qa, ka, va, da)], host
 
 
-def check(w, seed, topk, band=1, n_sink=0, so=False, fo=True, idx_fn=None, valu_fwd=False):
+def oracle_output(w, host, ih, s, band, n_sink, so, fo):
+    """The oracle's forward [B,H,T,D] for the GPU's routing, rounded to the input dtype."""
+    o = np.empty(host[0].shape)
+    N = -(-w.seq_len // 64)
+    for b in range(w.batch):
+        for h in range(w.heads):
+            qh, kh, vh = (x[b, h] for x in host[:3])
+            table = ih[b, h] if ih is not None else np.full((N, 1), -1, np.int32)
+            o[b, h] = O.pisa_forward_head(qh, kh, vh, B=64, scale=s, topk=table.shape[1], band=band,
+                                          n_sink=n_sink, second_order=so,
+                                          first_order="global" if fo else "none", routing=table)
+    if w.dtype == "bf16":
+        bits = I.bf16_bits(o.astype(np.float32))
+        return to_device(bits, "bf16"), I.as_f64(bits, "bf16")
+    o32 = o.astype(np.float32)
+    return to_device(o32, "f32"), o32.astype(np.float64)
+
+
+def check(w, seed, topk, band=1, n_sink=0, so=False, fo=True, idx_fn=None, valu_fwd=False, contract=False):
     say(f"[gpu] bwd case: {w.name} T={w.seq_len} D={w.head_dim} {w.dtype} heads={w.heads} topk={topk} "
-        f"band={band} sinks={n_sink} so={so} fo={fo} seed={seed}")
+        f"band={band} sinks={n_sink} so={so} fo={fo} seed={seed} contract={contract}")
     (q, k, v, do), host = device_case(w, seed)
     s = 1.0 / math.sqrt(w.head_dim)
     st = P.pisa_block_stats(q, k, v, second_order=so)
     idx, wg = P.pisa_route_topk(q, st, topk, band=band, second_order=so, n_sink=n_sink)
     if idx_fn is not None:
         idx = idx_fn(idx)
-    fwd = P.pisa_attn_fwd_valu if valu_fwd else P.pisa_attn_fwd
-    o = fwd(q, k, v, st, idx, wg, band=band, second_order=so, first_order=fo, n_sink=n_sink)
+    ih = None if idx is None else idx.cpu().numpy()
+    o_used = None
+    if contract:
+        o, o_used = oracle_output(w, host, ih, s, band, n_sink, so, fo)
+    else:
+        fwd = P.pisa_attn_fwd_valu if valu_fwd else P.pisa_attn_fwd
+        o = fwd(q, k, v, st, idx, wg, band=band, second_order=so, first_order=fo, n_sink=n_sink)
     dq, dk, dv = P.pisa_attn_bwd(q, k, v, o, do, st, idx, wg, band=band, second_order=so, first_order=fo,
                                  n_sink=n_sink)
     torch.cuda.synchronize()
     got = [t.double().cpu().numpy() for t in (dq, dk, dv)]
-    ih = None if idx is None else idx.cpu().numpy()
     worst = 0.0
     for b in range(w.batch):
         for h in range(w.heads):
@@ -64,11 +98,12 @@ def check(w, seed, topk, band=1, n_sink=0, so=False, fo=True, idx_fn=None, valu_
             N = -(-w.seq_len // 64)
             table = ih[b, h] if ih is not None else np.full((N, 1), -1, np.int32)
             ref = BO.grads(qh, kh, vh, dh, table, B=64, scale=s, band=band, n_sink=n_sink,
-                           second_order=so, first_order=fo)
+                           second_order=so, first_order=fo,
+                           o_used=None if o_used is None else o_used[b, h])
             for name, g, r in zip(("dq", "dk", "dv"), got, ref):
                 e = np.abs(g[b, h] - r).max() / np.abs(r).max()
                 worst = max(worst, e)
-                assert e <= TOL[w.dtype], (name, b, h, e)
+                assert e <= TOL[(w.dtype, contract)], (name, b, h, e)
     say(f"[gpu]   worst normalised error {worst:.2e}")
     return worst
 
@@ -90,10 +125,21 @@ def test_fp32_zeroth_order_second_order():
     check(wl("tiny", seq_len=1100, head_dim=64, heads=1, batch=2), seed=3, topk=4, so=True, fo=False)
 
 
+@pytest.mark.parametrize("contract", [False, True])
 @pytest.mark.parametrize("so", [False, True])
-def test_bf16_video(so):
+def test_bf16_video(so, contract):
     w = wl("wan14", heads=2, grid=(3, 11, 31), seq_len=1023, outlier_key_dims=(0, 1))
-    check(w, seed=4, topk=2, so=so)
+    check(w, seed=4, topk=2, so=so, contract=contract)
+
+
+def test_fp32_video_contract():
+    w = wl("wan14", heads=2, grid=(3, 11, 31), seq_len=1023, dtype="f32")
+    check(w, seed=11, topk=3, so=True, n_sink=1, contract=True)
+
+
+def test_bf16_image_sinks_contract():
+    w = wl("flux", heads=2, grid=(30, 32), seq_len=1472, text_tokens=512)
+    check(w, seed=12, topk=3, n_sink=8, so=True, contract=True)
 
 
 def test_bf16_d64_zeroth_order_vs_valu_forward():
@@ -134,3 +180,47 @@ def test_deterministic():
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+def test_full_size_wan14():
+    """The bench's workload in its launch configuration (all 40 heads of the
+    Wan2.1-14B shape, T = 32760, one call). Checked: dq of sampled query blocks
+    of two heads against the oracle one block at a time (end-to-end bf16 bar),
+    and two invariances that hold at any size: shifting every key by one
+    vector shifts all logits of a row equally (H and the key variance do not
+    change), so sum_k dk = 0; shifting every value by one vector shifts every
+    output by it (H does not change since sum (k - kbar) = 0 per block), so
+    sum_k dv = sum_t dout_t. Both sums are compared within 2^-7 of sum |.|
+    (bf16 rounding of each term, 2^-9, with fp32 accumulation)."""
+    from gpu_common import head_f64, oracle_topk, workload_inputs
+    w, arrs = workload_inputs("wan14")
+    say(f"[gpu] bwd full size: {w.batch}x{w.heads}x{w.seq_len}x{w.head_dim} {w.dtype}")
+    q, k, v = (to_device(a, w.dtype) for a in arrs)
+    r = np.random.default_rng(13)
+    dbits = I.bf16_bits(r.standard_normal(arrs[0].shape, dtype=np.float32))
+    do = to_device(dbits, "bf16")
+    s = 1.0 / math.sqrt(w.head_dim)
+    N = -(-w.seq_len // 64)
+    topk = oracle_topk(w.density, N)
+    st = P.pisa_block_stats(q, k, v)
+    idx, wg = P.pisa_route_topk(q, st, topk, band=w.band)
+    o = P.pisa_attn_fwd(q, k, v, st, idx, wg, band=w.band)
+    dq, dk, dv = P.pisa_attn_bwd(q, k, v, o, do, st, idx, wg, band=w.band)
+    torch.cuda.synchronize()
+    say("[gpu]   backward done")
+    dkf, dvf, dof = dk.float(), dv.float(), do.float()
+    for name, lhs, ref, mag in (("dk", dkf.sum(2), torch.zeros_like(dkf[:, :, 0]), dkf.abs().sum(2)),
+                                ("dv", dvf.sum(2), dof.sum(2), dvf.abs().sum(2))):
+        err = (lhs - ref).abs()
+        assert bool(torch.all(err <= 2.0 ** -7 * mag)), (name, float((err / mag).max()))
+    ih = idx.cpu().numpy()
+    for h in (3, 29):
+        qh, kh, vh = head_f64(arrs, w.dtype, 0, h)
+        doh = I.as_f64(dbits[0, h], "bf16")
+        blocks = [0, int(r.integers(1, N - 1)), int(r.integers(1, N - 1)), N - 1]
+        ref = BO.grads_q_blocks(qh, kh, vh, doh, ih[0, h], blocks, B=64, scale=s, band=w.band)
+        rows = np.concatenate([np.arange(64 * i, min(w.seq_len, 64 * i + 64)) for i in blocks])
+        got = dq[0, h].double().cpu().numpy()[rows]
+        e = np.abs(got - ref).max() / np.abs(ref).max()
+        say(f"[gpu]   head {h} blocks {blocks}: dq normalised error {e:.2e}")
+        assert e <= TOL[("bf16", False)], (h, blocks, e)

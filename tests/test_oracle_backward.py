@@ -81,3 +81,49 @@ def test_one_token_blocks_give_dense_gradients_for_any_routing():
     got = BO.grads(q, k, v, do, idx.astype(np.int32), B=1, scale=s, band=0)
     for g, w in zip(got, dense_grads(q, k, v, do, s)):
         np.testing.assert_allclose(g, w, rtol=0, atol=1e-11)
+
+
+def test_o_used_equal_to_o_changes_nothing():
+    T, B = 200, 32
+    q, k, v, do = rand(T, 8, 21)
+    _, parts = O.pisa_forward_head(q, k, v, B=B, scale=0.4, topk=2, band=1, return_parts=True)
+    o = O.pisa_forward_head(q, k, v, B=B, scale=0.4, topk=2, band=1)
+    a = BO.grads(q, k, v, do, parts["idx"], B=B, scale=0.4, band=1)
+    b = BO.grads(q, k, v, do, parts["idx"], o_used=o, B=B, scale=0.4, band=1)
+    for x, y in zip(a, b):
+        np.testing.assert_allclose(x, y, rtol=0, atol=1e-12)
+
+
+def test_o_used_closed_form_in_softmax_attention():
+    """Every block exact: log den_t = logsumexp_k s q_t.k, so a delta error
+    c_t moves dq_t by -c_t s E_P[k], dk_k by -sum_t c_t s P_tk q_t, and
+    leaves dv unchanged."""
+    T, B, D = 256, 64, 16
+    q, k, v, do = rand(T, D, 22)
+    s = 0.3
+    N = O.num_blocks(T, B)
+    idx = np.array([([j for j in range(N) if abs(i - j) > 1] + [-1] * N)[:N] for i in range(N)], np.int32)
+    o = O.dense_attention(q, k, v, s)
+    o_used = o + 1e-3 * np.random.default_rng(5).standard_normal(o.shape)
+    base = BO.grads(q, k, v, do, idx, B=B, scale=s, band=1)
+    got = BO.grads(q, k, v, do, idx, o_used=o_used, B=B, scale=s, band=1)
+    c = (do * (o_used - o)).sum(1)
+    z = s * q @ k.T
+    Pm = np.exp(z - z.max(1, keepdims=True))
+    Pm /= Pm.sum(1, keepdims=True)
+    np.testing.assert_allclose(got[0] - base[0], -(c[:, None] * s * (Pm @ k)), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(got[1] - base[1], -s * (Pm * c[:, None]).T @ q, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(got[2], base[2], rtol=0, atol=1e-13)
+
+
+def test_dq_of_sampled_blocks_equals_full_gradient():
+    T, B = 300, 32
+    q, k, v, do = rand(T, 8, 23)
+    for so in (False, True):
+        _, parts = O.pisa_forward_head(q, k, v, B=B, scale=0.5, topk=2, band=1, second_order=so,
+                                       return_parts=True)
+        full = BO.grads(q, k, v, do, parts["idx"], B=B, scale=0.5, band=1, second_order=so)[0]
+        blocks = [7, 0, 9]
+        got = BO.grads_q_blocks(q, k, v, do, parts["idx"], blocks, B=B, scale=0.5, band=1, second_order=so)
+        rows = np.concatenate([np.arange(32 * i, min(T, 32 * i + 32)) for i in blocks])
+        np.testing.assert_allclose(got, full[rows], rtol=0, atol=1e-12)

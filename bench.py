@@ -375,7 +375,8 @@ def main():
             "ms": round(bwd_ms, 3), "steps": args.bwd_steps, "algorithmic_tflop": round(bwd_flops / 1e12, 4),
             "roofline": {"bound": "alu", "achieved": round(bwd_tflops, 2), "peak": PEAK_FP32_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(bwd_tflops / PEAK_FP32_TFLOPS, 4), "traffic": None,
-                         "kernel": "pisa_attn_bwd (all its kernels, fp32 VALU)"}}
+                         "kernel": "pisa_attn_bwd (all its kernels: " + ("bf16 MFMA exact pairs, fp32 VALU "
+                                   "virtual tokens and chain)" if w.dtype == "bf16" else "fp32 VALU)")}}
 
     if args.copy_calibration:
         src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)

@@ -34,6 +34,8 @@
 //   kv    - per KV block: dk, dv of the exact pairs plus every chain term.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace pisa {
@@ -98,7 +100,10 @@ __global__ __launch_bounds__(kRowThreads) void bwd_row_kernel(
     const T* __restrict__ dout, const double* __restrict__ kbar, const float* __restrict__ vsum,
     const double* __restrict__ ksig2, const float* __restrict__ hsum, const uint32_t* __restrict__ mask,
     const float* __restrict__ wgate, T* __restrict__ dq, f32x4_t* __restrict__ rowstat, int Tn, int N, int NW,
-    float scale, int second_order, int first_order) {
+    float scale, int second_order, int first_order, const float2* __restrict__ me, float* __restrict__ dq_part) {
+    // me (optional): the exact keys' (max, sum) per row from the matrix-core
+    // kernel; the exact keys are then skipped here, and dq_part (fp32)
+    // receives this kernel's part of dq instead of dq.
     constexpr int C = D / 8;
     constexpr int HD = D / 2;
     constexpr int DPL = D / 64;     // dq2bar dims per lane of a wave
@@ -152,7 +157,12 @@ __global__ __launch_bounds__(kRowThreads) void bwd_row_kernel(
 
     // Pass 1: the forward's normaliser (running max m, sum l, tail mass lt).
     float m = -INFINITY, l = 0.f, lt = 0.f;
-    for (int j = 0; j < N; ++j) {
+    if (me) {
+        const float2 x = active ? me[bh * (int64_t)Tn + t] : make_float2(0.f, 1.f);
+        m = x.x;
+        l = x.y;
+    }
+    for (int j = 0; j < N && !me; ++j) {
         if (!bit_set(sel, j)) continue;
         const int nj = min(kBlock, Tn - j * kBlock);
         for (int h0 = 0; h0 < nj; h0 += kSub) {
@@ -227,7 +237,7 @@ __global__ __launch_bounds__(kRowThreads) void bwd_row_kernel(
     }
 
     // Pass 2: dq' over the exact keys.
-    for (int j = 0; j < N; ++j) {
+    for (int j = 0; j < N && !me; ++j) {
         if (!bit_set(sel, j)) continue;
         const int nj = min(kBlock, Tn - j * kBlock);
         for (int h0 = 0; h0 < nj; h0 += kSub) {
@@ -302,7 +312,8 @@ __global__ __launch_bounds__(kRowThreads) void bwd_row_kernel(
                 const int d = 8 * c + 4 * h + e;
                 float x = scale * dqv[4 * c + e];
                 if (second_order) x = fmaf(scale * qv[4 * c + e] * c2, sdq2[0][d] + sdq2[1][d], x);
-                dq[base + (int64_t)t * D + d] = store_cast<T>(x);
+                if (dq_part) dq_part[base + (int64_t)t * D + d] = x;
+                else dq[base + (int64_t)t * D + d] = store_cast<T>(x);
             }
     }
 }
@@ -488,7 +499,10 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_kernel(
     const double* __restrict__ kbar, const float* __restrict__ vsum, const f32x4_t* __restrict__ rowstat,
     const uint32_t* __restrict__ mask, const float* __restrict__ dH, const float* __restrict__ dkb_v,
     const float* __restrict__ dvh_v, const float* __restrict__ dsg_v, T* __restrict__ dk, T* __restrict__ dv,
-    int Tn, int N, int NW, float scale, int second_order, int first_order) {
+    int Tn, int N, int NW, float scale, int second_order, int first_order, const float* __restrict__ dk_part,
+    const float* __restrict__ dv_part) {
+    // dk_part / dv_part (optional): the exact pairs' dk, dv (fp32) from the
+    // matrix-core kernel; the exact loop is then skipped.
     constexpr int C = D / 16;
     constexpr int Q = D / 4;
     constexpr int LD = D + 4;                  // padded row stride of the chain's staging
@@ -516,11 +530,12 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_kernel(
             const int64_t a = base + (int64_t)row * D + 16 * c + 4 * p + e;
             kk[4 * c + e] = kvalid ? load_f32(k + a) : 0.f;
             vv[4 * c + e] = kvalid ? load_f32(v + a) : 0.f;
-            dkk[4 * c + e] = dvv[4 * c + e] = 0.f;
+            dkk[4 * c + e] = (dk_part && kvalid) ? dk_part[a] : 0.f;
+            dvv[4 * c + e] = (dv_part && kvalid) ? dv_part[a] : 0.f;
         }
 
     // Exact pairs: every query block i whose exact set holds j.
-    for (int i = 0; i < N; ++i) {
+    for (int i = 0; i < N && !dk_part; ++i) {
         if (!bit_set(mask + (bh * N + i) * (int64_t)NW, j)) continue;   // uniform
         const int rows = min(kBlock, Tn - i * kBlock);
         const int64_t src = base + (int64_t)i * kBlock * D;
@@ -640,13 +655,15 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_kernel(
 }
 
 struct BwdLayout {
-    size_t rowstat, mask, dkb, dvh, dsg, dhp, dh, total;
+    size_t rowstat, mask, dkb, dvh, dsg, dhp, dh, me, dqp, dkp, dvp, total;
     int NW, P;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-BwdLayout bwd_layout(const Geom& g) {
+// bf16 inputs add the matrix-core kernels' buffers: per-row exact (max, sum)
+// and fp32 partial dq, dk, dv.
+BwdLayout bwd_layout(const Geom& g, bool mfma) {
     BwdLayout L;
     L.NW = (g.N + 31) / 32;
     L.P = dh_parts(g.T);
@@ -659,6 +676,11 @@ BwdLayout bwd_layout(const Geom& g) {
     L.dsg = o;     o = align256(o + BH * ND * sizeof(float));
     L.dhp = o;     o = align256(o + BH * L.P * DD * sizeof(float));
     L.dh = o;      o = align256(o + BH * DD * sizeof(float));
+    const size_t TD = mfma ? (size_t)g.T * g.D : 0;
+    L.me = o;      o = align256(o + (mfma ? BH * g.T * sizeof(float2) : 0));
+    L.dqp = o;     o = align256(o + BH * TD * sizeof(float));
+    L.dkp = o;     o = align256(o + BH * TD * sizeof(float));
+    L.dvp = o;     o = align256(o + BH * TD * sizeof(float));
     L.total = o;
     return L;
 }
@@ -667,7 +689,8 @@ template <typename T, int D>
 hipError_t run_bwd(const Geom& g, const pisa_params_t* p, const void* q, const void* k, const void* v,
                    const void* o, const void* dout, const pisa_stats_t* st, const int32_t* idx,
                    const float* wgate, void* dq, void* dk, void* dv, void* ws, hipStream_t stream) {
-    const BwdLayout L = bwd_layout(g);
+    constexpr bool kMfma = std::is_same<T, bf16_t>::value;
+    const BwdLayout L = bwd_layout(g, kMfma);
     unsigned char* w = static_cast<unsigned char*>(ws);
     auto* rowstat = reinterpret_cast<f32x4_t*>(w + L.rowstat);
     auto* mask = reinterpret_cast<uint32_t*>(w + L.mask);
@@ -686,10 +709,25 @@ hipError_t run_bwd(const Geom& g, const pisa_params_t* p, const void* q, const v
 
     hipLaunchKernelGGL(bwd_mask_kernel, dim3(g.N, BH), dim3(64), L.NW * sizeof(uint32_t), stream,
                        p->topk > 0 ? idx : nullptr, mask, g.N, L.NW, p->topk, p->band, p->n_sink);
+    float2* me = kMfma ? reinterpret_cast<float2*>(w + L.me) : nullptr;
+    float* dqp = kMfma ? reinterpret_cast<float*>(w + L.dqp) : nullptr;
+    float* dkp = kMfma ? reinterpret_cast<float*>(w + L.dkp) : nullptr;
+    float* dvp = kMfma ? reinterpret_cast<float*>(w + L.dvp) : nullptr;
+    if constexpr (kMfma) {
+        const hipError_t e = launch_bwd_exact_stats(g, tq, tk, mask, me, L.NW, stream);
+        if (e != hipSuccess) return e;
+    }
     hipLaunchKernelGGL((bwd_row_kernel<T, D>), dim3(g.N, BH), dim3(kRowThreads), L.NW * sizeof(uint32_t),
                        stream, tq, tk, tv, to, tg, st->kbar, st->vsum, so ? st->ksig2 : nullptr, st->hsum,
                        mask, so ? wgate : nullptr, static_cast<T*>(dq), rowstat, g.T, g.N, L.NW, g.scale, so,
-                       fo);
+                       fo, me, dqp);
+    if constexpr (kMfma) {
+        hipError_t e = launch_bwd_dq_exact(g, tq, tk, tv, tg, mask, rowstat, dqp, static_cast<bf16_t*>(dq), L.NW,
+                                           stream);
+        if (e == hipSuccess)
+            e = launch_bwd_dkdv_exact(g, tq, tk, tv, tg, mask, rowstat, dkp, dvp, L.NW, stream);
+        if (e != hipSuccess) return e;
+    }
     if (fo) {
         const int rows_per = (g.T + L.P - 1) / L.P;
         hipLaunchKernelGGL((bwd_dh_kernel<T, D>), dim3(L.P, BH), dim3(kThreads), 0, stream, tq, tg, rowstat,
@@ -702,13 +740,13 @@ hipError_t run_bwd(const Geom& g, const pisa_params_t* p, const void* q, const v
                        so ? wgate : nullptr, dkb, dvh, dsg, g.T, g.N, L.NW, g.scale, so);
     hipLaunchKernelGGL((bwd_kv_kernel<T, D>), dim3(g.N, BH), dim3(kThreads), 0, stream, tq, tk, tv, tg,
                        st->kbar, st->vsum, rowstat, mask, dh, dkb, dvh, dsg, static_cast<T*>(dk),
-                       static_cast<T*>(dv), g.T, g.N, L.NW, g.scale, so, fo);
+                       static_cast<T*>(dv), g.T, g.N, L.NW, g.scale, so, fo, dkp, dvp);
     return hipGetLastError();
 }
 
 }  // namespace
 
-size_t attn_bwd_workspace_bytes(const Geom& g) { return bwd_layout(g).total; }
+size_t attn_bwd_workspace_bytes(const Geom& g, int dtype) { return bwd_layout(g, dtype == PISA_BF16).total; }
 
 hipError_t launch_attn_bwd(const Geom& g, int dtype, const pisa_params_t* p, const void* q, const void* k,
                            const void* v, const void* o, const void* dout, const pisa_stats_t* st,

@@ -1,0 +1,481 @@
+// Exact-pair parts of the backward on the matrix cores (bf16 inputs): the
+// block-sparse softmax-attention gradient of the exact branch (PISA §3.2
+// Eqs. 3-4 differentiated; Piecewise-Taylor-Attention README, trainable
+// regime), computed in 64 x 64 (query block, KV block) tiles with bf16 MFMA
+// 32x32x16 and fp32 accumulation.
+//
+//   exact_stats: per query row, max m2 and sum l of 2^(z log2e - m2) over
+//                the exact keys (S^T = K Q^T), merged later with the virtual
+//                tokens into lse;
+//   dq_exact:    dQ^T += K^T dS^T with dS^T = P^T (dP^T - delta),
+//                P^T = exp(S^T - lse), dP^T = V dO^T, added to the partial dq
+//                of the virtual tokens and written in bf16;
+//   dkdv_exact:  S = Q K^T and dP = dO V^T with the keys on the lanes, then
+//                dV^T += dO^T P and dK^T += Q^T dS; fp32 partials for the
+//                chain kernel.
+// A product over queries (or keys) takes its B operand straight from an
+// accumulator (the lane keeps its key, or query; the k-slots hold the
+// accumulator's 8 rows of a 16-row half, 4g + (0..3) and 8 + 4g + (0..3)),
+// and its A operand from the gfx950 LDS transpose read of a row-major tile
+// whose 16-byte chunks are XOR-swizzled by row % 4 (the read then hands
+// every lane the same 8 rows). dS and P are split into bf16 hi + lo parts
+// (two MFMAs each), so the cancelling sums dq = sum dS k, dk = sum dS q and
+// dv = sum P dout keep about 16 bits of every term.
+// Work per workgroup (4 waves): one 64-row block against a stream of 64-row
+// tiles; wave w takes the 32 x 32 sub-tile (w >> 1, w & 1) of each product
+// and the two waves sharing an output tile add their partials at the end.
+#include <math.h>
+
+#include "common.h"
+
+namespace pisa {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+template <int D>
+struct BC {
+    static_assert(2 * (D / 32) * 16 * 64 * 4 == 2 * 64 * 2 * D, "the partial exchange fills the two tiles");
+    static constexpr int KS = D / 16;          // k-steps over the head dim
+    static constexpr int DT = D / 32;          // 32-wide head-dim tiles
+    static constexpr int CH = D / 8;           // 16-byte chunks per row
+    static constexpr int RB = 2 * D;           // row bytes
+    static constexpr int TILE = 64 * RB;       // bytes of one 64-row tile
+    static constexpr int LPT = 64 * CH / kThreads;   // 16-byte loads per thread per tile
+};
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    bf16x2_t r = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ __forceinline__ uint2 lds_tr16(const unsigned char* p) {
+    typedef __attribute__((address_space(3))) v4i16_t lds_v4i16;
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p));
+}
+
+__device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16_t zero16() {
+    f32x16_t z;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) z[e] = 0.f;
+    return z;
+}
+
+// A 64-row tile (rows >= nval zero) from global memory into registers, then
+// into LDS with chunk c of row r at 16-byte position c ^ 2 (r % 4).
+template <int D>
+__device__ __forceinline__ void tile_load(uint4 (&r)[BC<D>::LPT], const bf16_t* src, int nval, int tid) {
+#pragma unroll
+    for (int n = 0; n < BC<D>::LPT; ++n) {
+        const int c = tid + kThreads * n;
+        const int row = c / BC<D>::CH, ch = c % BC<D>::CH;
+        r[n] = row < nval ? *reinterpret_cast<const uint4*>(src + (int64_t)row * D + 8 * ch) : make_uint4(0, 0, 0, 0);
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void tile_store(unsigned char* lds, const uint4 (&r)[BC<D>::LPT], int tid) {
+#pragma unroll
+    for (int n = 0; n < BC<D>::LPT; ++n) {
+        const int c = tid + kThreads * n;
+        const int row = c / BC<D>::CH, ch = c % BC<D>::CH;
+        *reinterpret_cast<uint4*>(lds + row * BC<D>::RB + 16 * (ch ^ (2 * (row & 3)))) = r[n];
+    }
+}
+
+// Row-format operand: row rr of a swizzled tile, head dims 16 ks + 8 g + (0..7).
+template <int D>
+__device__ __forceinline__ bf16x8_t row_op(const unsigned char* lds, int rr, int ks, int g) {
+    return as_bf16x8(*reinterpret_cast<const uint4*>(lds + rr * BC<D>::RB + 16 * ((2 * ks + g) ^ (2 * (rr & 3)))));
+}
+
+// Row-format operand straight from global memory (row t of a [T, D] matrix; zero past T).
+template <int D>
+__device__ __forceinline__ void rows_from_global(uint4 (&r)[BC<D>::KS], const bf16_t* base, int t, int T, int g) {
+#pragma unroll
+    for (int ks = 0; ks < BC<D>::KS; ++ks)
+        r[ks] = t < T ? *reinterpret_cast<const uint4*>(base + (int64_t)t * D + 16 * ks + 8 * g) : make_uint4(0, 0, 0, 0);
+}
+
+// Transposed-read addressing (lane-constant part) of a swizzled tile: the
+// A operand "rows = head dims of tile dt, k = tile rows r0 + 4g + (0..3) and
+// r0 + 8 + 4g + (0..3)".
+struct TrAddr {
+    uint32_t trow;
+    int trG, tra, tre;
+    __device__ TrAddr(int lane, int rb) {
+        const int g = lane >> 5, tri = lane & 15;
+        trG = lane >> 4;
+        tra = tri & 3;
+        tre = tri >> 2;
+        trow = (uint32_t)((4 * g + tre) * rb);
+    }
+    __device__ uint32_t off(int dt) const {
+        const int c8 = (dt * 32 + 16 * (trG & 1) + 4 * tra) >> 2;
+        return (uint32_t)(8 * (c8 ^ (4 * tre)));
+    }
+};
+
+template <int D>
+__device__ __forceinline__ bf16x8_t tr_op(const unsigned char* lds, const TrAddr& ta, int dt, int r0) {
+    const unsigned char* base = lds + ta.trow + ta.off(dt);
+    const uint2 a = lds_tr16(base + r0 * BC<D>::RB);
+    const uint2 b = lds_tr16(base + (r0 + 8) * BC<D>::RB);
+    return as_bf16x8(make_uint4(a.x, a.y, b.x, b.y));
+}
+
+// Registers 8 h .. 8 h + 7 of an accumulator as a bf16 B operand, and the
+// remainder (x - bf16(x)) as a second one.
+__device__ __forceinline__ void split_op(const f32x16_t& x, int h, bf16x8_t& hi, bf16x8_t& lo) {
+    uint32_t wh[4], wl[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const float a = x[8 * h + 2 * p], b = x[8 * h + 2 * p + 1];
+        wh[p] = pack_bf16x2(a, b);
+        wl[p] = pack_bf16x2(a - bf16_lo(wh[p]), b - bf16_hi(wh[p]));
+    }
+    hi = as_bf16x8(make_uint4(wh[0], wh[1], wh[2], wh[3]));
+    lo = as_bf16x8(make_uint4(wl[0], wl[1], wl[2], wl[3]));
+}
+
+// accumulator register r <-> tile row 8 (r / 4) + 4 g + r % 4
+__device__ __forceinline__ int acc_row(int r, int g) { return 8 * (r >> 2) + 4 * g + (r & 3); }
+
+// ---------------------------------------------------------------- exact stats
+template <int D>
+__global__ __launch_bounds__(kThreads) void bwd_exact_stats_kernel(const bf16_t* __restrict__ q,
+                                                                   const bf16_t* __restrict__ k,
+                                                                   const uint32_t* __restrict__ mask,
+                                                                   float2* __restrict__ me, int T, int N, int NW,
+                                                                   float scale) {
+    using C = BC<D>;
+    __shared__ __attribute__((aligned(16))) unsigned char sK[C::TILE];
+    __shared__ float2 sx[2][32];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r32 = lane & 31, g = lane >> 5;
+    const int kt = wave >> 1, qt = wave & 1;
+    const int64_t bh = blockIdx.y;
+    const int i = blockIdx.x;
+    const int t = i * kBlock + qt * 32 + r32;
+    const int64_t base = bh * (int64_t)T * D;
+    const uint32_t* mrow = mask + (bh * N + i) * (int64_t)NW;
+    const float c2 = scale * kLog2e;
+
+    uint4 qreg[C::KS];
+    rows_from_global<D>(qreg, q + base, t, T, g);
+    float m = -INFINITY, l = 0.f;
+    for (int j = 0; j < N; ++j) {
+        if (!((mrow[j >> 5] >> (j & 31)) & 1u)) continue;   // uniform
+        const int nval = min(kBlock, T - j * kBlock);
+        uint4 kr[C::LPT];
+        tile_load<D>(kr, k + base + (int64_t)j * kBlock * D, nval, tid);
+        __syncthreads();
+        tile_store<D>(sK, kr, tid);
+        __syncthreads();
+        f32x16_t s = zero16();
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) s = mfma(row_op<D>(sK, kt * 32 + r32, ks, g), as_bf16x8(qreg[ks]), s);
+        float mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float z = kt * 32 + acc_row(r, g) < nval ? s[r] * c2 : -INFINITY;
+            s[r] = z;
+            mx = fmaxf(mx, z);
+        }
+        if (mx > -INFINITY) {
+            const float mn = fmaxf(m, mx);
+            float a = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) a += exp2f(s[r] - mn);
+            l = l * exp2f(m - mn) + a;
+            m = mn;
+        }
+    }
+    // lanes l and l ^ 32 hold the same query (other keys); then the two key halves
+    {
+        const float mo = __shfl_xor(m, 32), lo = __shfl_xor(l, 32);
+        const float mn = fmaxf(m, mo);
+        if (mn > -INFINITY) {
+            l = l * exp2f(m - mn) + lo * exp2f(mo - mn);
+            m = mn;
+        }
+    }
+    if (kt == 1 && g == 0) sx[qt][r32] = make_float2(m, l);
+    __syncthreads();
+    if (kt == 0 && g == 0 && t < T) {
+        const float2 o = sx[qt][r32];
+        const float mn = fmaxf(m, o.x);
+        float ls = l, ms = m;
+        if (mn > -INFINITY) {
+            ls = l * exp2f(m - mn) + o.y * exp2f(o.x - mn);
+            ms = mn;
+        }
+        me[bh * (int64_t)T + t] = make_float2(ms * kLn2, ls);   // natural-log max, sum of e^{z - m}
+    }
+}
+
+// ---------------------------------------------------------------- dq exact
+template <int D>
+__global__ __launch_bounds__(kThreads) void bwd_dq_exact_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    const bf16_t* __restrict__ dout, const uint32_t* __restrict__ mask, const f32x4_t* __restrict__ rowstat,
+    const float* __restrict__ dq_part, bf16_t* __restrict__ dq, int T, int N, int NW, float scale) {
+    using C = BC<D>;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * C::TILE];   // K, V tiles; then the exchange
+    unsigned char* sK = smem;
+    unsigned char* sV = smem + C::TILE;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r32 = lane & 31, g = lane >> 5;
+    const int kt = wave >> 1, qt = wave & 1;
+    const int64_t bh = blockIdx.y;
+    const int i = blockIdx.x;
+    const int t = i * kBlock + qt * 32 + r32;
+    const int64_t base = bh * (int64_t)T * D;
+    const uint32_t* mrow = mask + (bh * N + i) * (int64_t)NW;
+    const float c2 = scale * kLog2e;
+    const TrAddr ta(lane, C::RB);
+
+    uint4 qreg[C::KS], oreg[C::KS];
+    rows_from_global<D>(qreg, q + base, t, T, g);
+    rows_from_global<D>(oreg, dout + base, t, T, g);
+    float lse2 = INFINITY, delta = 0.f;
+    if (t < T) {
+        const f32x4_t rs = rowstat[bh * (int64_t)T + t];
+        lse2 = rs[0] * kLog2e;
+        delta = rs[1];
+    }
+    f32x16_t acc[C::DT];
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) acc[dt] = zero16();
+
+    for (int j = 0; j < N; ++j) {
+        if (!((mrow[j >> 5] >> (j & 31)) & 1u)) continue;   // uniform
+        const int nval = min(kBlock, T - j * kBlock);
+        uint4 kr[C::LPT], vr[C::LPT];
+        tile_load<D>(kr, k + base + (int64_t)j * kBlock * D, nval, tid);
+        tile_load<D>(vr, v + base + (int64_t)j * kBlock * D, nval, tid);
+        __syncthreads();
+        tile_store<D>(sK, kr, tid);
+        tile_store<D>(sV, vr, tid);
+        __syncthreads();
+        f32x16_t s = zero16(), dp = zero16();
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) {
+            s = mfma(row_op<D>(sK, kt * 32 + r32, ks, g), as_bf16x8(qreg[ks]), s);
+            dp = mfma(row_op<D>(sV, kt * 32 + r32, ks, g), as_bf16x8(oreg[ks]), dp);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float p = kt * 32 + acc_row(r, g) < nval ? exp2f(fmaf(s[r], c2, -lse2)) : 0.f;
+            s[r] = p * (dp[r] - delta);   // dS^T
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            bf16x8_t hi, lo;
+            split_op(s, h, hi, lo);
+            const int r0 = kt * 32 + 16 * h;
+#pragma unroll
+            for (int dt = 0; dt < C::DT; ++dt) {
+                const bf16x8_t a = tr_op<D>(sK, ta, dt, r0);   // K^T: head dims x keys
+                acc[dt] = mfma(a, hi, acc[dt]);
+                acc[dt] = mfma(a, lo, acc[dt]);
+            }
+        }
+    }
+    // the two key halves of each query tile: wave (1, qt) hands its partial to wave (0, qt)
+    __syncthreads();
+    float* xs = reinterpret_cast<float*>(smem);   // [qt][dt][16][64]: 2 * DT * 4 KB = 2 tiles
+    if (kt == 1) {
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) xs[((qt * C::DT + dt) * 16 + r) * 64 + lane] = acc[dt][r];
+    }
+    __syncthreads();
+    if (kt == 0 && t < T) {
+        const float* part = dq_part + base + (int64_t)t * D;
+        bf16_t* out = dq + base + (int64_t)t * D;
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+            for (int run = 0; run < 4; ++run) {
+                const int d0 = dt * 32 + 8 * run + 4 * g;
+                const f32x4_t pv = *reinterpret_cast<const f32x4_t*>(part + d0);
+                uint32_t w[2];
+#pragma unroll
+                for (int e = 0; e < 4; e += 2) {
+                    const int r0 = 4 * run + e;
+                    const float x0 = fmaf(scale, acc[dt][r0] + xs[((qt * C::DT + dt) * 16 + r0) * 64 + lane], pv[e]);
+                    const float x1 = fmaf(scale, acc[dt][r0 + 1] + xs[((qt * C::DT + dt) * 16 + r0 + 1) * 64 + lane],
+                                          pv[e + 1]);
+                    w[e / 2] = (uint32_t)f32_to_bf16(x0) | ((uint32_t)f32_to_bf16(x1) << 16);
+                }
+                *reinterpret_cast<uint2*>(out + d0) = make_uint2(w[0], w[1]);
+            }
+    }
+}
+
+// ---------------------------------------------------------------- dk, dv exact
+template <int D>
+__global__ __launch_bounds__(kThreads) void bwd_dkdv_exact_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    const bf16_t* __restrict__ dout, const uint32_t* __restrict__ mask, const f32x4_t* __restrict__ rowstat,
+    float* __restrict__ dk_part, float* __restrict__ dv_part, int T, int N, int NW, float scale) {
+    using C = BC<D>;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * C::TILE];   // Q, dO tiles; then the exchange
+    __shared__ float slse[64], sdel[64];
+    unsigned char* sQ = smem;
+    unsigned char* sO = smem + C::TILE;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r32 = lane & 31, g = lane >> 5;
+    const int kt = wave >> 1, qt = wave & 1;
+    const int64_t bh = blockIdx.y;
+    const int j = blockIdx.x;
+    const int key = j * kBlock + kt * 32 + r32;
+    const int64_t base = bh * (int64_t)T * D;
+    const float c2 = scale * kLog2e;
+    const TrAddr ta(lane, C::RB);
+
+    uint4 kreg[C::KS], vreg[C::KS];
+    rows_from_global<D>(kreg, k + base, key, T, g);
+    rows_from_global<D>(vreg, v + base, key, T, g);
+    f32x16_t dva[C::DT], dka[C::DT];
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) dva[dt] = dka[dt] = zero16();
+
+    for (int i = 0; i < N; ++i) {
+        if (!((mask[(bh * N + i) * (int64_t)NW + (j >> 5)] >> (j & 31)) & 1u)) continue;   // uniform
+        const int rows = min(kBlock, T - i * kBlock);
+        uint4 qr[C::LPT], orr[C::LPT];
+        tile_load<D>(qr, q + base + (int64_t)i * kBlock * D, rows, tid);
+        tile_load<D>(orr, dout + base + (int64_t)i * kBlock * D, rows, tid);
+        float ls = INFINITY, dl = 0.f;
+        if (tid < rows) {
+            const f32x4_t rs = rowstat[bh * (int64_t)T + (int64_t)i * kBlock + tid];
+            ls = rs[0] * kLog2e;
+            dl = rs[1];
+        }
+        __syncthreads();
+        tile_store<D>(sQ, qr, tid);
+        tile_store<D>(sO, orr, tid);
+        if (tid < 64) {
+            slse[tid] = ls;
+            sdel[tid] = dl;
+        }
+        __syncthreads();
+        f32x16_t s = zero16(), dp = zero16();
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) {
+            s = mfma(row_op<D>(sQ, qt * 32 + r32, ks, g), as_bf16x8(kreg[ks]), s);    // S: queries x keys
+            dp = mfma(row_op<D>(sO, qt * 32 + r32, ks, g), as_bf16x8(vreg[ks]), dp);  // dP
+        }
+        f32x16_t p;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int qq = qt * 32 + acc_row(r, g);
+            p[r] = exp2f(fmaf(s[r], c2, -slse[qq]));       // rows past T: lse = +inf, P = 0
+            s[r] = p[r] * (dp[r] - sdel[qq]);              // dS
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            bf16x8_t phi, plo, hi, lo;
+            split_op(p, h, phi, plo);
+            split_op(s, h, hi, lo);
+            const int r0 = qt * 32 + 16 * h;
+#pragma unroll
+            for (int dt = 0; dt < C::DT; ++dt) {
+                const bf16x8_t ao = tr_op<D>(sO, ta, dt, r0);            // dO^T P
+                dva[dt] = mfma(ao, phi, dva[dt]);
+                dva[dt] = mfma(ao, plo, dva[dt]);
+                const bf16x8_t aq = tr_op<D>(sQ, ta, dt, r0);            // Q^T dS
+                dka[dt] = mfma(aq, hi, dka[dt]);
+                dka[dt] = mfma(aq, lo, dka[dt]);
+            }
+        }
+    }
+    // the two query halves of each key tile: wave (kt, 1) hands its partials to wave (kt, 0)
+    float* xs = reinterpret_cast<float*>(smem);   // [kt][dt][16][64] fp32: 2 * DT * 4 KB = 2 tiles
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+        f32x16_t* a = pass == 0 ? dva : dka;
+        __syncthreads();
+        if (qt == 1) {
+#pragma unroll
+            for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) xs[((kt * C::DT + dt) * 16 + r) * 64 + lane] = a[dt][r];
+        }
+        __syncthreads();
+        if (qt == 0 && key < T) {
+            float* out = (pass == 0 ? dv_part : dk_part) + base + (int64_t)key * D;
+            const float sc = pass == 0 ? 1.f : scale;
+#pragma unroll
+            for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+                for (int run = 0; run < 4; ++run) {
+                    f32x4_t w;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 4 * run + e;
+                        w[e] = sc * (a[dt][r] + xs[((kt * C::DT + dt) * 16 + r) * 64 + lane]);
+                    }
+                    *reinterpret_cast<f32x4_t*>(out + dt * 32 + 8 * run + 4 * g) = w;
+                }
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_bwd_exact_stats(const Geom& g, const bf16_t* q, const bf16_t* k, const uint32_t* mask,
+                                  float2* me, int NW, hipStream_t stream) {
+    const dim3 grid(g.N, (unsigned)g.BH);
+    if (g.D == 128)
+        hipLaunchKernelGGL((bwd_exact_stats_kernel<128>), grid, dim3(kThreads), 0, stream, q, k, mask, me, g.T, g.N,
+                           NW, g.scale);
+    else
+        hipLaunchKernelGGL((bwd_exact_stats_kernel<64>), grid, dim3(kThreads), 0, stream, q, k, mask, me, g.T, g.N,
+                           NW, g.scale);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq_exact(const Geom& g, const bf16_t* q, const bf16_t* k, const bf16_t* v,
+                               const bf16_t* dout, const uint32_t* mask, const f32x4_t* rowstat,
+                               const float* dq_part, bf16_t* dq, int NW, hipStream_t stream) {
+    const dim3 grid(g.N, (unsigned)g.BH);
+    if (g.D == 128)
+        hipLaunchKernelGGL((bwd_dq_exact_kernel<128>), grid, dim3(kThreads), 0, stream, q, k, v, dout, mask, rowstat,
+                           dq_part, dq, g.T, g.N, NW, g.scale);
+    else
+        hipLaunchKernelGGL((bwd_dq_exact_kernel<64>), grid, dim3(kThreads), 0, stream, q, k, v, dout, mask, rowstat,
+                           dq_part, dq, g.T, g.N, NW, g.scale);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkdv_exact(const Geom& g, const bf16_t* q, const bf16_t* k, const bf16_t* v,
+                                 const bf16_t* dout, const uint32_t* mask, const f32x4_t* rowstat, float* dk_part,
+                                 float* dv_part, int NW, hipStream_t stream) {
+    const dim3 grid(g.N, (unsigned)g.BH);
+    if (g.D == 128)
+        hipLaunchKernelGGL((bwd_dkdv_exact_kernel<128>), grid, dim3(kThreads), 0, stream, q, k, v, dout, mask,
+                           rowstat, dk_part, dv_part, g.T, g.N, NW, g.scale);
+    else
+        hipLaunchKernelGGL((bwd_dkdv_exact_kernel<64>), grid, dim3(kThreads), 0, stream, q, k, v, dout, mask,
+                           rowstat, dk_part, dv_part, g.T, g.N, NW, g.scale);
+    return hipGetLastError();
+}
+
+}  // namespace pisa

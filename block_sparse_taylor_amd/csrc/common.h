@@ -84,7 +84,15 @@ hipError_t launch_reorder(const Geom& g, int64_t batch, int64_t heads, int elem_
                           const int32_t* perm, const void* src, void* dst, hipStream_t stream);
 void z_order_host(const int64_t* grid, int ndim, int64_t prefix, int32_t* perm);
 
-size_t attn_bwd_workspace_bytes(const Geom& g);
+size_t attn_bwd_workspace_bytes(const Geom& g, int dtype);
+hipError_t launch_bwd_exact_stats(const Geom& g, const bf16_t* q, const bf16_t* k, const uint32_t* mask,
+                                  float2* me, int NW, hipStream_t stream);
+hipError_t launch_bwd_dq_exact(const Geom& g, const bf16_t* q, const bf16_t* k, const bf16_t* v,
+                               const bf16_t* dout, const uint32_t* mask, const f32x4_t* rowstat,
+                               const float* dq_part, bf16_t* dq, int NW, hipStream_t stream);
+hipError_t launch_bwd_dkdv_exact(const Geom& g, const bf16_t* q, const bf16_t* k, const bf16_t* v,
+                                 const bf16_t* dout, const uint32_t* mask, const f32x4_t* rowstat, float* dk_part,
+                                 float* dv_part, int NW, hipStream_t stream);
 hipError_t launch_attn_bwd(const Geom& g, int dtype, const pisa_params_t* p, const void* q, const void* k,
                            const void* v, const void* o, const void* dout, const pisa_stats_t* st,
                            const int32_t* idx, const float* wgate, void* dq, void* dk, void* dv, void* ws,

@@ -189,7 +189,7 @@ pisa_status_t pisa_attn_fwd_valu(const pisa_shape_t* shape, const pisa_params_t*
 size_t pisa_attn_bwd_workspace_bytes(const pisa_shape_t* shape) {
     Geom g;
     if (check_shape(shape, &g) != PISA_OK) return 0;
-    return attn_bwd_workspace_bytes(g);
+    return attn_bwd_workspace_bytes(g, shape->dtype);
 }
 
 pisa_status_t pisa_attn_bwd(const pisa_shape_t* shape, const pisa_params_t* params, const void* q,
@@ -206,7 +206,7 @@ pisa_status_t pisa_attn_bwd(const pisa_shape_t* shape, const pisa_params_t* para
     if (params->topk > 0) PISA_TRY(check_ptr(idx));
     if (params->second_order) PISA_TRY(check_ptr(wgate));
     if (params->phase_mask != 0) return PISA_ERR_UNSUPPORTED;
-    if (workspace_bytes < attn_bwd_workspace_bytes(g)) return PISA_ERR_WORKSPACE;
+    if (workspace_bytes < attn_bwd_workspace_bytes(g, shape->dtype)) return PISA_ERR_WORKSPACE;
     const void* outs[3] = {dq, dk, dv};
     const void* ins[6] = {q, k, v, o, dout, workspace};
     for (int a = 0; a < 3; ++a) {

@@ -500,7 +500,8 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_kernel(
     const uint32_t* __restrict__ mask, const float* __restrict__ dH, const float* __restrict__ dkb_v,
     const float* __restrict__ dvh_v, const float* __restrict__ dsg_v, T* __restrict__ dk, T* __restrict__ dv,
     int Tn, int N, int NW, float scale, int second_order, int first_order, const float* __restrict__ dk_part,
-    const float* __restrict__ dv_part) {
+    const float* __restrict__ dv_part, int nsplit) {
+    // dkb_v / dvh_v hold nsplit partial sums (consecutive [BH, N, D] arrays), added in order.
     // dk_part / dv_part (optional): the exact pairs' dk, dv (fp32) from the
     // matrix-core kernel; the exact loop is then skipped.
     constexpr int C = D / 16;
@@ -595,9 +596,15 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_kernel(
             const float kc = kvalid ? kk[y] - (float)kbar[jb + d] : 0.f;
             skc[u * LD + d] = kc;
             svr[u * LD + d] = vv[y];
-            dkk[y] += dkb_v[jb + d] * inv_n;
+            const int64_t stride = (int64_t)gridDim.y * N * D;
+            float sk_ = 0.f, sv_ = 0.f;
+            for (int sp = 0; sp < nsplit; ++sp) {
+                sk_ += dkb_v[sp * stride + jb + d];
+                sv_ += dvh_v[sp * stride + jb + d];
+            }
+            dkk[y] += sk_ * inv_n;
             if (second_order) dkk[y] = fmaf(2.f * dsg_v[jb + d] * inv_n, kc, dkk[y]);
-            dvv[y] += dvh_v[jb + d];
+            dvv[y] += sv_;
         }
     for (int d = tid; d < D; d += kThreads) svh[d] = vsum[jb + d];
     if (first_order) {
@@ -655,8 +662,8 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_kernel(
 }
 
 struct BwdLayout {
-    size_t rowstat, mask, dkb, dvh, dsg, dhp, dh, me, dqp, dkp, dvp, total;
-    int NW, P;
+    size_t rowstat, mask, dkb, dvh, dsg, dhp, dh, me, dqp, dkp, dvp, dw, total;
+    int NW, P, S;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -667,12 +674,13 @@ BwdLayout bwd_layout(const Geom& g, bool mfma) {
     BwdLayout L;
     L.NW = (g.N + 31) / 32;
     L.P = dh_parts(g.T);
+    L.S = mfma ? bwd_virt_splits(g) : 1;   // partial sums of dkbar, dV-hat over query ranges
     const size_t BH = (size_t)g.BH, ND = (size_t)g.N * g.D, DD = (size_t)g.D * g.D;
     size_t o = 0;
     L.rowstat = o; o = align256(o + BH * g.T * sizeof(f32x4_t));
     L.mask = o;    o = align256(o + BH * g.N * L.NW * sizeof(uint32_t));
-    L.dkb = o;     o = align256(o + BH * ND * sizeof(float));
-    L.dvh = o;     o = align256(o + BH * ND * sizeof(float));
+    L.dkb = o;     o = align256(o + L.S * BH * ND * sizeof(float));
+    L.dvh = o;     o = align256(o + L.S * BH * ND * sizeof(float));
     L.dsg = o;     o = align256(o + BH * ND * sizeof(float));
     L.dhp = o;     o = align256(o + BH * L.P * DD * sizeof(float));
     L.dh = o;      o = align256(o + BH * DD * sizeof(float));
@@ -681,6 +689,7 @@ BwdLayout bwd_layout(const Geom& g, bool mfma) {
     L.dqp = o;     o = align256(o + BH * TD * sizeof(float));
     L.dkp = o;     o = align256(o + BH * TD * sizeof(float));
     L.dvp = o;     o = align256(o + BH * TD * sizeof(float));
+    L.dw = o;      o = align256(o + (mfma ? BH * g.N * (size_t)g.N * sizeof(float) : 0));
     L.total = o;
     return L;
 }
@@ -735,12 +744,18 @@ hipError_t run_bwd(const Geom& g, const pisa_params_t* p, const void* q, const v
         hipLaunchKernelGGL(bwd_dh_reduce_kernel, dim3((D * D + kThreads - 1) / kThreads, BH), dim3(kThreads),
                            0, stream, dhp, dh, L.P, D * D);
     }
-    hipLaunchKernelGGL((bwd_virt_kernel<T, D>), dim3((g.N + kVirtBlocks - 1) / kVirtBlocks, BH), dim3(64), 0,
-                       stream, tq, tg, st->kbar, st->vsum, so ? st->q2bar : nullptr, rowstat, mask,
-                       so ? wgate : nullptr, dkb, dvh, dsg, g.T, g.N, L.NW, g.scale, so);
+    if constexpr (kMfma) {
+        const hipError_t e = launch_bwd_virt_mfma(g, tq, tg, st, mask, rowstat, so ? wgate : nullptr, dkb, dvh,
+                                                  reinterpret_cast<float*>(w + L.dw), dsg, L.NW, so, stream);
+        if (e != hipSuccess) return e;
+    } else {
+        hipLaunchKernelGGL((bwd_virt_kernel<T, D>), dim3((g.N + kVirtBlocks - 1) / kVirtBlocks, BH), dim3(64), 0,
+                           stream, tq, tg, st->kbar, st->vsum, so ? st->q2bar : nullptr, rowstat, mask,
+                           so ? wgate : nullptr, dkb, dvh, dsg, g.T, g.N, L.NW, g.scale, so);
+    }
     hipLaunchKernelGGL((bwd_kv_kernel<T, D>), dim3(g.N, BH), dim3(kThreads), 0, stream, tq, tk, tv, tg,
                        st->kbar, st->vsum, rowstat, mask, dh, dkb, dvh, dsg, static_cast<T*>(dk),
-                       static_cast<T*>(dv), g.T, g.N, L.NW, g.scale, so, fo, dkp, dvp);
+                       static_cast<T*>(dv), g.T, g.N, L.NW, g.scale, so, fo, dkp, dvp, L.S);
     return hipGetLastError();
 }
 

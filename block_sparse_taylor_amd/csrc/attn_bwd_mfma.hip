@@ -438,7 +438,208 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_exact_kernel(
     }
 }
 
+
+// ---------------------------------------------------------------- virtual tokens
+// One workgroup per (bh, group of 64 KV blocks, query split): the blocks'
+// virtual tokens (key kbar_j, value V-hat_j, both fp32 split into bf16 hi +
+// lo) against the query blocks of the split for which they are virtual.
+//   Lam = Q kbar^T, GV = dO V-hat^T (queries on registers, blocks on lanes),
+//   A = exp(s Lam + w_ij - lse), dlam = A (GV + n_j (beta - delta)),
+//   dkbar^T += Q^T dlam (times s), dV-hat^T += dO^T A,
+//   dW_ij = sum over the query block's rows of dlam (0 for gated pairs).
+template <int D>
+__global__ __launch_bounds__(kThreads) void bwd_virt_mfma_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ dout, const double* __restrict__ kbar,
+    const float* __restrict__ vsum, const uint32_t* __restrict__ mask, const f32x4_t* __restrict__ rowstat,
+    const float* __restrict__ wgate, float* __restrict__ dkb_part, float* __restrict__ dvh_part,
+    float* __restrict__ dw, int T, int N, int NW, float scale, int second_order, int i_per_split) {
+    using C = BC<D>;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * C::TILE];   // Q, dO tiles; then the exchange
+    __shared__ float slse[64], sdel[64], sbet[64];
+    __shared__ float sdw[2][64];
+    unsigned char* sQ = smem;
+    unsigned char* sO = smem + C::TILE;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r32 = lane & 31, g = lane >> 5;
+    const int kt = wave >> 1, qt = wave & 1;
+    const int64_t bh = blockIdx.y;
+    const int j = blockIdx.x * 64 + kt * 32 + r32;
+    const bool jvalid = j < N;
+    const int jc = jvalid ? j : N - 1;
+    const float nj = (float)min(kBlock, T - jc * kBlock);
+    const int64_t base = bh * (int64_t)T * D;
+    const float c2 = scale * kLog2e;
+    const TrAddr ta(lane, C::RB);
+    const int i0 = blockIdx.z * i_per_split, i1 = min(N, i0 + i_per_split);
+
+    // this lane's block as hi + lo bf16 operands (rows of kbar and V-hat, dims 16 ks + 8 g ..)
+    uint4 kh[C::KS], kl[C::KS], vh[C::KS], vl[C::KS];
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+        const int64_t a = (bh * N + jc) * (int64_t)D + 16 * ks + 8 * g;
+        uint32_t w[4][4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float k0 = jvalid ? (float)kbar[a + 2 * e] : 0.f, k1 = jvalid ? (float)kbar[a + 2 * e + 1] : 0.f;
+            const float v0 = jvalid ? vsum[a + 2 * e] : 0.f, v1 = jvalid ? vsum[a + 2 * e + 1] : 0.f;
+            w[0][e] = pack_bf16x2(k0, k1);
+            w[1][e] = pack_bf16x2(k0 - bf16_lo(w[0][e]), k1 - bf16_hi(w[0][e]));
+            w[2][e] = pack_bf16x2(v0, v1);
+            w[3][e] = pack_bf16x2(v0 - bf16_lo(w[2][e]), v1 - bf16_hi(w[2][e]));
+        }
+        kh[ks] = make_uint4(w[0][0], w[0][1], w[0][2], w[0][3]);
+        kl[ks] = make_uint4(w[1][0], w[1][1], w[1][2], w[1][3]);
+        vh[ks] = make_uint4(w[2][0], w[2][1], w[2][2], w[2][3]);
+        vl[ks] = make_uint4(w[3][0], w[3][1], w[3][2], w[3][3]);
+    }
+    f32x16_t dka[C::DT], dva[C::DT];
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) dka[dt] = dva[dt] = zero16();
+
+    for (int i = i0; i < i1; ++i) {
+        const bool use = jvalid && !((mask[(bh * N + i) * (int64_t)NW + (jc >> 5)] >> (jc & 31)) & 1u);
+        if (!__syncthreads_or(use)) {   // every block of the group exact for i: no virtual pair
+            if (second_order && qt == 0 && g == 0 && jvalid) dw[(bh * N + i) * (int64_t)N + j] = 0.f;
+            continue;
+        }
+        const float wg = (second_order && use) ? wgate[(bh * N + i) * (int64_t)N + j] : 0.f;
+        const int rows = min(kBlock, T - i * kBlock);
+        uint4 qr[C::LPT], orr[C::LPT];
+        tile_load<D>(qr, q + base + (int64_t)i * kBlock * D, rows, tid);
+        tile_load<D>(orr, dout + base + (int64_t)i * kBlock * D, rows, tid);
+        float ls = INFINITY, dl = 0.f, bt = 0.f;
+        if (tid < rows) {
+            const f32x4_t rs = rowstat[bh * (int64_t)T + (int64_t)i * kBlock + tid];
+            ls = rs[0] * kLog2e;
+            dl = rs[1];
+            bt = rs[2];
+        }
+        __syncthreads();
+        tile_store<D>(sQ, qr, tid);
+        tile_store<D>(sO, orr, tid);
+        if (tid < 64) {
+            slse[tid] = ls;
+            sdel[tid] = dl;
+            sbet[tid] = bt;
+        }
+        __syncthreads();
+        f32x16_t s = zero16(), gv = zero16();
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) {
+            const bf16x8_t aq = row_op<D>(sQ, qt * 32 + r32, ks, g);
+            const bf16x8_t ao = row_op<D>(sO, qt * 32 + r32, ks, g);
+            s = mfma(aq, as_bf16x8(kh[ks]), s);
+            s = mfma(aq, as_bf16x8(kl[ks]), s);
+            gv = mfma(ao, as_bf16x8(vh[ks]), gv);
+            gv = mfma(ao, as_bf16x8(vl[ks]), gv);
+        }
+        const float bias = wg * kLog2e;
+        f32x16_t a;
+        float dws = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int qq = qt * 32 + acc_row(r, g);
+            a[r] = use ? exp2f(fmaf(s[r], c2, bias - slse[qq])) : 0.f;   // rows past T: lse = +inf
+            s[r] = a[r] * (gv[r] + nj * (sbet[qq] - sdel[qq]));          // dlam
+            dws += s[r];
+        }
+        if (second_order) {   // dW_ij: this lane's 16 rows, the other lane half, the other query half
+            dws += __shfl_xor(dws, 32);
+            if (qt == 1 && g == 0) sdw[kt][r32] = dws;
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            bf16x8_t dh, dlo, ah, alo;
+            split_op(s, h, dh, dlo);
+            split_op(a, h, ah, alo);
+            const int r0 = qt * 32 + 16 * h;
+#pragma unroll
+            for (int dt = 0; dt < C::DT; ++dt) {
+                const bf16x8_t aq = tr_op<D>(sQ, ta, dt, r0);   // Q^T dlam
+                dka[dt] = mfma(aq, dh, dka[dt]);
+                dka[dt] = mfma(aq, dlo, dka[dt]);
+                const bf16x8_t ao = tr_op<D>(sO, ta, dt, r0);   // dO^T A
+                dva[dt] = mfma(ao, ah, dva[dt]);
+                dva[dt] = mfma(ao, alo, dva[dt]);
+            }
+        }
+        if (second_order) {
+            __syncthreads();
+            if (qt == 0 && g == 0 && jvalid)
+                dw[(bh * N + i) * (int64_t)N + j] = wg != 0.f ? dws + sdw[kt][r32] : 0.f;
+        }
+    }
+    // the two query halves of each block tile: wave (kt, 1) hands its partials to wave (kt, 0)
+    float* xs = reinterpret_cast<float*>(smem);
+    const int64_t pbase = ((int64_t)blockIdx.z * gridDim.y + bh) * N * (int64_t)D;
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+        f32x16_t* acc = pass == 0 ? dva : dka;
+        __syncthreads();
+        if (qt == 1) {
+#pragma unroll
+            for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) xs[((kt * C::DT + dt) * 16 + r) * 64 + lane] = acc[dt][r];
+        }
+        __syncthreads();
+        if (qt == 0 && jvalid) {
+            float* out = (pass == 0 ? dvh_part : dkb_part) + pbase + (int64_t)j * D;
+            const float sc = pass == 0 ? 1.f : scale;
+#pragma unroll
+            for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+                for (int run = 0; run < 4; ++run) {
+                    f32x4_t w;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 4 * run + e;
+                        w[e] = sc * (acc[dt][r] + xs[((kt * C::DT + dt) * 16 + r) * 64 + lane]);
+                    }
+                    *reinterpret_cast<f32x4_t*>(out + dt * 32 + 8 * run + 4 * g) = w;
+                }
+        }
+    }
+}
+
+// dsig2_j = 1/2 sum_i dW_ij q2bar_i (dW is 0 for gated and exact pairs).
+__global__ __launch_bounds__(128) void bwd_dsig2_kernel(const float* __restrict__ dw, const double* __restrict__ q2bar,
+                                                        float* __restrict__ dsg, int N, int D) {
+    const int j = blockIdx.x;
+    const int64_t bh = blockIdx.y;
+    for (int d = threadIdx.x; d < D; d += 128) {
+        float acc = 0.f;
+        for (int i = 0; i < N; ++i) acc = fmaf(dw[(bh * N + i) * (int64_t)N + j], (float)q2bar[(bh * N + i) * (int64_t)D + d], acc);
+        dsg[(bh * N + j) * (int64_t)D + d] = 0.5f * acc;
+    }
+}
+
 }  // namespace
+
+int bwd_virt_splits(const Geom& g) {
+    const int64_t groups = (int64_t)((g.N + 63) / 64) * g.BH;
+    int s = (int)((1024 + groups - 1) / groups);
+    return s < 1 ? 1 : (s > 8 ? 8 : (s > g.N ? g.N : s));
+}
+
+hipError_t launch_bwd_virt_mfma(const Geom& g, const bf16_t* q, const bf16_t* dout, const pisa_stats_t* st,
+                                const uint32_t* mask, const f32x4_t* rowstat, const float* wgate, float* dkb_part,
+                                float* dvh_part, float* dw, float* dsg, int NW, int second_order,
+                                hipStream_t stream) {
+    const int S = bwd_virt_splits(g);
+    const int per = (g.N + S - 1) / S;
+    const dim3 grid((g.N + 63) / 64, (unsigned)g.BH, S);
+    if (g.D == 128)
+        hipLaunchKernelGGL((bwd_virt_mfma_kernel<128>), grid, dim3(kThreads), 0, stream, q, dout, st->kbar, st->vsum,
+                           mask, rowstat, wgate, dkb_part, dvh_part, dw, g.T, g.N, NW, g.scale, second_order, per);
+    else
+        hipLaunchKernelGGL((bwd_virt_mfma_kernel<64>), grid, dim3(kThreads), 0, stream, q, dout, st->kbar, st->vsum,
+                           mask, rowstat, wgate, dkb_part, dvh_part, dw, g.T, g.N, NW, g.scale, second_order, per);
+    if (second_order)
+        hipLaunchKernelGGL(bwd_dsig2_kernel, dim3(g.N, (unsigned)g.BH), dim3(128), 0, stream, dw, st->q2bar, dsg,
+                           g.N, g.D);
+    return hipGetLastError();
+}
 
 hipError_t launch_bwd_exact_stats(const Geom& g, const bf16_t* q, const bf16_t* k, const uint32_t* mask,
                                   float2* me, int NW, hipStream_t stream) {

@@ -90,6 +90,11 @@ hipError_t launch_bwd_exact_stats(const Geom& g, const bf16_t* q, const bf16_t* 
 hipError_t launch_bwd_dq_exact(const Geom& g, const bf16_t* q, const bf16_t* k, const bf16_t* v,
                                const bf16_t* dout, const uint32_t* mask, const f32x4_t* rowstat,
                                const float* dq_part, bf16_t* dq, int NW, hipStream_t stream);
+int bwd_virt_splits(const Geom& g);
+hipError_t launch_bwd_virt_mfma(const Geom& g, const bf16_t* q, const bf16_t* dout, const pisa_stats_t* st,
+                                const uint32_t* mask, const f32x4_t* rowstat, const float* wgate, float* dkb_part,
+                                float* dvh_part, float* dw, float* dsg, int NW, int second_order,
+                                hipStream_t stream);
 hipError_t launch_bwd_dkdv_exact(const Geom& g, const bf16_t* q, const bf16_t* k, const bf16_t* v,
                                  const bf16_t* dout, const uint32_t* mask, const f32x4_t* rowstat, float* dk_part,
                                  float* dv_part, int NW, hipStream_t stream);

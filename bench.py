@@ -371,12 +371,14 @@ def main():
         # virtual tokens likewise with kbar and V-hat), plus H g and dH per row
         bwd_flops = 10 * D * (exact_pairs + virt_pairs) + 4 * D * D * B * H * T
         bwd_tflops = bwd_flops / (bwd_ms * 1e-3) / 1e12
+        # bf16: the products run on bf16 MFMA; fp32: on the fp32 vector units
+        bpeak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
         out["pisa_attn_bwd"] = {
             "ms": round(bwd_ms, 3), "steps": args.bwd_steps, "algorithmic_tflop": round(bwd_flops / 1e12, 4),
-            "roofline": {"bound": "alu", "achieved": round(bwd_tflops, 2), "peak": PEAK_FP32_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(bwd_tflops / PEAK_FP32_TFLOPS, 4), "traffic": None,
-                         "kernel": "pisa_attn_bwd (all its kernels: " + ("bf16 MFMA exact pairs, fp32 VALU "
-                                   "virtual tokens and chain)" if w.dtype == "bf16" else "fp32 VALU)")}}
+            "roofline": {"bound": "mfma" if w.dtype == "bf16" else "alu", "achieved": round(bwd_tflops, 2),
+                         "peak": bpeak, "unit": "TFLOP/s", "frac": round(bwd_tflops / bpeak, 4), "traffic": None,
+                         "kernel": "pisa_attn_bwd (all its kernels: " + ("bf16 MFMA products, fp32 VALU "
+                                   "mask, dH and chain)" if w.dtype == "bf16" else "fp32 VALU)")}}
 
     if args.copy_calibration:
         src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)

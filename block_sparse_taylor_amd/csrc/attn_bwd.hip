@@ -100,10 +100,7 @@ __global__ __launch_bounds__(kRowThreads) void bwd_row_kernel(
     const T* __restrict__ dout, const double* __restrict__ kbar, const float* __restrict__ vsum,
     const double* __restrict__ ksig2, const float* __restrict__ hsum, const uint32_t* __restrict__ mask,
     const float* __restrict__ wgate, T* __restrict__ dq, f32x4_t* __restrict__ rowstat, int Tn, int N, int NW,
-    float scale, int second_order, int first_order, const float2* __restrict__ me, float* __restrict__ dq_part) {
-    // me (optional): the exact keys' (max, sum) per row from the matrix-core
-    // kernel; the exact keys are then skipped here, and dq_part (fp32)
-    // receives this kernel's part of dq instead of dq.
+    float scale, int second_order, int first_order) {
     constexpr int C = D / 8;
     constexpr int HD = D / 2;
     constexpr int DPL = D / 64;     // dq2bar dims per lane of a wave
@@ -157,12 +154,7 @@ __global__ __launch_bounds__(kRowThreads) void bwd_row_kernel(
 
     // Pass 1: the forward's normaliser (running max m, sum l, tail mass lt).
     float m = -INFINITY, l = 0.f, lt = 0.f;
-    if (me) {
-        const float2 x = active ? me[bh * (int64_t)Tn + t] : make_float2(0.f, 1.f);
-        m = x.x;
-        l = x.y;
-    }
-    for (int j = 0; j < N && !me; ++j) {
+    for (int j = 0; j < N; ++j) {
         if (!bit_set(sel, j)) continue;
         const int nj = min(kBlock, Tn - j * kBlock);
         for (int h0 = 0; h0 < nj; h0 += kSub) {
@@ -237,7 +229,7 @@ __global__ __launch_bounds__(kRowThreads) void bwd_row_kernel(
     }
 
     // Pass 2: dq' over the exact keys.
-    for (int j = 0; j < N && !me; ++j) {
+    for (int j = 0; j < N; ++j) {
         if (!bit_set(sel, j)) continue;
         const int nj = min(kBlock, Tn - j * kBlock);
         for (int h0 = 0; h0 < nj; h0 += kSub) {
@@ -312,8 +304,7 @@ __global__ __launch_bounds__(kRowThreads) void bwd_row_kernel(
                 const int d = 8 * c + 4 * h + e;
                 float x = scale * dqv[4 * c + e];
                 if (second_order) x = fmaf(scale * qv[4 * c + e] * c2, sdq2[0][d] + sdq2[1][d], x);
-                if (dq_part) dq_part[base + (int64_t)t * D + d] = x;
-                else dq[base + (int64_t)t * D + d] = store_cast<T>(x);
+                dq[base + (int64_t)t * D + d] = store_cast<T>(x);
             }
     }
 }
@@ -662,14 +653,14 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_kernel(
 }
 
 struct BwdLayout {
-    size_t rowstat, mask, dkb, dvh, dsg, dhp, dh, me, dqp, dkp, dvp, dw, total;
+    size_t rowstat, mask, dkb, dvh, dsg, dhp, dh, planes, dq2, dkp, dvp, dw, total;
     int NW, P, S;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// bf16 inputs add the matrix-core kernels' buffers: per-row exact (max, sum)
-// and fp32 partial dq, dk, dv.
+// bf16 inputs add the matrix-core kernels' buffers: bf16 hi + lo planes of
+// kbar, V-hat and H, dq2bar, the exact pairs' fp32 dk and dv, and the dW table.
 BwdLayout bwd_layout(const Geom& g, bool mfma) {
     BwdLayout L;
     L.NW = (g.N + 31) / 32;
@@ -685,8 +676,8 @@ BwdLayout bwd_layout(const Geom& g, bool mfma) {
     L.dhp = o;     o = align256(o + BH * L.P * DD * sizeof(float));
     L.dh = o;      o = align256(o + BH * DD * sizeof(float));
     const size_t TD = mfma ? (size_t)g.T * g.D : 0;
-    L.me = o;      o = align256(o + (mfma ? BH * g.T * sizeof(float2) : 0));
-    L.dqp = o;     o = align256(o + BH * TD * sizeof(float));
+    L.planes = o;  o = align256(o + (mfma ? BH * (4 * ND + 2 * DD) * sizeof(bf16_t) : 0));
+    L.dq2 = o;     o = align256(o + (mfma ? BH * ND * sizeof(float) : 0));
     L.dkp = o;     o = align256(o + BH * TD * sizeof(float));
     L.dvp = o;     o = align256(o + BH * TD * sizeof(float));
     L.dw = o;      o = align256(o + (mfma ? BH * g.N * (size_t)g.N * sizeof(float) : 0));
@@ -718,24 +709,34 @@ hipError_t run_bwd(const Geom& g, const pisa_params_t* p, const void* q, const v
 
     hipLaunchKernelGGL(bwd_mask_kernel, dim3(g.N, BH), dim3(64), L.NW * sizeof(uint32_t), stream,
                        p->topk > 0 ? idx : nullptr, mask, g.N, L.NW, p->topk, p->band, p->n_sink);
-    float2* me = kMfma ? reinterpret_cast<float2*>(w + L.me) : nullptr;
-    float* dqp = kMfma ? reinterpret_cast<float*>(w + L.dqp) : nullptr;
     float* dkp = kMfma ? reinterpret_cast<float*>(w + L.dkp) : nullptr;
     float* dvp = kMfma ? reinterpret_cast<float*>(w + L.dvp) : nullptr;
     if constexpr (kMfma) {
-        const hipError_t e = launch_bwd_exact_stats(g, tq, tk, mask, me, L.NW, stream);
-        if (e != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL((bwd_row_kernel<T, D>), dim3(g.N, BH), dim3(kRowThreads), L.NW * sizeof(uint32_t),
-                       stream, tq, tk, tv, to, tg, st->kbar, st->vsum, so ? st->ksig2 : nullptr, st->hsum,
-                       mask, so ? wgate : nullptr, static_cast<T*>(dq), rowstat, g.T, g.N, L.NW, g.scale, so,
-                       fo, me, dqp);
-    if constexpr (kMfma) {
-        hipError_t e = launch_bwd_dq_exact(g, tq, tk, tv, tg, mask, rowstat, dqp, static_cast<bf16_t*>(dq), L.NW,
-                                           stream);
+        bf16_t* pl = reinterpret_cast<bf16_t*>(w + L.planes);
+        const size_t ND = (size_t)g.BH * g.N * D, DD = (size_t)g.BH * D * D;
+        bf16_t *kbh = pl, *kbl = pl + ND, *vhh = pl + 2 * ND, *vhl = pl + 3 * ND;
+        bf16_t *hh = pl + 4 * ND, *hl = pl + 4 * ND + DD;
+        float* dw = reinterpret_cast<float*>(w + L.dw);
+        const float* wg = so ? wgate : nullptr;
+        hipError_t e = launch_bwd_prep(g, st, kbh, kbl, vhh, vhl, hh, hl, stream);
         if (e == hipSuccess)
-            e = launch_bwd_dkdv_exact(g, tq, tk, tv, tg, mask, rowstat, dkp, dvp, L.NW, stream);
+            e = launch_bwd_rowstats(g, tq, tk, to, tg, kbh, kbl, hh, hl, mask, wg, rowstat, L.NW, so, fo, stream);
+        if (e == hipSuccess)
+            e = launch_bwd_virt_mfma(g, tq, tg, st, mask, rowstat, wg, dkb, dvh, dw, dsg, L.NW, so, stream);
+        if (e == hipSuccess)
+            e = launch_bwd_dq(g, tq, tk, tv, tg, kbh, kbl, vhh, vhl, hh, hl, mask, wg, rowstat, dw,
+                              so ? st->ksig2 : nullptr, reinterpret_cast<float*>(w + L.dq2), static_cast<bf16_t*>(dq),
+                              L.NW, so, fo, stream);
+        if (e == hipSuccess) e = launch_bwd_dkdv_exact(g, tq, tk, tv, tg, mask, rowstat, dkp, dvp, L.NW, stream);
         if (e != hipSuccess) return e;
+    } else {
+        hipLaunchKernelGGL((bwd_row_kernel<T, D>), dim3(g.N, BH), dim3(kRowThreads), L.NW * sizeof(uint32_t),
+                           stream, tq, tk, tv, to, tg, st->kbar, st->vsum, so ? st->ksig2 : nullptr, st->hsum,
+                           mask, so ? wgate : nullptr, static_cast<T*>(dq), rowstat, g.T, g.N, L.NW, g.scale, so,
+                           fo);
+        hipLaunchKernelGGL((bwd_virt_kernel<T, D>), dim3((g.N + kVirtBlocks - 1) / kVirtBlocks, BH), dim3(64), 0,
+                           stream, tq, tg, st->kbar, st->vsum, so ? st->q2bar : nullptr, rowstat, mask,
+                           so ? wgate : nullptr, dkb, dvh, dsg, g.T, g.N, L.NW, g.scale, so);
     }
     if (fo) {
         const int rows_per = (g.T + L.P - 1) / L.P;
@@ -743,15 +744,6 @@ hipError_t run_bwd(const Geom& g, const pisa_params_t* p, const void* q, const v
                            dhp, g.T, rows_per, g.scale);
         hipLaunchKernelGGL(bwd_dh_reduce_kernel, dim3((D * D + kThreads - 1) / kThreads, BH), dim3(kThreads),
                            0, stream, dhp, dh, L.P, D * D);
-    }
-    if constexpr (kMfma) {
-        const hipError_t e = launch_bwd_virt_mfma(g, tq, tg, st, mask, rowstat, so ? wgate : nullptr, dkb, dvh,
-                                                  reinterpret_cast<float*>(w + L.dw), dsg, L.NW, so, stream);
-        if (e != hipSuccess) return e;
-    } else {
-        hipLaunchKernelGGL((bwd_virt_kernel<T, D>), dim3((g.N + kVirtBlocks - 1) / kVirtBlocks, BH), dim3(64), 0,
-                           stream, tq, tg, st->kbar, st->vsum, so ? st->q2bar : nullptr, rowstat, mask,
-                           so ? wgate : nullptr, dkb, dvh, dsg, g.T, g.N, L.NW, g.scale, so);
     }
     hipLaunchKernelGGL((bwd_kv_kernel<T, D>), dim3(g.N, BH), dim3(kThreads), 0, stream, tq, tk, tv, tg,
                        st->kbar, st->vsum, rowstat, mask, dh, dkb, dvh, dsg, static_cast<T*>(dk),

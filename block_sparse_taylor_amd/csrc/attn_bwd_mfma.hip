@@ -154,16 +154,82 @@ __device__ __forceinline__ void split_op(const f32x16_t& x, int h, bf16x8_t& hi,
 // accumulator register r <-> tile row 8 (r / 4) + 4 g + r % 4
 __device__ __forceinline__ int acc_row(int r, int g) { return 8 * (r >> 2) + 4 * g + (r & 3); }
 
-// ---------------------------------------------------------------- exact stats
+// ---------------------------------------------------------------- prep
+// bf16 hi + lo planes (x = hi + lo to ~16 bits) of kbar and V-hat per block
+// (blockIdx.x < N) and of H per head (blockIdx.x == N): operands of the
+// virtual-token and first-order products.
+__device__ __forceinline__ void split_store(float x, bf16_t* hi, bf16_t* lo) {
+    const bf16_t h = f32_to_bf16(x);
+    *hi = h;
+    *lo = f32_to_bf16(x - bf16_to_f32(h));
+}
+
+__global__ __launch_bounds__(kThreads) void bwd_prep_kernel(const double* __restrict__ kbar,
+                                                            const float* __restrict__ vsum,
+                                                            const float* __restrict__ hsum, bf16_t* __restrict__ kbh,
+                                                            bf16_t* __restrict__ kbl, bf16_t* __restrict__ vhh,
+                                                            bf16_t* __restrict__ vhl, bf16_t* __restrict__ hh,
+                                                            bf16_t* __restrict__ hl, int N, int D) {
+    const int64_t bh = blockIdx.y;
+    if ((int)blockIdx.x < N) {
+        const int64_t a0 = (bh * N + blockIdx.x) * (int64_t)D;
+        for (int d = threadIdx.x; d < D; d += kThreads) {
+            split_store((float)kbar[a0 + d], kbh + a0 + d, kbl + a0 + d);
+            split_store(vsum[a0 + d], vhh + a0 + d, vhl + a0 + d);
+        }
+    } else {
+        const int64_t a0 = bh * (int64_t)D * D;
+        for (int e = threadIdx.x; e < D * D; e += kThreads) split_store(hsum[a0 + e], hh + a0 + e, hl + a0 + e);
+    }
+}
+
+// Virtual-token logit bias of block j for query block i (log2 units), or
+// -inf where j is not a virtual token of i (exact, or past N).
+struct VirtRow {
+    const uint32_t* mrow;
+    const float* wrow;
+    int N;
+    float lnlast2;
+    __device__ float bias(int j, bool with_mass) const {
+        if (j >= N || ((mrow[j >> 5] >> (j & 31)) & 1u)) return -INFINITY;
+        float b = wrow ? wrow[j] * kLog2e : 0.f;
+        if (with_mass) b += j == N - 1 ? lnlast2 : 6.0f;   // log2 n_j
+        return b;
+    }
+    __device__ float mass(int j) const { return j == N - 1 ? exp2f(lnlast2) : 64.f; }
+};
+
+// (H g)^T for the head-dim tiles [dt0, dt0 + D / 64): A = H rows (hi + lo), B = dout rows.
 template <int D>
-__global__ __launch_bounds__(kThreads) void bwd_exact_stats_kernel(const bf16_t* __restrict__ q,
-                                                                   const bf16_t* __restrict__ k,
-                                                                   const uint32_t* __restrict__ mask,
-                                                                   float2* __restrict__ me, int T, int N, int NW,
-                                                                   float scale) {
+__device__ __forceinline__ void hg_tiles(f32x16_t (&hg)[D / 64], const bf16_t* hh, const bf16_t* hl,
+                                         const uint4 (&oreg)[D / 16], int dt0, int r32, int g) {
+#pragma unroll
+    for (int x = 0; x < D / 64; ++x) {
+        f32x16_t c = zero16();
+        const int d = (dt0 + x) * 32 + r32;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+            const int64_t o = (int64_t)d * D + 16 * ks + 8 * g;
+            c = mfma(as_bf16x8(*reinterpret_cast<const uint4*>(hh + o)), as_bf16x8(oreg[ks]), c);
+            c = mfma(as_bf16x8(*reinterpret_cast<const uint4*>(hl + o)), as_bf16x8(oreg[ks]), c);
+        }
+        hg[x] = c;
+    }
+}
+
+// ---------------------------------------------------------------- row statistics
+// Per query row: lse over the exact keys and the virtual tokens (mass n_j),
+// delta = dout . o, beta = dout . (q' H) / T and c = l_tail / (T den).
+template <int D>
+__global__ __launch_bounds__(kThreads) void bwd_rowstats_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ o,
+    const bf16_t* __restrict__ dout, const bf16_t* __restrict__ kbh, const bf16_t* __restrict__ kbl,
+    const bf16_t* __restrict__ hh, const bf16_t* __restrict__ hl, const uint32_t* __restrict__ mask,
+    const float* __restrict__ wgate, f32x4_t* __restrict__ rowstat, int T, int N, int NW, float scale,
+    int second_order, int first_order) {
     using C = BC<D>;
     __shared__ __attribute__((aligned(16))) unsigned char sK[C::TILE];
-    __shared__ float2 sx[2][32];
+    __shared__ float sx[2][32][4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r32 = lane & 31, g = lane >> 5;
     const int kt = wave >> 1, qt = wave & 1;
@@ -173,10 +239,26 @@ __global__ __launch_bounds__(kThreads) void bwd_exact_stats_kernel(const bf16_t*
     const int64_t base = bh * (int64_t)T * D;
     const uint32_t* mrow = mask + (bh * N + i) * (int64_t)NW;
     const float c2 = scale * kLog2e;
+    const VirtRow vr{mrow, second_order ? wgate + (bh * N + i) * (int64_t)N : nullptr, N,
+                     log2f((float)(T - (N - 1) * kBlock))};
 
     uint4 qreg[C::KS];
     rows_from_global<D>(qreg, q + base, t, T, g);
-    float m = -INFINITY, l = 0.f;
+    float m = -INFINITY, l = 0.f, lt = 0.f;   // log2-domain max; sums against it
+    auto merge = [&](const f32x16_t& z, bool tail) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, z[r]);
+        if (mx == -INFINITY) return;
+        const float mn = fmaxf(m, mx);
+        float a = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) a += exp2f(z[r] - mn);
+        const float cr = m == -INFINITY ? 0.f : exp2f(m - mn);
+        l = l * cr + a;
+        lt = lt * cr + (tail ? a : 0.f);
+        m = mn;
+    };
     for (int j = 0; j < N; ++j) {
         if (!((mrow[j >> 5] >> (j & 31)) & 1u)) continue;   // uniform
         const int nval = min(kBlock, T - j * kBlock);
@@ -188,53 +270,102 @@ __global__ __launch_bounds__(kThreads) void bwd_exact_stats_kernel(const bf16_t*
         f32x16_t s = zero16();
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) s = mfma(row_op<D>(sK, kt * 32 + r32, ks, g), as_bf16x8(qreg[ks]), s);
-        float mx = -INFINITY;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float z = kt * 32 + acc_row(r, g) < nval ? s[r] * c2 : -INFINITY;
-            s[r] = z;
-            mx = fmaxf(mx, z);
-        }
-        if (mx > -INFINITY) {
-            const float mn = fmaxf(m, mx);
-            float a = 0.f;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) a += exp2f(s[r] - mn);
-            l = l * exp2f(m - mn) + a;
-            m = mn;
-        }
+        for (int r = 0; r < 16; ++r) s[r] = kt * 32 + acc_row(r, g) < nval ? s[r] * c2 : -INFINITY;
+        merge(s, false);
     }
-    // lanes l and l ^ 32 hold the same query (other keys); then the two key halves
-    {
-        const float mo = __shfl_xor(m, 32), lo = __shfl_xor(l, 32);
+    const bf16_t* kbh_h = kbh + bh * (int64_t)N * D;
+    const bf16_t* kbl_h = kbl + bh * (int64_t)N * D;
+    for (int G = 0; G * 64 < N; ++G) {   // virtual tokens, 64 blocks at a time (rows of kbar as A)
+        const int jr = G * 64 + kt * 32 + r32;
+        f32x16_t s = zero16();
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) {
+            const int64_t oo = (int64_t)jr * D + 16 * ks + 8 * g;
+            const uint4 ah = jr < N ? *reinterpret_cast<const uint4*>(kbh_h + oo) : make_uint4(0, 0, 0, 0);
+            const uint4 al = jr < N ? *reinterpret_cast<const uint4*>(kbl_h + oo) : make_uint4(0, 0, 0, 0);
+            s = mfma(as_bf16x8(ah), as_bf16x8(qreg[ks]), s);
+            s = mfma(as_bf16x8(al), as_bf16x8(qreg[ks]), s);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[r] = fmaf(s[r], c2, vr.bias(G * 64 + kt * 32 + acc_row(r, g), true));
+        merge(s, true);
+    }
+    // lanes l and l ^ 32 hold the same query
+    {   // (a state with no finite logit has m = -inf and sums 0)
+        const float mo = __shfl_xor(m, 32), lo_ = __shfl_xor(l, 32), to = __shfl_xor(lt, 32);
         const float mn = fmaxf(m, mo);
-        if (mn > -INFINITY) {
-            l = l * exp2f(m - mn) + lo * exp2f(mo - mn);
-            m = mn;
-        }
+        const float a = m == -INFINITY ? 0.f : exp2f(m - mn), b = mo == -INFINITY ? 0.f : exp2f(mo - mn);
+        l = l * a + lo_ * b;
+        lt = lt * a + to * b;
+        m = mn;
     }
-    if (kt == 1 && g == 0) sx[qt][r32] = make_float2(m, l);
-    __syncthreads();
-    if (kt == 0 && g == 0 && t < T) {
-        const float2 o = sx[qt][r32];
-        const float mn = fmaxf(m, o.x);
-        float ls = l, ms = m;
-        if (mn > -INFINITY) {
-            ls = l * exp2f(m - mn) + o.y * exp2f(o.x - mn);
-            ms = mn;
+    // beta: this wave's head-dim tiles of (H g)^T, dotted with q
+    float bp = 0.f;
+    if (first_order) {
+        uint4 oreg[C::KS];
+        rows_from_global<D>(oreg, dout + base, t, T, g);
+        f32x16_t hg[C::DT / 2];
+        hg_tiles<D>(hg, hh + bh * (int64_t)D * D, hl + bh * (int64_t)D * D, oreg, kt * C::DT / 2, r32, g);
+        if (t < T) {
+#pragma unroll
+            for (int x = 0; x < C::DT / 2; ++x)
+#pragma unroll
+                for (int run = 0; run < 4; ++run) {
+                    const int d0 = (kt * C::DT / 2 + x) * 32 + 8 * run + 4 * g;
+                    const uint2 qq = *reinterpret_cast<const uint2*>(q + base + (int64_t)t * D + d0);
+                    bp += bf16_lo(qq.x) * hg[x][4 * run] + bf16_hi(qq.x) * hg[x][4 * run + 1] +
+                          bf16_lo(qq.y) * hg[x][4 * run + 2] + bf16_hi(qq.y) * hg[x][4 * run + 3];
+                }
         }
-        me[bh * (int64_t)T + t] = make_float2(ms * kLn2, ls);   // natural-log max, sum of e^{z - m}
+        bp += __shfl_xor(bp, 32);
+    }
+    if (kt == 1 && g == 0) {
+        sx[qt][r32][0] = m;
+        sx[qt][r32][1] = l;
+        sx[qt][r32][2] = lt;
+        sx[qt][r32][3] = bp;
+    }
+    __syncthreads();
+    if (kt == 0 && t < T) {
+        // delta = dout . o over this lane's half of the head dims
+        float dl = 0.f;
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c) {
+            const int d0 = (D / 2) * g + 8 * c;
+            const uint4 a = *reinterpret_cast<const uint4*>(dout + base + (int64_t)t * D + d0);
+            const uint4 b = *reinterpret_cast<const uint4*>(o + base + (int64_t)t * D + d0);
+            dl += bf16_lo(a.x) * bf16_lo(b.x) + bf16_hi(a.x) * bf16_hi(b.x) + bf16_lo(a.y) * bf16_lo(b.y) +
+                  bf16_hi(a.y) * bf16_hi(b.y) + bf16_lo(a.z) * bf16_lo(b.z) + bf16_hi(a.z) * bf16_hi(b.z) +
+                  bf16_lo(a.w) * bf16_lo(b.w) + bf16_hi(a.w) * bf16_hi(b.w);
+        }
+        dl += __shfl_xor(dl, 32);
+        if (g == 0) {
+            const float mo = sx[qt][r32][0], lo_ = sx[qt][r32][1], to = sx[qt][r32][2];
+            const float mn = fmaxf(m, mo);   // finite: the query's own block is exact
+            const float a = m == -INFINITY ? 0.f : exp2f(m - mn), b = mo == -INFINITY ? 0.f : exp2f(mo - mn);
+            const float ls = l * a + lo_ * b, ts = lt * a + to * b;
+            const float beta = first_order ? scale * (bp + sx[qt][r32][3]) / (float)T : 0.f;
+            const float cf = first_order ? (ts / ls) / (float)T : 0.f;
+            f32x4_t rs = {(mn + log2f(ls)) * kLn2, dl, beta, cf};
+            rowstat[bh * (int64_t)T + t] = rs;
+        }
     }
 }
 
-// ---------------------------------------------------------------- dq exact
+// ---------------------------------------------------------------- dq
+// dq' = K^T dS^T (exact keys) + kbar^T dlam^T (virtual tokens, kbar hi + lo)
+// + c H g, then dq = s dq' + 2 s^2 q dq2bar_i / n_i (second order).
 template <int D>
-__global__ __launch_bounds__(kThreads) void bwd_dq_exact_kernel(
+__global__ __launch_bounds__(kThreads) void bwd_dq_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
-    const bf16_t* __restrict__ dout, const uint32_t* __restrict__ mask, const f32x4_t* __restrict__ rowstat,
-    const float* __restrict__ dq_part, bf16_t* __restrict__ dq, int T, int N, int NW, float scale) {
+    const bf16_t* __restrict__ dout, const bf16_t* __restrict__ kbh, const bf16_t* __restrict__ kbl,
+    const bf16_t* __restrict__ vhh, const bf16_t* __restrict__ vhl, const bf16_t* __restrict__ hh,
+    const bf16_t* __restrict__ hl, const uint32_t* __restrict__ mask, const float* __restrict__ wgate,
+    const f32x4_t* __restrict__ rowstat, const float* __restrict__ dq2, bf16_t* __restrict__ dq, int T, int N,
+    int NW, float scale, int second_order, int first_order) {
     using C = BC<D>;
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * C::TILE];   // K, V tiles; then the exchange
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * C::TILE];   // K, V (or kbar hi, lo) tiles; exchange
     unsigned char* sK = smem;
     unsigned char* sV = smem + C::TILE;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -247,15 +378,19 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_exact_kernel(
     const uint32_t* mrow = mask + (bh * N + i) * (int64_t)NW;
     const float c2 = scale * kLog2e;
     const TrAddr ta(lane, C::RB);
+    const VirtRow vr{mrow, second_order ? wgate + (bh * N + i) * (int64_t)N : nullptr, N,
+                     log2f((float)(T - (N - 1) * kBlock))};
 
     uint4 qreg[C::KS], oreg[C::KS];
     rows_from_global<D>(qreg, q + base, t, T, g);
     rows_from_global<D>(oreg, dout + base, t, T, g);
-    float lse2 = INFINITY, delta = 0.f;
+    float lse2 = INFINITY, delta = 0.f, beta = 0.f, cf = 0.f;
     if (t < T) {
         const f32x4_t rs = rowstat[bh * (int64_t)T + t];
         lse2 = rs[0] * kLog2e;
         delta = rs[1];
+        beta = rs[2];
+        cf = rs[3];
     }
     f32x16_t acc[C::DT];
 #pragma unroll
@@ -264,12 +399,12 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_exact_kernel(
     for (int j = 0; j < N; ++j) {
         if (!((mrow[j >> 5] >> (j & 31)) & 1u)) continue;   // uniform
         const int nval = min(kBlock, T - j * kBlock);
-        uint4 kr[C::LPT], vr[C::LPT];
+        uint4 kr[C::LPT], vr_[C::LPT];
         tile_load<D>(kr, k + base + (int64_t)j * kBlock * D, nval, tid);
-        tile_load<D>(vr, v + base + (int64_t)j * kBlock * D, nval, tid);
+        tile_load<D>(vr_, v + base + (int64_t)j * kBlock * D, nval, tid);
         __syncthreads();
         tile_store<D>(sK, kr, tid);
-        tile_store<D>(sV, vr, tid);
+        tile_store<D>(sV, vr_, tid);
         __syncthreads();
         f32x16_t s = zero16(), dp = zero16();
 #pragma unroll
@@ -295,6 +430,65 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_exact_kernel(
             }
         }
     }
+    // virtual tokens, 64 blocks at a time: kbar hi / lo tiles in LDS
+    const bf16_t* kbh_h = kbh + bh * (int64_t)N * D;
+    const bf16_t* kbl_h = kbl + bh * (int64_t)N * D;
+    const bf16_t* vhh_h = vhh + bh * (int64_t)N * D;
+    const bf16_t* vhl_h = vhl + bh * (int64_t)N * D;
+    for (int G = 0; G * 64 < N; ++G) {
+        const int nb = min(64, N - G * 64);
+        uint4 kr[C::LPT], kl[C::LPT];
+        tile_load<D>(kr, kbh_h + (int64_t)G * 64 * D, nb, tid);
+        tile_load<D>(kl, kbl_h + (int64_t)G * 64 * D, nb, tid);
+        __syncthreads();
+        tile_store<D>(sK, kr, tid);
+        tile_store<D>(sV, kl, tid);
+        __syncthreads();
+        const int jr = G * 64 + kt * 32 + r32;
+        f32x16_t s = zero16(), gv = zero16();
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) {
+            const bf16x8_t ah = row_op<D>(sK, kt * 32 + r32, ks, g), al = row_op<D>(sV, kt * 32 + r32, ks, g);
+            s = mfma(ah, as_bf16x8(qreg[ks]), s);
+            s = mfma(al, as_bf16x8(qreg[ks]), s);
+            const int64_t oo = (int64_t)jr * D + 16 * ks + 8 * g;
+            const uint4 vh = jr < N ? *reinterpret_cast<const uint4*>(vhh_h + oo) : make_uint4(0, 0, 0, 0);
+            const uint4 vl = jr < N ? *reinterpret_cast<const uint4*>(vhl_h + oo) : make_uint4(0, 0, 0, 0);
+            gv = mfma(as_bf16x8(vh), as_bf16x8(oreg[ks]), gv);
+            gv = mfma(as_bf16x8(vl), as_bf16x8(oreg[ks]), gv);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int j = G * 64 + kt * 32 + acc_row(r, g);
+            const float b = vr.bias(j, false);
+            const float a = b == -INFINITY ? 0.f : exp2f(fmaf(s[r], c2, b - lse2));
+            s[r] = a * (gv[r] + vr.mass(j < N ? j : 0) * (beta - delta));   // dlam^T
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            bf16x8_t dh, dlo;
+            split_op(s, h, dh, dlo);
+            const int r0 = kt * 32 + 16 * h;
+#pragma unroll
+            for (int dt = 0; dt < C::DT; ++dt) {
+                const bf16x8_t ah = tr_op<D>(sK, ta, dt, r0), al = tr_op<D>(sV, ta, dt, r0);   // kbar^T
+                acc[dt] = mfma(ah, dh, acc[dt]);
+                acc[dt] = mfma(ah, dlo, acc[dt]);
+                acc[dt] = mfma(al, dh, acc[dt]);
+            }
+        }
+    }
+    // c H g on this wave's head-dim tiles
+    if (first_order) {
+        f32x16_t hg[C::DT / 2];
+        hg_tiles<D>(hg, hh + bh * (int64_t)D * D, hl + bh * (int64_t)D * D, oreg, kt * C::DT / 2, r32, g);
+        // tile dt belongs to wave kt = dt / (DT / 2): compile-time indices, a runtime select
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt)
+            if (dt / (C::DT / 2) == kt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[dt][r] = fmaf(cf, hg[dt % (C::DT / 2)][r], acc[dt][r]);
+    }
     // the two key halves of each query tile: wave (1, qt) hands its partial to wave (0, qt)
     __syncthreads();
     float* xs = reinterpret_cast<float*>(smem);   // [qt][dt][16][64]: 2 * DT * 4 KB = 2 tiles
@@ -306,25 +500,46 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_exact_kernel(
     }
     __syncthreads();
     if (kt == 0 && t < T) {
-        const float* part = dq_part + base + (int64_t)t * D;
+        const int rows = min(kBlock, T - i * kBlock);
+        const float c2o = second_order ? 2.f * scale * scale / (float)rows : 0.f;
+        const float* q2 = second_order ? dq2 + (bh * N + i) * (int64_t)D : nullptr;
         bf16_t* out = dq + base + (int64_t)t * D;
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
             for (int run = 0; run < 4; ++run) {
                 const int d0 = dt * 32 + 8 * run + 4 * g;
-                const f32x4_t pv = *reinterpret_cast<const f32x4_t*>(part + d0);
-                uint32_t w[2];
+                float x[4];
 #pragma unroll
-                for (int e = 0; e < 4; e += 2) {
-                    const int r0 = 4 * run + e;
-                    const float x0 = fmaf(scale, acc[dt][r0] + xs[((qt * C::DT + dt) * 16 + r0) * 64 + lane], pv[e]);
-                    const float x1 = fmaf(scale, acc[dt][r0 + 1] + xs[((qt * C::DT + dt) * 16 + r0 + 1) * 64 + lane],
-                                          pv[e + 1]);
-                    w[e / 2] = (uint32_t)f32_to_bf16(x0) | ((uint32_t)f32_to_bf16(x1) << 16);
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * run + e;
+                    x[e] = scale * (acc[dt][r] + xs[((qt * C::DT + dt) * 16 + r) * 64 + lane]);
                 }
-                *reinterpret_cast<uint2*>(out + d0) = make_uint2(w[0], w[1]);
+                if (second_order) {
+                    const uint2 qq = *reinterpret_cast<const uint2*>(q + base + (int64_t)t * D + d0);
+                    const f32x4_t w = *reinterpret_cast<const f32x4_t*>(q2 + d0);
+                    x[0] = fmaf(c2o * bf16_lo(qq.x), w[0], x[0]);
+                    x[1] = fmaf(c2o * bf16_hi(qq.x), w[1], x[1]);
+                    x[2] = fmaf(c2o * bf16_lo(qq.y), w[2], x[2]);
+                    x[3] = fmaf(c2o * bf16_hi(qq.y), w[3], x[3]);
+                }
+                const uint32_t w0 = (uint32_t)f32_to_bf16(x[0]) | ((uint32_t)f32_to_bf16(x[1]) << 16);
+                const uint32_t w1 = (uint32_t)f32_to_bf16(x[2]) | ((uint32_t)f32_to_bf16(x[3]) << 16);
+                *reinterpret_cast<uint2*>(out + d0) = make_uint2(w0, w1);
             }
+    }
+}
+
+// dq2bar_i = 1/2 sum_j dW_ij sig2_j (dW is 0 for gated and exact pairs).
+__global__ __launch_bounds__(128) void bwd_dq2_kernel(const float* __restrict__ dw, const double* __restrict__ ksig2,
+                                                      float* __restrict__ dq2, int N, int D) {
+    const int i = blockIdx.x;
+    const int64_t bh = blockIdx.y;
+    const float* row = dw + (bh * N + i) * (int64_t)N;
+    for (int d = threadIdx.x; d < D; d += 128) {
+        float acc = 0.f;
+        for (int j = 0; j < N; ++j) acc = fmaf(row[j], (float)ksig2[(bh * N + j) * (int64_t)D + d], acc);
+        dq2[(bh * N + i) * (int64_t)D + d] = 0.5f * acc;
     }
 }
 
@@ -641,28 +856,41 @@ hipError_t launch_bwd_virt_mfma(const Geom& g, const bf16_t* q, const bf16_t* do
     return hipGetLastError();
 }
 
-hipError_t launch_bwd_exact_stats(const Geom& g, const bf16_t* q, const bf16_t* k, const uint32_t* mask,
-                                  float2* me, int NW, hipStream_t stream) {
-    const dim3 grid(g.N, (unsigned)g.BH);
-    if (g.D == 128)
-        hipLaunchKernelGGL((bwd_exact_stats_kernel<128>), grid, dim3(kThreads), 0, stream, q, k, mask, me, g.T, g.N,
-                           NW, g.scale);
-    else
-        hipLaunchKernelGGL((bwd_exact_stats_kernel<64>), grid, dim3(kThreads), 0, stream, q, k, mask, me, g.T, g.N,
-                           NW, g.scale);
+hipError_t launch_bwd_prep(const Geom& g, const pisa_stats_t* st, bf16_t* kbh, bf16_t* kbl, bf16_t* vhh,
+                           bf16_t* vhl, bf16_t* hh, bf16_t* hl, hipStream_t stream) {
+    hipLaunchKernelGGL(bwd_prep_kernel, dim3(g.N + 1, (unsigned)g.BH), dim3(kThreads), 0, stream, st->kbar, st->vsum,
+                       st->hsum, kbh, kbl, vhh, vhl, hh, hl, g.N, g.D);
     return hipGetLastError();
 }
 
-hipError_t launch_bwd_dq_exact(const Geom& g, const bf16_t* q, const bf16_t* k, const bf16_t* v,
-                               const bf16_t* dout, const uint32_t* mask, const f32x4_t* rowstat,
-                               const float* dq_part, bf16_t* dq, int NW, hipStream_t stream) {
+hipError_t launch_bwd_rowstats(const Geom& g, const bf16_t* q, const bf16_t* k, const bf16_t* o, const bf16_t* dout,
+                               const bf16_t* kbh, const bf16_t* kbl, const bf16_t* hh, const bf16_t* hl,
+                               const uint32_t* mask, const float* wgate, f32x4_t* rowstat, int NW, int second_order,
+                               int first_order, hipStream_t stream) {
     const dim3 grid(g.N, (unsigned)g.BH);
-    if (g.D == 128)
-        hipLaunchKernelGGL((bwd_dq_exact_kernel<128>), grid, dim3(kThreads), 0, stream, q, k, v, dout, mask, rowstat,
-                           dq_part, dq, g.T, g.N, NW, g.scale);
-    else
-        hipLaunchKernelGGL((bwd_dq_exact_kernel<64>), grid, dim3(kThreads), 0, stream, q, k, v, dout, mask, rowstat,
-                           dq_part, dq, g.T, g.N, NW, g.scale);
+#define PISA_ROWSTATS(DD)                                                                                      \
+    hipLaunchKernelGGL((bwd_rowstats_kernel<DD>), grid, dim3(kThreads), 0, stream, q, k, o, dout, kbh, kbl, hh, \
+                       hl, mask, wgate, rowstat, g.T, g.N, NW, g.scale, second_order, first_order)
+    if (g.D == 128) PISA_ROWSTATS(128);
+    else PISA_ROWSTATS(64);
+#undef PISA_ROWSTATS
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq(const Geom& g, const bf16_t* q, const bf16_t* k, const bf16_t* v, const bf16_t* dout,
+                         const bf16_t* kbh, const bf16_t* kbl, const bf16_t* vhh, const bf16_t* vhl,
+                         const bf16_t* hh, const bf16_t* hl, const uint32_t* mask, const float* wgate,
+                         const f32x4_t* rowstat, const float* dw, const double* ksig2, float* dq2, bf16_t* dq, int NW,
+                         int second_order, int first_order, hipStream_t stream) {
+    const dim3 grid(g.N, (unsigned)g.BH);
+    if (second_order)
+        hipLaunchKernelGGL(bwd_dq2_kernel, grid, dim3(128), 0, stream, dw, ksig2, dq2, g.N, g.D);
+#define PISA_DQ(DD)                                                                                            \
+    hipLaunchKernelGGL((bwd_dq_kernel<DD>), grid, dim3(kThreads), 0, stream, q, k, v, dout, kbh, kbl, vhh, vhl, \
+                       hh, hl, mask, wgate, rowstat, dq2, dq, g.T, g.N, NW, g.scale, second_order, first_order)
+    if (g.D == 128) PISA_DQ(128);
+    else PISA_DQ(64);
+#undef PISA_DQ
     return hipGetLastError();
 }
 

@@ -85,11 +85,17 @@ hipError_t launch_reorder(const Geom& g, int64_t batch, int64_t heads, int elem_
 void z_order_host(const int64_t* grid, int ndim, int64_t prefix, int32_t* perm);
 
 size_t attn_bwd_workspace_bytes(const Geom& g, int dtype);
-hipError_t launch_bwd_exact_stats(const Geom& g, const bf16_t* q, const bf16_t* k, const uint32_t* mask,
-                                  float2* me, int NW, hipStream_t stream);
-hipError_t launch_bwd_dq_exact(const Geom& g, const bf16_t* q, const bf16_t* k, const bf16_t* v,
-                               const bf16_t* dout, const uint32_t* mask, const f32x4_t* rowstat,
-                               const float* dq_part, bf16_t* dq, int NW, hipStream_t stream);
+hipError_t launch_bwd_prep(const Geom& g, const pisa_stats_t* st, bf16_t* kbh, bf16_t* kbl, bf16_t* vhh,
+                           bf16_t* vhl, bf16_t* hh, bf16_t* hl, hipStream_t stream);
+hipError_t launch_bwd_rowstats(const Geom& g, const bf16_t* q, const bf16_t* k, const bf16_t* o, const bf16_t* dout,
+                               const bf16_t* kbh, const bf16_t* kbl, const bf16_t* hh, const bf16_t* hl,
+                               const uint32_t* mask, const float* wgate, f32x4_t* rowstat, int NW, int second_order,
+                               int first_order, hipStream_t stream);
+hipError_t launch_bwd_dq(const Geom& g, const bf16_t* q, const bf16_t* k, const bf16_t* v, const bf16_t* dout,
+                         const bf16_t* kbh, const bf16_t* kbl, const bf16_t* vhh, const bf16_t* vhl,
+                         const bf16_t* hh, const bf16_t* hl, const uint32_t* mask, const float* wgate,
+                         const f32x4_t* rowstat, const float* dw, const double* ksig2, float* dq2, bf16_t* dq, int NW,
+                         int second_order, int first_order, hipStream_t stream);
 int bwd_virt_splits(const Geom& g);
 hipError_t launch_bwd_virt_mfma(const Geom& g, const bf16_t* q, const bf16_t* dout, const pisa_stats_t* st,
                                 const uint32_t* mask, const f32x4_t* rowstat, const float* wgate, float* dkb_part,

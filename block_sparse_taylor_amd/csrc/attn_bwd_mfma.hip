@@ -396,16 +396,29 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) acc[dt] = zero16();
 
-    for (int j = 0; j < N; ++j) {
-        if (!((mrow[j >> 5] >> (j & 31)) & 1u)) continue;   // uniform
+    // exact KV blocks, one step ahead: the next block's K, V rows are loaded
+    // into registers during this step's products
+    auto next_j = [&](int from) {
+        for (int x = from; x < N; ++x)
+            if ((mrow[x >> 5] >> (x & 31)) & 1u) return x;   // uniform
+        return N;
+    };
+    uint4 kr[C::LPT], vr_[C::LPT];
+    auto fetch = [&](int x) {
+        const int nv = min(kBlock, T - x * kBlock);
+        tile_load<D>(kr, k + base + (int64_t)x * kBlock * D, nv, tid);
+        tile_load<D>(vr_, v + base + (int64_t)x * kBlock * D, nv, tid);
+    };
+    int j = next_j(0);
+    if (j < N) fetch(j);
+    while (j < N) {
         const int nval = min(kBlock, T - j * kBlock);
-        uint4 kr[C::LPT], vr_[C::LPT];
-        tile_load<D>(kr, k + base + (int64_t)j * kBlock * D, nval, tid);
-        tile_load<D>(vr_, v + base + (int64_t)j * kBlock * D, nval, tid);
         __syncthreads();
         tile_store<D>(sK, kr, tid);
         tile_store<D>(sV, vr_, tid);
         __syncthreads();
+        const int jnext = next_j(j + 1);
+        if (jnext < N) fetch(jnext);
         f32x16_t s = zero16(), dp = zero16();
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
@@ -429,6 +442,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(
                 acc[dt] = mfma(a, lo, acc[dt]);
             }
         }
+        j = jnext;
     }
     // virtual tokens, 64 blocks at a time: kbar hi / lo tiles in LDS
     const bf16_t* kbh_h = kbh + bh * (int64_t)N * D;
@@ -437,7 +451,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(
     const bf16_t* vhl_h = vhl + bh * (int64_t)N * D;
     for (int G = 0; G * 64 < N; ++G) {
         const int nb = min(64, N - G * 64);
-        uint4 kr[C::LPT], kl[C::LPT];
+        uint4 kl[C::LPT];
         tile_load<D>(kr, kbh_h + (int64_t)G * 64 * D, nb, tid);
         tile_load<D>(kl, kbl_h + (int64_t)G * 64 * D, nb, tid);
         __syncthreads();
@@ -571,18 +585,31 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_exact_kernel(
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) dva[dt] = dka[dt] = zero16();
 
-    for (int i = 0; i < N; ++i) {
-        if (!((mask[(bh * N + i) * (int64_t)NW + (j >> 5)] >> (j & 31)) & 1u)) continue;   // uniform
-        const int rows = min(kBlock, T - i * kBlock);
-        uint4 qr[C::LPT], orr[C::LPT];
-        tile_load<D>(qr, q + base + (int64_t)i * kBlock * D, rows, tid);
-        tile_load<D>(orr, dout + base + (int64_t)i * kBlock * D, rows, tid);
-        float ls = INFINITY, dl = 0.f;
+    // query blocks whose exact set holds j, one step ahead: the next block's
+    // Q, dO rows and row statistics are loaded into registers during this
+    // step's products
+    auto next_i = [&](int from) {
+        for (int x = from; x < N; ++x)
+            if ((mask[(bh * N + x) * (int64_t)NW + (j >> 5)] >> (j & 31)) & 1u) return x;   // uniform
+        return N;
+    };
+    uint4 qr[C::LPT], orr[C::LPT];
+    float ls = INFINITY, dl = 0.f;
+    auto fetch = [&](int x) {
+        const int rows = min(kBlock, T - x * kBlock);
+        tile_load<D>(qr, q + base + (int64_t)x * kBlock * D, rows, tid);
+        tile_load<D>(orr, dout + base + (int64_t)x * kBlock * D, rows, tid);
+        ls = INFINITY;
+        dl = 0.f;
         if (tid < rows) {
-            const f32x4_t rs = rowstat[bh * (int64_t)T + (int64_t)i * kBlock + tid];
+            const f32x4_t rs = rowstat[bh * (int64_t)T + (int64_t)x * kBlock + tid];
             ls = rs[0] * kLog2e;
             dl = rs[1];
         }
+    };
+    int i = next_i(0);
+    if (i < N) fetch(i);
+    while (i < N) {
         __syncthreads();
         tile_store<D>(sQ, qr, tid);
         tile_store<D>(sO, orr, tid);
@@ -591,6 +618,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_exact_kernel(
             sdel[tid] = dl;
         }
         __syncthreads();
+        const int inext = next_i(i + 1);
+        if (inext < N) fetch(inext);
         f32x16_t s = zero16(), dp = zero16();
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
@@ -620,6 +649,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_exact_kernel(
                 dka[dt] = mfma(aq, lo, dka[dt]);
             }
         }
+        i = inext;
     }
     // the two query halves of each key tile: wave (kt, 1) hands its partials to wave (kt, 0)
     float* xs = reinterpret_cast<float*>(smem);   // [kt][dt][16][64] fp32: 2 * DT * 4 KB = 2 tiles

@@ -2,8 +2,10 @@
 // with the routing table and the second-order gate held constant
 // (Piecewise-Taylor-Attention README: the trainable regime, a backward pass
 // through both branches with the selection detached; PISA §3.2 Eqs. 3-5 and
-// §3.3 Eqs. 9-10 for the forward it differentiates). fp32 arithmetic for
-// either input dtype; results in the input dtype.
+// §3.3 Eqs. 9-10 for the forward it differentiates). This file holds the
+// fp32-input kernels (VALU, fp32 arithmetic) and the mask, dH and chain
+// kernels both dtypes share; bf16 inputs run every product on the matrix
+// cores (attn_bwd_mfma.hip). Results in the input dtype.
 //
 // Per query row t of block i, with q' = s q_t, g = dout_t, den_t the
 // normaliser, lse_t = log den_t, l_t the tail mass and T the sequence length:
@@ -28,10 +30,11 @@
 //
 // Kernels (all deterministic: fixed loop orders, no floating-point atomics):
 //   mask  - bit j of row i set iff block j is exact for query block i,
-//   row   - per query block: lse, delta, beta, c (rowstat) and dq,
+//   row   - per query block: lse, delta, beta, c (rowstat) and dq (fp32),
 //   dh    - partial sums of dH over row chunks, then their fixed-order sum,
-//   virt  - per group of 16 KV blocks: dkbar (virtual part), dV-hat, dsig2,
-//   kv    - per KV block: dk, dv of the exact pairs plus every chain term.
+//   virt  - per group of 16 KV blocks: dkbar (virtual part), dV-hat, dsig2 (fp32),
+//   kv    - per KV block: dk, dv of the exact pairs (fp32; for bf16 they come
+//           from the matrix-core kernel) plus every chain term.
 #include <math.h>
 
 #include <type_traits>

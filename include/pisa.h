@@ -289,9 +289,12 @@ pisa_status_t pisa_reorder_scatter(const pisa_shape_t *shape, const int32_t *per
  *                     statistics, the selection bitmask, per-block partial
  *                     gradients, dH); contents on entry are ignored and on
  *                     return unspecified.
- * params->phase_mask must be 0 (PISA_ERR_UNSUPPORTED otherwise). All
- * arithmetic is fp32 (bf16 inputs widened exactly); each gradient is rounded
- * once to the output dtype. Deterministic: no floating-point atomics.
+ * params->phase_mask must be 0 (PISA_ERR_UNSUPPORTED otherwise). fp32 inputs:
+ * fp32 arithmetic. bf16 inputs: every product on bf16 matrix cores with fp32
+ * accumulation; the intermediate weights (P, dS and the virtual tokens'
+ * A, dlam) and the fp32 statistics (kbar, V-hat, H) enter as bf16 hi + lo
+ * pairs (about 16 significant bits). Each gradient is rounded once to the
+ * output dtype. Deterministic: no floating-point atomics.
  */
 size_t pisa_attn_bwd_workspace_bytes(const pisa_shape_t *shape);
 pisa_status_t pisa_attn_bwd(const pisa_shape_t *shape, const pisa_params_t *params,

@@ -224,3 +224,27 @@ def test_full_size_wan14():
         e = np.abs(got - ref).max() / np.abs(ref).max()
         say(f"[gpu]   head {h} blocks {blocks}: dq normalised error {e:.2e}")
         assert e <= TOL[("bf16", False)], (h, blocks, e)
+
+
+def test_bf16_single_block_of_twenty_rows_contract():
+    """One partial block of 20 rows: the exact keys all sit in the first
+    32-key half of the tile (the other half of the kernels' waves sees none)."""
+    check(wl("tiny", seq_len=20, head_dim=128, heads=2, dtype="bf16"), seed=14, topk=0, contract=True)
+
+
+def test_bf16_last_block_partial_band0_contract():
+    """band 0, no routing: the last query block (25 rows) has only its own
+    partial block exact; every other block is a virtual token."""
+    check(wl("tiny", seq_len=64 * 6 + 25, head_dim=64, heads=2, dtype="bf16"), seed=15, topk=0, band=0,
+          so=True, contract=True)
+
+
+def test_bf16_d64_second_order_sinks_contract():
+    w = wl("flux", heads=2, grid=(30, 32), seq_len=1472, text_tokens=512, head_dim=64)
+    check(w, seed=16, topk=2, n_sink=3, so=True, contract=True)
+
+
+def test_bf16_many_groups_contract():
+    """N = 131 blocks: three groups of 64 virtual tokens, the last holding 3."""
+    check(wl("tiny", seq_len=64 * 130 + 7, head_dim=128, heads=1, dtype="bf16"), seed=17, topk=5, so=True,
+          n_sink=1, contract=True)

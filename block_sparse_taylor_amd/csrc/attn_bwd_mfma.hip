@@ -46,6 +46,7 @@ struct BC {
     static constexpr int RB = 2 * D;           // row bytes
     static constexpr int TILE = 64 * RB;       // bytes of one 64-row tile
     static constexpr int LPT = 64 * CH / kThreads;   // 16-byte loads per thread per tile
+    static constexpr int SWM = CH / 2 - 1;           // swizzle: chunk c of row r sits at c ^ 2 (r & SWM)
 };
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
@@ -63,6 +64,10 @@ __device__ __forceinline__ uint2 lds_tr16(const unsigned char* p) {
     return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p));
 }
 
+// 2^x by the hardware instruction (no denormal handling: every argument here
+// is a logit minus the row's log-normaliser, so <= ~0, or -inf).
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -75,7 +80,9 @@ __device__ __forceinline__ f32x16_t zero16() {
 }
 
 // A 64-row tile (rows >= nval zero) from global memory into registers, then
-// into LDS with chunk c of row r at 16-byte position c ^ 2 (r % 4).
+// into LDS with chunk c of row r at 16-byte position c ^ 2 (r & SWM): eight
+// consecutive rows (D = 128; four for D = 64) put a chunk in distinct banks,
+// so the row-format reads of 8 lanes do not collide.
 template <int D>
 __device__ __forceinline__ void tile_load(uint4 (&r)[BC<D>::LPT], const bf16_t* src, int nval, int tid) {
 #pragma unroll
@@ -92,14 +99,14 @@ __device__ __forceinline__ void tile_store(unsigned char* lds, const uint4 (&r)[
     for (int n = 0; n < BC<D>::LPT; ++n) {
         const int c = tid + kThreads * n;
         const int row = c / BC<D>::CH, ch = c % BC<D>::CH;
-        *reinterpret_cast<uint4*>(lds + row * BC<D>::RB + 16 * (ch ^ (2 * (row & 3)))) = r[n];
+        *reinterpret_cast<uint4*>(lds + row * BC<D>::RB + 16 * (ch ^ (2 * (row & BC<D>::SWM)))) = r[n];
     }
 }
 
 // Row-format operand: row rr of a swizzled tile, head dims 16 ks + 8 g + (0..7).
 template <int D>
 __device__ __forceinline__ bf16x8_t row_op(const unsigned char* lds, int rr, int ks, int g) {
-    return as_bf16x8(*reinterpret_cast<const uint4*>(lds + rr * BC<D>::RB + 16 * ((2 * ks + g) ^ (2 * (rr & 3)))));
+    return as_bf16x8(*reinterpret_cast<const uint4*>(lds + rr * BC<D>::RB + 16 * ((2 * ks + g) ^ (2 * (rr & BC<D>::SWM)))));
 }
 
 // Row-format operand straight from global memory (row t of a [T, D] matrix; zero past T).
@@ -112,20 +119,22 @@ __device__ __forceinline__ void rows_from_global(uint4 (&r)[BC<D>::KS], const bf
 
 // Transposed-read addressing (lane-constant part) of a swizzled tile: the
 // A operand "rows = head dims of tile dt, k = tile rows r0 + 4g + (0..3) and
-// r0 + 8 + 4g + (0..3)".
+// r0 + 8 + 4g + (0..3)". A lane reads row R = r0 (+ 8) + 4g + tre with r0 a
+// multiple of 8, so R & SWM = (4g + tre) & SWM does not depend on r0.
 struct TrAddr {
     uint32_t trow;
-    int trG, tra, tre;
-    __device__ TrAddr(int lane, int rb) {
+    int trG, tra, sw;
+    __device__ TrAddr(int lane, int rb, int swm) {
         const int g = lane >> 5, tri = lane & 15;
+        const int tre = tri >> 2;
         trG = lane >> 4;
         tra = tri & 3;
-        tre = tri >> 2;
+        sw = (4 * g + tre) & swm;
         trow = (uint32_t)((4 * g + tre) * rb);
     }
     __device__ uint32_t off(int dt) const {
-        const int c8 = (dt * 32 + 16 * (trG & 1) + 4 * tra) >> 2;
-        return (uint32_t)(8 * (c8 ^ (4 * tre)));
+        const int c8 = (dt * 32 + 16 * (trG & 1) + 4 * tra) >> 2;   // 8-byte unit
+        return (uint32_t)(8 * (c8 ^ (4 * sw)));
     }
 };
 
@@ -196,7 +205,7 @@ struct VirtRow {
         if (with_mass) b += j == N - 1 ? lnlast2 : 6.0f;   // log2 n_j
         return b;
     }
-    __device__ float mass(int j) const { return j == N - 1 ? exp2f(lnlast2) : 64.f; }
+    __device__ float mass(int j) const { return j == N - 1 ? fexp2(lnlast2) : 64.f; }
 };
 
 // (H g)^T for the head-dim tiles [dt0, dt0 + D / 64): A = H rows (hi + lo), B = dout rows.
@@ -253,8 +262,8 @@ __global__ __launch_bounds__(kThreads) void bwd_rowstats_kernel(
         const float mn = fmaxf(m, mx);
         float a = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) a += exp2f(z[r] - mn);
-        const float cr = m == -INFINITY ? 0.f : exp2f(m - mn);
+        for (int r = 0; r < 16; ++r) a += fexp2(z[r] - mn);
+        const float cr = m == -INFINITY ? 0.f : fexp2(m - mn);
         l = l * cr + a;
         lt = lt * cr + (tail ? a : 0.f);
         m = mn;
@@ -295,7 +304,7 @@ __global__ __launch_bounds__(kThreads) void bwd_rowstats_kernel(
     {   // (a state with no finite logit has m = -inf and sums 0)
         const float mo = __shfl_xor(m, 32), lo_ = __shfl_xor(l, 32), to = __shfl_xor(lt, 32);
         const float mn = fmaxf(m, mo);
-        const float a = m == -INFINITY ? 0.f : exp2f(m - mn), b = mo == -INFINITY ? 0.f : exp2f(mo - mn);
+        const float a = m == -INFINITY ? 0.f : fexp2(m - mn), b = mo == -INFINITY ? 0.f : fexp2(mo - mn);
         l = l * a + lo_ * b;
         lt = lt * a + to * b;
         m = mn;
@@ -343,7 +352,7 @@ __global__ __launch_bounds__(kThreads) void bwd_rowstats_kernel(
         if (g == 0) {
             const float mo = sx[qt][r32][0], lo_ = sx[qt][r32][1], to = sx[qt][r32][2];
             const float mn = fmaxf(m, mo);   // finite: the query's own block is exact
-            const float a = m == -INFINITY ? 0.f : exp2f(m - mn), b = mo == -INFINITY ? 0.f : exp2f(mo - mn);
+            const float a = m == -INFINITY ? 0.f : fexp2(m - mn), b = mo == -INFINITY ? 0.f : fexp2(mo - mn);
             const float ls = l * a + lo_ * b, ts = lt * a + to * b;
             const float beta = first_order ? scale * (bp + sx[qt][r32][3]) / (float)T : 0.f;
             const float cf = first_order ? (ts / ls) / (float)T : 0.f;
@@ -377,7 +386,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(
     const int64_t base = bh * (int64_t)T * D;
     const uint32_t* mrow = mask + (bh * N + i) * (int64_t)NW;
     const float c2 = scale * kLog2e;
-    const TrAddr ta(lane, C::RB);
+    const TrAddr ta(lane, C::RB, C::SWM);
     const VirtRow vr{mrow, second_order ? wgate + (bh * N + i) * (int64_t)N : nullptr, N,
                      log2f((float)(T - (N - 1) * kBlock))};
 
@@ -427,7 +436,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const float p = kt * 32 + acc_row(r, g) < nval ? exp2f(fmaf(s[r], c2, -lse2)) : 0.f;
+            const float p = kt * 32 + acc_row(r, g) < nval ? fexp2(fmaf(s[r], c2, -lse2)) : 0.f;
             s[r] = p * (dp[r] - delta);   // dS^T
         }
 #pragma unroll
@@ -475,7 +484,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(
         for (int r = 0; r < 16; ++r) {
             const int j = G * 64 + kt * 32 + acc_row(r, g);
             const float b = vr.bias(j, false);
-            const float a = b == -INFINITY ? 0.f : exp2f(fmaf(s[r], c2, b - lse2));
+            const float a = b == -INFINITY ? 0.f : fexp2(fmaf(s[r], c2, b - lse2));
             s[r] = a * (gv[r] + vr.mass(j < N ? j : 0) * (beta - delta));   // dlam^T
         }
 #pragma unroll
@@ -576,7 +585,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_exact_kernel(
     const int key = j * kBlock + kt * 32 + r32;
     const int64_t base = bh * (int64_t)T * D;
     const float c2 = scale * kLog2e;
-    const TrAddr ta(lane, C::RB);
+    const TrAddr ta(lane, C::RB, C::SWM);
 
     uint4 kreg[C::KS], vreg[C::KS];
     rows_from_global<D>(kreg, k + base, key, T, g);
@@ -630,7 +639,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_exact_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int qq = qt * 32 + acc_row(r, g);
-            p[r] = exp2f(fmaf(s[r], c2, -slse[qq]));       // rows past T: lse = +inf, P = 0
+            p[r] = fexp2(fmaf(s[r], c2, -slse[qq]));       // rows past T: lse = +inf, P = 0
             s[r] = p[r] * (dp[r] - sdel[qq]);              // dS
         }
 #pragma unroll
@@ -714,7 +723,7 @@ __global__ __launch_bounds__(kThreads) void bwd_virt_mfma_kernel(
     const float nj = (float)min(kBlock, T - jc * kBlock);
     const int64_t base = bh * (int64_t)T * D;
     const float c2 = scale * kLog2e;
-    const TrAddr ta(lane, C::RB);
+    const TrAddr ta(lane, C::RB, C::SWM);
     const int i0 = blockIdx.z * i_per_split, i1 = min(N, i0 + i_per_split);
 
     // this lane's block as hi + lo bf16 operands (rows of kbar and V-hat, dims 16 ks + 8 g ..)
@@ -784,7 +793,7 @@ __global__ __launch_bounds__(kThreads) void bwd_virt_mfma_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int qq = qt * 32 + acc_row(r, g);
-            a[r] = use ? exp2f(fmaf(s[r], c2, bias - slse[qq])) : 0.f;   // rows past T: lse = +inf
+            a[r] = use ? fexp2(fmaf(s[r], c2, bias - slse[qq])) : 0.f;   // rows past T: lse = +inf
             s[r] = a[r] * (gv[r] + nj * (sbet[qq] - sdel[qq]));          // dlam
             dws += s[r];
         }

@@ -504,6 +504,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_kernel(
     __shared__ __attribute__((aligned(16))) float pool[2 * kKvRows * LD];
     __shared__ __attribute__((aligned(16))) float sH[16 * LD];
     __shared__ __attribute__((aligned(16))) float svh[D];
+    __shared__ float sblk[3 * D];
     __shared__ f32x4_t srs[kKvRows];
     float* sA = pool;                           // main loop: q' rows (stride D)
     float* sB = pool + kKvRows * D;             //            g rows  (stride D)
@@ -581,6 +582,18 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_kernel(
     float* skc = pool;                  // (k - kbar_j) rows, stride LD
     float* svr = pool + kKvRows * LD;   // v rows, stride LD
     __syncthreads();
+    // the block's dkbar, dV-hat (summed over the partials, in order) and dsig2, once
+    for (int d = tid; d < D; d += kThreads) {
+        const int64_t stride = (int64_t)gridDim.y * N * D;
+        float sk_ = 0.f, sv_ = 0.f;
+        for (int sp = 0; sp < nsplit; ++sp) {
+            sk_ += dkb_v[sp * stride + jb + d];
+            sv_ += dvh_v[sp * stride + jb + d];
+        }
+        sblk[d] = sk_;
+        sblk[D + d] = sv_;
+        sblk[2 * D + d] = second_order ? dsg_v[jb + d] : 0.f;
+    }
 #pragma unroll
     for (int c = 0; c < C; ++c)
 #pragma unroll
@@ -590,15 +603,17 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_kernel(
             const float kc = kvalid ? kk[y] - (float)kbar[jb + d] : 0.f;
             skc[u * LD + d] = kc;
             svr[u * LD + d] = vv[y];
-            const int64_t stride = (int64_t)gridDim.y * N * D;
-            float sk_ = 0.f, sv_ = 0.f;
-            for (int sp = 0; sp < nsplit; ++sp) {
-                sk_ += dkb_v[sp * stride + jb + d];
-                sv_ += dvh_v[sp * stride + jb + d];
-            }
-            dkk[y] += sk_ * inv_n;
-            if (second_order) dkk[y] = fmaf(2.f * dsg_v[jb + d] * inv_n, kc, dkk[y]);
-            dvv[y] += sv_;
+        }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int d = 16 * c + 4 * p + e;
+            const int y = 4 * c + e;
+            dkk[y] += sblk[d] * inv_n;
+            if (second_order) dkk[y] = fmaf(2.f * sblk[2 * D + d] * inv_n, skc[u * LD + d], dkk[y]);
+            dvv[y] += sblk[D + d];
         }
     for (int d = tid; d < D; d += kThreads) svh[d] = vsum[jb + d];
     if (first_order) {

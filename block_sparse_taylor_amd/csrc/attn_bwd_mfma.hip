@@ -239,6 +239,7 @@ __global__ __launch_bounds__(kThreads) void bwd_rowstats_kernel(
     using C = BC<D>;
     __shared__ __attribute__((aligned(16))) unsigned char sK[C::TILE];
     __shared__ float sx[2][32][4];
+    __shared__ __attribute__((aligned(16))) float sbias[64];   // a group's virtual-token biases (log2)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r32 = lane & 31, g = lane >> 5;
     const int kt = wave >> 1, qt = wave & 1;
@@ -286,6 +287,9 @@ __global__ __launch_bounds__(kThreads) void bwd_rowstats_kernel(
     const bf16_t* kbh_h = kbh + bh * (int64_t)N * D;
     const bf16_t* kbl_h = kbl + bh * (int64_t)N * D;
     for (int G = 0; G * 64 < N; ++G) {   // virtual tokens, 64 blocks at a time (rows of kbar as A)
+        __syncthreads();                  // the previous group's biases have been read
+        if (tid < 64) sbias[tid] = vr.bias(G * 64 + tid, true);
+        __syncthreads();
         const int jr = G * 64 + kt * 32 + r32;
         f32x16_t s = zero16();
 #pragma unroll
@@ -297,7 +301,11 @@ __global__ __launch_bounds__(kThreads) void bwd_rowstats_kernel(
             s = mfma(as_bf16x8(al), as_bf16x8(qreg[ks]), s);
         }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[r] = fmaf(s[r], c2, vr.bias(G * 64 + kt * 32 + acc_row(r, g), true));
+        for (int run = 0; run < 4; ++run) {   // the biases of rows 8 run + 4 g + (0..3)
+            const f32x4_t b = *reinterpret_cast<const f32x4_t*>(sbias + kt * 32 + 8 * run + 4 * g);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s[4 * run + e] = fmaf(s[4 * run + e], c2, b[e]);
+        }
         merge(s, true);
     }
     // lanes l and l ^ 32 hold the same query
@@ -375,6 +383,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(
     int NW, float scale, int second_order, int first_order) {
     using C = BC<D>;
     __shared__ __attribute__((aligned(16))) unsigned char smem[2 * C::TILE];   // K, V (or kbar hi, lo) tiles; exchange
+    __shared__ __attribute__((aligned(16))) float sbias[64], smass[64];      // a virtual group's biases, n_j
     unsigned char* sK = smem;
     unsigned char* sV = smem + C::TILE;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -466,6 +475,11 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(
         __syncthreads();
         tile_store<D>(sK, kr, tid);
         tile_store<D>(sV, kl, tid);
+        if (tid < 64) {
+            const int jj = G * 64 + tid;
+            sbias[tid] = vr.bias(jj, false);
+            smass[tid] = jj < N ? vr.mass(jj) : 0.f;
+        }
         __syncthreads();
         const int jr = G * 64 + kt * 32 + r32;
         f32x16_t s = zero16(), gv = zero16();
@@ -481,11 +495,15 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(
             gv = mfma(as_bf16x8(vl), as_bf16x8(oreg[ks]), gv);
         }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int j = G * 64 + kt * 32 + acc_row(r, g);
-            const float b = vr.bias(j, false);
-            const float a = b == -INFINITY ? 0.f : fexp2(fmaf(s[r], c2, b - lse2));
-            s[r] = a * (gv[r] + vr.mass(j < N ? j : 0) * (beta - delta));   // dlam^T
+        for (int run = 0; run < 4; ++run) {   // blocks 8 run + 4 g + (0..3) of the key half kt
+            const f32x4_t b = *reinterpret_cast<const f32x4_t*>(sbias + kt * 32 + 8 * run + 4 * g);
+            const f32x4_t nm = *reinterpret_cast<const f32x4_t*>(smass + kt * 32 + 8 * run + 4 * g);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * run + e;
+                const float a = b[e] == -INFINITY ? 0.f : fexp2(fmaf(s[r], c2, b[e] - lse2));
+                s[r] = a * (gv[r] + nm[e] * (beta - delta));   // dlam^T
+            }
         }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {

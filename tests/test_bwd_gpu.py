@@ -182,19 +182,23 @@ def test_deterministic():
         assert torch.equal(x, y)
 
 
-def test_full_size_wan14():
-    """The bench's workload in its launch configuration (all 40 heads of the
-    Wan2.1-14B shape, T = 32760, one call). Checked: dq of sampled query blocks
-    of two heads against the oracle one block at a time (end-to-end bf16 bar),
-    and two invariances that hold at any size: shifting every key by one
-    vector shifts all logits of a row equally (H and the key variance do not
-    change), so sum_k dk = 0; shifting every value by one vector shifts every
-    output by it (H does not change since sum (k - kbar) = 0 per block), so
-    sum_k dv = sum_t dout_t. Both sums are compared within 2^-7 of sum |.|
-    (bf16 rounding of each term, 2^-9, with fp32 accumulation)."""
+@pytest.mark.parametrize("name,heads", [("wan14", (3, 29)), ("hunyuan", (5, 17))])
+def test_full_size(name, heads):
+    """A workload of the bench in its launch configuration (every head, one
+    call: the Wan2.1-14B shape, T = 32760; the Hunyuan shape, T = 118800 with
+    the second order). Checked: dq of sampled query blocks of two heads
+    against the oracle one block at a time (end-to-end bf16 bar), and two
+    invariances that hold at any size: shifting every key by one vector
+    shifts all logits of a row equally (H, the key variance and the pooled q^2
+    do not change), so sum_k dk = 0; shifting every value by one vector shifts
+    every output by it (H does not change since sum (k - kbar) = 0 per
+    block), so sum_k dv = sum_t dout_t. Both sums are compared within 2^-7 of
+    sum |.| (bf16 rounding of each term, 2^-9, with fp32 accumulation)."""
     from gpu_common import head_f64, oracle_topk, workload_inputs
-    w, arrs = workload_inputs("wan14")
-    say(f"[gpu] bwd full size: {w.batch}x{w.heads}x{w.seq_len}x{w.head_dim} {w.dtype}")
+    say(f"[gpu] bwd full size {name}: inputs")
+    w, arrs = workload_inputs(name)
+    so = w.second_order
+    say(f"[gpu] bwd full size {name}: {w.batch}x{w.heads}x{w.seq_len}x{w.head_dim} {w.dtype} second_order={so}")
     q, k, v = (to_device(a, w.dtype) for a in arrs)
     r = np.random.default_rng(13)
     dbits = I.bf16_bits(r.standard_normal(arrs[0].shape, dtype=np.float32))
@@ -202,23 +206,24 @@ def test_full_size_wan14():
     s = 1.0 / math.sqrt(w.head_dim)
     N = -(-w.seq_len // 64)
     topk = oracle_topk(w.density, N)
-    st = P.pisa_block_stats(q, k, v)
-    idx, wg = P.pisa_route_topk(q, st, topk, band=w.band)
-    o = P.pisa_attn_fwd(q, k, v, st, idx, wg, band=w.band)
-    dq, dk, dv = P.pisa_attn_bwd(q, k, v, o, do, st, idx, wg, band=w.band)
+    st = P.pisa_block_stats(q, k, v, second_order=so)
+    idx, wg = P.pisa_route_topk(q, st, topk, band=w.band, second_order=so)
+    o = P.pisa_attn_fwd(q, k, v, st, idx, wg, band=w.band, second_order=so)
+    dq, dk, dv = P.pisa_attn_bwd(q, k, v, o, do, st, idx, wg, band=w.band, second_order=so)
     torch.cuda.synchronize()
     say("[gpu]   backward done")
     dkf, dvf, dof = dk.float(), dv.float(), do.float()
-    for name, lhs, ref, mag in (("dk", dkf.sum(2), torch.zeros_like(dkf[:, :, 0]), dkf.abs().sum(2)),
-                                ("dv", dvf.sum(2), dof.sum(2), dvf.abs().sum(2))):
+    for nm, lhs, ref, mag in (("dk", dkf.sum(2), torch.zeros_like(dkf[:, :, 0]), dkf.abs().sum(2)),
+                              ("dv", dvf.sum(2), dof.sum(2), dvf.abs().sum(2))):
         err = (lhs - ref).abs()
-        assert bool(torch.all(err <= 2.0 ** -7 * mag)), (name, float((err / mag).max()))
+        assert bool(torch.all(err <= 2.0 ** -7 * mag)), (nm, float((err / mag).max()))
+    del dkf, dvf, dof
     ih = idx.cpu().numpy()
-    for h in (3, 29):
+    for h in heads:
         qh, kh, vh = head_f64(arrs, w.dtype, 0, h)
         doh = I.as_f64(dbits[0, h], "bf16")
         blocks = [0, int(r.integers(1, N - 1)), int(r.integers(1, N - 1)), N - 1]
-        ref = BO.grads_q_blocks(qh, kh, vh, doh, ih[0, h], blocks, B=64, scale=s, band=w.band)
+        ref = BO.grads_q_blocks(qh, kh, vh, doh, ih[0, h], blocks, B=64, scale=s, band=w.band, second_order=so)
         rows = np.concatenate([np.arange(64 * i, min(w.seq_len, 64 * i + 64)) for i in blocks])
         got = dq[0, h].double().cpu().numpy()[rows]
         e = np.abs(got - ref).max() / np.abs(ref).max()

@@ -585,16 +585,22 @@ __global__ __launch_bounds__(128) void bwd_dq2_kernel(const float* __restrict__ 
 }
 
 // ---------------------------------------------------------------- dk, dv exact
+// K and V of the block sit in LDS (read as B operands each step) rather than
+// in registers, so that a wave fits in 256 registers and two waves share a
+// SIMD: one wave's LDS waits overlap the other's products.
 template <int D>
-__global__ __launch_bounds__(kThreads) void bwd_dkdv_exact_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dkdv_exact_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const bf16_t* __restrict__ dout, const uint32_t* __restrict__ mask, const f32x4_t* __restrict__ rowstat,
     float* __restrict__ dk_part, float* __restrict__ dv_part, int T, int N, int NW, float scale) {
     using C = BC<D>;
     __shared__ __attribute__((aligned(16))) unsigned char smem[2 * C::TILE];   // Q, dO tiles; then the exchange
+    __shared__ __attribute__((aligned(16))) unsigned char skv[2 * C::TILE];    // K, V of the block
     __shared__ float slse[64], sdel[64];
     unsigned char* sQ = smem;
     unsigned char* sO = smem + C::TILE;
+    unsigned char* sKt = skv;
+    unsigned char* sVt = skv + C::TILE;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r32 = lane & 31, g = lane >> 5;
     const int kt = wave >> 1, qt = wave & 1;
@@ -605,38 +611,31 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_exact_kernel(
     const float c2 = scale * kLog2e;
     const TrAddr ta(lane, C::RB, C::SWM);
 
-    uint4 kreg[C::KS], vreg[C::KS];
-    rows_from_global<D>(kreg, k + base, key, T, g);
-    rows_from_global<D>(vreg, v + base, key, T, g);
+    {
+        const int nval = min(kBlock, T - j * kBlock);
+        uint4 kr[C::LPT], vr_[C::LPT];
+        tile_load<D>(kr, k + base + (int64_t)j * kBlock * D, nval, tid);
+        tile_load<D>(vr_, v + base + (int64_t)j * kBlock * D, nval, tid);
+        tile_store<D>(sKt, kr, tid);
+        tile_store<D>(sVt, vr_, tid);
+    }
     f32x16_t dva[C::DT], dka[C::DT];
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) dva[dt] = dka[dt] = zero16();
 
-    // query blocks whose exact set holds j, one step ahead: the next block's
-    // Q, dO rows and row statistics are loaded into registers during this
-    // step's products
-    auto next_i = [&](int from) {
-        for (int x = from; x < N; ++x)
-            if ((mask[(bh * N + x) * (int64_t)NW + (j >> 5)] >> (j & 31)) & 1u) return x;   // uniform
-        return N;
-    };
-    uint4 qr[C::LPT], orr[C::LPT];
-    float ls = INFINITY, dl = 0.f;
-    auto fetch = [&](int x) {
-        const int rows = min(kBlock, T - x * kBlock);
-        tile_load<D>(qr, q + base + (int64_t)x * kBlock * D, rows, tid);
-        tile_load<D>(orr, dout + base + (int64_t)x * kBlock * D, rows, tid);
-        ls = INFINITY;
-        dl = 0.f;
+    // query blocks whose exact set holds j
+    for (int i = 0; i < N; ++i) {
+        if (!((mask[(bh * N + i) * (int64_t)NW + (j >> 5)] >> (j & 31)) & 1u)) continue;   // uniform
+        const int rows = min(kBlock, T - i * kBlock);
+        uint4 qr[C::LPT], orr[C::LPT];
+        tile_load<D>(qr, q + base + (int64_t)i * kBlock * D, rows, tid);
+        tile_load<D>(orr, dout + base + (int64_t)i * kBlock * D, rows, tid);
+        float ls = INFINITY, dl = 0.f;
         if (tid < rows) {
-            const f32x4_t rs = rowstat[bh * (int64_t)T + (int64_t)x * kBlock + tid];
+            const f32x4_t rs = rowstat[bh * (int64_t)T + (int64_t)i * kBlock + tid];
             ls = rs[0] * kLog2e;
             dl = rs[1];
         }
-    };
-    int i = next_i(0);
-    if (i < N) fetch(i);
-    while (i < N) {
         __syncthreads();
         tile_store<D>(sQ, qr, tid);
         tile_store<D>(sO, orr, tid);
@@ -645,13 +644,11 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_exact_kernel(
             sdel[tid] = dl;
         }
         __syncthreads();
-        const int inext = next_i(i + 1);
-        if (inext < N) fetch(inext);
         f32x16_t s = zero16(), dp = zero16();
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
-            s = mfma(row_op<D>(sQ, qt * 32 + r32, ks, g), as_bf16x8(kreg[ks]), s);    // S: queries x keys
-            dp = mfma(row_op<D>(sO, qt * 32 + r32, ks, g), as_bf16x8(vreg[ks]), dp);  // dP
+            s = mfma(row_op<D>(sQ, qt * 32 + r32, ks, g), row_op<D>(sKt, kt * 32 + r32, ks, g), s);   // S
+            dp = mfma(row_op<D>(sO, qt * 32 + r32, ks, g), row_op<D>(sVt, kt * 32 + r32, ks, g), dp); // dP
         }
         f32x16_t p;
 #pragma unroll
@@ -676,7 +673,6 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_exact_kernel(
                 dka[dt] = mfma(aq, lo, dka[dt]);
             }
         }
-        i = inext;
     }
     // the two query halves of each key tile: wave (kt, 1) hands its partials to wave (kt, 0)
     float* xs = reinterpret_cast<float*>(smem);   // [kt][dt][16][64] fp32: 2 * DT * 4 KB = 2 tiles

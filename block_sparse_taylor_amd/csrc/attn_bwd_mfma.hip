@@ -209,9 +209,9 @@ struct VirtRow {
 };
 
 // (H g)^T for the head-dim tiles [dt0, dt0 + D / 64): A = H rows (hi + lo), B = dout rows.
-template <int D>
-__device__ __forceinline__ void hg_tiles(f32x16_t (&hg)[D / 64], const bf16_t* hh, const bf16_t* hl,
-                                         const uint4 (&oreg)[D / 16], int dt0, int r32, int g) {
+template <int D, typename BOp>
+__device__ __forceinline__ void hg_tiles(f32x16_t (&hg)[D / 64], const bf16_t* hh, const bf16_t* hl, BOp bop,
+                                         int dt0, int r32, int g) {
 #pragma unroll
     for (int x = 0; x < D / 64; ++x) {
         f32x16_t c = zero16();
@@ -219,8 +219,9 @@ __device__ __forceinline__ void hg_tiles(f32x16_t (&hg)[D / 64], const bf16_t* h
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) {
             const int64_t o = (int64_t)d * D + 16 * ks + 8 * g;
-            c = mfma(as_bf16x8(*reinterpret_cast<const uint4*>(hh + o)), as_bf16x8(oreg[ks]), c);
-            c = mfma(as_bf16x8(*reinterpret_cast<const uint4*>(hl + o)), as_bf16x8(oreg[ks]), c);
+            const bf16x8_t b = bop(ks);
+            c = mfma(as_bf16x8(*reinterpret_cast<const uint4*>(hh + o)), b, c);
+            c = mfma(as_bf16x8(*reinterpret_cast<const uint4*>(hl + o)), b, c);
         }
         hg[x] = c;
     }
@@ -323,7 +324,8 @@ __global__ __launch_bounds__(kThreads) void bwd_rowstats_kernel(
         uint4 oreg[C::KS];
         rows_from_global<D>(oreg, dout + base, t, T, g);
         f32x16_t hg[C::DT / 2];
-        hg_tiles<D>(hg, hh + bh * (int64_t)D * D, hl + bh * (int64_t)D * D, oreg, kt * C::DT / 2, r32, g);
+        hg_tiles<D>(hg, hh + bh * (int64_t)D * D, hl + bh * (int64_t)D * D,
+                    [&](int ks) { return as_bf16x8(oreg[ks]); }, kt * C::DT / 2, r32, g);
         if (t < T) {
 #pragma unroll
             for (int x = 0; x < C::DT / 2; ++x)
@@ -373,8 +375,10 @@ __global__ __launch_bounds__(kThreads) void bwd_rowstats_kernel(
 // ---------------------------------------------------------------- dq
 // dq' = K^T dS^T (exact keys) + kbar^T dlam^T (virtual tokens, kbar hi + lo)
 // + c H g, then dq = s dq' + 2 s^2 q dq2bar_i / n_i (second order).
+// Q and dO of the query block sit in LDS (B operands), so that a wave fits
+// in 256 registers and two waves share a SIMD.
 template <int D>
-__global__ __launch_bounds__(kThreads) void bwd_dq_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dq_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const bf16_t* __restrict__ dout, const bf16_t* __restrict__ kbh, const bf16_t* __restrict__ kbl,
     const bf16_t* __restrict__ vhh, const bf16_t* __restrict__ vhl, const bf16_t* __restrict__ hh,
@@ -384,8 +388,11 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(
     using C = BC<D>;
     __shared__ __attribute__((aligned(16))) unsigned char smem[2 * C::TILE];   // K, V (or kbar hi, lo) tiles; exchange
     __shared__ __attribute__((aligned(16))) float sbias[64], smass[64];      // a virtual group's biases, n_j
+    __shared__ __attribute__((aligned(16))) unsigned char sqo[2 * C::TILE];   // Q, dO of the query block
     unsigned char* sK = smem;
     unsigned char* sV = smem + C::TILE;
+    unsigned char* sQt = sqo;
+    unsigned char* sOt = sqo + C::TILE;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r32 = lane & 31, g = lane >> 5;
     const int kt = wave >> 1, qt = wave & 1;
@@ -399,9 +406,17 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(
     const VirtRow vr{mrow, second_order ? wgate + (bh * N + i) * (int64_t)N : nullptr, N,
                      log2f((float)(T - (N - 1) * kBlock))};
 
-    uint4 qreg[C::KS], oreg[C::KS];
-    rows_from_global<D>(qreg, q + base, t, T, g);
-    rows_from_global<D>(oreg, dout + base, t, T, g);
+    {
+        const int rows = min(kBlock, T - i * kBlock);
+        uint4 a_[C::LPT], b_[C::LPT];
+        tile_load<D>(a_, q + base + (int64_t)i * kBlock * D, rows, tid);
+        tile_load<D>(b_, dout + base + (int64_t)i * kBlock * D, rows, tid);
+        tile_store<D>(sQt, a_, tid);
+        tile_store<D>(sOt, b_, tid);
+    }
+    // B operands: this lane's query row, head dims 16 ks + 8 g ..
+    auto qop = [&](int ks) { return row_op<D>(sQt, qt * 32 + r32, ks, g); };
+    auto oop = [&](int ks) { return row_op<D>(sOt, qt * 32 + r32, ks, g); };
     float lse2 = INFINITY, delta = 0.f, beta = 0.f, cf = 0.f;
     if (t < T) {
         const f32x4_t rs = rowstat[bh * (int64_t)T + t];
@@ -414,34 +429,22 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) acc[dt] = zero16();
 
-    // exact KV blocks, one step ahead: the next block's K, V rows are loaded
-    // into registers during this step's products
-    auto next_j = [&](int from) {
-        for (int x = from; x < N; ++x)
-            if ((mrow[x >> 5] >> (x & 31)) & 1u) return x;   // uniform
-        return N;
-    };
-    uint4 kr[C::LPT], vr_[C::LPT];
-    auto fetch = [&](int x) {
-        const int nv = min(kBlock, T - x * kBlock);
-        tile_load<D>(kr, k + base + (int64_t)x * kBlock * D, nv, tid);
-        tile_load<D>(vr_, v + base + (int64_t)x * kBlock * D, nv, tid);
-    };
-    int j = next_j(0);
-    if (j < N) fetch(j);
-    while (j < N) {
+    // exact KV blocks
+    for (int j = 0; j < N; ++j) {
+        if (!((mrow[j >> 5] >> (j & 31)) & 1u)) continue;   // uniform
         const int nval = min(kBlock, T - j * kBlock);
+        uint4 kr[C::LPT], vr_[C::LPT];
+        tile_load<D>(kr, k + base + (int64_t)j * kBlock * D, nval, tid);
+        tile_load<D>(vr_, v + base + (int64_t)j * kBlock * D, nval, tid);
         __syncthreads();
         tile_store<D>(sK, kr, tid);
         tile_store<D>(sV, vr_, tid);
         __syncthreads();
-        const int jnext = next_j(j + 1);
-        if (jnext < N) fetch(jnext);
         f32x16_t s = zero16(), dp = zero16();
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
-            s = mfma(row_op<D>(sK, kt * 32 + r32, ks, g), as_bf16x8(qreg[ks]), s);
-            dp = mfma(row_op<D>(sV, kt * 32 + r32, ks, g), as_bf16x8(oreg[ks]), dp);
+            s = mfma(row_op<D>(sK, kt * 32 + r32, ks, g), qop(ks), s);
+            dp = mfma(row_op<D>(sV, kt * 32 + r32, ks, g), oop(ks), dp);
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -460,7 +463,6 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(
                 acc[dt] = mfma(a, lo, acc[dt]);
             }
         }
-        j = jnext;
     }
     // virtual tokens, 64 blocks at a time: kbar hi / lo tiles in LDS
     const bf16_t* kbh_h = kbh + bh * (int64_t)N * D;
@@ -469,7 +471,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(
     const bf16_t* vhl_h = vhl + bh * (int64_t)N * D;
     for (int G = 0; G * 64 < N; ++G) {
         const int nb = min(64, N - G * 64);
-        uint4 kl[C::LPT];
+        uint4 kr[C::LPT], kl[C::LPT];
         tile_load<D>(kr, kbh_h + (int64_t)G * 64 * D, nb, tid);
         tile_load<D>(kl, kbl_h + (int64_t)G * 64 * D, nb, tid);
         __syncthreads();
@@ -486,13 +488,15 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
             const bf16x8_t ah = row_op<D>(sK, kt * 32 + r32, ks, g), al = row_op<D>(sV, kt * 32 + r32, ks, g);
-            s = mfma(ah, as_bf16x8(qreg[ks]), s);
-            s = mfma(al, as_bf16x8(qreg[ks]), s);
+            const bf16x8_t bq = qop(ks);
+            s = mfma(ah, bq, s);
+            s = mfma(al, bq, s);
             const int64_t oo = (int64_t)jr * D + 16 * ks + 8 * g;
             const uint4 vh = jr < N ? *reinterpret_cast<const uint4*>(vhh_h + oo) : make_uint4(0, 0, 0, 0);
             const uint4 vl = jr < N ? *reinterpret_cast<const uint4*>(vhl_h + oo) : make_uint4(0, 0, 0, 0);
-            gv = mfma(as_bf16x8(vh), as_bf16x8(oreg[ks]), gv);
-            gv = mfma(as_bf16x8(vl), as_bf16x8(oreg[ks]), gv);
+            const bf16x8_t bo = oop(ks);
+            gv = mfma(as_bf16x8(vh), bo, gv);
+            gv = mfma(as_bf16x8(vl), bo, gv);
         }
 #pragma unroll
         for (int run = 0; run < 4; ++run) {   // blocks 8 run + 4 g + (0..3) of the key half kt
@@ -522,7 +526,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(
     // c H g on this wave's head-dim tiles
     if (first_order) {
         f32x16_t hg[C::DT / 2];
-        hg_tiles<D>(hg, hh + bh * (int64_t)D * D, hl + bh * (int64_t)D * D, oreg, kt * C::DT / 2, r32, g);
+        hg_tiles<D>(hg, hh + bh * (int64_t)D * D, hl + bh * (int64_t)D * D, oop, kt * C::DT / 2, r32, g);
         // tile dt belongs to wave kt = dt / (DT / 2): compile-time indices, a runtime select
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt)

@@ -33,8 +33,8 @@
 //   row   - per query block: lse, delta, beta, c (rowstat) and dq (fp32),
 //   dh    - partial sums of dH over row chunks, then their fixed-order sum,
 //   virt  - per group of 16 KV blocks: dkbar (virtual part), dV-hat, dsig2 (fp32),
-//   kv    - per KV block: dk, dv of the exact pairs (fp32; for bf16 they come
-//           from the matrix-core kernel) plus every chain term.
+//   kv    - per KV block: dk, dv of the exact pairs plus every chain term
+//           (fp32; for bf16 the matrix-core dk/dv kernel does both).
 #include <math.h>
 
 #include <type_traits>
@@ -365,14 +365,18 @@ __global__ __launch_bounds__(kThreads) void bwd_dh_kernel(const T* __restrict__ 
         for (int y = 0; y < R; ++y) out[(a * R + x) * D + b * R + y] = acc[x][y];
 }
 
+// dH (and, when dHT is given, its transpose) from the partial sums in fixed order.
 __global__ __launch_bounds__(kThreads) void bwd_dh_reduce_kernel(const float* __restrict__ part,
-                                                                 float* __restrict__ dH, int P, int DD) {
+                                                                 float* __restrict__ dH, float* __restrict__ dHT,
+                                                                 int P, int D) {
     const int64_t bh = blockIdx.y;
+    const int DD = D * D;
     const int e = blockIdx.x * kThreads + threadIdx.x;
     if (e >= DD) return;
     float s = 0.f;
     for (int p = 0; p < P; ++p) s += part[(bh * P + p) * (int64_t)DD + e];
     dH[bh * (int64_t)DD + e] = s;
+    if (dHT) dHT[bh * (int64_t)DD + (e % D) * D + e / D] = s;
 }
 
 // ---------------------------------------------------------------- virt
@@ -493,11 +497,8 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_kernel(
     const double* __restrict__ kbar, const float* __restrict__ vsum, const f32x4_t* __restrict__ rowstat,
     const uint32_t* __restrict__ mask, const float* __restrict__ dH, const float* __restrict__ dkb_v,
     const float* __restrict__ dvh_v, const float* __restrict__ dsg_v, T* __restrict__ dk, T* __restrict__ dv,
-    int Tn, int N, int NW, float scale, int second_order, int first_order, const float* __restrict__ dk_part,
-    const float* __restrict__ dv_part, int nsplit) {
+    int Tn, int N, int NW, float scale, int second_order, int first_order, int nsplit) {
     // dkb_v / dvh_v hold nsplit partial sums (consecutive [BH, N, D] arrays), added in order.
-    // dk_part / dv_part (optional): the exact pairs' dk, dv (fp32) from the
-    // matrix-core kernel; the exact loop is then skipped.
     constexpr int C = D / 16;
     constexpr int Q = D / 4;
     constexpr int LD = D + 4;                  // padded row stride of the chain's staging
@@ -526,12 +527,11 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_kernel(
             const int64_t a = base + (int64_t)row * D + 16 * c + 4 * p + e;
             kk[4 * c + e] = kvalid ? load_f32(k + a) : 0.f;
             vv[4 * c + e] = kvalid ? load_f32(v + a) : 0.f;
-            dkk[4 * c + e] = (dk_part && kvalid) ? dk_part[a] : 0.f;
-            dvv[4 * c + e] = (dv_part && kvalid) ? dv_part[a] : 0.f;
+            dkk[4 * c + e] = dvv[4 * c + e] = 0.f;
         }
 
     // Exact pairs: every query block i whose exact set holds j.
-    for (int i = 0; i < N && !dk_part; ++i) {
+    for (int i = 0; i < N; ++i) {
         if (!bit_set(mask + (bh * N + i) * (int64_t)NW, j)) continue;   // uniform
         const int rows = min(kBlock, Tn - i * kBlock);
         const int64_t src = base + (int64_t)i * kBlock * D;
@@ -671,14 +671,14 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_kernel(
 }
 
 struct BwdLayout {
-    size_t rowstat, mask, dkb, dvh, dsg, dhp, dh, planes, dq2, dkp, dvp, dw, total;
+    size_t rowstat, mask, dkb, dvh, dsg, dhp, dh, dht, planes, dq2, dw, total;
     int NW, P, S;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// bf16 inputs add the matrix-core kernels' buffers: bf16 hi + lo planes of
-// kbar, V-hat and H, dq2bar, the exact pairs' fp32 dk and dv, and the dW table.
+// bf16 inputs add the matrix-core kernels' buffers: dH transposed, bf16 hi +
+// lo planes of kbar, V-hat and H, dq2bar and the dW table.
 BwdLayout bwd_layout(const Geom& g, bool mfma) {
     BwdLayout L;
     L.NW = (g.N + 31) / 32;
@@ -693,11 +693,9 @@ BwdLayout bwd_layout(const Geom& g, bool mfma) {
     L.dsg = o;     o = align256(o + BH * ND * sizeof(float));
     L.dhp = o;     o = align256(o + BH * L.P * DD * sizeof(float));
     L.dh = o;      o = align256(o + BH * DD * sizeof(float));
-    const size_t TD = mfma ? (size_t)g.T * g.D : 0;
+    L.dht = o;     o = align256(o + (mfma ? BH * DD * sizeof(float) : 0));
     L.planes = o;  o = align256(o + (mfma ? BH * (4 * ND + 2 * DD) * sizeof(bf16_t) : 0));
     L.dq2 = o;     o = align256(o + (mfma ? BH * ND * sizeof(float) : 0));
-    L.dkp = o;     o = align256(o + BH * TD * sizeof(float));
-    L.dvp = o;     o = align256(o + BH * TD * sizeof(float));
     L.dw = o;      o = align256(o + (mfma ? BH * g.N * (size_t)g.N * sizeof(float) : 0));
     L.total = o;
     return L;
@@ -727,8 +725,7 @@ hipError_t run_bwd(const Geom& g, const pisa_params_t* p, const void* q, const v
 
     hipLaunchKernelGGL(bwd_mask_kernel, dim3(g.N, BH), dim3(64), L.NW * sizeof(uint32_t), stream,
                        p->topk > 0 ? idx : nullptr, mask, g.N, L.NW, p->topk, p->band, p->n_sink);
-    float* dkp = kMfma ? reinterpret_cast<float*>(w + L.dkp) : nullptr;
-    float* dvp = kMfma ? reinterpret_cast<float*>(w + L.dvp) : nullptr;
+    float* dht = kMfma ? reinterpret_cast<float*>(w + L.dht) : nullptr;
     if constexpr (kMfma) {
         bf16_t* pl = reinterpret_cast<bf16_t*>(w + L.planes);
         const size_t ND = (size_t)g.BH * g.N * D, DD = (size_t)g.BH * D * D;
@@ -745,7 +742,6 @@ hipError_t run_bwd(const Geom& g, const pisa_params_t* p, const void* q, const v
             e = launch_bwd_dq(g, tq, tk, tv, tg, kbh, kbl, vhh, vhl, hh, hl, mask, wg, rowstat, dw,
                               so ? st->ksig2 : nullptr, reinterpret_cast<float*>(w + L.dq2), static_cast<bf16_t*>(dq),
                               L.NW, so, fo, stream);
-        if (e == hipSuccess) e = launch_bwd_dkdv_exact(g, tq, tk, tv, tg, mask, rowstat, dkp, dvp, L.NW, stream);
         if (e != hipSuccess) return e;
     } else {
         hipLaunchKernelGGL((bwd_row_kernel<T, D>), dim3(g.N, BH), dim3(kRowThreads), L.NW * sizeof(uint32_t),
@@ -761,11 +757,18 @@ hipError_t run_bwd(const Geom& g, const pisa_params_t* p, const void* q, const v
         hipLaunchKernelGGL((bwd_dh_kernel<T, D>), dim3(L.P, BH), dim3(kThreads), 0, stream, tq, tg, rowstat,
                            dhp, g.T, rows_per, g.scale);
         hipLaunchKernelGGL(bwd_dh_reduce_kernel, dim3((D * D + kThreads - 1) / kThreads, BH), dim3(kThreads),
-                           0, stream, dhp, dh, L.P, D * D);
+                           0, stream, dhp, dh, dht, L.P, D);
     }
-    hipLaunchKernelGGL((bwd_kv_kernel<T, D>), dim3(g.N, BH), dim3(kThreads), 0, stream, tq, tk, tv, tg,
-                       st->kbar, st->vsum, rowstat, mask, dh, dkb, dvh, dsg, static_cast<T*>(dk),
-                       static_cast<T*>(dv), g.T, g.N, L.NW, g.scale, so, fo, dkp, dvp, L.S);
+    if constexpr (kMfma) {
+        const hipError_t e = launch_bwd_dkdv(g, tq, tk, tv, tg, mask, rowstat, st, dh, dht, dkb, dvh, dsg,
+                                             static_cast<bf16_t*>(dk), static_cast<bf16_t*>(dv), L.NW, L.S, so, fo,
+                                             stream);
+        if (e != hipSuccess) return e;
+    } else {
+        hipLaunchKernelGGL((bwd_kv_kernel<T, D>), dim3(g.N, BH), dim3(kThreads), 0, stream, tq, tk, tv, tg,
+                           st->kbar, st->vsum, rowstat, mask, dh, dkb, dvh, dsg, static_cast<T*>(dk),
+                           static_cast<T*>(dv), g.T, g.N, L.NW, g.scale, so, fo, L.S);
+    }
     return hipGetLastError();
 }
 

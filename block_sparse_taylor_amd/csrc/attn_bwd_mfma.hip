@@ -596,11 +596,15 @@ template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dkdv_exact_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const bf16_t* __restrict__ dout, const uint32_t* __restrict__ mask, const f32x4_t* __restrict__ rowstat,
-    float* __restrict__ dk_part, float* __restrict__ dv_part, int T, int N, int NW, float scale) {
+    const double* __restrict__ kbar, const float* __restrict__ vsum, const float* __restrict__ dH,
+    const float* __restrict__ dHT, const float* __restrict__ dkb_part, const float* __restrict__ dvh_part,
+    const float* __restrict__ dsg, bf16_t* __restrict__ dk, bf16_t* __restrict__ dv, int T, int N, int NW,
+    float scale, int nsplit, int second_order, int first_order) {
     using C = BC<D>;
     __shared__ __attribute__((aligned(16))) unsigned char smem[2 * C::TILE];   // Q, dO tiles; then the exchange
     __shared__ __attribute__((aligned(16))) unsigned char skv[2 * C::TILE];    // K, V of the block
     __shared__ float slse[64], sdel[64];
+    __shared__ float sblk[5][D];   // the block's kbar, dkbar, dV-hat, dsig2, dH V-hat
     unsigned char* sQ = smem;
     unsigned char* sO = smem + C::TILE;
     unsigned char* sKt = skv;
@@ -678,38 +682,132 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             }
         }
     }
-    // the two query halves of each key tile: wave (kt, 1) hands its partials to wave (kt, 0)
-    float* xs = reinterpret_cast<float*>(smem);   // [kt][dt][16][64] fp32: 2 * DT * 4 KB = 2 tiles
+    // ---- epilogue. The two query halves of a key tile swap partials, so that
+    // wave (kt, qt) holds the sums of head-dim tiles [qt HT, qt HT + HT); then
+    // it adds the chain terms of the block and stores dk, dv:
+    //   dk = s sum_t dS q + dH v + (dkbar_j - dH V-hat_j) / n_j + 2 dsig2_j (k - kbar_j) / n_j,
+    //   dv = sum_t P dout + dH^T (k - kbar_j) + dV-hat_j.
+    constexpr int HT = C::DT / 2;
+    f32x16_t ov[HT], ok_[HT];
+    float* xs = reinterpret_cast<float*>(smem);   // [kt][qt][x][16][64]: 4 * HT * 4 KB = 2 tiles
 #pragma unroll
     for (int pass = 0; pass < 2; ++pass) {
         f32x16_t* a = pass == 0 ? dva : dka;
+        f32x16_t* own = pass == 0 ? ov : ok_;
         __syncthreads();
-        if (qt == 1) {
 #pragma unroll
-            for (int dt = 0; dt < C::DT; ++dt)
+        for (int x = 0; x < HT; ++x) {
+            const f32x16_t lo_ = a[x], hi_ = a[HT + x];
+            const f32x16_t send = qt == 0 ? hi_ : lo_;
+            own[x] = qt == 0 ? lo_ : hi_;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) xs[((kt * C::DT + dt) * 16 + r) * 64 + lane] = a[dt][r];
+            for (int r = 0; r < 16; ++r) xs[(((kt * 2 + qt) * HT + x) * 16 + r) * 64 + lane] = send[r];
         }
         __syncthreads();
-        if (qt == 0 && key < T) {
-            float* out = (pass == 0 ? dv_part : dk_part) + base + (int64_t)key * D;
-            const float sc = pass == 0 ? 1.f : scale;
 #pragma unroll
-            for (int dt = 0; dt < C::DT; ++dt)
+        for (int x = 0; x < HT; ++x)
 #pragma unroll
-                for (int run = 0; run < 4; ++run) {
-                    f32x4_t w;
+            for (int r = 0; r < 16; ++r) own[x][r] += xs[(((kt * 2 + (1 - qt)) * HT + x) * 16 + r) * 64 + lane];
+    }
+    const int64_t jb = (bh * N + j) * (int64_t)D;
+    const int64_t pstride = (int64_t)gridDim.y * N * D;
+    for (int d = tid; d < D; d += kThreads) {
+        float sk_ = 0.f, sv_ = 0.f;
+        for (int sp = 0; sp < nsplit; ++sp) {
+            sk_ += dkb_part[sp * pstride + jb + d];
+            sv_ += dvh_part[sp * pstride + jb + d];
+        }
+        float xh = 0.f;
+        if (first_order) {
+            const float* hr = dH + bh * (int64_t)D * D + (int64_t)d * D;
+            for (int e = 0; e < D; ++e) xh = fmaf(hr[e], vsum[jb + e], xh);
+        }
+        sblk[0][d] = (float)kbar[jb + d];
+        sblk[1][d] = sk_;
+        sblk[2][d] = sv_;
+        sblk[3][d] = second_order ? dsg[jb + d] : 0.f;
+        sblk[4][d] = xh;
+    }
+    __syncthreads();
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int r = 4 * run + e;
-                        w[e] = sc * (a[dt][r] + xs[((kt * C::DT + dt) * 16 + r) * 64 + lane]);
-                    }
-                    *reinterpret_cast<f32x4_t*>(out + dt * 32 + 8 * run + 4 * g) = w;
+    for (int x = 0; x < HT; ++x)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ok_[x][r] *= scale;
+    if (first_order) {
+        const float* dHh = dH + bh * (int64_t)D * D;
+        const float* dHTh = dHT + bh * (int64_t)D * D;
+        auto split8 = [&](const float* src, bf16x8_t& hi, bf16x8_t& lo) {
+            const f32x4_t u0 = *reinterpret_cast<const f32x4_t*>(src), u1 = *reinterpret_cast<const f32x4_t*>(src + 4);
+            f32x16_t t = zero16();
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                t[e] = u0[e];
+                t[4 + e] = u1[e];
+            }
+            split_op(t, 0, hi, lo);
+        };
+#pragma unroll
+        for (int x = 0; x < HT; ++x) {
+            const int row = (qt * HT + x) * 32 + r32;   // head dim of this lane's A row
+#pragma unroll
+            for (int ks = 0; ks < C::KS; ++ks) {
+                const int c0 = 16 * ks + 8 * g;
+                bf16x8_t ah, al;
+                // dK^T += dH V^T: A = dH rows, B = V rows of the block
+                split8(dHh + (int64_t)row * D + c0, ah, al);
+                const bf16x8_t bv = row_op<D>(sVt, kt * 32 + r32, ks, g);
+                ok_[x] = mfma(ah, bv, ok_[x]);
+                ok_[x] = mfma(al, bv, ok_[x]);
+                // dV^T += dH^T (K - kbar)^T: A = dH^T rows, B = (k - kbar) of the block, hi + lo
+                split8(dHTh + (int64_t)row * D + c0, ah, al);
+                const uint4 kb = *reinterpret_cast<const uint4*>(sKt + (kt * 32 + r32) * C::RB +
+                                                                   16 * ((2 * ks + g) ^ (2 * ((kt * 32 + r32) & C::SWM))));
+                f32x16_t kc = zero16();
+                const uint32_t kw[4] = {kb.x, kb.y, kb.z, kb.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    kc[2 * e] = bf16_lo(kw[e]) - sblk[0][c0 + 2 * e];
+                    kc[2 * e + 1] = bf16_hi(kw[e]) - sblk[0][c0 + 2 * e + 1];
                 }
+                bf16x8_t kh, kl;
+                split_op(kc, 0, kh, kl);
+                ov[x] = mfma(ah, kh, ov[x]);
+                ov[x] = mfma(ah, kl, ov[x]);
+                ov[x] = mfma(al, kh, ov[x]);
+            }
         }
     }
+    if (key < T) {
+        const int nj = min(kBlock, T - j * kBlock);
+        const float inv_n = 1.f / (float)nj;
+        const unsigned char* krow = sKt + (kt * 32 + r32) * C::RB;
+        const int sw = (kt * 32 + r32) & C::SWM;
+#pragma unroll
+        for (int x = 0; x < HT; ++x)
+#pragma unroll
+            for (int run = 0; run < 4; ++run) {
+                const int d0 = (qt * HT + x) * 32 + 8 * run + 4 * g;
+                // k of this key at dims d0 .. d0 + 3 (one 8-byte piece of its chunk)
+                const uint2 kk = *reinterpret_cast<const uint2*>(krow + 16 * ((d0 >> 3) ^ (2 * sw)) + 2 * (d0 & 7));
+                const float kv[4] = {bf16_lo(kk.x), bf16_hi(kk.x), bf16_lo(kk.y), bf16_hi(kk.y)};
+                float gk[4], gv[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int d = d0 + e, r = 4 * run + e;
+                    gk[e] = ok_[x][r] + (sblk[1][d] - sblk[4][d]) * inv_n;
+                    if (second_order) gk[e] = fmaf(2.f * sblk[3][d] * inv_n, kv[e] - sblk[0][d], gk[e]);
+                    gv[e] = ov[x][r] + sblk[2][d];
+                }
+                const int64_t o = base + (int64_t)key * D + d0;
+                *reinterpret_cast<uint2*>(dk + o) =
+                    make_uint2((uint32_t)f32_to_bf16(gk[0]) | ((uint32_t)f32_to_bf16(gk[1]) << 16),
+                               (uint32_t)f32_to_bf16(gk[2]) | ((uint32_t)f32_to_bf16(gk[3]) << 16));
+                *reinterpret_cast<uint2*>(dv + o) =
+                    make_uint2((uint32_t)f32_to_bf16(gv[0]) | ((uint32_t)f32_to_bf16(gv[1]) << 16),
+                               (uint32_t)f32_to_bf16(gv[2]) | ((uint32_t)f32_to_bf16(gv[3]) << 16));
+            }
+    }
 }
-
 
 // ---------------------------------------------------------------- virtual tokens
 // One workgroup per (bh, group of 64 KV blocks, query split): the blocks'
@@ -951,16 +1049,19 @@ hipError_t launch_bwd_dq(const Geom& g, const bf16_t* q, const bf16_t* k, const 
     return hipGetLastError();
 }
 
-hipError_t launch_bwd_dkdv_exact(const Geom& g, const bf16_t* q, const bf16_t* k, const bf16_t* v,
-                                 const bf16_t* dout, const uint32_t* mask, const f32x4_t* rowstat, float* dk_part,
-                                 float* dv_part, int NW, hipStream_t stream) {
+hipError_t launch_bwd_dkdv(const Geom& g, const bf16_t* q, const bf16_t* k, const bf16_t* v, const bf16_t* dout,
+                           const uint32_t* mask, const f32x4_t* rowstat, const pisa_stats_t* st, const float* dH,
+                           const float* dHT, const float* dkb_part, const float* dvh_part, const float* dsg,
+                           bf16_t* dk, bf16_t* dv, int NW, int nsplit, int second_order, int first_order,
+                           hipStream_t stream) {
     const dim3 grid(g.N, (unsigned)g.BH);
-    if (g.D == 128)
-        hipLaunchKernelGGL((bwd_dkdv_exact_kernel<128>), grid, dim3(kThreads), 0, stream, q, k, v, dout, mask,
-                           rowstat, dk_part, dv_part, g.T, g.N, NW, g.scale);
-    else
-        hipLaunchKernelGGL((bwd_dkdv_exact_kernel<64>), grid, dim3(kThreads), 0, stream, q, k, v, dout, mask,
-                           rowstat, dk_part, dv_part, g.T, g.N, NW, g.scale);
+#define PISA_DKDV(DD)                                                                                          \
+    hipLaunchKernelGGL((bwd_dkdv_exact_kernel<DD>), grid, dim3(kThreads), 0, stream, q, k, v, dout, mask, rowstat, \
+                       st->kbar, st->vsum, dH, dHT, dkb_part, dvh_part, dsg, dk, dv, g.T, g.N, NW, g.scale, nsplit, \
+                       second_order, first_order)
+    if (g.D == 128) PISA_DKDV(128);
+    else PISA_DKDV(64);
+#undef PISA_DKDV
     return hipGetLastError();
 }
 

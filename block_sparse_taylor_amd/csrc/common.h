@@ -101,9 +101,11 @@ hipError_t launch_bwd_virt_mfma(const Geom& g, const bf16_t* q, const bf16_t* do
                                 const uint32_t* mask, const f32x4_t* rowstat, const float* wgate, float* dkb_part,
                                 float* dvh_part, float* dw, float* dsg, int NW, int second_order,
                                 hipStream_t stream);
-hipError_t launch_bwd_dkdv_exact(const Geom& g, const bf16_t* q, const bf16_t* k, const bf16_t* v,
-                                 const bf16_t* dout, const uint32_t* mask, const f32x4_t* rowstat, float* dk_part,
-                                 float* dv_part, int NW, hipStream_t stream);
+hipError_t launch_bwd_dkdv(const Geom& g, const bf16_t* q, const bf16_t* k, const bf16_t* v, const bf16_t* dout,
+                           const uint32_t* mask, const f32x4_t* rowstat, const pisa_stats_t* st, const float* dH,
+                           const float* dHT, const float* dkb_part, const float* dvh_part, const float* dsg,
+                           bf16_t* dk, bf16_t* dv, int NW, int nsplit, int second_order, int first_order,
+                           hipStream_t stream);
 hipError_t launch_attn_bwd(const Geom& g, int dtype, const pisa_params_t* p, const void* q, const void* k,
                            const void* v, const void* o, const void* dout, const pisa_stats_t* st,
                            const int32_t* idx, const float* wgate, void* dq, void* dk, void* dv, void* ws,

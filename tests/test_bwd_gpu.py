@@ -253,3 +253,9 @@ def test_bf16_many_groups_contract():
     """N = 131 blocks: three groups of 64 virtual tokens, the last holding 3."""
     check(wl("tiny", seq_len=64 * 130 + 7, head_dim=128, heads=1, dtype="bf16"), seed=17, topk=5, so=True,
           n_sink=1, contract=True)
+
+
+def test_bf16_two_batches_contract():
+    """batch 2 x 3 heads: the kernels index (batch, head) pairs as one axis."""
+    w = wl("wan14", batch=2, heads=3, grid=(3, 11, 31), seq_len=1023)
+    check(w, seed=18, topk=3, so=True, n_sink=1, contract=True)

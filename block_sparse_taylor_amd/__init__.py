@@ -255,6 +255,58 @@ def reorder_scatter(o: torch.Tensor, perm: torch.Tensor, out=None) -> torch.Tens
     return _reorder("pisa_reorder_scatter", o, perm, (B, H, T, D), (B, T, H, D), out)
 
 
+class _Attention(torch.autograd.Function):
+    """The three forward calls; backward = pisa_attn_bwd with the routing and
+    gate of the forward (argument marshalling only)."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, topk, band, second_order, scale, n_sink):
+        st = pisa_block_stats(q, k, v, second_order=second_order, scale=scale)
+        idx, wg = pisa_route_topk(q, st, topk, band=band, second_order=second_order, scale=scale,
+                                  n_sink=n_sink)
+        idx = idx if topk else None
+        o = pisa_attn_fwd(q, k, v, st, idx, wg, band=band, second_order=second_order, scale=scale,
+                          n_sink=n_sink)
+        ctx.save_for_backward(q, k, v, o)
+        ctx.st, ctx.idx, ctx.wg = st, idx, wg
+        ctx.cfg = (band, second_order, scale, n_sink)
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o = ctx.saved_tensors
+        band, so, scale, n_sink = ctx.cfg
+        dq, dk, dv = pisa_attn_bwd(q, k, v, o, do.contiguous(), ctx.st, ctx.idx, ctx.wg, band=band,
+                                   second_order=so, scale=scale, n_sink=n_sink)
+        return dq, dk, dv, None, None, None, None, None
+
+
+class _Gather(torch.autograd.Function):
+    """reorder_gather; its adjoint is reorder_scatter."""
+
+    @staticmethod
+    def forward(ctx, x, perm):
+        ctx.perm = perm
+        return reorder_gather(x, perm)
+
+    @staticmethod
+    def backward(ctx, g):
+        return reorder_scatter(g.contiguous(), ctx.perm), None
+
+
+class _Scatter(torch.autograd.Function):
+    """reorder_scatter; its adjoint is reorder_gather."""
+
+    @staticmethod
+    def forward(ctx, o, perm):
+        ctx.perm = perm
+        return reorder_scatter(o, perm)
+
+    @staticmethod
+    def backward(ctx, g):
+        return reorder_gather(g.contiguous(), ctx.perm), None
+
+
 def piecewise_sparse_attention(q, k, v, density=0.125, variant="pisa", band=1, scale=None,
                                n_sink_blocks=0, cov_bias=False, reorder="none", grid=None,
                                prefix=0):
@@ -268,6 +320,9 @@ def piecewise_sparse_attention(q, k, v, density=0.125, variant="pisa", band=1, s
     order over ``prefix`` fixed tokens then ``grid`` (slowest axis first); the
     tokens are gathered into Z-order (and [B, H, T, D]) before the operator and
     the output is scattered back to [B, T, H, D].
+    Differentiable: with inputs that require grad, backward runs
+    pisa_attn_bwd (the routing and gate of the forward held constant) and the
+    reorder's adjoint.
     """
     if cov_bias:
         raise NotImplementedError("the covariance-aware routing bias is not built")
@@ -282,15 +337,11 @@ def piecewise_sparse_attention(q, k, v, density=0.125, variant="pisa", band=1, s
         perm = z_order(grid, prefix).to(q.device)
         if perm.numel() != q.shape[1]:
             raise ValueError("prefix + prod(grid) must equal the token count")
-        q, k, v = (reorder_gather(t, perm) for t in (q, k, v))
+        q, k, v = (_Gather.apply(t, perm) for t in (q, k, v))
     so = variant == "pwt"
     N = num_blocks(q.shape[2])
     topk = topk_for_density(density, N)
     topk = min(topk, N)
     n_sink_blocks = min(int(n_sink_blocks), N)
-    st = pisa_block_stats(q, k, v, second_order=so, scale=scale)
-    idx, wg = pisa_route_topk(q, st, topk, band=band, second_order=so, scale=scale,
-                              n_sink=n_sink_blocks)
-    o = pisa_attn_fwd(q, k, v, st, idx if topk else None, wg, band=band, second_order=so,
-                      scale=scale, n_sink=n_sink_blocks)
-    return o if perm is None else reorder_scatter(o, perm)
+    o = _Attention.apply(q, k, v, topk, band, so, scale, n_sink_blocks)
+    return o if perm is None else _Scatter.apply(o, perm)

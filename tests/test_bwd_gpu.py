@@ -259,3 +259,37 @@ def test_bf16_two_batches_contract():
     """batch 2 x 3 heads: the kernels index (batch, head) pairs as one axis."""
     w = wl("wan14", batch=2, heads=3, grid=(3, 11, 31), seq_len=1023)
     check(w, seed=18, topk=3, so=True, n_sink=1, contract=True)
+
+
+@pytest.mark.parametrize("reorder", ["none", "morton"])
+def test_autograd_through_the_wrapper(reorder):
+    """piecewise_sparse_attention is differentiable: its gradients equal
+    pisa_attn_bwd's on the same routing bit for bit (through the Morton
+    reorder, whose adjoint is the inverse reorder)."""
+    w = wl("wan14", heads=2, grid=(3, 11, 31), seq_len=1023)
+    (q, k, v, do), _ = device_case(w, 19)
+    say(f"[gpu] autograd through piecewise_sparse_attention, reorder={reorder}")
+    if reorder == "morton":
+        perm = P.z_order(w.grid).cuda()
+        q, k, v, do = (P.reorder_scatter(t, perm) for t in (q, k, v, do))   # token-major raster inputs
+    leaves = [t.detach().clone().requires_grad_(True) for t in (q, k, v)]
+    kw = dict(density=0.25, variant="pwt", n_sink_blocks=1, reorder=reorder)
+    if reorder == "morton":
+        kw["grid"] = w.grid
+    o = P.piecewise_sparse_attention(*leaves, **kw)
+    o.backward(do)
+    # the same computation through the entry points
+    qq, kk, vv, dd = q, k, v, do
+    if reorder == "morton":
+        qq, kk, vv, dd = (P.reorder_gather(t, perm) for t in (q, k, v, do))
+    N = P.num_blocks(w.seq_len)
+    topk = P.topk_for_density(0.25, N)
+    st = P.pisa_block_stats(qq, kk, vv, second_order=True)
+    idx, wg = P.pisa_route_topk(qq, st, topk, band=1, second_order=True, n_sink=1)
+    oo = P.pisa_attn_fwd(qq, kk, vv, st, idx, wg, second_order=True, n_sink=1)
+    grads = P.pisa_attn_bwd(qq, kk, vv, oo, dd, st, idx, wg, second_order=True, n_sink=1)
+    if reorder == "morton":
+        grads = [P.reorder_scatter(g, perm) for g in grads]
+    torch.cuda.synchronize()
+    for leaf, g in zip(leaves, grads):
+        assert torch.equal(leaf.grad, g)

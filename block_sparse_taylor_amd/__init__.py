@@ -12,7 +12,10 @@ fused kernel Phases 1-3):
     idx, wg   = pisa_route_topk(q, stats, topk=..., band=1, second_order=...)
     o         = pisa_attn_fwd(q, k, v, stats, idx, wg, ...)
 
-``piecewise_sparse_attention`` chains them with topk = floor(density * N).
+and ``pisa_attn_bwd(q, k, v, o, dout, stats, idx, wg, ...)`` returns the
+gradients with the routing and gate held (the README's trainable regime).
+``piecewise_sparse_attention`` chains them with topk = floor(density * N)
+and is differentiable.
 """
 
 from __future__ import annotations

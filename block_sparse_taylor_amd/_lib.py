@@ -20,7 +20,7 @@ EXPORTED = (
     "pisa_abi_version", "pisa_status_str", "pisa_num_blocks", "pisa_stats_workspace_bytes",
     "pisa_block_stats", "pisa_route_topk", "pisa_attn_fwd", "pisa_attn_fwd_valu",
     "pisa_z_order", "pisa_reorder_gather", "pisa_reorder_scatter", "pisa_attn_bwd_workspace_bytes",
-    "pisa_attn_bwd",
+    "pisa_attn_bwd", "pisa_attn_fwd_plan",
 )
 
 
@@ -84,6 +84,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pisa_attn_bwd.restype = ctypes.c_int
     lib.pisa_attn_bwd.argtypes = [P(Shape), P(Params), vp, vp, vp, vp, vp, P(Stats), vp, vp, vp, vp, vp, vp,
                                   ctypes.c_size_t, vp]
+    lib.pisa_attn_fwd_plan.restype = ctypes.c_int
+    lib.pisa_attn_fwd_plan.argtypes = [P(Shape), P(Params), P(ctypes.c_int32), P(ctypes.c_int64)]
     lib.pisa_z_order.restype = ctypes.c_int
     lib.pisa_z_order.argtypes = [P(ctypes.c_int64), ctypes.c_int32, ctypes.c_int64, P(ctypes.c_int32),
                                  ctypes.c_int64]

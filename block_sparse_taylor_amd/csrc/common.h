@@ -111,6 +111,11 @@ hipError_t launch_attn_bwd(const Geom& g, int dtype, const pisa_params_t* p, con
                            const int32_t* idx, const float* wgate, void* dq, void* dk, void* dv, void* ws,
                            hipStream_t stream);
 
+// Kernel choice of pisa_attn_fwd (a pisa_attn_kernel_t) and the longest
+// per-wave item list of the persistent bf16 kernel for these parameters.
+int64_t attn_asm_wave_items(const Geom& g, const pisa_params_t* p);
+int attn_fwd_kernel(const Geom& g, int dtype, const pisa_params_t* p);
+
 hipError_t launch_attn_fwd_mfma(const Geom& g, const pisa_params_t* p, const void* q, const void* k,
                                 const void* v, const pisa_stats_t* st, const int32_t* idx,
                                 const float* wgate, void* o, hipStream_t stream);

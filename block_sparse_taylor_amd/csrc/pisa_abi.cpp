@@ -45,6 +45,15 @@ pisa_status_t check_params(const pisa_params_t* p, const Geom& g) {
     return PISA_OK;
 }
 
+// The parameters the kernels see: a band of N or more already makes every
+// block exact, so it is clamped to N (int arithmetic on i +- band stays in
+// range for any band the caller passes).
+pisa_params_t resolved(const pisa_params_t* p, const Geom& g) {
+    pisa_params_t r = *p;
+    if (r.band > g.N) r.band = g.N;
+    return r;
+}
+
 pisa_status_t check_ptr(const void* p) {
     if (!p) return PISA_ERR_NULL;
     return aligned16(p) ? PISA_OK : PISA_ERR_ALIGN;
@@ -162,7 +171,8 @@ pisa_status_t pisa_route_topk(const pisa_shape_t* shape, const pisa_params_t* pa
         PISA_TRY(check_ptr(wgate));
     }
     if (params->topk > 0) PISA_TRY(check_ptr(idx));
-    return from_hip(launch_route_topk(g, params, stats, idx, wgate, static_cast<hipStream_t>(stream)));
+    const pisa_params_t pr = resolved(params, g);
+    return from_hip(launch_route_topk(g, &pr, stats, idx, wgate, static_cast<hipStream_t>(stream)));
 }
 
 pisa_status_t pisa_attn_fwd(const pisa_shape_t* shape, const pisa_params_t* params, const void* q,
@@ -171,9 +181,10 @@ pisa_status_t pisa_attn_fwd(const pisa_shape_t* shape, const pisa_params_t* para
     Geom g;
     PISA_TRY(attn_common(shape, params, q, k, v, stats, idx, wgate, o, &g));
     hipStream_t s = static_cast<hipStream_t>(stream);
+    const pisa_params_t pr = resolved(params, g);
     if (shape->dtype == PISA_BF16)
-        return from_hip(launch_attn_fwd_mfma(g, params, q, k, v, stats, idx, wgate, o, s));
-    return from_hip(launch_attn_fwd_valu(g, shape->dtype, params, q, k, v, stats, idx, wgate, o, s));
+        return from_hip(launch_attn_fwd_mfma(g, &pr, q, k, v, stats, idx, wgate, o, s));
+    return from_hip(launch_attn_fwd_valu(g, shape->dtype, &pr, q, k, v, stats, idx, wgate, o, s));
 }
 
 pisa_status_t pisa_attn_fwd_valu(const pisa_shape_t* shape, const pisa_params_t* params,
@@ -182,8 +193,20 @@ pisa_status_t pisa_attn_fwd_valu(const pisa_shape_t* shape, const pisa_params_t*
                                  void* o, void* stream) {
     Geom g;
     PISA_TRY(attn_common(shape, params, q, k, v, stats, idx, wgate, o, &g));
-    return from_hip(launch_attn_fwd_valu(g, shape->dtype, params, q, k, v, stats, idx, wgate, o,
+    const pisa_params_t pr = resolved(params, g);
+    return from_hip(launch_attn_fwd_valu(g, shape->dtype, &pr, q, k, v, stats, idx, wgate, o,
                                          static_cast<hipStream_t>(stream)));
+}
+
+pisa_status_t pisa_attn_fwd_plan(const pisa_shape_t* shape, const pisa_params_t* params, int32_t* kernel,
+                                 int64_t* wave_items) {
+    Geom g;
+    PISA_TRY(check_shape(shape, &g));
+    PISA_TRY(check_params(params, g));
+    const pisa_params_t pr = resolved(params, g);
+    if (kernel) *kernel = attn_fwd_kernel(g, shape->dtype, &pr);
+    if (wave_items) *wave_items = attn_asm_wave_items(g, &pr);
+    return PISA_OK;
 }
 
 size_t pisa_attn_bwd_workspace_bytes(const pisa_shape_t* shape) {
@@ -215,7 +238,8 @@ pisa_status_t pisa_attn_bwd(const pisa_shape_t* shape, const pisa_params_t* para
         for (const void* in : ins)
             if (outs[a] == in) return PISA_ERR_PARAM;
     }
-    return from_hip(launch_attn_bwd(g, shape->dtype, params, q, k, v, o, dout, stats, idx, wgate, dq, dk,
+    const pisa_params_t pr = resolved(params, g);
+    return from_hip(launch_attn_bwd(g, shape->dtype, &pr, q, k, v, o, dout, stats, idx, wgate, dq, dk,
                                     dv, workspace, static_cast<hipStream_t>(stream)));
 }
 

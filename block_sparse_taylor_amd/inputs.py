@@ -15,6 +15,11 @@ stand in for them):
 * ``hunyuan`` Hunyuan-Video 720p: 24 heads, 33x45x80 grid (T=118800).
 * ``flux``    FLUX 1024^2: 24 heads, 512 text tokens (i.i.d. N(0,1)) then
               64x64 image tokens in 2D Morton order, T=4608.
+* ``wan14_kv`` a test case, not a benchmark: the Wan2.1-14B shape (8 heads)
+              with v built from the key noise (v[:, d] = eps_k[:, (d + 1) % D]),
+              so values follow the in-block key deviations and the global
+              first-order matrix sum_j (K_j - kbar_j)^T V_j grows like T
+              instead of averaging out.
 
 Spatially correlated q/k: per head a smooth field
 f_d(p) = sum_{m<8} a_{d,m} cos(2 pi w_m . p + phi_{d,m}) with integer
@@ -51,6 +56,7 @@ class Workload:
     grid: tuple = ()
     text_tokens: int = 0
     outlier_key_dims: tuple = ()
+    v_from_key_noise: bool = False
     block: int = 64
     note: str = field(default="", compare=False)
 
@@ -66,6 +72,8 @@ WORKLOADS = {
                         grid=(33, 45, 80)),
     "flux": Workload("flux", 1, 24, 4608, 128, "bf16", 0.15, 1, False, 4, "image",
                      grid=(64, 64), text_tokens=512),
+    "wan14_kv": Workload("wan14_kv", 1, 8, 32760, 128, "bf16", 0.125, 1, False, 5, "video",
+                         grid=(21, 30, 52), outlier_key_dims=(0, 1), v_from_key_noise=True),
 }
 
 
@@ -130,6 +138,8 @@ def make_head(w: Workload, b: int, h: int):
     k = ek.copy()
     q[n_text:] = f + 0.3 * eq[n_text:]
     k[n_text:] = f + 0.3 * ek[n_text:]
+    if w.v_from_key_noise:
+        v = np.roll(ek, -1, axis=1)
     for d in w.outlier_key_dims:
         k[:, d] *= 8.0
     return q, k, v

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define PISA_ABI_VERSION 9
+#define PISA_ABI_VERSION 10
 
 typedef enum {
     PISA_OK = 0,
@@ -221,6 +221,26 @@ pisa_status_t pisa_attn_fwd_valu(const pisa_shape_t *shape, const pisa_params_t 
                                  const void *q, const void *k, const void *v,
                                  const pisa_stats_t *stats, const int32_t *idx,
                                  const float *wgate, void *o, void *stream);
+
+/*
+ * pisa_attn_fwd_plan (HOST only, no GPU work): which kernel pisa_attn_fwd runs
+ * for this shape and these parameters, and the longest item list one wave of
+ * the persistent bf16 kernel would build.
+ *   kernel      PISA_KERNEL_VALU (fp32 inputs), PISA_KERNEL_MFMA_ASM (bf16,
+ *               head_dim 128, and every wave's list fits 256 items) or
+ *               PISA_KERNEL_MFMA (bf16 otherwise: head_dim 64, or lists too
+ *               long for the persistent kernel);
+ *   wave_items  ceil(E / 4) + ceil(G / 4) with E = min(N, 2 band + 1 +
+ *               n_sink) + topk (forced blocks and routed ids: the exact
+ *               items) and G = ceil(N / 64) (the virtual-token groups);
+ *               wave 0 takes every fourth item of each kind.
+ * Either output pointer may be NULL. Returns the validation status of shape
+ * and params (as pisa_attn_fwd checks them). A band larger than N is taken
+ * as N by every entry point.
+ */
+typedef enum { PISA_KERNEL_VALU = 0, PISA_KERNEL_MFMA_ASM = 1, PISA_KERNEL_MFMA = 2 } pisa_attn_kernel_t;
+pisa_status_t pisa_attn_fwd_plan(const pisa_shape_t *shape, const pisa_params_t *params,
+                                 int32_t *kernel, int64_t *wave_items);
 
 /*
  * Morton token reorder ("Piecewise-Taylor-Attention" README: the Wan2.1

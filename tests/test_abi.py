@@ -32,7 +32,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pisa_abi_version() == 9
+    assert lib.pisa_abi_version() == 10
     for code in range(9):
         assert lib.pisa_status_str(code)
     assert lib.pisa_status_str(99) == b"unknown status"
@@ -267,3 +267,64 @@ def test_reorder_validation(lib, name):
     assert fn(ctypes.byref(s), FAKE, FAKE, FAKE + 1024, None) == E["PISA_ERR_PARAM"]   # overlap
     assert fn(ctypes.byref(shape(D=96)), FAKE, FAKE, ok_dst, None) == E["PISA_ERR_SHAPE"]
     assert fn(ctypes.byref(shape(dtype=3)), FAKE, FAKE, ok_dst, None) == E["PISA_ERR_DTYPE"]
+
+
+def plan(lib, T, D, topk, band=1, n_sink=0, second_order=0, dtype=_lib.PISA_BF16, phase_mask=0):
+    sh = shape(T=T, D=D, dtype=dtype, H=1)
+    prm = _lib.Params(topk, band, second_order, 1, phase_mask, n_sink)
+    kern, items = ctypes.c_int32(-1), ctypes.c_int64(-1)
+    st = lib.pisa_attn_fwd_plan(ctypes.byref(sh), ctypes.byref(prm), ctypes.byref(kern), ctypes.byref(items))
+    return st, kern.value, items.value
+
+
+ASM, MFMA, VALU = 1, 2, 0
+
+
+@pytest.mark.parametrize("T,D,topk,band,n_sink,so,want_items,want_kernel", [
+    # Wan2.1-14B: 3 forced + 64 routed = 67 exact (17 on wave 0) + 8 groups (2)
+    (32760, 128, 64, 1, 0, 0, 19, ASM),
+    # Hunyuan: 3 + 232 = 235 (59) + 30 groups (8); second order changes nothing
+    (118800, 128, 232, 1, 0, 1, 67, ASM),
+    (118800, 128, 232, 1, 0, 0, 67, ASM),
+    # the window the persistent kernel must leave: N = 2048, 3 + 1000 exact
+    # (251 on wave 0) + 32 groups (8) = 259 > 256, with or without second order
+    (131072, 128, 1000, 1, 0, 1, 259, MFMA),
+    (131072, 128, 1000, 1, 0, 0, 259, MFMA),
+    # largest list that still fits: 3 + 989 = 992 (248) + 8 = 256
+    (131072, 128, 989, 1, 0, 1, 256, ASM),
+    (131072, 128, 990, 1, 0, 1, 257, MFMA),
+    # N = 8192, density 0.12: 3 + 983 (247) + 128 groups (32) = 279
+    (524288, 128, 983, 1, 0, 1, 279, MFMA),
+    # sinks count as forced blocks: N = 64, 3 + 32 + 4 = 39 (10) + 1 group (1)
+    (4096, 128, 4, 1, 32, 0, 11, ASM),
+    # ... but never more than N of them: N = 32, all forced, 32 + 4 = 36 (9) + 1
+    (2048, 128, 4, 1, 32, 0, 10, ASM),
+    # head_dim 64 always runs the C++ matrix-core kernel; fp32 the VALU kernel
+    (32760, 64, 64, 1, 0, 0, 19, MFMA),
+    (32760, 128, 64, 1, 0, 0, 19, VALU),
+])
+def test_attn_fwd_dispatch_rule(lib, T, D, topk, band, n_sink, so, want_items, want_kernel):
+    """pisa_attn_fwd_plan: the persistent bf16 kernel lists ceil(E/4) exact items
+    and ceil(G/4) virtual-token groups per wave in a 256-entry LDS list, so it is
+    chosen only where that bound fits, whatever the second-order switch says."""
+    dtype = _lib.PISA_F32 if want_kernel == VALU else _lib.PISA_BF16
+    st, kern, items = plan(lib, T, D, topk, band, n_sink, so, dtype)
+    assert st == 0
+    assert items == want_items
+    assert kern == want_kernel
+
+
+def test_attn_fwd_plan_clamps_band_and_validates(lib):
+    # a band beyond N makes every block forced: N exact items, clamped in
+    # 64-bit arithmetic (no int overflow for a band near 2^31)
+    N = 1857
+    for band in (N, N + 5, (1 << 31) - 1):
+        st, kern, items = plan(lib, 118800, 128, 0, band=band)
+        assert st == 0 and items == -(-N // 4) + -(-(-(-N // 64)) // 4)
+        assert kern == MFMA     # 465 + 8 > 256
+    assert plan(lib, 118800, 128, 0, band=-1)[0] == 4          # PISA_ERR_PARAM
+    assert plan(lib, 118800, 128, 1858)[0] == 4                 # topk > N
+    assert plan(lib, 0, 128, 0)[0] == 2                         # PISA_ERR_SHAPE
+    sh = shape(T=1024, D=128)
+    prm = _lib.Params(4, 1, 0, 1, 0, 0)
+    assert lib.pisa_attn_fwd_plan(ctypes.byref(sh), ctypes.byref(prm), None, None) == 0

@@ -182,8 +182,8 @@ def test_deterministic():
         assert torch.equal(x, y)
 
 
-@pytest.mark.parametrize("name,heads", [("wan14", (3, 29)), ("hunyuan", (5, 17))])
-def test_full_size(name, heads):
+@pytest.mark.parametrize("name,heads,dkdv_head", [("wan14", (3, 29), 3), ("hunyuan", (5, 17), None)])
+def test_full_size(name, heads, dkdv_head):
     """A workload of the bench in its launch configuration (every head, one
     call: the Wan2.1-14B shape, T = 32760; the Hunyuan shape, T = 118800 with
     the second order). Checked: dq of sampled query blocks of two heads
@@ -193,7 +193,13 @@ def test_full_size(name, heads):
     do not change), so sum_k dk = 0; shifting every value by one vector shifts
     every output by it (H does not change since sum (k - kbar) = 0 per
     block), so sum_k dv = sum_t dout_t. Both sums are compared within 2^-7 of
-    sum |.| (bf16 rounding of each term, 2^-9, with fp32 accumulation)."""
+    sum |.| (bf16 rounding of each term, 2^-9, with fp32 accumulation).
+    At the Wan2.1-14B shape one head's dk and dv are also compared element
+    by element on sampled KV blocks with the oracle's full-head gradient for
+    the o the backward was handed (the contract bar): a KV block's gradient
+    collects every query block that attends to it exactly and, through the
+    block mean, V-hat and H, every query block, so it needs the whole head
+    (about half a minute of float64 autograd on the host)."""
     from gpu_common import head_f64, oracle_topk, workload_inputs
     say(f"[gpu] bwd full size {name}: inputs")
     w, arrs = workload_inputs(name)
@@ -229,6 +235,20 @@ def test_full_size(name, heads):
         e = np.abs(got - ref).max() / np.abs(ref).max()
         say(f"[gpu]   head {h} blocks {blocks}: dq normalised error {e:.2e}")
         assert e <= TOL[("bf16", False)], (h, blocks, e)
+    if dkdv_head is not None:
+        h = dkdv_head
+        qh, kh, vh = head_f64(arrs, w.dtype, 0, h)
+        doh = I.as_f64(dbits[0, h], "bf16")
+        oh = o[0, h].double().cpu().numpy()
+        say(f"[gpu]   head {h}: full-head gradient oracle for dk, dv")
+        _, rdk, rdv = BO.grads(qh, kh, vh, doh, ih[0, h], o_used=oh, B=64, scale=s, band=w.band, second_order=so)
+        kvb = [0, 1, int(r.integers(2, N - 2)), int(r.integers(2, N - 2)), N - 2, N - 1]
+        rows = np.concatenate([np.arange(64 * j, min(w.seq_len, 64 * j + 64)) for j in kvb])
+        for nm, got_t, ref in (("dk", dk, rdk), ("dv", dv, rdv)):
+            got = got_t[0, h].double().cpu().numpy()[rows]
+            e = np.abs(got - ref[rows]).max() / np.abs(ref[rows]).max()
+            say(f"[gpu]   head {h} KV blocks {kvb}: {nm} normalised error {e:.2e}")
+            assert e <= TOL[("bf16", True)], (nm, h, kvb, e)
 
 
 def test_bf16_single_block_of_twenty_rows_contract():

@@ -157,8 +157,8 @@ def test_mfma_matches_valu_reference():
 
 @pytest.mark.parametrize("second_order", [False, True])
 def test_long_sequence_routing(second_order):
-    """N above the LDS-resident score-row limit (1920 blocks) takes the
-    per-query-block routing path; its table must equal the oracle's."""
+    """N = 1938 blocks: the fast router's widest variant (36 keys per lane,
+    score rows near the LDS limit); its table must equal the oracle's."""
     T, D = 124000, 64
     N = -(-T // 64)
     topk = 24
@@ -263,3 +263,92 @@ def test_sink_blocks_match_oracle(T, D, dtype, topk, band, n_sink, second_order)
         if topk:
             assert np.array_equal(idx_h[0, h], parts["idx"])
         tol_check(o[0, h], ref, dtype)
+
+
+def attn_plan(T, D, topk, band=1, n_sink=0, second_order=False, dtype=None):
+    """(kernel, per-wave items) that pisa_attn_fwd picks (pisa_attn_fwd_plan)."""
+    import ctypes
+    from block_sparse_taylor_amd import _lib
+    sh = _lib.Shape(1, 1, T, D, 64, _lib.PISA_BF16 if dtype != "f32" else _lib.PISA_F32, 0.0)
+    prm = _lib.Params(topk, band, int(second_order), 1, 0, n_sink)
+    kern, items = ctypes.c_int32(-1), ctypes.c_int64(-1)
+    _lib.check("pisa_attn_fwd_plan", P.library().pisa_attn_fwd_plan(
+        ctypes.byref(sh), ctypes.byref(prm), ctypes.byref(kern), ctypes.byref(items)))
+    return kern.value, items.value
+
+
+@pytest.mark.parametrize("topk,kernel", [(989, 1), (1000, 2)])
+def test_long_item_lists_second_order(topk, kernel):
+    """One head, T = 131000 (N = 2047, last block 56 rows), D = 128, bf16, with
+    the second-order term. topk 989: wave 0 lists 3 + 989 exact items (248) and
+    8 virtual groups, exactly the persistent kernel's 256-entry list. topk 1000:
+    259 items, more than the list holds, so the C++ matrix-core kernel runs
+    (an earlier launcher left the virtual groups out of this bound with the
+    second order on and overflowed the list). Sampled query blocks, the ragged
+    last one included, against the oracle fed the GPU's routing; the routing
+    itself against the oracle's."""
+    T, D, band = 131000, 128, 1
+    N = -(-T // 64)
+    kern, items = attn_plan(T, D, topk, band, second_order=True)
+    assert kern == kernel, (kern, items)
+    say(f"[gpu] long item lists T={T} topk={topk} kernel={kern} wave items={items}")
+    (q, k, v), (qh, kh, vh) = make(T, D, "bf16", 1000 + topk, H=1)
+    st, idx, wg, o = run_all(q, k, v, topk, band, second_order=True)
+    idx_h = idx.cpu().numpy()
+    s = 1 / math.sqrt(D)
+    ks = O.kv_block_stats(kh[0, 0], vh[0, 0], 64)
+    qbar, q2bar = O.pool_queries(qh[0, 0], 64, s)
+    wr = O.second_order_w(q2bar, ks.sig2, 64)[2]
+    ref_idx, _ = O.route_topk(qbar, ks.kbar, s, topk, band, wr)
+    assert np.array_equal(idx_h[0, 0], ref_idx)
+    blocks = [0, 1, 2, 511, 1023, 1024, 1500, N - 2, N - 1]
+    ref = O.pisa_forward_head(qh[0, 0], kh[0, 0], vh[0, 0], topk=topk, band=band, second_order=True,
+                              routing=idx_h[0, 0], query_blocks=blocks)
+    rows = np.isfinite(ref[:, 0])
+    got = o[0, 0].double().cpu().numpy()[rows]
+    assert np.isfinite(got).all()
+    err = float(np.abs(got - ref[rows]).max())
+    say(f"[gpu] long item lists topk={topk}: max abs error {err:.3e} over {len(blocks)} query blocks")
+    assert err <= 2e-2, err
+
+
+@pytest.mark.parametrize("second_order", [False, True])
+def test_slow_router_beyond_lds_rows(second_order):
+    """N = 2500 blocks (T = 160000) is beyond the fast router's 36 keys per
+    lane (N <= 2304), so route_slow_kernel scores every candidate in fp64.
+    Every row of its table against the oracle's (differences allowed only
+    where the oracle's score gap to the k-th candidate is below 1e-6, and
+    counted), and with the second order the gated table's decisions."""
+    T, D, band = 160000, 128, 1
+    N = -(-T // 64)
+    topk = int(np.floor(0.125 * N))
+    say(f"[gpu] slow router T={T} N={N} topk={topk} so={second_order}")
+    (q, k, v), (qh, kh, vh) = make(T, D, "bf16", 4242, H=1)
+    st = P.pisa_block_stats(q, k, v, second_order=second_order)
+    idx, wg = P.pisa_route_topk(q, st, topk, band=band, second_order=second_order)
+    torch.cuda.synchronize()
+    s = 1 / math.sqrt(D)
+    ks = O.kv_block_stats(kh[0, 0], vh[0, 0], 64)
+    qbar, q2bar = O.pool_queries(qh[0, 0], 64, s)
+    wraw, wgr, wr = O.second_order_w(q2bar, ks.sig2, 64) if second_order else (None, None, None)
+    ref, r = O.route_topk(qbar, ks.kbar, s, topk, band, wr)
+    got = idx.cpu().numpy()[0, 0]
+    diffs = 0
+    for i in range(N):
+        if np.array_equal(got[i], ref[i]):
+            continue
+        gs, rs = set(got[i][got[i] >= 0].tolist()), set(ref[i][ref[i] >= 0].tolist())
+        assert len(gs) == len(rs) and sorted(gs) == got[i][got[i] >= 0].tolist(), i
+        kth = min(r[i, j] for j in rs)
+        for j in gs ^ rs:
+            assert abs(r[i, j] - kth) < 1e-6, (i, j, r[i, j], kth)
+        diffs += len(gs - rs)
+    say(f"[gpu] slow router so={second_order}: {diffs} near-tie differences over {N} rows")
+    if second_order:
+        lnB = math.log(64)
+        w_gpu = wg.cpu().numpy()[0, 0]
+        near = np.abs(wraw - lnB) < 1e-9
+        gated = wraw > lnB
+        assert ((w_gpu == 0) | ~gated | near).all()
+        tol = 2 * (D + 4) * 2.0 ** -24 * wraw + 1e-30
+        assert ((np.abs(w_gpu - wgr) <= tol) | gated | near).all()

@@ -286,6 +286,72 @@ def test_router_uses_clamped_spread():
     assert idx_raw.tolist() == [[1]]
 
 
+def _pooling_case():
+    """T = 14 tokens, B = 4, D = 2, s = 1/2: blocks 0-2 full, block 3 ragged
+    (two rows). Query block 3 holds rows (1, 1) and (3, -1); key blocks:
+      0: four rows (1.3, 0)                      kbar (1.3, 0), sigma^2 (0, 0)
+      1: (1.3, 0), (-1.3, 0), (1.3, 0), (-1.3, 0) kbar (0, 0),   sigma^2 (1.69, 0)
+      2: (1.8, 0), (0.2, 0), (1.8, 0), (0.2, 0)   kbar (1, 0),   sigma^2 (0.64, 0)
+      3: (0, 0), (0, 0)."""
+    k = np.zeros((14, 2))
+    k[0:4, 0] = 1.3
+    k[4:8, 0] = [1.3, -1.3, 1.3, -1.3]
+    k[8:12, 0] = [1.8, 0.2, 1.8, 0.2]
+    q = np.zeros((14, 2))
+    q[0:12] = np.arange(24).reshape(12, 2) / 8.0
+    q[12] = [1.0, 1.0]
+    q[13] = [3.0, -1.0]
+    return q, k, np.zeros((14, 2))
+
+
+def test_pooled_queries_hand_worked_ragged_block():
+    """qbar_i is the mean of the block's query rows and q2bar_i the mean of
+    their squares after the softmax scale ([PISA] Algorithm 1 step 1 and
+    Fig. 4: block means; [PWT] "Blog post": q^2 pooled per query block), both
+    over the n_i rows present (R6). Worked by hand for the ragged block 3
+    (rows (1, 1), (3, -1)) and the full block 0 (rows (0, 1/8), (2/8, 3/8),
+    (4/8, 5/8), (6/8, 7/8))."""
+    q, _, _ = _pooling_case()
+    qbar, q2bar = O.pool_queries(q, 4, 0.5)
+    assert qbar.shape == (4, 2)
+    assert qbar[3].tolist() == [2.0, 0.0]
+    # s^2 * mean of squares: 0.25 * ((1 + 9) / 2, (1 + 1) / 2)
+    assert q2bar[3].tolist() == [1.25, 0.25]
+    assert qbar[0].tolist() == [12 / 32, 16 / 32]
+    # 0.25 * (0 + 4 + 16 + 36) / (4 * 64), 0.25 * (1 + 9 + 25 + 49) / (4 * 64)
+    np.testing.assert_allclose(q2bar[0], [56 / 1024, 84 / 1024], rtol=1e-15)
+
+
+def test_pooled_query_scale_decides_second_order_routing():
+    """With the second-order term the routing score s qbar_i . kbar_j +
+    min(w_ij, ln B) compares the pooled mean against the spread, so the scale of
+    qbar matters ([PISA] Algorithm 1 step 2 with Eq. 11's pooled score;
+    [PWT] router: min(w, ln B)). Query block 3 (ragged, n = 2), band 0,
+    top-1 over key blocks 0, 1, 2, worked by hand:
+      s qbar_3 . kbar_j = 0.5 * 2 * kbar_j0 = 1.3, 0, 1.0
+      w_3j = 0.5 (1.25 sigma^2_j0 + 0.25 sigma^2_j1) = 0, 1.05625, 0.4
+      r_3j = 1.3, 1.05625, 1.4  -> block 2.
+    A qbar too large by the row count (a sum: x2) picks block 0 (2.6 > 2.4);
+    one too small by half (s q instead of q, or dividing the two rows by B = 4
+    instead of n = 2) picks block 1 (0.65, 1.05625, 0.9)."""
+    q, k, v = _pooling_case()
+    B, s = 4, 0.5
+    st = O.kv_block_stats(k, v, B)
+    assert st.kbar[:3, 0].tolist() == [1.3, 0.0, 1.0]
+    np.testing.assert_allclose(st.sig2[:3, 0], [0.0, 1.69, 0.64], atol=1e-15)
+    qbar, q2bar = O.pool_queries(q, B, s)
+    w, wg, wr = O.second_order_w(q2bar, st.sig2, B)
+    np.testing.assert_allclose(w[3, :3], [0.0, 1.05625, 0.4], atol=1e-15)
+    idx, r = O.route_topk(qbar, st.kbar, s, 1, band=0, w_rank=wr)
+    np.testing.assert_allclose(r[3, :3], [1.3, 1.05625, 1.4], atol=1e-15)
+    assert idx[3].tolist() == [2]
+    # the case tells the plausible mis-scalings of qbar apart
+    for factor, want in ((2.0, 0), (0.5, 1)):
+        bad = qbar.copy()
+        bad[3] *= factor
+        assert O.route_topk(bad, st.kbar, s, 1, band=0, w_rank=wr)[0][3].tolist() == [want]
+
+
 # ---------------------------------------------------------------- routing
 
 def test_routing_known_ranking_band_ties_padding():

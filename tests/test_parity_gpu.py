@@ -199,11 +199,10 @@ def check_routing(name, run, heads):
 def test_route_topk(name):
     run = get_run(name)
     w = run.w
-    full, extra = sample_plan(name, w, run.N)
-    heads = sorted(set(full) | {h for h, _ in extra})[:6]
-    say(f"[gpu] routing parity {name} heads {heads}")
+    heads = list(range(w.heads))      # every head of every workload
+    say(f"[gpu] routing parity {name}: all {len(heads)} heads")
     diffs = check_routing(name, run, heads)
-    say(f"[gpu] routing {name}: {diffs} near-tie differences")
+    say(f"[gpu] routing {name}: {diffs} near-tie differences over {len(heads)} heads x {run.N} rows")
     if w.second_order:
         wg = run.wg.cpu().numpy()
         lnB = math.log(64)

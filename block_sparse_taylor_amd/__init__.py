@@ -12,6 +12,10 @@ fused kernel Phases 1-3):
     idx, wg   = pisa_route_topk(q, stats, topk=..., band=1, second_order=...)
     o         = pisa_attn_fwd(q, k, v, stats, idx, wg, ...)
 
+``stats`` holds the paper's statistics and the operand buffer the kernels
+read; ``pisa_prepare_operands(k, stats)`` builds that buffer from statistics
+computed by any other means.
+
 and ``pisa_attn_bwd(q, k, v, o, dout, stats, idx, wg, ...)`` returns the
 gradients with the routing and gate held (the README's trainable regime).
 ``piecewise_sparse_attention`` chains them with topk = floor(density * N)
@@ -29,7 +33,7 @@ import torch
 from . import _lib
 from ._lib import PISA_BF16, PISA_F32, PisaError
 
-__all__ = ["PisaStats", "pisa_block_stats", "pisa_route_topk", "pisa_attn_fwd",
+__all__ = ["PisaStats", "pisa_block_stats", "pisa_prepare_operands", "pisa_route_topk", "pisa_attn_fwd",
            "pisa_attn_fwd_valu", "pisa_attn_bwd", "piecewise_sparse_attention", "num_blocks", "topk_for_density",
            "z_order", "reorder_gather", "reorder_scatter", "PisaError", "library"]
 
@@ -74,25 +78,23 @@ def topk_for_density(density: float, n_blocks: int) -> int:
 
 @dataclass
 class PisaStats:
-    qbar: torch.Tensor      # fp64 [B,H,N,D]
-    q2bar: torch.Tensor | None
-    kbar: torch.Tensor      # fp64 [B,H,N,D]
-    vsum: torch.Tensor      # fp32 [B,H,N,D]
-    ksig2: torch.Tensor | None
-    hsum: torch.Tensor      # fp32 [B,H,D,D]
-    kbar_c: torch.Tensor    # input dtype [B,H,N,D]
-    vbar_c: torch.Tensor
-    kpack: torch.Tensor | None   # bf16 [B,H,N,64*D]: K in the fused kernel's operand order
-    hpack: torch.Tensor | None   # bf16 [B,H,2*D*D]: hsum split hi + lo in the fused kernel's operand order
-    kbpack: torch.Tensor | None  # bf16 [B,H,ceil(N/64),64*D]: kbar_c per group of 64 blocks, in kpack's order
-    kbar_r: torch.Tensor         # fp32 [B,H,ceil(N/16)*16*D]: kbar in the router's operand order
-    ksig2_r: torch.Tensor | None  # second order: ksig2 in fp32, the same order
+    """The paper's block statistics (pisa_stats_t) and the operand buffer the
+    routing and attention kernels read (opaque, built from them)."""
+    qbar: torch.Tensor | None     # fp64 [B,H,N,D]
+    q2bar: torch.Tensor | None    # fp64 [B,H,N,D] (second order)
+    kbar: torch.Tensor            # fp64 [B,H,N,D]
+    vsum: torch.Tensor            # fp32 [B,H,N,D]
+    ksig2: torch.Tensor | None    # fp64 [B,H,N,D] (second order)
+    hsum: torch.Tensor            # fp32 [B,H,D,D]
+    operands: torch.Tensor | None = None   # uint8 [pisa_operands_bytes]
 
     def as_c(self) -> _lib.Stats:
         return _lib.Stats(_ptr(self.qbar), _ptr(self.q2bar), _ptr(self.kbar), _ptr(self.vsum),
-                          _ptr(self.ksig2), _ptr(self.hsum), _ptr(self.kbar_c), _ptr(self.vbar_c),
-                          _ptr(self.kpack), _ptr(self.hpack), _ptr(self.kbpack),
-                          _ptr(self.kbar_r), _ptr(self.ksig2_r))
+                          _ptr(self.ksig2), _ptr(self.hsum))
+
+    def statistics_only(self) -> "PisaStats":
+        """The same statistics without the operand buffer (what the backward reads)."""
+        return PisaStats(self.qbar, self.q2bar, self.kbar, self.vsum, self.ksig2, self.hsum, None)
 
 
 def _contig(*ts):
@@ -101,27 +103,46 @@ def _contig(*ts):
             raise ValueError("tensors must be contiguous")
 
 
-def alloc_stats(k: torch.Tensor, second_order: bool) -> PisaStats:
+def operands_bytes(x: torch.Tensor, scale=None) -> int:
+    return int(library().pisa_operands_bytes(ctypes.byref(_shape(x, scale))))
+
+
+def alloc_operands(x: torch.Tensor) -> torch.Tensor:
+    return torch.empty(max(16, operands_bytes(x)), dtype=torch.uint8, device=x.device)
+
+
+def alloc_stats(k: torch.Tensor, second_order: bool, operands: bool = True) -> PisaStats:
     B, H, T, D = k.shape
     N = num_blocks(T)
     dev = k.device
+    f64 = dict(dtype=torch.float64, device=dev)
     return PisaStats(
-        qbar=torch.empty(B, H, N, D, dtype=torch.float64, device=dev),
-        q2bar=torch.empty(B, H, N, D, dtype=torch.float64, device=dev) if second_order else None,
-        kbar=torch.empty(B, H, N, D, dtype=torch.float64, device=dev),
+        qbar=torch.empty(B, H, N, D, **f64),
+        q2bar=torch.empty(B, H, N, D, **f64) if second_order else None,
+        kbar=torch.empty(B, H, N, D, **f64),
         vsum=torch.empty(B, H, N, D, dtype=torch.float32, device=dev),
-        ksig2=torch.empty(B, H, N, D, dtype=torch.float64, device=dev) if second_order else None,
+        ksig2=torch.empty(B, H, N, D, **f64) if second_order else None,
         hsum=torch.empty(B, H, D, D, dtype=torch.float32, device=dev),
-        kbar_c=torch.empty(B, H, N, D, dtype=k.dtype, device=dev),
-        vbar_c=torch.empty(B, H, N, D, dtype=k.dtype, device=dev),
-        kpack=torch.empty(B, H, N, BLOCK * D, dtype=k.dtype, device=dev) if k.dtype == torch.bfloat16 else None,
-        hpack=torch.empty(B, H, 2 * D * D, dtype=k.dtype, device=dev) if k.dtype == torch.bfloat16 else None,
-        kbpack=(torch.empty(B, H, -(-N // BLOCK), BLOCK * D, dtype=k.dtype, device=dev)
-                if k.dtype == torch.bfloat16 else None),
-        kbar_r=torch.empty(B, H, -(-N // 16) * 16 * D, dtype=torch.float32, device=dev),
-        ksig2_r=(torch.empty(B, H, -(-N // 16) * 16 * D, dtype=torch.float32, device=dev)
-                 if second_order else None),
+        operands=alloc_operands(k) if operands else None,
     )
+
+
+def operand_views(stats: PisaStats, like: torch.Tensor) -> dict:
+    """Views of the arrangements inside stats.operands (pisa_operands_offsets),
+    for diagnostics and tests: name -> flat tensor of its element type."""
+    lib = library()
+    sh = _shape(like, None)
+    off = (ctypes.c_int64 * len(_lib.OPERANDS))()
+    _lib.check("pisa_operands_offsets", lib.pisa_operands_offsets(ctypes.byref(sh), off))
+    ends = list(off[1:]) + [operands_bytes(like)]
+    el = {"kbar_c": like.dtype, "vbar_c": like.dtype, "kbar_r": torch.float32, "ksig2_r": torch.float32,
+          "kpack": torch.bfloat16, "kbpack": torch.bfloat16, "hpack": torch.bfloat16}
+    out = {}
+    for n, name in enumerate(_lib.OPERANDS):
+        raw = stats.operands[off[n]:ends[n]]
+        size = torch.empty(0, dtype=el[name]).element_size()
+        out[name] = raw[: raw.numel() // size * size].view(el[name])
+    return out
 
 
 def stats_workspace(k: torch.Tensor, scale=None) -> torch.Tensor:
@@ -137,13 +158,38 @@ def pisa_block_stats(q, k, v, second_order=False, scale=None, out: PisaStats | N
     _contig(q, k, v)
     sh = _shape(k, scale)
     out = out or alloc_stats(k, second_order)
+    if out.operands is None:
+        out.operands = alloc_operands(k)
     ws = workspace if workspace is not None else stats_workspace(k, scale)
     prm = _lib.Params(0, 0, int(second_order), 1, 0)
     cs = out.as_c()
     _lib.check("pisa_block_stats", lib.pisa_block_stats(
-        ctypes.byref(sh), ctypes.byref(prm), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(cs), _ptr(ws),
-        ws.numel(), _stream(k.device)))
+        ctypes.byref(sh), ctypes.byref(prm), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(cs),
+        _ptr(out.operands), out.operands.numel(), _ptr(ws), ws.numel(), _stream(k.device)))
     return out
+
+
+def pisa_prepare_operands(k, stats: PisaStats, second_order=False, scale=None) -> PisaStats:
+    """Fill stats.operands from the statistics in `stats` (any source) and k."""
+    lib = library()
+    _contig(k, stats.kbar, stats.vsum, stats.hsum, stats.ksig2)
+    sh = _shape(k, scale)
+    if stats.operands is None:
+        stats.operands = alloc_operands(k)
+    prm = _lib.Params(0, 0, int(second_order), 1, 0)
+    cs = stats.as_c()
+    _lib.check("pisa_prepare_operands", lib.pisa_prepare_operands(
+        ctypes.byref(sh), ctypes.byref(prm), _ptr(k), ctypes.byref(cs), _ptr(stats.operands),
+        stats.operands.numel(), _stream(k.device)))
+    return stats
+
+
+def _operands(stats, required):
+    if stats.operands is None:
+        if required:
+            raise ValueError("stats carry no operand buffer: run pisa_block_stats or pisa_prepare_operands")
+        return None, 0
+    return _ptr(stats.operands), stats.operands.numel()
 
 
 def pisa_route_topk(q, stats: PisaStats, topk: int, band: int = 1, second_order=False, scale=None,
@@ -159,8 +205,9 @@ def pisa_route_topk(q, stats: PisaStats, topk: int, band: int = 1, second_order=
         wgate = torch.empty(B, H, N, N, dtype=torch.float32, device=q.device)
     prm = _lib.Params(int(topk), int(band), int(second_order), 1, 0, int(n_sink))
     cs = stats.as_c()
+    ops, nops = _operands(stats, True)
     _lib.check("pisa_route_topk", lib.pisa_route_topk(
-        ctypes.byref(sh), ctypes.byref(prm), ctypes.byref(cs),
+        ctypes.byref(sh), ctypes.byref(prm), ctypes.byref(cs), ops, nops,
         _ptr(idx) if topk else None, _ptr(wgate) if second_order else None, _stream(q.device)))
     return idx, (wgate if second_order else None)
 
@@ -174,9 +221,10 @@ def _attn(fn_name, q, k, v, stats, idx, wgate, topk, band, second_order, first_o
     prm = _lib.Params(int(topk), int(band), int(second_order), int(first_order), int(phase_mask),
                       int(n_sink))
     cs = stats.as_c()
+    ops, nops = _operands(stats, fn_name == "pisa_attn_fwd" and q.dtype == torch.bfloat16)
     fn = getattr(lib, fn_name)
     _lib.check(fn_name, fn(ctypes.byref(sh), ctypes.byref(prm), _ptr(q), _ptr(k), _ptr(v),
-                           ctypes.byref(cs), _ptr(idx) if topk else None,
+                           ctypes.byref(cs), ops, nops, _ptr(idx) if topk else None,
                            _ptr(wgate) if second_order else None, _ptr(o), _stream(q.device)))
     return o
 
@@ -270,16 +318,18 @@ class _Attention(torch.autograd.Function):
         idx = idx if topk else None
         o = pisa_attn_fwd(q, k, v, st, idx, wg, band=band, second_order=second_order, scale=scale,
                           n_sink=n_sink)
-        ctx.save_for_backward(q, k, v, o)
-        ctx.st, ctx.idx, ctx.wg = st, idx, wg
+        # the backward reads the statistics (not the operand buffer), the
+        # routing table and the gated table: kept as saved tensors
+        ctx.save_for_backward(q, k, v, o, st.kbar, st.vsum, st.hsum, st.q2bar, st.ksig2, idx, wg)
         ctx.cfg = (band, second_order, scale, n_sink)
         return o
 
     @staticmethod
     def backward(ctx, do):
-        q, k, v, o = ctx.saved_tensors
+        q, k, v, o, kbar, vsum, hsum, q2bar, ksig2, idx, wg = ctx.saved_tensors
         band, so, scale, n_sink = ctx.cfg
-        dq, dk, dv = pisa_attn_bwd(q, k, v, o, do.contiguous(), ctx.st, ctx.idx, ctx.wg, band=band,
+        st = PisaStats(None, q2bar, kbar, vsum, ksig2, hsum, None)
+        dq, dk, dv = pisa_attn_bwd(q, k, v, o, do.contiguous(), st, idx, wg, band=band,
                                    second_order=so, scale=scale, n_sink=n_sink)
         return dq, dk, dv, None, None, None, None, None
 

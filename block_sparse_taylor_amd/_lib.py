@@ -20,8 +20,11 @@ EXPORTED = (
     "pisa_abi_version", "pisa_status_str", "pisa_num_blocks", "pisa_stats_workspace_bytes",
     "pisa_block_stats", "pisa_route_topk", "pisa_attn_fwd", "pisa_attn_fwd_valu",
     "pisa_z_order", "pisa_reorder_gather", "pisa_reorder_scatter", "pisa_attn_bwd_workspace_bytes",
-    "pisa_attn_bwd", "pisa_attn_fwd_plan",
+    "pisa_attn_bwd", "pisa_attn_fwd_plan", "pisa_operands_bytes", "pisa_operands_offsets",
+    "pisa_prepare_operands",
 )
+# pisa_operand_t: the arrangements inside the operand buffer
+OPERANDS = ("kbar_c", "vbar_c", "kbar_r", "ksig2_r", "kpack", "kbpack", "hpack")
 
 
 class Shape(ctypes.Structure):
@@ -38,10 +41,7 @@ class Params(ctypes.Structure):
 
 class Stats(ctypes.Structure):
     _fields_ = [("qbar", ctypes.c_void_p), ("q2bar", ctypes.c_void_p), ("kbar", ctypes.c_void_p),
-                ("vsum", ctypes.c_void_p), ("ksig2", ctypes.c_void_p), ("hsum", ctypes.c_void_p),
-                ("kbar_c", ctypes.c_void_p), ("vbar_c", ctypes.c_void_p), ("kpack", ctypes.c_void_p),
-                ("hpack", ctypes.c_void_p), ("kbpack", ctypes.c_void_p),
-                ("kbar_r", ctypes.c_void_p), ("ksig2_r", ctypes.c_void_p)]
+                ("vsum", ctypes.c_void_p), ("ksig2", ctypes.c_void_p), ("hsum", ctypes.c_void_p)]
 
 
 class PisaError(RuntimeError):
@@ -71,14 +71,21 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pisa_num_blocks.argtypes = [P(Shape)]
     lib.pisa_stats_workspace_bytes.restype = ctypes.c_size_t
     lib.pisa_stats_workspace_bytes.argtypes = [P(Shape)]
+    lib.pisa_operands_bytes.restype = ctypes.c_size_t
+    lib.pisa_operands_bytes.argtypes = [P(Shape)]
+    lib.pisa_operands_offsets.restype = ctypes.c_int
+    lib.pisa_operands_offsets.argtypes = [P(Shape), P(ctypes.c_int64)]
     lib.pisa_block_stats.restype = ctypes.c_int
-    lib.pisa_block_stats.argtypes = [P(Shape), P(Params), vp, vp, vp, P(Stats), vp, ctypes.c_size_t, vp]
+    lib.pisa_block_stats.argtypes = [P(Shape), P(Params), vp, vp, vp, P(Stats), vp, ctypes.c_size_t, vp,
+                                     ctypes.c_size_t, vp]
+    lib.pisa_prepare_operands.restype = ctypes.c_int
+    lib.pisa_prepare_operands.argtypes = [P(Shape), P(Params), vp, P(Stats), vp, ctypes.c_size_t, vp]
     lib.pisa_route_topk.restype = ctypes.c_int
-    lib.pisa_route_topk.argtypes = [P(Shape), P(Params), P(Stats), vp, vp, vp]
+    lib.pisa_route_topk.argtypes = [P(Shape), P(Params), P(Stats), vp, ctypes.c_size_t, vp, vp, vp]
     for name in ("pisa_attn_fwd", "pisa_attn_fwd_valu"):
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
-        fn.argtypes = [P(Shape), P(Params), vp, vp, vp, P(Stats), vp, vp, vp, vp]
+        fn.argtypes = [P(Shape), P(Params), vp, vp, vp, P(Stats), vp, ctypes.c_size_t, vp, vp, vp, vp]
     lib.pisa_attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.pisa_attn_bwd_workspace_bytes.argtypes = [P(Shape)]
     lib.pisa_attn_bwd.restype = ctypes.c_int

@@ -703,7 +703,7 @@ BwdLayout bwd_layout(const Geom& g, bool mfma) {
 
 template <typename T, int D>
 hipError_t run_bwd(const Geom& g, const pisa_params_t* p, const void* q, const void* k, const void* v,
-                   const void* o, const void* dout, const pisa_stats_t* st, const int32_t* idx,
+                   const void* o, const void* dout, const StatsView* st, const int32_t* idx,
                    const float* wgate, void* dq, void* dk, void* dv, void* ws, hipStream_t stream) {
     constexpr bool kMfma = std::is_same<T, bf16_t>::value;
     const BwdLayout L = bwd_layout(g, kMfma);
@@ -777,7 +777,7 @@ hipError_t run_bwd(const Geom& g, const pisa_params_t* p, const void* q, const v
 size_t attn_bwd_workspace_bytes(const Geom& g, int dtype) { return bwd_layout(g, dtype == PISA_BF16).total; }
 
 hipError_t launch_attn_bwd(const Geom& g, int dtype, const pisa_params_t* p, const void* q, const void* k,
-                           const void* v, const void* o, const void* dout, const pisa_stats_t* st,
+                           const void* v, const void* o, const void* dout, const StatsView* st,
                            const int32_t* idx, const float* wgate, void* dq, void* dk, void* dv, void* ws,
                            hipStream_t stream) {
     if (dtype == PISA_BF16) {

@@ -992,7 +992,7 @@ int bwd_virt_splits(const Geom& g) {
     return s < 1 ? 1 : (s > 8 ? 8 : (s > g.N ? g.N : s));
 }
 
-hipError_t launch_bwd_virt_mfma(const Geom& g, const bf16_t* q, const bf16_t* dout, const pisa_stats_t* st,
+hipError_t launch_bwd_virt_mfma(const Geom& g, const bf16_t* q, const bf16_t* dout, const StatsView* st,
                                 const uint32_t* mask, const f32x4_t* rowstat, const float* wgate, float* dkb_part,
                                 float* dvh_part, float* dw, float* dsg, int NW, int second_order,
                                 hipStream_t stream) {
@@ -1011,7 +1011,7 @@ hipError_t launch_bwd_virt_mfma(const Geom& g, const bf16_t* q, const bf16_t* do
     return hipGetLastError();
 }
 
-hipError_t launch_bwd_prep(const Geom& g, const pisa_stats_t* st, bf16_t* kbh, bf16_t* kbl, bf16_t* vhh,
+hipError_t launch_bwd_prep(const Geom& g, const StatsView* st, bf16_t* kbh, bf16_t* kbl, bf16_t* vhh,
                            bf16_t* vhl, bf16_t* hh, bf16_t* hl, hipStream_t stream) {
     hipLaunchKernelGGL(bwd_prep_kernel, dim3(g.N + 1, (unsigned)g.BH), dim3(kThreads), 0, stream, st->kbar, st->vsum,
                        st->hsum, kbh, kbl, vhh, vhl, hh, hl, g.N, g.D);
@@ -1050,7 +1050,7 @@ hipError_t launch_bwd_dq(const Geom& g, const bf16_t* q, const bf16_t* k, const 
 }
 
 hipError_t launch_bwd_dkdv(const Geom& g, const bf16_t* q, const bf16_t* k, const bf16_t* v, const bf16_t* dout,
-                           const uint32_t* mask, const f32x4_t* rowstat, const pisa_stats_t* st, const float* dH,
+                           const uint32_t* mask, const f32x4_t* rowstat, const StatsView* st, const float* dH,
                            const float* dHT, const float* dkb_part, const float* dvh_part, const float* dsg,
                            bf16_t* dk, bf16_t* dv, int NW, int nsplit, int second_order, int first_order,
                            hipStream_t stream) {

@@ -166,7 +166,7 @@ __global__ __launch_bounds__(kRows) void attn_valu_kernel(
 }  // namespace
 
 hipError_t launch_attn_fwd_valu(const Geom& g, int dtype, const pisa_params_t* p, const void* q,
-                                const void* k, const void* v, const pisa_stats_t* st,
+                                const void* k, const void* v, const StatsView* st,
                                 const int32_t* idx, const float* wgate, void* o, hipStream_t stream) {
     dim3 grid(g.N, (unsigned)g.BH), block(kRows);
     const size_t shm = (size_t)g.N;

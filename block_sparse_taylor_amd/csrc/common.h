@@ -57,6 +57,24 @@ struct Forced {
     __host__ __device__ bool forced(int j) const { return (j >= lo && j <= hi) || j < ns; }
 };
 
+// What the kernels read and write: the caller's statistics (pisa_stats_t)
+// and the views of its operand buffer (the kernels' own layouts of them).
+struct StatsView {
+    double* qbar;
+    double* q2bar;
+    double* kbar;
+    float* vsum;
+    double* ksig2;
+    float* hsum;
+    void* kbar_c;      // kbar rounded to the input dtype              [BH,N,D]
+    void* vbar_c;      // vsum / n rounded to the input dtype          [BH,N,D]
+    void* kpack;       // bf16: K in the fused kernel's operand order  [BH,N,64 D]
+    void* hpack;       // bf16: H split hi + lo, operand order         [BH,2 D D]
+    void* kbpack;      // bf16: kbar_c in kpack's order per 64 blocks  [BH,ceil(N/64),64 D]
+    float* kbar_r;     // kbar in fp32, the router's operand order     [BH,ceil(N/16) 16 D]
+    float* ksig2_r;    // ksig2 in fp32, the same order
+};
+
 // Problem geometry resolved once on the host.
 struct Geom {
     int64_t BH;       // batch * heads
@@ -67,17 +85,32 @@ struct Geom {
     double scale64;   // the same scale in fp64 (routing decisions)
 };
 
+// Byte offsets of the kernel layouts inside a caller's operand buffer (each
+// 256-byte aligned; the bf16-only layouts are empty for fp32 inputs), in the
+// order of pisa_operand_t, and the buffer's total size.
+struct OperandLayout {
+    size_t off[PISA_OPERAND_COUNT];
+    size_t bytes[PISA_OPERAND_COUNT];
+    size_t total;
+};
+OperandLayout operand_layout(const Geom& g, int dtype);
+// The kernel view of caller statistics plus an operand buffer.
+StatsView stats_view(const Geom& g, int dtype, const pisa_stats_t* st, const void* operands);
+
 // Kernel launchers (return hipSuccess or the launch error).
 hipError_t launch_block_stats(const Geom& g, int dtype, int second_order, const void* q, const void* k,
-                              const void* v, const pisa_stats_t* out, void* workspace,
+                              const void* v, const StatsView* out, void* workspace,
                               hipStream_t stream);
 size_t stats_workspace_bytes(const Geom& g);
+// The operand layouts from statistics of any source (and K for kpack).
+hipError_t launch_prepare_operands(const Geom& g, int dtype, int second_order, const void* k,
+                                   const StatsView* st, hipStream_t stream);
 
-hipError_t launch_route_topk(const Geom& g, const pisa_params_t* p, const pisa_stats_t* st,
+hipError_t launch_route_topk(const Geom& g, const pisa_params_t* p, const StatsView* st,
                              int32_t* idx, float* wgate, hipStream_t stream);
 
 hipError_t launch_attn_fwd_valu(const Geom& g, int dtype, const pisa_params_t* p, const void* q,
-                                const void* k, const void* v, const pisa_stats_t* st,
+                                const void* k, const void* v, const StatsView* st,
                                 const int32_t* idx, const float* wgate, void* o, hipStream_t stream);
 
 hipError_t launch_reorder(const Geom& g, int64_t batch, int64_t heads, int elem_bytes, bool gather,
@@ -85,7 +118,7 @@ hipError_t launch_reorder(const Geom& g, int64_t batch, int64_t heads, int elem_
 void z_order_host(const int64_t* grid, int ndim, int64_t prefix, int32_t* perm);
 
 size_t attn_bwd_workspace_bytes(const Geom& g, int dtype);
-hipError_t launch_bwd_prep(const Geom& g, const pisa_stats_t* st, bf16_t* kbh, bf16_t* kbl, bf16_t* vhh,
+hipError_t launch_bwd_prep(const Geom& g, const StatsView* st, bf16_t* kbh, bf16_t* kbl, bf16_t* vhh,
                            bf16_t* vhl, bf16_t* hh, bf16_t* hl, hipStream_t stream);
 hipError_t launch_bwd_rowstats(const Geom& g, const bf16_t* q, const bf16_t* k, const bf16_t* o, const bf16_t* dout,
                                const bf16_t* kbh, const bf16_t* kbl, const bf16_t* hh, const bf16_t* hl,
@@ -97,17 +130,17 @@ hipError_t launch_bwd_dq(const Geom& g, const bf16_t* q, const bf16_t* k, const 
                          const f32x4_t* rowstat, const float* dw, const double* ksig2, float* dq2, bf16_t* dq, int NW,
                          int second_order, int first_order, hipStream_t stream);
 int bwd_virt_splits(const Geom& g);
-hipError_t launch_bwd_virt_mfma(const Geom& g, const bf16_t* q, const bf16_t* dout, const pisa_stats_t* st,
+hipError_t launch_bwd_virt_mfma(const Geom& g, const bf16_t* q, const bf16_t* dout, const StatsView* st,
                                 const uint32_t* mask, const f32x4_t* rowstat, const float* wgate, float* dkb_part,
                                 float* dvh_part, float* dw, float* dsg, int NW, int second_order,
                                 hipStream_t stream);
 hipError_t launch_bwd_dkdv(const Geom& g, const bf16_t* q, const bf16_t* k, const bf16_t* v, const bf16_t* dout,
-                           const uint32_t* mask, const f32x4_t* rowstat, const pisa_stats_t* st, const float* dH,
+                           const uint32_t* mask, const f32x4_t* rowstat, const StatsView* st, const float* dH,
                            const float* dHT, const float* dkb_part, const float* dvh_part, const float* dsg,
                            bf16_t* dk, bf16_t* dv, int NW, int nsplit, int second_order, int first_order,
                            hipStream_t stream);
 hipError_t launch_attn_bwd(const Geom& g, int dtype, const pisa_params_t* p, const void* q, const void* k,
-                           const void* v, const void* o, const void* dout, const pisa_stats_t* st,
+                           const void* v, const void* o, const void* dout, const StatsView* st,
                            const int32_t* idx, const float* wgate, void* dq, void* dk, void* dv, void* ws,
                            hipStream_t stream);
 
@@ -117,7 +150,7 @@ int64_t attn_asm_wave_items(const Geom& g, const pisa_params_t* p);
 int attn_fwd_kernel(const Geom& g, int dtype, const pisa_params_t* p);
 
 hipError_t launch_attn_fwd_mfma(const Geom& g, const pisa_params_t* p, const void* q, const void* k,
-                                const void* v, const pisa_stats_t* st, const int32_t* idx,
+                                const void* v, const StatsView* st, const int32_t* idx,
                                 const float* wgate, void* o, hipStream_t stream);
 
 }  // namespace pisa

@@ -65,44 +65,113 @@ pisa_status_t check_ptr(const void* p) {
         if (st_ != PISA_OK) return st_;       \
     } while (0)
 
-pisa_status_t check_stats(const pisa_stats_t* st, int second_order, bool need_c, bool need_kpack) {
+// The statistics a call reads: kbar, vsum, hsum always (the fp32 attention
+// and the backward read them, the router kbar), qbar for the router, and the
+// second-order pair when the term is on.
+pisa_status_t check_stats(const pisa_stats_t* st, int second_order, bool need_qbar) {
     if (!st) return PISA_ERR_NULL;
     PISA_TRY(check_ptr(st->kbar));
     PISA_TRY(check_ptr(st->vsum));
     PISA_TRY(check_ptr(st->hsum));
-    if (need_c) {
-        PISA_TRY(check_ptr(st->kbar_c));
-        PISA_TRY(check_ptr(st->vbar_c));
+    if (need_qbar) PISA_TRY(check_ptr(st->qbar));
+    if (second_order) {
+        PISA_TRY(check_ptr(st->ksig2));
+        PISA_TRY(check_ptr(st->q2bar));
+    } else {
+        if (st->ksig2 && !aligned16(st->ksig2)) return PISA_ERR_ALIGN;
+        if (st->q2bar && !aligned16(st->q2bar)) return PISA_ERR_ALIGN;
     }
-    if (need_kpack) {
-        PISA_TRY(check_ptr(st->kpack));
-        PISA_TRY(check_ptr(st->hpack));
-        PISA_TRY(check_ptr(st->kbpack));
-    }
-    if (second_order) PISA_TRY(check_ptr(st->ksig2));
-    else if (st->ksig2 && !aligned16(st->ksig2)) return PISA_ERR_ALIGN;
     return PISA_OK;
+}
+
+pisa_status_t check_operands(const Geom& g, int dtype, const void* operands, size_t bytes) {
+    PISA_TRY(check_ptr(operands));
+    if (bytes < operand_layout(g, dtype).total) return PISA_ERR_WORKSPACE;
+    return PISA_OK;
+}
+
+// [a, a + na) and [b, b + nb) share a byte
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return a && b && x < y + nb && y < x + na;
+}
+
+size_t tensor_bytes(const Geom& g, int dtype) {
+    return (size_t)g.BH * g.T * g.D * (dtype == PISA_BF16 ? 2 : 4);
 }
 
 pisa_status_t from_hip(hipError_t e) { return e == hipSuccess ? PISA_OK : PISA_ERR_HIP; }
 
 pisa_status_t attn_common(const pisa_shape_t* shape, const pisa_params_t* params, const void* q,
-                          const void* k, const void* v, const pisa_stats_t* stats,
-                          const int32_t* idx, const float* wgate, void* o, Geom* g) {
+                          const void* k, const void* v, const pisa_stats_t* stats, const void* operands,
+                          size_t operands_bytes, const int32_t* idx, const float* wgate, void* o, Geom* g,
+                          bool need_operands) {
     PISA_TRY(check_shape(shape, g));
     PISA_TRY(check_params(params, *g));
     PISA_TRY(check_ptr(q));
     PISA_TRY(check_ptr(k));
     PISA_TRY(check_ptr(v));
     PISA_TRY(check_ptr(o));
-    PISA_TRY(check_stats(stats, 0, shape->dtype == PISA_BF16, shape->dtype == PISA_BF16));
+    PISA_TRY(check_stats(stats, 0, false));
+    if (need_operands) PISA_TRY(check_operands(*g, shape->dtype, operands, operands_bytes));
     if (params->topk > 0) PISA_TRY(check_ptr(idx));
     if (params->second_order) PISA_TRY(check_ptr(wgate));
-    if (o == q || o == k || o == v) return PISA_ERR_PARAM;
+    const size_t tb = tensor_bytes(*g, shape->dtype);
+    if (overlap(o, tb, q, tb) || overlap(o, tb, k, tb) || overlap(o, tb, v, tb)) return PISA_ERR_PARAM;
     return PISA_OK;
 }
 
 }  // namespace
+
+namespace pisa {
+
+OperandLayout operand_layout(const Geom& g, int dtype) {
+    const size_t e = dtype == PISA_BF16 ? 2 : 4;
+    const bool bf = dtype == PISA_BF16;
+    const size_t BH = (size_t)g.BH, N = (size_t)g.N, D = (size_t)g.D;
+    size_t sz[PISA_OPERAND_COUNT];
+    sz[PISA_OPERAND_KBAR_C] = BH * N * D * e;
+    sz[PISA_OPERAND_VBAR_C] = BH * N * D * e;
+    sz[PISA_OPERAND_KBAR_R] = BH * ((N + 15) / 16) * 16 * D * 4;
+    sz[PISA_OPERAND_KSIG2_R] = sz[PISA_OPERAND_KBAR_R];
+    sz[PISA_OPERAND_KPACK] = bf ? BH * N * 64 * D * 2 : 0;
+    sz[PISA_OPERAND_KBPACK] = bf ? BH * ((N + 63) / 64) * 64 * D * 2 : 0;
+    sz[PISA_OPERAND_HPACK] = bf ? BH * 2 * D * D * 2 : 0;
+    OperandLayout L{};
+    size_t at = 0;
+    for (int i = 0; i < PISA_OPERAND_COUNT; ++i) {
+        L.off[i] = at;
+        L.bytes[i] = sz[i];
+        at += (sz[i] + 255) / 256 * 256;
+    }
+    L.total = at;
+    return L;
+}
+
+StatsView stats_view(const Geom& g, int dtype, const pisa_stats_t* st, const void* operands) {
+    StatsView v{};
+    v.qbar = st->qbar;
+    v.q2bar = st->q2bar;
+    v.kbar = st->kbar;
+    v.vsum = st->vsum;
+    v.ksig2 = st->ksig2;
+    v.hsum = st->hsum;
+    if (operands) {
+        const OperandLayout L = operand_layout(g, dtype);
+        char* b = static_cast<char*>(const_cast<void*>(operands));
+        auto at = [&](int i) -> void* { return L.bytes[i] ? b + L.off[i] : nullptr; };
+        v.kbar_c = at(PISA_OPERAND_KBAR_C);
+        v.vbar_c = at(PISA_OPERAND_VBAR_C);
+        v.kbar_r = static_cast<float*>(at(PISA_OPERAND_KBAR_R));
+        v.ksig2_r = static_cast<float*>(at(PISA_OPERAND_KSIG2_R));
+        v.kpack = at(PISA_OPERAND_KPACK);
+        v.kbpack = at(PISA_OPERAND_KBPACK);
+        v.hpack = at(PISA_OPERAND_HPACK);
+    }
+    return v;
+}
+
+}  // namespace pisa
 
 extern "C" {
 
@@ -135,66 +204,97 @@ size_t pisa_stats_workspace_bytes(const pisa_shape_t* shape) {
     return stats_workspace_bytes(g);
 }
 
+size_t pisa_operands_bytes(const pisa_shape_t* shape) {
+    Geom g;
+    if (check_shape(shape, &g) != PISA_OK) return 0;
+    return operand_layout(g, shape->dtype).total;
+}
+
+pisa_status_t pisa_operands_offsets(const pisa_shape_t* shape, int64_t* offsets) {
+    Geom g;
+    PISA_TRY(check_shape(shape, &g));
+    if (!offsets) return PISA_ERR_NULL;
+    const OperandLayout L = operand_layout(g, shape->dtype);
+    for (int i = 0; i < PISA_OPERAND_COUNT; ++i) offsets[i] = (int64_t)L.off[i];
+    return PISA_OK;
+}
+
 pisa_status_t pisa_block_stats(const pisa_shape_t* shape, const pisa_params_t* params, const void* q,
-                               const void* k, const void* v, const pisa_stats_t* out, void* workspace,
-                               size_t workspace_bytes, void* stream) {
+                               const void* k, const void* v, const pisa_stats_t* out, void* operands,
+                               size_t operands_bytes, void* workspace, size_t workspace_bytes, void* stream) {
     Geom g;
     PISA_TRY(check_shape(shape, &g));
     PISA_TRY(check_params(params, g));
     PISA_TRY(check_ptr(q));
     PISA_TRY(check_ptr(k));
     PISA_TRY(check_ptr(v));
-    PISA_TRY(check_stats(out, params->second_order, true, shape->dtype == PISA_BF16));
-    PISA_TRY(check_ptr(out->qbar));
-    PISA_TRY(check_ptr(out->kbar_r));
-    if (params->second_order) PISA_TRY(check_ptr(out->ksig2_r));
-    if (params->second_order) PISA_TRY(check_ptr(out->q2bar));
+    PISA_TRY(check_stats(out, params->second_order, true));
+    PISA_TRY(check_operands(g, shape->dtype, operands, operands_bytes));
     PISA_TRY(check_ptr(workspace));
     if (workspace_bytes < stats_workspace_bytes(g)) return PISA_ERR_WORKSPACE;
-    return from_hip(launch_block_stats(g, shape->dtype, params->second_order, q, k, v, out,
-                                       workspace, static_cast<hipStream_t>(stream)));
+    const size_t tb = tensor_bytes(g, shape->dtype), ob = operand_layout(g, shape->dtype).total;
+    for (const void* in : {q, k, v})
+        if (overlap(operands, ob, in, tb) || overlap(workspace, workspace_bytes, in, tb)) return PISA_ERR_PARAM;
+    if (overlap(operands, ob, workspace, workspace_bytes)) return PISA_ERR_PARAM;
+    const StatsView sv = stats_view(g, shape->dtype, out, operands);
+    return from_hip(launch_block_stats(g, shape->dtype, params->second_order, q, k, v, &sv, workspace,
+                                       static_cast<hipStream_t>(stream)));
 }
 
-pisa_status_t pisa_route_topk(const pisa_shape_t* shape, const pisa_params_t* params,
-                              const pisa_stats_t* stats, int32_t* idx, float* wgate, void* stream) {
+pisa_status_t pisa_prepare_operands(const pisa_shape_t* shape, const pisa_params_t* params, const void* k,
+                                    const pisa_stats_t* stats, void* operands, size_t operands_bytes,
+                                    void* stream) {
     Geom g;
     PISA_TRY(check_shape(shape, &g));
     PISA_TRY(check_params(params, g));
-    if (!stats) return PISA_ERR_NULL;
-    PISA_TRY(check_ptr(stats->qbar));
-    PISA_TRY(check_ptr(stats->kbar));
-    PISA_TRY(check_ptr(stats->kbar_r));
-    if (params->second_order) PISA_TRY(check_ptr(stats->ksig2_r));
-    if (params->second_order) {
-        PISA_TRY(check_ptr(stats->q2bar));
-        PISA_TRY(check_ptr(stats->ksig2));
-        PISA_TRY(check_ptr(wgate));
-    }
+    if (shape->dtype == PISA_BF16) PISA_TRY(check_ptr(k));
+    PISA_TRY(check_stats(stats, params->second_order, false));
+    PISA_TRY(check_operands(g, shape->dtype, operands, operands_bytes));
+    const size_t ob = operand_layout(g, shape->dtype).total;
+    if (overlap(operands, ob, k, tensor_bytes(g, shape->dtype))) return PISA_ERR_PARAM;
+    const StatsView sv = stats_view(g, shape->dtype, stats, operands);
+    return from_hip(launch_prepare_operands(g, shape->dtype, params->second_order, k, &sv,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+pisa_status_t pisa_route_topk(const pisa_shape_t* shape, const pisa_params_t* params,
+                              const pisa_stats_t* stats, const void* operands, size_t operands_bytes,
+                              int32_t* idx, float* wgate, void* stream) {
+    Geom g;
+    PISA_TRY(check_shape(shape, &g));
+    PISA_TRY(check_params(params, g));
+    PISA_TRY(check_stats(stats, params->second_order, true));
+    PISA_TRY(check_operands(g, shape->dtype, operands, operands_bytes));
+    if (params->second_order) PISA_TRY(check_ptr(wgate));
     if (params->topk > 0) PISA_TRY(check_ptr(idx));
     const pisa_params_t pr = resolved(params, g);
-    return from_hip(launch_route_topk(g, &pr, stats, idx, wgate, static_cast<hipStream_t>(stream)));
+    const StatsView sv = stats_view(g, shape->dtype, stats, operands);
+    return from_hip(launch_route_topk(g, &pr, &sv, idx, wgate, static_cast<hipStream_t>(stream)));
 }
 
 pisa_status_t pisa_attn_fwd(const pisa_shape_t* shape, const pisa_params_t* params, const void* q,
-                            const void* k, const void* v, const pisa_stats_t* stats,
-                            const int32_t* idx, const float* wgate, void* o, void* stream) {
+                            const void* k, const void* v, const pisa_stats_t* stats, const void* operands,
+                            size_t operands_bytes, const int32_t* idx, const float* wgate, void* o,
+                            void* stream) {
     Geom g;
-    PISA_TRY(attn_common(shape, params, q, k, v, stats, idx, wgate, o, &g));
+    const bool bf = shape && shape->dtype == PISA_BF16;
+    PISA_TRY(attn_common(shape, params, q, k, v, stats, operands, operands_bytes, idx, wgate, o, &g, bf));
     hipStream_t s = static_cast<hipStream_t>(stream);
     const pisa_params_t pr = resolved(params, g);
-    if (shape->dtype == PISA_BF16)
-        return from_hip(launch_attn_fwd_mfma(g, &pr, q, k, v, stats, idx, wgate, o, s));
-    return from_hip(launch_attn_fwd_valu(g, shape->dtype, &pr, q, k, v, stats, idx, wgate, o, s));
+    const StatsView sv = stats_view(g, shape->dtype, stats, bf ? operands : nullptr);
+    if (bf) return from_hip(launch_attn_fwd_mfma(g, &pr, q, k, v, &sv, idx, wgate, o, s));
+    return from_hip(launch_attn_fwd_valu(g, shape->dtype, &pr, q, k, v, &sv, idx, wgate, o, s));
 }
 
 pisa_status_t pisa_attn_fwd_valu(const pisa_shape_t* shape, const pisa_params_t* params,
                                  const void* q, const void* k, const void* v,
-                                 const pisa_stats_t* stats, const int32_t* idx, const float* wgate,
-                                 void* o, void* stream) {
+                                 const pisa_stats_t* stats, const void* operands, size_t operands_bytes,
+                                 const int32_t* idx, const float* wgate, void* o, void* stream) {
     Geom g;
-    PISA_TRY(attn_common(shape, params, q, k, v, stats, idx, wgate, o, &g));
+    PISA_TRY(attn_common(shape, params, q, k, v, stats, operands, operands_bytes, idx, wgate, o, &g, false));
     const pisa_params_t pr = resolved(params, g);
-    return from_hip(launch_attn_fwd_valu(g, shape->dtype, &pr, q, k, v, stats, idx, wgate, o,
+    const StatsView sv = stats_view(g, shape->dtype, stats, nullptr);
+    return from_hip(launch_attn_fwd_valu(g, shape->dtype, &pr, q, k, v, &sv, idx, wgate, o,
                                          static_cast<hipStream_t>(stream)));
 }
 
@@ -224,22 +324,25 @@ pisa_status_t pisa_attn_bwd(const pisa_shape_t* shape, const pisa_params_t* para
     PISA_TRY(check_params(params, g));
     const void* ptrs[9] = {q, k, v, o, dout, dq, dk, dv, workspace};
     for (const void* ptr : ptrs) PISA_TRY(check_ptr(ptr));
-    PISA_TRY(check_stats(stats, params->second_order, false, false));
-    if (params->second_order) PISA_TRY(check_ptr(stats->q2bar));
+    PISA_TRY(check_stats(stats, params->second_order, false));
     if (params->topk > 0) PISA_TRY(check_ptr(idx));
     if (params->second_order) PISA_TRY(check_ptr(wgate));
     if (params->phase_mask != 0) return PISA_ERR_UNSUPPORTED;
     if (workspace_bytes < attn_bwd_workspace_bytes(g, shape->dtype)) return PISA_ERR_WORKSPACE;
+    // no output may share a byte with another output, an input or the workspace
+    const size_t tb = tensor_bytes(g, shape->dtype);
     const void* outs[3] = {dq, dk, dv};
-    const void* ins[6] = {q, k, v, o, dout, workspace};
+    const void* ins[5] = {q, k, v, o, dout};
     for (int a = 0; a < 3; ++a) {
         for (int b = a + 1; b < 3; ++b)
-            if (outs[a] == outs[b]) return PISA_ERR_PARAM;
+            if (overlap(outs[a], tb, outs[b], tb)) return PISA_ERR_PARAM;
         for (const void* in : ins)
-            if (outs[a] == in) return PISA_ERR_PARAM;
+            if (overlap(outs[a], tb, in, tb)) return PISA_ERR_PARAM;
+        if (overlap(outs[a], tb, workspace, workspace_bytes)) return PISA_ERR_PARAM;
     }
     const pisa_params_t pr = resolved(params, g);
-    return from_hip(launch_attn_bwd(g, shape->dtype, &pr, q, k, v, o, dout, stats, idx, wgate, dq, dk,
+    const StatsView sv = stats_view(g, shape->dtype, stats, nullptr);
+    return from_hip(launch_attn_bwd(g, shape->dtype, &pr, q, k, v, o, dout, &sv, idx, wgate, dq, dk,
                                     dv, workspace, static_cast<hipStream_t>(stream)));
 }
 

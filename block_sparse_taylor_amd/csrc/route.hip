@@ -589,7 +589,7 @@ __global__ __launch_bounds__(kThreads) void route_slow_kernel(
 
 }  // namespace
 
-hipError_t launch_route_topk(const Geom& g, const pisa_params_t* p, const pisa_stats_t* st,
+hipError_t launch_route_topk(const Geom& g, const pisa_params_t* p, const StatsView* st,
                              int32_t* idx, float* wgate, hipStream_t stream) {
     const int so = p->second_order;
     if (p->topk == 0 && !so) return hipSuccess;

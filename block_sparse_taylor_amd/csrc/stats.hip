@@ -121,8 +121,11 @@ __device__ __forceinline__ void column_stats(const T* tq, const T* tk, const T* 
             static_cast<bf16_t*>(out.kbpack)[gbase + (((r / 32) * (D / 8) + c / 8) * 32 + r % 32) * 8 + c % 8] =
                 f32_to_bf16((float)mean);
         }
-        out.vsum[off + c] = (float)a[5];
-        static_cast<T*>(out.vbar_c)[off + c] = store_cast<T>((float)(a[5] / n));
+        const float vs = (float)a[5];
+        out.vsum[off + c] = vs;
+        // the virtual token's value from the stored fp32 V-hat (as
+        // prepare_operands_kernel forms it from a caller's statistics)
+        static_cast<T*>(out.vbar_c)[off + c] = store_cast<T>((float)((double)vs / n));
         kb_s[c] = (float)mean;
         vs_s[c] = (float)a[5];
         if (second_order) {
@@ -341,6 +344,19 @@ __global__ __launch_bounds__(kThreads) void stats_f32_kernel(
     for (int r = 0; r < PER; ++r) hp[tid + r * kThreads] = (float)acc[r];
 }
 
+// H split into bf16 hi + lo in the fused kernel's MFMA A-operand order for
+// G = Q H: element (dt, ks, part, lane, e) is the part of
+// H[16 ks + 8 (lane / 32) + e][32 dt + lane % 32].
+__device__ __forceinline__ void write_hpack(bf16_t* hpack, int64_t bh, int D, int e, float h) {
+    const int DD = D * D;
+    const int a = e / D, b = e % D;            // key dim, value dim
+    const int dt = b / 32, lane = 32 * ((a % 16) / 8) + b % 32, ks = a / 16, el = a % 8;
+    const int64_t o = bh * (int64_t)(2 * DD) + ((int64_t)((dt * (D / 16) + ks) * 2) * 64 + lane) * 8 + el;
+    const bf16_t hi = f32_to_bf16(h);
+    hpack[o] = hi;
+    hpack[o + 64 * 8] = f32_to_bf16(h - bf16_to_f32(hi));
+}
+
 // Fixed-order sum of the per-workgroup partials of each head.
 // Sums the partial H of a head in fixed order. For bf16 inputs it also writes
 // H split into bf16 hi + lo in the fused kernel's MFMA A-operand order for
@@ -358,13 +374,72 @@ __global__ __launch_bounds__(kThreads) void hsum_reduce_kernel(const float* __re
     for (int g = 0; g < G; ++g) s += (double)p[(int64_t)g * DD];
     const float h = (float)s;
     hsum[bh * DD + e] = h;
-    if (hpack) {
-        const int a = e / D, b = e % D;            // key dim, value dim
-        const int dt = b / 32, lane = 32 * ((a % 16) / 8) + b % 32, ks = a / 16, el = a % 8;
-        const int64_t o = bh * (int64_t)(2 * DD) + ((int64_t)((dt * (D / 16) + ks) * 2) * 64 + lane) * 8 + el;
-        const bf16_t hi = f32_to_bf16(h);
-        hpack[o] = hi;
-        hpack[o + 64 * 8] = f32_to_bf16(h - bf16_to_f32(hi));
+    if (hpack) write_hpack(hpack, bh, D, e, h);
+}
+
+// The operand layouts from a caller's statistics (and K). Workgroup (j, bh)
+// with j < N writes block j's entries, exactly as the statistics pass does
+// from its own results; workgroup (N, bh) writes the head's hpack and the zero
+// rows of the last virtual-key group.
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void prepare_operands_kernel(
+    const T* __restrict__ k, const double* __restrict__ kbar, const float* __restrict__ vsum,
+    const double* __restrict__ ksig2, const float* __restrict__ hsum, int T_, int N, StatsOut out,
+    bf16_t* __restrict__ hpack) {
+    constexpr int CH = D / 8;
+    constexpr int LD = D + 8;
+    __shared__ __attribute__((aligned(16))) bf16_t sk[kBlock * LD];
+    const int tid = threadIdx.x;
+    const int64_t bh = blockIdx.y;
+    const int j = blockIdx.x;
+    if (j == N) {
+        if (hpack) {
+            for (int e = tid; e < D * D; e += kThreads) write_hpack(hpack, bh, D, e, hsum[bh * D * D + e]);
+        }
+        if (out.kbpack && N % 64 != 0) {
+            const int GV = (N + 63) / 64;
+            bf16_t* gp = static_cast<bf16_t*>(out.kbpack) + (bh * GV + GV - 1) * (int64_t)(64 * D);
+            for (int e = tid; e < 64 * D; e += kThreads) {
+                const int r = (e / (32 * D)) * 32 + (e / 8) % 32;
+                if (r >= N % 64) gp[e] = 0;
+            }
+        }
+        return;
+    }
+    const int rows = min(kBlock, T_ - j * kBlock);
+    const int64_t off = (bh * N + j) * D;
+    if (tid < D) {
+        const int c = tid;
+        const double mean = kbar[off + c];
+        const int64_t roff = bh * (int64_t)((N + 15) / 16) * 16 * D +
+                             ((((int64_t)(j / 16)) * (D / 16) + (c % (D / 4)) / 4) * 64 + 16 * (c / (D / 4)) +
+                              j % 16) * 4 + c % 4;
+        out.kbar_r[roff] = (float)mean;
+        static_cast<T*>(out.kbar_c)[off + c] = store_cast<T>((float)mean);
+        if (out.kbpack) {
+            const int r = j % 64;
+            const int64_t gbase = (bh * ((N + 63) / 64) + j / 64) * (int64_t)(64 * D);
+            static_cast<bf16_t*>(out.kbpack)[gbase + (((r / 32) * (D / 8) + c / 8) * 32 + r % 32) * 8 + c % 8] =
+                f32_to_bf16((float)mean);
+        }
+        static_cast<T*>(out.vbar_c)[off + c] = store_cast<T>((float)((double)vsum[off + c] / (double)rows));
+        if (out.ksig2_r) out.ksig2_r[roff] = (float)ksig2[off + c];
+    }
+    if (out.kpack) {
+        // the block's K rows through LDS (coalesced loads), then in packed order
+        const bf16_t* kh = reinterpret_cast<const bf16_t*>(k) + bh * (int64_t)T_ * D;
+        for (int c = tid; c < kBlock * CH; c += kThreads) {
+            const int row = c / CH, ch = c % CH;
+            uint4 u = make_uint4(0, 0, 0, 0);
+            if (row < rows) u = *reinterpret_cast<const uint4*>(kh + ((int64_t)j * kBlock + row) * D + 8 * ch);
+            *reinterpret_cast<uint4*>(sk + row * LD + 8 * ch) = u;
+        }
+        __syncthreads();
+        uint4* kp = reinterpret_cast<uint4*>(out.kpack) + (bh * N + j) * (int64_t)(kBlock * CH);
+        for (int c = tid; c < kBlock * CH; c += kThreads) {
+            const int half = c / (32 * CH), ch = (c / 32) % CH, r = c % 32;
+            kp[c] = *reinterpret_cast<const uint4*>(sk + (32 * half + r) * LD + 8 * ch);
+        }
     }
 }
 
@@ -385,8 +460,31 @@ size_t stats_workspace_bytes(const Geom& g) {
     return (size_t)g.BH * stats_groups(g) * g.D * g.D * sizeof(float);
 }
 
+hipError_t launch_prepare_operands(const Geom& g, int dtype, int second_order, const void* k,
+                                   const StatsView* st, hipStream_t stream) {
+    const bool bf = dtype == PISA_BF16;
+    StatsOut out{nullptr, nullptr, nullptr, nullptr, nullptr, st->kbar_c, st->vbar_c,
+                 bf ? st->kpack : nullptr, bf ? st->kbpack : nullptr, st->kbar_r,
+                 second_order ? st->ksig2_r : nullptr};
+    bf16_t* hp = bf ? static_cast<bf16_t*>(st->hpack) : nullptr;
+    const dim3 grid(g.N + 1, (unsigned)g.BH), block(kThreads);
+#define PISA_PREP_LAUNCH(TT, DD)                                                                   \
+    hipLaunchKernelGGL((prepare_operands_kernel<TT, DD>), grid, block, 0, stream,                 \
+                       static_cast<const TT*>(k), st->kbar, st->vsum, second_order ? st->ksig2 : nullptr, \
+                       st->hsum, g.T, g.N, out, hp)
+    if (bf) {
+        if (g.D == 128) PISA_PREP_LAUNCH(bf16_t, 128);
+        else PISA_PREP_LAUNCH(bf16_t, 64);
+    } else {
+        if (g.D == 128) PISA_PREP_LAUNCH(float, 128);
+        else PISA_PREP_LAUNCH(float, 64);
+    }
+#undef PISA_PREP_LAUNCH
+    return hipGetLastError();
+}
+
 hipError_t launch_block_stats(const Geom& g, int dtype, int second_order, const void* q, const void* k,
-                              const void* v, const pisa_stats_t* st, void* workspace,
+                              const void* v, const StatsView* st, void* workspace,
                               hipStream_t stream) {
     const int G = stats_groups(g), bpw = stats_bpw(g);
     dim3 grid(G, (unsigned)g.BH), block(kThreads);

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define PISA_ABI_VERSION 10
+#define PISA_ABI_VERSION 11
 
 typedef enum {
     PISA_OK = 0,
@@ -86,9 +86,10 @@ typedef struct {
 } pisa_params_t;
 
 /*
- * Block statistics (Algorithm 1 step 1 and Fig. 4: block means of Q and K,
- * block value sums, the global first-order matrix; §3.2 Formulation;
- * Appendix C; README "Blog post" for the variance and the pooled q^2):
+ * Block statistics (Algorithm 1 step 1 and Fig. 4 "Prepare Phase": block
+ * means of Q and K, block value sums, the global first-order matrix; §3.2
+ * Formulation; Appendix C; README "Blog post" for the key variance and the
+ * pooled q^2). All are caller-owned device arrays:
  *   qbar[i]   = (1/n_i) sum_t q_t                      fp64 [B,H,N,D]
  *   q2bar[i]  = (1/n_i) sum_t (s q_t)^2  (elementwise)  fp64 [B,H,N,D]
  *   kbar[j]   = (1/n_j) sum_n k_{j,n}                  fp64 [B,H,N,D]
@@ -97,34 +98,12 @@ typedef struct {
  *   hsum      = sum_j sum_n (k_{j,n} - kbar_j)^T v_{j,n}
  *                                            (D x D)   fp32 [B,H,D,D]
  *               (row index: key dim, column index: value dim)
- *   kbar_c[j] = kbar[j] rounded to the input dtype      [B,H,N,D]
- *   vbar_c[j] = vsum[j] / n_j rounded to the input dtype [B,H,N,D]
  * n_i, n_j are the rows present in the block (the last one may be partial).
  * qbar, kbar, q2bar and ksig2 are fp64 so that routing decisions (a top-k, a
- * gate) match a float64 evaluation; kbar_c / vbar_c feed the virtual tokens.
- * q2bar and ksig2 may be NULL unless params.second_order.
- * kpack (bf16 inputs; ignored for fp32) is K re-ordered for the fused
- * kernel's matrix-core operands, bf16 [B,H,N,64*D]: within block j, for each
- * 32-row half h, chunk c (dims 8c..8c+7) and row r,
- *   kpack[b,h,j][((h * D/8 + c) * 32 + r) * 8 + e] = k[b,h,64 j + 32 h + r][8 c + e],
- * and 0 for rows past seq_len. It is not one of the paper's statistics: it
- * lets every 64-lane load of the fused kernel read one contiguous 1 KB run.
- * hpack (bf16 inputs; ignored for fp32) is hsum split into bf16 hi + lo
- * (hi = hsum rounded to bf16, lo = the remainder rounded to bf16), in the
- * fused kernel's operand order, bf16 [B,H,2*D*D]: for dt < D/32, ks < D/16,
- * part p (0 hi, 1 lo), lane l < 64 and e < 8,
- *   hpack[b,h][(((dt * D/16 + ks) * 2 + p) * 64 + l) * 8 + e]
- *     = part p of hsum[b,h][16 ks + 8 (l / 32) + e][32 dt + l % 32].
- * kbpack (bf16 inputs; ignored for fp32) is kbar_c in kpack's order per group
- * of 64 consecutive blocks (the keys of the virtual tokens), bf16
- * [B,H,ceil(N/64),64*D]: kbpack[b,h,g] holds rows kbar_c[b,h,64 g + r] as kpack
- * holds rows of k, and 0 for 64 g + r >= N.
- * kbar_r is kbar rounded to fp32 in the router's MFMA operand order, fp32
- * [B,H,ceil(N/16)*16*D]: key j = 16 c + n, dim d = (D/4) g + 4 q + e (g < 4,
- * q < D/16, e < 4) sits at ((c * D/16 + q) * 64 + 16 g + n) * 4 + e; slots of
- * keys past N are unspecified (the router masks them).
- * ksig2_r (second order only; may be NULL otherwise) is ksig2 rounded to fp32
- * in the same order and size as kbar_r.
+ * gate) can match a float64 evaluation; q2bar and ksig2 may be NULL unless
+ * params.second_order. pisa_block_stats computes them from q, k, v; a caller
+ * may also fill them by any other means and hand them to
+ * pisa_prepare_operands.
  */
 typedef struct {
     double *qbar;
@@ -133,14 +112,44 @@ typedef struct {
     float *vsum;
     double *ksig2;
     float *hsum;
-    void *kbar_c;
-    void *vbar_c;
-    void *kpack;
-    void *hpack;
-    void *kbpack;
-    float *kbar_r;
-    float *ksig2_r;
 } pisa_stats_t;
+
+/*
+ * The operand buffer: one caller-owned device allocation of
+ * pisa_operands_bytes(shape) bytes holding the kernels' own arrangements of
+ * the statistics (and of K), which the routing and attention kernels read
+ * with contiguous matrix-core operand loads. Its contents are produced by
+ * pisa_block_stats (fused with the statistics) or by pisa_prepare_operands
+ * (from statistics of any source); they are opaque to callers. Its size
+ * depends on the shape only. For diagnostics, pisa_operands_offsets reports
+ * where each arrangement starts:
+ *   PISA_OPERAND_KBAR_C   kbar rounded to fp32, then to the input dtype [B,H,N,D]
+ *   PISA_OPERAND_VBAR_C   (vsum / n_j, in fp64 from the fp32 vsum) rounded to
+ *                         fp32, then to the input dtype                 [B,H,N,D]
+ *   PISA_OPERAND_KBAR_R   kbar in fp32, router order: key j = 16 c + n, dim
+ *                         d = (D/4) g + 4 q + e (g < 4, q < D/16, e < 4) at
+ *                         ((c D/16 + q) 64 + 16 g + n) 4 + e, [B,H,ceil(N/16) 16 D];
+ *                         slots of keys past N unspecified
+ *   PISA_OPERAND_KSIG2_R  ksig2 in fp32, the same order (second order only)
+ *   PISA_OPERAND_KPACK    bf16 only: K per block j, 32-row half h, chunk c
+ *                         (dims 8c..8c+7), row r: element ((h D/8 + c) 32 + r) 8 + e
+ *                         = k[64 j + 32 h + r][8 c + e]; 0 past seq_len   [B,H,N,64 D]
+ *   PISA_OPERAND_KBPACK   bf16 only: kbar_c rows per group of 64 blocks in
+ *                         KPACK's order, 0 past N                    [B,H,ceil(N/64),64 D]
+ *   PISA_OPERAND_HPACK    bf16 only: hsum split into bf16 hi + lo, element
+ *                         (((dt D/16 + ks) 2 + p) 64 + l) 8 + e = part p of
+ *                         hsum[16 ks + 8 (l/32) + e][32 dt + l % 32]     [B,H,2 D D]
+ */
+typedef enum {
+    PISA_OPERAND_KBAR_C = 0,
+    PISA_OPERAND_VBAR_C = 1,
+    PISA_OPERAND_KBAR_R = 2,
+    PISA_OPERAND_KSIG2_R = 3,
+    PISA_OPERAND_KPACK = 4,
+    PISA_OPERAND_KBPACK = 5,
+    PISA_OPERAND_HPACK = 6,
+    PISA_OPERAND_COUNT = 7
+} pisa_operand_t;
 
 /* ABI version of the library (PISA_ABI_VERSION). */
 int pisa_abi_version(void);
@@ -155,17 +164,38 @@ int64_t pisa_num_blocks(const pisa_shape_t *shape);
  * the shape is invalid. */
 size_t pisa_stats_workspace_bytes(const pisa_shape_t *shape);
 
+/* Bytes of the operand buffer for this shape, or 0 if the shape is invalid. */
+size_t pisa_operands_bytes(const pisa_shape_t *shape);
+
+/* Byte offset of each pisa_operand_t arrangement inside the operand buffer
+ * (offsets[PISA_OPERAND_COUNT]; an arrangement the dtype does not use gets
+ * the offset of the next one and no bytes). Host only, for diagnostics. */
+pisa_status_t pisa_operands_offsets(const pisa_shape_t *shape, int64_t *offsets);
+
 /*
  * pisa_block_stats: reads q, k, v once; writes every field of `out` (q2bar
- * and ksig2 only if params->second_order). `workspace` is caller-owned
- * device memory of at least pisa_stats_workspace_bytes(shape) bytes; its
- * contents on entry are ignored and on return are unspecified. Outputs must
- * not alias inputs.
+ * and ksig2 only if params->second_order) and fills the operand buffer
+ * `operands` (at least pisa_operands_bytes(shape) bytes). `workspace` is
+ * caller-owned device memory of at least pisa_stats_workspace_bytes(shape)
+ * bytes; its contents on entry are ignored and on return are unspecified.
+ * Outputs must not alias inputs.
  */
 pisa_status_t pisa_block_stats(const pisa_shape_t *shape, const pisa_params_t *params,
                                const void *q, const void *k, const void *v,
-                               const pisa_stats_t *out, void *workspace,
-                               size_t workspace_bytes, void *stream);
+                               const pisa_stats_t *out, void *operands, size_t operands_bytes,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * pisa_prepare_operands: fills the operand buffer from statistics of any
+ * source (for example ones computed elsewhere, or by a reference
+ * implementation): reads stats->kbar, vsum, hsum (and ksig2 if
+ * params->second_order) and, for bf16 inputs, k (for PISA_OPERAND_KPACK).
+ * For statistics pisa_block_stats wrote, the buffer equals the one
+ * pisa_block_stats filled, bit for bit.
+ */
+pisa_status_t pisa_prepare_operands(const pisa_shape_t *shape, const pisa_params_t *params,
+                                    const void *k, const pisa_stats_t *stats, void *operands,
+                                    size_t operands_bytes, void *stream);
 
 /*
  * pisa_route_topk (Algorithm 1 step 2 with the pooled score of Eq. 11 minus
@@ -181,12 +211,12 @@ pisa_status_t pisa_block_stats(const pisa_shape_t *shape, const pisa_params_t *p
  * wgate: fp32 [B,H,N,N], required iff second_order: the gated term used by
  *   the virtual-token logits: w_ij where w_ij <= ln B, and 0 where w_ij is
  *   larger (the README's gate, not a clamp), decided as in float64.
- * Reads stats->qbar, kbar, kbar_r (and q2bar, ksig2, ksig2_r if
- * second_order).
+ * Reads stats->qbar, kbar (and q2bar, ksig2 if second_order) and the
+ * operand buffer.
  */
 pisa_status_t pisa_route_topk(const pisa_shape_t *shape, const pisa_params_t *params,
-                              const pisa_stats_t *stats, int32_t *idx, float *wgate,
-                              void *stream);
+                              const pisa_stats_t *stats, const void *operands,
+                              size_t operands_bytes, int32_t *idx, float *wgate, void *stream);
 
 /*
  * pisa_attn_fwd (Algorithm 1 Phases 1-3, Eqs. 3-5 and 9-10): for each query
@@ -203,12 +233,12 @@ pisa_status_t pisa_route_topk(const pisa_shape_t *shape, const pisa_params_t *pa
  * one inside the band makes the result unspecified. o: [B,H,T,D] in the input
  * dtype; must not alias q, k, v. bf16 runs compute QK^T and PV with bf16 MFMA (fp32
  * accumulation, P rounded to bf16); fp32 runs compute in fp32.
- * Reads stats->kbar_c, vbar_c, kpack, hpack and kbpack (bf16), vsum, kbar and
- * hsum (fp32 path).
+ * Reads the operand buffer (bf16) or stats->vsum, kbar and hsum (fp32).
  */
 pisa_status_t pisa_attn_fwd(const pisa_shape_t *shape, const pisa_params_t *params,
                             const void *q, const void *k, const void *v,
-                            const pisa_stats_t *stats, const int32_t *idx,
+                            const pisa_stats_t *stats, const void *operands,
+                            size_t operands_bytes, const int32_t *idx,
                             const float *wgate, void *o, void *stream);
 
 /*
@@ -219,7 +249,8 @@ pisa_status_t pisa_attn_fwd(const pisa_shape_t *shape, const pisa_params_t *para
  */
 pisa_status_t pisa_attn_fwd_valu(const pisa_shape_t *shape, const pisa_params_t *params,
                                  const void *q, const void *k, const void *v,
-                                 const pisa_stats_t *stats, const int32_t *idx,
+                                 const pisa_stats_t *stats, const void *operands,
+                                 size_t operands_bytes, const int32_t *idx,
                                  const float *wgate, void *o, void *stream);
 
 /*

@@ -32,7 +32,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pisa_abi_version() == 10
+    assert lib.pisa_abi_version() == 11
     for code in range(9):
         assert lib.pisa_status_str(code)
     assert lib.pisa_status_str(99) == b"unknown status"
@@ -70,39 +70,87 @@ def test_workspace_bytes(lib):
 
 FAKE = 1 << 20          # 16-byte aligned fake device address: only used where validation fails first
 MIS = FAKE + 4
+GAP = 1 << 32           # fake buffers this far apart never overlap
+
+
+def fake(n):
+    """The n-th fake device buffer (distinct, non-overlapping)."""
+    return FAKE + n * GAP
 
 
 def stats(**kw):
-    d = dict(qbar=FAKE, q2bar=None, kbar=FAKE, vsum=FAKE, ksig2=None, hsum=FAKE, kbar_c=FAKE, vbar_c=FAKE,
-             kpack=FAKE, hpack=FAKE, kbpack=FAKE, kbar_r=FAKE, ksig2_r=None)
+    d = dict(qbar=fake(10), q2bar=None, kbar=fake(11), vsum=fake(12), ksig2=None, hsum=fake(13))
     d.update(kw)
     return _lib.Stats(**d)
 
 
-def call_stats(lib, s=None, p=None, q=FAKE, k=FAKE, v=FAKE, st=None, ws=FAKE, wsb=1 << 30):
+OPS = fake(20)          # operand buffer
+OPSB = 1 << 31          # its size (enough for every shape used here)
+
+
+def call_stats(lib, s=None, p=None, q=fake(1), k=fake(2), v=fake(3), st=None, ops=OPS, opsb=OPSB,
+               ws=fake(21), wsb=1 << 30):
     s = s or shape()
     p = p or _lib.Params(4, 1, 0, 1, 0)
     st = st or stats()
-    return lib.pisa_block_stats(ctypes.byref(s), ctypes.byref(p), q, k, v, ctypes.byref(st), ws, wsb, None)
+    return lib.pisa_block_stats(ctypes.byref(s), ctypes.byref(p), q, k, v, ctypes.byref(st), ops, opsb, ws, wsb,
+                                None)
 
 
-def call_route(lib, s=None, p=None, st=None, idx=FAKE, wg=None):
+def call_prepare(lib, s=None, p=None, k=fake(2), st=None, ops=OPS, opsb=OPSB):
     s = s or shape()
     p = p or _lib.Params(4, 1, 0, 1, 0)
     st = st or stats()
-    return lib.pisa_route_topk(ctypes.byref(s), ctypes.byref(p), ctypes.byref(st), idx, wg, None)
+    return lib.pisa_prepare_operands(ctypes.byref(s), ctypes.byref(p), k, ctypes.byref(st), ops, opsb, None)
 
 
-def call_attn(lib, name="pisa_attn_fwd", s=None, p=None, q=FAKE, k=FAKE + 64, v=FAKE + 128,
-              st=None, idx=FAKE, wg=None, o=FAKE + 256):
+def call_route(lib, s=None, p=None, st=None, ops=OPS, opsb=OPSB, idx=fake(30), wg=None):
+    s = s or shape()
+    p = p or _lib.Params(4, 1, 0, 1, 0)
+    st = st or stats()
+    return lib.pisa_route_topk(ctypes.byref(s), ctypes.byref(p), ctypes.byref(st), ops, opsb, idx, wg, None)
+
+
+def call_attn(lib, name="pisa_attn_fwd", s=None, p=None, q=fake(1), k=fake(2), v=fake(3),
+              st=None, ops=OPS, opsb=OPSB, idx=fake(30), wg=None, o=fake(4)):
     s = s or shape()
     p = p or _lib.Params(4, 1, 0, 1, 0)
     st = st or stats()
     fn = getattr(lib, name)
-    return fn(ctypes.byref(s), ctypes.byref(p), q, k, v, ctypes.byref(st), idx, wg, o, None)
+    return fn(ctypes.byref(s), ctypes.byref(p), q, k, v, ctypes.byref(st), ops, opsb, idx, wg, o, None)
 
 
 E = {n: c for c, n in _lib.STATUS_NAMES.items()}
+
+
+def test_operand_buffer_layout(lib):
+    """pisa_operands_bytes / pisa_operands_offsets: the arrangements in
+    pisa_operand_t order, each 256-byte aligned; the bf16-only ones are empty
+    for fp32 inputs."""
+    def layout(**kw):
+        sh = shape(**kw)
+        off = (ctypes.c_int64 * len(_lib.OPERANDS))()
+        assert lib.pisa_operands_offsets(ctypes.byref(sh), off) == 0
+        return list(off), lib.pisa_operands_bytes(ctypes.byref(sh))
+    rnd = lambda x: -(-x // 256) * 256
+    B, H, N, D = 1, 40, 512, 128                        # Wan2.1-14B
+    off, total = layout(T=32760, D=D, H=H)
+    sizes = [H * N * D * 2, H * N * D * 2, H * 512 * D * 4, H * 512 * D * 4, H * N * 64 * D * 2,
+             H * 8 * 64 * D * 2, H * 2 * D * D * 2]
+    want, at = [], 0
+    for sz in sizes:
+        want.append(at)
+        at += rnd(sz)
+    assert off == want and total == at
+    off, total = layout(T=1000, D=64, H=2, dtype=_lib.PISA_F32)   # N = 16, fp32: no packed layouts
+    sizes = [2 * 16 * 64 * 4, 2 * 16 * 64 * 4, 2 * 16 * 64 * 4, 2 * 16 * 64 * 4, 0, 0, 0]
+    want, at = [], 0
+    for sz in sizes:
+        want.append(at)
+        at += rnd(sz)
+    assert off == want and total == at
+    assert lib.pisa_operands_bytes(ctypes.byref(shape(T=0))) == 0
+    assert lib.pisa_operands_offsets(ctypes.byref(shape()), None) == E["PISA_ERR_NULL"]
 
 
 def test_stats_validation(lib):
@@ -112,20 +160,33 @@ def test_stats_validation(lib):
     assert call_stats(lib, v=MIS) == E["PISA_ERR_ALIGN"]
     assert call_stats(lib, s=shape(D=32)) == E["PISA_ERR_SHAPE"]
     assert call_stats(lib, st=stats(hsum=None)) == E["PISA_ERR_NULL"]
-    assert call_stats(lib, st=stats(kbar_c=MIS)) == E["PISA_ERR_ALIGN"]
-    # kpack: required for bf16 inputs, ignored for fp32
-    assert call_stats(lib, st=stats(kpack=None)) == E["PISA_ERR_NULL"]
-    assert call_stats(lib, st=stats(kpack=MIS)) == E["PISA_ERR_ALIGN"]
-    assert call_stats(lib, st=stats(hpack=None)) == E["PISA_ERR_NULL"]
-    assert call_stats(lib, st=stats(kbpack=None)) == E["PISA_ERR_NULL"]
-    assert call_stats(lib, st=stats(kbar_r=None)) == E["PISA_ERR_NULL"]
-    assert call_stats(lib, st=stats(kbar_r=MIS)) == E["PISA_ERR_ALIGN"]
+    assert call_stats(lib, st=stats(kbar=MIS)) == E["PISA_ERR_ALIGN"]
+    # the operand buffer: required, aligned, at least pisa_operands_bytes
+    need = lib.pisa_operands_bytes(ctypes.byref(shape()))
+    assert call_stats(lib, ops=None) == E["PISA_ERR_NULL"]
+    assert call_stats(lib, ops=MIS) == E["PISA_ERR_ALIGN"]
+    assert call_stats(lib, opsb=need - 1) == E["PISA_ERR_WORKSPACE"]
     # second order needs ksig2 and q2bar
     assert call_stats(lib, p=_lib.Params(4, 1, 1, 1, 0)) == E["PISA_ERR_NULL"]
-    assert call_stats(lib, p=_lib.Params(4, 1, 1, 1, 0), st=stats(ksig2=FAKE)) == E["PISA_ERR_NULL"]
+    assert call_stats(lib, p=_lib.Params(4, 1, 1, 1, 0), st=stats(ksig2=fake(14))) == E["PISA_ERR_NULL"]
     assert call_stats(lib, ws=None) == E["PISA_ERR_NULL"]
     assert call_stats(lib, wsb=16) == E["PISA_ERR_WORKSPACE"]
     assert call_stats(lib, p=_lib.Params(4, 1, 2, 1, 0)) == E["PISA_ERR_PARAM"]
+    # the operand buffer or the workspace inside an input, or each other
+    assert call_stats(lib, ops=fake(2) + 4096) == E["PISA_ERR_PARAM"]
+    assert call_stats(lib, ws=fake(3) + 256) == E["PISA_ERR_PARAM"]
+    assert call_stats(lib, ws=OPS + 1024) == E["PISA_ERR_PARAM"]
+
+
+def test_prepare_validation(lib):
+    assert call_prepare(lib, k=None) == E["PISA_ERR_NULL"]               # bf16: kpack needs k
+    assert call_prepare(lib, st=stats(kbar=None)) == E["PISA_ERR_NULL"]
+    assert call_prepare(lib, st=stats(vsum=MIS)) == E["PISA_ERR_ALIGN"]
+    assert call_prepare(lib, ops=None) == E["PISA_ERR_NULL"]
+    assert call_prepare(lib, opsb=64) == E["PISA_ERR_WORKSPACE"]
+    assert call_prepare(lib, p=_lib.Params(4, 1, 1, 1, 0)) == E["PISA_ERR_NULL"]   # second order: ksig2
+    assert call_prepare(lib, ops=fake(2) + 256) == E["PISA_ERR_PARAM"]              # inside k
+    assert call_prepare(lib, s=shape(dtype=5)) == E["PISA_ERR_DTYPE"]
 
 
 def test_route_validation(lib):
@@ -136,15 +197,14 @@ def test_route_validation(lib):
     assert call_route(lib, st=stats(qbar=None)) == E["PISA_ERR_NULL"]
     assert call_route(lib, idx=None) == E["PISA_ERR_NULL"]
     assert call_route(lib, st=stats(kbar=None)) == E["PISA_ERR_NULL"]
-    assert call_route(lib, st=stats(kbar_r=None)) == E["PISA_ERR_NULL"]
+    assert call_route(lib, ops=None) == E["PISA_ERR_NULL"]
+    assert call_route(lib, opsb=0) == E["PISA_ERR_WORKSPACE"]
     # second order: q2bar, ksig2 and wgate required
-    assert call_route(lib, p=_lib.Params(4, 1, 1, 1, 0)) == E["PISA_ERR_NULL"]
-    assert call_route(lib, p=_lib.Params(4, 1, 1, 1, 0), st=stats(ksig2=FAKE)) == E["PISA_ERR_NULL"]
-    assert call_route(lib, p=_lib.Params(4, 1, 1, 1, 0), st=stats(ksig2=FAKE, q2bar=FAKE)) == E["PISA_ERR_NULL"]
-    # ... and ksig2_r
-    assert call_route(lib, p=_lib.Params(4, 1, 1, 1, 0), st=stats(ksig2=FAKE, q2bar=FAKE), wg=FAKE) == E["PISA_ERR_NULL"]
-    assert call_route(lib, p=_lib.Params(4, 1, 1, 1, 0), st=stats(ksig2=FAKE, q2bar=FAKE, ksig2_r=MIS),
-                      wg=FAKE) == E["PISA_ERR_ALIGN"]
+    so = _lib.Params(4, 1, 1, 1, 0)
+    assert call_route(lib, p=so) == E["PISA_ERR_NULL"]
+    assert call_route(lib, p=so, st=stats(ksig2=fake(14))) == E["PISA_ERR_NULL"]
+    assert call_route(lib, p=so, st=stats(ksig2=fake(14), q2bar=fake(15))) == E["PISA_ERR_NULL"]
+    assert call_route(lib, p=so, st=stats(ksig2=fake(14), q2bar=MIS), wg=fake(31)) == E["PISA_ERR_ALIGN"]
     assert call_route(lib, s=shape(block=128)) == E["PISA_ERR_PARAM"]
     # sink blocks: 0..N
     assert call_route(lib, p=_lib.Params(4, 1, 0, 1, 0, -1)) == E["PISA_ERR_PARAM"]
@@ -154,22 +214,24 @@ def test_route_validation(lib):
 @pytest.mark.parametrize("name", ["pisa_attn_fwd", "pisa_attn_fwd_valu"])
 def test_attn_validation(lib, name):
     assert call_attn(lib, name, o=None) == E["PISA_ERR_NULL"]
-    assert call_attn(lib, name, o=FAKE) == E["PISA_ERR_PARAM"]          # o aliases q
+    assert call_attn(lib, name, o=fake(1)) == E["PISA_ERR_PARAM"]          # o aliases q
+    assert call_attn(lib, name, o=fake(3) + 1024) == E["PISA_ERR_PARAM"]   # o overlaps v
     assert call_attn(lib, name, k=MIS) == E["PISA_ERR_ALIGN"]
     assert call_attn(lib, name, idx=None) == E["PISA_ERR_NULL"]
     assert call_attn(lib, name, p=_lib.Params(4, 1, 1, 1, 0)) == E["PISA_ERR_NULL"]   # wgate
     assert call_attn(lib, name, p=_lib.Params(4, 1, 0, 1, 8)) == E["PISA_ERR_PARAM"]  # phase mask
-    assert call_attn(lib, name, st=stats(kpack=None)) == E["PISA_ERR_NULL"]           # bf16 needs kpack
-    assert call_attn(lib, name, st=stats(hpack=None)) == E["PISA_ERR_NULL"]           # and hpack
     assert call_attn(lib, name, p=_lib.Params(4, 1, 0, 3, 0)) == E["PISA_ERR_PARAM"]
-    assert call_attn(lib, name, st=stats(vbar_c=None)) == E["PISA_ERR_NULL"]
+    assert call_attn(lib, name, st=stats(hsum=None)) == E["PISA_ERR_NULL"]
     assert call_attn(lib, name, s=shape(dtype=2)) == E["PISA_ERR_DTYPE"]
     assert call_attn(lib, name, s=shape(T=10 ** 7)) == E["PISA_ERR_SHAPE"]
+    if name == "pisa_attn_fwd":   # bf16: the matrix-core kernels read the operand buffer
+        assert call_attn(lib, name, ops=None) == E["PISA_ERR_NULL"]
+        assert call_attn(lib, name, opsb=1024) == E["PISA_ERR_WORKSPACE"]
 
 
-def call_bwd(lib, s=None, p=None, q=FAKE, k=FAKE + 64, v=FAKE + 128, o=FAKE + 192, do=FAKE + 256,
-             st=None, idx=FAKE, wg=None, dq=FAKE + 320, dk=FAKE + 384, dv=FAKE + 448, ws=FAKE + 512,
-             wsb=1 << 40):
+def call_bwd(lib, s=None, p=None, q=fake(1), k=fake(2), v=fake(3), o=fake(4), do=fake(5),
+             st=None, idx=fake(30), wg=None, dq=fake(6), dk=fake(7), dv=fake(8), ws=fake(9),
+             wsb=1 << 31):
     s = s or shape()
     p = p or _lib.Params(4, 1, 0, 1, 0)
     st = st or stats()
@@ -192,17 +254,18 @@ def test_bwd_validation(lib):
         assert call_bwd(lib, **{name: MIS}) == E["PISA_ERR_ALIGN"], name
     assert call_bwd(lib, idx=None) == E["PISA_ERR_NULL"]
     assert call_bwd(lib, st=stats(hsum=None)) == E["PISA_ERR_NULL"]
-    assert call_bwd(lib, st=stats(kpack=None, hpack=None, kbpack=None, kbar_c=None, vbar_c=None),
-                    wsb=0) == E["PISA_ERR_WORKSPACE"]                                  # packs not needed
+    assert call_bwd(lib, st=stats(qbar=None), wsb=0) == E["PISA_ERR_WORKSPACE"]        # qbar not needed
     so = _lib.Params(4, 1, 1, 1, 0)
-    assert call_bwd(lib, p=so, wg=FAKE) == E["PISA_ERR_NULL"]                          # ksig2
-    assert call_bwd(lib, p=so, wg=FAKE, st=stats(ksig2=FAKE)) == E["PISA_ERR_NULL"]    # q2bar
-    assert call_bwd(lib, p=so, st=stats(ksig2=FAKE, q2bar=FAKE)) == E["PISA_ERR_NULL"]  # wgate
+    assert call_bwd(lib, p=so, wg=fake(31)) == E["PISA_ERR_NULL"]                          # ksig2
+    assert call_bwd(lib, p=so, wg=fake(31), st=stats(ksig2=fake(14))) == E["PISA_ERR_NULL"]  # q2bar
+    assert call_bwd(lib, p=so, st=stats(ksig2=fake(14), q2bar=fake(15))) == E["PISA_ERR_NULL"]  # wgate
     assert call_bwd(lib, p=_lib.Params(4, 1, 0, 1, 1)) == E["PISA_ERR_UNSUPPORTED"]   # phase mask
     assert call_bwd(lib, wsb=100) == E["PISA_ERR_WORKSPACE"]
-    assert call_bwd(lib, dk=FAKE + 320) == E["PISA_ERR_PARAM"]                          # dq == dk
-    assert call_bwd(lib, dv=FAKE) == E["PISA_ERR_PARAM"]                                # dv == q
-    assert call_bwd(lib, dq=FAKE + 512) == E["PISA_ERR_PARAM"]                          # dq == workspace
+    assert call_bwd(lib, dk=fake(6)) == E["PISA_ERR_PARAM"]                 # dq == dk
+    assert call_bwd(lib, dk=fake(6) + 512) == E["PISA_ERR_PARAM"]           # dq overlaps dk
+    assert call_bwd(lib, dv=fake(1)) == E["PISA_ERR_PARAM"]                 # dv == q
+    assert call_bwd(lib, dv=fake(5) + 2048) == E["PISA_ERR_PARAM"]          # dv overlaps dout
+    assert call_bwd(lib, dq=fake(9) + (1 << 20)) == E["PISA_ERR_PARAM"]     # dq inside the workspace
     assert call_bwd(lib, p=_lib.Params(4, 1, 0, 1, 0, 99)) == E["PISA_ERR_PARAM"]      # sinks > N
 
 
@@ -210,10 +273,16 @@ def test_null_structs(lib):
     st = stats()
     p = _lib.Params(4, 1, 0, 1, 0)
     s = shape()
-    assert lib.pisa_block_stats(None, ctypes.byref(p), FAKE, FAKE, FAKE, ctypes.byref(st), FAKE, 1 << 30, None) == E["PISA_ERR_NULL"]
-    assert lib.pisa_route_topk(ctypes.byref(s), None, ctypes.byref(st), FAKE, None, None) == E["PISA_ERR_NULL"]
-    assert lib.pisa_route_topk(ctypes.byref(s), ctypes.byref(p), None, FAKE, None, None) == E["PISA_ERR_NULL"]
-    assert lib.pisa_attn_fwd(ctypes.byref(s), ctypes.byref(p), FAKE, FAKE + 64, FAKE + 128, None, FAKE, None, FAKE + 256, None) == E["PISA_ERR_NULL"]
+    assert lib.pisa_block_stats(None, ctypes.byref(p), fake(1), fake(2), fake(3), ctypes.byref(st), OPS, OPSB,
+                                fake(21), 1 << 30, None) == E["PISA_ERR_NULL"]
+    assert lib.pisa_route_topk(ctypes.byref(s), None, ctypes.byref(st), OPS, OPSB, fake(30), None,
+                               None) == E["PISA_ERR_NULL"]
+    assert lib.pisa_route_topk(ctypes.byref(s), ctypes.byref(p), None, OPS, OPSB, fake(30), None,
+                               None) == E["PISA_ERR_NULL"]
+    assert lib.pisa_attn_fwd(ctypes.byref(s), ctypes.byref(p), fake(1), fake(2), fake(3), None, OPS, OPSB,
+                             fake(30), None, fake(4), None) == E["PISA_ERR_NULL"]
+    assert lib.pisa_prepare_operands(ctypes.byref(s), ctypes.byref(p), fake(2), None, OPS, OPSB,
+                                     None) == E["PISA_ERR_NULL"]
 
 
 # ---------------------------------------------------------------- Morton reorder

@@ -140,7 +140,9 @@ def test_deterministic(dtype):
     (q, k, v), _ = make(1000, 128, dtype, 23)
     a = run_all(q, k, v, 3, 1, second_order=True)
     b = run_all(q, k, v, 3, 1, second_order=True)
-    for x, y in zip(a[0].__dict__.values(), b[0].__dict__.values()):
+    # the statistics (the operand buffer has padding no kernel writes; its
+    # contents are compared byte for byte by the prepare-operands test)
+    for x, y in zip(a[0].statistics_only().__dict__.values(), b[0].statistics_only().__dict__.values()):
         if x is not None:
             assert torch.equal(x, y)
     assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2]) and torch.equal(a[3], b[3])

@@ -98,15 +98,20 @@ def test_block_stats(name):
     q2bar = run.st.q2bar.cpu().numpy() if w.second_order else None
     vsum = run.st.vsum.cpu().numpy()
     hsum = run.st.hsum.cpu().numpy()
-    kbc = run.host(run.st.kbar_c)
-    vbc = run.host(run.st.vbar_c)
     ks2 = run.st.ksig2.cpu().numpy() if w.second_order else None
-    kp = run.st.kpack.view(torch.int16).cpu().numpy().view(np.uint16) if w.dtype == "bf16" else None
-    hp = run.host(run.st.hpack) if w.dtype == "bf16" else None
-    kbp = run.st.kbpack.view(torch.int16).cpu().numpy().view(np.uint16) if w.dtype == "bf16" else None
-    kbb = run.st.kbar_c.view(torch.int16).cpu().numpy().view(np.uint16) if w.dtype == "bf16" else None
-    kbr = run.host(run.st.kbar_r)
-    ksr = run.host(run.st.ksig2_r) if w.second_order else None
+    # the kernels' arrangements inside the operand buffer
+    B, H, D, N = w.batch, w.heads, w.head_dim, run.N
+    ops = P.operand_views(run.st, run.k)
+    view = lambda name, *shape: ops[name][:math.prod(shape)].reshape(shape)
+    bits = lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)
+    kbc = run.host(view("kbar_c", B, H, N, D))
+    vbc = run.host(view("vbar_c", B, H, N, D))
+    kp = bits(view("kpack", B, H, N, 64 * D)) if w.dtype == "bf16" else None
+    hp = run.host(view("hpack", B, H, 2 * D * D)) if w.dtype == "bf16" else None
+    kbp = bits(view("kbpack", B, H, -(-N // 64), 64 * D)) if w.dtype == "bf16" else None
+    kbb = bits(view("kbar_c", B, H, N, D)) if w.dtype == "bf16" else None
+    kbr = run.host(view("kbar_r", B, H, -(-N // 16) * 16 * D))
+    ksr = run.host(view("ksig2_r", B, H, -(-N // 16) * 16 * D)) if w.second_order else None
     for h in heads:
         # kbar in fp32, router operand order: per 16-column chunk and 16-dim
         # step q, 64 lanes (g = dim quarter, n = column) of 4 dims each
@@ -160,11 +165,14 @@ def test_block_stats(name):
         np.testing.assert_allclose(vsum[0, h], ref.vsum.astype(np.float32), rtol=2 * U32, atol=1e-30)
         if ks2 is not None:
             np.testing.assert_allclose(ks2[0, h], ref.sig2, rtol=1e-12, atol=1e-13)
+        # the virtual tokens' values: the stored fp32 V-hat over n, rounded to fp32, then the dtype
+        vbar_ref = (vsum[0, h].astype(np.float64) / ref.n[:, None]).astype(np.float32).astype(np.float64)
         if w.dtype == "bf16":
             assert np.array_equal(kbc[0, h], bf16_round_f32(ref.kbar))
-            assert np.array_equal(vbc[0, h], bf16_round_f32(ref.vsum / ref.n[:, None]))
+            assert np.array_equal(vbc[0, h], bf16_round_f32(vbar_ref))
         else:
             np.testing.assert_allclose(kbc[0, h], ref.kbar.astype(np.float32), rtol=U32, atol=0)
+            assert np.array_equal(vbc[0, h], vbar_ref)
         mag = np.abs(k).T @ np.abs(v)
         err = np.abs(hsum[0, h] - ref.H)
         assert (err <= 64 * U32 * mag + 1e-30).all(), (h, float((err / mag).max()))
@@ -251,3 +259,78 @@ def test_attn_fwd(name):
             assert err <= 2e-2, (h, err)
             worst = max(worst, err)
     say(f"[gpu] attn {name}: worst {'rel' if w.dtype == 'f32' else 'abs'} error {worst:.3e}")
+
+
+def _zero_operands(x):
+    return torch.zeros(P.operands_bytes(x), dtype=torch.uint8, device=x.device)
+
+
+@pytest.mark.parametrize("name", ["tiny", "flux", "hunyuan"])
+def test_prepare_operands_equals_the_fused_pass(name):
+    """pisa_prepare_operands rebuilds the operand buffer from the statistics
+    alone (and k): equal, byte for byte, to what pisa_block_stats wrote."""
+    w, arrs = workload_inputs(name)
+    say(f"[gpu] prepare operands {name}")
+    q, k, v = (to_device(a, w.dtype) for a in arrs)
+    st = P.alloc_stats(k, w.second_order, operands=False)
+    st.operands = _zero_operands(k)
+    P.pisa_block_stats(q, k, v, second_order=w.second_order, out=st)
+    st2 = P.PisaStats(st.qbar, st.q2bar, st.kbar, st.vsum, st.ksig2, st.hsum, _zero_operands(k))
+    P.pisa_prepare_operands(k, st2, second_order=w.second_order)
+    torch.cuda.synchronize()
+    assert torch.equal(st.operands, st2.operands)
+
+
+@pytest.mark.parametrize("name,heads,so", [("tiny", None, False), ("flux", None, False), ("wan14", [0, 7], True)])
+def test_oracle_statistics_drive_the_kernels(name, heads, so):
+    """Statistics from another source: the oracle's (float64 on the host,
+    rounded to the ABI's storage types) go through pisa_prepare_operands into
+    the router and the fused kernel. Routing equals the oracle's (near-tie
+    rule) and the output the oracle's for that routing, to the dtype's bar."""
+    w = I.WORKLOADS[name]
+    arrs = I.make_inputs(w, heads=heads)
+    Bn, H, T, D = arrs[0].shape
+    N = n_blocks(T)
+    topk = oracle_topk(w.density, N)
+    s = 1 / math.sqrt(D)
+    say(f"[gpu] oracle statistics -> kernels: {name} heads {H} second_order={so}")
+    q, k, v = (to_device(a, w.dtype) for a in arrs)
+    qb, q2, kb, vs, sg, hs = ([] for _ in range(6))
+    hosts = []
+    for h in range(H):
+        qh, kh, vh = head_f64(arrs, w.dtype, 0, h)
+        hosts.append((qh, kh, vh))
+        ks = O.kv_block_stats(kh, vh, 64)
+        rq, rq2 = O.pool_queries(qh, 64, s)
+        qb.append(rq); q2.append(rq2); kb.append(ks.kbar); vs.append(ks.vsum); sg.append(ks.sig2); hs.append(ks.H)
+    dev = lambda xs, dt: torch.from_numpy(np.stack(xs)[None].astype(dt)).cuda()
+    st = P.PisaStats(dev(qb, np.float64), dev(q2, np.float64) if so else None, dev(kb, np.float64),
+                     dev(vs, np.float32), dev(sg, np.float64) if so else None, dev(hs, np.float32))
+    P.pisa_prepare_operands(k, st, second_order=so)
+    idx, wg = P.pisa_route_topk(q, st, topk, band=w.band, second_order=so)
+    o = P.pisa_attn_fwd(q, k, v, st, idx, wg, band=w.band, second_order=so)
+    torch.cuda.synchronize()
+    idx_h = idx.cpu().numpy()
+    worst = 0.0
+    for h, (qh, kh, vh) in enumerate(hosts):
+        wr = O.second_order_w(q2[h], sg[h], 64)[2] if so else None
+        ref_idx, r = O.route_topk(qb[h], kb[h], s, topk, w.band, wr)
+        for i in range(N):
+            got = idx_h[0, h, i]
+            if not np.array_equal(got, ref_idx[i]):
+                gs, rs = set(got[got >= 0].tolist()), set(ref_idx[i][ref_idx[i] >= 0].tolist())
+                kth = min(r[i, j] for j in rs)
+                assert all(abs(r[i, j] - kth) < 1e-6 for j in gs ^ rs), (h, i)
+        blocks = None if N <= 128 else sorted({0, 1, N // 3, N // 2, N - 2, N - 1})
+        ref = O.pisa_forward_head(qh, kh, vh, topk=topk, band=w.band, second_order=so, routing=idx_h[0, h],
+                                  query_blocks=blocks)
+        rows = np.isfinite(ref[:, 0])
+        got = o[0, h].double().cpu().numpy()[rows]
+        err = float(np.abs(got - ref[rows]).max())
+        if w.dtype == "f32":
+            err /= float(np.abs(ref[rows]).max())
+            assert err <= 1e-5, (h, err)
+        else:
+            assert err <= 2e-2, (h, err)
+        worst = max(worst, err)
+    say(f"[gpu] oracle statistics -> kernels {name}: worst {'rel' if w.dtype == 'f32' else 'abs'} error {worst:.3e}")

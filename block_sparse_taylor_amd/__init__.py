@@ -33,7 +33,7 @@ import torch
 from . import _lib
 from ._lib import PISA_BF16, PISA_F32, PisaError
 
-__all__ = ["PisaStats", "pisa_block_stats", "pisa_prepare_operands", "pisa_route_topk", "pisa_attn_fwd",
+__all__ = ["PisaStats", "pisa_block_stats", "pisa_block_stats_noalloc", "pisa_prepare_operands", "pisa_route_topk", "pisa_attn_fwd",
            "pisa_attn_fwd_valu", "pisa_attn_bwd", "piecewise_sparse_attention", "num_blocks", "topk_for_density",
            "z_order", "reorder_gather", "reorder_scatter", "PisaError", "library"]
 
@@ -166,6 +166,23 @@ def pisa_block_stats(q, k, v, second_order=False, scale=None, out: PisaStats | N
     _lib.check("pisa_block_stats", lib.pisa_block_stats(
         ctypes.byref(sh), ctypes.byref(prm), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(cs),
         _ptr(out.operands), out.operands.numel(), _ptr(ws), ws.numel(), _stream(k.device)))
+    return out
+
+
+def pisa_block_stats_noalloc(q, k, v, out: PisaStats, second_order=False, scale=None) -> PisaStats:
+    """pisa_block_stats_noalloc: the statistics pass with the library's static
+    scratch instead of a workspace. `out` (statistics and operand buffer) must
+    be allocated by the caller beforehand; the call allocates nothing."""
+    lib = library()
+    _contig(q, k, v)
+    if out.operands is None:
+        raise ValueError("out.operands must be allocated by the caller")
+    sh = _shape(k, scale)
+    prm = _lib.Params(0, 0, int(second_order), 1, 0)
+    cs = out.as_c()
+    _lib.check("pisa_block_stats_noalloc", lib.pisa_block_stats_noalloc(
+        ctypes.byref(sh), ctypes.byref(prm), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(cs),
+        _ptr(out.operands), out.operands.numel(), _stream(k.device)))
     return out
 
 

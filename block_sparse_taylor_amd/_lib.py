@@ -21,8 +21,9 @@ EXPORTED = (
     "pisa_block_stats", "pisa_route_topk", "pisa_attn_fwd", "pisa_attn_fwd_valu",
     "pisa_z_order", "pisa_reorder_gather", "pisa_reorder_scatter", "pisa_attn_bwd_workspace_bytes",
     "pisa_attn_bwd", "pisa_attn_fwd_plan", "pisa_operands_bytes", "pisa_operands_offsets",
-    "pisa_prepare_operands",
+    "pisa_prepare_operands", "pisa_block_stats_noalloc",
 )
+STATS_SCRATCH_BYTES = 32 << 20   # PISA_STATS_SCRATCH_BYTES
 # pisa_operand_t: the arrangements inside the operand buffer
 OPERANDS = ("kbar_c", "vbar_c", "kbar_r", "ksig2_r", "kpack", "kbpack", "hpack")
 
@@ -78,6 +79,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pisa_block_stats.restype = ctypes.c_int
     lib.pisa_block_stats.argtypes = [P(Shape), P(Params), vp, vp, vp, P(Stats), vp, ctypes.c_size_t, vp,
                                      ctypes.c_size_t, vp]
+    lib.pisa_block_stats_noalloc.restype = ctypes.c_int
+    lib.pisa_block_stats_noalloc.argtypes = [P(Shape), P(Params), vp, vp, vp, P(Stats), vp, ctypes.c_size_t, vp]
     lib.pisa_prepare_operands.restype = ctypes.c_int
     lib.pisa_prepare_operands.argtypes = [P(Shape), P(Params), vp, P(Stats), vp, ctypes.c_size_t, vp]
     lib.pisa_route_topk.restype = ctypes.c_int

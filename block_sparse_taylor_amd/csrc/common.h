@@ -102,6 +102,9 @@ hipError_t launch_block_stats(const Geom& g, int dtype, int second_order, const 
                               const void* v, const StatsView* out, void* workspace,
                               hipStream_t stream);
 size_t stats_workspace_bytes(const Geom& g);
+// This device's copy of the statistics pass's static scratch
+// (PISA_STATS_SCRATCH_BYTES), its address taken once per device.
+hipError_t stats_scratch(void** ptr);
 // The operand layouts from statistics of any source (and K for kpack).
 hipError_t launch_prepare_operands(const Geom& g, int dtype, int second_order, const void* k,
                                    const StatsView* st, hipStream_t stream);

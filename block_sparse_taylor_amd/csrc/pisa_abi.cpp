@@ -241,6 +241,28 @@ pisa_status_t pisa_block_stats(const pisa_shape_t* shape, const pisa_params_t* p
                                        static_cast<hipStream_t>(stream)));
 }
 
+pisa_status_t pisa_block_stats_noalloc(const pisa_shape_t* shape, const pisa_params_t* params, const void* q,
+                                       const void* k, const void* v, const pisa_stats_t* out, void* operands,
+                                       size_t operands_bytes, void* stream) {
+    Geom g;
+    PISA_TRY(check_shape(shape, &g));
+    PISA_TRY(check_params(params, g));
+    PISA_TRY(check_ptr(q));
+    PISA_TRY(check_ptr(k));
+    PISA_TRY(check_ptr(v));
+    PISA_TRY(check_stats(out, params->second_order, true));
+    PISA_TRY(check_operands(g, shape->dtype, operands, operands_bytes));
+    if (stats_workspace_bytes(g) > PISA_STATS_SCRATCH_BYTES) return PISA_ERR_WORKSPACE;
+    const size_t tb = tensor_bytes(g, shape->dtype), ob = operand_layout(g, shape->dtype).total;
+    for (const void* in : {q, k, v})
+        if (overlap(operands, ob, in, tb)) return PISA_ERR_PARAM;
+    void* ws = nullptr;
+    PISA_TRY(from_hip(stats_scratch(&ws)));
+    const StatsView sv = stats_view(g, shape->dtype, out, operands);
+    return from_hip(launch_block_stats(g, shape->dtype, params->second_order, q, k, v, &sv, ws,
+                                       static_cast<hipStream_t>(stream)));
+}
+
 pisa_status_t pisa_prepare_operands(const pisa_shape_t* shape, const pisa_params_t* params, const void* k,
                                     const pisa_stats_t* stats, void* operands, size_t operands_bytes,
                                     void* stream) {

@@ -18,11 +18,20 @@
 //     inputs an fp64 VALU loop. Partials go to the workspace and a second
 //     kernel adds those of a head in a fixed order (deterministic).
 #include <algorithm>
+#include <mutex>
 
 #include "common.h"
 
 namespace pisa {
 namespace {
+
+// Scratch of pisa_block_stats_noalloc (the partial H sums): a file-scope
+// device array, one copy per GPU, held until the process ends. Host code
+// never passes its name to a kernel (in host code the name is a host-side
+// stand-in, not a device address); it uses the per-device address from
+// hipGetSymbolAddress below.
+__device__ __attribute__((aligned(256))) unsigned char scratch[PISA_STATS_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
 
 // Q, K, V are read once and the packed K copy is not read again by this
 // kernel: both go through non-temporal loads / stores (measured: 322 -> 297 us
@@ -455,6 +464,24 @@ int stats_groups(const Geom& g) {
 }
 
 }  // namespace
+
+hipError_t stats_scratch(void** ptr) {
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));   // with this device current
+        if (e != hipSuccess) return e;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 size_t stats_workspace_bytes(const Geom& g) {
     return (size_t)g.BH * stats_groups(g) * g.D * g.D * sizeof(float);

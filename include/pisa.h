@@ -186,6 +186,27 @@ pisa_status_t pisa_block_stats(const pisa_shape_t *shape, const pisa_params_t *p
                                void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * pisa_block_stats_noalloc: pisa_block_stats for callers that cannot
+ * allocate device memory or hand in a workspace (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation). The same
+ * kernels and results as pisa_block_stats; the partial H sums go to a static
+ * device array of PISA_STATS_SCRATCH_BYTES that the library holds on each GPU
+ * it runs on until the process ends (its address is looked up once per
+ * device, on the first call there). No allocation happens in the call.
+ * Shapes with pisa_stats_workspace_bytes(shape) > PISA_STATS_SCRATCH_BYTES
+ * (for head_dim 128: batch * heads > 512) are rejected with
+ * PISA_ERR_WORKSPACE before any HIP call. Every call on one GPU uses that
+ * GPU's one array: calls that overlap on one GPU (other streams, other
+ * threads) race and must be serialised by the caller. The array needs no
+ * clearing: each call writes every partial it reads.
+ */
+#define PISA_STATS_SCRATCH_BYTES ((size_t)32 << 20)
+pisa_status_t pisa_block_stats_noalloc(const pisa_shape_t *shape, const pisa_params_t *params,
+                                       const void *q, const void *k, const void *v,
+                                       const pisa_stats_t *out, void *operands,
+                                       size_t operands_bytes, void *stream);
+
+/*
  * pisa_prepare_operands: fills the operand buffer from statistics of any
  * source (for example ones computed elsewhere, or by a reference
  * implementation): reads stats->kbar, vsum, hsum (and ksig2 if

@@ -397,3 +397,27 @@ def test_attn_fwd_plan_clamps_band_and_validates(lib):
     sh = shape(T=1024, D=128)
     prm = _lib.Params(4, 1, 0, 1, 0, 0)
     assert lib.pisa_attn_fwd_plan(ctypes.byref(sh), ctypes.byref(prm), None, None) == 0
+
+
+def test_noalloc_stats_rejects_shapes_beyond_its_scratch(lib):
+    """pisa_block_stats_noalloc runs only where the partial H sums fit the
+    library's static scratch (PISA_STATS_SCRATCH_BYTES); beyond it the call
+    returns PISA_ERR_WORKSPACE before any HIP call (so on this GPU-less host)."""
+    p = _lib.Params(0, 0, 0, 1, 0)
+    st = stats()
+    def call(s):
+        return lib.pisa_block_stats_noalloc(ctypes.byref(s), ctypes.byref(p), fake(1), fake(2), fake(3),
+                                            ctypes.byref(st), OPS, OPSB, None)
+    # 1024 heads of head_dim 128: one 64 KiB partial per head, 64 MiB
+    big = _lib.Shape(1, 1024, 4096, 128, 64, _lib.PISA_BF16, 0.0)
+    assert lib.pisa_stats_workspace_bytes(ctypes.byref(big)) > _lib.STATS_SCRATCH_BYTES
+    assert call(big) == E["PISA_ERR_WORKSPACE"]
+    # the Wan2.1-14B and Hunyuan shapes fit
+    for T, H in ((32760, 40), (118800, 24)):
+        sh = _lib.Shape(1, H, T, 128, 64, _lib.PISA_BF16, 0.0)
+        assert lib.pisa_stats_workspace_bytes(ctypes.byref(sh)) <= _lib.STATS_SCRATCH_BYTES
+    # validation as pisa_block_stats
+    assert lib.pisa_block_stats_noalloc(ctypes.byref(shape()), ctypes.byref(p), None, fake(2), fake(3),
+                                        ctypes.byref(st), OPS, OPSB, None) == E["PISA_ERR_NULL"]
+    assert lib.pisa_block_stats_noalloc(ctypes.byref(shape()), ctypes.byref(p), fake(1), fake(2), fake(3),
+                                        ctypes.byref(st), OPS, 16, None) == E["PISA_ERR_WORKSPACE"]

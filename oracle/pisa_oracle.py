@@ -32,7 +32,7 @@ R4  global first order: F_t = (l_tail_t / T) * q'_t H with H = sum_j H_j and
 R5  a virtual token carries mass n_j * exp(lambda)  ([PISA] Eq. 3).
 R6  partial last block: n_j = rows present; the gate threshold stays ln B.
 R7  routing score r_ij = s * qbar_i . kbar_j (+ min(w_ij, ln B) when the
-    second-order term is on); no covariance bias.
+    second-order term is on); the covariance prior only when asked for (R19).
 R8  topk is an integer argument (callers use floor(density * N)).
 R9  the +-band is forced exact and top-k is taken over the non-band blocks
     (band_mode="additive"); band_mode="union" is the alternative reading.
@@ -44,6 +44,13 @@ R13 the gated w enters the virtual logit, hence numerator, mass and l_tail.
 R16 sink blocks ([PWT] knobs: n_sink_blocks=n forces the first n KV blocks,
     e.g. an MMDiT text prefix, into the exact branch): like the band they are
     forced for every query block and top-k is taken over the other blocks.
+R19 covariance-aware routing ([PISA] §3.3 "Covariance-Aware Block Selection",
+    Eq. 11, Appendix D Eq. 14; [PWT] knobs cov_bias=True and the changelog's
+    per-block Frobenius norm in the router): the routing score gains
+    log(M_j + eps) with M_j = ||H_j - Hbar||_F, Hbar = (1/N) sum_j H_j over all
+    N blocks (the global statistic of Eq. 10), eps = 1e-6. The paper's own
+    notation makes ||.||_2 the spectral norm; cov_norm="spectral" is that
+    alternative reading. Eq. 11's softmax is dropped as in R7.
 """
 
 from __future__ import annotations
@@ -53,7 +60,12 @@ from dataclasses import dataclass
 
 import numpy as np
 
+COV_EPS = 1e-6   # eps of log(M_j + eps) (R19)
+
 __all__ = [
+    "COV_EPS",
+    "block_heterogeneity",
+    "cov_bias",
     "num_blocks",
     "block_slices",
     "kv_block_stats",
@@ -150,11 +162,29 @@ def second_order_w(q2bar: np.ndarray, sig2: np.ndarray, B: int):
     return w, w_gated, w_rank
 
 
-def route_topk(qbar, kbar, scale, topk, band, w_rank=None, band_mode="additive", n_sink=0):
+def block_heterogeneity(Hj: np.ndarray, norm: str = "fro") -> np.ndarray:
+    """M_j = ||H_j - Hbar|| per block, Hbar = (1/N) sum_j H_j  ([PISA] Eq. 10
+    for Hbar, Eq. 11 and Appendix D for M_j; R19). Hj: [N, D, D]."""
+    Hbar = Hj.sum(axis=0) / Hj.shape[0]
+    diff = Hj - Hbar[None]
+    if norm == "fro":
+        return np.sqrt((diff * diff).sum(axis=(1, 2)))
+    if norm == "spectral":
+        return np.array([np.linalg.norm(d, ord=2) for d in diff])
+    raise ValueError(norm)
+
+
+def cov_bias(M: np.ndarray, eps: float = COV_EPS) -> np.ndarray:
+    """The routing prior log(M_j + eps)  ([PISA] Eq. 11)."""
+    return np.log(M + eps)
+
+
+def route_topk(qbar, kbar, scale, topk, band, w_rank=None, band_mode="additive", n_sink=0, bias=None):
     """Per query block, the top-k KV blocks by pooled score.
 
-    r_ij = s qbar_i . kbar_j (+ w_rank_ij)   ([PISA] Algorithm 1 step 2 with
-    Eq. 11 minus its covariance term, R7; [PWT] router with min(w, ln B)).
+    r_ij = s qbar_i . kbar_j (+ w_rank_ij) (+ bias_j)   ([PISA] Algorithm 1
+    step 2 with Eq. 11, R7; [PWT] router with min(w, ln B); bias_j the
+    covariance prior log(M_j + eps) of R19 when given).
     Band_i = {j : |i-j| <= band} is forced exact ([PWT] knobs: band=b).
     additive (R9): Top_i = the min(topk, |Cand_i|) best of Cand_i = all \\ Band_i
     \\ Sinks, Sinks = {j < n_sink} (R16).
@@ -166,6 +196,8 @@ def route_topk(qbar, kbar, scale, topk, band, w_rank=None, band_mode="additive",
     r = scale * (qbar @ kbar.T)
     if w_rank is not None:
         r = r + w_rank
+    if bias is not None:
+        r = r + np.asarray(bias)[None, :]
     idx = np.full((Nq, topk), -1, dtype=np.int32)
     for i in range(Nq):
         if band_mode == "additive":
@@ -202,7 +234,8 @@ def dense_attention(q, k, v, scale):
 
 def pisa_forward_head(q, k, v, *, B=64, scale=None, topk, band=1, second_order=False,
                       first_order="global", sparse_only=False, routing=None,
-                      query_blocks=None, band_mode="additive", return_parts=False, n_sink=0):
+                      query_blocks=None, band_mode="additive", return_parts=False, n_sink=0,
+                      cov_bias=False, cov_norm="fro"):
     """PISA forward for one (batch, head); q, k, v are [T, D] float64.
 
     Per query block i and query row t (q' = s q_t):
@@ -225,6 +258,7 @@ def pisa_forward_head(q, k, v, *, B=64, scale=None, topk, band=1, second_order=F
     routing: None (computed here) or an [N, topk] table (-1 padded) that is
     used as Top_i verbatim ("fed the GPU's routing").
     n_sink: the first n_sink KV blocks are exact for every query block (R16).
+    cov_bias: route with the covariance prior log(M_j + eps) (R19).
     query_blocks: iterable of block indices to evaluate (others stay NaN).
     Returns o [T, D] (and a dict of intermediate quantities if return_parts).
     """
@@ -233,14 +267,16 @@ def pisa_forward_head(q, k, v, *, B=64, scale=None, topk, band=1, second_order=F
         scale = 1.0 / math.sqrt(D)
     N = num_blocks(T, B)
     sl = block_slices(T, B)
-    st = kv_block_stats(k, v, B, per_block_H=(first_order == "blockwise"))
+    st = kv_block_stats(k, v, B, per_block_H=(first_order == "blockwise" or cov_bias))
     qbar, q2bar = pool_queries(q, B, scale)
     if second_order:
         w, w_gated, w_rank = second_order_w(q2bar, st.sig2, B)
     else:
         w = w_gated = w_rank = None
+    M = block_heterogeneity(st.Hj, cov_norm) if cov_bias else None
     if routing is None:
-        idx, _ = route_topk(qbar, st.kbar, scale, topk, band, w_rank, band_mode, n_sink)
+        idx, _ = route_topk(qbar, st.kbar, scale, topk, band, w_rank, band_mode, n_sink,
+                            bias=cov_bias_fn(M) if cov_bias else None)
     else:
         idx = np.asarray(routing)
     lnn = np.log(st.n)
@@ -288,7 +324,7 @@ def pisa_forward_head(q, k, v, *, B=64, scale=None, topk, band=1, second_order=F
         parts["den"][a0:a1] = den
         parts["m"][a0:a1] = m
     if return_parts:
-        parts.update(stats=st, qbar=qbar, q2bar=q2bar, w=w, w_gated=w_gated, w_rank=w_rank)
+        parts.update(stats=st, qbar=qbar, q2bar=q2bar, w=w, w_gated=w_gated, w_rank=w_rank, M=M)
         return out, parts
     return out
 
@@ -301,3 +337,6 @@ def pisa_forward(q, k, v, **kw):
         for h in range(Hh):
             o[b, h] = pisa_forward_head(q[b, h], k[b, h], v[b, h], **kw)
     return o
+
+
+cov_bias_fn = cov_bias   # the function, under a name the keyword argument does not shadow

@@ -352,6 +352,113 @@ def test_pooled_query_scale_decides_second_order_routing():
         assert O.route_topk(bad, st.kbar, s, 1, band=0, w_rank=wr)[0][3].tolist() == [want]
 
 
+# ---------------------------------------------------------------- covariance-aware routing (R19)
+
+def _equal_block_matrices_case(T=256, B=16, D=4, seed=5):
+    """Every block has the same in-block key deviations and the same V rows,
+    so every H_j is the same matrix; the block means differ."""
+    r = np.random.default_rng(seed)
+    dev = r.standard_normal((B, D))
+    dev -= dev.mean(axis=0)
+    vrows = r.standard_normal((B, D))
+    N = T // B
+    k = np.concatenate([r.standard_normal(D)[None] * 2 + dev for _ in range(N)])
+    v = np.tile(vrows, (N, 1))
+    q = r.standard_normal((T, D))
+    return q, k, v
+
+
+def test_cov_bias_equal_block_matrices_leave_routing_unchanged():
+    """All H_j equal => M_j = ||H_j - Hbar|| = 0 for every block => the prior
+    log(M_j + eps) is the same for every block and the ranking is that of the
+    plain pooled score ([PISA] Eq. 11)."""
+    q, k, v = _equal_block_matrices_case()
+    st = O.kv_block_stats(k, v, 16, per_block_H=True)
+    M = O.block_heterogeneity(st.Hj)
+    assert np.abs(M).max() < 1e-12
+    s = 0.5
+    qbar, _ = O.pool_queries(q, 16, s)
+    plain, _ = O.route_topk(qbar, st.kbar, s, 3, band=1)
+    biased, _ = O.route_topk(qbar, st.kbar, s, 3, band=1, bias=O.cov_bias(M))
+    assert np.array_equal(plain, biased)
+    assert np.array_equal(O.pisa_forward_head(q, k, v, B=16, scale=s, topk=3, cov_bias=True, return_parts=True)[1]["idx"],
+                          plain)
+
+
+def test_cov_bias_hand_worked_scalar_blocks():
+    """D = 1, B = 2: H_j is the scalar sum_n (k_n - kbar_j) v_n.
+      block 0: k (1, -1), v (1, 0)  ->  kbar 0, H_0 = 1
+      block 1: k (2, 2),  v (5, 7)  ->  kbar 2, H_1 = 0
+      block 2: k (0, 2),  v (0, 3)  ->  kbar 1, H_2 = (-1)(0) + (1)(3) = 3
+      block 3: k (4, 4),  v (1, 1)  ->  kbar 4, H_3 = 0
+    Hbar = (1 + 0 + 3 + 0) / 4 = 1, so M = (0, 1, 2, 1) and the prior is
+    log(M + eps). Query block 3 (rows 0.5, 0.5: qbar 0.5), band 0, scale 1,
+    top-1 over blocks 0, 1, 2 with pooled scores 0.5 kbar = (0, 1, 0.5):
+    without the prior block 1 wins (1 > 0.5 > 0); with it the scores are
+    (log 1e-6, 1 + log(1 + 1e-6), 0.5 + log(2 + 1e-6)) = (-13.8, 1.000001,
+    1.193148): block 2."""
+    k = np.array([1, -1, 2, 2, 0, 2, 4, 4], float)[:, None]
+    v = np.array([1, 0, 5, 7, 0, 3, 1, 1], float)[:, None]
+    q = np.full((8, 1), 0.5)
+    st = O.kv_block_stats(k, v, 2, per_block_H=True)
+    assert st.Hj[:, 0, 0].tolist() == [1.0, 0.0, 3.0, 0.0]
+    M = O.block_heterogeneity(st.Hj)
+    assert M.tolist() == [0.0, 1.0, 2.0, 1.0]
+    b = O.cov_bias(M)
+    np.testing.assert_allclose(b, [math.log(1e-6), math.log(1 + 1e-6), math.log(2 + 1e-6), math.log(1 + 1e-6)],
+                               rtol=1e-15)
+    qbar, _ = O.pool_queries(q, 2, 1.0)
+    plain, _ = O.route_topk(qbar, st.kbar, 1.0, 1, band=0)
+    assert plain[3].tolist() == [1]
+    biased, r = O.route_topk(qbar, st.kbar, 1.0, 1, band=0, bias=b)
+    assert biased[3].tolist() == [2]
+    np.testing.assert_allclose(r[3, :3], [math.log(1e-6), 1 + math.log(1 + 1e-6), 0.5 + math.log(2 + 1e-6)],
+                               rtol=1e-15)
+    _, parts = O.pisa_forward_head(q, k, v, B=2, scale=1.0, topk=1, band=0, cov_bias=True, return_parts=True)
+    assert parts["idx"][3].tolist() == [2]
+    assert parts["M"].tolist() == [0.0, 1.0, 2.0, 1.0]
+
+
+def test_cov_norm_frobenius_against_spectral():
+    """R19 takes the Frobenius norm: for H_j - Hbar = +-diag(3, 4) it is 5 (the
+    spectral norm, the alternative reading, is 4)."""
+    Hj = np.array([[[3.0, 0.0], [0.0, 4.0]], [[-3.0, 0.0], [0.0, -4.0]]])
+    assert O.block_heterogeneity(Hj, "fro").tolist() == [5.0, 5.0]
+    np.testing.assert_allclose(O.block_heterogeneity(Hj, "spectral"), [4.0, 4.0], rtol=1e-15)
+
+
+def test_cov_heterogeneity_invariances():
+    """H_j is centred on the block mean: k -> k + c and v -> v + c leave every
+    H_j, hence M_j, unchanged; v -> a v scales M_j by |a|."""
+    r = np.random.default_rng(11)
+    k, v = r.standard_normal((200, 8)), r.standard_normal((200, 8))
+    M = O.block_heterogeneity(O.kv_block_stats(k, v, 32, per_block_H=True).Hj)
+    c = r.standard_normal(8)
+    Mk = O.block_heterogeneity(O.kv_block_stats(k + c, v, 32, per_block_H=True).Hj)
+    Mv = O.block_heterogeneity(O.kv_block_stats(k, v + c, 32, per_block_H=True).Hj)
+    Ma = O.block_heterogeneity(O.kv_block_stats(k, -2.5 * v, 32, per_block_H=True).Hj)
+    np.testing.assert_allclose(Mk, M, rtol=1e-12)
+    np.testing.assert_allclose(Mv, M, rtol=1e-12)
+    np.testing.assert_allclose(Ma, 2.5 * M, rtol=1e-12)
+
+
+def test_cov_heterogeneity_brute_force():
+    """M_j from scalar loops over rows and matrix entries (ragged last block)."""
+    r = np.random.default_rng(12)
+    T, D, B = 45, 3, 8
+    k, v = r.standard_normal((T, D)), r.standard_normal((T, D))
+    N = -(-T // B)
+    Hs = []
+    for j in range(N):
+        rows = range(j * B, min(T, j * B + B))
+        kb = [sum(k[n][a] for n in rows) / len(rows) for a in range(D)]
+        Hs.append([[sum((k[n][a] - kb[a]) * v[n][b] for n in rows) for b in range(D)] for a in range(D)])
+    Hbar = [[sum(Hs[j][a][b] for j in range(N)) / N for b in range(D)] for a in range(D)]
+    want = [math.sqrt(sum((Hs[j][a][b] - Hbar[a][b]) ** 2 for a in range(D) for b in range(D))) for j in range(N)]
+    got = O.block_heterogeneity(O.kv_block_stats(k, v, B, per_block_H=True).Hj)
+    np.testing.assert_allclose(got, want, rtol=1e-12)
+
+
 # ---------------------------------------------------------------- routing
 
 def test_routing_known_ranking_band_ties_padding():

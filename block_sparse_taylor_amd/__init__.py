@@ -87,14 +87,15 @@ class PisaStats:
     ksig2: torch.Tensor | None    # fp64 [B,H,N,D] (second order)
     hsum: torch.Tensor            # fp32 [B,H,D,D]
     operands: torch.Tensor | None = None   # uint8 [pisa_operands_bytes]
+    hnorm: torch.Tensor | None = None      # fp64 [B,H,N]: ||H_j - Hbar||_F (covariance prior)
 
     def as_c(self) -> _lib.Stats:
         return _lib.Stats(_ptr(self.qbar), _ptr(self.q2bar), _ptr(self.kbar), _ptr(self.vsum),
-                          _ptr(self.ksig2), _ptr(self.hsum))
+                          _ptr(self.ksig2), _ptr(self.hsum), _ptr(self.hnorm))
 
     def statistics_only(self) -> "PisaStats":
         """The same statistics without the operand buffer (what the backward reads)."""
-        return PisaStats(self.qbar, self.q2bar, self.kbar, self.vsum, self.ksig2, self.hsum, None)
+        return PisaStats(self.qbar, self.q2bar, self.kbar, self.vsum, self.ksig2, self.hsum, None, self.hnorm)
 
 
 def _contig(*ts):
@@ -111,7 +112,7 @@ def alloc_operands(x: torch.Tensor) -> torch.Tensor:
     return torch.empty(max(16, operands_bytes(x)), dtype=torch.uint8, device=x.device)
 
 
-def alloc_stats(k: torch.Tensor, second_order: bool, operands: bool = True) -> PisaStats:
+def alloc_stats(k: torch.Tensor, second_order: bool, operands: bool = True, cov_bias: bool = False) -> PisaStats:
     B, H, T, D = k.shape
     N = num_blocks(T)
     dev = k.device
@@ -124,6 +125,7 @@ def alloc_stats(k: torch.Tensor, second_order: bool, operands: bool = True) -> P
         ksig2=torch.empty(B, H, N, D, **f64) if second_order else None,
         hsum=torch.empty(B, H, D, D, dtype=torch.float32, device=dev),
         operands=alloc_operands(k) if operands else None,
+        hnorm=torch.empty(B, H, N, **f64) if cov_bias else None,
     )
 
 
@@ -153,15 +155,18 @@ def stats_workspace(k: torch.Tensor, scale=None) -> torch.Tensor:
 
 
 def pisa_block_stats(q, k, v, second_order=False, scale=None, out: PisaStats | None = None,
-                     workspace: torch.Tensor | None = None) -> PisaStats:
+                     workspace: torch.Tensor | None = None, cov_bias=False) -> PisaStats:
     lib = library()
     _contig(q, k, v)
     sh = _shape(k, scale)
-    out = out or alloc_stats(k, second_order)
+    out = out or alloc_stats(k, second_order, cov_bias=cov_bias)
     if out.operands is None:
         out.operands = alloc_operands(k)
+    if cov_bias and out.hnorm is None:
+        B, H, T, _ = k.shape
+        out.hnorm = torch.empty(B, H, num_blocks(T), dtype=torch.float64, device=k.device)
     ws = workspace if workspace is not None else stats_workspace(k, scale)
-    prm = _lib.Params(0, 0, int(second_order), 1, 0)
+    prm = _lib.Params(0, 0, int(second_order), 1, 0, 0, int(cov_bias))
     cs = out.as_c()
     _lib.check("pisa_block_stats", lib.pisa_block_stats(
         ctypes.byref(sh), ctypes.byref(prm), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(cs),
@@ -210,8 +215,10 @@ def _operands(stats, required):
 
 
 def pisa_route_topk(q, stats: PisaStats, topk: int, band: int = 1, second_order=False, scale=None,
-                    idx: torch.Tensor | None = None, wgate: torch.Tensor | None = None, n_sink: int = 0):
-    """q is used for its shape and device only; routing reads the pooled statistics."""
+                    idx: torch.Tensor | None = None, wgate: torch.Tensor | None = None, n_sink: int = 0,
+                    cov_bias=False):
+    """q is used for its shape and device only; routing reads the pooled
+    statistics (and with cov_bias the block heterogeneity stats.hnorm)."""
     lib = library()
     sh = _shape(q, scale)
     B, H, T, D = q.shape
@@ -220,7 +227,7 @@ def pisa_route_topk(q, stats: PisaStats, topk: int, band: int = 1, second_order=
         idx = torch.empty(B, H, N, topk, dtype=torch.int32, device=q.device)
     if second_order and wgate is None:
         wgate = torch.empty(B, H, N, N, dtype=torch.float32, device=q.device)
-    prm = _lib.Params(int(topk), int(band), int(second_order), 1, 0, int(n_sink))
+    prm = _lib.Params(int(topk), int(band), int(second_order), 1, 0, int(n_sink), int(cov_bias))
     cs = stats.as_c()
     ops, nops = _operands(stats, True)
     _lib.check("pisa_route_topk", lib.pisa_route_topk(
@@ -328,10 +335,10 @@ class _Attention(torch.autograd.Function):
     gate of the forward (argument marshalling only)."""
 
     @staticmethod
-    def forward(ctx, q, k, v, topk, band, second_order, scale, n_sink):
-        st = pisa_block_stats(q, k, v, second_order=second_order, scale=scale)
+    def forward(ctx, q, k, v, topk, band, second_order, scale, n_sink, cov_bias):
+        st = pisa_block_stats(q, k, v, second_order=second_order, scale=scale, cov_bias=cov_bias)
         idx, wg = pisa_route_topk(q, st, topk, band=band, second_order=second_order, scale=scale,
-                                  n_sink=n_sink)
+                                  n_sink=n_sink, cov_bias=cov_bias)
         idx = idx if topk else None
         o = pisa_attn_fwd(q, k, v, st, idx, wg, band=band, second_order=second_order, scale=scale,
                           n_sink=n_sink)
@@ -348,7 +355,7 @@ class _Attention(torch.autograd.Function):
         st = PisaStats(None, q2bar, kbar, vsum, ksig2, hsum, None)
         dq, dk, dv = pisa_attn_bwd(q, k, v, o, do.contiguous(), st, idx, wg, band=band,
                                    second_order=so, scale=scale, n_sink=n_sink)
-        return dq, dk, dv, None, None, None, None, None
+        return dq, dk, dv, None, None, None, None, None, None
 
 
 class _Gather(torch.autograd.Function):
@@ -385,7 +392,8 @@ def piecewise_sparse_attention(q, k, v, density=0.125, variant="pisa", band=1, s
     q, k, v: [B, H, T, D] bf16 or fp32 on the GPU. topk = floor(density * N)
     routed blocks per query block, plus the +-band and the first
     ``n_sink_blocks`` KV blocks (e.g. an MMDiT text prefix), are computed
-    exactly.
+    exactly. cov_bias=True routes with the covariance-aware prior
+    log(||H_j - Hbar||_F + 1e-6) of the PISA paper's Eq. 11.
     With reorder="morton", q, k, v are token-major [B, T, H, D] in raster
     order over ``prefix`` fixed tokens then ``grid`` (slowest axis first); the
     tokens are gathered into Z-order (and [B, H, T, D]) before the operator and
@@ -394,8 +402,6 @@ def piecewise_sparse_attention(q, k, v, density=0.125, variant="pisa", band=1, s
     pisa_attn_bwd (the routing and gate of the forward held constant) and the
     reorder's adjoint.
     """
-    if cov_bias:
-        raise NotImplementedError("the covariance-aware routing bias is not built")
     if reorder not in ("none", "morton"):
         raise ValueError(reorder)
     if variant not in ("pisa", "pwt"):
@@ -413,5 +419,5 @@ def piecewise_sparse_attention(q, k, v, density=0.125, variant="pisa", band=1, s
     topk = topk_for_density(density, N)
     topk = min(topk, N)
     n_sink_blocks = min(int(n_sink_blocks), N)
-    o = _Attention.apply(q, k, v, topk, band, so, scale, n_sink_blocks)
+    o = _Attention.apply(q, k, v, topk, band, so, scale, n_sink_blocks, bool(cov_bias))
     return o if perm is None else _Scatter.apply(o, perm)

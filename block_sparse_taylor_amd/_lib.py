@@ -24,6 +24,7 @@ EXPORTED = (
     "pisa_prepare_operands", "pisa_block_stats_noalloc",
 )
 STATS_SCRATCH_BYTES = 32 << 20   # PISA_STATS_SCRATCH_BYTES
+COV_EPS = 1e-6                   # PISA_COV_EPS
 # pisa_operand_t: the arrangements inside the operand buffer
 OPERANDS = ("kbar_c", "vbar_c", "kbar_r", "ksig2_r", "kpack", "kbpack", "hpack")
 
@@ -37,12 +38,13 @@ class Shape(ctypes.Structure):
 class Params(ctypes.Structure):
     _fields_ = [("topk", ctypes.c_int32), ("band", ctypes.c_int32), ("second_order", ctypes.c_int32),
                 ("first_order", ctypes.c_int32), ("phase_mask", ctypes.c_int32),
-                ("n_sink", ctypes.c_int32)]
+                ("n_sink", ctypes.c_int32), ("cov_bias", ctypes.c_int32)]
 
 
 class Stats(ctypes.Structure):
     _fields_ = [("qbar", ctypes.c_void_p), ("q2bar", ctypes.c_void_p), ("kbar", ctypes.c_void_p),
-                ("vsum", ctypes.c_void_p), ("ksig2", ctypes.c_void_p), ("hsum", ctypes.c_void_p)]
+                ("vsum", ctypes.c_void_p), ("ksig2", ctypes.c_void_p), ("hsum", ctypes.c_void_p),
+                ("hnorm", ctypes.c_void_p)]
 
 
 class PisaError(RuntimeError):

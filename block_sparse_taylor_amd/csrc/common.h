@@ -66,6 +66,7 @@ struct StatsView {
     float* vsum;
     double* ksig2;
     float* hsum;
+    double* hnorm;     // ||H_j - Hbar||_F per block (covariance prior)  [BH,N]
     void* kbar_c;      // kbar rounded to the input dtype              [BH,N,D]
     void* vbar_c;      // vsum / n rounded to the input dtype          [BH,N,D]
     void* kpack;       // bf16: K in the fused kernel's operand order  [BH,N,64 D]
@@ -98,10 +99,16 @@ OperandLayout operand_layout(const Geom& g, int dtype);
 StatsView stats_view(const Geom& g, int dtype, const pisa_stats_t* st, const void* operands);
 
 // Kernel launchers (return hipSuccess or the launch error).
-hipError_t launch_block_stats(const Geom& g, int dtype, int second_order, const void* q, const void* k,
-                              const void* v, const StatsView* out, void* workspace,
+hipError_t launch_block_stats(const Geom& g, int dtype, int second_order, int cov_bias, const void* q,
+                              const void* k, const void* v, const StatsView* out, void* workspace,
                               hipStream_t stream);
+// Workspace of pisa_block_stats: the larger of its two uses (fp32 partial H
+// sums; with the covariance prior, fp64 partial sums and Hbar).
 size_t stats_workspace_bytes(const Geom& g);
+size_t stats_workspace_bytes_for(const Geom& g, int cov_bias);
+size_t cov_workspace_bytes(const Geom& g, int stats_groups);
+hipError_t launch_cov_norm(const Geom& g, int dtype, const void* k, const void* v, const double* kbar,
+                           double* hnorm, void* workspace, int stats_groups, hipStream_t stream);
 // This device's copy of the statistics pass's static scratch
 // (PISA_STATS_SCRATCH_BYTES), its address taken once per device.
 hipError_t stats_scratch(void** ptr);

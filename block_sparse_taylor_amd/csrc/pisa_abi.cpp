@@ -42,6 +42,7 @@ pisa_status_t check_params(const pisa_params_t* p, const Geom& g) {
     if (p->first_order != 0 && p->first_order != 1) return PISA_ERR_PARAM;
     if (p->phase_mask < 0 || p->phase_mask > 7) return PISA_ERR_PARAM;
     if (p->n_sink < 0 || p->n_sink > g.N) return PISA_ERR_PARAM;
+    if (p->cov_bias != 0 && p->cov_bias != 1) return PISA_ERR_PARAM;
     return PISA_OK;
 }
 
@@ -156,6 +157,7 @@ StatsView stats_view(const Geom& g, int dtype, const pisa_stats_t* st, const voi
     v.vsum = st->vsum;
     v.ksig2 = st->ksig2;
     v.hsum = st->hsum;
+    v.hnorm = st->hnorm;
     if (operands) {
         const OperandLayout L = operand_layout(g, dtype);
         char* b = static_cast<char*>(const_cast<void*>(operands));
@@ -229,16 +231,17 @@ pisa_status_t pisa_block_stats(const pisa_shape_t* shape, const pisa_params_t* p
     PISA_TRY(check_ptr(k));
     PISA_TRY(check_ptr(v));
     PISA_TRY(check_stats(out, params->second_order, true));
+    if (params->cov_bias) PISA_TRY(check_ptr(out->hnorm));
     PISA_TRY(check_operands(g, shape->dtype, operands, operands_bytes));
     PISA_TRY(check_ptr(workspace));
-    if (workspace_bytes < stats_workspace_bytes(g)) return PISA_ERR_WORKSPACE;
+    if (workspace_bytes < stats_workspace_bytes_for(g, params->cov_bias)) return PISA_ERR_WORKSPACE;
     const size_t tb = tensor_bytes(g, shape->dtype), ob = operand_layout(g, shape->dtype).total;
     for (const void* in : {q, k, v})
         if (overlap(operands, ob, in, tb) || overlap(workspace, workspace_bytes, in, tb)) return PISA_ERR_PARAM;
     if (overlap(operands, ob, workspace, workspace_bytes)) return PISA_ERR_PARAM;
     const StatsView sv = stats_view(g, shape->dtype, out, operands);
-    return from_hip(launch_block_stats(g, shape->dtype, params->second_order, q, k, v, &sv, workspace,
-                                       static_cast<hipStream_t>(stream)));
+    return from_hip(launch_block_stats(g, shape->dtype, params->second_order, params->cov_bias, q, k, v, &sv,
+                                       workspace, static_cast<hipStream_t>(stream)));
 }
 
 pisa_status_t pisa_block_stats_noalloc(const pisa_shape_t* shape, const pisa_params_t* params, const void* q,
@@ -251,15 +254,16 @@ pisa_status_t pisa_block_stats_noalloc(const pisa_shape_t* shape, const pisa_par
     PISA_TRY(check_ptr(k));
     PISA_TRY(check_ptr(v));
     PISA_TRY(check_stats(out, params->second_order, true));
+    if (params->cov_bias) PISA_TRY(check_ptr(out->hnorm));
     PISA_TRY(check_operands(g, shape->dtype, operands, operands_bytes));
-    if (stats_workspace_bytes(g) > PISA_STATS_SCRATCH_BYTES) return PISA_ERR_WORKSPACE;
+    if (stats_workspace_bytes_for(g, params->cov_bias) > PISA_STATS_SCRATCH_BYTES) return PISA_ERR_WORKSPACE;
     const size_t tb = tensor_bytes(g, shape->dtype), ob = operand_layout(g, shape->dtype).total;
     for (const void* in : {q, k, v})
         if (overlap(operands, ob, in, tb)) return PISA_ERR_PARAM;
     void* ws = nullptr;
     PISA_TRY(from_hip(stats_scratch(&ws)));
     const StatsView sv = stats_view(g, shape->dtype, out, operands);
-    return from_hip(launch_block_stats(g, shape->dtype, params->second_order, q, k, v, &sv, ws,
+    return from_hip(launch_block_stats(g, shape->dtype, params->second_order, params->cov_bias, q, k, v, &sv, ws,
                                        static_cast<hipStream_t>(stream)));
 }
 
@@ -286,6 +290,7 @@ pisa_status_t pisa_route_topk(const pisa_shape_t* shape, const pisa_params_t* pa
     PISA_TRY(check_shape(shape, &g));
     PISA_TRY(check_params(params, g));
     PISA_TRY(check_stats(stats, params->second_order, true));
+    if (params->cov_bias) PISA_TRY(check_ptr(stats->hnorm));
     PISA_TRY(check_operands(g, shape->dtype, operands, operands_bytes));
     if (params->second_order) PISA_TRY(check_ptr(wgate));
     if (params->topk > 0) PISA_TRY(check_ptr(idx));

@@ -3,7 +3,9 @@
 // Piecewise-Taylor-Attention README: +-band forced exact, clamped ranking
 // spread min(w, ln B), set-identical top-k).
 //
-//   r_ij = s qbar_i . kbar_j  [+ min(w_ij, ln B)],   w_ij = 1/2 q2bar_i . ksig2_j
+//   r_ij = s qbar_i . kbar_j  [+ min(w_ij, ln B)]  [+ log(M_j + eps)],
+//   w_ij = 1/2 q2bar_i . ksig2_j,  M_j = hnorm_j (the covariance-aware prior of
+//   PISA Eq. 11, when asked for)
 //   Top_i = the topk largest r_ij over |i - j| > band and j >= n_sink (the
 //   band and the README's sink blocks are forced exact), ties to the lower j.
 //
@@ -34,7 +36,12 @@ namespace {
 constexpr int kQB = 16;               // query blocks per workgroup
 constexpr int kAmbCap = 64;           // close calls ranked pairwise per row (more: radix select)
 constexpr int kLdsMax = 160 * 1024;   // LDS of a gfx950 workgroup
+constexpr int kLdsStatic = 256;        // at most this much static LDS beside the dynamic part
 constexpr double kU = 5.9604644775390625e-08;   // 2^-24
+
+// The covariance prior of block j, in fp64 (the same expression everywhere a
+// score is formed, so fp32 and fp64 scores see the same value).
+__device__ __forceinline__ double cov_prior(const double* hn, int j) { return log(hn[j] + PISA_COV_EPS); }
 
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f4_t;
 
@@ -169,11 +176,11 @@ __host__ __device__ constexpr int route_waves(int kpl) { return kpl > 16 ? 8 : 4
 
 // KPL: keys per lane of a score row (N <= 64 KPL); rows of up to 1024 blocks
 // without the second order fit four waves per SIMD.
-template <int D, bool SO, int KPL>
+template <int D, bool SO, int KPL, bool COV>
 __global__ __launch_bounds__(64 * route_waves(KPL)) __attribute__((amdgpu_waves_per_eu(SO || KPL > 16 ? 2 : 4))) void route_fast_kernel(
     const double* __restrict__ qbar, const double* __restrict__ q2bar, const double* __restrict__ kbar,
     const float* __restrict__ kbar_r, const double* __restrict__ ksig2, const float* __restrict__ ksig2_r,
-    int N, double s64, int topk, int band, int n_sink,
+    const double* __restrict__ hnorm, int N, double s64, int topk, int band, int n_sink,
     int32_t* __restrict__ idx, float* __restrict__ wgate) {
     constexpr int KS = D / 4;       // 16x16x4 k-steps; MFMA k-slot (ks, l/16) <-> dim (D/4)(l/16) + ks
     constexpr bool second_order = SO;
@@ -187,6 +194,8 @@ __global__ __launch_bounds__(64 * route_waves(KPL)) __attribute__((amdgpu_waves_
     double* amb_r_s = reinterpret_cast<double*>(amb_j_s + NWV * kAmbCap);
     uint32_t* take_s = reinterpret_cast<uint32_t*>(amb_r_s + NWV * kAmbCap);
     __shared__ float kmax_s[NWV];
+    __shared__ float bmax_s[NWV];
+    static_assert(2 * 4 * NWV <= kLdsStatic, "static LDS beyond the launcher's reserve");
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -226,7 +235,9 @@ __global__ __launch_bounds__(64 * route_waves(KPL)) __attribute__((amdgpu_waves_
     for (int ks = 0; ks < KS; ++ks) a2[ks] = SO ? (float)q2_s[m16 * D + (D / 4) * g4 + ks] : 0.f;
     const double* kb = kbar + bh * (int64_t)N * D;
     const double* sg = SO ? ksig2 + bh * (int64_t)N * D : nullptr;
+    const double* hn = COV ? hnorm + bh * (int64_t)N : nullptr;   // covariance prior
     float kmax2 = 0.f;
+    float bmax = 0.f;   // max |prior| over this wave's columns (of the fp32 roundings)
     const int NC = (N + 15) / 16;
     const float4* kr4 = reinterpret_cast<const float4*>(kbar_r + bh * (int64_t)NC * 16 * D);
     const float4* sr4 = SO ? reinterpret_cast<const float4*>(ksig2_r + bh * (int64_t)NC * 16 * D) : nullptr;
@@ -272,6 +283,11 @@ __global__ __launch_bounds__(64 * route_waves(KPL)) __attribute__((amdgpu_waves_
         n2 += __shfl_xor(n2, 16);
         n2 += __shfl_xor(n2, 32);
         kmax2 = fmaxf(kmax2, n2);
+        float prior = 0.f;
+        if (COV && ok) {
+            prior = (float)cov_prior(hn, col);
+            bmax = fmaxf(bmax, fabsf(prior));
+        }
         // C layout: lane holds column m16, rows 4 g4 + e
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -292,6 +308,7 @@ __global__ __launch_bounds__(64 * route_waves(KPL)) __attribute__((amdgpu_waves_
                 wgate[(bh * N + i0 + r) * (int64_t)N + col] = wg;
                 sc += fminf(w, lnBf);
             }
+            sc += prior;
             if (ok) score_s[r * NP + col] = sc;
         }
     }
@@ -299,11 +316,21 @@ __global__ __launch_bounds__(64 * route_waves(KPL)) __attribute__((amdgpu_waves_
     kmax2 = fmaxf(kmax2, __shfl_xor(kmax2, 2));
     kmax2 = fmaxf(kmax2, __shfl_xor(kmax2, 4));
     kmax2 = fmaxf(kmax2, __shfl_xor(kmax2, 8));
-    if (lane == 0) kmax_s[wave] = kmax2;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) bmax = fmaxf(bmax, __shfl_xor(bmax, off));
+    if (lane == 0) {
+        kmax_s[wave] = kmax2;
+        bmax_s[wave] = bmax;
+    }
     __syncthreads();
     float kmx = kmax_s[0];
+    float bmxf = bmax_s[0];
 #pragma unroll
-    for (int w = 1; w < NWV; ++w) kmx = fmaxf(kmx, kmax_s[w]);
+    for (int w = 1; w < NWV; ++w) {
+        kmx = fmaxf(kmx, kmax_s[w]);
+        bmxf = fmaxf(bmxf, bmax_s[w]);
+    }
+    const double bmx = (double)bmxf * (1.0 + 1e-6);   // bounds |prior| in fp64 too
     const double kmax = sqrt((double)kmx) *
                         (1.0 + 1e-6);
 
@@ -337,7 +364,9 @@ __global__ __launch_bounds__(64 * route_waves(KPL)) __attribute__((amdgpu_waves_
             for (int d = lane; d < D; d += 64) qn += qg[d] * qg[d];
 #pragma unroll
             for (int off = 32; off > 0; off >>= 1) qn += __shfl_xor(qn, off);
-            const double bound = s64 * sqrt(qn) * kmax + (second_order ? lnB : 0.0);
+            // |r| bound: the dot product, the clamped spread, the prior (the
+            // latter two each add at most two fp32 roundings of their size)
+            const double bound = s64 * sqrt(qn) * kmax + (second_order ? lnB : 0.0) + bmx;
             const float eps = (float)(4.0 * (D + 8) * kU * bound) + 1e-30f;
             int need_eq;
             const uint32_t tk = wave_select32<KPL>(kv, k, &need_eq);
@@ -369,6 +398,7 @@ __global__ __launch_bounds__(64 * route_waves(KPL)) __attribute__((amdgpu_waves_
                     for (int d = 0; d < D; ++d) w = fma(q2_s[r * D + d], sq[d], w);
                     rr += fmin(0.5 * w, lnB);
                 }
+                if (COV) rr += cov_prior(hn, j);
                 return rr;
             };
             // the same score with the whole wave on one block: each lane takes
@@ -394,6 +424,7 @@ __global__ __launch_bounds__(64 * route_waves(KPL)) __attribute__((amdgpu_waves_
                 }
                 double rr = s64 * dot;
                 if (second_order) rr += fmin(0.5 * w, lnB);
+                if (COV) rr += cov_prior(hn, j);
                 return rr;
             };
             auto ambiguous = [&](int j) {
@@ -494,8 +525,8 @@ __device__ __forceinline__ int block_scan(int x, int* scratch, int* excl) {
 template <int D>
 __global__ __launch_bounds__(kThreads) void route_slow_kernel(
     const double* __restrict__ qbar, const double* __restrict__ q2bar, const double* __restrict__ kbar,
-    const double* __restrict__ ksig2, int N, double s64, int topk, int band, int n_sink, int second_order,
-    int32_t* __restrict__ idx, float* __restrict__ wgate) {
+    const double* __restrict__ ksig2, const double* __restrict__ hnorm, int N, double s64, int topk, int band,
+    int n_sink, int second_order, int32_t* __restrict__ idx, float* __restrict__ wgate) {
     __shared__ double qbar_s[D];
     __shared__ double q2_s[D];
     __shared__ uint64_t key_s[kMaxN];
@@ -530,6 +561,7 @@ __global__ __launch_bounds__(kThreads) void route_slow_kernel(
             r += fmin(w, lnB);
             wrow[j] = (float)(w > lnB ? 0.0 : w);
         }
+        if (hnorm) r += cov_prior(hnorm + bh * (int64_t)N, j);
         const bool cand = abs(i - j) > band && j >= n_sink;
         key_s[j] = cand ? key64(r) : 0ull;
         ncand += cand;
@@ -593,39 +625,41 @@ hipError_t launch_route_topk(const Geom& g, const pisa_params_t* p, const StatsV
                              int32_t* idx, float* wgate, hipStream_t stream) {
     const int so = p->second_order;
     if (p->topk == 0 && !so) return hipSuccess;
+    const double* hn = p->cov_bias ? st->hnorm : nullptr;
     const int kc = g.N <= 64 * 8 ? 0 : (g.N <= 64 * 16 ? 1 : 2);
     const int nwv = route_waves(kc == 0 ? 8 : (kc == 1 ? 16 : kKeysPerLane));
     const size_t lds = fast_lds_bytes(g.D, g.N, so, nwv);
-    if (lds + 64 <= (size_t)kLdsMax && g.N <= 64 * kKeysPerLane) {
+    if (lds + kLdsStatic <= (size_t)kLdsMax && g.N <= 64 * kKeysPerLane) {
         const dim3 block(64 * nwv);
         using Fn = void (*)(const double*, const double*, const double*, const float*, const double*, const float*,
-                            int, double, int, int, int, int32_t*, float*);
-        static bool attr_set[2][2][3] = {};
-        static const Fn table[2][2][3] = {
-            {{&route_fast_kernel<64, false, 8>, &route_fast_kernel<64, false, 16>,
-              &route_fast_kernel<64, false, kKeysPerLane>},
-             {&route_fast_kernel<64, true, 8>, &route_fast_kernel<64, true, 16>,
-              &route_fast_kernel<64, true, kKeysPerLane>}},
-            {{&route_fast_kernel<128, false, 8>, &route_fast_kernel<128, false, 16>,
-              &route_fast_kernel<128, false, kKeysPerLane>},
-             {&route_fast_kernel<128, true, 8>, &route_fast_kernel<128, true, 16>,
-              &route_fast_kernel<128, true, kKeysPerLane>}}};
-        bool& set = attr_set[g.D == 128][so ? 1 : 0][kc];
-        const Fn fn = table[g.D == 128][so ? 1 : 0][kc];
+                            const double*, int, double, int, int, int, int32_t*, float*);
+        static bool attr_set[2][2][2][3] = {};
+#define PISA_ROUTE_ROW(DD, SO, CV) \
+    {&route_fast_kernel<DD, SO, 8, CV>, &route_fast_kernel<DD, SO, 16, CV>, &route_fast_kernel<DD, SO, kKeysPerLane, CV>}
+        static const Fn table[2][2][2][3] = {
+            {{PISA_ROUTE_ROW(64, false, false), PISA_ROUTE_ROW(64, true, false)},
+             {PISA_ROUTE_ROW(64, false, true), PISA_ROUTE_ROW(64, true, true)}},
+            {{PISA_ROUTE_ROW(128, false, false), PISA_ROUTE_ROW(128, true, false)},
+             {PISA_ROUTE_ROW(128, false, true), PISA_ROUTE_ROW(128, true, true)}}};
+#undef PISA_ROUTE_ROW
+        const int cv = hn ? 1 : 0;
+        bool& set = attr_set[g.D == 128][cv][so ? 1 : 0][kc];
+        const Fn fn = table[g.D == 128][cv][so ? 1 : 0][kc];
         if (!set) {   // opt in to more than 64 KB of dynamic LDS
             const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax - 64);
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                     kLdsMax - kLdsStatic);
             if (e != hipSuccess) return e;
             set = true;
         }
         dim3 grid((g.N + kQB - 1) / kQB, (unsigned)g.BH);
-        hipLaunchKernelGGL(fn, grid, block, lds, stream, st->qbar, st->q2bar, st->kbar, st->kbar_r, st->ksig2, st->ksig2_r, g.N,
-                           g.scale64, p->topk, p->band, p->n_sink, idx, wgate);
+        hipLaunchKernelGGL(fn, grid, block, lds, stream, st->qbar, st->q2bar, st->kbar, st->kbar_r, st->ksig2, st->ksig2_r,
+                           hn, g.N, g.scale64, p->topk, p->band, p->n_sink, idx, wgate);
     } else {
         const dim3 grid(g.N, (unsigned)g.BH), block(kThreads);
 #define PISA_ROUTE_LAUNCH(DD)                                                                      \
     hipLaunchKernelGGL(route_slow_kernel<DD>, grid, block, 0, stream, st->qbar, st->q2bar,         \
-                       st->kbar, st->ksig2, g.N, g.scale64, p->topk, p->band, p->n_sink, so, idx, wgate)
+                       st->kbar, st->ksig2, hn, g.N, g.scale64, p->topk, p->band, p->n_sink, so, idx, wgate)
         if (g.D == 128) PISA_ROUTE_LAUNCH(128);
         else PISA_ROUTE_LAUNCH(64);
 #undef PISA_ROUTE_LAUNCH

@@ -483,9 +483,12 @@ hipError_t stats_scratch(void** ptr) {
     return hipSuccess;
 }
 
-size_t stats_workspace_bytes(const Geom& g) {
-    return (size_t)g.BH * stats_groups(g) * g.D * g.D * sizeof(float);
+size_t stats_workspace_bytes_for(const Geom& g, int cov_bias) {
+    const size_t part = (size_t)g.BH * stats_groups(g) * g.D * g.D * sizeof(float);
+    return cov_bias ? std::max(part, cov_workspace_bytes(g, stats_groups(g))) : part;
 }
+
+size_t stats_workspace_bytes(const Geom& g) { return stats_workspace_bytes_for(g, 1); }
 
 hipError_t launch_prepare_operands(const Geom& g, int dtype, int second_order, const void* k,
                                    const StatsView* st, hipStream_t stream) {
@@ -510,8 +513,8 @@ hipError_t launch_prepare_operands(const Geom& g, int dtype, int second_order, c
     return hipGetLastError();
 }
 
-hipError_t launch_block_stats(const Geom& g, int dtype, int second_order, const void* q, const void* k,
-                              const void* v, const StatsView* st, void* workspace,
+hipError_t launch_block_stats(const Geom& g, int dtype, int second_order, int cov_bias, const void* q,
+                              const void* k, const void* v, const StatsView* st, void* workspace,
                               hipStream_t stream) {
     const int G = stats_groups(g), bpw = stats_bpw(g);
     dim3 grid(G, (unsigned)g.BH), block(kThreads);
@@ -537,7 +540,10 @@ hipError_t launch_block_stats(const Geom& g, int dtype, int second_order, const 
     dim3 rgrid((DD + kThreads - 1) / kThreads, (unsigned)g.BH);
     hipLaunchKernelGGL(hsum_reduce_kernel, rgrid, block, 0, stream, hpart, G, g.D, st->hsum,
                        dtype == PISA_BF16 ? static_cast<bf16_t*>(st->hpack) : nullptr);
-    return hipGetLastError();
+    e = hipGetLastError();
+    if (e != hipSuccess || !cov_bias) return e;
+    // the covariance prior's block norms, after the block means (same workspace)
+    return launch_cov_norm(g, dtype, k, v, st->kbar, st->hnorm, workspace, G, stream);
 }
 
 }  // namespace pisa

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define PISA_ABI_VERSION 11
+#define PISA_ABI_VERSION 12
 
 typedef enum {
     PISA_OK = 0,
@@ -83,7 +83,13 @@ typedef struct {
     int32_t n_sink;       /* the first n_sink KV blocks are exact for every query
                              block, like the band (README knobs: n_sink_blocks,
                              e.g. an MMDiT text prefix); 0..N                    */
+    int32_t cov_bias;     /* 1: covariance-aware routing (Eq. 11): the routing
+                             score gains log(M_j + PISA_COV_EPS), M_j = hnorm[j];
+                             pisa_block_stats then also computes hnorm        */
 } pisa_params_t;
+
+/* eps of the covariance prior log(M_j + eps) (Eq. 11 leaves it unvalued) */
+#define PISA_COV_EPS 1e-6
 
 /*
  * Block statistics (Algorithm 1 step 1 and Fig. 4 "Prepare Phase": block
@@ -98,10 +104,16 @@ typedef struct {
  *   hsum      = sum_j sum_n (k_{j,n} - kbar_j)^T v_{j,n}
  *                                            (D x D)   fp32 [B,H,D,D]
  *               (row index: key dim, column index: value dim)
+ *   hnorm[j]  = || H_j - Hbar ||_F, H_j = sum_n (k_{j,n} - kbar_j)^T v_{j,n},
+ *               Hbar = (1/N) sum_j H_j (the block heterogeneity M_j of
+ *               Eq. 11 and Appendix D, with the Frobenius norm the README's
+ *               router uses)                            fp64 [B,H,N]
  * n_i, n_j are the rows present in the block (the last one may be partial).
  * qbar, kbar, q2bar and ksig2 are fp64 so that routing decisions (a top-k, a
  * gate) can match a float64 evaluation; q2bar and ksig2 may be NULL unless
- * params.second_order. pisa_block_stats computes them from q, k, v; a caller
+ * params.second_order; hnorm may be NULL unless params.cov_bias (it is
+ * computed from H_j and Hbar in fp64 from the exact inputs, in two more passes
+ * over k and v). pisa_block_stats computes them from q, k, v; a caller
  * may also fill them by any other means and hand them to
  * pisa_prepare_operands.
  */
@@ -112,6 +124,7 @@ typedef struct {
     float *vsum;
     double *ksig2;
     float *hsum;
+    double *hnorm;
 } pisa_stats_t;
 
 /*
@@ -160,8 +173,9 @@ const char *pisa_status_str(pisa_status_t s);
 /* N = ceil(seq_len / block_size), or -1 if the shape is invalid. */
 int64_t pisa_num_blocks(const pisa_shape_t *shape);
 
-/* Bytes of device workspace pisa_block_stats needs (partial H sums), or 0 if
- * the shape is invalid. */
+/* Bytes of device workspace pisa_block_stats needs (partial H sums, and with
+ * params.cov_bias the fp64 partial sums and Hbar of the prior; the larger of
+ * the two, so any params fit), or 0 if the shape is invalid. */
 size_t pisa_stats_workspace_bytes(const pisa_shape_t *shape);
 
 /* Bytes of the operand buffer for this shape, or 0 if the shape is invalid. */
@@ -193,8 +207,9 @@ pisa_status_t pisa_block_stats(const pisa_shape_t *shape, const pisa_params_t *p
  * device array of PISA_STATS_SCRATCH_BYTES that the library holds on each GPU
  * it runs on until the process ends (its address is looked up once per
  * device, on the first call there). No allocation happens in the call.
- * Shapes with pisa_stats_workspace_bytes(shape) > PISA_STATS_SCRATCH_BYTES
- * (for head_dim 128: batch * heads > 512) are rejected with
+ * Shapes whose scratch need exceeds PISA_STATS_SCRATCH_BYTES (the partial H
+ * sums: for head_dim 128, batch * heads > 512; with params.cov_bias the fp64
+ * partials of the prior: batch * heads > 128) are rejected with
  * PISA_ERR_WORKSPACE before any HIP call. Every call on one GPU uses that
  * GPU's one array: calls that overlap on one GPU (other streams, other
  * threads) race and must be serialised by the caller. The array needs no
@@ -219,9 +234,10 @@ pisa_status_t pisa_prepare_operands(const pisa_shape_t *shape, const pisa_params
                                     size_t operands_bytes, void *stream);
 
 /*
- * pisa_route_topk (Algorithm 1 step 2 with the pooled score of Eq. 11 minus
- * its covariance term; README router): for each query block i,
- *   r_ij = s qbar_i . kbar_j + [second_order] min(w_ij, ln B),
+ * pisa_route_topk (Algorithm 1 step 2 with the pooled score of Eq. 11;
+ * README router): for each query block i,
+ *   r_ij = s qbar_i . kbar_j + [second_order] min(w_ij, ln B)
+ *          + [cov_bias] log(hnorm_j + PISA_COV_EPS),
  *   w_ij = 1/2 q2bar_i . ksig2_j,
  * over the candidates j with |i - j| > band. idx[b,h,i,:] receives the
  * min(topk, #candidates) best j (ties: lower j wins), ascending, then -1.
@@ -232,8 +248,8 @@ pisa_status_t pisa_prepare_operands(const pisa_shape_t *shape, const pisa_params
  * wgate: fp32 [B,H,N,N], required iff second_order: the gated term used by
  *   the virtual-token logits: w_ij where w_ij <= ln B, and 0 where w_ij is
  *   larger (the README's gate, not a clamp), decided as in float64.
- * Reads stats->qbar, kbar (and q2bar, ksig2 if second_order) and the
- * operand buffer.
+ * Reads stats->qbar, kbar (and q2bar, ksig2 if second_order; hnorm if
+ * cov_bias) and the operand buffer.
  */
 pisa_status_t pisa_route_topk(const pisa_shape_t *shape, const pisa_params_t *params,
                               const pisa_stats_t *stats, const void *operands,

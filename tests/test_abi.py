@@ -32,7 +32,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pisa_abi_version() == 11
+    assert lib.pisa_abi_version() == 12
     for code in range(9):
         assert lib.pisa_status_str(code)
     assert lib.pisa_status_str(99) == b"unknown status"
@@ -55,6 +55,20 @@ def test_invalid_shapes(lib, bad):
     s = shape(**bad)
     assert lib.pisa_num_blocks(ctypes.byref(s)) == -1
     assert lib.pisa_stats_workspace_bytes(ctypes.byref(s)) == 0
+
+
+def test_workspace_bytes_fit_the_covariance_prior(lib):
+    """With the prior the workspace also holds fp64 partial sums of H_j (half
+    as many ranges as the fp32 partials, less one) and Hbar: never more than
+    the fp32 partials when a head has four or more ranges."""
+    for T, D, H in ((32760, 128, 40), (118800, 128, 24), (4608, 128, 24), (1000, 64, 2)):
+        s = shape(T=T, D=D, H=H)
+        N = -(-T // 64)
+        groups = min(max(1, 512 // H), -(-N // 4))
+        G = -(-N // -(-N // groups))
+        fp32 = H * G * D * D * 4
+        G2 = max(1, min(N, G // 2 - 1))
+        assert lib.pisa_stats_workspace_bytes(ctypes.byref(s)) == max(fp32, H * (G2 + 1) * D * D * 8)
 
 
 def test_workspace_bytes(lib):
@@ -172,6 +186,8 @@ def test_stats_validation(lib):
     assert call_stats(lib, ws=None) == E["PISA_ERR_NULL"]
     assert call_stats(lib, wsb=16) == E["PISA_ERR_WORKSPACE"]
     assert call_stats(lib, p=_lib.Params(4, 1, 2, 1, 0)) == E["PISA_ERR_PARAM"]
+    # the covariance prior's block norms need hnorm
+    assert call_stats(lib, p=_lib.Params(4, 1, 0, 1, 0, 0, 1)) == E["PISA_ERR_NULL"]
     # the operand buffer or the workspace inside an input, or each other
     assert call_stats(lib, ops=fake(2) + 4096) == E["PISA_ERR_PARAM"]
     assert call_stats(lib, ws=fake(3) + 256) == E["PISA_ERR_PARAM"]
@@ -206,6 +222,10 @@ def test_route_validation(lib):
     assert call_route(lib, p=so, st=stats(ksig2=fake(14), q2bar=fake(15))) == E["PISA_ERR_NULL"]
     assert call_route(lib, p=so, st=stats(ksig2=fake(14), q2bar=MIS), wg=fake(31)) == E["PISA_ERR_ALIGN"]
     assert call_route(lib, s=shape(block=128)) == E["PISA_ERR_PARAM"]
+    # covariance prior: 0 or 1, and it needs hnorm
+    assert call_route(lib, p=_lib.Params(4, 1, 0, 1, 0, 0, 2)) == E["PISA_ERR_PARAM"]
+    assert call_route(lib, p=_lib.Params(4, 1, 0, 1, 0, 0, 1)) == E["PISA_ERR_NULL"]
+    assert call_route(lib, p=_lib.Params(4, 1, 0, 1, 0, 0, 1), st=stats(hnorm=MIS)) == E["PISA_ERR_ALIGN"]
     # sink blocks: 0..N
     assert call_route(lib, p=_lib.Params(4, 1, 0, 1, 0, -1)) == E["PISA_ERR_PARAM"]
     assert call_route(lib, p=_lib.Params(4, 1, 0, 1, 0, 17)) == E["PISA_ERR_PARAM"]

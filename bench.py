@@ -45,6 +45,40 @@ def traffic_file(workload):
     return os.path.join(ROOT, "profiles", f"attn_mfma_{workload}_traffic.json")
 
 
+def kernel_stats_file(workload):
+    return os.path.join(ROOT, "profiles", f"{workload}_kernel_stats.txt")
+
+
+def profile_avg_ns(workload, kernel=ATTN_KERNEL):
+    """Average duration (ns) of `kernel` in the committed rocprofv3 --stats
+    summary of this workload, if that summary was taken on the current kernel
+    source (its header names the source's sha256), else None."""
+    import csv
+    try:
+        with open(kernel_stats_file(workload)) as f:
+            lines = f.read().splitlines()
+    except OSError:
+        return None
+    if not any(ln.startswith("#") and source_digest() in ln for ln in lines):
+        return None
+    rows = [ln for ln in lines if not ln.startswith("#") and ln.strip()]
+    for row in csv.DictReader(rows):
+        if kernel in row.get("Name", ""):
+            return float(row["AverageNs"])
+    return None
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.lower().startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def source_digest():
     import hashlib
     h = hashlib.sha256()
@@ -151,6 +185,10 @@ def main():
 
     w = I.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
+    plan_kernel = P.attn_fwd_plan(w.batch, w.heads, w.seq_len, w.head_dim, w.dtype,
+                                  P.topk_for_density(w.density, P.num_blocks(w.seq_len)), w.band,
+                                  w.second_order)
+    attn_kernel_name = {0: "attn_valu_kernel", 1: ATTN_KERNEL, 2: "attn_mfma_kernel"}[plan_kernel]
     torch.cuda.set_device(dev)
     t0 = time.time()
     qa, ka, va = I.make_inputs(w)
@@ -312,21 +350,36 @@ def main():
     phase1_tflops = 4 * D * exact_pairs / (phase1_ms * 1e-3) / 1e12 if phase1_ms else None
     dense_flops = 4.0 * B * H * T * T * D
     attn_tflops = attn_flops / (attn_ms * 1e-3) / 1e12
+    prof_ns = profile_avg_ns(w.name) if attn_kernel_name == ATTN_KERNEL else None
+    traffic = load_traffic(w.name) if attn_kernel_name == ATTN_KERNEL else None
+    unique_bytes = 4 * B * H * T * D * (2 if w.dtype == "bf16" else 4)   # Q, K, V read and O written once
 
     e = 2 if w.dtype == "bf16" else 4
     groups = min(max(1, 512 // (B * H)), -(-N // 4))      # the statistics pass's block ranges per head
     G = -(-N // -(-N // groups))
     BHND = B * H * N * D
-    stats_bytes = (3 * B * H * T * D * e                     # read Q, K, V
-                   + BHND * (8 + 8 + 4 + 4 + 2 * e)          # qbar, kbar, kbar_r, vsum, kbar_c, vbar_c
-                   + (BHND * 16 if so else 0)                # q2bar, ksig2
-                   + (B * H * N * 64 * D * 2 if w.dtype == "bf16" else 0)   # packed K copy
-                   + B * H * D * D * 4                       # hsum
-                   + 2 * B * H * G * D * D * 4)              # partial H write + read
-    route_bytes = (BHND * 12                                 # qbar (fp64), kbar_r (fp32)
-                   + (BHND * 16 if so else 0)                # q2bar, ksig2
-                   + B * H * N * topk * 4                    # idx
-                   + (B * H * N * N * 4 if so else 0))       # gated w table
+    NC16 = -(-N // 16) * 16
+    # statistics pass, algorithmic: read Q, K, V once; write the paper's
+    # statistics in their storage types (qbar, kbar fp64; V-hat fp32; q2bar,
+    # key variance fp64 with the second order; H fp32)
+    stats_bytes = (3 * B * H * T * D * e
+                   + BHND * (8 + 8 + 4) + (BHND * 16 if so else 0)
+                   + B * H * D * D * 4)
+    # beyond that it writes the kernels' operand layouts and round-trips the
+    # partial H sums through memory: reported, not rated
+    stats_layout_bytes = (2 * BHND * e                                   # kbar, vbar in the input dtype
+                          + B * H * NC16 * D * 4 * (2 if so else 1)       # router-order kbar (, variance)
+                          + (B * H * N * 64 * D * 2 + B * H * -(-N // 64) * 64 * D * 2
+                             + B * H * 2 * D * D * 2 if w.dtype == "bf16" else 0)   # packed K, kbar, H
+                          + 2 * B * H * G * D * D * 4)                    # partial H write + read
+    # routing, algorithmic: read the pooled statistics it ranks (qbar fp64,
+    # router-order kbar fp32; q2bar fp64 and router-order variance fp32 with
+    # the second order), write the table (and the gated w table)
+    route_bytes = (B * H * N * D * 8 + B * H * NC16 * D * 4
+                   + ((B * H * N * D * 8 + B * H * NC16 * D * 4) if so else 0)
+                   + B * H * N * topk * 4
+                   + (B * H * N * N * 4 if so else 0))
+    route_gemm_flops = 2 * B * H * N * N * D * (2 if so else 1)   # fp32 score (and spread) products
 
     out = {
         "metric": ("pisa_attn_fwd ms & dense-equiv TFLOP/s, Wan2.1-14B shape, density 0.125"
@@ -357,13 +410,27 @@ def main():
         "morton_reorder": reorder,
         "pisa_block_stats": {"ms": round(stats_ms, 4), **spread(per_kernel[0]), "algorithmic_bytes": stats_bytes,
                              "gbs": round(stats_bytes / (stats_ms * 1e-3) / 1e9, 1),
-                             "frac_hbm": round(stats_bytes / (stats_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+                             "frac_hbm": round(stats_bytes / (stats_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                             "layout_overhead_bytes": stats_layout_bytes,
+                             "note": "algorithmic bytes: Q, K, V read + the statistics written; the operand "
+                                     "layouts and the partial-H round trip are layout_overhead_bytes, not rated"},
         "pisa_route_topk": {"ms": round(route_ms, 4), **spread(per_kernel[1]), "algorithmic_bytes": route_bytes,
                             "gbs": round(route_bytes / (route_ms * 1e-3) / 1e9, 1),
-                            "frac_hbm": round(route_bytes / (route_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+                            "frac_hbm": round(route_bytes / (route_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                            "score_gemm_tflop": round(route_gemm_flops / 1e12, 5),
+                            "score_gemm_floor_ms": round(route_gemm_flops / (PEAK_FP32_TFLOPS * 1e12) * 1e3, 4),
+                            "frac_fp32_mfma": round(route_gemm_flops / (route_ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS, 4)},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": load_traffic(w.name), "kernel": ATTN_KERNEL + " (pisa_attn_fwd)"},
+                     "frac_profile": (None if prof_ns is None else
+                                      round(attn_flops / (prof_ns * 1e-9) / 1e12 / PEAK_BF16_TFLOPS, 4)),
+                     "traffic": traffic,
+                     "traffic_kind": ("L2-to-fabric bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, each "
+                                      "scaled by its reading for a plain 1 GiB copy); requests the Infinity "
+                                      "Cache serves are included, so this bounds HBM bytes from above"),
+                     "traffic_over_unique": None if traffic is None else round(traffic / unique_bytes, 2),
+                     "unique_bytes": unique_bytes,
+                     "kernel": ATTN_KERNEL + " (pisa_attn_fwd)"},
         "input_generation_s": round(gen_s, 1),
     }
     if bwd_ms is not None:
@@ -416,7 +483,7 @@ def cpu_baseline(w, qa, ka, va, nheads, topk):
         assert np.isfinite(o).all()
     dense_flops = 4.0 * nheads * T * T * D
     return {"value": round(dense_flops / dt / 1e12, 5), "unit": "TFLOP/s dense-equivalent",
-            "cores": threads, "kind": "oracle",
+            "cores": threads, "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"heads 0..{nheads - 1} of {w.name} (of {qa.shape[1]}), every query block: "
                       f"statistics, routing and forward in float64 numpy; {dt:.1f} s",
             "seconds": round(dt, 2)}

@@ -137,8 +137,8 @@ def operand_views(stats: PisaStats, like: torch.Tensor) -> dict:
     off = (ctypes.c_int64 * len(_lib.OPERANDS))()
     _lib.check("pisa_operands_offsets", lib.pisa_operands_offsets(ctypes.byref(sh), off))
     ends = list(off[1:]) + [operands_bytes(like)]
-    el = {"kbar_c": like.dtype, "vbar_c": like.dtype, "kbar_r": torch.float32, "ksig2_r": torch.float32,
-          "kpack": torch.bfloat16, "kbpack": torch.bfloat16, "hpack": torch.bfloat16}
+    el = {"kbar_c": like.dtype, "vbar_c": like.dtype, "kbar_r": torch.bfloat16, "ksig2_r": torch.bfloat16,
+          "kpack": torch.bfloat16, "kbpack": torch.bfloat16, "hpack": torch.bfloat16, "knorm": torch.float32}
     out = {}
     for n, name in enumerate(_lib.OPERANDS):
         raw = stats.operands[off[n]:ends[n]]
@@ -290,6 +290,19 @@ def pisa_attn_bwd(q, k, v, o, dout, stats, idx, wgate=None, band=1, second_order
         ctypes.byref(cs), _ptr(idx) if topk else None, _ptr(wgate) if second_order else None,
         _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), _stream(q.device)))
     return dq, dk, dv
+
+
+def attn_fwd_plan(batch, heads, seq_len, head_dim, dtype, topk, band=1, second_order=False, n_sink=0) -> int:
+    """The kernel pisa_attn_fwd runs for these arguments (pisa_attn_fwd_plan;
+    host only): 0 fp32 VALU, 1 persistent bf16 matrix-core kernel, 2 the
+    non-persistent bf16 matrix-core kernel."""
+    code = PISA_BF16 if dtype in ("bf16", torch.bfloat16) else PISA_F32
+    sh = _lib.Shape(batch, heads, seq_len, head_dim, BLOCK, code, 0.0)
+    prm = _lib.Params(int(topk), int(band), int(second_order), 1, 0, int(n_sink))
+    kern = ctypes.c_int32(-1)
+    _lib.check("pisa_attn_fwd_plan", library().pisa_attn_fwd_plan(ctypes.byref(sh), ctypes.byref(prm),
+                                                                   ctypes.byref(kern), None))
+    return kern.value
 
 
 def z_order(grid, prefix: int = 0) -> torch.Tensor:

@@ -26,7 +26,7 @@ EXPORTED = (
 STATS_SCRATCH_BYTES = 32 << 20   # PISA_STATS_SCRATCH_BYTES
 COV_EPS = 1e-6                   # PISA_COV_EPS
 # pisa_operand_t: the arrangements inside the operand buffer
-OPERANDS = ("kbar_c", "vbar_c", "kbar_r", "ksig2_r", "kpack", "kbpack", "hpack")
+OPERANDS = ("kbar_c", "vbar_c", "kbar_r", "ksig2_r", "kpack", "kbpack", "hpack", "knorm")
 
 
 class Shape(ctypes.Structure):

@@ -72,9 +72,25 @@ struct StatsView {
     void* kpack;       // bf16: K in the fused kernel's operand order  [BH,N,64 D]
     void* hpack;       // bf16: H split hi + lo, operand order         [BH,2 D D]
     void* kbpack;      // bf16: kbar_c in kpack's order per 64 blocks  [BH,ceil(N/64),64 D]
-    float* kbar_r;     // kbar in fp32, the router's operand order     [BH,ceil(N/16) 16 D]
-    float* ksig2_r;    // ksig2 in fp32, the same order
+    bf16_t* kbar_r;    // kbar split bf16 hi + lo, the router's operand order [BH,ceil(N/16) 16 D 2]
+    bf16_t* ksig2_r;   // ksig2 the same way
+    float* knorm;      // ||kbar_j||_2 rounded up (the router's error bound) [BH,ceil(N/16) 16]
 };
+
+// The router's operand order for a per-block row x[j][d] (kbar or ksig2) of a
+// head: split into bf16 hi = rn(x), lo = rn(x - hi) (|x - hi - lo| <= 2^-17 |x|),
+// chunk c = j / 16 of 16 keys, k-step s < D / 32, part p (hi, lo), lane
+// 16 g + (j % 16) with d = (D / 4) g + 8 s + e: bf16 element
+// ((c D/32 + s) 2 + p) 512 + (16 g + j % 16) 8 + e. A 64-lane 16-byte load of
+// (c, s, p) is one MFMA 16x16x32 B operand of 16 keys.
+__device__ __forceinline__ void router_store(bf16_t* head, int j, int d, int D, double x) {
+    const int c = j >> 4, n16 = j & 15, g = d / (D / 4), s = (d % (D / 4)) >> 3, e = d & 7;
+    const int64_t o = (int64_t)((c * (D / 32) + s) * 2) * 512 + (16 * g + n16) * 8 + e;
+    const bf16_t hi = f32_to_bf16((float)x);
+    head[o] = hi;
+    head[o + 512] = f32_to_bf16((float)(x - (double)bf16_to_f32(hi)));
+}
+__host__ __device__ inline int64_t router_head_elems(int N, int D) { return (int64_t)((N + 15) / 16) * 16 * D * 2; }
 
 // Problem geometry resolved once on the host.
 struct Geom {

@@ -138,6 +138,7 @@ OperandLayout operand_layout(const Geom& g, int dtype) {
     sz[PISA_OPERAND_KPACK] = bf ? BH * N * 64 * D * 2 : 0;
     sz[PISA_OPERAND_KBPACK] = bf ? BH * ((N + 63) / 64) * 64 * D * 2 : 0;
     sz[PISA_OPERAND_HPACK] = bf ? BH * 2 * D * D * 2 : 0;
+    sz[PISA_OPERAND_KNORM] = BH * ((N + 15) / 16) * 16 * 4;
     OperandLayout L{};
     size_t at = 0;
     for (int i = 0; i < PISA_OPERAND_COUNT; ++i) {
@@ -164,8 +165,9 @@ StatsView stats_view(const Geom& g, int dtype, const pisa_stats_t* st, const voi
         auto at = [&](int i) -> void* { return L.bytes[i] ? b + L.off[i] : nullptr; };
         v.kbar_c = at(PISA_OPERAND_KBAR_C);
         v.vbar_c = at(PISA_OPERAND_VBAR_C);
-        v.kbar_r = static_cast<float*>(at(PISA_OPERAND_KBAR_R));
-        v.ksig2_r = static_cast<float*>(at(PISA_OPERAND_KSIG2_R));
+        v.kbar_r = static_cast<bf16_t*>(at(PISA_OPERAND_KBAR_R));
+        v.ksig2_r = static_cast<bf16_t*>(at(PISA_OPERAND_KSIG2_R));
+        v.knorm = static_cast<float*>(at(PISA_OPERAND_KNORM));
         v.kpack = at(PISA_OPERAND_KPACK);
         v.kbpack = at(PISA_OPERAND_KBPACK);
         v.hpack = at(PISA_OPERAND_HPACK);

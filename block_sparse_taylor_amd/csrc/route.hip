@@ -44,6 +44,7 @@ constexpr double kU = 5.9604644775390625e-08;   // 2^-24
 __device__ __forceinline__ double cov_prior(const double* hn, int j) { return log(hn[j] + PISA_COV_EPS); }
 
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f4_t;
+typedef double d2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t key32(float f) {
     f = f + 0.0f;
@@ -179,8 +180,9 @@ __host__ __device__ constexpr int route_waves(int kpl) { return kpl > 16 ? 8 : 4
 template <int D, bool SO, int KPL, bool COV>
 __global__ __launch_bounds__(64 * route_waves(KPL)) __attribute__((amdgpu_waves_per_eu(SO || KPL > 16 ? 2 : 4))) void route_fast_kernel(
     const double* __restrict__ qbar, const double* __restrict__ q2bar, const double* __restrict__ kbar,
-    const float* __restrict__ kbar_r, const double* __restrict__ ksig2, const float* __restrict__ ksig2_r,
-    const double* __restrict__ hnorm, int N, double s64, int topk, int band, int n_sink,
+    const bf16_t* __restrict__ kbar_r, const double* __restrict__ ksig2, const bf16_t* __restrict__ ksig2_r,
+    const float* __restrict__ knorm, const double* __restrict__ hnorm, int N, double s64, int topk, int band,
+    int n_sink,
     int32_t* __restrict__ idx, float* __restrict__ wgate) {
     constexpr int KS = D / 4;       // 16x16x4 k-steps; MFMA k-slot (ks, l/16) <-> dim (D/4)(l/16) + ks
     constexpr bool second_order = SO;
@@ -215,74 +217,82 @@ __global__ __launch_bounds__(64 * route_waves(KPL)) __attribute__((amdgpu_waves_
     }
     const double* qrows = qbar + (bh * N + i0) * (int64_t)D;   // fp64 pooled queries of the tile
 
-    // ---- scores: S[r][j] = s qbar_r . kbar_j (+ min(w, ln B)) via fp32 MFMA.
-    // Wave w takes the 16-column chunks c = w, w+NWV, ...; lane (m16, g4) needs
-    // kbar[16 c + m16][(D/4) g4 + ks] for ks < KS, which kbar_r holds as D/16
-    // 1 KB runs per chunk (16 bytes per lane), loaded one chunk ahead.
-    typedef double d2_t __attribute__((ext_vector_type(2)));
+    // ---- scores: S[r][j] = s qbar_r . kbar_j (+ min(w, ln B)) (+ prior) via
+    // bf16 MFMA 16x16x32 on operands split into hi + lo (hi.hi + hi.lo + lo.hi:
+    // what is dropped is below 3.01 2^-18 of each |q_d k_d|, and the products are
+    // exact in fp32). Wave w takes the 16-column chunks c = w, w+NWV, ...; lane
+    // (m16, g4) holds k-slots 8 g4 + e of k-step s for dim (D/4) g4 + 8 s + e:
+    // for the A operand the pooled query row m16, for B key 16 c + m16, which
+    // kbar_r holds as 2 (D/32) 1 KB runs per chunk, loaded one chunk ahead.
+    constexpr int KB = D / 32;      // bf16 16x16x32 k-steps
     const int m16 = lane & 15, g4 = lane >> 4;
-    float a[KS], a2[KS];
-    {
-        const d2_t* qa = reinterpret_cast<const d2_t*>(qrows + min(m16, nq - 1) * D + (D / 4) * g4);
+    auto split8 = [&](const double* x, bool valid, bf16x8_t& hi, bf16x8_t& lo) {
 #pragma unroll
-        for (int h = 0; h < KS / 2; ++h) {
-            const d2_t x = qa[h];
-            a[2 * h] = m16 < nq ? (float)x.x : 0.f;
-            a[2 * h + 1] = m16 < nq ? (float)x.y : 0.f;
+        for (int e = 0; e < 8; ++e) {
+            const double v = valid ? x[e] : 0.0;
+            const __bf16 h = (__bf16)(float)v;
+            hi[e] = h;
+            lo[e] = (__bf16)(float)(v - (double)(float)h);
+        }
+    };
+    bf16x8_t ah[KB], al[KB], a2h[SO ? KB : 1], a2l[SO ? KB : 1];
+    {
+        const double* qa = qrows + min(m16, nq - 1) * D + (D / 4) * g4;
+#pragma unroll
+        for (int sk = 0; sk < KB; ++sk) split8(qa + 8 * sk, m16 < nq, ah[sk], al[sk]);
+        if (SO) {
+#pragma unroll
+            for (int sk = 0; sk < KB; ++sk) split8(q2_s + m16 * D + (D / 4) * g4 + 8 * sk, true, a2h[sk], a2l[sk]);
         }
     }
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) a2[ks] = SO ? (float)q2_s[m16 * D + (D / 4) * g4 + ks] : 0.f;
     const double* kb = kbar + bh * (int64_t)N * D;
     const double* sg = SO ? ksig2 + bh * (int64_t)N * D : nullptr;
     const double* hn = COV ? hnorm + bh * (int64_t)N : nullptr;   // covariance prior
-    float kmax2 = 0.f;
+    float kmaxf = 0.f;
     float bmax = 0.f;   // max |prior| over this wave's columns (of the fp32 roundings)
     const int NC = (N + 15) / 16;
-    const float4* kr4 = reinterpret_cast<const float4*>(kbar_r + bh * (int64_t)NC * 16 * D);
-    const float4* sr4 = SO ? reinterpret_cast<const float4*>(ksig2_r + bh * (int64_t)NC * 16 * D) : nullptr;
-    float4 kv[KS / 4];
+    const uint4* kr4 = reinterpret_cast<const uint4*>(kbar_r + bh * router_head_elems(N, D));
+    const uint4* sr4 = SO ? reinterpret_cast<const uint4*>(ksig2_r + bh * router_head_elems(N, D)) : nullptr;
+    const float* kn = knorm + bh * (int64_t)NC * 16;
+    uint4 kv[2 * KB];
     auto kload = [&](int c) {
 #pragma unroll
-        for (int qq = 0; qq < KS / 4; ++qq) kv[qq] = kr4[((int64_t)c * (KS / 4) + qq) * 64 + lane];
+        for (int u = 0; u < 2 * KB; ++u) kv[u] = kr4[((int64_t)c * 2 * KB + u) * 64 + lane];
     };
     if (wave < NC) kload(wave);
     for (int c = wave; c < NC; c += NWV) {
         const int col = c * 16 + m16;
         const bool ok = col < N;
-        float b[KS];
+        bf16x8_t bh8[KB], bl8[KB];
 #pragma unroll
-        for (int qq = 0; qq < KS / 4; ++qq) {
-            b[4 * qq + 0] = ok ? kv[qq].x : 0.f;
-            b[4 * qq + 1] = ok ? kv[qq].y : 0.f;
-            b[4 * qq + 2] = ok ? kv[qq].z : 0.f;
-            b[4 * qq + 3] = ok ? kv[qq].w : 0.f;
+        for (int sk = 0; sk < KB; ++sk) {
+            bh8[sk] = __builtin_bit_cast(bf16x8_t, ok ? kv[2 * sk] : make_uint4(0, 0, 0, 0));
+            bl8[sk] = __builtin_bit_cast(bf16x8_t, ok ? kv[2 * sk + 1] : make_uint4(0, 0, 0, 0));
         }
         if (c + NWV < NC) kload(c + NWV);   // the next chunk
-        float4 sv[SO ? KS / 4 : 1];       // ksig2 of this chunk (second order), same order as kbar_r
+        uint4 sv[SO ? 2 * KB : 1];          // ksig2 of this chunk (second order), same order
         if (SO) {
 #pragma unroll
-            for (int qq = 0; qq < KS / 4; ++qq) sv[qq] = sr4[((int64_t)c * (KS / 4) + qq) * 64 + lane];
+            for (int u = 0; u < 2 * KB; ++u) sv[u] = sr4[((int64_t)c * 2 * KB + u) * 64 + lane];
         }
+        if (ok) kmaxf = fmaxf(kmaxf, kn[col]);
         f4_t acc = {0.f, 0.f, 0.f, 0.f}, accw = {0.f, 0.f, 0.f, 0.f};
-        float n2 = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            n2 = fmaf(b[ks], b[ks], n2);
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[ks], b[ks], acc, 0, 0, 0);
+        for (int sk = 0; sk < KB; ++sk) {
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[sk], bh8[sk], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[sk], bl8[sk], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[sk], bh8[sk], acc, 0, 0, 0);
         }
         if (SO) {
 #pragma unroll
-            for (int qq = 0; qq < KS / 4; ++qq) {
-                accw = __builtin_amdgcn_mfma_f32_16x16x4f32(a2[4 * qq + 0], ok ? sv[qq].x : 0.f, accw, 0, 0, 0);
-                accw = __builtin_amdgcn_mfma_f32_16x16x4f32(a2[4 * qq + 1], ok ? sv[qq].y : 0.f, accw, 0, 0, 0);
-                accw = __builtin_amdgcn_mfma_f32_16x16x4f32(a2[4 * qq + 2], ok ? sv[qq].z : 0.f, accw, 0, 0, 0);
-                accw = __builtin_amdgcn_mfma_f32_16x16x4f32(a2[4 * qq + 3], ok ? sv[qq].w : 0.f, accw, 0, 0, 0);
+            for (int sk = 0; sk < KB; ++sk) {
+                const bf16x8_t sh = __builtin_bit_cast(bf16x8_t, ok ? sv[2 * sk] : make_uint4(0, 0, 0, 0));
+                const bf16x8_t sl = __builtin_bit_cast(bf16x8_t, ok ? sv[2 * sk + 1] : make_uint4(0, 0, 0, 0));
+                accw = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2h[sk], sh, accw, 0, 0, 0);
+                accw = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2h[sk], sl, accw, 0, 0, 0);
+                accw = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2l[sk], sh, accw, 0, 0, 0);
             }
         }
-        n2 += __shfl_xor(n2, 16);
-        n2 += __shfl_xor(n2, 32);
-        kmax2 = fmaxf(kmax2, n2);
         float prior = 0.f;
         if (COV && ok) {
             prior = (float)cov_prior(hn, col);
@@ -293,33 +303,46 @@ __global__ __launch_bounds__(64 * route_waves(KPL)) __attribute__((amdgpu_waves_
         for (int e = 0; e < 4; ++e) {
             const int r = 4 * g4 + e;
             float sc = (float)s64 * acc[e];
-            if (SO && ok && r < nq) {
+            if (SO) {
+                const bool live = ok && r < nq;
                 const float w = 0.5f * accw[e];
-                const float ew = 2.0f * (float)((D + 4) * kU) * w + 1e-30f;
-                float wg;
-                if (fabsf(w - lnBf) > ew) {
-                    wg = w > lnBf ? 0.f : w;
-                } else {   // too close to call in fp32: decide in fp64
-                    double w64 = 0.0;
-                    for (int d = 0; d < D; ++d) w64 = fma(q2_s[r * D + d], sg[(int64_t)col * D + d], w64);
-                    w64 *= 0.5;
-                    wg = w64 > lnB ? 0.f : (float)w64;
+                // all terms of w are >= 0: relative bound (split + fp32 sums)
+                const float ew = (float)(2.0 * (3 * D + 4) * kU + 8.0 * 0x1p-18) * w + 1e-30f;
+                const bool close = live && !(fabsf(w - lnBf) > ew);
+                float wg = w > lnBf ? 0.f : w;
+                // the few pairs too close to call in fp32 are decided in fp64, one
+                // at a time by the whole wave (each lane two dims, a wave sum)
+                unsigned long long cm = __ballot(close);
+                while (cm) {
+                    const int L = __ffsll((long long)cm) - 1;
+                    cm &= cm - 1;
+                    const int rr = 4 * (L >> 4) + e, cc = c * 16 + (L & 15);
+                    double part = 0.0;
+                    if (2 * lane < D) {
+                        const d2_t y = *reinterpret_cast<const d2_t*>(sg + (int64_t)cc * D + 2 * lane);
+                        part = fma(q2_s[rr * D + 2 * lane], y.x, q2_s[rr * D + 2 * lane + 1] * y.y);
+                    }
+#pragma unroll
+                    for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off);
+                    const double w64 = 0.5 * part;
+                    if (lane == L) wg = w64 > lnB ? 0.f : (float)w64;
                 }
-                wgate[(bh * N + i0 + r) * (int64_t)N + col] = wg;
-                sc += fminf(w, lnBf);
+                if (live) {
+                    wgate[(bh * N + i0 + r) * (int64_t)N + col] = wg;
+                    sc += fminf(w, lnBf);
+                }
             }
             sc += prior;
             if (ok) score_s[r * NP + col] = sc;
         }
     }
-    kmax2 = fmaxf(kmax2, __shfl_xor(kmax2, 1));
-    kmax2 = fmaxf(kmax2, __shfl_xor(kmax2, 2));
-    kmax2 = fmaxf(kmax2, __shfl_xor(kmax2, 4));
-    kmax2 = fmaxf(kmax2, __shfl_xor(kmax2, 8));
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) bmax = fmaxf(bmax, __shfl_xor(bmax, off));
+    for (int off = 32; off > 0; off >>= 1) {
+        kmaxf = fmaxf(kmaxf, __shfl_xor(kmaxf, off));
+        bmax = fmaxf(bmax, __shfl_xor(bmax, off));
+    }
     if (lane == 0) {
-        kmax_s[wave] = kmax2;
+        kmax_s[wave] = kmaxf;
         bmax_s[wave] = bmax;
     }
     __syncthreads();
@@ -331,8 +354,7 @@ __global__ __launch_bounds__(64 * route_waves(KPL)) __attribute__((amdgpu_waves_
         bmxf = fmaxf(bmxf, bmax_s[w]);
     }
     const double bmx = (double)bmxf * (1.0 + 1e-6);   // bounds |prior| in fp64 too
-    const double kmax = sqrt((double)kmx) *
-                        (1.0 + 1e-6);
+    const double kmax = (double)kmx;                  // the norms are rounded up already
 
     // ---- selection: wave w handles rows w, w+NWV, ... A row's candidate
     // keys stay in registers (lane l holds columns 64 i + l, i < KPL) from the
@@ -367,7 +389,9 @@ __global__ __launch_bounds__(64 * route_waves(KPL)) __attribute__((amdgpu_waves_
             // |r| bound: the dot product, the clamped spread, the prior (the
             // latter two each add at most two fp32 roundings of their size)
             const double bound = s64 * sqrt(qn) * kmax + (second_order ? lnB : 0.0) + bmx;
-            const float eps = (float)(4.0 * (D + 8) * kU * bound) + 1e-30f;
+            // fp32 sums of 3 D exact products (and of the spread and prior), plus
+            // the split's dropped terms: |r~ - r| <= eps
+            const float eps = (float)((4.0 * (3 * D + 8) * kU + 4.0 * 0x1p-18) * bound) + 1e-30f;
             int need_eq;
             const uint32_t tk = wave_select32<KPL>(kv, k, &need_eq);
             const float tau = unkey32(tk);
@@ -631,8 +655,9 @@ hipError_t launch_route_topk(const Geom& g, const pisa_params_t* p, const StatsV
     const size_t lds = fast_lds_bytes(g.D, g.N, so, nwv);
     if (lds + kLdsStatic <= (size_t)kLdsMax && g.N <= 64 * kKeysPerLane) {
         const dim3 block(64 * nwv);
-        using Fn = void (*)(const double*, const double*, const double*, const float*, const double*, const float*,
-                            const double*, int, double, int, int, int, int32_t*, float*);
+        using Fn = void (*)(const double*, const double*, const double*, const bf16_t*, const double*,
+                            const bf16_t*, const float*, const double*, int, double, int, int, int, int32_t*,
+                            float*);
         static bool attr_set[2][2][2][3] = {};
 #define PISA_ROUTE_ROW(DD, SO, CV) \
     {&route_fast_kernel<DD, SO, 8, CV>, &route_fast_kernel<DD, SO, 16, CV>, &route_fast_kernel<DD, SO, kKeysPerLane, CV>}
@@ -653,8 +678,8 @@ hipError_t launch_route_topk(const Geom& g, const pisa_params_t* p, const StatsV
             set = true;
         }
         dim3 grid((g.N + kQB - 1) / kQB, (unsigned)g.BH);
-        hipLaunchKernelGGL(fn, grid, block, lds, stream, st->qbar, st->q2bar, st->kbar, st->kbar_r, st->ksig2, st->ksig2_r,
-                           hn, g.N, g.scale64, p->topk, p->band, p->n_sink, idx, wgate);
+        hipLaunchKernelGGL(fn, grid, block, lds, stream, st->qbar, st->q2bar, st->kbar, st->kbar_r, st->ksig2,
+                           st->ksig2_r, st->knorm, hn, g.N, g.scale64, p->topk, p->band, p->n_sink, idx, wgate);
     } else {
         const dim3 grid(g.N, (unsigned)g.BH), block(kThreads);
 #define PISA_ROUTE_LAUNCH(DD)                                                                      \

@@ -65,9 +65,22 @@ struct StatsOut {
     void* vbar_c;
     void* kpack;      // bf16 only: K in the fused kernel's operand order
     void* kbpack;     // bf16 only: kbar_c in the same order, per group of 64 blocks
-    float* kbar_r;    // kbar in fp32, in the router's MFMA operand order
-    float* ksig2_r;   // second order: ksig2 in fp32, the same order
+    bf16_t* kbar_r;   // kbar split bf16 hi + lo, in the router's MFMA operand order
+    bf16_t* ksig2_r;  // second order: ksig2 the same way
+    float* knorm;     // ||kbar_j||_2, rounded up
 };
+
+// ||kbar_j|| of block j from the fp32 means kb_s (wave 0; a visible kb_s),
+// rounded up so that it bounds the fp64 norm: the router's error bound.
+template <int D>
+__device__ __forceinline__ void write_knorm(const float* kb_s, float* knorm, int64_t bh, int j, int N) {
+    if (threadIdx.x >= 64) return;
+    double s = 0.0;
+    for (int d = threadIdx.x; d < D; d += 64) s = fma((double)kb_s[d], (double)kb_s[d], s);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+    if (threadIdx.x == 0) knorm[bh * ((N + 15) / 16) * 16 + j] = (float)(sqrt(s) * (1.0 + 1e-6));
+}
 
 // Column statistics of one block from its LDS tiles (row pitch ld).
 template <typename T, int D>
@@ -117,11 +130,8 @@ __device__ __forceinline__ void column_stats(const T* tq, const T* tk, const T* 
         const int64_t off = (bh * n_blocks + j) * D;
         out.qbar[off + c] = a[0] / n;
         out.kbar[off + c] = mean;
-        // router operand order: key j = 16 cc + n, dim c = (D/4) g + 4 q + e
-        const int64_t roff = bh * (int64_t)((n_blocks + 15) / 16) * 16 * D +
-                             ((((int64_t)(j / 16)) * (D / 16) + (c % (D / 4)) / 4) * 64 + 16 * (c / (D / 4)) +
-                              j % 16) * 4 + c % 4;
-        out.kbar_r[roff] = (float)mean;
+        const int64_t rhead = bh * router_head_elems(n_blocks, D);
+        router_store(out.kbar_r + rhead, j, c, D, mean);
         static_cast<T*>(out.kbar_c)[off + c] = store_cast<T>((float)mean);
         if (out.kbpack) {
             // block j = row j % 64 of virtual group j / 64, laid out like kpack
@@ -142,7 +152,7 @@ __device__ __forceinline__ void column_stats(const T* tq, const T* tk, const T* 
             const double mx = a[3] / n;
             const double s2 = fmax(a[4] / n - mx * mx, 0.0);
             out.ksig2[off + c] = s2;
-            out.ksig2_r[roff] = (float)s2;
+            router_store(out.ksig2_r + rhead, j, c, D, s2);
         }
     }
 }
@@ -260,6 +270,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 
         column_stats<bf16_t, D>(sq, sk, sv, LD, rows, bh, j, N, second_order, s64, out, red, kb_s, vs_s);
         __syncthreads();  // kb_s / vs_s visible
+        write_knorm<D>(kb_s, out.knorm, bh, j, N);
         // acc -= kbar_j (x) V-hat_j
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
@@ -333,6 +344,8 @@ __global__ __launch_bounds__(kThreads) void stats_f32_kernel(
         __syncthreads();
         column_stats<float, D>(sq, sk, sv, LD, rows, bh, j, N, second_order, s64, out, red,
                                kb_s, vs_s);
+        __syncthreads();  // kb_s visible
+        write_knorm<D>(kb_s, out.knorm, bh, j, N);
         // partial H in fp64 from the exact products and exact column sums
 #pragma unroll
         for (int r = 0; r < PER; ++r) {
@@ -415,15 +428,15 @@ __global__ __launch_bounds__(kThreads) void prepare_operands_kernel(
         }
         return;
     }
+    __shared__ float kb_s[D];
     const int rows = min(kBlock, T_ - j * kBlock);
     const int64_t off = (bh * N + j) * D;
     if (tid < D) {
         const int c = tid;
         const double mean = kbar[off + c];
-        const int64_t roff = bh * (int64_t)((N + 15) / 16) * 16 * D +
-                             ((((int64_t)(j / 16)) * (D / 16) + (c % (D / 4)) / 4) * 64 + 16 * (c / (D / 4)) +
-                              j % 16) * 4 + c % 4;
-        out.kbar_r[roff] = (float)mean;
+        const int64_t rhead = bh * router_head_elems(N, D);
+        router_store(out.kbar_r + rhead, j, c, D, mean);
+        kb_s[c] = (float)mean;
         static_cast<T*>(out.kbar_c)[off + c] = store_cast<T>((float)mean);
         if (out.kbpack) {
             const int r = j % 64;
@@ -432,8 +445,10 @@ __global__ __launch_bounds__(kThreads) void prepare_operands_kernel(
                 f32_to_bf16((float)mean);
         }
         static_cast<T*>(out.vbar_c)[off + c] = store_cast<T>((float)((double)vsum[off + c] / (double)rows));
-        if (out.ksig2_r) out.ksig2_r[roff] = (float)ksig2[off + c];
+        if (out.ksig2_r) router_store(out.ksig2_r + rhead, j, c, D, ksig2[off + c]);
     }
+    __syncthreads();
+    write_knorm<D>(kb_s, out.knorm, bh, j, N);
     if (out.kpack) {
         // the block's K rows through LDS (coalesced loads), then in packed order
         const bf16_t* kh = reinterpret_cast<const bf16_t*>(k) + bh * (int64_t)T_ * D;
@@ -495,7 +510,7 @@ hipError_t launch_prepare_operands(const Geom& g, int dtype, int second_order, c
     const bool bf = dtype == PISA_BF16;
     StatsOut out{nullptr, nullptr, nullptr, nullptr, nullptr, st->kbar_c, st->vbar_c,
                  bf ? st->kpack : nullptr, bf ? st->kbpack : nullptr, st->kbar_r,
-                 second_order ? st->ksig2_r : nullptr};
+                 second_order ? st->ksig2_r : nullptr, st->knorm};
     bf16_t* hp = bf ? static_cast<bf16_t*>(st->hpack) : nullptr;
     const dim3 grid(g.N + 1, (unsigned)g.BH), block(kThreads);
 #define PISA_PREP_LAUNCH(TT, DD)                                                                   \
@@ -521,7 +536,7 @@ hipError_t launch_block_stats(const Geom& g, int dtype, int second_order, int co
     float* hpart = static_cast<float*>(workspace);
     StatsOut out{st->qbar, st->q2bar, st->kbar, st->vsum, st->ksig2, st->kbar_c, st->vbar_c, st->kpack,
                  dtype == PISA_BF16 ? st->kbpack : nullptr, st->kbar_r,
-                 second_order ? st->ksig2_r : nullptr};
+                 second_order ? st->ksig2_r : nullptr, st->knorm};
 #define PISA_STATS_LAUNCH(KERN, TT, DD)                                                            \
     hipLaunchKernelGGL(KERN<DD>, grid, block, 0, stream, static_cast<const TT*>(q),               \
                        static_cast<const TT*>(k), static_cast<const TT*>(v), g.T, g.N, bpw,       \

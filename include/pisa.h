@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define PISA_ABI_VERSION 12
+#define PISA_ABI_VERSION 13
 
 typedef enum {
     PISA_OK = 0,
@@ -139,11 +139,12 @@ typedef struct {
  *   PISA_OPERAND_KBAR_C   kbar rounded to fp32, then to the input dtype [B,H,N,D]
  *   PISA_OPERAND_VBAR_C   (vsum / n_j, in fp64 from the fp32 vsum) rounded to
  *                         fp32, then to the input dtype                 [B,H,N,D]
- *   PISA_OPERAND_KBAR_R   kbar in fp32, router order: key j = 16 c + n, dim
- *                         d = (D/4) g + 4 q + e (g < 4, q < D/16, e < 4) at
- *                         ((c D/16 + q) 64 + 16 g + n) 4 + e, [B,H,ceil(N/16) 16 D];
- *                         slots of keys past N unspecified
- *   PISA_OPERAND_KSIG2_R  ksig2 in fp32, the same order (second order only)
+ *   PISA_OPERAND_KBAR_R   kbar split into bf16 hi = rn(kbar), lo = rn(kbar - hi),
+ *                         router order: key j = 16 c + n, dim d = (D/4) g + 8 s + e
+ *                         (g < 4, s < D/32, e < 8), part p (hi, lo) at bf16 element
+ *                         ((c D/32 + s) 2 + p) 512 + (16 g + n) 8 + e,
+ *                         [B,H,ceil(N/16) 16 D 2]; slots of keys past N unspecified
+ *   PISA_OPERAND_KSIG2_R  ksig2 the same way (second order only)
  *   PISA_OPERAND_KPACK    bf16 only: K per block j, 32-row half h, chunk c
  *                         (dims 8c..8c+7), row r: element ((h D/8 + c) 32 + r) 8 + e
  *                         = k[64 j + 32 h + r][8 c + e]; 0 past seq_len   [B,H,N,64 D]
@@ -152,6 +153,7 @@ typedef struct {
  *   PISA_OPERAND_HPACK    bf16 only: hsum split into bf16 hi + lo, element
  *                         (((dt D/16 + ks) 2 + p) 64 + l) 8 + e = part p of
  *                         hsum[16 ks + 8 (l/32) + e][32 dt + l % 32]     [B,H,2 D D]
+ *   PISA_OPERAND_KNORM    fp32 ||kbar_j||_2, rounded up        [B,H,ceil(N/16) 16]
  */
 typedef enum {
     PISA_OPERAND_KBAR_C = 0,
@@ -161,7 +163,8 @@ typedef enum {
     PISA_OPERAND_KPACK = 4,
     PISA_OPERAND_KBPACK = 5,
     PISA_OPERAND_HPACK = 6,
-    PISA_OPERAND_COUNT = 7
+    PISA_OPERAND_KNORM = 7,
+    PISA_OPERAND_COUNT = 8
 } pisa_operand_t;
 
 /* ABI version of the library (PISA_ABI_VERSION). */

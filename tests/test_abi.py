@@ -32,7 +32,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pisa_abi_version() == 12
+    assert lib.pisa_abi_version() == 13
     for code in range(9):
         assert lib.pisa_status_str(code)
     assert lib.pisa_status_str(99) == b"unknown status"
@@ -150,14 +150,14 @@ def test_operand_buffer_layout(lib):
     B, H, N, D = 1, 40, 512, 128                        # Wan2.1-14B
     off, total = layout(T=32760, D=D, H=H)
     sizes = [H * N * D * 2, H * N * D * 2, H * 512 * D * 4, H * 512 * D * 4, H * N * 64 * D * 2,
-             H * 8 * 64 * D * 2, H * 2 * D * D * 2]
+             H * 8 * 64 * D * 2, H * 2 * D * D * 2, H * 512 * 4]
     want, at = [], 0
     for sz in sizes:
         want.append(at)
         at += rnd(sz)
     assert off == want and total == at
     off, total = layout(T=1000, D=64, H=2, dtype=_lib.PISA_F32)   # N = 16, fp32: no packed layouts
-    sizes = [2 * 16 * 64 * 4, 2 * 16 * 64 * 4, 2 * 16 * 64 * 4, 2 * 16 * 64 * 4, 0, 0, 0]
+    sizes = [2 * 16 * 64 * 4, 2 * 16 * 64 * 4, 2 * 16 * 64 * 4, 2 * 16 * 64 * 4, 0, 0, 0, 2 * 16 * 4]
     want, at = [], 0
     for sz in sizes:
         want.append(at)

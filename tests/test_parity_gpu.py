@@ -110,24 +110,32 @@ def test_block_stats(name):
     hp = run.host(view("hpack", B, H, 2 * D * D)) if w.dtype == "bf16" else None
     kbp = bits(view("kbpack", B, H, -(-N // 64), 64 * D)) if w.dtype == "bf16" else None
     kbb = bits(view("kbar_c", B, H, N, D)) if w.dtype == "bf16" else None
-    kbr = run.host(view("kbar_r", B, H, -(-N // 16) * 16 * D))
-    ksr = run.host(view("ksig2_r", B, H, -(-N // 16) * 16 * D)) if w.second_order else None
+    NC = -(-N // 16)
+    kbr = bits(view("kbar_r", B, H, NC * 16 * D * 2))
+    ksr = bits(view("ksig2_r", B, H, NC * 16 * D * 2)) if w.second_order else None
+    knr = view("knorm", B, H, NC * 16).cpu().numpy()
+    def router_order(x):
+        # split into bf16 hi = rn(x), lo = rn(x - hi); per 16-key chunk c,
+        # k-step s < D/32 and part p, 64 lanes (g = dim quarter, n = key) of 8
+        # dims (D/4) g + 8 s + e
+        xp = np.zeros((NC * 16, D))
+        xp[:N] = x
+        hi = I.bf16_bits(xp)
+        lo = I.bf16_bits(xp - I.bf16_to_f64(hi))
+        arr = np.stack([hi, lo]).reshape(2, NC, 16, 4, D // 32, 8)      # p, c, n, g, s, e
+        return arr.transpose(1, 4, 0, 3, 2, 5)                          # c, s, p, g, n, e
+    valid = (np.arange(NC * 16) < N).reshape(NC, 16)[:, None, None, None, :, None]
     for h in heads:
-        # kbar in fp32, router operand order: per 16-column chunk and 16-dim
-        # step q, 64 lanes (g = dim quarter, n = column) of 4 dims each
-        D = w.head_dim
-        NC = -(-run.N // 16)
-        kpad = np.zeros((NC * 16, D), np.float32)
-        kpad[:run.N] = kbar[0, h].astype(np.float32)
-        want_r = kpad.reshape(NC, 16, 4, D // 16, 4).transpose(0, 3, 2, 1, 4)
-        valid = (np.arange(NC * 16) < run.N).reshape(NC, 16)[:, None, None, :, None]
+        want_r = router_order(kbar[0, h])
         got_r = kbr[0, h].reshape(want_r.shape)
-        assert np.array_equal(np.where(valid, got_r, 0), want_r), h
-        if ksr is not None:   # ksig2 in fp32, the same order
-            spad = np.zeros((NC * 16, D), np.float32)
-            spad[:run.N] = ks2[0, h].astype(np.float32)
-            want_s = spad.reshape(NC, 16, 4, D // 16, 4).transpose(0, 3, 2, 1, 4)
-            assert np.array_equal(np.where(valid, ksr[0, h].reshape(want_s.shape), 0), want_s), h
+        assert np.array_equal(np.where(valid, got_r, 0), np.where(valid, want_r, 0)), h
+        if ksr is not None:
+            want_s = router_order(ks2[0, h])
+            assert np.array_equal(np.where(valid, ksr[0, h].reshape(want_s.shape), 0), np.where(valid, want_s, 0)), h
+        # the key norms bound ||kbar_j|| from above, within 2e-6
+        nrm = np.sqrt((kbar[0, h] ** 2).sum(axis=1))
+        kn = knr[0, h][:N].astype(np.float64)
+        assert (kn >= nrm).all() and (kn <= nrm * (1 + 2e-6) + 1e-30).all(), h
         if kp is not None:
             # packed K is a pure re-ordering of k's bits: per block and 32-row
             # half, 16-byte chunks chunk-major, then row; zero rows past T

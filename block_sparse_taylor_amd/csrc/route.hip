@@ -128,14 +128,17 @@ __device__ __forceinline__ Key wave_radix_select(int n, int need, KeyFn key, Tak
 }
 
 // The need-th largest of the wave's 32-bit keys (KPL per lane, in registers;
-// 0 marks an excluded slot, below every real key): a bitwise search from the
-// top bit down, counting keys >= the candidate with ballots (no atomics). It
-// stops as soon as exactly `need` keys reach the candidate: the answer is then
-// the smallest of those keys (a wave minimum). need_eq: how many keys equal to
-// the result belong to the selection.
+// 0 marks an excluded slot, below every real key), to within `width` in value:
+// a bitwise search from the top bit down, counting keys >= the candidate with
+// ballots (no atomics). After bit b the answer lies in [t, t | (2^b - 1)]; the
+// search stops as soon as that interval spans at most `width` in value (the
+// caller settles everything within its error bound of the interval exactly)
+// or exactly `need` keys reach the candidate (the answer is then the smallest
+// of them, a wave minimum). Returns the interval in *lo, *hi.
 constexpr int kKeysPerLane = 36;       // the fast kernel's rows: N <= 64 * 36
 template <int KPL>
-__device__ __forceinline__ uint32_t wave_select32(const uint32_t (&kv)[KPL], int need, int* need_eq) {
+__device__ __forceinline__ void wave_select32(const uint32_t (&kv)[KPL], int need, float width, uint32_t* lo,
+                                              uint32_t* hi) {
     uint32_t t = 0;
     for (int b = 31; b >= 0; --b) {
         const uint32_t cand = t | (1u << b);
@@ -144,21 +147,27 @@ __device__ __forceinline__ uint32_t wave_select32(const uint32_t (&kv)[KPL], int
         for (int i = 0; i < KPL; ++i) cnt += __popcll(__ballot(kv[i] >= cand));
         if (cnt >= need) {
             t = cand;
-            if (cnt == need) break;
+            if (cnt == need) {
+                uint32_t mn = 0xFFFFFFFFu;
+#pragma unroll
+                for (int i = 0; i < KPL; ++i) mn = kv[i] >= t ? min(mn, kv[i]) : mn;
+#pragma unroll
+                for (int off = 32; off > 0; off >>= 1) mn = min(mn, (uint32_t)__shfl_xor((int)mn, off));
+                *lo = *hi = mn;
+                return;
+            }
+        }
+        if (b > 0) {
+            const uint32_t top = t | ((1u << b) - 1u);
+            // both ends real scores of one sign region; NaN (key 0) never passes
+            if (t >= 0x00800000u && unkey32(top) - unkey32(t) <= width) {
+                *lo = t;
+                *hi = top;
+                return;
+            }
         }
     }
-    // the smallest key >= t (t itself when the search ran to the last bit)
-    uint32_t mn = 0xFFFFFFFFu;
-#pragma unroll
-    for (int i = 0; i < KPL; ++i) mn = kv[i] >= t ? min(mn, kv[i]) : mn;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) mn = min(mn, (uint32_t)__shfl_xor((int)mn, off));
-    t = mn;
-    int gt = 0;
-#pragma unroll
-    for (int i = 0; i < KPL; ++i) gt += __popcll(__ballot(kv[i] > t));
-    *need_eq = need - gt;
-    return t;
+    *lo = *hi = t;
 }
 
 // LDS of the fast kernel: the fp64 pooled q'^2 rows (second order only), fp32
@@ -254,27 +263,30 @@ __global__ __launch_bounds__(64 * route_waves(KPL)) __attribute__((amdgpu_waves_
     const uint4* kr4 = reinterpret_cast<const uint4*>(kbar_r + bh * router_head_elems(N, D));
     const uint4* sr4 = SO ? reinterpret_cast<const uint4*>(ksig2_r + bh * router_head_elems(N, D)) : nullptr;
     const float* kn = knorm + bh * (int64_t)NC * 16;
-    uint4 kv[2 * KB];
-    auto kload = [&](int c) {
+    uint4 kv[2 * KB], sv[SO ? 2 * KB : 1];   // this chunk's B operands (key means; variances)
+    auto kload = [&](int c) {   // one chunk ahead of its MFMAs
 #pragma unroll
         for (int u = 0; u < 2 * KB; ++u) kv[u] = kr4[((int64_t)c * 2 * KB + u) * 64 + lane];
+        if (SO) {
+#pragma unroll
+            for (int u = 0; u < 2 * KB; ++u) sv[u] = sr4[((int64_t)c * 2 * KB + u) * 64 + lane];
+        }
     };
     if (wave < NC) kload(wave);
     for (int c = wave; c < NC; c += NWV) {
         const int col = c * 16 + m16;
         const bool ok = col < N;
-        bf16x8_t bh8[KB], bl8[KB];
+        bf16x8_t bh8[KB], bl8[KB], sh8[SO ? KB : 1], sl8[SO ? KB : 1];
 #pragma unroll
         for (int sk = 0; sk < KB; ++sk) {
             bh8[sk] = __builtin_bit_cast(bf16x8_t, ok ? kv[2 * sk] : make_uint4(0, 0, 0, 0));
             bl8[sk] = __builtin_bit_cast(bf16x8_t, ok ? kv[2 * sk + 1] : make_uint4(0, 0, 0, 0));
+            if (SO) {
+                sh8[sk] = __builtin_bit_cast(bf16x8_t, ok ? sv[2 * sk] : make_uint4(0, 0, 0, 0));
+                sl8[sk] = __builtin_bit_cast(bf16x8_t, ok ? sv[2 * sk + 1] : make_uint4(0, 0, 0, 0));
+            }
         }
         if (c + NWV < NC) kload(c + NWV);   // the next chunk
-        uint4 sv[SO ? 2 * KB : 1];          // ksig2 of this chunk (second order), same order
-        if (SO) {
-#pragma unroll
-            for (int u = 0; u < 2 * KB; ++u) sv[u] = sr4[((int64_t)c * 2 * KB + u) * 64 + lane];
-        }
         if (ok) kmaxf = fmaxf(kmaxf, kn[col]);
         f4_t acc = {0.f, 0.f, 0.f, 0.f}, accw = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -286,11 +298,9 @@ __global__ __launch_bounds__(64 * route_waves(KPL)) __attribute__((amdgpu_waves_
         if (SO) {
 #pragma unroll
             for (int sk = 0; sk < KB; ++sk) {
-                const bf16x8_t sh = __builtin_bit_cast(bf16x8_t, ok ? sv[2 * sk] : make_uint4(0, 0, 0, 0));
-                const bf16x8_t sl = __builtin_bit_cast(bf16x8_t, ok ? sv[2 * sk + 1] : make_uint4(0, 0, 0, 0));
-                accw = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2h[sk], sh, accw, 0, 0, 0);
-                accw = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2h[sk], sl, accw, 0, 0, 0);
-                accw = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2l[sk], sh, accw, 0, 0, 0);
+                accw = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2h[sk], sh8[sk], accw, 0, 0, 0);
+                accw = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2h[sk], sl8[sk], accw, 0, 0, 0);
+                accw = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2l[sk], sh8[sk], accw, 0, 0, 0);
             }
         }
         float prior = 0.f;
@@ -392,11 +402,11 @@ __global__ __launch_bounds__(64 * route_waves(KPL)) __attribute__((amdgpu_waves_
             // fp32 sums of 3 D exact products (and of the spread and prior), plus
             // the split's dropped terms: |r~ - r| <= eps
             const float eps = (float)((4.0 * (3 * D + 8) * kU + 4.0 * 0x1p-18) * bound) + 1e-30f;
-            int need_eq;
-            const uint32_t tk = wave_select32<KPL>(kv, k, &need_eq);
-            const float tau = unkey32(tk);
-            // the band around tau in key space: x > hi <=> key > khi, x >= lo <=> key >= klo
-            const uint32_t khi = key32(tau + 2.f * eps), klo = key32(tau - 2.f * eps);
+            uint32_t tlo, thi;
+            wave_select32<KPL>(kv, k, eps, &tlo, &thi);
+            // the k-th largest fp32 score lies in [unkey(tlo), unkey(thi)]; the band
+            // around it in key space: x > hi <=> key > khi, x >= lo <=> key >= klo
+            const uint32_t khi = key32(unkey32(thi) + 2.f * eps), klo = key32(unkey32(tlo) - 2.f * eps);
             // certain members (above the band) and the close calls inside it,
             // the latter listed in ascending j
             int cg = 0, ca = 0;

@@ -161,6 +161,10 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run a plain copy of COPY_BYTES three times "
                          "(the reference kernel for the HBM byte counters)")
+    ap.add_argument("--routing-locality", action="store_true",
+                    help="after the timed steps, time the fused kernel again under routings of the same "
+                         "size but other locality (a sliding window, one fixed set per head, uniform "
+                         "random) to bound what re-fetched K/V blocks cost")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU run: derive the fused kernel's HBM bytes per launch from two "
                          "rocprofv3 --pmc counter_collection.csv files and record them")
@@ -279,6 +283,43 @@ def main():
         torch.cuda.synchronize()
         phase1_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(p1[:-1], p1[1:])]))
         del o1
+
+    # The fused kernel under routings with the router's list sizes but other
+    # locality: "window" routes query block i to blocks i+2 .. i+1+topk (mod N),
+    # so neighbouring query blocks share all but one; "fixed" routes every
+    # query block of a head to the same blocks; "random" draws distinct
+    # non-band blocks uniformly. Outside the timed steps.
+    locality = None
+    if args.routing_locality and topk and not so and w.band == 1 and N > topk + 3:
+        ii = torch.arange(N, device=dev).view(N, 1)
+        jj = torch.arange(topk, device=dev).view(1, topk)
+        routings = {"router": idx,
+                    "window": ((ii + 2 + jj) % N).to(torch.int32).expand(B, H, N, topk).contiguous(),
+                    "fixed": ((N // 2 + 2 + jj) % N).to(torch.int32).expand(B, H, N, topk).contiguous()}
+        gen = torch.Generator(device="cpu").manual_seed(0)
+        rnd = torch.empty(B, H, N, topk, dtype=torch.int32)
+        band_rows = torch.arange(N).repeat_interleave(3)
+        band_cols = (torch.arange(N).view(N, 1) + torch.tensor([-1, 0, 1])).clamp(0, N - 1).reshape(-1)
+        for bh in range(B * H):
+            sc = torch.rand(N, N, generator=gen)
+            sc[band_rows, band_cols] = -1.0
+            rnd.view(B * H, N, topk)[bh] = sc.topk(topk, dim=1).indices.to(torch.int32)
+        routings["random"] = rnd.to(dev)
+        locality = {}
+        o_l = torch.empty_like(q)
+        for name, ix in routings.items():
+            for _ in range(2):
+                P.pisa_attn_fwd(q, k, v, st, ix, None, band=1, out=o_l)
+            evs = [ev() for _ in range(args.steps + 1)]
+            torch.cuda.synchronize()
+            evs[0].record(stream)
+            for e_ in evs[1:]:
+                P.pisa_attn_fwd(q, k, v, st, ix, None, band=1, out=o_l)
+                e_.record(stream)
+            torch.cuda.synchronize()
+            locality[name] = round(float(np.mean([a_.elapsed_time(b_) for a_, b_ in zip(evs[:-1], evs[1:])])), 4)
+        locality = {"ms": locality, "note": "pisa_attn_fwd mean ms under each routing (same list sizes)"}
+        del o_l, routings
 
     # Morton token reorder around the operator (raster-order token-major
     # [B,T,H,D] activations -> Z-order [B,H,T,D] for q, k, v, and the output
@@ -433,6 +474,8 @@ def main():
                      "kernel": ATTN_KERNEL + " (pisa_attn_fwd)"},
         "input_generation_s": round(gen_s, 1),
     }
+    if locality is not None:
+        out["routing_locality"] = locality
     if bwd_ms is not None:
         # five products per attended pair (recomputed logits, dP, dV, dK, dQ; the
         # virtual tokens likewise with kbar and V-hat), plus H g and dH per row

@@ -208,6 +208,16 @@ struct VirtRow {
     __device__ float mass(int j) const { return j == N - 1 ? fexp2(lnlast2) : 64.f; }
 };
 
+// Bits j = 32 w0 .. 32 w0 + 63 of a query block's exact-set mask row (words
+// w0 and w0 + 1; bits at j >= N are zero). The row is the same for the whole
+// workgroup, so these are scalar loads and a loop over the set bits skips
+// the blocks that are not exact without touching them.
+__device__ __forceinline__ uint64_t mask_pair(const uint32_t* mrow, int w0, int NW) {
+    uint64_t b = mrow[w0];
+    if (w0 + 1 < NW) b |= (uint64_t)mrow[w0 + 1] << 32;
+    return b;
+}
+
 // (H g)^T for the head-dim tiles [dt0, dt0 + D / 64): A = H rows (hi + lo), B = dout rows.
 template <int D, typename BOp>
 __device__ __forceinline__ void hg_tiles(f32x16_t (&hg)[D / 64], const bf16_t* hh, const bf16_t* hl, BOp bop,
@@ -231,7 +241,7 @@ __device__ __forceinline__ void hg_tiles(f32x16_t (&hg)[D / 64], const bf16_t* h
 // Per query row: lse over the exact keys and the virtual tokens (mass n_j),
 // delta = dout . o, beta = dout . (q' H) / T and c = l_tail / (T den).
 template <int D>
-__global__ __launch_bounds__(kThreads) void bwd_rowstats_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void bwd_rowstats_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ o,
     const bf16_t* __restrict__ dout, const bf16_t* __restrict__ kbh, const bf16_t* __restrict__ kbl,
     const bf16_t* __restrict__ hh, const bf16_t* __restrict__ hl, const uint32_t* __restrict__ mask,
@@ -270,20 +280,24 @@ __global__ __launch_bounds__(kThreads) void bwd_rowstats_kernel(
         lt = lt * cr + (tail ? a : 0.f);
         m = mn;
     };
-    for (int j = 0; j < N; ++j) {
-        if (!((mrow[j >> 5] >> (j & 31)) & 1u)) continue;   // uniform
-        const int nval = min(kBlock, T - j * kBlock);
-        uint4 kr[C::LPT];
-        tile_load<D>(kr, k + base + (int64_t)j * kBlock * D, nval, tid);
-        __syncthreads();
-        tile_store<D>(sK, kr, tid);
-        __syncthreads();
-        f32x16_t s = zero16();
+    for (int w0 = 0; w0 < NW; w0 += 2) {   // exact KV blocks j: the set bits of the mask row
+        uint64_t bits = mask_pair(mrow, w0, NW);
+        while (bits) {
+            const int j = 32 * w0 + __builtin_ctzll(bits);
+            bits &= bits - 1;
+            const int nval = min(kBlock, T - j * kBlock);
+            uint4 kr[C::LPT];
+            tile_load<D>(kr, k + base + (int64_t)j * kBlock * D, nval, tid);
+            __syncthreads();
+            tile_store<D>(sK, kr, tid);
+            __syncthreads();
+            f32x16_t s = zero16();
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) s = mfma(row_op<D>(sK, kt * 32 + r32, ks, g), as_bf16x8(qreg[ks]), s);
+            for (int ks = 0; ks < C::KS; ++ks) s = mfma(row_op<D>(sK, kt * 32 + r32, ks, g), as_bf16x8(qreg[ks]), s);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[r] = kt * 32 + acc_row(r, g) < nval ? s[r] * c2 : -INFINITY;
-        merge(s, false);
+            for (int r = 0; r < 16; ++r) s[r] = kt * 32 + acc_row(r, g) < nval ? s[r] * c2 : -INFINITY;
+            merge(s, false);
+        }
     }
     const bf16_t* kbh_h = kbh + bh * (int64_t)N * D;
     const bf16_t* kbl_h = kbl + bh * (int64_t)N * D;
@@ -430,37 +444,41 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     for (int dt = 0; dt < C::DT; ++dt) acc[dt] = zero16();
 
     // exact KV blocks
-    for (int j = 0; j < N; ++j) {
-        if (!((mrow[j >> 5] >> (j & 31)) & 1u)) continue;   // uniform
-        const int nval = min(kBlock, T - j * kBlock);
-        uint4 kr[C::LPT], vr_[C::LPT];
-        tile_load<D>(kr, k + base + (int64_t)j * kBlock * D, nval, tid);
-        tile_load<D>(vr_, v + base + (int64_t)j * kBlock * D, nval, tid);
-        __syncthreads();
-        tile_store<D>(sK, kr, tid);
-        tile_store<D>(sV, vr_, tid);
-        __syncthreads();
-        f32x16_t s = zero16(), dp = zero16();
+    for (int w0 = 0; w0 < NW; w0 += 2) {   // exact KV blocks j: the set bits of the mask row
+        uint64_t bits = mask_pair(mrow, w0, NW);
+        while (bits) {
+            const int j = 32 * w0 + __builtin_ctzll(bits);
+            bits &= bits - 1;
+            const int nval = min(kBlock, T - j * kBlock);
+            uint4 kr[C::LPT], vr_[C::LPT];
+            tile_load<D>(kr, k + base + (int64_t)j * kBlock * D, nval, tid);
+            tile_load<D>(vr_, v + base + (int64_t)j * kBlock * D, nval, tid);
+            __syncthreads();
+            tile_store<D>(sK, kr, tid);
+            tile_store<D>(sV, vr_, tid);
+            __syncthreads();
+            f32x16_t s = zero16(), dp = zero16();
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
-            s = mfma(row_op<D>(sK, kt * 32 + r32, ks, g), qop(ks), s);
-            dp = mfma(row_op<D>(sV, kt * 32 + r32, ks, g), oop(ks), dp);
-        }
+            for (int ks = 0; ks < C::KS; ++ks) {
+                s = mfma(row_op<D>(sK, kt * 32 + r32, ks, g), qop(ks), s);
+                dp = mfma(row_op<D>(sV, kt * 32 + r32, ks, g), oop(ks), dp);
+            }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float p = kt * 32 + acc_row(r, g) < nval ? fexp2(fmaf(s[r], c2, -lse2)) : 0.f;
-            s[r] = p * (dp[r] - delta);   // dS^T
-        }
+            for (int r = 0; r < 16; ++r) {
+                const float p = kt * 32 + acc_row(r, g) < nval ? fexp2(fmaf(s[r], c2, -lse2)) : 0.f;
+                s[r] = p * (dp[r] - delta);   // dS^T
+            }
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            bf16x8_t hi, lo;
-            split_op(s, h, hi, lo);
-            const int r0 = kt * 32 + 16 * h;
+            for (int h = 0; h < 2; ++h) {
+                bf16x8_t hi, lo;
+                split_op(s, h, hi, lo);
+                const int r0 = kt * 32 + 16 * h;
 #pragma unroll
-            for (int dt = 0; dt < C::DT; ++dt) {
-                const bf16x8_t a = tr_op<D>(sK, ta, dt, r0);   // K^T: head dims x keys
-                acc[dt] = mfma(a, hi, acc[dt]);
-                acc[dt] = mfma(a, lo, acc[dt]);
+                for (int dt = 0; dt < C::DT; ++dt) {
+                    const bf16x8_t a = tr_op<D>(sK, ta, dt, r0);   // K^T: head dims x keys
+                    acc[dt] = mfma(a, hi, acc[dt]);
+                    acc[dt] = mfma(a, lo, acc[dt]);
+                }
             }
         }
     }
@@ -605,6 +623,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     __shared__ __attribute__((aligned(16))) unsigned char skv[2 * C::TILE];    // K, V of the block
     __shared__ float slse[64], sdel[64];
     __shared__ float sblk[5][D];   // the block's kbar, dkbar, dV-hat, dsig2, dH V-hat
+    __shared__ uint32_t scol[kThreads / 32];   // selection bits of kThreads query blocks
     unsigned char* sQ = smem;
     unsigned char* sO = smem + C::TILE;
     unsigned char* sKt = skv;
@@ -631,54 +650,72 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) dva[dt] = dka[dt] = zero16();
 
-    // query blocks whose exact set holds j
-    for (int i = 0; i < N; ++i) {
-        if (!((mask[(bh * N + i) * (int64_t)NW + (j >> 5)] >> (j & 31)) & 1u)) continue;   // uniform
-        const int rows = min(kBlock, T - i * kBlock);
-        uint4 qr[C::LPT], orr[C::LPT];
-        tile_load<D>(qr, q + base + (int64_t)i * kBlock * D, rows, tid);
-        tile_load<D>(orr, dout + base + (int64_t)i * kBlock * D, rows, tid);
-        float ls = INFINITY, dl = 0.f;
-        if (tid < rows) {
-            const f32x4_t rs = rowstat[bh * (int64_t)T + (int64_t)i * kBlock + tid];
-            ls = rs[0] * kLog2e;
-            dl = rs[1];
+    // query blocks whose exact set holds j, kThreads at a time: one mask word per
+    // thread, the selections gathered by ballot; the set bits are then walked in order
+    for (int i0 = 0; i0 < N; i0 += kThreads) {
+        const bool sel = i0 + tid < N &&
+                         ((mask[(bh * N + i0 + tid) * (int64_t)NW + (j >> 5)] >> (j & 31)) & 1u);
+        const uint64_t bal = __ballot(sel);
+        __syncthreads();   // the previous chunk's words have been read
+        if (lane == 0) {
+            scol[2 * wave] = (uint32_t)bal;
+            scol[2 * wave + 1] = (uint32_t)(bal >> 32);
         }
         __syncthreads();
-        tile_store<D>(sQ, qr, tid);
-        tile_store<D>(sO, orr, tid);
-        if (tid < 64) {
-            slse[tid] = ls;
-            sdel[tid] = dl;
-        }
-        __syncthreads();
-        f32x16_t s = zero16(), dp = zero16();
+        for (int w0 = 0; w0 < kThreads / 32; w0 += 2) {
+            // (readfirstlane returns int: through uint32_t, so the low word is not sign-extended)
+            uint64_t bits = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(scol[w0]) |
+                            ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(scol[w0 + 1]) << 32);
+            while (bits) {
+                const int i = i0 + 32 * w0 + __builtin_ctzll(bits);
+                bits &= bits - 1;
+                const int rows = min(kBlock, T - i * kBlock);
+                uint4 qr[C::LPT], orr[C::LPT];
+                tile_load<D>(qr, q + base + (int64_t)i * kBlock * D, rows, tid);
+                tile_load<D>(orr, dout + base + (int64_t)i * kBlock * D, rows, tid);
+                float ls = INFINITY, dl = 0.f;
+                if (tid < rows) {
+                    const f32x4_t rs = rowstat[bh * (int64_t)T + (int64_t)i * kBlock + tid];
+                    ls = rs[0] * kLog2e;
+                    dl = rs[1];
+                }
+                __syncthreads();
+                tile_store<D>(sQ, qr, tid);
+                tile_store<D>(sO, orr, tid);
+                if (tid < 64) {
+                    slse[tid] = ls;
+                    sdel[tid] = dl;
+                }
+                __syncthreads();
+                f32x16_t s = zero16(), dp = zero16();
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
-            s = mfma(row_op<D>(sQ, qt * 32 + r32, ks, g), row_op<D>(sKt, kt * 32 + r32, ks, g), s);   // S
-            dp = mfma(row_op<D>(sO, qt * 32 + r32, ks, g), row_op<D>(sVt, kt * 32 + r32, ks, g), dp); // dP
-        }
-        f32x16_t p;
+                for (int ks = 0; ks < C::KS; ++ks) {
+                    s = mfma(row_op<D>(sQ, qt * 32 + r32, ks, g), row_op<D>(sKt, kt * 32 + r32, ks, g), s);   // S
+                    dp = mfma(row_op<D>(sO, qt * 32 + r32, ks, g), row_op<D>(sVt, kt * 32 + r32, ks, g), dp); // dP
+                }
+                f32x16_t p;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int qq = qt * 32 + acc_row(r, g);
-            p[r] = fexp2(fmaf(s[r], c2, -slse[qq]));       // rows past T: lse = +inf, P = 0
-            s[r] = p[r] * (dp[r] - sdel[qq]);              // dS
-        }
+                for (int r = 0; r < 16; ++r) {
+                    const int qq = qt * 32 + acc_row(r, g);
+                    p[r] = fexp2(fmaf(s[r], c2, -slse[qq]));       // rows past T: lse = +inf, P = 0
+                    s[r] = p[r] * (dp[r] - sdel[qq]);              // dS
+                }
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            bf16x8_t phi, plo, hi, lo;
-            split_op(p, h, phi, plo);
-            split_op(s, h, hi, lo);
-            const int r0 = qt * 32 + 16 * h;
+                for (int h = 0; h < 2; ++h) {
+                    bf16x8_t phi, plo, hi, lo;
+                    split_op(p, h, phi, plo);
+                    split_op(s, h, hi, lo);
+                    const int r0 = qt * 32 + 16 * h;
 #pragma unroll
-            for (int dt = 0; dt < C::DT; ++dt) {
-                const bf16x8_t ao = tr_op<D>(sO, ta, dt, r0);            // dO^T P
-                dva[dt] = mfma(ao, phi, dva[dt]);
-                dva[dt] = mfma(ao, plo, dva[dt]);
-                const bf16x8_t aq = tr_op<D>(sQ, ta, dt, r0);            // Q^T dS
-                dka[dt] = mfma(aq, hi, dka[dt]);
-                dka[dt] = mfma(aq, lo, dka[dt]);
+                    for (int dt = 0; dt < C::DT; ++dt) {
+                        const bf16x8_t ao = tr_op<D>(sO, ta, dt, r0);            // dO^T P
+                        dva[dt] = mfma(ao, phi, dva[dt]);
+                        dva[dt] = mfma(ao, plo, dva[dt]);
+                        const bf16x8_t aq = tr_op<D>(sQ, ta, dt, r0);            // Q^T dS
+                        dka[dt] = mfma(aq, hi, dka[dt]);
+                        dka[dt] = mfma(aq, lo, dka[dt]);
+                    }
+                }
             }
         }
     }

@@ -164,6 +164,25 @@ def test_routing_with_invalid_ids_and_padding():
     check(wl("tiny", seq_len=900, head_dim=64, heads=2), seed=8, topk=4, idx_fn=mangle)
 
 
+def test_bf16_query_blocks_beyond_one_chunk():
+    """N = 301: the dk/dv kernel gathers the query blocks that hold a KV block
+    exactly 256 at a time (one mask word per thread, a ballot per wave), so a
+    column spans two chunks. Every query block is also routed to block 5
+    (where that is not already so), so block 5's column has every bit set,
+    bit 31 of each 32-block word included (a word taken as signed would set
+    the upper half of its 64-bit pair)."""
+    w = wl("wan14", heads=1, grid=(7, 41, 67), seq_len=19229)
+
+    def force5(idx):
+        x = idx.cpu().clone()
+        for i in range(x.shape[2]):
+            row = x[0, 0, i]
+            if abs(i - 5) > 1 and not bool((row == 5).any()):
+                row[0] = 5
+        return x.to(idx.device)
+    check(w, seed=14, topk=6, idx_fn=force5)
+
+
 def test_every_block_exact():
     w = wl("tiny", seq_len=640, head_dim=128, heads=1)
     check(w, seed=9, topk=8, band=1)   # N = 10: every candidate routed

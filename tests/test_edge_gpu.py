@@ -148,13 +148,24 @@ def test_deterministic(dtype):
     assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2]) and torch.equal(a[3], b[3])
 
 
-def test_mfma_matches_valu_reference():
-    """The bf16 MFMA kernel and the fp32 VALU kernel agree on the same routing."""
-    (q, k, v), _ = make(2048, 128, "bf16", 31, H=3)
+def test_mfma_and_valu_kernels_match_oracle():
+    """pisa_attn_fwd (bf16 matrix cores) and pisa_attn_fwd_valu (the fp32
+    vector kernel) on the same bf16 inputs and routing, with the second-order
+    term: each against the oracle fed that routing (the bf16 bar), and the
+    two against each other within twice it."""
+    (q, k, v), (qh, kh, vh) = make(2048, 128, "bf16", 31, H=3)
     st, idx, wg, o = run_all(q, k, v, 4, 1, second_order=True)
-    o_ref = P.pisa_attn_fwd_valu(q, k, v, st, idx, wg, band=1, second_order=True)
+    o_valu = P.pisa_attn_fwd_valu(q, k, v, st, idx, wg, band=1, second_order=True)
     torch.cuda.synchronize()
-    assert (o.double() - o_ref.double()).abs().max() <= 2e-2
+    idx_h = idx.cpu().numpy()
+    worst = [0.0, 0.0]
+    for h in range(3):
+        ref = O.pisa_forward_head(qh[0, h], kh[0, h], vh[0, h], topk=4, band=1, second_order=True,
+                                  routing=idx_h[0, h])
+        for n, out in enumerate((o, o_valu)):
+            worst[n] = max(worst[n], tol_check(out[0, h], ref, "bf16"))
+    say(f"[gpu]   worst abs error: matrix-core kernel {worst[0]:.2e}, vector kernel {worst[1]:.2e}")
+    assert (o.double() - o_valu.double()).abs().max() <= 4e-2
 
 
 @pytest.mark.parametrize("second_order", [False, True])

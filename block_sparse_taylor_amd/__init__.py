@@ -154,6 +154,13 @@ def stats_workspace(k: torch.Tensor, scale=None) -> torch.Tensor:
     return torch.empty(max(16, n), dtype=torch.uint8, device=k.device)
 
 
+def attn_bwd_workspace(q: torch.Tensor, scale=None) -> torch.Tensor:
+    """A workspace of pisa_attn_bwd_workspace_bytes for tensors of q's shape."""
+    lib = library()
+    n = lib.pisa_attn_bwd_workspace_bytes(ctypes.byref(_shape(q, scale)))
+    return torch.empty(max(16, n), dtype=torch.uint8, device=q.device)
+
+
 def pisa_block_stats(q, k, v, second_order=False, scale=None, out: PisaStats | None = None,
                      workspace: torch.Tensor | None = None, cov_bias=False) -> PisaStats:
     lib = library()

@@ -158,6 +158,8 @@ def parse():
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the pisa_attn_bwd leg (timed after the forward steps)")
     ap.add_argument("--bwd-steps", type=int, default=3)
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip timing the step captured into a HIP graph (after the timed steps)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run a plain copy of COPY_BYTES three times "
                          "(the reference kernel for the HBM byte counters)")
@@ -264,6 +266,31 @@ def main():
             cold.append(c0.elapsed_time(c1))
         cold_ms = round(float(np.mean(cold)), 4)
         del scratch
+
+    # the same step captured once into a HIP graph (no entry point allocates,
+    # clears memory or synchronises with the host) and replayed: the launch
+    # overhead a graph removes, after the timed steps and outside them
+    graph_ms = None
+    if not args.no_graph:
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        graph.replay()
+        torch.cuda.synchronize()
+        g0, g1 = ev(), ev()
+        g0.record(stream)
+        for _ in range(args.steps):
+            graph.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = g0.elapsed_time(g1) / args.steps
+        del graph
 
     # Phase 1 alone (exact tiles only, phase_mask bit 0), after the timed steps
     # and outside them, on the same inputs and routing table
@@ -442,6 +469,7 @@ def main():
                                + (", second order" if so else ""),
                    "topk": topk, "band": w.band, "second_order": so},
         "ms_per_step_cache_flushed": cold_ms,
+        "ms_per_step_graph": None if graph_ms is None else round(graph_ms, 4),
         "pisa_attn_fwd": {"ms": round(attn_ms, 4), **spread(per_kernel[2]),
                           "dense_equiv_tflops": round(dense_flops / (attn_ms * 1e-3) / 1e12, 2),
                           "algorithmic_tflop": round(attn_flops / 1e12, 4)},

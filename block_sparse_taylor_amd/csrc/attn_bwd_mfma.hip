@@ -194,6 +194,16 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(const double* __rest
 
 // Virtual-token logit bias of block j for query block i (log2 units), or
 // -inf where j is not a virtual token of i (exact, or past N).
+// Buffer descriptor of a wave-uniform range of `bytes`: loads past it read
+// zero, so a tile of fewer than 64 rows loads without per-row branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t brsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    void* p = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
 struct VirtRow {
     const uint32_t* mrow;
     const float* wrow;
@@ -287,7 +297,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
             bits &= bits - 1;
             const int nval = min(kBlock, T - j * kBlock);
             uint4 kr[C::LPT];
-            tile_load<D>(kr, k + base + (int64_t)j * kBlock * D, nval, tid);
+            const __amdgpu_buffer_rsrc_t rk = brsrc(k + base + (int64_t)j * kBlock * D, (uint32_t)(nval * C::RB));
+#pragma unroll
+            for (int m = 0; m < C::LPT; ++m)
+                kr[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, (int)(16 * (tid + kThreads * m)), 0, 0));
             __syncthreads();
             tile_store<D>(sK, kr, tid);
             __syncthreads();
@@ -451,8 +464,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             bits &= bits - 1;
             const int nval = min(kBlock, T - j * kBlock);
             uint4 kr[C::LPT], vr_[C::LPT];
-            tile_load<D>(kr, k + base + (int64_t)j * kBlock * D, nval, tid);
-            tile_load<D>(vr_, v + base + (int64_t)j * kBlock * D, nval, tid);
+            const __amdgpu_buffer_rsrc_t rk = brsrc(k + base + (int64_t)j * kBlock * D, (uint32_t)(nval * C::RB));
+            const __amdgpu_buffer_rsrc_t rv = brsrc(v + base + (int64_t)j * kBlock * D, (uint32_t)(nval * C::RB));
+#pragma unroll
+            for (int m = 0; m < C::LPT; ++m) {
+                const uint32_t o = (uint32_t)(16 * (tid + kThreads * m));
+                kr[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, (int)o, 0, 0));
+                vr_[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, (int)o, 0, 0));
+            }
             __syncthreads();
             tile_store<D>(sK, kr, tid);
             tile_store<D>(sV, vr_, tid);
@@ -671,14 +690,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                 bits &= bits - 1;
                 const int rows = min(kBlock, T - i * kBlock);
                 uint4 qr[C::LPT], orr[C::LPT];
-                tile_load<D>(qr, q + base + (int64_t)i * kBlock * D, rows, tid);
-                tile_load<D>(orr, dout + base + (int64_t)i * kBlock * D, rows, tid);
-                float ls = INFINITY, dl = 0.f;
-                if (tid < rows) {
-                    const f32x4_t rs = rowstat[bh * (int64_t)T + (int64_t)i * kBlock + tid];
-                    ls = rs[0] * kLog2e;
-                    dl = rs[1];
+                const __amdgpu_buffer_rsrc_t rq = brsrc(q + base + (int64_t)i * kBlock * D, (uint32_t)(rows * C::RB));
+                const __amdgpu_buffer_rsrc_t ro = brsrc(dout + base + (int64_t)i * kBlock * D, (uint32_t)(rows * C::RB));
+#pragma unroll
+                for (int m = 0; m < C::LPT; ++m) {
+                    const uint32_t o = (uint32_t)(16 * (tid + kThreads * m));
+                    qr[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)o, 0, 0));
+                    orr[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ro, (int)o, 0, 0));
                 }
+                const f32x4_t rs = rowstat[bh * (int64_t)T + (int64_t)i * kBlock + min(tid & 63, rows - 1)];
+                const bool in = (tid & 63) < rows;
+                const float ls = in ? rs[0] * kLog2e : INFINITY;
+                const float dl = in ? rs[1] : 0.f;
                 __syncthreads();
                 tile_store<D>(sQ, qr, tid);
                 tile_store<D>(sO, orr, tid);

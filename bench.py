@@ -381,26 +381,36 @@ def main():
             del xt, ht, ot
 
     # Backward (pisa_attn_bwd) of the last step's forward, on seeded dout,
-    # timed on its own after the steps: one call runs all its kernels
-    bwd_ms = None
+    # timed on its own after the steps: one call runs all its kernels. The
+    # forward is run once more (untimed) writing its row statistics, which
+    # the backward takes as training does; the backward that recomputes them
+    # is timed beside it.
+    bwd_ms = bwd_re_ms = None
     if not args.no_backward:
         gen = torch.Generator(device=dev).manual_seed(1234)
         dout = torch.randn(q.shape, generator=gen, device=dev, dtype=torch.float32).to(q.dtype)
         grads = tuple(torch.empty_like(q) for _ in range(3))
-        bws = torch.empty(P.library().pisa_attn_bwd_workspace_bytes(ctypes.byref(P._shape(q, None))),
-                          dtype=torch.uint8, device=dev)
-        bwd = lambda: P.pisa_attn_bwd(q, k, v, o, dout, st, idx if topk else None, wg, band=w.band,
-                                      second_order=so, workspace=bws, out=grads)
-        bwd()
-        torch.cuda.synchronize()
-        b0, b1 = ev(), ev()
-        b0.record(stream)
-        for _ in range(args.bwd_steps):
+        bws = P.attn_bwd_workspace(q)
+        rs = P.alloc_row_stats(q)
+        P.pisa_attn_fwd(q, k, v, st, idx if topk else None, wg, band=w.band, second_order=so, out=o,
+                        row_stats=rs)
+
+        def time_bwd(row_stats):
+            bwd = lambda: P.pisa_attn_bwd(q, k, v, o, dout, st, idx if topk else None, wg, band=w.band,
+                                          second_order=so, workspace=bws, out=grads, row_stats=row_stats)
             bwd()
-        b1.record(stream)
-        torch.cuda.synchronize()
-        bwd_ms = b0.elapsed_time(b1) / args.bwd_steps
-        del grads, bws, dout
+            torch.cuda.synchronize()
+            b0, b1 = ev(), ev()
+            b0.record(stream)
+            for _ in range(args.bwd_steps):
+                bwd()
+            b1.record(stream)
+            torch.cuda.synchronize()
+            return b0.elapsed_time(b1) / args.bwd_steps
+
+        bwd_ms = time_bwd(rs)
+        bwd_re_ms = time_bwd(None)
+        del grads, bws, dout, rs
 
     # ---- algorithmic work of the fused kernel (from the routing table actually used)
     idx_h = idx.cpu().numpy().reshape(B * H, N, topk)
@@ -513,6 +523,8 @@ def main():
         bpeak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
         out["pisa_attn_bwd"] = {
             "ms": round(bwd_ms, 3), "steps": args.bwd_steps, "algorithmic_tflop": round(bwd_flops / 1e12, 4),
+            "ms_recomputing_row_stats": round(bwd_re_ms, 3),
+            "note": "with the forward's row statistics (lse, c); ms_recomputing_row_stats without them",
             "roofline": {"bound": "mfma" if w.dtype == "bf16" else "alu", "achieved": round(bwd_tflops, 2),
                          "peak": bpeak, "unit": "TFLOP/s", "frac": round(bwd_tflops / bpeak, 4), "traffic": None,
                          "kernel": "pisa_attn_bwd (all its kernels: " + ("bf16 MFMA products and chain, "

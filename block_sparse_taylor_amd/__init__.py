@@ -243,10 +243,19 @@ def pisa_route_topk(q, stats: PisaStats, topk: int, band: int = 1, second_order=
     return idx, (wgate if second_order else None)
 
 
+def alloc_row_stats(q: torch.Tensor) -> torch.Tensor:
+    """[B, H, T, 2] fp32: each row's lse and first-order weight c, as
+    pisa_attn_fwd writes them for pisa_attn_bwd."""
+    B, H, T, _ = q.shape
+    return torch.empty(B, H, T, 2, dtype=torch.float32, device=q.device)
+
+
 def _attn(fn_name, q, k, v, stats, idx, wgate, topk, band, second_order, first_order,
-          phase_mask, scale, out, n_sink=0):
+          phase_mask, scale, out, n_sink=0, row_stats=None):
     lib = library()
-    _contig(q, k, v, idx, wgate)
+    _contig(q, k, v, idx, wgate, row_stats)
+    if row_stats is not None and (row_stats.dtype != torch.float32 or row_stats.shape != (*q.shape[:3], 2)):
+        raise ValueError("row_stats must be a float32 tensor of shape [B, H, T, 2]")
     sh = _shape(q, scale)
     o = out if out is not None else torch.empty_like(q)
     prm = _lib.Params(int(topk), int(band), int(second_order), int(first_order), int(phase_mask),
@@ -256,31 +265,34 @@ def _attn(fn_name, q, k, v, stats, idx, wgate, topk, band, second_order, first_o
     fn = getattr(lib, fn_name)
     _lib.check(fn_name, fn(ctypes.byref(sh), ctypes.byref(prm), _ptr(q), _ptr(k), _ptr(v),
                            ctypes.byref(cs), ops, nops, _ptr(idx) if topk else None,
-                           _ptr(wgate) if second_order else None, _ptr(o), _stream(q.device)))
+                           _ptr(wgate) if second_order else None, _ptr(o),
+                           None if row_stats is None else _ptr(row_stats), _stream(q.device)))
     return o
 
 
 def pisa_attn_fwd(q, k, v, stats, idx, wgate=None, band=1, second_order=False, first_order=True,
-                  phase_mask=0, scale=None, out=None, n_sink=0):
+                  phase_mask=0, scale=None, out=None, n_sink=0, row_stats=None):
+    """o; with ``row_stats`` (alloc_row_stats) also each row's lse and c."""
     topk = 0 if idx is None else idx.shape[-1]
     return _attn("pisa_attn_fwd", q, k, v, stats, idx, wgate, topk, band, second_order,
-                 first_order, phase_mask, scale, out, n_sink)
+                 first_order, phase_mask, scale, out, n_sink, row_stats)
 
 
 def pisa_attn_fwd_valu(q, k, v, stats, idx, wgate=None, band=1, second_order=False,
-                       first_order=True, phase_mask=0, scale=None, out=None, n_sink=0):
+                       first_order=True, phase_mask=0, scale=None, out=None, n_sink=0, row_stats=None):
     topk = 0 if idx is None else idx.shape[-1]
     return _attn("pisa_attn_fwd_valu", q, k, v, stats, idx, wgate, topk, band, second_order,
-                 first_order, phase_mask, scale, out, n_sink)
+                 first_order, phase_mask, scale, out, n_sink, row_stats)
 
 
 def pisa_attn_bwd(q, k, v, o, dout, stats, idx, wgate=None, band=1, second_order=False,
-                  first_order=True, scale=None, n_sink=0, workspace=None, out=None):
+                  first_order=True, scale=None, n_sink=0, workspace=None, out=None, row_stats=None):
     """(dq, dk, dv) of sum(dout * o) for o = pisa_attn_fwd(q, k, v, stats, idx,
     wgate, ...) with the same arguments; the routing and the gate are held
-    constant (pisa_attn_bwd). ``out`` may pass three preallocated tensors."""
+    constant (pisa_attn_bwd). ``out`` may pass three preallocated tensors;
+    ``row_stats`` what the forward wrote for this o (optional)."""
     lib = library()
-    _contig(q, k, v, o, dout, idx, wgate)
+    _contig(q, k, v, o, dout, idx, wgate, row_stats)
     for t in (k, v, o, dout):
         if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
             raise ValueError("q, k, v, o, dout must share shape, dtype and device")
@@ -295,6 +307,7 @@ def pisa_attn_bwd(q, k, v, o, dout, stats, idx, wgate=None, band=1, second_order
     _lib.check("pisa_attn_bwd", lib.pisa_attn_bwd(
         ctypes.byref(sh), ctypes.byref(prm), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout),
         ctypes.byref(cs), _ptr(idx) if topk else None, _ptr(wgate) if second_order else None,
+        None if row_stats is None else _ptr(row_stats),
         _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), _stream(q.device)))
     return dq, dk, dv
 
@@ -360,21 +373,23 @@ class _Attention(torch.autograd.Function):
         idx, wg = pisa_route_topk(q, st, topk, band=band, second_order=second_order, scale=scale,
                                   n_sink=n_sink, cov_bias=cov_bias)
         idx = idx if topk else None
+        rs = alloc_row_stats(q)
         o = pisa_attn_fwd(q, k, v, st, idx, wg, band=band, second_order=second_order, scale=scale,
-                          n_sink=n_sink)
+                          n_sink=n_sink, row_stats=rs)
         # the backward reads the statistics (not the operand buffer), the
-        # routing table and the gated table: kept as saved tensors
-        ctx.save_for_backward(q, k, v, o, st.kbar, st.vsum, st.hsum, st.q2bar, st.ksig2, idx, wg)
+        # routing table, the gated table and each row's lse and c: kept as
+        # saved tensors
+        ctx.save_for_backward(q, k, v, o, st.kbar, st.vsum, st.hsum, st.q2bar, st.ksig2, idx, wg, rs)
         ctx.cfg = (band, second_order, scale, n_sink)
         return o
 
     @staticmethod
     def backward(ctx, do):
-        q, k, v, o, kbar, vsum, hsum, q2bar, ksig2, idx, wg = ctx.saved_tensors
+        q, k, v, o, kbar, vsum, hsum, q2bar, ksig2, idx, wg, rs = ctx.saved_tensors
         band, so, scale, n_sink = ctx.cfg
         st = PisaStats(None, q2bar, kbar, vsum, ksig2, hsum, None)
         dq, dk, dv = pisa_attn_bwd(q, k, v, o, do.contiguous(), st, idx, wg, band=band,
-                                   second_order=so, scale=scale, n_sink=n_sink)
+                                   second_order=so, scale=scale, n_sink=n_sink, row_stats=rs)
         return dq, dk, dv, None, None, None, None, None, None
 
 

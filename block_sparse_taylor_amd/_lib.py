@@ -90,12 +90,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     for name in ("pisa_attn_fwd", "pisa_attn_fwd_valu"):
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
-        fn.argtypes = [P(Shape), P(Params), vp, vp, vp, P(Stats), vp, ctypes.c_size_t, vp, vp, vp, vp]
+        fn.argtypes = [P(Shape), P(Params), vp, vp, vp, P(Stats), vp, ctypes.c_size_t, vp, vp, vp, vp, vp]
     lib.pisa_attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.pisa_attn_bwd_workspace_bytes.argtypes = [P(Shape)]
     lib.pisa_attn_bwd.restype = ctypes.c_int
     lib.pisa_attn_bwd.argtypes = [P(Shape), P(Params), vp, vp, vp, vp, vp, P(Stats), vp, vp, vp, vp, vp, vp,
-                                  ctypes.c_size_t, vp]
+                                  vp, ctypes.c_size_t, vp]
     lib.pisa_attn_fwd_plan.restype = ctypes.c_int
     lib.pisa_attn_fwd_plan.argtypes = [P(Shape), P(Params), P(ctypes.c_int32), P(ctypes.c_int64)]
     lib.pisa_z_order.restype = ctypes.c_int

@@ -704,7 +704,8 @@ BwdLayout bwd_layout(const Geom& g, bool mfma) {
 template <typename T, int D>
 hipError_t run_bwd(const Geom& g, const pisa_params_t* p, const void* q, const void* k, const void* v,
                    const void* o, const void* dout, const StatsView* st, const int32_t* idx,
-                   const float* wgate, void* dq, void* dk, void* dv, void* ws, hipStream_t stream) {
+                   const float* wgate, const float* fwd_rstat, void* dq, void* dk, void* dv, void* ws,
+                   hipStream_t stream) {
     constexpr bool kMfma = std::is_same<T, bf16_t>::value;
     const BwdLayout L = bwd_layout(g, kMfma);
     unsigned char* w = static_cast<unsigned char*>(ws);
@@ -735,7 +736,9 @@ hipError_t run_bwd(const Geom& g, const pisa_params_t* p, const void* q, const v
         const float* wg = so ? wgate : nullptr;
         hipError_t e = launch_bwd_prep(g, st, kbh, kbl, vhh, vhl, hh, hl, stream);
         if (e == hipSuccess)
-            e = launch_bwd_rowstats(g, tq, tk, to, tg, kbh, kbl, hh, hl, mask, wg, rowstat, L.NW, so, fo, stream);
+            e = fwd_rstat ? launch_bwd_rowstats_fwd(g, tq, to, tg, hh, hl, fwd_rstat, rowstat, fo, stream)
+                          : launch_bwd_rowstats(g, tq, tk, to, tg, kbh, kbl, hh, hl, mask, wg, rowstat, L.NW, so, fo,
+                                                stream);
         if (e == hipSuccess)
             e = launch_bwd_virt_mfma(g, tq, tg, st, mask, rowstat, wg, dkb, dvh, dw, dsg, L.NW, so, stream);
         if (e == hipSuccess)
@@ -778,14 +781,16 @@ size_t attn_bwd_workspace_bytes(const Geom& g, int dtype) { return bwd_layout(g,
 
 hipError_t launch_attn_bwd(const Geom& g, int dtype, const pisa_params_t* p, const void* q, const void* k,
                            const void* v, const void* o, const void* dout, const StatsView* st,
-                           const int32_t* idx, const float* wgate, void* dq, void* dk, void* dv, void* ws,
-                           hipStream_t stream) {
+                           const int32_t* idx, const float* wgate, const float* fwd_rstat, void* dq, void* dk,
+                           void* dv, void* ws, hipStream_t stream) {
     if (dtype == PISA_BF16) {
-        if (g.D == 128) return run_bwd<bf16_t, 128>(g, p, q, k, v, o, dout, st, idx, wgate, dq, dk, dv, ws, stream);
-        return run_bwd<bf16_t, 64>(g, p, q, k, v, o, dout, st, idx, wgate, dq, dk, dv, ws, stream);
+        if (g.D == 128)
+            return run_bwd<bf16_t, 128>(g, p, q, k, v, o, dout, st, idx, wgate, fwd_rstat, dq, dk, dv, ws, stream);
+        return run_bwd<bf16_t, 64>(g, p, q, k, v, o, dout, st, idx, wgate, fwd_rstat, dq, dk, dv, ws, stream);
     }
-    if (g.D == 128) return run_bwd<float, 128>(g, p, q, k, v, o, dout, st, idx, wgate, dq, dk, dv, ws, stream);
-    return run_bwd<float, 64>(g, p, q, k, v, o, dout, st, idx, wgate, dq, dk, dv, ws, stream);
+    // fp32 inputs: the row kernel derives lse together with dq, so it recomputes them
+    if (g.D == 128) return run_bwd<float, 128>(g, p, q, k, v, o, dout, st, idx, wgate, nullptr, dq, dk, dv, ws, stream);
+    return run_bwd<float, 64>(g, p, q, k, v, o, dout, st, idx, wgate, nullptr, dq, dk, dv, ws, stream);
 }
 
 }  // namespace pisa

@@ -399,6 +399,67 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     }
 }
 
+// Row statistics when the forward wrote each row's lse and c (pisa_attn_fwd's
+// row_stats): the exact and virtual pairs are not re-scored; only delta =
+// dout . o and beta = s dout . (q H) / T are formed, as above (beta by the
+// same hi + lo products of H with dout, summed over the two key halves).
+template <int D>
+__global__ __launch_bounds__(kThreads) void bwd_rowstats_fwd_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ o, const bf16_t* __restrict__ dout,
+    const bf16_t* __restrict__ hh, const bf16_t* __restrict__ hl, const float* __restrict__ fwd_rstat,
+    f32x4_t* __restrict__ rowstat, int T, float scale, int first_order) {
+    using C = BC<D>;
+    __shared__ float sbp[2][32];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r32 = lane & 31, g = lane >> 5;
+    const int kt = wave >> 1, qt = wave & 1;
+    const int64_t bh = blockIdx.y;
+    const int i = blockIdx.x;
+    const int t = i * kBlock + qt * 32 + r32;
+    const int64_t base = bh * (int64_t)T * D;
+    float bp = 0.f;
+    if (first_order) {
+        uint4 oreg[C::KS];
+        rows_from_global<D>(oreg, dout + base, t, T, g);
+        f32x16_t hg[C::DT / 2];
+        hg_tiles<D>(hg, hh + bh * (int64_t)D * D, hl + bh * (int64_t)D * D,
+                    [&](int ks) { return as_bf16x8(oreg[ks]); }, kt * C::DT / 2, r32, g);
+        if (t < T) {
+#pragma unroll
+            for (int x = 0; x < C::DT / 2; ++x)
+#pragma unroll
+                for (int run = 0; run < 4; ++run) {
+                    const int d0 = (kt * C::DT / 2 + x) * 32 + 8 * run + 4 * g;
+                    const uint2 qq = *reinterpret_cast<const uint2*>(q + base + (int64_t)t * D + d0);
+                    bp += bf16_lo(qq.x) * hg[x][4 * run] + bf16_hi(qq.x) * hg[x][4 * run + 1] +
+                          bf16_lo(qq.y) * hg[x][4 * run + 2] + bf16_hi(qq.y) * hg[x][4 * run + 3];
+                }
+        }
+        bp += __shfl_xor(bp, 32);
+    }
+    if (kt == 1 && g == 0) sbp[qt][r32] = bp;
+    __syncthreads();
+    if (kt == 0 && t < T) {
+        float dl = 0.f;
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c) {
+            const int d0 = (D / 2) * g + 8 * c;
+            const uint4 a = *reinterpret_cast<const uint4*>(dout + base + (int64_t)t * D + d0);
+            const uint4 b = *reinterpret_cast<const uint4*>(o + base + (int64_t)t * D + d0);
+            dl += bf16_lo(a.x) * bf16_lo(b.x) + bf16_hi(a.x) * bf16_hi(b.x) + bf16_lo(a.y) * bf16_lo(b.y) +
+                  bf16_hi(a.y) * bf16_hi(b.y) + bf16_lo(a.z) * bf16_lo(b.z) + bf16_hi(a.z) * bf16_hi(b.z) +
+                  bf16_lo(a.w) * bf16_lo(b.w) + bf16_hi(a.w) * bf16_hi(b.w);
+        }
+        dl += __shfl_xor(dl, 32);
+        if (g == 0) {
+            const float2 fr = *reinterpret_cast<const float2*>(fwd_rstat + 2 * (bh * (int64_t)T + t));
+            const float beta = first_order ? scale * (bp + sbp[qt][r32]) / (float)T : 0.f;
+            f32x4_t rs = {fr.x, dl, beta, first_order ? fr.y : 0.f};
+            rowstat[bh * (int64_t)T + t] = rs;
+        }
+    }
+}
+
 // ---------------------------------------------------------------- dq
 // dq' = K^T dS^T (exact keys) + kbar^T dlam^T (virtual tokens, kbar hi + lo)
 // + c H g, then dq = s dq' + 2 s^2 q dq2bar_i / n_i (second order).
@@ -1089,6 +1150,19 @@ hipError_t launch_bwd_rowstats(const Geom& g, const bf16_t* q, const bf16_t* k, 
     if (g.D == 128) PISA_ROWSTATS(128);
     else PISA_ROWSTATS(64);
 #undef PISA_ROWSTATS
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_rowstats_fwd(const Geom& g, const bf16_t* q, const bf16_t* o, const bf16_t* dout,
+                                   const bf16_t* hh, const bf16_t* hl, const float* fwd_rstat, f32x4_t* rowstat,
+                                   int first_order, hipStream_t stream) {
+    const dim3 grid(g.N, (unsigned)g.BH);
+    if (g.D == 128)
+        hipLaunchKernelGGL((bwd_rowstats_fwd_kernel<128>), grid, dim3(kThreads), 0, stream, q, o, dout, hh, hl,
+                           fwd_rstat, rowstat, g.T, g.scale, first_order);
+    else
+        hipLaunchKernelGGL((bwd_rowstats_fwd_kernel<64>), grid, dim3(kThreads), 0, stream, q, o, dout, hh, hl,
+                           fwd_rstat, rowstat, g.T, g.scale, first_order);
     return hipGetLastError();
 }
 

@@ -23,7 +23,8 @@ template <typename T, int D>
 __global__ __launch_bounds__(kRows) void attn_valu_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const double* __restrict__ kbar, const float* __restrict__ vsum, const float* __restrict__ hsum,
-    const int32_t* __restrict__ idx, const float* __restrict__ wgate, T* __restrict__ o, int Tn,
+    const int32_t* __restrict__ idx, const float* __restrict__ wgate, T* __restrict__ o,
+    float* __restrict__ rstat, int Tn,
     int N, float scale, int topk, int band, int n_sink, int second_order, int first_order, int phase_mask) {
     constexpr int kSub = 32;                 // K/V rows staged per step
     __shared__ float sk[kSub * D];
@@ -160,6 +161,11 @@ __global__ __launch_bounds__(kRows) void attn_valu_kernel(
         const float inv = 1.f / l;
 #pragma unroll
         for (int d = 0; d < D; ++d) o[base + (int64_t)t * D + d] = store_cast<T>(acc[d] * inv);
+        if (rstat != nullptr) {   // the row's lse and c
+            const int64_t rr = 2 * (bh * (int64_t)Tn + t);
+            rstat[rr] = m + logf(l);
+            rstat[rr + 1] = do_first ? ltail / l / (float)Tn : 0.f;
+        }
     }
 }
 
@@ -167,14 +173,15 @@ __global__ __launch_bounds__(kRows) void attn_valu_kernel(
 
 hipError_t launch_attn_fwd_valu(const Geom& g, int dtype, const pisa_params_t* p, const void* q,
                                 const void* k, const void* v, const StatsView* st,
-                                const int32_t* idx, const float* wgate, void* o, hipStream_t stream) {
+                                const int32_t* idx, const float* wgate, void* o, float* rstat,
+                                hipStream_t stream) {
     dim3 grid(g.N, (unsigned)g.BH), block(kRows);
     const size_t shm = (size_t)g.N;
 #define PISA_VALU_LAUNCH(TT, DD)                                                                   \
     hipLaunchKernelGGL((attn_valu_kernel<TT, DD>), grid, block, shm, stream,                       \
                        static_cast<const TT*>(q), static_cast<const TT*>(k),                       \
                        static_cast<const TT*>(v), st->kbar, st->vsum, st->hsum, idx, wgate,        \
-                       static_cast<TT*>(o), g.T, g.N, g.scale, p->topk, p->band, p->n_sink, p->second_order,  \
+                       static_cast<TT*>(o), rstat, g.T, g.N, g.scale, p->topk, p->band, p->n_sink, p->second_order,  \
                        p->first_order, p->phase_mask)
     if (dtype == PISA_BF16) {
         if (g.D == 128) PISA_VALU_LAUNCH(bf16_t, 128);

@@ -137,7 +137,8 @@ hipError_t launch_route_topk(const Geom& g, const pisa_params_t* p, const StatsV
 
 hipError_t launch_attn_fwd_valu(const Geom& g, int dtype, const pisa_params_t* p, const void* q,
                                 const void* k, const void* v, const StatsView* st,
-                                const int32_t* idx, const float* wgate, void* o, hipStream_t stream);
+                                const int32_t* idx, const float* wgate, void* o, float* rstat,
+                                hipStream_t stream);
 
 hipError_t launch_reorder(const Geom& g, int64_t batch, int64_t heads, int elem_bytes, bool gather,
                           const int32_t* perm, const void* src, void* dst, hipStream_t stream);
@@ -150,6 +151,10 @@ hipError_t launch_bwd_rowstats(const Geom& g, const bf16_t* q, const bf16_t* k, 
                                const bf16_t* kbh, const bf16_t* kbl, const bf16_t* hh, const bf16_t* hl,
                                const uint32_t* mask, const float* wgate, f32x4_t* rowstat, int NW, int second_order,
                                int first_order, hipStream_t stream);
+// Row statistics from the forward's per-row lse and c: only delta and beta computed.
+hipError_t launch_bwd_rowstats_fwd(const Geom& g, const bf16_t* q, const bf16_t* o, const bf16_t* dout,
+                                   const bf16_t* hh, const bf16_t* hl, const float* fwd_rstat, f32x4_t* rowstat,
+                                   int first_order, hipStream_t stream);
 hipError_t launch_bwd_dq(const Geom& g, const bf16_t* q, const bf16_t* k, const bf16_t* v, const bf16_t* dout,
                          const bf16_t* kbh, const bf16_t* kbl, const bf16_t* vhh, const bf16_t* vhl,
                          const bf16_t* hh, const bf16_t* hl, const uint32_t* mask, const float* wgate,
@@ -167,8 +172,8 @@ hipError_t launch_bwd_dkdv(const Geom& g, const bf16_t* q, const bf16_t* k, cons
                            hipStream_t stream);
 hipError_t launch_attn_bwd(const Geom& g, int dtype, const pisa_params_t* p, const void* q, const void* k,
                            const void* v, const void* o, const void* dout, const StatsView* st,
-                           const int32_t* idx, const float* wgate, void* dq, void* dk, void* dv, void* ws,
-                           hipStream_t stream);
+                           const int32_t* idx, const float* wgate, const float* fwd_rstat, void* dq, void* dk,
+                           void* dv, void* ws, hipStream_t stream);
 
 // Kernel choice of pisa_attn_fwd (a pisa_attn_kernel_t) and the longest
 // per-wave item list of the persistent bf16 kernel for these parameters.
@@ -177,6 +182,6 @@ int attn_fwd_kernel(const Geom& g, int dtype, const pisa_params_t* p);
 
 hipError_t launch_attn_fwd_mfma(const Geom& g, const pisa_params_t* p, const void* q, const void* k,
                                 const void* v, const StatsView* st, const int32_t* idx,
-                                const float* wgate, void* o, hipStream_t stream);
+                                const float* wgate, void* o, float* rstat, hipStream_t stream);
 
 }  // namespace pisa

@@ -103,10 +103,13 @@ size_t tensor_bytes(const Geom& g, int dtype) {
 
 pisa_status_t from_hip(hipError_t e) { return e == hipSuccess ? PISA_OK : PISA_ERR_HIP; }
 
+// bytes of a [B,H,T,2] fp32 row-statistics array
+size_t row_stats_bytes(const Geom& g) { return (size_t)g.BH * (size_t)g.T * 2 * sizeof(float); }
+
 pisa_status_t attn_common(const pisa_shape_t* shape, const pisa_params_t* params, const void* q,
                           const void* k, const void* v, const pisa_stats_t* stats, const void* operands,
-                          size_t operands_bytes, const int32_t* idx, const float* wgate, void* o, Geom* g,
-                          bool need_operands) {
+                          size_t operands_bytes, const int32_t* idx, const float* wgate, void* o,
+                          const float* row_stats, Geom* g, bool need_operands) {
     PISA_TRY(check_shape(shape, g));
     PISA_TRY(check_params(params, *g));
     PISA_TRY(check_ptr(q));
@@ -119,6 +122,12 @@ pisa_status_t attn_common(const pisa_shape_t* shape, const pisa_params_t* params
     if (params->second_order) PISA_TRY(check_ptr(wgate));
     const size_t tb = tensor_bytes(*g, shape->dtype);
     if (overlap(o, tb, q, tb) || overlap(o, tb, k, tb) || overlap(o, tb, v, tb)) return PISA_ERR_PARAM;
+    if (row_stats) {   // an optional output: shares no byte with o or the inputs
+        PISA_TRY(check_ptr(row_stats));
+        const size_t rb = row_stats_bytes(*g);
+        for (const void* t : {static_cast<const void*>(q), k, v, static_cast<const void*>(o)})
+            if (overlap(row_stats, rb, t, tb)) return PISA_ERR_PARAM;
+    }
     return PISA_OK;
 }
 
@@ -304,26 +313,28 @@ pisa_status_t pisa_route_topk(const pisa_shape_t* shape, const pisa_params_t* pa
 pisa_status_t pisa_attn_fwd(const pisa_shape_t* shape, const pisa_params_t* params, const void* q,
                             const void* k, const void* v, const pisa_stats_t* stats, const void* operands,
                             size_t operands_bytes, const int32_t* idx, const float* wgate, void* o,
-                            void* stream) {
+                            float* row_stats, void* stream) {
     Geom g;
     const bool bf = shape && shape->dtype == PISA_BF16;
-    PISA_TRY(attn_common(shape, params, q, k, v, stats, operands, operands_bytes, idx, wgate, o, &g, bf));
+    PISA_TRY(attn_common(shape, params, q, k, v, stats, operands, operands_bytes, idx, wgate, o, row_stats, &g, bf));
     hipStream_t s = static_cast<hipStream_t>(stream);
     const pisa_params_t pr = resolved(params, g);
     const StatsView sv = stats_view(g, shape->dtype, stats, bf ? operands : nullptr);
-    if (bf) return from_hip(launch_attn_fwd_mfma(g, &pr, q, k, v, &sv, idx, wgate, o, s));
-    return from_hip(launch_attn_fwd_valu(g, shape->dtype, &pr, q, k, v, &sv, idx, wgate, o, s));
+    if (bf) return from_hip(launch_attn_fwd_mfma(g, &pr, q, k, v, &sv, idx, wgate, o, row_stats, s));
+    return from_hip(launch_attn_fwd_valu(g, shape->dtype, &pr, q, k, v, &sv, idx, wgate, o, row_stats, s));
 }
 
 pisa_status_t pisa_attn_fwd_valu(const pisa_shape_t* shape, const pisa_params_t* params,
                                  const void* q, const void* k, const void* v,
                                  const pisa_stats_t* stats, const void* operands, size_t operands_bytes,
-                                 const int32_t* idx, const float* wgate, void* o, void* stream) {
+                                 const int32_t* idx, const float* wgate, void* o, float* row_stats,
+                                 void* stream) {
     Geom g;
-    PISA_TRY(attn_common(shape, params, q, k, v, stats, operands, operands_bytes, idx, wgate, o, &g, false));
+    PISA_TRY(attn_common(shape, params, q, k, v, stats, operands, operands_bytes, idx, wgate, o, row_stats, &g,
+                         false));
     const pisa_params_t pr = resolved(params, g);
     const StatsView sv = stats_view(g, shape->dtype, stats, nullptr);
-    return from_hip(launch_attn_fwd_valu(g, shape->dtype, &pr, q, k, v, &sv, idx, wgate, o,
+    return from_hip(launch_attn_fwd_valu(g, shape->dtype, &pr, q, k, v, &sv, idx, wgate, o, row_stats,
                                          static_cast<hipStream_t>(stream)));
 }
 
@@ -346,8 +357,9 @@ size_t pisa_attn_bwd_workspace_bytes(const pisa_shape_t* shape) {
 
 pisa_status_t pisa_attn_bwd(const pisa_shape_t* shape, const pisa_params_t* params, const void* q,
                             const void* k, const void* v, const void* o, const void* dout,
-                            const pisa_stats_t* stats, const int32_t* idx, const float* wgate, void* dq,
-                            void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream) {
+                            const pisa_stats_t* stats, const int32_t* idx, const float* wgate,
+                            const float* row_stats, void* dq, void* dk, void* dv, void* workspace,
+                            size_t workspace_bytes, void* stream) {
     Geom g;
     PISA_TRY(check_shape(shape, &g));
     PISA_TRY(check_params(params, g));
@@ -356,6 +368,7 @@ pisa_status_t pisa_attn_bwd(const pisa_shape_t* shape, const pisa_params_t* para
     PISA_TRY(check_stats(stats, params->second_order, false));
     if (params->topk > 0) PISA_TRY(check_ptr(idx));
     if (params->second_order) PISA_TRY(check_ptr(wgate));
+    if (row_stats) PISA_TRY(check_ptr(row_stats));
     if (params->phase_mask != 0) return PISA_ERR_UNSUPPORTED;
     if (workspace_bytes < attn_bwd_workspace_bytes(g, shape->dtype)) return PISA_ERR_WORKSPACE;
     // no output may share a byte with another output, an input or the workspace
@@ -368,10 +381,12 @@ pisa_status_t pisa_attn_bwd(const pisa_shape_t* shape, const pisa_params_t* para
         for (const void* in : ins)
             if (overlap(outs[a], tb, in, tb)) return PISA_ERR_PARAM;
         if (overlap(outs[a], tb, workspace, workspace_bytes)) return PISA_ERR_PARAM;
+        if (row_stats && overlap(outs[a], tb, row_stats, row_stats_bytes(g))) return PISA_ERR_PARAM;
     }
+    if (row_stats && overlap(workspace, workspace_bytes, row_stats, row_stats_bytes(g))) return PISA_ERR_PARAM;
     const pisa_params_t pr = resolved(params, g);
     const StatsView sv = stats_view(g, shape->dtype, stats, nullptr);
-    return from_hip(launch_attn_bwd(g, shape->dtype, &pr, q, k, v, o, dout, &sv, idx, wgate, dq, dk,
+    return from_hip(launch_attn_bwd(g, shape->dtype, &pr, q, k, v, o, dout, &sv, idx, wgate, row_stats, dq, dk,
                                     dv, workspace, static_cast<hipStream_t>(stream)));
 }
 

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define PISA_ABI_VERSION 13
+#define PISA_ABI_VERSION 14
 
 typedef enum {
     PISA_OK = 0,
@@ -273,13 +273,20 @@ pisa_status_t pisa_route_topk(const pisa_shape_t *shape, const pisa_params_t *pa
  * one inside the band makes the result unspecified. o: [B,H,T,D] in the input
  * dtype; must not alias q, k, v. bf16 runs compute QK^T and PV with bf16 MFMA (fp32
  * accumulation, P rounded to bf16); fp32 runs compute in fp32.
+ * row_stats: NULL, or a [B,H,T,2] fp32 output (it must not overlap o, q, k,
+ * v): for each row t, row_stats[t][0] = lse_t = ln(sum_{j in S_i} sum_n
+ * e^{s q.k} + l_tail_t), the natural log of the output's denominator, and
+ * row_stats[t][1] = c_t = first_order ? l_tail_t / (T (that denominator)) :
+ * 0, the weight of F_t per unit of (s q_t) H after normalisation. They are
+ * the per-row quantities pisa_attn_bwd would otherwise recompute (both
+ * follow from the same sums as o; a row whose output is NaN gets NaN).
  * Reads the operand buffer (bf16) or stats->vsum, kbar and hsum (fp32).
  */
 pisa_status_t pisa_attn_fwd(const pisa_shape_t *shape, const pisa_params_t *params,
                             const void *q, const void *k, const void *v,
                             const pisa_stats_t *stats, const void *operands,
                             size_t operands_bytes, const int32_t *idx,
-                            const float *wgate, void *o, void *stream);
+                            const float *wgate, void *o, float *row_stats, void *stream);
 
 /*
  * pisa_attn_fwd_valu: the same contract as pisa_attn_fwd, computed by a plain
@@ -291,7 +298,7 @@ pisa_status_t pisa_attn_fwd_valu(const pisa_shape_t *shape, const pisa_params_t 
                                  const void *q, const void *k, const void *v,
                                  const pisa_stats_t *stats, const void *operands,
                                  size_t operands_bytes, const int32_t *idx,
-                                 const float *wgate, void *o, void *stream);
+                                 const float *wgate, void *o, float *row_stats, void *stream);
 
 /*
  * pisa_attn_fwd_plan (HOST only, no GPU work): which kernel pisa_attn_fwd runs
@@ -373,8 +380,12 @@ pisa_status_t pisa_reorder_scatter(const pisa_shape_t *shape, const int32_t *per
  *   stats             as pisa_block_stats wrote them for q, k, v; reads kbar,
  *                     vsum, hsum (and q2bar, ksig2 if second_order);
  *   idx, wgate        as passed to pisa_attn_fwd;
+ *   row_stats         NULL, or the row_stats pisa_attn_fwd wrote with this o:
+ *                     bf16 inputs then take each row's lse and c from it
+ *                     instead of re-scoring the row's exact and virtual
+ *                     pairs (fp32 inputs recompute them either way);
  *   dq, dk, dv        [B,H,T,D] outputs in the shape's dtype; they must not
- *                     alias each other, the inputs, or the workspace;
+ *                     alias each other, the inputs, row_stats or the workspace;
  *   workspace         caller-owned device memory of at least
  *                     pisa_attn_bwd_workspace_bytes(shape) bytes (per-row
  *                     statistics, the selection bitmask, per-block partial
@@ -391,8 +402,8 @@ size_t pisa_attn_bwd_workspace_bytes(const pisa_shape_t *shape);
 pisa_status_t pisa_attn_bwd(const pisa_shape_t *shape, const pisa_params_t *params,
                             const void *q, const void *k, const void *v, const void *o,
                             const void *dout, const pisa_stats_t *stats, const int32_t *idx,
-                            const float *wgate, void *dq, void *dk, void *dv, void *workspace,
-                            size_t workspace_bytes, void *stream);
+                            const float *wgate, const float *row_stats, void *dq, void *dk,
+                            void *dv, void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -105,10 +105,13 @@ int main(void) {
         pisa_params_t badcov = params(4, 1, 0, 0, 2);
         EXPECT(pisa_route_topk(&s, &badcov, &st, ops, opsb, (int32_t*)fake(30), NULL, NULL) == PISA_ERR_PARAM);
     }
-    EXPECT(pisa_attn_fwd(&s, &p, q, k, v, &st, ops, opsb, (int32_t*)fake(30), NULL, q, NULL) == PISA_ERR_PARAM);
-    EXPECT(pisa_attn_fwd_valu(&s, &p, q, k, v, NULL, ops, opsb, (int32_t*)fake(30), NULL, o, NULL) == PISA_ERR_NULL);
-    EXPECT(pisa_attn_bwd(&s, &p, q, k, v, o, fake(6), &st, (int32_t*)fake(30), NULL, fake(7), fake(7), fake(8), ws,
-                         (size_t)1 << 40, NULL) == PISA_ERR_PARAM);
+    EXPECT(pisa_attn_fwd(&s, &p, q, k, v, &st, ops, opsb, (int32_t*)fake(30), NULL, q, NULL, NULL) == PISA_ERR_PARAM);
+    EXPECT(pisa_attn_fwd(&s, &p, q, k, v, &st, ops, opsb, (int32_t*)fake(30), NULL, o, (float*)k, NULL) ==
+           PISA_ERR_PARAM);
+    EXPECT(pisa_attn_fwd_valu(&s, &p, q, k, v, NULL, ops, opsb, (int32_t*)fake(30), NULL, o, NULL, NULL) ==
+           PISA_ERR_NULL);
+    EXPECT(pisa_attn_bwd(&s, &p, q, k, v, o, fake(6), &st, (int32_t*)fake(30), NULL, NULL, fake(7), fake(7), fake(8),
+                         ws, (size_t)1 << 40, NULL) == PISA_ERR_PARAM);
     EXPECT(pisa_reorder_gather(&s, (int32_t*)fake(31), q, (char*)q + 1024, NULL) == PISA_ERR_PARAM);
     EXPECT(pisa_reorder_scatter(&s, NULL, q, k, NULL) == PISA_ERR_NULL);
 

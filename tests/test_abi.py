@@ -32,7 +32,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pisa_abi_version() == 13
+    assert lib.pisa_abi_version() == 14
     for code in range(9):
         assert lib.pisa_status_str(code)
     assert lib.pisa_status_str(99) == b"unknown status"
@@ -126,12 +126,12 @@ def call_route(lib, s=None, p=None, st=None, ops=OPS, opsb=OPSB, idx=fake(30), w
 
 
 def call_attn(lib, name="pisa_attn_fwd", s=None, p=None, q=fake(1), k=fake(2), v=fake(3),
-              st=None, ops=OPS, opsb=OPSB, idx=fake(30), wg=None, o=fake(4)):
+              st=None, ops=OPS, opsb=OPSB, idx=fake(30), wg=None, o=fake(4), rs=None):
     s = s or shape()
     p = p or _lib.Params(4, 1, 0, 1, 0)
     st = st or stats()
     fn = getattr(lib, name)
-    return fn(ctypes.byref(s), ctypes.byref(p), q, k, v, ctypes.byref(st), ops, opsb, idx, wg, o, None)
+    return fn(ctypes.byref(s), ctypes.byref(p), q, k, v, ctypes.byref(st), ops, opsb, idx, wg, o, rs, None)
 
 
 E = {n: c for c, n in _lib.STATUS_NAMES.items()}
@@ -244,6 +244,11 @@ def test_attn_validation(lib, name):
     assert call_attn(lib, name, st=stats(hsum=None)) == E["PISA_ERR_NULL"]
     assert call_attn(lib, name, s=shape(dtype=2)) == E["PISA_ERR_DTYPE"]
     assert call_attn(lib, name, s=shape(T=10 ** 7)) == E["PISA_ERR_SHAPE"]
+    # the optional row statistics: aligned, and sharing no byte with o or the inputs
+    assert call_attn(lib, name, rs=MIS) == E["PISA_ERR_ALIGN"]
+    assert call_attn(lib, name, rs=fake(4) + 4096) == E["PISA_ERR_PARAM"]   # inside o
+    assert call_attn(lib, name, rs=fake(2)) == E["PISA_ERR_PARAM"]          # k
+    assert call_attn(lib, name, rs=fake(4) - 1024) == E["PISA_ERR_PARAM"]   # runs into o
     if name == "pisa_attn_fwd":   # bf16: the matrix-core kernels read the operand buffer
         assert call_attn(lib, name, ops=None) == E["PISA_ERR_NULL"]
         assert call_attn(lib, name, opsb=1024) == E["PISA_ERR_WORKSPACE"]
@@ -251,12 +256,12 @@ def test_attn_validation(lib, name):
 
 def call_bwd(lib, s=None, p=None, q=fake(1), k=fake(2), v=fake(3), o=fake(4), do=fake(5),
              st=None, idx=fake(30), wg=None, dq=fake(6), dk=fake(7), dv=fake(8), ws=fake(9),
-             wsb=1 << 31):
+             wsb=1 << 31, rs=None):
     s = s or shape()
     p = p or _lib.Params(4, 1, 0, 1, 0)
     st = st or stats()
     return lib.pisa_attn_bwd(ctypes.byref(s), ctypes.byref(p), q, k, v, o, do, ctypes.byref(st), idx, wg,
-                             dq, dk, dv, ws, wsb, None)
+                             rs, dq, dk, dv, ws, wsb, None)
 
 
 def test_bwd_workspace_bytes(lib):
@@ -287,6 +292,9 @@ def test_bwd_validation(lib):
     assert call_bwd(lib, dv=fake(5) + 2048) == E["PISA_ERR_PARAM"]          # dv overlaps dout
     assert call_bwd(lib, dq=fake(9) + (1 << 20)) == E["PISA_ERR_PARAM"]     # dq inside the workspace
     assert call_bwd(lib, p=_lib.Params(4, 1, 0, 1, 0, 99)) == E["PISA_ERR_PARAM"]      # sinks > N
+    assert call_bwd(lib, rs=MIS) == E["PISA_ERR_ALIGN"]                     # row statistics
+    assert call_bwd(lib, rs=fake(6) + 4096) == E["PISA_ERR_PARAM"]          # inside dq
+    assert call_bwd(lib, rs=fake(9) + 4096) == E["PISA_ERR_PARAM"]          # inside the workspace
 
 
 def test_null_structs(lib):
@@ -300,7 +308,7 @@ def test_null_structs(lib):
     assert lib.pisa_route_topk(ctypes.byref(s), ctypes.byref(p), None, OPS, OPSB, fake(30), None,
                                None) == E["PISA_ERR_NULL"]
     assert lib.pisa_attn_fwd(ctypes.byref(s), ctypes.byref(p), fake(1), fake(2), fake(3), None, OPS, OPSB,
-                             fake(30), None, fake(4), None) == E["PISA_ERR_NULL"]
+                             fake(30), None, fake(4), None, None) == E["PISA_ERR_NULL"]
     assert lib.pisa_prepare_operands(ctypes.byref(s), ctypes.byref(p), fake(2), None, OPS, OPSB,
                                      None) == E["PISA_ERR_NULL"]
 

@@ -17,7 +17,8 @@ Tolerances, per head and per gradient, on e = max|g - g_ref| / max|g_ref|:
   sharing a smooth field, two key dims scaled by 8) that ratio reaches ~10,
   hence the bound; the i.i.d. cases stay near 1e-6.
 * bf16, contract: e <= 4e-3: each gradient is rounded once to bf16 (at most
-  2^-9 of its magnitude), on top of the fp32 arithmetic above.
+  2^-8 of its magnitude: bf16 keeps 8 significant bits), on top of the fp32
+  arithmetic above.
 * bf16, end to end: e <= 2e-2. delta = dout . o uses o stored in bf16, and a
   delta error c_t moves dq_t by -c_t s E_P[k] (dk likewise; dv not at all),
   which the mean key of an attended set can make larger than dq_t itself
@@ -71,9 +72,11 @@ def oracle_output(w, host, ih, s, band, n_sink, so, fo):
     return to_device(o32, "f32"), o32.astype(np.float64)
 
 
-def check(w, seed, topk, band=1, n_sink=0, so=False, fo=True, idx_fn=None, valu_fwd=False, contract=False):
+def check(w, seed, topk, band=1, n_sink=0, so=False, fo=True, idx_fn=None, valu_fwd=False, contract=False,
+          row_stats=False):
     say(f"[gpu] bwd case: {w.name} T={w.seq_len} D={w.head_dim} {w.dtype} heads={w.heads} topk={topk} "
-        f"band={band} sinks={n_sink} so={so} fo={fo} seed={seed} contract={contract}")
+        f"band={band} sinks={n_sink} so={so} fo={fo} seed={seed} contract={contract} row_stats={row_stats}")
+    assert not (row_stats and contract), "the row statistics come from the GPU forward"
     (q, k, v, do), host = device_case(w, seed)
     s = 1.0 / math.sqrt(w.head_dim)
     st = P.pisa_block_stats(q, k, v, second_order=so)
@@ -84,11 +87,12 @@ def check(w, seed, topk, band=1, n_sink=0, so=False, fo=True, idx_fn=None, valu_
     o_used = None
     if contract:
         o, o_used = oracle_output(w, host, ih, s, band, n_sink, so, fo)
-    else:
+    rs = P.alloc_row_stats(q) if row_stats else None
+    if not contract:
         fwd = P.pisa_attn_fwd_valu if valu_fwd else P.pisa_attn_fwd
-        o = fwd(q, k, v, st, idx, wg, band=band, second_order=so, first_order=fo, n_sink=n_sink)
+        o = fwd(q, k, v, st, idx, wg, band=band, second_order=so, first_order=fo, n_sink=n_sink, row_stats=rs)
     dq, dk, dv = P.pisa_attn_bwd(q, k, v, o, do, st, idx, wg, band=band, second_order=so, first_order=fo,
-                                 n_sink=n_sink)
+                                 n_sink=n_sink, row_stats=rs)
     torch.cuda.synchronize()
     got = [t.double().cpu().numpy() for t in (dq, dk, dv)]
     worst = 0.0
@@ -130,6 +134,77 @@ def test_fp32_zeroth_order_second_order():
 def test_bf16_video(so, contract):
     w = wl("wan14", heads=2, grid=(3, 11, 31), seq_len=1023, outlier_key_dims=(0, 1))
     check(w, seed=4, topk=2, so=so, contract=contract)
+
+
+@pytest.mark.parametrize("so", [False, True])
+def test_bf16_video_with_forward_row_stats(so):
+    """End to end, the backward taking each row's lse and c from the forward
+    (pisa_attn_fwd's row_stats) instead of re-scoring the row's pairs."""
+    w = wl("wan14", heads=2, grid=(3, 11, 31), seq_len=1023, outlier_key_dims=(0, 1))
+    check(w, seed=4, topk=2, so=so, row_stats=True)
+
+
+def test_bf16_image_sinks_with_forward_row_stats():
+    w = wl("flux", heads=2, grid=(30, 32), seq_len=1472, text_tokens=512)
+    check(w, seed=12, topk=3, n_sink=8, so=True, row_stats=True)
+
+
+def test_fp32_with_forward_row_stats():
+    """fp32 inputs recompute the row statistics whether or not the forward's are passed."""
+    check(wl("tiny", seq_len=777, head_dim=128, heads=2), seed=2, topk=2, band=0, n_sink=1, so=True,
+          row_stats=True)
+
+
+@pytest.mark.parametrize("kernel", ["asm", "mfma_d64", "valu_bf16", "f32"])
+def test_forward_row_stats_match_oracle(kernel):
+    """pisa_attn_fwd's row_stats against the oracle's per-row sums: lse_t =
+    m_t + ln den_t and c_t = l_tail_t / (T den_t), on each forward kernel (the
+    persistent and the non-persistent matrix-core kernel, the vector kernel
+    on bf16 and on fp32 inputs), with sinks and the second order. The bf16
+    matrix-core kernels sum bf16-rounded weights (each within 2^-8 of the
+    exact one: bf16 keeps 8 significant bits), so den is within 2^-8
+    relative: lse within ln(1 + 2^-8) = 3.9e-3, 4.5e-3 with the fp32 sums.
+    They take l_tail as the row sum minus its value after the last exact
+    item, so the fraction l_tail / den (= T c) is within 2^-7 of itself plus
+    the fp32 rounding of the running sum, at most ~10^3 additions of 2^-24
+    each: 1e-4 absolute. The vector kernels sum in fp32 without a difference;
+    there the logits' own fp32 rounding decides: a 128-term dot product
+    within 128 * 2^-24 of its terms' magnitude (logits up to ~30 on these
+    inputs, two key dims scaled by 8), 2.5e-4 in lse and twice that,
+    relative, in the ratio l_tail / den."""
+    D = 64 if kernel == "mfma_d64" else 128
+    dtype = "f32" if kernel == "f32" else "bf16"
+    w = wl("wan14", heads=2, grid=(3, 11, 31), seq_len=1023, head_dim=D, dtype=dtype)
+    (q, k, v, do), host = device_case(w, 20)
+    st = P.pisa_block_stats(q, k, v, second_order=True)
+    idx, wg = P.pisa_route_topk(q, st, 3, band=1, second_order=True, n_sink=1)
+    want_kernel = {"asm": 1, "mfma_d64": 2, "valu_bf16": None, "f32": 0}[kernel]
+    if want_kernel is not None:
+        assert P.attn_fwd_plan(1, 2, w.seq_len, D, dtype, 3, 1, True, 1) == want_kernel
+    rs = P.alloc_row_stats(q)
+    fwd = P.pisa_attn_fwd_valu if kernel == "valu_bf16" else P.pisa_attn_fwd
+    o = fwd(q, k, v, st, idx, wg, band=1, second_order=True, n_sink=1, row_stats=rs)
+    o_plain = fwd(q, k, v, st, idx, wg, band=1, second_order=True, n_sink=1)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_plain)   # the extra output changes nothing else
+    got = rs.double().cpu().numpy()
+    ih = idx.cpu().numpy()
+    exact = kernel in ("asm", "mfma_d64")
+    tl, tc = (4.5e-3, 2.0 ** -7) if exact else (2.5e-4, 5e-4)
+    worst = [0.0, 0.0]
+    for h in range(2):
+        qh, kh, vh = (x[0, h] for x in host[:3])
+        _, parts = O.pisa_forward_head(qh, kh, vh, B=64, scale=1 / math.sqrt(D), topk=3, band=1, n_sink=1,
+                                       second_order=True, routing=ih[0, h], return_parts=True)
+        lse = parts["m"] + np.log(parts["den"])
+        c = parts["l_tail"] / (w.seq_len * parts["den"])
+        el = np.abs(got[0, h, :, 0] - lse).max()
+        frac_got, frac = w.seq_len * got[0, h, :, 1], w.seq_len * c   # l_tail / den
+        ec = np.abs(frac_got - frac)
+        worst = [max(worst[0], el), max(worst[1], float(ec.max()))]
+        assert el <= tl, (h, el)
+        assert bool(np.all(ec <= tc * frac + (1e-4 if exact else 0.0))), (h, float((ec - tc * frac).max()))
+    say(f"[gpu]   {kernel}: lse worst abs error {worst[0]:.2e}, l_tail/den worst abs error {worst[1]:.2e}")
 
 
 def test_fp32_video_contract():
@@ -212,7 +287,7 @@ def test_full_size(name, heads, dkdv_head):
     do not change), so sum_k dk = 0; shifting every value by one vector shifts
     every output by it (H does not change since sum (k - kbar) = 0 per
     block), so sum_k dv = sum_t dout_t. Both sums are compared within 2^-7 of
-    sum |.| (bf16 rounding of each term, 2^-9, with fp32 accumulation).
+    sum |.| (bf16 rounding of each term, 2^-8, with fp32 accumulation).
     At the Wan2.1-14B shape one head's dk and dv are also compared element
     by element on sampled KV blocks with the oracle's full-head gradient for
     the o the backward was handed (the contract bar): a KV block's gradient
@@ -237,6 +312,20 @@ def test_full_size(name, heads, dkdv_head):
     dq, dk, dv = P.pisa_attn_bwd(q, k, v, o, do, st, idx, wg, band=w.band, second_order=so)
     torch.cuda.synchronize()
     say("[gpu]   backward done")
+    # with the forward's row statistics: the same o, and gradients within
+    # the bf16 weights' 2^-8 (uniformly scaling a row's weights by 1 + e
+    # scales its terms of every gradient by 1 + e) plus the two gradients'
+    # own bf16 rounding (2^-8 each) of the recomputed ones: 3 * 2^-8
+    rs = P.alloc_row_stats(q)
+    o_rs = P.pisa_attn_fwd(q, k, v, st, idx, wg, band=w.band, second_order=so, row_stats=rs)
+    g_rs = P.pisa_attn_bwd(q, k, v, o_rs, do, st, idx, wg, band=w.band, second_order=so, row_stats=rs)
+    torch.cuda.synchronize()
+    assert torch.equal(o_rs, o)
+    for nm, a, b in zip(("dq", "dk", "dv"), g_rs, (dq, dk, dv)):
+        e = float((a.float() - b.float()).abs().max() / b.float().abs().max())
+        say(f"[gpu]   {nm} with the forward's row statistics vs recomputed: {e:.2e} of max")
+        assert e <= 3 * 2.0 ** -8, (nm, e)
+    del o_rs, g_rs, rs
     dkf, dvf, dof = dk.float(), dv.float(), do.float()
     for nm, lhs, ref, mag in (("dk", dkf.sum(2), torch.zeros_like(dkf[:, :, 0]), dkf.abs().sum(2)),
                               ("dv", dvf.sum(2), dof.sum(2), dvf.abs().sum(2))):
@@ -303,8 +392,9 @@ def test_bf16_two_batches_contract():
 @pytest.mark.parametrize("reorder", ["none", "morton"])
 def test_autograd_through_the_wrapper(reorder):
     """piecewise_sparse_attention is differentiable: its gradients equal
-    pisa_attn_bwd's on the same routing bit for bit (through the Morton
-    reorder, whose adjoint is the inverse reorder)."""
+    pisa_attn_bwd's on the same routing, given the forward's row statistics,
+    bit for bit (through the Morton reorder, whose adjoint is the inverse
+    reorder)."""
     w = wl("wan14", heads=2, grid=(3, 11, 31), seq_len=1023)
     (q, k, v, do), _ = device_case(w, 19)
     say(f"[gpu] autograd through piecewise_sparse_attention, reorder={reorder}")
@@ -325,8 +415,9 @@ def test_autograd_through_the_wrapper(reorder):
     topk = P.topk_for_density(0.25, N)
     st = P.pisa_block_stats(qq, kk, vv, second_order=True)
     idx, wg = P.pisa_route_topk(qq, st, topk, band=1, second_order=True, n_sink=1)
-    oo = P.pisa_attn_fwd(qq, kk, vv, st, idx, wg, second_order=True, n_sink=1)
-    grads = P.pisa_attn_bwd(qq, kk, vv, oo, dd, st, idx, wg, second_order=True, n_sink=1)
+    rs = P.alloc_row_stats(qq)
+    oo = P.pisa_attn_fwd(qq, kk, vv, st, idx, wg, second_order=True, n_sink=1, row_stats=rs)
+    grads = P.pisa_attn_bwd(qq, kk, vv, oo, dd, st, idx, wg, second_order=True, n_sink=1, row_stats=rs)
     if reorder == "morton":
         grads = [P.reorder_scatter(g, perm) for g in grads]
     torch.cuda.synchronize()

@@ -141,8 +141,9 @@ def test_cov_prior_through_the_operator():
     o.backward(do)
     st = P.pisa_block_stats(q, k, v, cov_bias=True)
     idx, _ = P.pisa_route_topk(q, st, topk, band=1, n_sink=8, cov_bias=True)
-    o2 = P.pisa_attn_fwd(q, k, v, st, idx, None, band=1, n_sink=8)
-    grads = P.pisa_attn_bwd(q, k, v, o2, do, st, idx, None, band=1, n_sink=8)
+    rs = P.alloc_row_stats(q)
+    o2 = P.pisa_attn_fwd(q, k, v, st, idx, None, band=1, n_sink=8, row_stats=rs)
+    grads = P.pisa_attn_bwd(q, k, v, o2, do, st, idx, None, band=1, n_sink=8, row_stats=rs)
     torch.cuda.synchronize()
     assert torch.equal(o, o2)
     for leaf, g in zip(leaves, grads):

@@ -402,60 +402,86 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 // Row statistics when the forward wrote each row's lse and c (pisa_attn_fwd's
 // row_stats): the exact and virtual pairs are not re-scored; only delta =
 // dout . o and beta = s dout . (q H) / T are formed, as above (beta by the
-// same hi + lo products of H with dout, summed over the two key halves).
+// same hi + lo products of H with dout, summed over the two key halves). A
+// workgroup takes kRsBlocks query blocks, so each wave loads its H operands
+// (its half of the head dims, hi and lo) once for all of them.
+constexpr int kRsBlocks = 8;
 template <int D>
-__global__ __launch_bounds__(kThreads) void bwd_rowstats_fwd_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void bwd_rowstats_fwd_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ o, const bf16_t* __restrict__ dout,
     const bf16_t* __restrict__ hh, const bf16_t* __restrict__ hl, const float* __restrict__ fwd_rstat,
-    f32x4_t* __restrict__ rowstat, int T, float scale, int first_order) {
+    f32x4_t* __restrict__ rowstat, int T, int N, float scale, int first_order) {
     using C = BC<D>;
+    constexpr int HX = C::DT / 2;
     __shared__ float sbp[2][32];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r32 = lane & 31, g = lane >> 5;
     const int kt = wave >> 1, qt = wave & 1;
     const int64_t bh = blockIdx.y;
-    const int i = blockIdx.x;
-    const int t = i * kBlock + qt * 32 + r32;
     const int64_t base = bh * (int64_t)T * D;
-    float bp = 0.f;
+    const int i0 = blockIdx.x * kRsBlocks, i1 = min(N, i0 + kRsBlocks);
+    bf16x8_t ha[HX][C::KS], la[HX][C::KS];   // A = H rows (hi, lo) of this wave's head-dim tiles
     if (first_order) {
-        uint4 oreg[C::KS];
-        rows_from_global<D>(oreg, dout + base, t, T, g);
-        f32x16_t hg[C::DT / 2];
-        hg_tiles<D>(hg, hh + bh * (int64_t)D * D, hl + bh * (int64_t)D * D,
-                    [&](int ks) { return as_bf16x8(oreg[ks]); }, kt * C::DT / 2, r32, g);
-        if (t < T) {
 #pragma unroll
-            for (int x = 0; x < C::DT / 2; ++x)
+        for (int x = 0; x < HX; ++x)
 #pragma unroll
-                for (int run = 0; run < 4; ++run) {
-                    const int d0 = (kt * C::DT / 2 + x) * 32 + 8 * run + 4 * g;
-                    const uint2 qq = *reinterpret_cast<const uint2*>(q + base + (int64_t)t * D + d0);
-                    bp += bf16_lo(qq.x) * hg[x][4 * run] + bf16_hi(qq.x) * hg[x][4 * run + 1] +
-                          bf16_lo(qq.y) * hg[x][4 * run + 2] + bf16_hi(qq.y) * hg[x][4 * run + 3];
-                }
-        }
-        bp += __shfl_xor(bp, 32);
+            for (int ks = 0; ks < C::KS; ++ks) {
+                const int64_t a = bh * (int64_t)D * D + (int64_t)((kt * HX + x) * 32 + r32) * D + 16 * ks + 8 * g;
+                ha[x][ks] = as_bf16x8(*reinterpret_cast<const uint4*>(hh + a));
+                la[x][ks] = as_bf16x8(*reinterpret_cast<const uint4*>(hl + a));
+            }
     }
-    if (kt == 1 && g == 0) sbp[qt][r32] = bp;
-    __syncthreads();
-    if (kt == 0 && t < T) {
-        float dl = 0.f;
+    for (int i = i0; i < i1; ++i) {
+        const int t = i * kBlock + qt * 32 + r32;
+        float bp = 0.f;
+        if (first_order) {
+            uint4 oreg[C::KS];
+            rows_from_global<D>(oreg, dout + base, t, T, g);
+            f32x16_t hg[HX];
 #pragma unroll
-        for (int c = 0; c < D / 16; ++c) {
-            const int d0 = (D / 2) * g + 8 * c;
-            const uint4 a = *reinterpret_cast<const uint4*>(dout + base + (int64_t)t * D + d0);
-            const uint4 b = *reinterpret_cast<const uint4*>(o + base + (int64_t)t * D + d0);
-            dl += bf16_lo(a.x) * bf16_lo(b.x) + bf16_hi(a.x) * bf16_hi(b.x) + bf16_lo(a.y) * bf16_lo(b.y) +
-                  bf16_hi(a.y) * bf16_hi(b.y) + bf16_lo(a.z) * bf16_lo(b.z) + bf16_hi(a.z) * bf16_hi(b.z) +
-                  bf16_lo(a.w) * bf16_lo(b.w) + bf16_hi(a.w) * bf16_hi(b.w);
+            for (int x = 0; x < HX; ++x) {
+                f32x16_t c = zero16();
+#pragma unroll
+                for (int ks = 0; ks < C::KS; ++ks) {
+                    c = mfma(ha[x][ks], as_bf16x8(oreg[ks]), c);
+                    c = mfma(la[x][ks], as_bf16x8(oreg[ks]), c);
+                }
+                hg[x] = c;
+            }
+            if (t < T) {
+#pragma unroll
+                for (int x = 0; x < HX; ++x)
+#pragma unroll
+                    for (int run = 0; run < 4; ++run) {
+                        const int d0 = (kt * HX + x) * 32 + 8 * run + 4 * g;
+                        const uint2 qq = *reinterpret_cast<const uint2*>(q + base + (int64_t)t * D + d0);
+                        bp += bf16_lo(qq.x) * hg[x][4 * run] + bf16_hi(qq.x) * hg[x][4 * run + 1] +
+                              bf16_lo(qq.y) * hg[x][4 * run + 2] + bf16_hi(qq.y) * hg[x][4 * run + 3];
+                    }
+            }
+            bp += __shfl_xor(bp, 32);
         }
-        dl += __shfl_xor(dl, 32);
-        if (g == 0) {
-            const float2 fr = *reinterpret_cast<const float2*>(fwd_rstat + 2 * (bh * (int64_t)T + t));
-            const float beta = first_order ? scale * (bp + sbp[qt][r32]) / (float)T : 0.f;
-            f32x4_t rs = {fr.x, dl, beta, first_order ? fr.y : 0.f};
-            rowstat[bh * (int64_t)T + t] = rs;
+        __syncthreads();   // the previous block's partial sums have been read
+        if (kt == 1 && g == 0) sbp[qt][r32] = bp;
+        __syncthreads();
+        if (kt == 0 && t < T) {
+            float dl = 0.f;
+#pragma unroll
+            for (int c = 0; c < D / 16; ++c) {
+                const int d0 = (D / 2) * g + 8 * c;
+                const uint4 a = *reinterpret_cast<const uint4*>(dout + base + (int64_t)t * D + d0);
+                const uint4 b = *reinterpret_cast<const uint4*>(o + base + (int64_t)t * D + d0);
+                dl += bf16_lo(a.x) * bf16_lo(b.x) + bf16_hi(a.x) * bf16_hi(b.x) + bf16_lo(a.y) * bf16_lo(b.y) +
+                      bf16_hi(a.y) * bf16_hi(b.y) + bf16_lo(a.z) * bf16_lo(b.z) + bf16_hi(a.z) * bf16_hi(b.z) +
+                      bf16_lo(a.w) * bf16_lo(b.w) + bf16_hi(a.w) * bf16_hi(b.w);
+            }
+            dl += __shfl_xor(dl, 32);
+            if (g == 0) {
+                const float2 fr = *reinterpret_cast<const float2*>(fwd_rstat + 2 * (bh * (int64_t)T + t));
+                const float beta = first_order ? scale * (bp + sbp[qt][r32]) / (float)T : 0.f;
+                f32x4_t rs = {fr.x, dl, beta, first_order ? fr.y : 0.f};
+                rowstat[bh * (int64_t)T + t] = rs;
+            }
         }
     }
 }
@@ -1156,13 +1182,13 @@ hipError_t launch_bwd_rowstats(const Geom& g, const bf16_t* q, const bf16_t* k, 
 hipError_t launch_bwd_rowstats_fwd(const Geom& g, const bf16_t* q, const bf16_t* o, const bf16_t* dout,
                                    const bf16_t* hh, const bf16_t* hl, const float* fwd_rstat, f32x4_t* rowstat,
                                    int first_order, hipStream_t stream) {
-    const dim3 grid(g.N, (unsigned)g.BH);
+    const dim3 grid((g.N + kRsBlocks - 1) / kRsBlocks, (unsigned)g.BH);
     if (g.D == 128)
         hipLaunchKernelGGL((bwd_rowstats_fwd_kernel<128>), grid, dim3(kThreads), 0, stream, q, o, dout, hh, hl,
-                           fwd_rstat, rowstat, g.T, g.scale, first_order);
+                           fwd_rstat, rowstat, g.T, g.N, g.scale, first_order);
     else
         hipLaunchKernelGGL((bwd_rowstats_fwd_kernel<64>), grid, dim3(kThreads), 0, stream, q, o, dout, hh, hl,
-                           fwd_rstat, rowstat, g.T, g.scale, first_order);
+                           fwd_rstat, rowstat, g.T, g.N, g.scale, first_order);
     return hipGetLastError();
 }
 

@@ -527,8 +527,8 @@ def main():
             "note": "with the forward's row statistics (lse, c); ms_recomputing_row_stats without them",
             "roofline": {"bound": "mfma" if w.dtype == "bf16" else "alu", "achieved": round(bwd_tflops, 2),
                          "peak": bpeak, "unit": "TFLOP/s", "frac": round(bwd_tflops / bpeak, 4), "traffic": None,
-                         "kernel": "pisa_attn_bwd (all its kernels: " + ("bf16 MFMA products and chain, "
-                                   "fp32 VALU mask and dH)" if w.dtype == "bf16" else "fp32 VALU)")}}
+                         "kernel": "pisa_attn_bwd (all its kernels: " + ("bf16 MFMA products, chain and dH; "
+                                   "integer selection mask)" if w.dtype == "bf16" else "fp32 VALU)")}}
 
     if args.copy_calibration:
         src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)

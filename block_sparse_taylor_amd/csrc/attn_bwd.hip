@@ -757,8 +757,13 @@ hipError_t run_bwd(const Geom& g, const pisa_params_t* p, const void* q, const v
     }
     if (fo) {
         const int rows_per = (g.T + L.P - 1) / L.P;
-        hipLaunchKernelGGL((bwd_dh_kernel<T, D>), dim3(L.P, BH), dim3(kThreads), 0, stream, tq, tg, rowstat,
-                           dhp, g.T, rows_per, g.scale);
+        if constexpr (kMfma) {
+            const hipError_t e = launch_bwd_dh_mfma(g, tq, tg, rowstat, dhp, L.P, stream);
+            if (e != hipSuccess) return e;
+        } else {
+            hipLaunchKernelGGL((bwd_dh_kernel<T, D>), dim3(L.P, BH), dim3(kThreads), 0, stream, tq, tg, rowstat,
+                               dhp, g.T, rows_per, g.scale);
+        }
         hipLaunchKernelGGL(bwd_dh_reduce_kernel, dim3((D * D + kThreads - 1) / kThreads, BH), dim3(kThreads),
                            0, stream, dhp, dh, dht, L.P, D);
     }

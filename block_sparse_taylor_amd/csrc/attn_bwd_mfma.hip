@@ -486,6 +486,79 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     }
 }
 
+// ---------------------------------------------------------------- dH
+// dH = sum_t (c_t s q_t)^T dout_t over one range of rows (a partial sum; the
+// ranges are added in a fixed order afterwards), on the matrix cores: the Q
+// and dO tiles are staged in LDS and read transposed, which gives both
+// operands the same rows in the same k-slots; A = Q^T (exact in bf16), B =
+// dO^T with each row scaled by c_t s, split into bf16 hi + lo (two products).
+template <int D>
+__global__ __launch_bounds__(kThreads) void bwd_dh_mfma_kernel(const bf16_t* __restrict__ q,
+                                                               const bf16_t* __restrict__ dout,
+                                                               const f32x4_t* __restrict__ rowstat,
+                                                               float* __restrict__ part, int T, int rows_per,
+                                                               float scale) {
+    using C = BC<D>;
+    constexpr int TPW = C::DT * C::DT / 4;   // 32 x 32 output tiles per wave
+    __shared__ __attribute__((aligned(16))) unsigned char sq[C::TILE];
+    __shared__ __attribute__((aligned(16))) unsigned char so[C::TILE];
+    __shared__ float sc[64];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r32 = lane & 31, g = lane >> 5;
+    const int64_t bh = blockIdx.y;
+    const int64_t base = bh * (int64_t)T * D;
+    const int t0 = blockIdx.x * rows_per, t1 = min(T, t0 + rows_per);
+    const TrAddr ta(lane, C::RB, C::SWM);
+    f32x16_t acc[TPW];
+#pragma unroll
+    for (int x = 0; x < TPW; ++x) acc[x] = zero16();
+    for (int ts = t0; ts < t1; ts += kBlock) {
+        const int nh = min(kBlock, t1 - ts);
+        uint4 qr[C::LPT], orr[C::LPT];
+        tile_load<D>(qr, q + base + (int64_t)ts * D, nh, tid);
+        tile_load<D>(orr, dout + base + (int64_t)ts * D, nh, tid);
+        const float cst = tid < nh ? rowstat[bh * (int64_t)T + ts + tid][3] * scale : 0.f;
+        __syncthreads();   // the previous tiles have been read
+        tile_store<D>(sq, qr, tid);
+        tile_store<D>(so, orr, tid);
+        if (tid < kBlock) sc[tid] = cst;
+        __syncthreads();
+#pragma unroll
+        for (int r0 = 0; r0 < kBlock; r0 += 16) {
+            float cs[8];   // k-slots 0..3: rows r0 + 4g + e; 4..7: rows r0 + 8 + 4g + e
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                cs[e] = sc[r0 + 4 * g + e];
+                cs[4 + e] = sc[r0 + 8 + 4 * g + e];
+            }
+#pragma unroll
+            for (int x = 0; x < TPW; ++x) {
+                const int u = wave * TPW + x, da = u / C::DT, db = u % C::DT;
+                const bf16x8_t a = tr_op<D>(sq, ta, da, r0);
+                const uint4 bw = __builtin_bit_cast(uint4, tr_op<D>(so, ta, db, r0));
+                const uint32_t w[4] = {bw.x, bw.y, bw.z, bw.w};
+                f32x16_t bs;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    bs[2 * e] = bf16_lo(w[e]) * cs[2 * e];
+                    bs[2 * e + 1] = bf16_hi(w[e]) * cs[2 * e + 1];
+                }
+                bf16x8_t bhi, blo;
+                split_op(bs, 0, bhi, blo);
+                acc[x] = mfma(a, bhi, acc[x]);
+                acc[x] = mfma(a, blo, acc[x]);
+            }
+        }
+    }
+    float* out = part + (bh * gridDim.x + blockIdx.x) * (int64_t)D * D;
+#pragma unroll
+    for (int x = 0; x < TPW; ++x) {
+        const int u = wave * TPW + x, da = u / C::DT, db = u % C::DT;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) out[(da * 32 + acc_row(i, g)) * D + db * 32 + r32] = acc[x][i];
+    }
+}
+
 // ---------------------------------------------------------------- dq
 // dq' = K^T dS^T (exact keys) + kbar^T dlam^T (virtual tokens, kbar hi + lo)
 // + c H g, then dq = s dq' + 2 s^2 q dq2bar_i / n_i (second order).
@@ -1189,6 +1262,19 @@ hipError_t launch_bwd_rowstats_fwd(const Geom& g, const bf16_t* q, const bf16_t*
     else
         hipLaunchKernelGGL((bwd_rowstats_fwd_kernel<64>), grid, dim3(kThreads), 0, stream, q, o, dout, hh, hl,
                            fwd_rstat, rowstat, g.T, g.N, g.scale, first_order);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_dh_mfma(const Geom& g, const bf16_t* q, const bf16_t* dout, const f32x4_t* rowstat,
+                              float* part, int parts, hipStream_t stream) {
+    const int rows_per = (g.T + parts - 1) / parts;
+    const dim3 grid((unsigned)parts, (unsigned)g.BH);
+    if (g.D == 128)
+        hipLaunchKernelGGL((bwd_dh_mfma_kernel<128>), grid, dim3(kThreads), 0, stream, q, dout, rowstat, part, g.T,
+                           rows_per, g.scale);
+    else
+        hipLaunchKernelGGL((bwd_dh_mfma_kernel<64>), grid, dim3(kThreads), 0, stream, q, dout, rowstat, part, g.T,
+                           rows_per, g.scale);
     return hipGetLastError();
 }
 

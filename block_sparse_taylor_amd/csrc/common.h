@@ -155,6 +155,9 @@ hipError_t launch_bwd_rowstats(const Geom& g, const bf16_t* q, const bf16_t* k, 
 hipError_t launch_bwd_rowstats_fwd(const Geom& g, const bf16_t* q, const bf16_t* o, const bf16_t* dout,
                                    const bf16_t* hh, const bf16_t* hl, const float* fwd_rstat, f32x4_t* rowstat,
                                    int first_order, hipStream_t stream);
+// dH partial sums over `parts` row ranges on the matrix cores (bf16 inputs).
+hipError_t launch_bwd_dh_mfma(const Geom& g, const bf16_t* q, const bf16_t* dout, const f32x4_t* rowstat,
+                              float* part, int parts, hipStream_t stream);
 hipError_t launch_bwd_dq(const Geom& g, const bf16_t* q, const bf16_t* k, const bf16_t* v, const bf16_t* dout,
                          const bf16_t* kbh, const bf16_t* kbl, const bf16_t* vhh, const bf16_t* vhl,
                          const bf16_t* hh, const bf16_t* hl, const uint32_t* mask, const float* wgate,

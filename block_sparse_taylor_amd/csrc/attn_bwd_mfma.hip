@@ -1095,15 +1095,18 @@ __global__ __launch_bounds__(kThreads) void bwd_virt_mfma_kernel(
         const float wg = (second_order && use) ? wgate[(bh * N + i) * (int64_t)N + j] : 0.f;
         const int rows = min(kBlock, T - i * kBlock);
         uint4 qr[C::LPT], orr[C::LPT];
-        tile_load<D>(qr, q + base + (int64_t)i * kBlock * D, rows, tid);
-        tile_load<D>(orr, dout + base + (int64_t)i * kBlock * D, rows, tid);
-        float ls = INFINITY, dl = 0.f, bt = 0.f;
-        if (tid < rows) {
-            const f32x4_t rs = rowstat[bh * (int64_t)T + (int64_t)i * kBlock + tid];
-            ls = rs[0] * kLog2e;
-            dl = rs[1];
-            bt = rs[2];
+        const __amdgpu_buffer_rsrc_t rq = brsrc(q + base + (int64_t)i * kBlock * D, (uint32_t)(rows * C::RB));
+        const __amdgpu_buffer_rsrc_t ro = brsrc(dout + base + (int64_t)i * kBlock * D, (uint32_t)(rows * C::RB));
+#pragma unroll
+        for (int m = 0; m < C::LPT; ++m) {
+            const int o_ = 16 * (tid + kThreads * m);
+            qr[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, o_, 0, 0));
+            orr[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ro, o_, 0, 0));
         }
+        const f32x4_t rs = rowstat[bh * (int64_t)T + (int64_t)i * kBlock + min(tid & 63, rows - 1)];
+        const bool in = (tid & 63) < rows;
+        const float ls = in ? rs[0] * kLog2e : INFINITY;
+        const float dl = in ? rs[1] : 0.f, bt = in ? rs[2] : 0.f;
         __syncthreads();
         tile_store<D>(sQ, qr, tid);
         tile_store<D>(sO, orr, tid);

@@ -72,6 +72,10 @@ WORKLOADS = {
                         grid=(33, 45, 80)),
     "flux": Workload("flux", 1, 24, 4608, 128, "bf16", 0.15, 1, False, 4, "image",
                      grid=(64, 64), text_tokens=512),
+    # one GPU's share of the Wan2.1-14B shape with its 40 heads sharded over 8
+    # GPUs: heads 0..4 of the same inputs (the streams are per (seed, batch, head))
+    "wan14_shard8": Workload("wan14_shard8", 1, 5, 32760, 128, "bf16", 0.125, 1, False, 2, "video",
+                             grid=(21, 30, 52), outlier_key_dims=(0, 1)),
     "wan14_kv": Workload("wan14_kv", 1, 8, 32760, 128, "bf16", 0.125, 1, False, 5, "video",
                          grid=(21, 30, 52), outlier_key_dims=(0, 1), v_from_key_noise=True),
 }

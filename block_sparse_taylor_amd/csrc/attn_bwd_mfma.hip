@@ -46,8 +46,22 @@ struct BC {
     static constexpr int RB = 2 * D;           // row bytes
     static constexpr int TILE = 64 * RB;       // bytes of one 64-row tile
     static constexpr int LPT = 64 * CH / kThreads;   // 16-byte loads per thread per tile
-    static constexpr int SWM = CH / 2 - 1;           // swizzle: chunk c of row r sits at c ^ 2 (r & SWM)
+    static constexpr int SWM = CH / 2 - 1;           // low row bits of the swizzle (below)
 };
+
+// Chunk c of row r of a staged tile sits at 16-byte position c ^ swz(r). For
+// D = 128 (16 chunks per row), swz(r) = 2 (r & 7) | ((r >> 3) & 1): the 16
+// consecutive rows that one row-format read serves (16 lanes at a time, one
+// chunk each) land on 16 distinct positions, and a transposed read, which
+// covers 8 rows starting at a multiple of 8, sees bit 0 constant, so its
+// lanes keep the distinct positions of 2 (r & 7). (Measured on gfx950 with a
+// standalone pattern benchmark: 2 (r & 7) alone costs row reads a two-way
+// bank conflict; r & 15 makes the transposed reads conflict.) D = 64 keeps
+// swz(r) = 2 (r & 3).
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+    return D == 128 ? ((2 * (r & 7)) | ((r >> 3) & 1)) : 2 * (r & BC<D>::SWM);
+}
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
 
@@ -80,9 +94,7 @@ __device__ __forceinline__ f32x16_t zero16() {
 }
 
 // A 64-row tile (rows >= nval zero) from global memory into registers, then
-// into LDS with chunk c of row r at 16-byte position c ^ 2 (r & SWM): eight
-// consecutive rows (D = 128; four for D = 64) put a chunk in distinct banks,
-// so the row-format reads of 8 lanes do not collide.
+// into LDS with chunk c of row r at 16-byte position c ^ swz(r).
 template <int D>
 __device__ __forceinline__ void tile_load(uint4 (&r)[BC<D>::LPT], const bf16_t* src, int nval, int tid) {
 #pragma unroll
@@ -99,14 +111,14 @@ __device__ __forceinline__ void tile_store(unsigned char* lds, const uint4 (&r)[
     for (int n = 0; n < BC<D>::LPT; ++n) {
         const int c = tid + kThreads * n;
         const int row = c / BC<D>::CH, ch = c % BC<D>::CH;
-        *reinterpret_cast<uint4*>(lds + row * BC<D>::RB + 16 * (ch ^ (2 * (row & BC<D>::SWM)))) = r[n];
+        *reinterpret_cast<uint4*>(lds + row * BC<D>::RB + 16 * (ch ^ swz<D>(row))) = r[n];
     }
 }
 
 // Row-format operand: row rr of a swizzled tile, head dims 16 ks + 8 g + (0..7).
 template <int D>
 __device__ __forceinline__ bf16x8_t row_op(const unsigned char* lds, int rr, int ks, int g) {
-    return as_bf16x8(*reinterpret_cast<const uint4*>(lds + rr * BC<D>::RB + 16 * ((2 * ks + g) ^ (2 * (rr & BC<D>::SWM)))));
+    return as_bf16x8(*reinterpret_cast<const uint4*>(lds + rr * BC<D>::RB + 16 * ((2 * ks + g) ^ swz<D>(rr))));
 }
 
 // Row-format operand straight from global memory (row t of a [T, D] matrix; zero past T).
@@ -120,7 +132,9 @@ __device__ __forceinline__ void rows_from_global(uint4 (&r)[BC<D>::KS], const bf
 // Transposed-read addressing (lane-constant part) of a swizzled tile: the
 // A operand "rows = head dims of tile dt, k = tile rows r0 + 4g + (0..3) and
 // r0 + 8 + 4g + (0..3)". A lane reads row R = r0 (+ 8) + 4g + tre with r0 a
-// multiple of 8, so R & SWM = (4g + tre) & SWM does not depend on r0.
+// multiple of 8, so R & SWM = (4g + tre) & SWM does not depend on r0; the
+// remaining swizzle bit of D = 128, (R >> 3) & 1, is that of r0 (and of r0 +
+// 8 for the second read) and enters as 16 bytes in tr_op.
 struct TrAddr {
     uint32_t trow;
     int trG, tra, sw;
@@ -140,9 +154,11 @@ struct TrAddr {
 
 template <int D>
 __device__ __forceinline__ bf16x8_t tr_op(const unsigned char* lds, const TrAddr& ta, int dt, int r0) {
-    const unsigned char* base = lds + ta.trow + ta.off(dt);
-    const uint2 a = lds_tr16(base + r0 * BC<D>::RB);
-    const uint2 b = lds_tr16(base + (r0 + 8) * BC<D>::RB);
+    const uint32_t o = ta.off(dt);
+    const uint32_t oa = D == 128 ? o ^ (uint32_t)(16 * ((r0 >> 3) & 1)) : o;
+    const uint32_t ob = D == 128 ? o ^ (uint32_t)(16 * (((r0 + 8) >> 3) & 1)) : o;
+    const uint2 a = lds_tr16(lds + ta.trow + oa + r0 * BC<D>::RB);
+    const uint2 b = lds_tr16(lds + ta.trow + ob + (r0 + 8) * BC<D>::RB);
     return as_bf16x8(make_uint4(a.x, a.y, b.x, b.y));
 }
 
@@ -981,7 +997,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                 // dV^T += dH^T (K - kbar)^T: A = dH^T rows, B = (k - kbar) of the block, hi + lo
                 split8(dHTh + (int64_t)row * D + c0, ah, al);
                 const uint4 kb = *reinterpret_cast<const uint4*>(sKt + (kt * 32 + r32) * C::RB +
-                                                                   16 * ((2 * ks + g) ^ (2 * ((kt * 32 + r32) & C::SWM))));
+                                                                   16 * ((2 * ks + g) ^ swz<D>(kt * 32 + r32)));
                 f32x16_t kc = zero16();
                 const uint32_t kw[4] = {kb.x, kb.y, kb.z, kb.w};
 #pragma unroll
@@ -1001,14 +1017,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         const int nj = min(kBlock, T - j * kBlock);
         const float inv_n = 1.f / (float)nj;
         const unsigned char* krow = sKt + (kt * 32 + r32) * C::RB;
-        const int sw = (kt * 32 + r32) & C::SWM;
+        const int sw = swz<D>(kt * 32 + r32);
 #pragma unroll
         for (int x = 0; x < HT; ++x)
 #pragma unroll
             for (int run = 0; run < 4; ++run) {
                 const int d0 = (qt * HT + x) * 32 + 8 * run + 4 * g;
                 // k of this key at dims d0 .. d0 + 3 (one 8-byte piece of its chunk)
-                const uint2 kk = *reinterpret_cast<const uint2*>(krow + 16 * ((d0 >> 3) ^ (2 * sw)) + 2 * (d0 & 7));
+                const uint2 kk = *reinterpret_cast<const uint2*>(krow + 16 * ((d0 >> 3) ^ sw) + 2 * (d0 & 7));
                 const float kv[4] = {bf16_lo(kk.x), bf16_hi(kk.x), bf16_lo(kk.y), bf16_hi(kk.y)};
                 float gk[4], gv[4];
 #pragma unroll

@@ -26,6 +26,8 @@
 // and the two waves sharing an output tile add their partials at the end.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace pisa {
@@ -218,6 +220,33 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t brsrc(const void* base, uint32
     const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
     void* p = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
     return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
+// 16 bytes per lane from a buffer straight into LDS: lane l writes the
+// wave-uniform LDS address + 16 l. The host pass of this compiler drops any
+// kernel whose body names this builtin, so only the device pass sees it.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, (int)voff, 0, 0, 0);
+#endif
+}
+
+// A 64-row tile into LDS by buffer->LDS DMA, in the staged layout (chunk c of
+// row r at 16-byte position c ^ swz(r)): 1 KB instruction n fills LDS bytes
+// [1024 n, 1024 n + 1024), i.e. rows RPI n .. RPI n + RPI - 1, so lane l,
+// landing on row RPI n + l / CH at position l % CH, loads that row's chunk
+// (l % CH) ^ swz(row). Each of the 4 waves issues a quarter of the
+// instructions; rows past the descriptor's range read zero.
+template <int D>
+__device__ __forceinline__ void tile_dma(unsigned char* lds, __amdgpu_buffer_rsrc_t r, int wave, int lane) {
+    constexpr int NI = BC<D>::TILE / 1024, RPI = 1024 / BC<D>::RB;
+    static_assert(NI % 4 == 0 && kThreads == 256, "four waves share a tile's DMA instructions");
+#pragma unroll
+    for (int m = 0; m < NI / 4; ++m) {
+        const int n = wave * (NI / 4) + m;
+        const int row = RPI * n + lane / BC<D>::CH, pos = lane % BC<D>::CH;
+        dma16(r, lds + 1024 * n, (uint32_t)(row * BC<D>::RB + 16 * (pos ^ swz<D>(row))));
+    }
 }
 
 struct VirtRow {
@@ -1060,16 +1089,23 @@ __global__ __launch_bounds__(kThreads) void bwd_virt_mfma_kernel(
     const float* __restrict__ wgate, float* __restrict__ dkb_part, float* __restrict__ dvh_part,
     float* __restrict__ dw, int T, int N, int NW, float scale, int second_order, int i_per_split) {
     using C = BC<D>;
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * C::TILE];   // Q, dO tiles; then the exchange
-    __shared__ float slse[64], sdel[64], sbet[64];
+    // The Q and dO tiles and the row statistics of two consecutive query
+    // blocks live in separate arrays: those of block i + 1 arrive by
+    // buffer->LDS DMA while block i is computed (separate arrays, so that the
+    // compiler can tell the DMA into one from the reads of the other). The
+    // partial exchange at the end reuses tqo0.
+    __shared__ __attribute__((aligned(16))) unsigned char tqo0[2 * C::TILE];
+    __shared__ __attribute__((aligned(16))) unsigned char tqo1[2 * C::TILE];
+    __shared__ __attribute__((aligned(16))) f32x4_t trs0[64];
+    __shared__ __attribute__((aligned(16))) f32x4_t trs1[64];
     __shared__ float sdw[2][64];
-    unsigned char* sQ = smem;
-    unsigned char* sO = smem + C::TILE;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r32 = lane & 31, g = lane >> 5;
     const int kt = wave >> 1, qt = wave & 1;
     const int64_t bh = blockIdx.y;
-    const int j = blockIdx.x * 64 + kt * 32 + r32;
+    const int g0 = blockIdx.x * 64;   // the group's first block
+    const int j = g0 + kt * 32 + r32;
     const bool jvalid = j < N;
     const int jc = jvalid ? j : N - 1;
     const float nj = (float)min(kBlock, T - jc * kBlock);
@@ -1077,6 +1113,17 @@ __global__ __launch_bounds__(kThreads) void bwd_virt_mfma_kernel(
     const float c2 = scale * kLog2e;
     const TrAddr ta(lane, C::RB, C::SWM);
     const int i0 = blockIdx.z * i_per_split, i1 = min(N, i0 + i_per_split);
+    const int nvg = min(64, N - g0);
+    const uint64_t gvalid = nvg == 64 ? ~0ull : (1ull << nvg) - 1ull;   // the group's blocks below N
+
+    auto dma_block = [&](int i, unsigned char* tqo, f32x4_t* trs) {
+        const int rows = min(kBlock, T - i * kBlock);
+        tile_dma<D>(tqo, brsrc(q + base + (int64_t)i * kBlock * D, (uint32_t)(rows * C::RB)), wave, lane);
+        tile_dma<D>(tqo + C::TILE, brsrc(dout + base + (int64_t)i * kBlock * D, (uint32_t)(rows * C::RB)), wave, lane);
+        if (wave == 0)   // (lse, delta, beta) of the block's rows; rows past T read zero
+            dma16(brsrc(rowstat + bh * (int64_t)T + (int64_t)i * kBlock, (uint32_t)(rows * 16)), trs,
+                  (uint32_t)(16 * lane));
+    };
 
     // this lane's block as hi + lo bf16 operands (rows of kbar and V-hat, dims 16 ks + 8 g ..)
     uint4 kh[C::KS], kl[C::KS], vh[C::KS], vl[C::KS];
@@ -1101,37 +1148,33 @@ __global__ __launch_bounds__(kThreads) void bwd_virt_mfma_kernel(
     f32x16_t dka[C::DT], dva[C::DT];
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) dka[dt] = dva[dt] = zero16();
+    if (i0 < i1) dma_block(i0, tqo0, trs0);
 
-    for (int i = i0; i < i1; ++i) {
-        const bool use = jvalid && !((mask[(bh * N + i) * (int64_t)NW + (jc >> 5)] >> (jc & 31)) & 1u);
-        if (!__syncthreads_or(use)) {   // every block of the group exact for i: no virtual pair
-            if (second_order && qt == 0 && g == 0 && jvalid) dw[(bh * N + i) * (int64_t)N + j] = 0.f;
-            continue;
-        }
+    // query block i, its tiles in the arrays of parity PAR
+    auto body = [&](auto par, int i) {
+        constexpr int PAR = decltype(par)::value;
+        unsigned char* sQ = PAR == 0 ? tqo0 : tqo1;
+        unsigned char* sO = sQ + C::TILE;
+        const f32x4_t* srs = PAR == 0 ? trs0 : trs1;
+        // selection bits of the group's 64 blocks for query block i (scalar loads)
+        const uint32_t* mrow = mask + (bh * N + i) * (int64_t)NW;
+        const int wi = g0 >> 5;
+        const uint64_t sel = (uint64_t)mrow[wi] | ((uint64_t)(wi + 1 < NW ? mrow[wi + 1] : 0u) << 32);
+        const bool use = jvalid && !((sel >> (j - g0)) & 1ull);
+        const bool any = (~sel & gvalid) != 0ull;   // uniform: some block of the group is virtual for i
         const float wg = (second_order && use) ? wgate[(bh * N + i) * (int64_t)N + j] : 0.f;
+        float bias = wg * kLog2e;
+        // this wave's DMAs of block i have landed; after the barrier every
+        // wave's have, and every wave is done with the other parity's arrays.
+        // (bias is an operand, so that its load is waited for here and not
+        // after the next block's DMA, which a later wait would include.)
+        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" : "+v"(bias) : : "memory");
+        if (i + 1 < i1) dma_block(i + 1, PAR == 0 ? tqo1 : tqo0, PAR == 0 ? trs1 : trs0);
+        if (!any) {   // every block of the group exact for i: no virtual pair
+            if (second_order && qt == 0 && g == 0 && jvalid) dw[(bh * N + i) * (int64_t)N + j] = 0.f;
+            return;
+        }
         const int rows = min(kBlock, T - i * kBlock);
-        uint4 qr[C::LPT], orr[C::LPT];
-        const __amdgpu_buffer_rsrc_t rq = brsrc(q + base + (int64_t)i * kBlock * D, (uint32_t)(rows * C::RB));
-        const __amdgpu_buffer_rsrc_t ro = brsrc(dout + base + (int64_t)i * kBlock * D, (uint32_t)(rows * C::RB));
-#pragma unroll
-        for (int m = 0; m < C::LPT; ++m) {
-            const int o_ = 16 * (tid + kThreads * m);
-            qr[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, o_, 0, 0));
-            orr[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ro, o_, 0, 0));
-        }
-        const f32x4_t rs = rowstat[bh * (int64_t)T + (int64_t)i * kBlock + min(tid & 63, rows - 1)];
-        const bool in = (tid & 63) < rows;
-        const float ls = in ? rs[0] * kLog2e : INFINITY;
-        const float dl = in ? rs[1] : 0.f, bt = in ? rs[2] : 0.f;
-        __syncthreads();
-        tile_store<D>(sQ, qr, tid);
-        tile_store<D>(sO, orr, tid);
-        if (tid < 64) {
-            slse[tid] = ls;
-            sdel[tid] = dl;
-            sbet[tid] = bt;
-        }
-        __syncthreads();
         f32x16_t s = zero16(), gv = zero16();
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
@@ -1142,14 +1185,14 @@ __global__ __launch_bounds__(kThreads) void bwd_virt_mfma_kernel(
             gv = mfma(ao, as_bf16x8(vh[ks]), gv);
             gv = mfma(ao, as_bf16x8(vl[ks]), gv);
         }
-        const float bias = wg * kLog2e;
         f32x16_t a;
         float dws = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int qq = qt * 32 + acc_row(r, g);
-            a[r] = use ? fexp2(fmaf(s[r], c2, bias - slse[qq])) : 0.f;   // rows past T: lse = +inf
-            s[r] = a[r] * (gv[r] + nj * (sbet[qq] - sdel[qq]));          // dlam
+            const f32x4_t rs = srs[qq];   // (lse, delta, beta)
+            a[r] = (use && qq < rows) ? fexp2(fmaf(s[r], c2, bias - rs[0] * kLog2e)) : 0.f;
+            s[r] = a[r] * (gv[r] + nj * (rs[2] - rs[1]));   // dlam
             dws += s[r];
         }
         if (second_order) {   // dW_ij: this lane's 16 rows, the other lane half, the other query half
@@ -1173,13 +1216,18 @@ __global__ __launch_bounds__(kThreads) void bwd_virt_mfma_kernel(
             }
         }
         if (second_order) {
-            __syncthreads();
+            // LDS writes done, then the barrier (no wait for the DMA in flight)
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
             if (qt == 0 && g == 0 && jvalid)
                 dw[(bh * N + i) * (int64_t)N + j] = wg != 0.f ? dws + sdw[kt][r32] : 0.f;
         }
+    };
+    for (int i = i0; i < i1; i += 2) {
+        body(std::integral_constant<int, 0>(), i);
+        if (i + 1 < i1) body(std::integral_constant<int, 1>(), i + 1);
     }
     // the two query halves of each block tile: wave (kt, 1) hands its partials to wave (kt, 0)
-    float* xs = reinterpret_cast<float*>(smem);
+    float* xs = reinterpret_cast<float*>(tqo0);
     const int64_t pbase = ((int64_t)blockIdx.z * gridDim.y + bh) * N * (int64_t)D;
 #pragma unroll
     for (int pass = 0; pass < 2; ++pass) {

@@ -19,13 +19,16 @@ pack into P, bf16 dot2 row sums; the writes of P group g precede the PV MFMAs
 that read it), the K loads of item n+2 (each after the last QK MFMA that reads
 the AGPRs it overwrites), the V DMA of item n+1 into the other LDS tile, and
 after the last QK MFMA the tail mask, row max and reference update of
-S^T(n+1). The last item runs its softmax and PV alone. The softmax keeps a
+S^T(n+1). The last item runs its softmax and PV alone, with the loads of
+the first-order term's H operand (into the K registers) issued before them;
+after it, G^T = H^T Q^T (32 MFMAs, H split hi + lo) accumulates into two
+operand tiles the caller combines with the merged state. The softmax keeps a
 fixed reference (a row's first finite tile max), tracks the running maximum
 and flags a tile more than 64 (log2 units) above the reference; the caller
 reruns with the exact maxima in that case.
 
 Register plan (explicitly named, declared clobbered): a128-a191 K of the
-next item (kreg[kt][ks]); v56-v119 / v120-v183 the S^T buffers of two
+next item (kreg[kt][ks]), H during the last item; v56-v119 / v120-v183 the S^T buffers of two
 consecutive items; v184-v215 P; v216-v231 Q^T operand buffers; v232-v243
 transposed-V operand buffers; v244-v255 scratch (v244:v245 the pending
 item-list entry); s70-s90 loop state, buffer descriptors, offsets and the
@@ -66,6 +69,7 @@ KBA, QBA = 192, 200                       # AGPRs: bias operands of the virtual-
 SOFF = {0: "0", 4096: f"s{S_C1}", 8192: f"s{S_C2}", 12288: f"s{S_C3}"}
 def SR(a, n=4): return f"s[{a}:{a+n-1}]"
 ACC = [f"%[a{i}]" for i in range(8)]      # acc[dt][qt] -> a{2 dt + qt}
+GACC = ["%[g0]", "%[g1]"]                 # G^T accumulators of the two query tiles
 MINF = "0xff800000"
 GROUPS = [(kt, h) for kt in range(2) for h in range(2)]
 TR = {0: ["%[tr0_0]", "%[tr0_1]", "%[tr0_2]", "%[tr0_3]"],
@@ -484,10 +488,50 @@ def snapshot():
     emit(f"{skip}:")
 
 
+def hload_lines():
+    """the H^T operand of G^T = H^T Q^T for this wave's 32 output dims (the
+    packed H: 16 contiguous 1 KB runs, k-step ks hi at run 2 ks, lo at run
+    2 ks + 1) into the K AGPRs, which no later item needs; skipped without
+    the first-order term."""
+    skip = label("noh")
+    out = ["s_cmp_eq_u32 %[hf], 0", f"s_cbranch_scc1 {skip}",
+           f"s_mov_b32 s{S_KRS}, %[hb_lo]", f"s_mov_b32 s{S_KRS + 1}, %[hb_hi]",
+           f"s_movk_i32 s{S_KRS + 2}, {16 * 1024}", f"s_mov_b32 s{S_KRS + 3}, 0x00020000"]
+    for u in range(2 * KS):
+        off = 1024 * u
+        out.append(f"buffer_load_dwordx4 a[{KA + 4 * u}:{KA + 4 * u + 3}], %[koff], {SR(S_KRS)}, "
+                   f"{SOFF[off & ~4095]} offen offset:{off & 4095}")
+    out.append(f"{skip}:")
+    return out
+
+
+def g_ops():
+    """G^T += H^T Q^T for both query tiles: 32 MFMAs (A = H hi or lo from the
+    AGPRs, B = the Q^T operand read from LDS as in QK) and their 16 Q reads."""
+    mf, lds, idx = [], [], {}
+    for ks in range(KS):
+        for part in range(2):
+            for qt in range(2):
+                u = 2 * ks + part
+                idx[(qt, ks, part)] = len(mf)
+                mf.append(Op("mfma", [f"v_mfma_f32_32x32x16_bf16 {GACC[qt]}, a[{KA + 4 * u}:{KA + 4 * u + 3}], "
+                                      f"{qbuf((ks % 2) * 2 + qt)}, {GACC[qt]}"], needs=[("q", qt, ks)]))
+    for ks in range(KS):
+        for qt in range(2):
+            after = max(idx[(qt, ks - 2, part)] for part in range(2)) if ks >= 2 else -1
+            lds.append(Op("lds", [f"ds_read_b128 {qbuf((ks % 2) * 2 + qt)}, %[qa] offset:{(qt * 32 * QP) * 2 + 32 * ks}"],
+                          lds_id=("q", qt, ks), after=after))
+    return mf, lds
+
+
 def tail(par):
-    """the last item: softmax of S^T(par), PV from tile par."""
+    """the last item: softmax of S^T(par), PV from tile par (the H loads of
+    the first-order term go out first, so their latency hides behind both)."""
     emit(f"; ---- last item, parity {par}")
     emit("s_waitcnt vmcnt(0) lgkmcnt(0)")
+    if WITH_G[0]:
+        for ln in hload_lines():
+            emit(ln)
     for o in softmax_ops(par, 0):
         for ln in o.lines:
             emit(ln)
@@ -498,16 +542,17 @@ def tail(par):
 
 
 def program():
-    done, tail0, tail1, loop = label("done"), label("tail0"), label("tail1"), label("loop")
+    done, tail0, tail1, loop, empty = (label("done"), label("tail0"), label("tail1"), label("loop"),
+                                       label("empty"))
     emit(f"s_mov_b32 s{S_M0}, m0")
     emit("s_nop 4")                                # the accumulator was just written by VALU
     emit(f"s_mov_b32 s{S_NI}, %[ni]")
     emit(f"s_mov_b32 s{S_N}, 0")
-    emit(f"s_cmp_eq_u32 s{S_NI}, 0")
-    emit(f"s_cbranch_scc1 {done}")
     emit(f"s_movk_i32 s{S_C1}, 4096")
     emit(f"s_movk_i32 s{S_C2}, 8192")
     emit(f"s_movk_i32 s{S_C3}, 12288")
+    emit(f"s_cmp_eq_u32 s{S_NI}, 0")
+    emit(f"s_cbranch_scc1 {empty}")
     emit(f"s_mov_b32 s{S_ONES}, 0x3f803f80")       # bf16 (1, 1)
     # constant parts of the bias operands: B = (1, 1, 0, ...) in the lower lane half
     emit(f"v_bfe_u32 {t(6)}, %[koff], 9, 1")        # lane half
@@ -554,18 +599,31 @@ def program():
         emit(f"{lab}:")
         tail(par)
         emit(f"s_branch {done}")
+    emit(f"{empty}:")                              # no items: only the first-order term
+    if WITH_G[0]:
+        for ln in hload_lines():
+            emit(ln)
     emit(f"{done}:")
     emit("s_waitcnt vmcnt(0) lgkmcnt(0)")
+    if WITH_G[0]:
+        nog = label("nog")
+        emit("s_cmp_eq_u32 %[hf], 0")
+        emit(f"s_cbranch_scc1 {nog}")
+        mg, lg = g_ops()
+        Sched().run(mg, lg, [], [])
+        emit(f"{nog}:")
     emit("s_nop 15")
     emit("s_nop 15")                               # last accumulator MFMAs before later reads
     emit(f"s_mov_b32 m0, s{S_M0}")
 
 
 TRACK_MAX = [True]
+WITH_G = [True]
 bodies = {}
 for name, track in (("PISA_ATTN_LOOP_D128_ASM", False), ("PISA_ATTN_LOOP_D128_SAFE_ASM", True)):
     L.clear()
     TRACK_MAX[0] = track
+    WITH_G[0] = not track
     program()
     bodies[name] = list(L)
 clob = ([f'"v{i}"' for i in range(SREG, 256)] + [f'"a{i}"' for i in range(KA, QBA + 4)] +

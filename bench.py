@@ -30,7 +30,7 @@ import time
 import numpy as np
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, datasheet
-PEAK_FP32_TFLOPS = 157.3   # MI355X fp32 vector (packed) peak
+PEAK_FP32_TFLOPS = 157.3   # MI355X fp32 peak (matrix cores; the packed vector peak is the same)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, datasheet
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -194,7 +194,7 @@ def main():
     plan_kernel = P.attn_fwd_plan(w.batch, w.heads, w.seq_len, w.head_dim, w.dtype,
                                   P.topk_for_density(w.density, P.num_blocks(w.seq_len)), w.band,
                                   w.second_order)
-    attn_kernel_name = {0: "attn_valu_kernel", 1: ATTN_KERNEL, 2: "attn_mfma_kernel"}[plan_kernel]
+    attn_kernel_name = {0: "attn_valu_kernel", 1: ATTN_KERNEL, 2: "attn_mfma_kernel", 3: "attn_f32_kernel"}[plan_kernel]
     torch.cuda.set_device(dev)
     t0 = time.time()
     qa, ka, va = I.make_inputs(w)
@@ -428,6 +428,7 @@ def main():
     phase1_tflops = 4 * D * exact_pairs / (phase1_ms * 1e-3) / 1e12 if phase1_ms else None
     dense_flops = 4.0 * B * H * T * T * D
     attn_tflops = attn_flops / (attn_ms * 1e-3) / 1e12
+    apeak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS   # the fused kernel's own matrix-core peak
     prof_ns = profile_avg_ns(w.name) if attn_kernel_name == ATTN_KERNEL else None
     traffic = load_traffic(w.name) if attn_kernel_name == ATTN_KERNEL else None
     unique_bytes = 4 * B * H * T * D * (2 if w.dtype == "bf16" else 4)   # Q, K, V read and O written once
@@ -485,7 +486,7 @@ def main():
                           "algorithmic_tflop": round(attn_flops / 1e12, 4)},
         "phase1_exact": None if phase1_ms is None else {
             "ms": round(phase1_ms, 4), "algorithmic_tflop": round(4 * D * exact_pairs / 1e12, 4),
-            "tflops": round(phase1_tflops, 2), "frac_mfma": round(phase1_tflops / PEAK_BF16_TFLOPS, 4)},
+            "tflops": round(phase1_tflops, 2), "frac_mfma": round(phase1_tflops / apeak, 4)},
         "morton_reorder": reorder,
         "pisa_block_stats": {"ms": round(stats_ms, 4), **spread(per_kernel[0]), "algorithmic_bytes": stats_bytes,
                              "gbs": round(stats_bytes / (stats_ms * 1e-3) / 1e9, 1),
@@ -499,17 +500,17 @@ def main():
                             "score_gemm_tflop": round(route_gemm_flops / 1e12, 5),
                             "score_gemm_floor_ms": round(route_gemm_flops / (PEAK_FP32_TFLOPS * 1e12) * 1e3, 4),
                             "frac_fp32_mfma": round(route_gemm_flops / (route_ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS, 4)},
-        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": apeak,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / apeak, 4),
                      "frac_profile": (None if prof_ns is None else
-                                      round(attn_flops / (prof_ns * 1e-9) / 1e12 / PEAK_BF16_TFLOPS, 4)),
+                                      round(attn_flops / (prof_ns * 1e-9) / 1e12 / apeak, 4)),
                      "traffic": traffic,
                      "traffic_kind": ("L2-to-fabric bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, each "
                                       "scaled by its reading for a plain 1 GiB copy); requests the Infinity "
                                       "Cache serves are included, so this bounds HBM bytes from above"),
                      "traffic_over_unique": None if traffic is None else round(traffic / unique_bytes, 2),
                      "unique_bytes": unique_bytes,
-                     "kernel": ATTN_KERNEL + " (pisa_attn_fwd)"},
+                     "kernel": attn_kernel_name + " (pisa_attn_fwd)"},
         "input_generation_s": round(gen_s, 1),
     }
     if locality is not None:

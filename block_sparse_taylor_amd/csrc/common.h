@@ -140,6 +140,11 @@ hipError_t launch_attn_fwd_valu(const Geom& g, int dtype, const pisa_params_t* p
                                 const int32_t* idx, const float* wgate, void* o, float* rstat,
                                 hipStream_t stream);
 
+// fp32 inputs on the fp32 matrix cores (reads stats kbar, vsum, hsum).
+hipError_t launch_attn_fwd_f32(const Geom& g, const pisa_params_t* p, const void* q, const void* k,
+                               const void* v, const StatsView* st, const int32_t* idx, const float* wgate,
+                               void* o, float* rstat, hipStream_t stream);
+
 hipError_t launch_reorder(const Geom& g, int64_t batch, int64_t heads, int elem_bytes, bool gather,
                           const int32_t* perm, const void* src, void* dst, hipStream_t stream);
 void z_order_host(const int64_t* grid, int ndim, int64_t prefix, int32_t* perm);

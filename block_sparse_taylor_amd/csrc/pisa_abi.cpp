@@ -321,7 +321,7 @@ pisa_status_t pisa_attn_fwd(const pisa_shape_t* shape, const pisa_params_t* para
     const pisa_params_t pr = resolved(params, g);
     const StatsView sv = stats_view(g, shape->dtype, stats, bf ? operands : nullptr);
     if (bf) return from_hip(launch_attn_fwd_mfma(g, &pr, q, k, v, &sv, idx, wgate, o, row_stats, s));
-    return from_hip(launch_attn_fwd_valu(g, shape->dtype, &pr, q, k, v, &sv, idx, wgate, o, row_stats, s));
+    return from_hip(launch_attn_fwd_f32(g, &pr, q, k, v, &sv, idx, wgate, o, row_stats, s));
 }
 
 pisa_status_t pisa_attn_fwd_valu(const pisa_shape_t* shape, const pisa_params_t* params,

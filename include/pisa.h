@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define PISA_ABI_VERSION 14
+#define PISA_ABI_VERSION 15
 
 typedef enum {
     PISA_OK = 0,
@@ -272,7 +272,8 @@ pisa_status_t pisa_route_topk(const pisa_shape_t *shape, const pisa_params_t *pa
  * ignored like -1 (the kernels address no memory from it); a repeated id or
  * one inside the band makes the result unspecified. o: [B,H,T,D] in the input
  * dtype; must not alias q, k, v. bf16 runs compute QK^T and PV with bf16 MFMA (fp32
- * accumulation, P rounded to bf16); fp32 runs compute in fp32.
+ * accumulation, P rounded to bf16); fp32 runs compute every product on the
+ * fp32 matrix cores (fp32 products and sums; P, kbar and V-hat stay fp32).
  * row_stats: NULL, or a [B,H,T,2] fp32 output (it must not overlap o, q, k,
  * v): for each row t, row_stats[t][0] = lse_t = ln(sum_{j in S_i} sum_n
  * e^{s q.k} + l_tail_t), the natural log of the output's denominator, and
@@ -291,8 +292,8 @@ pisa_status_t pisa_attn_fwd(const pisa_shape_t *shape, const pisa_params_t *para
 /*
  * pisa_attn_fwd_valu: the same contract as pisa_attn_fwd, computed by a plain
  * fp32 VALU kernel for either dtype (bf16 inputs are widened exactly; P is
- * not rounded). It is the fp32 path of pisa_attn_fwd and a GPU reference for
- * the bf16 MFMA kernel.
+ * not rounded, one thread per query row). It is a GPU reference for the
+ * matrix-core kernels of pisa_attn_fwd (bf16 and fp32).
  */
 pisa_status_t pisa_attn_fwd_valu(const pisa_shape_t *shape, const pisa_params_t *params,
                                  const void *q, const void *k, const void *v,
@@ -304,7 +305,7 @@ pisa_status_t pisa_attn_fwd_valu(const pisa_shape_t *shape, const pisa_params_t 
  * pisa_attn_fwd_plan (HOST only, no GPU work): which kernel pisa_attn_fwd runs
  * for this shape and these parameters, and the longest item list one wave of
  * the persistent bf16 kernel would build.
- *   kernel      PISA_KERNEL_VALU (fp32 inputs), PISA_KERNEL_MFMA_ASM (bf16,
+ *   kernel      PISA_KERNEL_MFMA_F32 (fp32 inputs), PISA_KERNEL_MFMA_ASM (bf16,
  *               head_dim 128, and every wave's list fits 256 items) or
  *               PISA_KERNEL_MFMA (bf16 otherwise: head_dim 64, or lists too
  *               long for the persistent kernel);
@@ -316,7 +317,8 @@ pisa_status_t pisa_attn_fwd_valu(const pisa_shape_t *shape, const pisa_params_t 
  * and params (as pisa_attn_fwd checks them). A band larger than N is taken
  * as N by every entry point.
  */
-typedef enum { PISA_KERNEL_VALU = 0, PISA_KERNEL_MFMA_ASM = 1, PISA_KERNEL_MFMA = 2 } pisa_attn_kernel_t;
+typedef enum { PISA_KERNEL_VALU = 0, PISA_KERNEL_MFMA_ASM = 1, PISA_KERNEL_MFMA = 2,
+               PISA_KERNEL_MFMA_F32 = 3 } pisa_attn_kernel_t;
 pisa_status_t pisa_attn_fwd_plan(const pisa_shape_t *shape, const pisa_params_t *params,
                                  int32_t *kernel, int64_t *wave_items);
 

@@ -32,7 +32,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pisa_abi_version() == 14
+    assert lib.pisa_abi_version() == 15
     for code in range(9):
         assert lib.pisa_status_str(code)
     assert lib.pisa_status_str(99) == b"unknown status"
@@ -374,7 +374,7 @@ def plan(lib, T, D, topk, band=1, n_sink=0, second_order=0, dtype=_lib.PISA_BF16
     return st, kern.value, items.value
 
 
-ASM, MFMA, VALU = 1, 2, 0
+ASM, MFMA, F32 = 1, 2, 3
 
 
 @pytest.mark.parametrize("T,D,topk,band,n_sink,so,want_items,want_kernel", [
@@ -396,15 +396,17 @@ ASM, MFMA, VALU = 1, 2, 0
     (4096, 128, 4, 1, 32, 0, 11, ASM),
     # ... but never more than N of them: N = 32, all forced, 32 + 4 = 36 (9) + 1
     (2048, 128, 4, 1, 32, 0, 10, ASM),
-    # head_dim 64 always runs the C++ matrix-core kernel; fp32 the VALU kernel
+    # head_dim 64 always runs the C++ matrix-core kernel; fp32 the fp32
+    # matrix-core kernel (either head_dim)
     (32760, 64, 64, 1, 0, 0, 19, MFMA),
-    (32760, 128, 64, 1, 0, 0, 19, VALU),
+    (32760, 128, 64, 1, 0, 0, 19, F32),
+    (1024, 64, 4, 1, 0, 0, 3, F32),
 ])
 def test_attn_fwd_dispatch_rule(lib, T, D, topk, band, n_sink, so, want_items, want_kernel):
     """pisa_attn_fwd_plan: the persistent bf16 kernel lists ceil(E/4) exact items
     and ceil(G/4) virtual-token groups per wave in a 256-entry LDS list, so it is
     chosen only where that bound fits, whatever the second-order switch says."""
-    dtype = _lib.PISA_F32 if want_kernel == VALU else _lib.PISA_BF16
+    dtype = _lib.PISA_F32 if want_kernel == F32 else _lib.PISA_BF16
     st, kern, items = plan(lib, T, D, topk, band, n_sink, so, dtype)
     assert st == 0
     assert items == want_items

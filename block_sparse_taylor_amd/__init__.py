@@ -314,8 +314,9 @@ def pisa_attn_bwd(q, k, v, o, dout, stats, idx, wgate=None, band=1, second_order
 
 def attn_fwd_plan(batch, heads, seq_len, head_dim, dtype, topk, band=1, second_order=False, n_sink=0) -> int:
     """The kernel pisa_attn_fwd runs for these arguments (pisa_attn_fwd_plan;
-    host only): 0 fp32 VALU, 1 persistent bf16 matrix-core kernel, 2 the
-    non-persistent bf16 matrix-core kernel."""
+    host only): 1 persistent bf16 matrix-core kernel, 2 the non-persistent
+    bf16 matrix-core kernel, 3 the fp32 matrix-core kernel (0, the vector
+    kernel, only runs as pisa_attn_fwd_valu)."""
     code = PISA_BF16 if dtype in ("bf16", torch.bfloat16) else PISA_F32
     sh = _lib.Shape(batch, heads, seq_len, head_dim, BLOCK, code, 0.0)
     prm = _lib.Params(int(topk), int(band), int(second_order), 1, 0, int(n_sink))

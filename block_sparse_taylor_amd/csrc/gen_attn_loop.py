@@ -12,27 +12,26 @@ buffer offsets held in SGPRs, and the softmax ordered so that no pad is needed
 between an exp2 and its consumer.
 
 Per step n (n = 0 .. ni - 2), one stream of 64 MFMAs:
-  QK(n+1): S^T(n+1) = K(n+1) Q^T      32 MFMAs, K from AGPRs, Q^T from LDS
+  QK(n+1): S^T(n+1) = K(n+1) Q^T      32 MFMAs, K and Q^T from AGPRs
   PV(n):   O^T     += V(n)^T P(n)     32 MFMAs, V^T by transposed LDS reads
 and between them: the softmax of item n (exp2 against the row reference, bf16
 pack into P, bf16 dot2 row sums; the writes of P group g precede the PV MFMAs
 that read it), the K loads of item n+2 (each after the last QK MFMA that reads
 the AGPRs it overwrites), the V DMA of item n+1 into the other LDS tile, and
 after the last QK MFMA the tail mask, row max and reference update of
-S^T(n+1). The last item runs its softmax and PV alone, with the loads of
-the first-order term's H operand (into the K registers) issued before them;
-after it, G^T = H^T Q^T (32 MFMAs, H split hi + lo) accumulates into two
-operand tiles the caller combines with the merged state. The softmax keeps a
+S^T(n+1). The last item runs its softmax and PV alone. The softmax keeps a
 fixed reference (a row's first finite tile max), tracks the running maximum
 and flags a tile more than 64 (log2 units) above the reference; the caller
 reruns with the exact maxima in that case.
 
 Register plan (explicitly named, declared clobbered): a128-a191 K of the
-next item (kreg[kt][ks]), H during the last item; v56-v119 / v120-v183 the S^T buffers of two
-consecutive items; v184-v215 P; v216-v231 Q^T operand buffers; v232-v243
-transposed-V operand buffers; v244-v255 scratch (v244:v245 the pending
-item-list entry); s70-s90 loop state, buffer descriptors, offsets and the
-bf16 pair (1, 1) for the row sums. The PV
+next item (kreg[kt][ks]); a192-a255 the 16 Q^T operands of the query block
+(loaded once at the start: operand 2 ks + qt holds, in lane l, query row
+32 qt + l % 32, head dims 16 ks + 8 (l / 32) + (0..7)); v56-v119 / v120-v183 the S^T buffers of two
+consecutive items; v184-v215 P; v216-v227 the bias operands of a
+virtual-token item; v232-v243 transposed-V operand buffers; v244-v255
+scratch (v244:v245 the pending item-list entry); s70-s90 loop state, buffer
+descriptors, offsets and the bf16 pair (1, 1) for the row sums. The PV
 accumulators (AGPRs), the softmax state and the per-lane addresses are
 operands. VALU work is written in 4-byte encodings where one exists (an
 8-byte instruction costs about a cycle more to issue). Hazard pads follow the
@@ -45,8 +44,8 @@ write to an LDS DMA.
 import os
 import sys
 
-D, KS, DT, CH, VL, RB, QP = 128, 8, 4, 16, 16, 256, 136
-KA, SREG, PREG, QB, VB, T = 128, 56, 184, 216, 232, 244
+D, KS, DT, CH, VL, RB = 128, 8, 4, 16, 16, 256
+KA, QA, SREG, PREG, KBV, QBV, VB, T = 128, 192, 56, 184, 216, 224, 232, 244
 
 
 def kreg(kt, ks): x = KA + 4 * (kt * KS + ks); return f"a[{x}:{x+3}]"
@@ -54,7 +53,7 @@ def sreg(b, kt, qt): x = SREG + 64 * b + 16 * (kt * 2 + qt); return f"v[{x}:{x+1
 def se(b, kt, qt, e): return f"v{SREG + 64 * b + 16 * (kt * 2 + qt) + e}"
 def preg(kt, h, qt): x = PREG + 4 * ((kt * 2 + h) * 2 + qt); return f"v[{x}:{x+3}]"
 def pw(kt, h, qt, w): return f"v{PREG + 4 * ((kt * 2 + h) * 2 + qt) + w}"
-def qbuf(i): x = QB + 4 * i; return f"v[{x}:{x+3}]"
+def qop(ks, qt): x = QA + 4 * (2 * ks + qt); return f"a[{x}:{x+3}]"   # Q^T operand
 def vbuf(i): x = VB + 4 * i; return f"v[{x}:{x+3}]"
 def vlo(i): x = VB + 4 * i; return f"v[{x}:{x+1}]"
 def vhi(i): x = VB + 4 * i; return f"v[{x+2}:{x+3}]"
@@ -65,11 +64,9 @@ S_N, S_NI, S_OFFA, S_NVA, S_OFFB, S_NVB = 70, 71, 72, 73, 74, 75
 S_KRS, S_VRS = 76, 80                     # 4-SGPR buffer descriptors
 S_M0, S_C1, S_X, S_Y, S_C2, S_C3, S_ONES, S_NVC = 84, 85, 86, 87, 88, 89, 90, 91
 SGPRS = list(range(70, 92))
-KBA, QBA = 192, 200                       # AGPRs: bias operands of the virtual-token step
 SOFF = {0: "0", 4096: f"s{S_C1}", 8192: f"s{S_C2}", 12288: f"s{S_C3}"}
 def SR(a, n=4): return f"s[{a}:{a+n-1}]"
 ACC = [f"%[a{i}]" for i in range(8)]      # acc[dt][qt] -> a{2 dt + qt}
-GACC = ["%[g0]", "%[g1]"]                 # G^T accumulators of the two query tiles
 MINF = "0xff800000"
 GROUPS = [(kt, h) for kt in range(2) for h in range(2)]
 TR = {0: ["%[tr0_0]", "%[tr0_1]", "%[tr0_2]", "%[tr0_3]"],
@@ -257,7 +254,7 @@ def kbias_lines(off, nv):
                 f"v_bfe_u32 {tmp}, %[koff], 9, 1",               # lane half
                 f"v_subrev_u32 {tmp}, 1, {tmp}",                 # lower half: all ones
                 f"v_and_b32 {pk}, {pk}, {tmp}",
-                f"v_accvgpr_write_b32 a{KBA + 4 * kt}, {pk}"]
+                f"v_mov_b32 v{KBV + 4 * kt}, {pk}"]
     out.append(f"{skip}:")
     return out
 
@@ -268,8 +265,8 @@ def bias_mfma_op(sb, nv):
     lines = [f"s_bitcmp1_b32 s{nv}, 16", f"s_cbranch_scc0 {skip}"]
     for kt in range(2):
         for qt in range(2):
-            lines.append(f"v_mfma_f32_32x32x16_bf16 {sreg(sb, kt, qt)}, a[{KBA + 4 * kt}:{KBA + 4 * kt + 3}], "
-                         f"a[{QBA}:{QBA + 3}], {sreg(sb, kt, qt)}")
+            lines.append(f"v_mfma_f32_32x32x16_bf16 {sreg(sb, kt, qt)}, v[{KBV + 4 * kt}:{KBV + 4 * kt + 3}], "
+                         f"v[{QBV}:{QBV + 3}], {sreg(sb, kt, qt)}")
     lines.append(f"{skip}:")
     return Op("mfma", lines)
 
@@ -313,23 +310,18 @@ def prev_after_of(vm):
 
 
 def qk_ops(sb, vneed):
-    """S^T(sb) = K Q^T: 32 MFMAs (k-step-major), their 16 Q^T reads, and the
-    index of the last MFMA reading each K operand."""
-    mf, lds, idx = [], [], {}
+    """S^T(sb) = K Q^T: 32 MFMAs (k-step-major; both operands in AGPRs) and
+    the index of the last MFMA reading each K operand."""
+    mf, idx = [], {}
     for ks in range(KS):
         for kt in range(2):
             for qt in range(2):
                 src_c = "0" if ks == 0 else sreg(sb, kt, qt)
                 idx[(kt, qt, ks)] = len(mf)
-                mf.append(Op("mfma", [f"v_mfma_f32_32x32x16_bf16 {sreg(sb, kt, qt)}, {kreg(kt, ks)}, {qbuf((ks % 2) * 2 + qt)}, {src_c}"],
-                             needs=[("q", qt, ks)], vneeds=[("k", kt, ks)] if vneed else []))
-    for ks in range(KS):
-        for qt in range(2):
-            after = max(idx[(kt, qt, ks - 2)] for kt in range(2)) if ks >= 2 else -1
-            lds.append(Op("lds", [f"ds_read_b128 {qbuf((ks % 2) * 2 + qt)}, %[qa] offset:{(qt * 32 * QP) * 2 + 32 * ks}"],
-                          lds_id=("q", qt, ks), after=after))
+                mf.append(Op("mfma", [f"v_mfma_f32_32x32x16_bf16 {sreg(sb, kt, qt)}, {kreg(kt, ks)}, {qop(ks, qt)}, {src_c}"],
+                             vneeds=[("k", kt, ks)] if vneed else []))
     last = {(kt, ks): max(idx[(kt, qt, ks)] for qt in range(2)) for kt in range(2) for ks in range(KS)}
-    return mf, lds, last
+    return mf, [], last
 
 
 def pv_ops(par, base, vneed):
@@ -488,50 +480,10 @@ def snapshot():
     emit(f"{skip}:")
 
 
-def hload_lines():
-    """the H^T operand of G^T = H^T Q^T for this wave's 32 output dims (the
-    packed H: 16 contiguous 1 KB runs, k-step ks hi at run 2 ks, lo at run
-    2 ks + 1) into the K AGPRs, which no later item needs; skipped without
-    the first-order term."""
-    skip = label("noh")
-    out = ["s_cmp_eq_u32 %[hf], 0", f"s_cbranch_scc1 {skip}",
-           f"s_mov_b32 s{S_KRS}, %[hb_lo]", f"s_mov_b32 s{S_KRS + 1}, %[hb_hi]",
-           f"s_movk_i32 s{S_KRS + 2}, {16 * 1024}", f"s_mov_b32 s{S_KRS + 3}, 0x00020000"]
-    for u in range(2 * KS):
-        off = 1024 * u
-        out.append(f"buffer_load_dwordx4 a[{KA + 4 * u}:{KA + 4 * u + 3}], %[koff], {SR(S_KRS)}, "
-                   f"{SOFF[off & ~4095]} offen offset:{off & 4095}")
-    out.append(f"{skip}:")
-    return out
-
-
-def g_ops():
-    """G^T += H^T Q^T for both query tiles: 32 MFMAs (A = H hi or lo from the
-    AGPRs, B = the Q^T operand read from LDS as in QK) and their 16 Q reads."""
-    mf, lds, idx = [], [], {}
-    for ks in range(KS):
-        for part in range(2):
-            for qt in range(2):
-                u = 2 * ks + part
-                idx[(qt, ks, part)] = len(mf)
-                mf.append(Op("mfma", [f"v_mfma_f32_32x32x16_bf16 {GACC[qt]}, a[{KA + 4 * u}:{KA + 4 * u + 3}], "
-                                      f"{qbuf((ks % 2) * 2 + qt)}, {GACC[qt]}"], needs=[("q", qt, ks)]))
-    for ks in range(KS):
-        for qt in range(2):
-            after = max(idx[(qt, ks - 2, part)] for part in range(2)) if ks >= 2 else -1
-            lds.append(Op("lds", [f"ds_read_b128 {qbuf((ks % 2) * 2 + qt)}, %[qa] offset:{(qt * 32 * QP) * 2 + 32 * ks}"],
-                          lds_id=("q", qt, ks), after=after))
-    return mf, lds
-
-
 def tail(par):
-    """the last item: softmax of S^T(par), PV from tile par (the H loads of
-    the first-order term go out first, so their latency hides behind both)."""
+    """the last item: softmax of S^T(par), PV from tile par."""
     emit(f"; ---- last item, parity {par}")
     emit("s_waitcnt vmcnt(0) lgkmcnt(0)")
-    if WITH_G[0]:
-        for ln in hload_lines():
-            emit(ln)
     for o in softmax_ops(par, 0):
         for ln in o.lines:
             emit(ln)
@@ -553,14 +505,22 @@ def program():
     emit(f"s_movk_i32 s{S_C3}, 12288")
     emit(f"s_cmp_eq_u32 s{S_NI}, 0")
     emit(f"s_cbranch_scc1 {empty}")
+    # the Q^T operands (rows past T read zero: the descriptor's range)
+    emit(f"s_mov_b32 s{S_VRS}, %[q_lo]")
+    emit(f"s_mov_b32 s{S_VRS + 1}, %[q_hi]")
+    emit(f"s_mov_b32 s{S_VRS + 2}, %[q_bytes]")
+    emit(f"s_mov_b32 s{S_VRS + 3}, 0x00020000")
+    for ks in range(KS):
+        for qt in range(2):
+            emit(f"buffer_load_dwordx4 {qop(ks, qt)}, %[qoff], {SR(S_VRS)}, {SOFF[8192 * qt]} offen offset:{32 * ks}")
     emit(f"s_mov_b32 s{S_ONES}, 0x3f803f80")       # bf16 (1, 1)
     # constant parts of the bias operands: B = (1, 1, 0, ...) in the lower lane half
     emit(f"v_bfe_u32 {t(6)}, %[koff], 9, 1")        # lane half
     emit(f"v_subrev_u32 {t(6)}, 1, {t(6)}")
     emit(f"v_and_b32 {t(6)}, s{S_ONES}, {t(6)}")
-    emit(f"v_accvgpr_write_b32 a{QBA}, {t(6)}")
-    for r in list(range(QBA + 1, QBA + 4)) + [KBA + 1, KBA + 2, KBA + 3, KBA + 5, KBA + 6, KBA + 7]:
-        emit(f"v_accvgpr_write_b32 a{r}, 0")
+    emit(f"v_mov_b32 v{QBV}, {t(6)}")
+    for r in list(range(QBV + 1, QBV + 4)) + [KBV + 1, KBV + 2, KBV + 3, KBV + 5, KBV + 6, KBV + 7]:
+        emit(f"v_mov_b32 v{r}, 0")
     # item 0: its K, then (pipelined with QK(0)) K of item 1 and V of item 0
     emit(f"ds_read_b64 v[{T}:{T+1}], %[il]")
     emit("s_waitcnt lgkmcnt(0)")
@@ -599,34 +559,22 @@ def program():
         emit(f"{lab}:")
         tail(par)
         emit(f"s_branch {done}")
-    emit(f"{empty}:")                              # no items: only the first-order term
-    if WITH_G[0]:
-        for ln in hload_lines():
-            emit(ln)
+    emit(f"{empty}:")                              # no items
     emit(f"{done}:")
     emit("s_waitcnt vmcnt(0) lgkmcnt(0)")
-    if WITH_G[0]:
-        nog = label("nog")
-        emit("s_cmp_eq_u32 %[hf], 0")
-        emit(f"s_cbranch_scc1 {nog}")
-        mg, lg = g_ops()
-        Sched().run(mg, lg, [], [])
-        emit(f"{nog}:")
     emit("s_nop 15")
     emit("s_nop 15")                               # last accumulator MFMAs before later reads
     emit(f"s_mov_b32 m0, s{S_M0}")
 
 
 TRACK_MAX = [True]
-WITH_G = [True]
 bodies = {}
 for name, track in (("PISA_ATTN_LOOP_D128_ASM", False), ("PISA_ATTN_LOOP_D128_SAFE_ASM", True)):
     L.clear()
     TRACK_MAX[0] = track
-    WITH_G[0] = not track
     program()
     bodies[name] = list(L)
-clob = ([f'"v{i}"' for i in range(SREG, 256)] + [f'"a{i}"' for i in range(KA, QBA + 4)] +
+clob = ([f'"v{i}"' for i in range(SREG, 256)] + [f'"a{i}"' for i in range(KA, 256)] +
         [f'"s{i}"' for i in SGPRS])
 out = ["// Generated by gen_attn_loop.py (do not edit): the D = 128 item loop of the fused PISA forward for gfx950.",
        "// PISA_ATTN_LOOP_D128_ASM: the row maximum of the first item only (sets the reference);",

@@ -306,13 +306,13 @@ pisa_status_t pisa_attn_fwd_valu(const pisa_shape_t *shape, const pisa_params_t 
  * for this shape and these parameters, and the longest item list one wave of
  * the persistent bf16 kernel would build.
  *   kernel      PISA_KERNEL_MFMA_F32 (fp32 inputs), PISA_KERNEL_MFMA_ASM (bf16,
- *               head_dim 128, and every wave's list fits 256 items) or
- *               PISA_KERNEL_MFMA (bf16 otherwise: head_dim 64, or lists too
- *               long for the persistent kernel);
- *   wave_items  ceil(E / 4) + ceil(G / 4) with E = min(N, 2 band + 1 +
- *               n_sink) + topk (forced blocks and routed ids: the exact
- *               items) and G = ceil(N / 64) (the virtual-token groups);
- *               wave 0 takes every fourth item of each kind.
+ *               head_dim 128, and a query block's item list fits 512
+ *               entries) or PISA_KERNEL_MFMA (bf16 otherwise: head_dim 64,
+ *               or lists too long for the persistent kernel);
+ *   wave_items  E + G with E = min(N, 2 band + 1 + n_sink) + topk (forced
+ *               blocks and routed ids: the exact items) and G = ceil(N / 64)
+ *               (the virtual-token groups): one wave of the persistent
+ *               kernel lists all of a query block's items.
  * Either output pointer may be NULL. Returns the validation status of shape
  * and params (as pisa_attn_fwd checks them). A band larger than N is taken
  * as N by every entry point.

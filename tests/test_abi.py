@@ -378,34 +378,33 @@ ASM, MFMA, F32 = 1, 2, 3
 
 
 @pytest.mark.parametrize("T,D,topk,band,n_sink,so,want_items,want_kernel", [
-    # Wan2.1-14B: 3 forced + 64 routed = 67 exact (17 on wave 0) + 8 groups (2)
-    (32760, 128, 64, 1, 0, 0, 19, ASM),
-    # Hunyuan: 3 + 232 = 235 (59) + 30 groups (8); second order changes nothing
-    (118800, 128, 232, 1, 0, 1, 67, ASM),
-    (118800, 128, 232, 1, 0, 0, 67, ASM),
-    # the window the persistent kernel must leave: N = 2048, 3 + 1000 exact
-    # (251 on wave 0) + 32 groups (8) = 259 > 256, with or without second order
-    (131072, 128, 1000, 1, 0, 1, 259, MFMA),
-    (131072, 128, 1000, 1, 0, 0, 259, MFMA),
-    # largest list that still fits: 3 + 989 = 992 (248) + 8 = 256
-    (131072, 128, 989, 1, 0, 1, 256, ASM),
-    (131072, 128, 990, 1, 0, 1, 257, MFMA),
-    # N = 8192, density 0.12: 3 + 983 (247) + 128 groups (32) = 279
-    (524288, 128, 983, 1, 0, 1, 279, MFMA),
-    # sinks count as forced blocks: N = 64, 3 + 32 + 4 = 39 (10) + 1 group (1)
-    (4096, 128, 4, 1, 32, 0, 11, ASM),
-    # ... but never more than N of them: N = 32, all forced, 32 + 4 = 36 (9) + 1
-    (2048, 128, 4, 1, 32, 0, 10, ASM),
+    # Wan2.1-14B: 3 forced + 64 routed = 67 exact items + 8 virtual groups
+    (32760, 128, 64, 1, 0, 0, 75, ASM),
+    # Hunyuan: 3 + 232 = 235 + 30 groups; second order changes nothing
+    (118800, 128, 232, 1, 0, 1, 265, ASM),
+    (118800, 128, 232, 1, 0, 0, 265, ASM),
+    # N = 2048: 3 + 477 + 32 groups = 512 fills the list exactly; one more
+    # routed id does not fit, with or without second order
+    (131072, 128, 477, 1, 0, 1, 512, ASM),
+    (131072, 128, 478, 1, 0, 1, 513, MFMA),
+    (131072, 128, 478, 1, 0, 0, 513, MFMA),
+    (131072, 128, 1000, 1, 0, 1, 1035, MFMA),
+    # N = 8192, density 0.12: 3 + 983 + 128 groups = 1114
+    (524288, 128, 983, 1, 0, 1, 1114, MFMA),
+    # sinks count as forced blocks: N = 64, 3 + 32 + 4 = 39 + 1 group
+    (4096, 128, 4, 1, 32, 0, 40, ASM),
+    # ... but never more than N of them: N = 32, all forced, 32 + 4 = 36 + 1
+    (2048, 128, 4, 1, 32, 0, 37, ASM),
     # head_dim 64 always runs the C++ matrix-core kernel; fp32 the fp32
     # matrix-core kernel (either head_dim)
-    (32760, 64, 64, 1, 0, 0, 19, MFMA),
-    (32760, 128, 64, 1, 0, 0, 19, F32),
-    (1024, 64, 4, 1, 0, 0, 3, F32),
+    (32760, 64, 64, 1, 0, 0, 75, MFMA),
+    (32760, 128, 64, 1, 0, 0, 75, F32),
+    (1024, 64, 4, 1, 0, 0, 8, F32),
 ])
 def test_attn_fwd_dispatch_rule(lib, T, D, topk, band, n_sink, so, want_items, want_kernel):
-    """pisa_attn_fwd_plan: the persistent bf16 kernel lists ceil(E/4) exact items
-    and ceil(G/4) virtual-token groups per wave in a 256-entry LDS list, so it is
-    chosen only where that bound fits, whatever the second-order switch says."""
+    """pisa_attn_fwd_plan: a wave of the persistent bf16 kernel lists a query
+    block's E exact items and G virtual-token groups in a 512-entry LDS list, so
+    it is chosen only where E + G fits, whatever the second-order switch says."""
     dtype = _lib.PISA_F32 if want_kernel == F32 else _lib.PISA_BF16
     st, kern, items = plan(lib, T, D, topk, band, n_sink, so, dtype)
     assert st == 0
@@ -419,8 +418,8 @@ def test_attn_fwd_plan_clamps_band_and_validates(lib):
     N = 1857
     for band in (N, N + 5, (1 << 31) - 1):
         st, kern, items = plan(lib, 118800, 128, 0, band=band)
-        assert st == 0 and items == -(-N // 4) + -(-(-(-N // 64)) // 4)
-        assert kern == MFMA     # 465 + 8 > 256
+        assert st == 0 and items == N + -(-N // 64)
+        assert kern == MFMA     # 1857 + 30 > 512
     assert plan(lib, 118800, 128, 0, band=-1)[0] == 4          # PISA_ERR_PARAM
     assert plan(lib, 118800, 128, 1858)[0] == 4                 # topk > N
     assert plan(lib, 0, 128, 0)[0] == 2                         # PISA_ERR_SHAPE

@@ -290,16 +290,16 @@ def attn_plan(T, D, topk, band=1, n_sink=0, second_order=False, dtype=None):
     return kern.value, items.value
 
 
-@pytest.mark.parametrize("topk,kernel", [(989, 1), (1000, 2)])
+@pytest.mark.parametrize("topk,kernel", [(477, 1), (478, 2), (1000, 2)])
 def test_long_item_lists_second_order(topk, kernel):
     """One head, T = 131000 (N = 2047, last block 56 rows), D = 128, bf16, with
-    the second-order term. topk 989: wave 0 lists 3 + 989 exact items (248) and
-    8 virtual groups, exactly the persistent kernel's 256-entry list. topk 1000:
-    259 items, more than the list holds, so the C++ matrix-core kernel runs
-    (an earlier launcher left the virtual groups out of this bound with the
-    second order on and overflowed the list). Sampled query blocks, the ragged
-    last one included, against the oracle fed the GPU's routing; the routing
-    itself against the oracle's."""
+    the second-order term. The persistent kernel's wave lists a query block's
+    3 forced + topk routed exact items and its 32 virtual-token groups in a
+    512-entry list: topk 477 fills it exactly; topk 478 and 1000 do not fit,
+    so the C++ matrix-core kernel runs (an earlier launcher left the virtual
+    groups out of such a bound with the second order on and overflowed the
+    list). Sampled query blocks, the ragged last one included, against the
+    oracle fed the GPU's routing; the routing itself against the oracle's."""
     T, D, band = 131000, 128, 1
     N = -(-T // 64)
     kern, items = attn_plan(T, D, topk, band, second_order=True)

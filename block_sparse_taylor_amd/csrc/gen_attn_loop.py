@@ -29,11 +29,14 @@ next item (kreg[kt][ks]); a192-a255 the 16 Q^T operands of the query block
 (loaded once at the start: operand 2 ks + qt holds, in lane l, query row
 32 qt + l % 32, head dims 16 ks + 8 (l / 32) + (0..7)); v56-v119 / v120-v183 the S^T buffers of two
 consecutive items; v184-v215 P; v216-v227 the bias operands of a
-virtual-token item; v232-v243 transposed-V operand buffers; v244-v255
+virtual-token item; v228-v229 the gate values of a virtual-token item two
+ahead (per item parity, key l in lane l); v232-v243 three transposed-V
+operand buffers; v244-v255
 scratch (v244:v245 the pending item-list entry); s70-s90 loop state, buffer
 descriptors, offsets and the bf16 pair (1, 1) for the row sums. The PV
 accumulators (AGPRs), the softmax state and the per-lane addresses are
-operands. VALU work is written in 4-byte encodings where one exists (an
+operands. At the end the Q^T operands are written to the wave's first V tile
+in LDS (operand u at 1 KB u, lane l at 16 l) for the first-order term. VALU work is written in 4-byte encodings where one exists (an
 8-byte instruction costs about a cycle more to issue). Hazard pads follow the
 ones the compiler itself emits on gfx950:
 12 wait states from an MFMA result to a VALU read, 2 from a VALU write to an
@@ -45,7 +48,9 @@ import os
 import sys
 
 D, KS, DT, CH, VL, RB = 128, 8, 4, 16, 16, 256
-KA, QA, SREG, PREG, KBV, QBV, VB, T = 128, 192, 56, 184, 216, 224, 232, 244
+KA, QA, SREG, PREG, KBV, QBV, WV, VB, T = 128, 192, 56, 184, 216, 224, 228, 232, 244
+NVB = 3                                   # transposed-V operand buffers (v232-v243)
+W_LAST = False                            # gate-value load after the K loads (else before)
 
 
 def kreg(kt, ks): x = KA + 4 * (kt * KS + ks); return f"a[{x}:{x+3}]"
@@ -63,7 +68,8 @@ def t(i): return f"v{T + i}"
 S_N, S_NI, S_OFFA, S_NVA, S_OFFB, S_NVB = 70, 71, 72, 73, 74, 75
 S_KRS, S_VRS = 76, 80                     # 4-SGPR buffer descriptors
 S_M0, S_C1, S_X, S_Y, S_C2, S_C3, S_ONES, S_NVC = 84, 85, 86, 87, 88, 89, 90, 91
-SGPRS = list(range(70, 92))
+S_WRS = 92                                # 4-SGPR descriptor of a gate-value DMA
+SGPRS = list(range(70, 96))
 SOFF = {0: "0", 4096: f"s{S_C1}", 8192: f"s{S_C2}", 12288: f"s{S_C3}"}
 def SR(a, n=4): return f"s[{a}:{a+n-1}]"
 ACC = [f"%[a{i}]" for i in range(8)]      # acc[dt][qt] -> a{2 dt + qt}
@@ -113,7 +119,15 @@ class Sched:
         self.prev_after, self.vm_issued, self.prev_ok = prev_after or {}, 0, None
 
     def issue(self, op):
-        for ln in op.lines:
+        lines = op.lines
+        if op.kind == "valu" and op.vneeds:
+            # a VALU op waiting for memory (the bias of a virtual-token item
+            # for its gate values): the wait goes after the op's leading
+            # branch (lines 0-1), so the exact items that skip it do not wait;
+            # it is conditional, so later waits do not count on it
+            need = min(self.prev_after[v] for v in op.vneeds)
+            lines = lines[:2] + [f"s_waitcnt vmcnt({min(need + self.vm_issued, 63)})"] + lines[2:]
+        for ln in lines:
             emit(ln)
         if op.lds_id is not None:
             self.lds_seq[op.lds_id] = self.n_lds
@@ -202,10 +216,13 @@ def rsrc_item(base, kind, off, nv):
     emit(f"s_mov_b32 s{base+3}, 0x00020000")
 
 
-def kbias_lines(off, nv):
+def kbias_lines(off, nv, wpar):
     """for a virtual-token item: the A operand of the bias k-step. Key j = 64 g
     + 32 kt + lane % 32 of group g = off >> 14 gets b_j = log2(n_j) / c2
-    (+ w_ij / scale with the second-order term), or -inf if block j is
+    (+ w_ij / scale with the second-order term: the item's gated values
+    were loaded a step earlier into the gate register of parity wpar, key
+    l in lane l; the lower lane half, which alone carries the operand, takes
+    keys 32 .. 63 from the upper half by a lane swap), or -inf if block j is
     selected (exact) or past N, split into bf16 hi + lo in
     k-slots 0 and 1 of the lower lane half (zero elsewhere); with the constant
     B operand (1, 1 in slots 0, 1) one MFMA k-step adds b_j to S^T."""
@@ -223,6 +240,11 @@ def kbias_lines(off, nv):
     skipw = [label("now"), label("now")]
     for kt in range(2):
         word = f"s{S_X}" if kt == 0 else f"s{S_Y}"
+        if kt:
+            # keys 32 .. 63 (upper lanes of the gate register) to the lower
+            # lanes of pk: the swap exchanges tmp's upper and pk's lower half
+            out += [f"v_mov_b32 {tmp}, v{WV + wpar}", f"v_mov_b32 {pk}, v{WV + wpar}", "s_nop 1",
+                    f"v_permlane32_swap_b32 {tmp}, {pk}", "s_nop 2"]
         out += [f"v_bfe_u32 {j}, %[koff], 4, 5",                 # lane % 32 (koff = 16 lane)
                 f"v_lshrrev_b32_e64 {tmp}, 8, s{off}",           # 64 g
                 f"v_add_u32 {j}, {j}, {tmp}"]
@@ -237,11 +259,7 @@ def kbias_lines(off, nv):
                 # query block; j clamped into the row, keys past N are -inf anyway)
                 "s_cmp_eq_u32 %[so], 0",
                 f"s_cbranch_scc1 {skipw[kt]}",
-                f"v_min_u32 {j}, %[nm1], {j}",
-                f"v_lshlrev_b32 {j}, 2, {j}",
-                f"global_load_dword {j}, {j}, %[wrow]",
-                "s_waitcnt vmcnt(0)",
-                f"v_fma_f32 {tmp}, {j}, %[winv], {tmp}",
+                f"v_fma_f32 {tmp}, {f'v{WV + wpar}' if kt == 0 else pk}, %[winv], {tmp}",
                 f"{skipw[kt]}:",
                 f"v_mov_b32 {j}, {tmp}",
                 f"v_cvt_pk_bf16_f32 {pk}, {j}, {j}",
@@ -278,29 +296,45 @@ def kload_op(kt, ks, after):
               after=after, vm_id=("k", kt, ks))
 
 
-def vm_list(vl, qk_last_reader):
-    """the step's VMEM ops in issue order: K loads (ks-major, each after the
-    last QK MFMA reading its registers, + 1) and the V DMA of the next item
-    (rows 4 i .. 4 i + 3 -> LDS tile + 1024 i; M0 set once per four)."""
+def wload_ops(off, nv, wpar):
+    """the gated second-order values of an item two ahead (group g = off >> 14:
+    entry 64 g + l of the query block's row in lane l) -> the gate register of
+    parity wpar. The descriptor covers exactly the group's part of the row:
+    size 0 for an exact block or without the second-order term, so no byte
+    outside the row is addressed."""
+    return [Op("vmem", [
+        f"s_lshr_b32 s{S_Y}, s{off}, 6",                   # 256 g
+        f"s_add_u32 s{S_WRS}, %[wrow_lo], s{S_Y}",
+        f"s_addc_u32 s{S_WRS + 1}, %[wrow_hi], 0",
+        f"s_sub_u32 s{S_WRS + 2}, %[wbytes], s{S_Y}",        # 4 N - 256 g (> 0 for a virtual group)
+        f"s_bitcmp1_b32 s{nv}, 16",
+        f"s_cselect_b32 s{S_WRS + 2}, s{S_WRS + 2}, 0",
+        "s_cmp_eq_u32 %[so], 0",
+        f"s_cselect_b32 s{S_WRS + 2}, 0, s{S_WRS + 2}",
+        f"buffer_load_dword v{WV + wpar}, %[wlane], {SR(S_WRS)}, 0 offen"], vm_id=("w", 0))]
+
+
+def vm_list(vl, qk_last_reader, woff, wnv, wpar):
+    """the step's VMEM ops in issue order: the V DMA of the next item (rows
+    4 i .. 4 i + 3 -> LDS tile + 1024 i; M0 set once per four; its tile was
+    last read in the previous step), the K loads (ks-major, each after the
+    last QK MFMA reading its registers, + 1) and the gate-value loads of the
+    item after next (their register parity was last read in the previous
+    step)."""
     ops = []
-    dmas = []
     for a in range(4):
-        dmas.append(Op("m0", [f"s_add_u32 m0, {vl}, {4096 * a}" if a else f"s_mov_b32 m0, {vl}", "s_nop 0"]))
+        ops.append(Op("m0", [f"s_add_u32 m0, {vl}, {4096 * a}" if a else f"s_mov_b32 m0, {vl}", "s_nop 0"]))
         for b in range(4):
             i = 4 * a + b
-            dmas.append(Op("vmem", [f"buffer_load_dwordx4 %[voff], {SR(S_VRS)}, {SOFF[4096 * a]} offen offset:{1024 * b} lds"],
-                           vm_id=("d", i)))
-    di = 0
+            ops.append(Op("vmem", [f"buffer_load_dwordx4 %[voff], {SR(S_VRS)}, {SOFF[4096 * a]} offen offset:{1024 * b} lds"],
+                          vm_id=("d", i)))
+    if not W_LAST:
+        ops += wload_ops(woff, wnv, wpar)
     for ks in range(KS):
         for kt in range(2):
             ops.append(kload_op(kt, ks, qk_last_reader[(kt, ks)] + 1))
-        # two DMAs (with their M0 write) per k-step
-        n = 0
-        while di < len(dmas) and n < 2:
-            ops.append(dmas[di])
-            n += dmas[di].kind == "vmem"
-            di += 1
-    ops.extend(dmas[di:])
+    if W_LAST:
+        ops += wload_ops(woff, wnv, wpar)
     return ops
 
 
@@ -325,18 +359,22 @@ def qk_ops(sb, vneed):
 
 
 def pv_ops(par, base, vneed):
-    """O^T += V^T P: 32 MFMAs (group-major) and their 32 transposed V reads from tile par."""
+    """O^T += V^T P: 32 MFMAs (group-major) and their 32 transposed V reads from tile par.
+    base(k) is the position of PV MFMA k in the step's MFMA stream."""
+    if isinstance(base, int):
+        b0 = base
+        base = lambda k: b0 + k
     mf, lds = [], []
     pairs = [(kt, h, dt) for (kt, h) in GROUPS for dt in range(DT)]
     for r, (kt, h, dt) in enumerate(pairs):
         for qt in range(2):
-            mf.append(Op("mfma", [f"v_mfma_f32_32x32x16_bf16 {ACC[dt * 2 + qt]}, {vbuf(r % 3)}, {preg(kt, h, qt)}, {ACC[dt * 2 + qt]}"],
+            mf.append(Op("mfma", [f"v_mfma_f32_32x32x16_bf16 {ACC[dt * 2 + qt]}, {vbuf(r % NVB)}, {preg(kt, h, qt)}, {ACC[dt * 2 + qt]}"],
                          needs=[("v", r, 0), ("v", r, 1)], vneeds=[("d", i) for i in range(VL)] if vneed else []))
     for r, (kt, h, dt) in enumerate(pairs):
         r0 = 32 * kt + 16 * h
-        after = base + 2 * (r - 3) + 1 if r >= 3 else -1       # buffer r % 3 last read by pair r - 3
-        lds.append(Op("lds", [f"ds_read_b64_tr_b16 {vlo(r % 3)}, {TR[par][dt]} offset:{r0 * RB}"], lds_id=("v", r, 0), after=after))
-        lds.append(Op("lds", [f"ds_read_b64_tr_b16 {vhi(r % 3)}, {TR[par][dt]} offset:{(r0 + 8) * RB}"], lds_id=("v", r, 1), after=after))
+        after = base(2 * (r - NVB) + 1) if r >= NVB else -1   # buffer r % NVB last read by pair r - NVB
+        lds.append(Op("lds", [f"ds_read_b64_tr_b16 {vlo(r % NVB)}, {TR[par][dt]} offset:{r0 * RB}"], lds_id=("v", r, 0), after=after))
+        lds.append(Op("lds", [f"ds_read_b64_tr_b16 {vhi(r % NVB)}, {TR[par][dt]} offset:{(r0 + 8) * RB}"], lds_id=("v", r, 1), after=after))
     return mf, lds
 
 
@@ -388,7 +426,7 @@ def max_lines(sb):
     return out
 
 
-def softmax_ops(sb, pv_base):
+def softmax_ops(sb, pv_first):
     """exp2(S^T c2 - m) of S^T(sb) packed into P in pairs; the exp2 of pair p
     is separated from its consumers by the FMAs of pair p + 1. The writes of P
     group g precede the first PV MFMA of that group (pv_base + 8 g)."""
@@ -415,7 +453,7 @@ def softmax_ops(sb, pv_base):
         gi, kt, h, qt, w = pairs[p]
         x0, x1 = tmp(p)
         return [Op("valu", (["s_nop 0"] if pad else []) + [f"v_cvt_pk_bf16_f32 {pw(kt, h, qt, w)}, {x0}, {x1}"],
-                   before=pv_base + 8 * gi),
+                   before=pv_first[gi]),
                 Op("valu", [f"v_dot2c_f32_bf16 %[l{qt}], s{S_ONES}, {pw(kt, h, qt, w)}"])]
 
     ops = F(0) + E(0)
@@ -453,15 +491,27 @@ def full_step(par, vm_order):
     s = Sched(prev_after=prev_after_of(vm_order), n_lds=1)
     mq, lq, last = qk_ops(1 - par, vneed=True)
     mq.append(bias_mfma_op(1 - par, S_NVA))
-    mp, lp = pv_ops(par, len(mq), vneed=True)
-    vm = vm_list(VLDS[1 - par], last)
+    # MFMA stream: the PV groups of item n interleaved with the QK k-steps of
+    # item n+1, so that the softmax of item n (which feeds PV group by group)
+    # spreads over the whole step
+    nq = len(mq)
+    order = ([("q", k) for k in range(16)] + [("p", k) for k in range(8)] + [("q", k) for k in range(16, 24)] +
+             [("p", k) for k in range(8, 16)] + [("q", k) for k in range(24, nq)] + [("p", k) for k in range(16, 32)])
+    posq = {k: n for n, (w, k) in enumerate(order) if w == "q"}
+    posp = {k: n for n, (w, k) in enumerate(order) if w == "p"}
+    last = {key: posq[v] for key, v in last.items()}
+    mp, lp = pv_ops(par, lambda k: posp[k], vneed=True)
+    vm = vm_list(VLDS[1 - par], last, S_OFFB, S_NVB, par)      # gate values of item n+2
     assert [o.vm_id for o in vm] == [o.vm_id for o in vm_order]
-    valu = [Op("valu", kbias_lines(S_OFFA, S_NVA), before=len(mq) - 1)]
-    valu += softmax_ops(par, len(mq))
-    valu.append(Op("valu", mask_lines(1 - par, S_NVA), after=len(mq) - 1))
+    # the bias of a virtual item n+1 first (its gate values arrived a step
+    # ago), then the softmax of item n
+    valu = [Op("valu", kbias_lines(S_OFFA, S_NVA, 1 - par), before=posq[nq - 1], vneeds=[("w", 0)])]
+    valu += softmax_ops(par, [posp[8 * gi] for gi in range(4)])
+    valu.append(Op("valu", mask_lines(1 - par, S_NVA), after=posq[nq - 1]))
     if TRACK_MAX[0]:
-        valu += [Op("valu", [ln], after=len(mq) - 1) for ln in max_lines(1 - par)]
-    s.run(mq + mp, lq + lp, vm, valu)
+        valu += [Op("valu", [ln], after=posq[nq - 1]) for ln in max_lines(1 - par)]
+    mf = [mq[k] if w == "q" else mp[k] for (w, k) in order]
+    s.run(mf, lq + lp, vm, valu)
     snapshot()
     emit(f"s_mov_b32 s{S_OFFA}, s{S_OFFB}")
     emit(f"s_mov_b32 s{S_NVC}, s{S_NVA}")
@@ -484,7 +534,7 @@ def tail(par):
     """the last item: softmax of S^T(par), PV from tile par."""
     emit(f"; ---- last item, parity {par}")
     emit("s_waitcnt vmcnt(0) lgkmcnt(0)")
-    for o in softmax_ops(par, 0):
+    for o in softmax_ops(par, [8 * gi for gi in range(4)]):
         for ln in o.lines:
             emit(ln)
     snapshot()
@@ -503,8 +553,7 @@ def program():
     emit(f"s_movk_i32 s{S_C1}, 4096")
     emit(f"s_movk_i32 s{S_C2}, 8192")
     emit(f"s_movk_i32 s{S_C3}, 12288")
-    emit(f"s_cmp_eq_u32 s{S_NI}, 0")
-    emit(f"s_cbranch_scc1 {empty}")
+    emit(f"s_mov_b32 s{S_WRS + 3}, 0x00020000")    # gate-value descriptor, word 3 (words 0-2 per DMA)
     # the Q^T operands (rows past T read zero: the descriptor's range)
     emit(f"s_mov_b32 s{S_VRS}, %[q_lo]")
     emit(f"s_mov_b32 s{S_VRS + 1}, %[q_hi]")
@@ -513,6 +562,8 @@ def program():
     for ks in range(KS):
         for qt in range(2):
             emit(f"buffer_load_dwordx4 {qop(ks, qt)}, %[qoff], {SR(S_VRS)}, {SOFF[8192 * qt]} offen offset:{32 * ks}")
+    emit(f"s_cmp_eq_u32 s{S_NI}, 0")
+    emit(f"s_cbranch_scc1 {empty}")
     emit(f"s_mov_b32 s{S_ONES}, 0x3f803f80")       # bf16 (1, 1)
     # constant parts of the bias operands: B = (1, 1, 0, ...) in the lower lane half
     emit(f"v_bfe_u32 {t(6)}, %[koff], 9, 1")        # lane half
@@ -528,6 +579,9 @@ def program():
     emit(f"s_mov_b32 s{S_NVC}, s{S_NVB}")
     rsrc_item(S_KRS, "k", S_OFFB, S_NVB)
     rsrc_item(S_VRS, "v", S_OFFB, S_NVB)
+    for op in wload_ops(S_OFFB, S_NVB, 0):            # gate values of item 0 (waited with K(0))
+        for ln in op.lines:
+            emit(ln)
     for ks in range(KS):
         for kt in range(2):
             for ln in kload_op(kt, ks, -1).lines:
@@ -539,8 +593,8 @@ def program():
     read_list([f"s_sub_u32 s{S_Y}, s{S_NI}, 1", f"s_min_u32 s{S_X}, s{S_Y}, 2"])   # entry 2 (clamped), pending
     emit("s_waitcnt vmcnt(0)")                     # K(0)
     mq, lq, last = qk_ops(0, vneed=False)
-    vm0 = vm_list(VLDS[0], last)
-    Sched(n_lds=1).run(mq + [bias_mfma_op(0, S_NVB)], lq, vm0, [Op("valu", kbias_lines(S_OFFB, S_NVB), before=len(mq))])
+    vm0 = vm_list(VLDS[0], last, S_OFFA, S_NVA, 1)             # gate values of item 1
+    Sched(n_lds=1).run(mq + [bias_mfma_op(0, S_NVB)], lq, vm0, [Op("valu", kbias_lines(S_OFFB, S_NVB, 0), before=len(mq))])
     for ln in mask_lines(0, S_NVB):
         emit(ln)
     for ln in max_lines(0):
@@ -562,6 +616,14 @@ def program():
     emit(f"{empty}:")                              # no items
     emit(f"{done}:")
     emit("s_waitcnt vmcnt(0) lgkmcnt(0)")
+    # the Q^T operands to the wave's first V tile (free now) for the caller:
+    # operand u at bytes [1024 u, 1024 u + 1024), lane l at 16 l
+    for u in range(2 * KS):
+        for r in range(4):
+            emit(f"v_accvgpr_read_b32 v{SREG + 4 * u + r}, a{QA + 4 * u + r}")
+    for u in range(2 * KS):
+        emit(f"ds_write_b128 %[qdump], v[{SREG + 4 * u}:{SREG + 4 * u + 3}] offset:{1024 * u}")
+    emit("s_waitcnt lgkmcnt(0)")
     emit("s_nop 15")
     emit("s_nop 15")                               # last accumulator MFMAs before later reads
     emit(f"s_mov_b32 m0, s{S_M0}")

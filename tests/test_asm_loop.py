@@ -42,16 +42,18 @@ def test_loop_register_plan():
         assert named <= declared[k], (k, sorted(named - declared[k]))
     # the compiler keeps v0-v55 and a0-a127 (the PV accumulators) for itself
     assert min(declared["v"]) >= 56 and min(declared["a"]) >= 128
-    # the loop's instruction set: memory is read with vector loads (buffer,
-    # global) and LDS reads only, never written; scalar instructions are ALU
+    # the loop's instruction set: global memory is read with vector loads
+    # (buffer, global) only, never written; LDS is read, and written only with
+    # vector LDS writes (the Q^T copy at the end); scalar instructions are ALU
     # and control flow
     ops = set(re.findall(r'^\s*"\s*([a-z_0-9]+)', body, re.M))
     allowed = {
-        "buffer_load_dwordx4", "ds_read_b128", "ds_read_b64", "ds_read_b64_tr_b16",
+        "buffer_load_dword", "buffer_load_dwordx4", "ds_read_b32", "ds_read_b128", "ds_read_b64", "ds_read_b64_tr_b16",
+        "ds_write_b128",
         "global_load_dword", "s_add_u32", "s_addc_u32", "s_and_b32", "s_bitcmp1_b32", "s_branch",
         "s_cbranch_scc0", "s_cbranch_scc1", "s_cmp_eq_u32", "s_cmp_ge_u32", "s_cmp_lt_u32",
         "s_cselect_b32", "s_lshl_b32", "s_lshr_b32", "s_min_u32", "s_mov_b32", "s_movk_i32",
-        "s_nop", "s_sub_u32", "s_waitcnt", "v_accvgpr_write_b32", "v_add_f32", "v_add_u32",
+        "s_nop", "s_sub_u32", "s_waitcnt", "v_accvgpr_read_b32", "v_accvgpr_write_b32", "v_add_f32", "v_add_u32",
         "v_and_b32", "v_bfe_u32", "v_cmp_eq_f32", "v_cmp_eq_u32", "v_cmp_gt_f32", "v_cmp_gt_u32",
         "v_cmp_le_u32", "v_cndmask_b32", "v_cndmask_b32_e64", "v_cvt_pk_bf16_f32",
         "v_dot2c_f32_bf16", "v_exp_f32", "v_fma_f32", "v_lshlrev_b32", "v_lshrrev_b32_e64",

@@ -29,9 +29,10 @@ next item (kreg[kt][ks]); a192-a255 the 16 Q^T operands of the query block
 (loaded once at the start: operand 2 ks + qt holds, in lane l, query row
 32 qt + l % 32, head dims 16 ks + 8 (l / 32) + (0..7)); v56-v119 / v120-v183 the S^T buffers of two
 consecutive items; v184-v215 P; v216-v227 the bias operands of a
-virtual-token item; v228-v229 the gate values of a virtual-token item two
-ahead (per item parity, key l in lane l); v232-v243 three transposed-V
-operand buffers; v244-v255
+virtual-token item; with the second-order term v228-v229 the gate values
+of a virtual-token item two ahead (per item parity, key l in lane l) and
+v232-v243 three transposed-V operand buffers, without it v228-v243 four;
+v244-v255
 scratch (v244:v245 the pending item-list entry); s70-s90 loop state, buffer
 descriptors, offsets and the bf16 pair (1, 1) for the row sums. The PV
 accumulators (AGPRs), the softmax state and the per-lane addresses are
@@ -49,7 +50,7 @@ import sys
 
 D, KS, DT, CH, VL, RB = 128, 8, 4, 16, 16, 256
 KA, QA, SREG, PREG, KBV, QBV, WV, VB, T = 128, 192, 56, 184, 216, 224, 228, 232, 244
-NVB = 3                                   # transposed-V operand buffers (v232-v243)
+NVB = 3                                   # transposed-V operand buffers (v232-v243; set per variant)
 W_LAST = False                            # gate-value load after the K loads (else before)
 
 
@@ -237,10 +238,9 @@ def kbias_lines(off, nv, wpar):
            f"v_readfirstlane_b32 s{S_Y}, {t(7)}",
            "s_nop 1"]
     j, tmp, sel, pk = t(2), t(3), t(6), t(7)
-    skipw = [label("now"), label("now")]
     for kt in range(2):
         word = f"s{S_X}" if kt == 0 else f"s{S_Y}"
-        if kt:
+        if kt and WITH_SO[0]:
             # keys 32 .. 63 (upper lanes of the gate register) to the lower
             # lanes of pk: the swap exchanges tmp's upper and pk's lower half
             out += [f"v_mov_b32 {tmp}, v{WV + wpar}", f"v_mov_b32 {pk}, v{WV + wpar}", "s_nop 1",
@@ -254,14 +254,12 @@ def kbias_lines(off, nv, wpar):
                 f"v_cmp_le_u32 vcc, %[nblk], {j}",
                 f"v_cndmask_b32_e64 {sel}, {sel}, 1, vcc",       # or j >= N
                 f"v_cmp_eq_u32 vcc, %[nm1], {j}",
-                f"v_cndmask_b32 {tmp}, %[bfull], %[blast], vcc", # b_j
-                # second-order term: + w_ij / scale (the gated table row of this
-                # query block; j clamped into the row, keys past N are -inf anyway)
-                "s_cmp_eq_u32 %[so], 0",
-                f"s_cbranch_scc1 {skipw[kt]}",
-                f"v_fma_f32 {tmp}, {f'v{WV + wpar}' if kt == 0 else pk}, %[winv], {tmp}",
-                f"{skipw[kt]}:",
-                f"v_mov_b32 {j}, {tmp}",
+                f"v_cndmask_b32 {tmp}, %[bfull], %[blast], vcc"] # b_j
+        if WITH_SO[0]:
+            # second-order term: + w_ij / scale (the gated table row of this
+            # query block; keys past N are -inf anyway)
+            out.append(f"v_fma_f32 {tmp}, {f'v{WV + wpar}' if kt == 0 else pk}, %[winv], {tmp}")
+        out += [f"v_mov_b32 {j}, {tmp}",
                 f"v_cvt_pk_bf16_f32 {pk}, {j}, {j}",
                 f"v_and_b32 {pk}, 0xffff0000, {pk}",             # hi as fp32
                 f"v_sub_f32 {j}, {j}, {pk}",                      # lo = b - hi (exact)
@@ -309,8 +307,6 @@ def wload_ops(off, nv, wpar):
         f"s_sub_u32 s{S_WRS + 2}, %[wbytes], s{S_Y}",        # 4 N - 256 g (> 0 for a virtual group)
         f"s_bitcmp1_b32 s{nv}, 16",
         f"s_cselect_b32 s{S_WRS + 2}, s{S_WRS + 2}, 0",
-        "s_cmp_eq_u32 %[so], 0",
-        f"s_cselect_b32 s{S_WRS + 2}, 0, s{S_WRS + 2}",
         f"buffer_load_dword v{WV + wpar}, %[wlane], {SR(S_WRS)}, 0 offen"], vm_id=("w", 0))]
 
 
@@ -328,12 +324,12 @@ def vm_list(vl, qk_last_reader, woff, wnv, wpar):
             i = 4 * a + b
             ops.append(Op("vmem", [f"buffer_load_dwordx4 %[voff], {SR(S_VRS)}, {SOFF[4096 * a]} offen offset:{1024 * b} lds"],
                           vm_id=("d", i)))
-    if not W_LAST:
+    if WITH_SO[0] and not W_LAST:
         ops += wload_ops(woff, wnv, wpar)
     for ks in range(KS):
         for kt in range(2):
             ops.append(kload_op(kt, ks, qk_last_reader[(kt, ks)] + 1))
-    if W_LAST:
+    if WITH_SO[0] and W_LAST:
         ops += wload_ops(woff, wnv, wpar)
     return ops
 
@@ -505,7 +501,8 @@ def full_step(par, vm_order):
     assert [o.vm_id for o in vm] == [o.vm_id for o in vm_order]
     # the bias of a virtual item n+1 first (its gate values arrived a step
     # ago), then the softmax of item n
-    valu = [Op("valu", kbias_lines(S_OFFA, S_NVA, 1 - par), before=posq[nq - 1], vneeds=[("w", 0)])]
+    valu = [Op("valu", kbias_lines(S_OFFA, S_NVA, 1 - par), before=posq[nq - 1],
+               vneeds=[("w", 0)] if WITH_SO[0] else [])]
     valu += softmax_ops(par, [posp[8 * gi] for gi in range(4)])
     valu.append(Op("valu", mask_lines(1 - par, S_NVA), after=posq[nq - 1]))
     if TRACK_MAX[0]:
@@ -579,9 +576,10 @@ def program():
     emit(f"s_mov_b32 s{S_NVC}, s{S_NVB}")
     rsrc_item(S_KRS, "k", S_OFFB, S_NVB)
     rsrc_item(S_VRS, "v", S_OFFB, S_NVB)
-    for op in wload_ops(S_OFFB, S_NVB, 0):            # gate values of item 0 (waited with K(0))
-        for ln in op.lines:
-            emit(ln)
+    if WITH_SO[0]:
+        for op in wload_ops(S_OFFB, S_NVB, 0):        # gate values of item 0 (waited with K(0))
+            for ln in op.lines:
+                emit(ln)
     for ks in range(KS):
         for kt in range(2):
             for ln in kload_op(kt, ks, -1).lines:
@@ -630,17 +628,22 @@ def program():
 
 
 TRACK_MAX = [True]
+WITH_SO = [True]
 bodies = {}
-for name, track in (("PISA_ATTN_LOOP_D128_ASM", False), ("PISA_ATTN_LOOP_D128_SAFE_ASM", True)):
+for name, track, so in (("PISA_ATTN_LOOP_D128_ASM", False, False), ("PISA_ATTN_LOOP_D128_SAFE_ASM", True, False),
+                        ("PISA_ATTN_LOOP_D128_SO_ASM", False, True), ("PISA_ATTN_LOOP_D128_SO_SAFE_ASM", True, True)):
     L.clear()
-    TRACK_MAX[0] = track
+    TRACK_MAX[0], WITH_SO[0] = track, so
+    VB, NVB = (232, 3) if so else (228, 4)
     program()
     bodies[name] = list(L)
 clob = ([f'"v{i}"' for i in range(SREG, 256)] + [f'"a{i}"' for i in range(KA, 256)] +
         [f'"s{i}"' for i in SGPRS])
 out = ["// Generated by gen_attn_loop.py (do not edit): the D = 128 item loop of the fused PISA forward for gfx950.",
        "// PISA_ATTN_LOOP_D128_ASM: the row maximum of the first item only (sets the reference);",
-       "// PISA_ATTN_LOOP_D128_SAFE_ASM: the row maximum of every item, the restart flag and the running maximum."]
+       "// PISA_ATTN_LOOP_D128_SAFE_ASM: the row maximum of every item, the restart flag and the running maximum;",
+       "// the _SO_ variants add the gated second-order term to the virtual tokens' logits (a kernel",
+       "// instantiation holds one pair: two pairs in one kernel measured ~15% slower)."]
 for name, body in bodies.items():
     out.append(f"#define {name} \\")
     out.append(" \\\n".join('    "' + l + '\\n"' for l in body))

@@ -180,9 +180,12 @@ __host__ __device__ inline size_t fast_lds_bytes(int D, int N, int second_order,
     return (size_t)8 * kQB * D * (second_order ? 1 : 0) + (size_t)4 * kQB * NP + (size_t)nwv * 4 * 256 +
            (size_t)nwv * kAmbCap * (4 + 8) + (size_t)4 * nwv * ((NP + 31) / 32);
 }
-// Waves per workgroup: rows of more than 1024 blocks fill most of the LDS
-// (one workgroup per CU), so those take eight waves (two per SIMD).
-__host__ __device__ constexpr int route_waves(int kpl) { return kpl > 16 ? 8 : 4; }
+// Waves per workgroup: eight (two per SIMD), each taking two of the 16 score
+// rows. Rows of more than 1024 blocks fill most of the LDS (one workgroup per
+// CU); shorter rows fit two workgroups per CU, and smaller workgroups leave a
+// shorter tail than four-wave ones (measured at N = 512: 118 -> 112 us with
+// 40 heads, 63 -> 54 us with 12, FLUX 45 -> 34 us; same routing).
+__host__ __device__ constexpr int route_waves(int) { return 8; }
 
 // KPL: keys per lane of a score row (N <= 64 KPL); rows of up to 1024 blocks
 // without the second order fit four waves per SIMD.

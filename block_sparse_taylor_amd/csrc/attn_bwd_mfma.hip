@@ -84,6 +84,20 @@ __device__ __forceinline__ uint2 lds_tr16(const unsigned char* p) {
 // is a logit minus the row's log-normaliser, so <= ~0, or -inf).
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// The (block, head) tile of this workgroup in an (x, y) grid, XCD-aware:
+// workgroups are dispatched in linear order (x fastest) and dealt round-robin
+// to the 8 XCDs, so consecutive ids land on different XCDs; this bijection
+// gives each XCD a contiguous range of tiles instead, so that neighbouring
+// blocks of a head (whose routed partners overlap) share that XCD's L2.
+__device__ __forceinline__ void xcd_tile(int* x, int64_t* y) {
+    const int64_t nx = gridDim.x, total = nx * gridDim.y;
+    const int64_t lin = (int64_t)blockIdx.y * nx + blockIdx.x;
+    const int64_t xcd = lin % 8, pos = lin / 8, per = total / 8, rem = total % 8;
+    const int64_t L = xcd < rem ? xcd * (per + 1) + pos : rem * (per + 1) + (xcd - rem) * per + pos;
+    *x = (int)(L % nx);
+    *y = L / nx;
+}
+
 __device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -309,8 +323,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r32 = lane & 31, g = lane >> 5;
     const int kt = wave >> 1, qt = wave & 1;
-    const int64_t bh = blockIdx.y;
-    const int i = blockIdx.x;
+    int i;
+    int64_t bh;
+    xcd_tile(&i, &bh);
     const int t = i * kBlock + qt * 32 + r32;
     const int64_t base = bh * (int64_t)T * D;
     const uint32_t* mrow = mask + (bh * N + i) * (int64_t)NW;
@@ -628,8 +643,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r32 = lane & 31, g = lane >> 5;
     const int kt = wave >> 1, qt = wave & 1;
-    const int64_t bh = blockIdx.y;
-    const int i = blockIdx.x;
+    int i;
+    int64_t bh;
+    xcd_tile(&i, &bh);
     const int t = i * kBlock + qt * 32 + r32;
     const int64_t base = bh * (int64_t)T * D;
     const uint32_t* mrow = mask + (bh * N + i) * (int64_t)NW;
@@ -855,8 +871,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r32 = lane & 31, g = lane >> 5;
     const int kt = wave >> 1, qt = wave & 1;
-    const int64_t bh = blockIdx.y;
-    const int j = blockIdx.x;
+    int j;
+    int64_t bh;
+    xcd_tile(&j, &bh);
     const int key = j * kBlock + kt * 32 + r32;
     const int64_t base = bh * (int64_t)T * D;
     const float c2 = scale * kLog2e;

@@ -84,19 +84,6 @@ __device__ __forceinline__ uint2 lds_tr16(const unsigned char* p) {
 // is a logit minus the row's log-normaliser, so <= ~0, or -inf).
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// The (block, head) tile of this workgroup in an (x, y) grid, XCD-aware:
-// workgroups are dispatched in linear order (x fastest) and dealt round-robin
-// to the 8 XCDs, so consecutive ids land on different XCDs; this bijection
-// gives each XCD a contiguous range of tiles instead, so that neighbouring
-// blocks of a head (whose routed partners overlap) share that XCD's L2.
-__device__ __forceinline__ void xcd_tile(int* x, int64_t* y) {
-    const int64_t nx = gridDim.x, total = nx * gridDim.y;
-    const int64_t lin = (int64_t)blockIdx.y * nx + blockIdx.x;
-    const int64_t xcd = lin % 8, pos = lin / 8, per = total / 8, rem = total % 8;
-    const int64_t L = xcd < rem ? xcd * (per + 1) + pos : rem * (per + 1) + (xcd - rem) * per + pos;
-    *x = (int)(L % nx);
-    *y = L / nx;
-}
 
 __device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -1120,8 +1107,10 @@ __global__ __launch_bounds__(kThreads) void bwd_virt_mfma_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r32 = lane & 31, g = lane >> 5;
     const int kt = wave >> 1, qt = wave & 1;
-    const int64_t bh = blockIdx.y;
-    const int g0 = blockIdx.x * 64;   // the group's first block
+    int gx, zs;   // group, query-range split
+    int64_t bh;
+    xcd_tile(&gx, &bh, &zs);
+    const int g0 = gx * 64;   // the group's first block
     const int j = g0 + kt * 32 + r32;
     const bool jvalid = j < N;
     const int jc = jvalid ? j : N - 1;
@@ -1129,7 +1118,7 @@ __global__ __launch_bounds__(kThreads) void bwd_virt_mfma_kernel(
     const int64_t base = bh * (int64_t)T * D;
     const float c2 = scale * kLog2e;
     const TrAddr ta(lane, C::RB, C::SWM);
-    const int i0 = blockIdx.z * i_per_split, i1 = min(N, i0 + i_per_split);
+    const int i0 = zs * i_per_split, i1 = min(N, i0 + i_per_split);
     const int nvg = min(64, N - g0);
     const uint64_t gvalid = nvg == 64 ? ~0ull : (1ull << nvg) - 1ull;   // the group's blocks below N
 
@@ -1245,7 +1234,7 @@ __global__ __launch_bounds__(kThreads) void bwd_virt_mfma_kernel(
     }
     // the two query halves of each block tile: wave (kt, 1) hands its partials to wave (kt, 0)
     float* xs = reinterpret_cast<float*>(tqo0);
-    const int64_t pbase = ((int64_t)blockIdx.z * gridDim.y + bh) * N * (int64_t)D;
+    const int64_t pbase = ((int64_t)zs * gridDim.y + bh) * N * (int64_t)D;
 #pragma unroll
     for (int pass = 0; pass < 2; ++pass) {
         f32x16_t* acc = pass == 0 ? dva : dka;

@@ -57,6 +57,21 @@ struct Forced {
     __host__ __device__ bool forced(int j) const { return (j >= lo && j <= hi) || j < ns; }
 };
 
+// The tile (x, y, z) of this workgroup in its grid, XCD-aware: workgroups are
+// dispatched in linear order (x fastest) and dealt round-robin to the 8 XCDs,
+// so consecutive ids land on different XCDs; this bijection of the linear ids
+// gives each XCD a contiguous range of tiles instead, so that neighbouring
+// tiles (blocks of one head, whose operands overlap) share that XCD's L2.
+__device__ __forceinline__ void xcd_tile(int* x, int64_t* y, int* z = nullptr) {
+    const int64_t nx = gridDim.x, ny = gridDim.y, total = nx * ny * gridDim.z;
+    const int64_t lin = ((int64_t)blockIdx.z * ny + blockIdx.y) * nx + blockIdx.x;
+    const int64_t xcd = lin % 8, pos = lin / 8, per = total / 8, rem = total % 8;
+    const int64_t L = xcd < rem ? xcd * (per + 1) + pos : rem * (per + 1) + (xcd - rem) * per + pos;
+    *x = (int)(L % nx);
+    *y = (L / nx) % ny;
+    if (z) *z = (int)(L / (nx * ny));
+}
+
 // What the kernels read and write: the caller's statistics (pisa_stats_t)
 // and the views of its operand buffer (the kernels' own layouts of them).
 struct StatsView {

@@ -258,6 +258,25 @@ def test_bf16_query_blocks_beyond_one_chunk():
     check(w, seed=14, topk=6, idx_fn=force5)
 
 
+def test_bf16_bit31_of_mask_words_routed_contract():
+    """N = 100: every query block is routed to blocks 31 and 95, bit 31 of
+    the first mask word of virtual-token groups 0 and 1 (the virtual-token
+    kernel joins a group's two 32-bit words into one 64-bit selection; a
+    word taken as signed would mark the group's upper 32 blocks exact and
+    drop their virtual-token gradients)."""
+    w = wl("tiny", seq_len=64 * 100, head_dim=128, heads=1, dtype="bf16")
+
+    def force(idx):
+        x = idx.cpu().clone()
+        for i in range(x.shape[2]):
+            row = x[0, 0, i]
+            for slot, j in enumerate((31, 95)):
+                if abs(i - j) > 1 and not bool((row == j).any()):
+                    row[slot] = j
+        return x.to(idx.device)
+    check(w, seed=21, topk=4, idx_fn=force, contract=True)
+
+
 def test_every_block_exact():
     w = wl("tiny", seq_len=640, head_dim=128, heads=1)
     check(w, seed=9, topk=8, band=1)   # N = 10: every candidate routed

@@ -128,46 +128,81 @@ __device__ __forceinline__ Key wave_radix_select(int n, int need, KeyFn key, Tak
 }
 
 // The need-th largest of the wave's 32-bit keys (KPL per lane, in registers;
-// 0 marks an excluded slot, below every real key), to within `width` in value:
-// a bitwise search from the top bit down, counting keys >= the candidate with
-// ballots (no atomics). After bit b the answer lies in [t, t | (2^b - 1)]; the
-// search stops as soon as that interval spans at most `width` in value (the
-// caller settles everything within its error bound of the interval exactly)
-// or exactly `need` keys reach the candidate (the answer is then the smallest
-// of them, a wave minimum). Returns the interval in *lo, *hi.
+// 0 marks an excluded slot, below every real key), to within `width` in value.
+// The search keeps a key interval [L, H] that holds the answer, with
+// cL = #keys >= L >= need > cH = #keys > H, and probes one key c in (L, H]
+// per step, counting the keys >= c with ballots (no atomics). The probe is
+// a false-position step on the counts: the value at which a uniform spread
+// of the keys between unkey(L) and unkey(H) would put the need-th largest,
+// with the Illinois rule (an end kept twice in a row has its rank distance
+// halved, so both ends move); after 24 steps the probes are value midpoints.
+// A probe that would not split the interval is replaced by the key midpoint.
+// It stops when the interval spans at most `width` in value (the caller
+// settles everything within its error bound of the interval exactly), when
+// L = H, or when exactly `need` keys reach L (the answer is then the smallest
+// of them, a wave minimum). Real keys are those of finite floats, so unkey()
+// of any key in [L, H] is finite. Returns the interval in *lo, *hi.
 constexpr int kKeysPerLane = 36;       // the fast kernel's rows: N <= 64 * 36
 template <int KPL>
 __device__ __forceinline__ void wave_select32(const uint32_t (&kv)[KPL], int need, float width, uint32_t* lo,
                                               uint32_t* hi) {
-    uint32_t t = 0;
-    for (int b = 31; b >= 0; --b) {
-        const uint32_t cand = t | (1u << b);
-        int cnt = 0;
+    auto count_ge = [&](uint32_t c) {
+        int n = 0;
 #pragma unroll
-        for (int i = 0; i < KPL; ++i) cnt += __popcll(__ballot(kv[i] >= cand));
-        if (cnt >= need) {
-            t = cand;
-            if (cnt == need) {
-                uint32_t mn = 0xFFFFFFFFu;
+        for (int i = 0; i < KPL; ++i) n += __popcll(__ballot(kv[i] >= c));
+        return n;
+    };
+    auto min_ge = [&](uint32_t c) {   // the smallest key >= c, a wave minimum
+        uint32_t mn = 0xFFFFFFFFu;
 #pragma unroll
-                for (int i = 0; i < KPL; ++i) mn = kv[i] >= t ? min(mn, kv[i]) : mn;
+        for (int i = 0; i < KPL; ++i) mn = kv[i] >= c ? min(mn, kv[i]) : mn;
 #pragma unroll
-                for (int off = 32; off > 0; off >>= 1) mn = min(mn, (uint32_t)__shfl_xor((int)mn, off));
-                *lo = *hi = mn;
-                return;
-            }
+        for (int off = 32; off > 0; off >>= 1) mn = min(mn, (uint32_t)__shfl_xor((int)mn, off));
+        return mn;
+    };
+    uint32_t mx = 0u;
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) mx = max(mx, kv[i]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off));
+    uint32_t L = min_ge(1u), H = mx;   // the smallest and largest real keys
+    int cL = count_ge(L), cH = 0;
+    float wl = 1.f, wh = 1.f;   // Illinois weights of the two ends' rank distances
+    int last = 0;               // the end the previous step moved: 1 = L, 2 = H
+    for (int step = 0; step < 80; ++step) {
+        if (cL == need) {
+            *lo = *hi = min_ge(L);
+            return;
         }
-        if (b > 0) {
-            const uint32_t top = t | ((1u << b) - 1u);
-            // both ends real scores of one sign region; NaN (key 0) never passes
-            if (t >= 0x00800000u && unkey32(top) - unkey32(t) <= width) {
-                *lo = t;
-                *hi = top;
-                return;
-            }
+        if (L == H) break;
+        const float fl = unkey32(L), fh = unkey32(H);
+        if (fh - fl <= width) break;
+        float x;
+        if (step < 24) {
+            const float dl = (float)(cL - need) * wl, dh = (float)(need - cH) * wh;
+            x = fh - (fh - fl) * (dh / (dl + dh));
+        } else {
+            x = 0.5f * fl + 0.5f * fh;
+        }
+        uint32_t c = key32(x);
+        if (c <= L || c > H) c = L + ((H - L) >> 1) + 1u;   // progress: L < c <= H
+        const int n = count_ge(c);
+        if (n >= need) {
+            L = c;
+            cL = n;
+            wh = last == 1 ? 0.5f * wh : 1.f;
+            wl = 1.f;
+            last = 1;
+        } else {
+            H = c - 1u;
+            cH = n;
+            wl = last == 2 ? 0.5f * wl : 1.f;
+            wh = 1.f;
+            last = 2;
         }
     }
-    *lo = *hi = t;
+    *lo = L;
+    *hi = H;
 }
 
 // LDS of the fast kernel: the fp64 pooled q'^2 rows (second order only), fp32

@@ -188,6 +188,39 @@ def test_long_sequence_routing(second_order):
     assert np.array_equal(idx.cpu().numpy()[0, 0], ref)
 
 
+@pytest.mark.parametrize("N", [300, 1100])
+@pytest.mark.parametrize("second_order", [False, True])
+def test_routing_exact_ties(N, second_order):
+    """Exact score ties at the selection threshold: the keys of block j repeat
+    those of block j mod 7, and q and k hold multiples of 1/8 in [-1/8, 1/8]
+    (exact in bf16), so block means, variances and every score are exact in
+    float64 whatever the summation order, and each query block's scores take
+    at most 7 values, ~N/7 blocks each. The threshold then falls inside a tie
+    group (43 members at N = 300; 157 at N = 1100, more than the 64 close
+    calls a row ranks pairwise, so the 64-bit radix path runs), and the
+    routing must take the group's lowest block ids, as the oracle does."""
+    T, D, topk = 64 * N, 64, 20
+    say(f"[gpu] routing exact ties N={N} so={second_order}")
+    r = np.random.default_rng(N + second_order)
+    q = r.integers(-1, 2, (1, 1, T, D)) / 8.0
+    base = r.integers(-1, 2, (7, 64, D)) / 8.0
+    k = base[np.arange(N) % 7].reshape(1, 1, T, D)
+    v = r.standard_normal((1, 1, T, D))
+    dev = [torch.from_numpy(a).to(torch.bfloat16).cuda().contiguous() for a in (q, k, v)]
+    st = P.pisa_block_stats(*dev, second_order=second_order)
+    idx, _ = P.pisa_route_topk(dev[0], st, topk, band=1, second_order=second_order)
+    torch.cuda.synchronize()
+    s = 1 / math.sqrt(D)
+    ks = O.kv_block_stats(k[0, 0], v[0, 0], 64)
+    qbar, q2bar = O.pool_queries(q[0, 0], 64, s)
+    wr = O.second_order_w(q2bar, ks.sig2, 64)[2] if second_order else None
+    ref, sc = O.route_topk(qbar, ks.kbar, s, topk, 1, wr)
+    # the threshold does fall inside a tie group in most rows
+    tied = sum(int(np.sum(row == np.sort(row)[::-1][topk + 2])) > 1 for row in sc)
+    assert tied > N // 2, tied
+    assert np.array_equal(idx.cpu().numpy()[0, 0], ref)
+
+
 @pytest.mark.parametrize("D", [128, 64])
 @pytest.mark.parametrize("second_order", [False, True])
 def test_wide_logit_range_restarts(D, second_order):

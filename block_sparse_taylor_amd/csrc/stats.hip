@@ -82,17 +82,19 @@ __device__ __forceinline__ void write_knorm(const float* kb_s, float* knorm, int
     if (threadIdx.x == 0) knorm[bh * ((N + 15) / 16) * 16 + j] = (float)(sqrt(s) * (1.0 + 1e-6));
 }
 
-// Column statistics of one block from its LDS tiles (row pitch ld).
-template <typename T, int D>
+// Column statistics of one block from its LDS tiles (row pitch ld). The
+// sums of squares (the pooled q'^2 and the key variances) only with the
+// second-order term (SO).
+template <typename T, int D, bool SO>
 __device__ __forceinline__ void column_stats(const T* tq, const T* tk, const T* tv, int ld, int rows,
-                                             int64_t bh, int j, int n_blocks, int second_order, double s64,
+                                             int64_t bh, int j, int n_blocks, double s64,
                                              const StatsOut& out, double* red, float* kb_s,
                                              float* vs_s) {
     constexpr int H = kThreads / D;           // threads per column
     constexpr int RH = kBlock / H;            // rows per thread
     const int tid = threadIdx.x;
     const int c = tid % D, h = tid / D;
-    const double shift = (double)load_f32(tk + c);   // block row 0 of this key column
+    const double shift = SO ? (double)load_f32(tk + c) : 0.0;   // block row 0 of this key column
     double sq = 0.0, sq2 = 0.0, sk = 0.0, skx = 0.0, skx2 = 0.0, sv = 0.0;
     const int n0 = h * RH, n1 = min(rows, n0 + RH);
     for (int n = n0; n < n1; ++n) {
@@ -100,29 +102,35 @@ __device__ __forceinline__ void column_stats(const T* tq, const T* tk, const T* 
         const double xk = (double)load_f32(tk + n * ld + c);
         const double xv = (double)load_f32(tv + n * ld + c);
         sq += xq;
-        const double yq = s64 * xq;
-        sq2 += yq * yq;
         sk += xk;
-        const double dk = xk - shift;
-        skx += dk;
-        skx2 += dk * dk;
         sv += xv;
+        if (SO) {
+            const double yq = s64 * xq;
+            sq2 += yq * yq;
+            const double dk = xk - shift;
+            skx += dk;
+            skx2 += dk * dk;
+        }
     }
     double* r = red + tid;
     r[0 * kThreads] = sq;
-    r[1 * kThreads] = sq2;
     r[2 * kThreads] = sk;
-    r[3 * kThreads] = skx;
-    r[4 * kThreads] = skx2;
     r[5 * kThreads] = sv;
+    if (SO) {
+        r[1 * kThreads] = sq2;
+        r[3 * kThreads] = skx;
+        r[4 * kThreads] = skx2;
+    }
     __syncthreads();
     if (tid < D) {
         double a[6];
 #pragma unroll
         for (int s = 0; s < 6; ++s) {
             double x = 0.0;
+            if (SO || s == 0 || s == 2 || s == 5) {
 #pragma unroll
-            for (int hh = 0; hh < H; ++hh) x += red[s * kThreads + hh * D + tid];
+                for (int hh = 0; hh < H; ++hh) x += red[s * kThreads + hh * D + tid];
+            }
             a[s] = x;
         }
         const double n = (double)rows;
@@ -147,7 +155,7 @@ __device__ __forceinline__ void column_stats(const T* tq, const T* tk, const T* 
         static_cast<T*>(out.vbar_c)[off + c] = store_cast<T>((float)((double)vs / n));
         kb_s[c] = (float)mean;
         vs_s[c] = (float)a[5];
-        if (second_order) {
+        if (SO) {
             out.q2bar[off + c] = a[1] / n;
             const double mx = a[3] / n;
             const double s2 = fmax(a[4] / n - mx * mx, 0.0);
@@ -158,15 +166,34 @@ __device__ __forceinline__ void column_stats(const T* tq, const T* tk, const T* 
 }
 
 // ---------------------------------------------------------------- bf16 path (MFMA)
+// An MFMA operand of 8 bf16 k-values from a row-major LDS tile (row pitch LD
+// elements) by two transposed reads: lane l (tile column c0 + l % 32) gets
+// rows r0 + 4 g + (0..3) and r0 + 8 + 4 g + (0..3), g = l / 32. Lanes address
+// 4 consecutive elements of one row each: within a group of 16 lanes, lane
+// 4 a + b reads row 4 g + a at columns 16 (l / 16 % 2) + 4 b .. + 3.
+template <int LD>
+__device__ __forceinline__ bf16x8_t tr_operand(const bf16_t* tile, int r0, int c0, int lane) {
+    typedef short v4i16_t __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4i16_t lds_v4i16;
+    const int tri = lane & 15;
+    const int row = r0 + 4 * (lane >> 5) + (tri >> 2);
+    const int col = c0 + 16 * ((lane >> 4) & 1) + 4 * (tri & 3);
+    const bf16_t* p = tile + row * LD + col;
+    const v4i16_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
+    const v4i16_t y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + 8 * LD));
+    const uint2 ux = __builtin_bit_cast(uint2, x), uy = __builtin_bit_cast(uint2, y);
+    return __builtin_bit_cast(bf16x8_t, make_uint4(ux.x, ux.y, uy.x, uy.y));
+}
+
 // 32x32x16 bf16 MFMA operand layout (lane l, element e in 0..7):
 //   A[m = l%32][k = 8(l/32) + e],  B[k = 8(l/32) + e][n = l%32]
 //   C[m = 8(i/4) + 4(l/32) + i%4][n = l%32] for accumulator register i.
 // C[a][b] += sum_t K[t][a] V[t][b]: A = K^T and B = V, both gathered
 // column-wise from the row-major LDS tiles.
-template <int D>
+template <int D, bool SO>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void stats_bf16_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, int T,
-    int N, int bpw, int second_order, double s64, StatsOut out, float* __restrict__ hpart) {
+    int N, int bpw, double s64, StatsOut out, float* __restrict__ hpart) {
     constexpr int LD = D + kPad;
     constexpr int CH = D / 8;                       // 16-byte chunks per row
     constexpr int LOADS = kBlock * CH / kThreads;   // uint4 loads per thread per tensor
@@ -249,26 +276,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             }
         }
 
-        // acc += K_j^T V_j  (rows >= `rows` are zero in LDS)
+        // acc += K_j^T V_j  (rows >= `rows` are zero in LDS). Both operands by
+        // the gfx950 transposed LDS read (ds_read_b64_tr_b16): lane l receives
+        // column l % 32 of a 32-column tile at 4 consecutive rows; the two
+        // reads of a 16-row k-step cover rows 4 (l / 32) + (0..3) and
+        // 8 + 4 (l / 32) + (0..3), the same order of k for A = K^T and B = V.
         const int m = lane & 31, hi = lane >> 5;
 #pragma unroll
         for (int ks = 0; ks < kBlock / 16; ++ks) {
-            const int t0 = ks * 16 + hi * 8;
 #pragma unroll
             for (int t = 0; t < TPW; ++t) {
                 const int tile = wave * TPW + t;
                 const int mt = tile / NT, nt = tile % NT;
-                bf16x8_t a, b;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    a[e] = __builtin_bit_cast(__bf16, sk[(t0 + e) * LD + mt * 32 + m]);
-                    b[e] = __builtin_bit_cast(__bf16, sv[(t0 + e) * LD + nt * 32 + m]);
-                }
+                const bf16x8_t a = tr_operand<LD>(sk, ks * 16, mt * 32, lane);
+                const bf16x8_t b = tr_operand<LD>(sv, ks * 16, nt * 32, lane);
                 acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[t], 0, 0, 0);
             }
         }
 
-        column_stats<bf16_t, D>(sq, sk, sv, LD, rows, bh, j, N, second_order, s64, out, red, kb_s, vs_s);
+        column_stats<bf16_t, D, SO>(sq, sk, sv, LD, rows, bh, j, N, s64, out, red, kb_s, vs_s);
         __syncthreads();  // kb_s / vs_s visible
         write_knorm<D>(kb_s, out.knorm, bh, j, N);
         // acc -= kbar_j (x) V-hat_j
@@ -342,8 +368,8 @@ __global__ __launch_bounds__(kThreads) void stats_f32_kernel(
             sv[row * LD + col] = ok ? v[o] : 0.f;
         }
         __syncthreads();
-        column_stats<float, D>(sq, sk, sv, LD, rows, bh, j, N, second_order, s64, out, red,
-                               kb_s, vs_s);
+        if (second_order) column_stats<float, D, true>(sq, sk, sv, LD, rows, bh, j, N, s64, out, red, kb_s, vs_s);
+        else column_stats<float, D, false>(sq, sk, sv, LD, rows, bh, j, N, s64, out, red, kb_s, vs_s);
         __syncthreads();  // kb_s visible
         write_knorm<D>(kb_s, out.knorm, bh, j, N);
         // partial H in fp64 from the exact products and exact column sums
@@ -537,18 +563,28 @@ hipError_t launch_block_stats(const Geom& g, int dtype, int second_order, int co
     StatsOut out{st->qbar, st->q2bar, st->kbar, st->vsum, st->ksig2, st->kbar_c, st->vbar_c, st->kpack,
                  dtype == PISA_BF16 ? st->kbpack : nullptr, st->kbar_r,
                  second_order ? st->ksig2_r : nullptr, st->knorm};
-#define PISA_STATS_LAUNCH(KERN, TT, DD)                                                            \
-    hipLaunchKernelGGL(KERN<DD>, grid, block, 0, stream, static_cast<const TT*>(q),               \
-                       static_cast<const TT*>(k), static_cast<const TT*>(v), g.T, g.N, bpw,       \
+#define PISA_STATS_BF16(DD, SO)                                                                    \
+    hipLaunchKernelGGL((stats_bf16_kernel<DD, SO>), grid, block, 0, stream,                       \
+                       static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),              \
+                       static_cast<const bf16_t*>(v), g.T, g.N, bpw, g.scale64, out, hpart)
+#define PISA_STATS_F32(DD)                                                                         \
+    hipLaunchKernelGGL(stats_f32_kernel<DD>, grid, block, 0, stream, static_cast<const float*>(q), \
+                       static_cast<const float*>(k), static_cast<const float*>(v), g.T, g.N, bpw, \
                        second_order, g.scale64, out, hpart)
     if (dtype == PISA_BF16) {
-        if (g.D == 128) PISA_STATS_LAUNCH(stats_bf16_kernel, bf16_t, 128);
-        else PISA_STATS_LAUNCH(stats_bf16_kernel, bf16_t, 64);
+        if (g.D == 128) {
+            if (second_order) PISA_STATS_BF16(128, true);
+            else PISA_STATS_BF16(128, false);
+        } else {
+            if (second_order) PISA_STATS_BF16(64, true);
+            else PISA_STATS_BF16(64, false);
+        }
     } else {
-        if (g.D == 128) PISA_STATS_LAUNCH(stats_f32_kernel, float, 128);
-        else PISA_STATS_LAUNCH(stats_f32_kernel, float, 64);
+        if (g.D == 128) PISA_STATS_F32(128);
+        else PISA_STATS_F32(64);
     }
-#undef PISA_STATS_LAUNCH
+#undef PISA_STATS_BF16
+#undef PISA_STATS_F32
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int DD = g.D * g.D;

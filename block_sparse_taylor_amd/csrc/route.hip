@@ -263,6 +263,18 @@ __global__ __launch_bounds__(64 * route_waves(KPL)) __attribute__((amdgpu_waves_
         __syncthreads();
     }
     const double* qrows = qbar + (bh * N + i0) * (int64_t)D;   // fp64 pooled queries of the tile
+    // the pooled query of each row this wave selects for (dims 2 lane, 2 lane
+    // + 1), loaded now so that the loads overlap the score products (with the
+    // covariance prior, whose kernels hold fewer free registers, per row)
+    constexpr int RPW = COV ? 1 : (kQB + NWV - 1) / NWV;   // rows per wave preloaded
+    auto load_q = [&](int r) {
+        d2_t x = {0.0, 0.0};
+        if (r < nq && 2 * lane < D) x = *reinterpret_cast<const d2_t*>(qrows + (int64_t)r * D + 2 * lane);
+        return x;
+    };
+    d2_t qpre[RPW];
+#pragma unroll
+    for (int rr = 0; rr < RPW; ++rr) qpre[rr] = COV ? d2_t{0.0, 0.0} : load_q(wave + rr * NWV);
 
     // ---- scores: S[r][j] = s qbar_r . kbar_j (+ min(w, ln B)) (+ prior) via
     // bf16 MFMA 16x16x32 on operands split into hi + lo (hi.hi + hi.lo + lo.hi:
@@ -412,7 +424,7 @@ __global__ __launch_bounds__(64 * route_waves(KPL)) __attribute__((amdgpu_waves_
     double* amb_r = amb_r_s + wave * kAmbCap;
     uint32_t* tbits = take_s + wave * NW;
     const unsigned long long lt_mask = (1ull << lane) - 1ull;
-    auto row_pass = [&](int r) {
+    auto row_pass = [&](int r, d2_t qpair) {   // qpair: dims 2 lane, 2 lane + 1 of the row's pooled query
         const int i = i0 + r;
         int32_t* out = idx + (bh * N + i) * (int64_t)topk;
         const Forced fs(i, band, n_sink, N);
@@ -430,8 +442,7 @@ __global__ __launch_bounds__(64 * route_waves(KPL)) __attribute__((amdgpu_waves_
                 const float x = sr[min(j, N - 1)];
                 kv[t] = j < N && is_cand(j) ? key32(x) : 0u;
             }
-            double qn = 0.0;
-            for (int d = lane; d < D; d += 64) qn += qg[d] * qg[d];
+            double qn = fma(qpair.x, qpair.x, qpair.y * qpair.y);
 #pragma unroll
             for (int off = 32; off > 0; off >>= 1) qn += __shfl_xor(qn, off);
             // |r| bound: the dot product, the clamped spread, the prior (the
@@ -477,27 +488,41 @@ __global__ __launch_bounds__(64 * route_waves(KPL)) __attribute__((amdgpu_waves_
             // two dims (one 16-byte load, contiguous across lanes), then a
             // wave reduction (the fp64 sum in another order; decisions stay
             // those of float64 up to near-exact ties)
-            d2_t qpair = {0.0, 0.0};
-            if (2 * lane < D) qpair = *reinterpret_cast<const d2_t*>(qg + 2 * lane);
-            auto exact_wave = [&](int j) {
-                double dot = 0.0, w = 0.0;
-                if (2 * lane < D) {
-                    const d2_t x = *reinterpret_cast<const d2_t*>(kb + (int64_t)j * D + 2 * lane);
-                    dot = fma(qpair.x, x.x, qpair.y * x.y);
-                    if (second_order) {
-                        const d2_t y = *reinterpret_cast<const d2_t*>(sg + (int64_t)j * D + 2 * lane);
-                        w = fma(q2_s[r * D + 2 * lane], y.x, q2_s[r * D + 2 * lane + 1] * y.y);
+            // CB close calls at a time: all their loads first, then the
+            // products and the wave sums (two with the covariance prior,
+            // whose kernels hold fewer free registers)
+            constexpr int CB = COV ? 2 : 4;
+            auto exact_batch = [&](const int (&j)[CB], double (&rr)[CB]) {
+                d2_t x[CB], y[CB];
+#pragma unroll
+                for (int u = 0; u < CB; ++u) {
+                    x[u] = y[u] = d2_t{0.0, 0.0};
+                    if (2 * lane < D) {
+                        x[u] = *reinterpret_cast<const d2_t*>(kb + (int64_t)j[u] * D + 2 * lane);
+                        if (second_order) y[u] = *reinterpret_cast<const d2_t*>(sg + (int64_t)j[u] * D + 2 * lane);
                     }
                 }
+                double dot[CB], w[CB];
 #pragma unroll
-                for (int off = 32; off > 0; off >>= 1) {
-                    dot += __shfl_xor(dot, off);
-                    if (second_order) w += __shfl_xor(w, off);
+                for (int u = 0; u < CB; ++u) {
+                    dot[u] = fma(qpair.x, x[u].x, qpair.y * x[u].y);
+                    w[u] = second_order && 2 * lane < D
+                               ? fma(q2_s[r * D + 2 * lane], y[u].x, q2_s[r * D + 2 * lane + 1] * y[u].y)
+                               : 0.0;
                 }
-                double rr = s64 * dot;
-                if (second_order) rr += fmin(0.5 * w, lnB);
-                if (COV) rr += cov_prior(hn, j);
-                return rr;
+#pragma unroll
+                for (int off = 32; off > 0; off >>= 1)
+#pragma unroll
+                    for (int u = 0; u < CB; ++u) {
+                        dot[u] += __shfl_xor(dot[u], off);
+                        if (second_order) w[u] += __shfl_xor(w[u], off);
+                    }
+#pragma unroll
+                for (int u = 0; u < CB; ++u) {
+                    rr[u] = s64 * dot[u];
+                    if (second_order) rr[u] += fmin(0.5 * w[u], lnB);
+                    if (COV) rr[u] += cov_prior(hn, j[u]);
+                }
             };
             auto ambiguous = [&](int j) {
                 const uint32_t x = key32(sr[j]);
@@ -512,14 +537,19 @@ __global__ __launch_bounds__(64 * route_waves(KPL)) __attribute__((amdgpu_waves_
                 for (int w = lane; w < NW; w += 64) tbits[w] = 0u;
                 double rmine = 0.0;
                 int jmine = -1;
-                for (int c = 0; c < ca; ++c) {     // ca <= kAmbCap here; uniform
-                    const int jc = amb_j[c];
-                    const double rc = exact_wave(jc);
-                    if (lane == c) {
-                        jmine = jc;
-                        rmine = rc;
-                        amb_r[c] = rc;
-                    }
+                for (int c0 = 0; c0 < ca; c0 += CB) {     // ca <= kAmbCap here; uniform
+                    int jc[CB];
+                    double rc[CB];
+#pragma unroll
+                    for (int u = 0; u < CB; ++u) jc[u] = amb_j[min(c0 + u, ca - 1)];
+                    exact_batch(jc, rc);
+#pragma unroll
+                    for (int u = 0; u < CB; ++u)
+                        if (c0 + u < ca && lane == c0 + u) {
+                            jmine = jc[u];
+                            rmine = rc[u];
+                            amb_r[c0 + u] = rc[u];
+                        }
                 }
                 __builtin_amdgcn_wave_barrier();
                 __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -570,7 +600,14 @@ __global__ __launch_bounds__(64 * route_waves(KPL)) __attribute__((amdgpu_waves_
         }
         for (int c = written + lane; c < topk; c += 64) out[c] = -1;
     };
-    for (int r = wave; r < nq; r += NWV) row_pass(r);
+    for (int r = wave; r < nq; r += NWV) {
+        d2_t qp = qpre[0];
+#pragma unroll
+        for (int rr = 1; rr < RPW; ++rr)
+            if (r == wave + rr * NWV) qp = qpre[rr];
+        if (COV) qp = load_q(r);
+        row_pass(r, qp);
+    }
 }
 
 // General fallback for long sequences (score rows beyond the LDS): one workgroup per

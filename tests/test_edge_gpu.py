@@ -221,6 +221,77 @@ def test_routing_exact_ties(N, second_order):
     assert np.array_equal(idx.cpu().numpy()[0, 0], ref)
 
 
+@pytest.mark.parametrize("second_order", [False, True])
+def test_routing_scores_across_many_binades(second_order):
+    """Key block j scaled by 2^((7 j mod 24) - 12): the block scores of a row
+    span ~32 binades (a CPU model of the router's threshold search takes
+    ~13.5 count passes per row on these rows, up to 20). The routing equals
+    the oracle's float64 ranking, up to near-exact ties (gap below 1e-9 of
+    the k-th score: the two sum the fp64 products in another order)."""
+    T, D, topk = 64 * 600, 128, 40
+    N = T // 64
+    say(f"[gpu] routing across binades N={N} so={second_order}")
+    r = np.random.default_rng(600 + second_order)
+    scale_j = 2.0 ** ((7 * np.arange(N)) % 24 - 12)
+    q = r.standard_normal((1, 1, T, D))
+    k = (r.standard_normal((N, 64, D)) * scale_j[:, None, None]).reshape(1, 1, T, D)
+    v = r.standard_normal((1, 1, T, D))
+    dev = [torch.from_numpy(a).to(torch.bfloat16).cuda().contiguous() for a in (q, k, v)]
+    host = [t.double().cpu().numpy() for t in dev]   # exact values the GPU sees
+    st = P.pisa_block_stats(*dev, second_order=second_order)
+    idx, _ = P.pisa_route_topk(dev[0], st, topk, band=1, second_order=second_order)
+    torch.cuda.synchronize()
+    s = 1 / math.sqrt(D)
+    ks = O.kv_block_stats(host[1][0, 0], host[2][0, 0], 64)
+    qbar, q2bar = O.pool_queries(host[0][0, 0], 64, s)
+    wr = O.second_order_w(q2bar, ks.sig2, 64)[2] if second_order else None
+    ref, sc = O.route_topk(qbar, ks.kbar, s, topk, 1, wr)
+    got = idx.cpu().numpy()[0, 0]
+    diffs = 0
+    for i in range(N):
+        if np.array_equal(got[i], ref[i]):
+            continue
+        gs, rs = set(got[i][got[i] >= 0].tolist()), set(ref[i][ref[i] >= 0].tolist())
+        assert len(gs) == len(rs), i
+        kth = min(sc[i, j] for j in rs)
+        for j in gs ^ rs:
+            assert abs(sc[i, j] - kth) <= 1e-9 * (1 + abs(kth)), (i, j, sc[i, j], kth)
+        diffs += len(gs - rs)
+    say(f"[gpu]   {diffs} near-tie differences over {N} rows")
+
+
+@pytest.mark.parametrize("second_order", [False, True])
+def test_routing_power_of_two_scores(second_order):
+    """Every query row is e_1 and key block j is constant with first
+    coordinate 2^e_j, e_j uniform in [-20, 20): each score s 2^e_j is exact in
+    float64 and fp32, the 600 scores of a row take 40 values across 40
+    binades with ~15 exact ties each, and the variances are zero. On such
+    rows false position converges slowly: a CPU model of the router's
+    threshold search needs more than 24 count passes on most rows at topk 40,
+    so the search's value-bisection fallback runs. The routing must equal the
+    oracle's (ties: lower block id)."""
+    T, D, topk = 64 * 600, 128, 40
+    N = T // 64
+    say(f"[gpu] routing power-of-two scores N={N} so={second_order}")
+    e = np.random.default_rng(0).integers(-20, 20, N)
+    q = np.zeros((1, 1, T, D))
+    q[..., 0] = 1.0
+    k = np.zeros((N, 64, D))
+    k[:, :, 0] = (2.0 ** e)[:, None]
+    k = k.reshape(1, 1, T, D)
+    v = np.random.default_rng(1).standard_normal((1, 1, T, D))
+    dev = [torch.from_numpy(a).to(torch.bfloat16).cuda().contiguous() for a in (q, k, v)]
+    st = P.pisa_block_stats(*dev, second_order=second_order)
+    idx, _ = P.pisa_route_topk(dev[0], st, topk, band=1, second_order=second_order)
+    torch.cuda.synchronize()
+    s = 1 / math.sqrt(D)
+    ks = O.kv_block_stats(k[0, 0], v[0, 0], 64)
+    qbar, q2bar = O.pool_queries(q[0, 0], 64, s)
+    wr = O.second_order_w(q2bar, ks.sig2, 64)[2] if second_order else None
+    ref, _ = O.route_topk(qbar, ks.kbar, s, topk, 1, wr)
+    assert np.array_equal(idx.cpu().numpy()[0, 0], ref)
+
+
 @pytest.mark.parametrize("D", [128, 64])
 @pytest.mark.parametrize("second_order", [False, True])
 def test_wide_logit_range_restarts(D, second_order):

@@ -46,7 +46,11 @@ __device__ __forceinline__ void nt_store(void* p, uint4 v) {
 }
 
 
-constexpr int kPad = 4;   // LDS row padding (elements): rows 8 apart fall on disjoint bank halves
+// LDS row padding of the bf16 tiles (elements): a row pitch of 328 bytes
+// (D = 128) or 200 (D = 64), an odd multiple of 8 bytes, so the 32 rows one
+// packed-K read covers (8 bytes each) fall on distinct bank pairs, and the 4
+// rows of a half-wave's transposed operand read overlap in few banks.
+constexpr int kPad = 36;
 // Blocks per workgroup: the (head, block range) workgroups of one call should
 // all be resident at once. Two of these workgroups fit on a CU and MI355X has
 // 256 CUs, so a head gets max(1, 512 / heads) ranges of at least 4 blocks

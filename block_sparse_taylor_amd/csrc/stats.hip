@@ -137,10 +137,13 @@ __device__ __forceinline__ void column_stats(const T* tq, const T* tk, const T* 
             }
             a[s] = x;
         }
+        // x / rows; for a full block the exact product with 2^-6 (the same
+        // correctly rounded value, without a division)
         const double n = (double)rows;
-        const double mean = a[2] / n;
+        auto per_row = [&](double x) { return rows == kBlock ? x * 0x1p-6 : x / n; };
+        const double mean = per_row(a[2]);
         const int64_t off = (bh * n_blocks + j) * D;
-        out.qbar[off + c] = a[0] / n;
+        out.qbar[off + c] = per_row(a[0]);
         out.kbar[off + c] = mean;
         const int64_t rhead = bh * router_head_elems(n_blocks, D);
         router_store(out.kbar_r + rhead, j, c, D, mean);
@@ -156,13 +159,13 @@ __device__ __forceinline__ void column_stats(const T* tq, const T* tk, const T* 
         out.vsum[off + c] = vs;
         // the virtual token's value from the stored fp32 V-hat (as
         // prepare_operands_kernel forms it from a caller's statistics)
-        static_cast<T*>(out.vbar_c)[off + c] = store_cast<T>((float)((double)vs / n));
+        static_cast<T*>(out.vbar_c)[off + c] = store_cast<T>((float)per_row((double)vs));
         kb_s[c] = (float)mean;
         vs_s[c] = (float)a[5];
         if (SO) {
-            out.q2bar[off + c] = a[1] / n;
-            const double mx = a[3] / n;
-            const double s2 = fmax(a[4] / n - mx * mx, 0.0);
+            out.q2bar[off + c] = per_row(a[1]);
+            const double mx = per_row(a[3]);
+            const double s2 = fmax(per_row(a[4]) - mx * mx, 0.0);
             out.ksig2[off + c] = s2;
             router_store(out.ksig2_r + rhead, j, c, D, s2);
         }

@@ -186,6 +186,48 @@ def test_block_stats(name):
         assert (err <= 64 * U32 * mag + 1e-30).all(), (h, float((err / mag).max()))
 
 
+@pytest.mark.parametrize("second_order", [False, True])
+def test_block_stats_bf16_d64_ragged(second_order):
+    """The bf16 statistics kernel at D = 64 (the bench workloads are D = 128),
+    2 heads, T = 64 * 45 + 23 (a 23-row last block), keys and values with
+    per-dimension offsets so that H and the variances are far from zero:
+    block means bit-identical to float64, V-hat to fp32 rounding, H within
+    64 fp32 ulps of sum |k| |v|, q'^2 and sigma^2 to 1e-14 / 1e-12, and the
+    key norms bounding ||kbar_j|| from above within 2e-6."""
+    T, D, H = 64 * 45 + 23, 64, 2
+    N = -(-T // 64)
+    say(f"[gpu] stats parity bf16 D=64 T={T} so={second_order}")
+    r = np.random.default_rng(64 + second_order)
+    off = r.standard_normal(D)
+    q = r.standard_normal((1, H, T, D))
+    k = r.standard_normal((1, H, T, D)) + off
+    v = 0.5 * r.standard_normal((1, H, T, D)) - off
+    dev = [torch.from_numpy(a).to(torch.bfloat16).cuda().contiguous() for a in (q, k, v)]
+    host = [t.double().cpu().numpy() for t in dev]   # the exact values the GPU sees
+    st = P.pisa_block_stats(*dev, second_order=second_order)
+    torch.cuda.synchronize()
+    ops = P.operand_views(st, dev[1])
+    NC = -(-N // 16)
+    knr = ops["knorm"][:H * NC * 16].reshape(1, H, NC * 16).cpu().numpy()
+    s = 1 / math.sqrt(D)
+    for h in range(H):
+        qh, kh, vh = (x[0, h] for x in host)
+        ref = O.kv_block_stats(kh, vh, 64)
+        rq, rq2 = O.pool_queries(qh, 64, s)
+        assert np.array_equal(st.kbar[0, h].cpu().numpy(), ref.kbar), h
+        assert np.array_equal(st.qbar[0, h].cpu().numpy(), rq), h
+        np.testing.assert_allclose(st.vsum[0, h].cpu().numpy(), ref.vsum.astype(np.float32), rtol=2 * U32, atol=1e-30)
+        mag = np.abs(kh).T @ np.abs(vh)
+        err = np.abs(st.hsum[0, h].cpu().numpy() - ref.H)
+        assert (err <= 64 * U32 * mag + 1e-30).all(), (h, float((err / mag).max()))
+        if second_order:
+            np.testing.assert_allclose(st.q2bar[0, h].cpu().numpy(), rq2, rtol=1e-14, atol=0)
+            np.testing.assert_allclose(st.ksig2[0, h].cpu().numpy(), ref.sig2, rtol=1e-12, atol=1e-13)
+        nrm = np.sqrt((ref.kbar ** 2).sum(axis=1))
+        kn = knr[0, h][:N].astype(np.float64)
+        assert (kn >= nrm).all() and (kn <= nrm * (1 + 2e-6) + 1e-30).all(), h
+
+
 def check_routing(name, run, heads):
     w = run.w
     idx = run.idx.cpu().numpy()

@@ -664,26 +664,44 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) acc[dt] = zero16();
 
-    // exact KV blocks
-    for (int w0 = 0; w0 < NW; w0 += 2) {   // exact KV blocks j: the set bits of the mask row
-        uint64_t bits = mask_pair(mrow, w0, NW);
-        while (bits) {
-            const int j = 32 * w0 + __builtin_ctzll(bits);
-            bits &= bits - 1;
-            const int nval = min(kBlock, T - j * kBlock);
-            uint4 kr[C::LPT], vr_[C::LPT];
-            const __amdgpu_buffer_rsrc_t rk = brsrc(k + base + (int64_t)j * kBlock * D, (uint32_t)(nval * C::RB));
-            const __amdgpu_buffer_rsrc_t rv = brsrc(v + base + (int64_t)j * kBlock * D, (uint32_t)(nval * C::RB));
+    // exact KV blocks j: the set bits of the mask row, in ascending order; the
+    // K and V tiles of the next one load into registers while this one's
+    // products run
+    int w0 = 0;
+    uint64_t bits = mask_pair(mrow, 0, NW);
+    auto next_exact = [&]() {   // the next exact block, or -1
+        while (bits == 0) {
+            w0 += 2;
+            if (w0 >= NW) return -1;
+            bits = mask_pair(mrow, w0, NW);
+        }
+        const int jn = 32 * w0 + __builtin_ctzll(bits);
+        bits &= bits - 1;
+        return jn;
+    };
+    uint4 kr[C::LPT], vr_[C::LPT];
+    auto load_kv = [&](int jl) {
+        const int nl = min(kBlock, T - jl * kBlock);
+        const __amdgpu_buffer_rsrc_t rk = brsrc(k + base + (int64_t)jl * kBlock * D, (uint32_t)(nl * C::RB));
+        const __amdgpu_buffer_rsrc_t rv = brsrc(v + base + (int64_t)jl * kBlock * D, (uint32_t)(nl * C::RB));
 #pragma unroll
-            for (int m = 0; m < C::LPT; ++m) {
-                const uint32_t o = (uint32_t)(16 * (tid + kThreads * m));
-                kr[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, (int)o, 0, 0));
-                vr_[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, (int)o, 0, 0));
-            }
+        for (int m = 0; m < C::LPT; ++m) {
+            const uint32_t o = (uint32_t)(16 * (tid + kThreads * m));
+            kr[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, (int)o, 0, 0));
+            vr_[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, (int)o, 0, 0));
+        }
+    };
+    int j = next_exact();
+    if (j >= 0) load_kv(j);
+    while (j >= 0) {
+        {
+            const int nval = min(kBlock, T - j * kBlock);
             __syncthreads();
             tile_store<D>(sK, kr, tid);
             tile_store<D>(sV, vr_, tid);
             __syncthreads();
+            const int jn = next_exact();
+            if (jn >= 0) load_kv(jn);
             f32x16_t s = zero16(), dp = zero16();
 #pragma unroll
             for (int ks = 0; ks < C::KS; ++ks) {
@@ -707,6 +725,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                     acc[dt] = mfma(a, lo, acc[dt]);
                 }
             }
+            j = jn;
         }
     }
     // virtual tokens, 64 blocks at a time: kbar hi / lo tiles in LDS

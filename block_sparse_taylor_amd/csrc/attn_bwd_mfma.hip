@@ -250,6 +250,35 @@ __device__ __forceinline__ void tile_dma(unsigned char* lds, __amdgpu_buffer_rsr
     }
 }
 
+// The staged tile of tile_dma, issued from inline asm: the compiler does not
+// count these among its memory operations and adds no wait of its own
+// before reads of the destination, so a kernel that uses them orders every
+// such read with an explicit s_waitcnt vmcnt and a barrier. M0 (the LDS
+// address operand) is saved and restored around each instruction.
+template <int D>
+__device__ __forceinline__ void tile_dma_asm(unsigned char* lds, const void* src, uint32_t bytes, int wave,
+                                             int lane) {
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+    constexpr int NI = BC<D>::TILE / 1024, RPI = 1024 / BC<D>::RB;
+    static_assert(NI % 4 == 0 && kThreads == 256, "four waves share a tile's DMA instructions");
+    const uint64_t a = reinterpret_cast<uint64_t>(src);
+    const u32x4_t d = {(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a),
+                       (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xFFFFu),
+                       (uint32_t)__builtin_amdgcn_readfirstlane(bytes), 0x00020000u};
+#pragma unroll
+    for (int m = 0; m < NI / 4; ++m) {
+        const int n = wave * (NI / 4) + m;
+        const int row = RPI * n + lane / BC<D>::CH, pos = lane % BC<D>::CH;
+        const uint32_t voff = (uint32_t)(row * BC<D>::RB + 16 * (pos ^ swz<D>(row)));
+        const uint32_t la = __builtin_amdgcn_readfirstlane(
+            (uint32_t)(size_t)(__attribute__((address_space(3))) unsigned char*)(lds + 1024 * n));
+        uint32_t saved;
+        asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+                     "buffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+                     : "=&s"(saved) : "s"(la), "v"(voff), "s"(d) : "memory");
+    }
+}
+
 struct VirtRow {
     const uint32_t* mrow;
     const float* wrow;
@@ -454,14 +483,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 // (its half of the head dims, hi and lo) once for all of them.
 constexpr int kRsBlocks = 8;
 template <int D>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void bwd_rowstats_fwd_kernel(
+__global__ __launch_bounds__(kThreads) void bwd_rowstats_fwd_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ o, const bf16_t* __restrict__ dout,
     const bf16_t* __restrict__ hh, const bf16_t* __restrict__ hl, const float* __restrict__ fwd_rstat,
     f32x4_t* __restrict__ rowstat, int T, int N, float scale, int first_order) {
     using C = BC<D>;
     constexpr int HX = C::DT / 2;
+    // The Q, O and dout tiles of a query block, coalesced by buffer->LDS DMA
+    // in the staged layout, two blocks deep: those of block i + 1 arrive while
+    // block i is computed. The DMAs are inline asm (tile_dma_asm); every read
+    // of a stage follows the explicit wait and barrier at the block's start.
+    __shared__ __attribute__((aligned(16))) unsigned char st0[3 * C::TILE];
+    __shared__ __attribute__((aligned(16))) unsigned char st1[3 * C::TILE];
     __shared__ float sbp[2][32];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r32 = lane & 31, g = lane >> 5;
     const int kt = wave >> 1, qt = wave & 1;
     const int64_t bh = blockIdx.y;
@@ -478,20 +514,48 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                 la[x][ks] = as_bf16x8(*reinterpret_cast<const uint4*>(hl + a));
             }
     }
-    for (int i = i0; i < i1; ++i) {
-        const int t = i * kBlock + qt * 32 + r32;
+    // the H operands have landed (an s_waitcnt vmcnt(0) the compiler sees, so
+    // that it issues no waits of its own for them inside the loop, where they
+    // would also wait for the tile DMAs in flight)
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    auto dma_block = [&](int i, unsigned char* stg) {
+        const int rows = min(kBlock, T - i * kBlock);
+        const uint32_t bytes = (uint32_t)(rows * C::RB);
+        const int64_t off = base + (int64_t)i * kBlock * D;
+        tile_dma_asm<D>(stg, q + off, bytes, wave, lane);
+        tile_dma_asm<D>(stg + C::TILE, o + off, bytes, wave, lane);
+        tile_dma_asm<D>(stg + 2 * C::TILE, dout + off, bytes, wave, lane);
+    };
+    // 8 bytes (4 bf16: head dims d0 .. d0 + 3, d0 % 4 = 0) of row rr of a staged tile
+    auto row8 = [&](const unsigned char* tile, int rr, int d0) {
+        return *reinterpret_cast<const uint2*>(tile + rr * C::RB + 16 * ((d0 >> 3) ^ swz<D>(rr)) + 2 * (d0 & 7));
+    };
+    if (i0 < i1) dma_block(i0, st0);
+    auto body = [&](auto par, int i) {
+        constexpr int PAR = decltype(par)::value;
+        const unsigned char* sQ = PAR == 0 ? st0 : st1;
+        const unsigned char* sO = sQ + C::TILE;
+        const unsigned char* sG = sQ + 2 * C::TILE;
+        const int rr = qt * 32 + r32;
+        const int t = i * kBlock + rr;
+        float2 fr = {0.f, 0.f};
+        if (kt == 0 && g == 0 && t < T) fr = *reinterpret_cast<const float2*>(fwd_rstat + 2 * (bh * (int64_t)T + t));
+        // this wave's DMAs of block i (and every earlier load) have landed;
+        // after the barrier every wave's have, every wave is done with the
+        // other stage and with the previous block's partial sums
+        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" : "+v"(fr.x), "+v"(fr.y) : : "memory");
+        if (i + 1 < i1) dma_block(i + 1, PAR == 0 ? st1 : st0);
         float bp = 0.f;
         if (first_order) {
-            uint4 oreg[C::KS];
-            rows_from_global<D>(oreg, dout + base, t, T, g);
             f32x16_t hg[HX];
 #pragma unroll
             for (int x = 0; x < HX; ++x) {
                 f32x16_t c = zero16();
 #pragma unroll
                 for (int ks = 0; ks < C::KS; ++ks) {
-                    c = mfma(ha[x][ks], as_bf16x8(oreg[ks]), c);
-                    c = mfma(la[x][ks], as_bf16x8(oreg[ks]), c);
+                    const bf16x8_t b = row_op<D>(sG, rr, ks, g);
+                    c = mfma(ha[x][ks], b, c);
+                    c = mfma(la[x][ks], b, c);
                 }
                 hg[x] = c;
             }
@@ -501,14 +565,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
                     for (int run = 0; run < 4; ++run) {
                         const int d0 = (kt * HX + x) * 32 + 8 * run + 4 * g;
-                        const uint2 qq = *reinterpret_cast<const uint2*>(q + base + (int64_t)t * D + d0);
+                        const uint2 qq = row8(sQ, rr, d0);
                         bp += bf16_lo(qq.x) * hg[x][4 * run] + bf16_hi(qq.x) * hg[x][4 * run + 1] +
                               bf16_lo(qq.y) * hg[x][4 * run + 2] + bf16_hi(qq.y) * hg[x][4 * run + 3];
                     }
             }
             bp += __shfl_xor(bp, 32);
         }
-        __syncthreads();   // the previous block's partial sums have been read
         if (kt == 1 && g == 0) sbp[qt][r32] = bp;
         __syncthreads();
         if (kt == 0 && t < T) {
@@ -516,20 +579,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
             for (int c = 0; c < D / 16; ++c) {
                 const int d0 = (D / 2) * g + 8 * c;
-                const uint4 a = *reinterpret_cast<const uint4*>(dout + base + (int64_t)t * D + d0);
-                const uint4 b = *reinterpret_cast<const uint4*>(o + base + (int64_t)t * D + d0);
+                const uint2 a0 = row8(sG, rr, d0), a1 = row8(sG, rr, d0 + 4);
+                const uint2 b0 = row8(sO, rr, d0), b1 = row8(sO, rr, d0 + 4);
+                const uint4 a = make_uint4(a0.x, a0.y, a1.x, a1.y), b = make_uint4(b0.x, b0.y, b1.x, b1.y);
                 dl += bf16_lo(a.x) * bf16_lo(b.x) + bf16_hi(a.x) * bf16_hi(b.x) + bf16_lo(a.y) * bf16_lo(b.y) +
                       bf16_hi(a.y) * bf16_hi(b.y) + bf16_lo(a.z) * bf16_lo(b.z) + bf16_hi(a.z) * bf16_hi(b.z) +
                       bf16_lo(a.w) * bf16_lo(b.w) + bf16_hi(a.w) * bf16_hi(b.w);
             }
             dl += __shfl_xor(dl, 32);
             if (g == 0) {
-                const float2 fr = *reinterpret_cast<const float2*>(fwd_rstat + 2 * (bh * (int64_t)T + t));
                 const float beta = first_order ? scale * (bp + sbp[qt][r32]) / (float)T : 0.f;
                 f32x4_t rs = {fr.x, dl, beta, first_order ? fr.y : 0.f};
                 rowstat[bh * (int64_t)T + t] = rs;
             }
         }
+    };
+    for (int i = i0; i < i1; i += 2) {
+        body(std::integral_constant<int, 0>(), i);
+        if (i + 1 < i1) body(std::integral_constant<int, 1>(), i + 1);
     }
 }
 

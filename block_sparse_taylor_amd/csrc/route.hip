@@ -11,17 +11,18 @@
 //
 // The decision must equal a float64 evaluation, so the kernel scores in fp32
 // and settles every close call in fp64:
-//   1. One workgroup per (batch*head, 16 query blocks). fp32 MFMA
-//      (16x16x4) computes the 16 x N score rows into LDS; the inputs are the
-//      fp64 pooled statistics rounded to fp32. |r~ - r| <= eps_i with a
-//      rigorous bound eps_i = c (D + 4) u (s ||qbar_i|| max_j ||kbar_j|| [+ ln B]).
-//   2. Per row (one wave), a radix select over order-preserving 32-bit keys
-//      finds tau~, the topk-th largest r~. Blocks with r~ > tau~ + 2 eps are
-//      in Top_i; blocks with r~ < tau~ - 2 eps are out; the few in between
-//      (close calls) are ranked exactly: each one's r_ij is recomputed once in
-//      fp64 and the remaining members are those of smallest rank (ties: lower
-//      j). Rows with more than kAmbCap close calls use a 64-bit radix select
-//      over the fp64 scores instead.
+//   1. One workgroup per (batch*head, 16 query blocks). bf16 MFMA
+//      (16x16x32) on the fp64 pooled statistics split into bf16 hi + lo
+//      (three products per k-step) computes the 16 x N fp32 score rows into
+//      LDS. |r~ - r| <= eps_i with a rigorous bound eps_i = (4 (3 D + 8) u +
+//      4 2^-18) (s ||qbar_i|| max_j ||kbar_j|| [+ ln B] [+ max |prior|]).
+//   2. Per row (one wave), a search over order-preserving 32-bit keys
+//      (wave_select32) brackets tau~, the topk-th largest r~, within eps.
+//      Blocks with r~ above the bracket by 2 eps are in Top_i, below it by
+//      2 eps out; the few in between (close calls) are ranked exactly: each
+//      one's r_ij is recomputed once in fp64 and the remaining members are
+//      those of smallest rank (ties: lower j). Rows with more than kAmbCap
+//      close calls use a 64-bit radix select over the fp64 scores instead.
 //   3. Ids are written ascending, -1 padded.
 // The gate of the second-order term is decided the same way (fp32, with an
 // fp64 recomputation within the error bound of ln B) and the gated w table is

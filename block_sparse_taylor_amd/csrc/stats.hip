@@ -195,8 +195,9 @@ __device__ __forceinline__ bf16x8_t tr_operand(const bf16_t* tile, int r0, int c
 // 32x32x16 bf16 MFMA operand layout (lane l, element e in 0..7):
 //   A[m = l%32][k = 8(l/32) + e],  B[k = 8(l/32) + e][n = l%32]
 //   C[m = 8(i/4) + 4(l/32) + i%4][n = l%32] for accumulator register i.
-// C[a][b] += sum_t K[t][a] V[t][b]: A = K^T and B = V, both gathered
-// column-wise from the row-major LDS tiles.
+// C[a][b] += sum_t K[t][a] V[t][b]: A = K^T and B = V, both by transposed
+// reads of the row-major LDS tiles (tr_operand; the k order of a k-step is
+// permuted alike in both operands, which leaves the sum unchanged).
 template <int D, bool SO>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void stats_bf16_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, int T,
